@@ -1,0 +1,166 @@
+/*
+ * moe_mx.h -- C ABI of the MI355X (gfx950) routed-experts MoE decode step:
+ * MXFP8 activations x FP4 (e2m1 + E8M0) expert weights.
+ *
+ * The operation (vLLM API pages "vllm.models.kimi_k3.nvidia.specialized_decode.
+ * cutedsl.moe.experts" and "...cutedsl.moe.experts_runtime", PersistentExperts.run):
+ * each token's BF16 row is quantized to MXFP8 (32-element blocks, e4m3 codes and an
+ * E8M0 scale); each (token, top-k slot) route then computes, against its expert's
+ * weights,
+ *     a   = W13[e] . x            (FC1, 2I rows: gate 0..I-1, up I..2I-1)
+ *     h   = silu(gate) * up       (FP32, SwiGLU)
+ *     hq  = MXFP8(h)              (32-blocks, hidden exponent rule)
+ *     y   = W2[e] . hq            (FC2, D rows), rounded to BF16
+ * and the result is written as output row t*topk + s (the caller's top-k order, no
+ * routing weight applied).  Experts shared by several tokens stream their weights
+ * once per call for all of them.
+ *
+ * Conventions of every entry point:
+ *   - pointers named *_dev are DEVICE pointers, owned by the caller; the library
+ *     allocates nothing and keeps no pointer past the call;
+ *   - `stream` is a hipStream_t (NULL = the null stream); calls only enqueue work on
+ *     it and never synchronize;
+ *   - the return value is MOE_OK (0) or a negative moe_status; arguments are checked
+ *     on the host before anything is enqueued, so an error enqueues nothing;
+ *   - device-side preconditions that are NOT checked: expert ids within [0, E) and
+ *     distinct within each token's top-k (out-of-range ids are skipped and flagged in
+ *     the unit table, see moe_units_export).
+ *
+ * Canonical data layouts (row-major, bytes):
+ *   x        BF16  [B, D]
+ *   plan     u8    [B, D] e4m3 codes, followed by u8 [B, D/32] E8M0 scales
+ *   ids      i32   [B, topk]
+ *   w13      u8    [E, 2I, D/2]  two e2m1 codes per byte, low nibble = even k
+ *   s13      u8    [E, 2I, D/32] E8M0 (2^(byte-127)) per 32 consecutive k of a row
+ *   w2       u8    [E, D, I/2],  s2 u8 [E, D, I/32]
+ *   out      BF16  [B*topk, D]
+ * Supported shapes: 512 <= D <= 16384 with D % 512 == 0, 32 <= I <= 512 with
+ * I % 32 == 0, 1 <= E <= 1024, 1 <= topk <= 64, 1 <= B*topk <= 65536; moe_group also
+ * needs E * ceil(B/32) + 2E <= 15360 (its per-expert token bitmasks live in LDS).
+ */
+#ifndef MOE_MX_H
+#define MOE_MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* null pointer, bad size or unsupported shape */
+  MOE_ENOSPACE = -2,     /* plan, workspace or output buffer too small */
+  MOE_EHIP = -3,         /* a HIP call or kernel launch failed */
+};
+
+/* Human-readable name of a moe_status value (static string). */
+const char* moe_status_string(int status);
+
+/* ---------------------------------------------------------------- sizes ---- */
+
+/* Bytes of the MXFP8 plan of B tokens of D features: B*D codes + B*D/32 scales
+ * (experts page, ExpertsPlanKernel / plan_chunk).  0 on invalid sizes. */
+size_t moe_plan_bytes(int32_t B, int32_t D);
+
+/* Bytes of the caller-owned workspace for calls with up to B_max tokens of topk
+ * routes (unit table, hidden-exchange images, FC1 partial sums and the self-resetting
+ * counters; runtime page, scratch()).  0 on invalid sizes. */
+size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32_t topk);
+
+/* Bytes of the four packed weight buffers written by moe_pack_weights.  They equal
+ * the canonical sizes (the packing only reorders 16-byte code runs and scale bytes),
+ * except that FC2 codes and scales are padded to a multiple of 128 along I.
+ * Returns MOE_OK or MOE_EINVAL. */
+int moe_packed_weight_bytes(int32_t E, int32_t D, int32_t I, size_t* w13_bytes,
+                            size_t* s13_bytes, size_t* w2_bytes, size_t* s2_bytes);
+
+/* ---------------------------------------------------------------- setup ---- */
+
+/* One-time, untimed re-layout of canonical expert weights (layouts above) into the
+ * tile-major order the experts kernel streams: per 16-row tile and 128-wide K step, one
+ * contiguous 1 KB run of FP4 codes, and per tile the E8M0 bytes of four K steps in one
+ * 32-bit word per lane (the pages likewise keep their scales tile-major, experts page
+ * ExpertsKernel.schedule / produce).  All eight pointers are device buffers of the
+ * sizes above; canonical and packed buffers must not overlap. */
+int moe_pack_weights(int32_t E, int32_t D, int32_t I, const void* w13_dev, const void* s13_dev,
+                     const void* w2_dev, const void* s2_dev, void* w13p_dev, void* s13p_dev,
+                     void* w2p_dev, void* s2p_dev, void* stream);
+
+/* Zero the workspace once after allocating it (runtime page, scratch(): the pages
+ * pre-fill theirs with a sentinel).  Every experts call leaves its counters zero
+ * again, so no per-call reset is needed. */
+int moe_workspace_init(void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Packed expert weights of one layer (pointers from moe_pack_weights). */
+typedef struct {
+  int32_t E, D, I;
+  const void* w13; /* packed FC1 codes   */
+  const void* s13; /* packed FC1 scales  */
+  const void* w2;  /* packed FC2 codes   */
+  const void* s2;  /* packed FC2 scales  */
+} moe_weights_t;
+
+/* ----------------------------------------------------------- hot path ---- */
+
+/* MXFP8 quantization of x (BF16 [B, D]) into `plan` (experts page, plan_chunk /
+ * mx_block): per 32-element block, exact amax; E8M0 exponent e = the smallest with
+ * amax * 2^-e <= 448 (0 -> e = -127); codes = e4m3 round-to-nearest-even of
+ * x * 2^-e.  plan_bytes must be >= moe_plan_bytes(B, D). */
+int moe_plan(const void* x_dev, int32_t B, int32_t D, void* plan_dev, size_t plan_bytes,
+             void* stream);
+
+/* Unit table of the batch's routes (experts page, ExpertsKernel.group and
+ * ExpertsGroupKernel): expert e's routes, in token order, fill ceil(n_e / 8) units
+ * numbered in ascending expert order; each unit row holds eight pair indices
+ * t*topk + s, -1 where padded.  Also lists the distinct experts ("groups") with their
+ * first unit and unit count, which the experts kernel walks.  Written into the
+ * workspace; run it before moe_experts_run on the same stream. */
+int moe_group(const int32_t* ids_dev, int32_t B, int32_t topk, int32_t E, void* ws_dev,
+              size_t ws_bytes, void* stream);
+
+/* Copy the unit table that moe_group left in the workspace into caller device
+ * buffers (for inspection): header_dev i32[4] = {n_units, n_groups, n_column_tiles,
+ * flags (bit 0: an id was out of range, bit 1: an id repeated within a token, bit 2: an
+ * experts call gave up waiting for a hidden block -- never expected)},
+ * unit_expert_dev i32[max_units],
+ * unit_rows_dev i32[max_units, 8].  Enqueued device-to-device copies. */
+int moe_units_export(const void* ws_dev, size_t ws_bytes, int32_t B, int32_t topk, int32_t E,
+                     void* header_dev, void* unit_expert_dev, void* unit_rows_dev,
+                     int32_t max_units, void* stream);
+
+/* Options of moe_experts_run (zero-initialise for the defaults). */
+typedef struct {
+  /* Exponent rule of the hidden requantization: 0 = default (the pages' choice: floor
+   * on the TP8 shard, I == 384; the no-saturation rule otherwise), 1 = no saturation
+   * (smallest e with amax * 2^-e <= 448), 2 = floor (OCP: e = floor(log2 amax) - 8,
+   * saturating). */
+  int32_t hidden_rule;
+  int32_t ksplit;     /* FC1 K split into this many work items, 0 = auto */
+  int32_t fc2_rows;   /* output rows per FC2 work item: 0 (auto) or 256 */
+  int32_t grid;       /* persistent workgroups, 0 = auto */
+  int32_t col_tiles;  /* 16-token column tiles per weight pass (1, 2 or 4), 0 = auto */
+  int32_t reserved[3];
+  void* hidden_codes_dev;  /* optional u8 [B*topk, I]: the hidden's e4m3 codes per route */
+  void* hidden_scales_dev; /* optional u8 [B*topk, I/32]: its E8M0 scales */
+} moe_run_opts_t;
+
+/* The routed experts (experts page, ExpertsKernel; runtime page, PersistentExperts.run):
+ * FC1 against the packed w13 for every distinct expert of the batch and all of its
+ * tokens, SwiGLU, MXFP8 requantization of the hidden, FC2 against the packed w2, BF16
+ * rows into out_dev [B*topk, D] in the caller's top-k order.  Reads the plan written by
+ * moe_plan and the unit table written by moe_group (same B, topk and workspace).
+ * One persistent kernel: work items (FC1 K-slices, then FC2 row blocks) are claimed in
+ * order from one device-wide counter; FC2 items wait for their expert's hidden, which
+ * only earlier-claimed FC1 items produce, so no co-residency is required.  Calls that
+ * share a workspace must not overlap (one stream, or ordered streams). */
+int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
+                    const void* plan_dev, int32_t B, int32_t topk, void* ws_dev, size_t ws_bytes,
+                    void* out_dev, size_t out_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MX_H */

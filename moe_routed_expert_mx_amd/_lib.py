@@ -1,0 +1,140 @@
+"""ctypes binding of libmoe_mx.so (include/moe_mx.h): argument marshalling only.
+
+Every entry point keeps the C name.  Tensors are torch tensors on the GPU (PyTorch is
+used for device memory and streams only); every step of the path runs in the HIP
+library.  Errors from the library raise ``MoeError``.  There is no fallback: if the
+library is not built, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mx.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOSPACE, MOE_EHIP = 0, -1, -2, -3
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class moe_weights_t(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("D", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("w13", ctypes.c_void_p), ("s13", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+
+
+class moe_run_opts_t(ctypes.Structure):
+    _fields_ = [("hidden_rule", ctypes.c_int32), ("ksplit", ctypes.c_int32),
+                ("fc2_rows", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("col_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+                ("hidden_codes_dev", ctypes.c_void_p), ("hidden_scales_dev", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m moe_routed_expert_mx_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    c, P = ctypes, ctypes.c_void_p
+    sig = {
+        "moe_status_string": (c.c_char_p, [c.c_int]),
+        "moe_plan_bytes": (c.c_size_t, [c.c_int32, c.c_int32]),
+        "moe_workspace_bytes": (c.c_size_t, [c.c_int32] * 5),
+        "moe_packed_weight_bytes": (c.c_int, [c.c_int32] * 3 + [c.POINTER(c.c_size_t)] * 4),
+        "moe_pack_weights": (c.c_int, [c.c_int32] * 3 + [P] * 9),
+        "moe_workspace_init": (c.c_int, [P, c.c_size_t, P]),
+        "moe_plan": (c.c_int, [P, c.c_int32, c.c_int32, P, c.c_size_t, P]),
+        "moe_group": (c.c_int, [P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
+        "moe_units_export": (c.c_int, [P, c.c_size_t, c.c_int32, c.c_int32, c.c_int32, P, P, P,
+                                       c.c_int32, P]),
+        "moe_experts_run": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P,
+                                      c.c_int32, c.c_int32, P, c.c_size_t, P, c.c_size_t, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
+    return L
+
+
+lib = _load()
+EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
+            "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_units_export",
+            "moe_experts_run")
+
+
+def status_string(status: int) -> str:
+    return lib.moe_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ------------------------------------------------------------------- entry points
+def moe_plan_bytes(B: int, D: int) -> int:
+    return lib.moe_plan_bytes(B, D)
+
+
+def moe_workspace_bytes(E: int, D: int, I: int, B_max: int, topk: int) -> int:
+    return lib.moe_workspace_bytes(E, D, I, B_max, topk)
+
+
+def moe_packed_weight_bytes(E: int, D: int, I: int):
+    out = [ctypes.c_size_t(0) for _ in range(4)]
+    _check("moe_packed_weight_bytes", lib.moe_packed_weight_bytes(E, D, I, *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def moe_pack_weights(E, D, I, w13, s13, w2, s2, w13p, s13p, w2p, s2p, stream=None):
+    _check("moe_pack_weights", lib.moe_pack_weights(E, D, I, *map(_ptr, (w13, s13, w2, s2, w13p, s13p, w2p, s2p)),
+                                                    _stream(stream)))
+
+
+def moe_workspace_init(ws, stream=None):
+    _check("moe_workspace_init", lib.moe_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_plan(x, plan, stream=None):
+    B, D = x.shape
+    _check("moe_plan", lib.moe_plan(_ptr(x), B, D, _ptr(plan), _nbytes(plan), _stream(stream)))
+
+
+def moe_group(ids, E: int, ws, stream=None):
+    B, K = ids.shape
+    _check("moe_group", lib.moe_group(_ptr(ids), B, K, E, _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_units_export(ws, B, topk, E, header, unit_expert, unit_rows, stream=None):
+    _check("moe_units_export", lib.moe_units_export(_ptr(ws), _nbytes(ws), B, topk, E, _ptr(header),
+                                                    _ptr(unit_expert), _ptr(unit_rows), unit_expert.numel(),
+                                                    _stream(stream)))
+
+
+def moe_experts_run(weights: moe_weights_t, plan, B: int, topk: int, ws, out, *, hidden_rule=0, ksplit=0,
+                    fc2_rows=0, grid=0, col_tiles=0, hidden_codes=None, hidden_scales=None, stream=None):
+    opts = moe_run_opts_t(hidden_rule, ksplit, fc2_rows, grid, col_tiles, (ctypes.c_int32 * 3)(0, 0, 0),
+                          _ptr(hidden_codes), _ptr(hidden_scales))
+    _check("moe_experts_run", lib.moe_experts_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(plan), B, topk,
+                                                  _ptr(ws), _nbytes(ws), _ptr(out), _nbytes(out),
+                                                  _stream(stream)))

@@ -1,0 +1,74 @@
+"""Device buffers of one routed-experts layer, driven through the C ABI.
+
+``MoeLayer`` uploads canonical FP4/E8M0 weights once, packs them with
+``moe_pack_weights`` (the canonical copies are freed), owns the workspace and the
+plan buffer, and runs one decode step as the three ABI calls the runtime page's
+PersistentExperts.run makes: plan (MXFP8 of x), units (moe_group), experts.
+torch only allocates memory and supplies the stream.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib
+
+
+def _dev(a, device, dtype=None):
+    t = torch.as_tensor(a) if isinstance(a, np.ndarray) else a
+    return t.to(device=device, dtype=dtype) if dtype is not None else t.to(device)
+
+
+class MoeLayer:
+    def __init__(self, w13, s13, w2, s2, *, B_max: int, topk: int, device="cuda", replicas: int = 1):
+        E, I2, Dh = w13.shape
+        self.E, self.D, self.I = int(E), int(Dh) * 2, int(I2) // 2
+        self.B_max, self.topk, self.device = int(B_max), int(topk), torch.device(device)
+        sizes = _lib.moe_packed_weight_bytes(self.E, self.D, self.I)
+        canon = [_dev(a, self.device, torch.uint8).contiguous() for a in (w13, s13, w2, s2)]
+        self.packed = []
+        for _ in range(max(1, replicas)):
+            p = [torch.empty(n, dtype=torch.uint8, device=self.device) for n in sizes]
+            _lib.moe_pack_weights(self.E, self.D, self.I, *canon, *p)
+            self.packed.append(p)
+        del canon
+        self.structs = [_lib.moe_weights_t(self.E, self.D, self.I, *[t.data_ptr() for t in p]) for p in self.packed]
+        ws_bytes = _lib.moe_workspace_bytes(self.E, self.D, self.I, self.B_max, self.topk)
+        if ws_bytes == 0:
+            raise ValueError("unsupported shape for the workspace")
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
+        _lib.moe_workspace_init(self.ws)
+        self.plan = torch.empty(_lib.moe_plan_bytes(self.B_max, self.D), dtype=torch.uint8, device=self.device)
+
+    def out_buffer(self, B: int) -> torch.Tensor:
+        return torch.empty(B * self.topk, self.D, dtype=torch.bfloat16, device=self.device)
+
+    def forward(self, x: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None, *, replica: int = 0,
+                stream=None, **opts) -> torch.Tensor:
+        """x: BF16 [B, D] (or its uint16 bits), ids: int32 [B, topk], both on the device."""
+        B = x.shape[0]
+        if B > self.B_max or ids.shape != (B, self.topk):
+            raise ValueError("batch larger than B_max or ids of the wrong shape")
+        if out is None:
+            out = self.out_buffer(B)
+        _lib.moe_plan(x, self.plan, stream=stream)
+        _lib.moe_group(ids, self.E, self.ws, stream=stream)
+        _lib.moe_experts_run(self.structs[replica], self.plan, B, self.topk, self.ws, out, stream=stream, **opts)
+        return out
+
+    def units(self, B: int):
+        """The unit table moe_group left in the workspace: (header[4], unit_expert, unit_rows)."""
+        U = B * self.topk
+        hdr = torch.empty(4, dtype=torch.int32, device=self.device)
+        ue = torch.empty(U, dtype=torch.int32, device=self.device)
+        ur = torch.empty(U, 8, dtype=torch.int32, device=self.device)
+        _lib.moe_units_export(self.ws, B, self.topk, self.E, hdr, ue, ur)
+        h = hdr.cpu().numpy()
+        n = int(h[0])
+        return h, ue[:n].cpu().numpy(), ur[:n].cpu().numpy()
+
+    def plan_arrays(self, B: int):
+        p = self.plan.cpu().numpy()
+        codes = p[: B * self.D].reshape(B, self.D)
+        scales = p[B * self.D: B * self.D + B * self.D // 32].reshape(B, self.D // 32)
+        return codes, scales

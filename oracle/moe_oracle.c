@@ -233,6 +233,7 @@ typedef struct {
   const int32_t* routes;
   int n_routes;
   uint16_t* out;
+  float* out_f32;
   float* fc1;
   uint8_t *hcodes, *hscales;
   double *e2m1, *e4m3, *e8m0; /* decode tables (plain lookups of the decoders above) */
@@ -292,6 +293,7 @@ static int64_t oracle_route(const oracle_job* j, int out_row, int route) {
       acc = two_sum(acc, w * x, &inexact);
     }
     y[d] = oracle_float_to_bf16((float)acc);
+    if (j->out_f32) j->out_f32[(size_t)out_row * D + d] = (float)acc;
   }
   if (j->fc1) memcpy(j->fc1 + (size_t)out_row * 2 * I, a, sizeof(float) * 2 * I);
   if (j->hcodes) memcpy(j->hcodes + (size_t)out_row * I, hq, I);
@@ -318,7 +320,8 @@ static void* oracle_worker_main(void* arg) {
 }
 
 /* Runs the routes listed in `routes` (NULL: all B*K routes, in pair order) and writes
- * output row i for the i-th listed route.  Routes are independent of each other, so
+ * output row i for the i-th listed route (`out_f32`, optional: the same rows before
+ * their BF16 rounding, i.e. the exact FC2 sums rounded once to FP32).  Routes are independent of each other, so
  * they are spread over `nthreads` threads.  `inexact` (optional) receives the number
  * of FP64 additions that rounded (0 certifies the FC1/FC2 sums as exact).
  * Returns 0, or -1 on invalid arguments / ids. */
@@ -326,8 +329,8 @@ ORACLE_API int oracle_experts(int E, int D, int I, const uint8_t* w13, const uin
                               const uint8_t* w2, const uint8_t* s2, const uint8_t* xcodes,
                               const uint8_t* xscales, const int32_t* ids, int B, int K,
                               const int32_t* routes, int n_routes, int hidden_floor,
-                              uint16_t* out, float* fc1, uint8_t* hcodes, uint8_t* hscales,
-                              int nthreads, int64_t* inexact) {
+                              uint16_t* out, float* out_f32, float* fc1, uint8_t* hcodes,
+                              uint8_t* hscales, int nthreads, int64_t* inexact) {
   if (E <= 0 || D <= 0 || I <= 0 || D % 32 || I % 32 || B < 0 || K <= 0) return -1;
   for (int r = 0; r < B * K; ++r)
     if (ids[r] < 0 || ids[r] >= E) return -1;
@@ -339,7 +342,7 @@ ORACLE_API int oracle_experts(int E, int D, int I, const uint8_t* w13, const uin
   for (int c = 0; c < 256; ++c) e4m3[c] = oracle_e4m3_value((unsigned)c);
   for (int c = 0; c < 256; ++c) e8m0[c] = oracle_e8m0_value((unsigned)c);
   oracle_job job = {E, D, I, hidden_floor, w13, s13, w2, s2, xcodes, xscales, ids, B, K,
-                    routes, n_routes, out, fc1, hcodes, hscales, e2m1, e4m3, e8m0};
+                    routes, n_routes, out, out_f32, fc1, hcodes, hscales, e2m1, e4m3, e8m0};
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   oracle_worker workers[256];

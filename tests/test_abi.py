@@ -1,0 +1,94 @@
+"""The C ABI library loads, exports every entry point include/moe_mx.h declares, and
+rejects bad arguments on the host (no GPU needed: all of these return before any
+HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mx.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    import moe_routed_expert_mx_amd as pkg
+    return pkg
+
+
+def test_every_declared_symbol_is_exported(m):
+    names = _declared()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(m._lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(m.EXPORTED)
+
+
+def test_status_strings(m):
+    assert m.status_string(0) == "ok"
+    for s in (-1, -2, -3):
+        assert m.status_string(s) != "unknown status"
+
+
+def test_sizes(m):
+    assert m.moe_plan_bytes(1, 3584) == 3584 + 112
+    assert m.moe_plan_bytes(256, 3584) == 256 * 3584 * 33 // 32
+    assert m.moe_plan_bytes(0, 3584) == 0 and m.moe_plan_bytes(4, 100) == 0
+    w13, s13, w2, s2 = m.moe_packed_weight_bytes(160, 3584, 384)
+    # the packing only reorders: same bytes as the canonical layout when I % 128 == 0
+    assert (w13, s13, w2, s2) == (160 * 768 * 1792, 160 * 768 * 112, 160 * 3584 * 192, 160 * 224 * 256)
+    w13, s13, w2, s2 = m.moe_packed_weight_bytes(8, 512, 96)          # I padded to 128 for FC2
+    assert w2 == 8 * 32 * 1 * 1024 and s2 == 8 * 32 * 256
+    assert m.moe_workspace_bytes(160, 3584, 384, 256, 16) > m.moe_workspace_bytes(160, 3584, 384, 1, 16) > 0
+    assert m.moe_workspace_bytes(160, 3584, 385, 8, 16) == 0            # I % 32 != 0
+    assert m.moe_workspace_bytes(160, 3000, 384, 8, 16) == 0            # D % 512 != 0
+    with pytest.raises(m.MoeError):
+        m.moe_packed_weight_bytes(0, 3584, 384)
+
+
+def test_host_side_argument_errors(m):
+    L = m._lib.lib
+    fake = ctypes.c_void_p(0x1000)      # never dereferenced: every call below fails its checks first
+    assert L.moe_plan(None, 1, 512, fake, 10**6, None) == m._lib.MOE_EINVAL
+    assert L.moe_plan(fake, 1, 500, fake, 10**6, None) == m._lib.MOE_EINVAL
+    assert L.moe_plan(fake, 2, 512, fake, 100, None) == m._lib.MOE_ENOSPACE
+    assert L.moe_group(fake, 1, 0, 16, fake, 10**6, None) == m._lib.MOE_EINVAL
+    assert L.moe_group(fake, 1, 4, 16, fake, 10, None) == m._lib.MOE_ENOSPACE
+    w = m.moe_weights_t(16, 512, 128, 0x1000, 0x1000, 0x1000, 0x1000)
+    o = m.moe_run_opts_t()
+    args = lambda B, K, ws, out: (ctypes.byref(w), ctypes.byref(o), fake, B, K, fake, ws, fake, out, None)
+    assert L.moe_experts_run(*args(1, 4, 10**8, 16)) == m._lib.MOE_ENOSPACE         # output too small
+    assert L.moe_experts_run(*args(1, 4, 100, 4 * 512 * 2)) == m._lib.MOE_ENOSPACE  # workspace too small
+    assert L.moe_experts_run(*args(0, 4, 10**8, 10**8)) == m._lib.MOE_EINVAL
+    o.col_tiles = 3
+    assert L.moe_experts_run(*args(1, 4, 10**8, 10**8)) == m._lib.MOE_EINVAL
+    o.col_tiles = 0
+    o.hidden_rule = 5
+    assert L.moe_experts_run(*args(1, 4, 10**8, 10**8)) == m._lib.MOE_EINVAL
+    bad = m.moe_weights_t(16, 512, 100, 0x1000, 0x1000, 0x1000, 0x1000)
+    assert L.moe_experts_run(ctypes.byref(bad), None, fake, 1, 4, fake, 10**8, fake, 10**8, None) == m._lib.MOE_EINVAL
+    assert L.moe_pack_weights(16, 512, 128, None, fake, fake, fake, fake, fake, fake, fake, None) == m._lib.MOE_EINVAL
+    assert L.moe_workspace_init(None, 1024, None) == m._lib.MOE_EINVAL
+
+
+def test_product_does_not_reach_the_oracle():
+    """The HIP path and the oracle share nothing: no imports either way, no shared
+    sources."""
+    pkg = os.path.join(ROOT, "moe_routed_expert_mx_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in re.sub(r"#.*|//.*", "", src).lower().replace("oracle_", ""), f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".c")):
+            src = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "moe_routed_expert_mx_amd" not in src and "moe_mx.h" not in src

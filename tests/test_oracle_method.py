@@ -272,3 +272,16 @@ def test_combine_matches_weighted_sum(orc):
     y = torch.from_numpy(r["out"]).view(torch.bfloat16).double().numpy().reshape(3, 3, -1)
     ref = bf16_bits((d["weights"].astype(np.float64)[..., None] * y).sum(1).astype(np.float32))
     assert np.array_equal(out, ref)
+
+
+def test_out_f32_rounds_to_out(orc):
+    """The FP32 rows the oracle exposes are the rows before their BF16 rounding, and
+    equal the dense FP64 FC2 of its hidden rounded once to FP32."""
+    d = small(seed=13, B=3, E=4, K=2)
+    codes, scales = orc.plan(d["x"])
+    r = orc.experts(d["w13"], d["s13"], d["w2"], d["s2"], codes, scales, d["ids"], hidden_floor=False)
+    assert np.array_equal(bf16_bits(r["out_f32"]), r["out"])
+    for i in range(6):
+        e = d["ids"].ravel()[i]
+        y = dq_fp4(d["w2"][e], d["s2"][e]) @ dq_fp8(r["hcodes"][i], r["hscales"][i])
+        assert np.array_equal(r["out_f32"][i], y.astype(np.float32))
