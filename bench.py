@@ -41,7 +41,6 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 24, log=pr
     import torch
 
     import workloads
-    from moe_routed_expert_mx_amd import _lib
     from moe_routed_expert_mx_amd.layer import MoeLayer
 
     d = workloads.generate(name)
@@ -81,7 +80,7 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 24, log=pr
     ge = torch.cuda.CUDAGraph()
     with torch.cuda.graph(ge):
         for i in range(G):
-            _lib.moe_experts_run(layer.structs[i % R], layer.plan, w.B, w.K, layer.ws, out)
+            layer.experts(w.B, out, replica=i % R)
     ge.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -64,9 +64,15 @@ const char* moe_status_string(int status);
  * (experts page, ExpertsPlanKernel / plan_chunk).  0 on invalid sizes. */
 size_t moe_plan_bytes(int32_t B, int32_t D);
 
-/* Bytes of the caller-owned workspace for calls with up to B_max tokens of topk
- * routes (unit table, hidden-exchange images, FC1 partial sums and the self-resetting
- * counters; runtime page, scratch()).  0 on invalid sizes. */
+/* Bytes of the unit-table buffer of a batch of B tokens with topk routes each over E
+ * experts (header, per-unit expert and pair rows, the distinct-expert list). */
+size_t moe_units_bytes(int32_t B, int32_t topk, int32_t E);
+
+/* Bytes of the caller-owned workspace of the experts kernel for calls with up to B_max
+ * tokens (runtime page, scratch()): call counters, hidden-block flags and arrival
+ * counters, the hidden-exchange images and the FC1 partial sums.  Its layout is a
+ * function of (E, D, I, topk) and its size, so one workspace serves every batch up to
+ * the B_max it was sized for.  0 on invalid sizes. */
 size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32_t topk);
 
 /* Bytes of the four packed weight buffers written by moe_pack_weights.  They equal
@@ -89,8 +95,9 @@ int moe_pack_weights(int32_t E, int32_t D, int32_t I, const void* w13_dev, const
                      void* w2p_dev, void* s2p_dev, void* stream);
 
 /* Zero the workspace once after allocating it (runtime page, scratch(): the pages
- * pre-fill theirs with a sentinel).  Every experts call leaves its counters zero
- * again, so no per-call reset is needed. */
+ * pre-fill theirs with a sentinel).  The experts kernel keeps it consistent from call
+ * to call (arrival counters re-armed, flags tagged with the call number), so no
+ * per-call reset is needed. */
 int moe_workspace_init(void* ws_dev, size_t ws_bytes, void* stream);
 
 /* Packed expert weights of one layer (pointers from moe_pack_weights). */
@@ -115,18 +122,18 @@ int moe_plan(const void* x_dev, int32_t B, int32_t D, void* plan_dev, size_t pla
  * ExpertsGroupKernel): expert e's routes, in token order, fill ceil(n_e / 8) units
  * numbered in ascending expert order; each unit row holds eight pair indices
  * t*topk + s, -1 where padded.  Also lists the distinct experts ("groups") with their
- * first unit and unit count, which the experts kernel walks.  Written into the
- * workspace; run it before moe_experts_run on the same stream. */
-int moe_group(const int32_t* ids_dev, int32_t B, int32_t topk, int32_t E, void* ws_dev,
-              size_t ws_bytes, void* stream);
+ * first unit, unit count and first 16-column tile, which the experts kernel walks.
+ * Written into `units_dev` (moe_units_bytes(B, topk, E) bytes); run it before
+ * moe_experts_run on the same stream. */
+int moe_group(const int32_t* ids_dev, int32_t B, int32_t topk, int32_t E, void* units_dev,
+              size_t units_bytes, void* stream);
 
-/* Copy the unit table that moe_group left in the workspace into caller device
- * buffers (for inspection): header_dev i32[4] = {n_units, n_groups, n_column_tiles,
- * flags (bit 0: an id was out of range, bit 1: an id repeated within a token, bit 2: an
- * experts call gave up waiting for a hidden block -- never expected)},
- * unit_expert_dev i32[max_units],
+/* Copy the unit table that moe_group wrote into caller device buffers (for
+ * inspection): header_dev i32[4] = {n_units, n_groups, n_column_tiles, flags (bit 0: an
+ * id was out of range, bit 1: an id repeated within a token, bit 2: an experts call gave
+ * up waiting for a hidden block -- never expected)}, unit_expert_dev i32[max_units],
  * unit_rows_dev i32[max_units, 8].  Enqueued device-to-device copies. */
-int moe_units_export(const void* ws_dev, size_t ws_bytes, int32_t B, int32_t topk, int32_t E,
+int moe_units_export(const void* units_dev, size_t units_bytes, int32_t B, int32_t topk, int32_t E,
                      void* header_dev, void* unit_expert_dev, void* unit_rows_dev,
                      int32_t max_units, void* stream);
 
@@ -137,11 +144,10 @@ typedef struct {
    * (smallest e with amax * 2^-e <= 448), 2 = floor (OCP: e = floor(log2 amax) - 8,
    * saturating). */
   int32_t hidden_rule;
-  int32_t ksplit;     /* FC1 K split into this many work items, 0 = auto */
-  int32_t fc2_rows;   /* output rows per FC2 work item: 0 (auto) or 256 */
-  int32_t grid;       /* persistent workgroups, 0 = auto */
-  int32_t col_tiles;  /* 16-token column tiles per weight pass (1, 2 or 4), 0 = auto */
-  int32_t reserved[3];
+  int32_t grid;       /* persistent workgroups, at most the device's resident capacity
+                         for the kernel variant (MOE_EINVAL above it); 0 = all of it */
+  int32_t col_tiles;  /* 16-token column tiles per weight pass (1 or 2), 0 = auto */
+  int32_t reserved[5];
   void* hidden_codes_dev;  /* optional u8 [B*topk, I]: the hidden's e4m3 codes per route */
   void* hidden_scales_dev; /* optional u8 [B*topk, I/32]: its E8M0 scales */
 } moe_run_opts_t;
@@ -150,14 +156,17 @@ typedef struct {
  * FC1 against the packed w13 for every distinct expert of the batch and all of its
  * tokens, SwiGLU, MXFP8 requantization of the hidden, FC2 against the packed w2, BF16
  * rows into out_dev [B*topk, D] in the caller's top-k order.  Reads the plan written by
- * moe_plan and the unit table written by moe_group (same B, topk and workspace).
- * One persistent kernel: work items (FC1 K-slices, then FC2 row blocks) are claimed in
- * order from one device-wide counter; FC2 items wait for their expert's hidden, which
- * only earlier-claimed FC1 items produce, so no co-residency is required.  Calls that
- * share a workspace must not overlap (one stream, or ordered streams). */
+ * moe_plan and the unit table written by moe_group (same B and topk).
+ * One persistent, co-resident kernel: every workgroup takes an equal contiguous slice
+ * of the FC1 weight stream, then of the FC2 weight stream; FC2 waits, per expert, for
+ * the hidden blocks that FC1 slices publish (device-coherent stores, call-tagged flags).
+ * The grid is sized from the kernel's occupancy so that it is resident at once; do not
+ * run other kernels on the device concurrently with it.  Calls that share a workspace
+ * must not overlap (one stream, or ordered streams). */
 int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
-                    const void* plan_dev, int32_t B, int32_t topk, void* ws_dev, size_t ws_bytes,
-                    void* out_dev, size_t out_bytes, void* stream);
+                    const void* plan_dev, const void* units_dev, size_t units_bytes, int32_t B,
+                    int32_t topk, void* ws_dev, size_t ws_bytes, void* out_dev, size_t out_bytes,
+                    void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,9 +29,8 @@ class moe_weights_t(ctypes.Structure):
 
 
 class moe_run_opts_t(ctypes.Structure):
-    _fields_ = [("hidden_rule", ctypes.c_int32), ("ksplit", ctypes.c_int32),
-                ("fc2_rows", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("col_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+    _fields_ = [("hidden_rule", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("col_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5),
                 ("hidden_codes_dev", ctypes.c_void_p), ("hidden_scales_dev", ctypes.c_void_p)]
 
 
@@ -44,6 +43,7 @@ def _load():
     sig = {
         "moe_status_string": (c.c_char_p, [c.c_int]),
         "moe_plan_bytes": (c.c_size_t, [c.c_int32, c.c_int32]),
+        "moe_units_bytes": (c.c_size_t, [c.c_int32, c.c_int32, c.c_int32]),
         "moe_workspace_bytes": (c.c_size_t, [c.c_int32] * 5),
         "moe_packed_weight_bytes": (c.c_int, [c.c_int32] * 3 + [c.POINTER(c.c_size_t)] * 4),
         "moe_pack_weights": (c.c_int, [c.c_int32] * 3 + [P] * 9),
@@ -52,7 +52,7 @@ def _load():
         "moe_group": (c.c_int, [P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
         "moe_units_export": (c.c_int, [P, c.c_size_t, c.c_int32, c.c_int32, c.c_int32, P, P, P,
                                        c.c_int32, P]),
-        "moe_experts_run": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P,
+        "moe_experts_run": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_size_t,
                                       c.c_int32, c.c_int32, P, c.c_size_t, P, c.c_size_t, P]),
     }
     for name, (res, args) in sig.items():
@@ -62,7 +62,7 @@ def _load():
 
 
 lib = _load()
-EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
+EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_units_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
             "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_units_export",
             "moe_experts_run")
 
@@ -96,6 +96,10 @@ def moe_plan_bytes(B: int, D: int) -> int:
     return lib.moe_plan_bytes(B, D)
 
 
+def moe_units_bytes(B: int, topk: int, E: int) -> int:
+    return lib.moe_units_bytes(B, topk, E)
+
+
 def moe_workspace_bytes(E: int, D: int, I: int, B_max: int, topk: int) -> int:
     return lib.moe_workspace_bytes(E, D, I, B_max, topk)
 
@@ -120,21 +124,21 @@ def moe_plan(x, plan, stream=None):
     _check("moe_plan", lib.moe_plan(_ptr(x), B, D, _ptr(plan), _nbytes(plan), _stream(stream)))
 
 
-def moe_group(ids, E: int, ws, stream=None):
+def moe_group(ids, E: int, units, stream=None):
     B, K = ids.shape
-    _check("moe_group", lib.moe_group(_ptr(ids), B, K, E, _ptr(ws), _nbytes(ws), _stream(stream)))
+    _check("moe_group", lib.moe_group(_ptr(ids), B, K, E, _ptr(units), _nbytes(units), _stream(stream)))
 
 
-def moe_units_export(ws, B, topk, E, header, unit_expert, unit_rows, stream=None):
-    _check("moe_units_export", lib.moe_units_export(_ptr(ws), _nbytes(ws), B, topk, E, _ptr(header),
+def moe_units_export(units, B, topk, E, header, unit_expert, unit_rows, stream=None):
+    _check("moe_units_export", lib.moe_units_export(_ptr(units), _nbytes(units), B, topk, E, _ptr(header),
                                                     _ptr(unit_expert), _ptr(unit_rows), unit_expert.numel(),
                                                     _stream(stream)))
 
 
-def moe_experts_run(weights: moe_weights_t, plan, B: int, topk: int, ws, out, *, hidden_rule=0, ksplit=0,
-                    fc2_rows=0, grid=0, col_tiles=0, hidden_codes=None, hidden_scales=None, stream=None):
-    opts = moe_run_opts_t(hidden_rule, ksplit, fc2_rows, grid, col_tiles, (ctypes.c_int32 * 3)(0, 0, 0),
+def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, out, *, hidden_rule=0, grid=0,
+                    col_tiles=0, hidden_codes=None, hidden_scales=None, stream=None):
+    opts = moe_run_opts_t(hidden_rule, grid, col_tiles, (ctypes.c_int32 * 5)(0, 0, 0, 0, 0),
                           _ptr(hidden_codes), _ptr(hidden_scales))
-    _check("moe_experts_run", lib.moe_experts_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(plan), B, topk,
-                                                  _ptr(ws), _nbytes(ws), _ptr(out), _nbytes(out),
-                                                  _stream(stream)))
+    _check("moe_experts_run", lib.moe_experts_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(plan),
+                                                  _ptr(units), _nbytes(units), B, topk, _ptr(ws), _nbytes(ws),
+                                                  _ptr(out), _nbytes(out), _stream(stream)))

@@ -30,8 +30,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWG = 256;          // threads per experts workgroup (4 waves)
-constexpr int kHBMax = 128;       // hidden blocks of 32 per expert (I <= 4096)
-constexpr int kFC2Rows = 256;     // output rows per FC2 work item (4 tiles per wave)
 constexpr int kGroupThreads = 1024;
 constexpr uint32_t kSpinLimit = 1u << 22;  // polls of a flag before giving up
 
@@ -145,7 +143,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ x
   scales[idx] = static_cast<uint8_t>(e + 127);
 }
 
-// ------------------------------------------------------------------ workspace
+// ------------------------------------------------------------------ units buffer
+// The unit table lives in its own caller buffer: header, per-unit expert and eight
+// pair indices, then the distinct experts ("groups") with their first unit, unit count
+// and first 16-column tile.
 struct Table {
   int32_t* hdr;          // [16]: n_units, n_groups, n_tiles, flags (1: id out of range,
                          //        2: id repeated in a token, 4: a hidden wait timed out)
@@ -157,31 +158,22 @@ struct Table {
   int32_t* g_tile0;      // [G]
 };
 
-struct Layout {
-  size_t ready, arrive, hdr, unit_expert, unit_rows, g_expert, g_unit0, g_nunits, g_tile0;
-  size_t hcodes, hscales, partials, end;
-  int64_t max_tiles;
-};
-
 constexpr size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
-// Offsets depend only on (E, B, topk) up to the table, so moe_group and
-// moe_experts_run agree; the counters live in a region sized by E alone, which every
-// experts call leaves zero.
-Layout make_layout(int E, int B, int K, int I, int S) {
-  Layout L{};
+struct UnitsLayout {
+  size_t hdr, unit_expert, unit_rows, g_expert, g_unit0, g_nunits, g_tile0, end;
+};
+
+UnitsLayout units_layout(int B, int K, int E) {
+  UnitsLayout L{};
   const int64_t U = static_cast<int64_t>(B) * K;
   const int64_t G = U < E ? U : E;
-  size_t off = 256;  // control words: [0] claim counter, [1] done counter
-  L.ready = off;
-  off += static_cast<size_t>(E) * 4;
-  L.arrive = off;
-  off = align256(off + static_cast<size_t>(E) * kHBMax * 4);
+  size_t off = 0;
   L.hdr = off;
   off += 64;
   L.unit_expert = off;
-  off += U * 4;
-  L.unit_rows = off;
+  off = align256(off + U * 4);
+  L.unit_rows = off;  // 16-byte aligned: read as int4
   off += U * 32;
   L.g_expert = off;
   off += G * 4;
@@ -190,30 +182,20 @@ Layout make_layout(int E, int B, int K, int I, int S) {
   L.g_nunits = off;
   off += G * 4;
   L.g_tile0 = off;
-  off = align256(off + G * 4);
-  L.max_tiles = (U + 15 * G + 15) / 16;
-  if (I > 0) {
-    const int64_t IP = (I + 127) / 128 * 128;
-    L.hcodes = off;
-    off = align256(off + L.max_tiles * 16 * IP);
-    L.hscales = off;
-    off = align256(off + L.max_tiles * 16 * (IP / 32));
-    L.partials = off;
-    if (S > 1) off = align256(off + L.max_tiles * (I / 32) * S * 4096);
-  }
-  L.end = off;
+  off += G * 4;
+  L.end = align256(off);
   return L;
 }
 
-Table table_at(uint8_t* ws, const Layout& L) {
+Table table_at(uint8_t* base, const UnitsLayout& L) {
   Table t;
-  t.hdr = reinterpret_cast<int32_t*>(ws + L.hdr);
-  t.unit_expert = reinterpret_cast<int32_t*>(ws + L.unit_expert);
-  t.unit_rows = reinterpret_cast<int32_t*>(ws + L.unit_rows);
-  t.g_expert = reinterpret_cast<int32_t*>(ws + L.g_expert);
-  t.g_unit0 = reinterpret_cast<int32_t*>(ws + L.g_unit0);
-  t.g_nunits = reinterpret_cast<int32_t*>(ws + L.g_nunits);
-  t.g_tile0 = reinterpret_cast<int32_t*>(ws + L.g_tile0);
+  t.hdr = reinterpret_cast<int32_t*>(base + L.hdr);
+  t.unit_expert = reinterpret_cast<int32_t*>(base + L.unit_expert);
+  t.unit_rows = reinterpret_cast<int32_t*>(base + L.unit_rows);
+  t.g_expert = reinterpret_cast<int32_t*>(base + L.g_expert);
+  t.g_unit0 = reinterpret_cast<int32_t*>(base + L.g_unit0);
+  t.g_nunits = reinterpret_cast<int32_t*>(base + L.g_nunits);
+  t.g_tile0 = reinterpret_cast<int32_t*>(base + L.g_tile0);
   return t;
 }
 
@@ -382,6 +364,55 @@ __global__ void pack_w2_scales(const uint8_t* __restrict__ src, uint32_t* __rest
 }
 
 // ------------------------------------------------------------------ experts
+// Workspace of the experts kernel (caller-owned, zeroed once): per-workgroup call
+// counters kept in lockstep, per-hidden-block arrival counters (self-resetting) and
+// ready flags (tagged with the call number, so they never need a reset), the hidden
+// images that FC2 reads, and the split-block FP32 partial sums.
+constexpr int kMaxGrid = 2048;     // workgroups of the persistent grid (call counters)
+constexpr int kMaxGroups = 1024;   // distinct experts per call (E <= 1024)
+
+struct WsLayout {
+  size_t calls, arrive, flags, hcodes, hscales, partials, end;
+  int64_t max_tiles, max_blocks;
+  int nt_cap;
+};
+
+// 16-column tiles of all expert groups of a batch: sum_g ceil(n_g / 16) with
+// sum_g n_g = U over at most min(E, U) groups.
+int64_t max_tiles_for(int64_t U, int E) {
+  const int64_t G = U < E ? U : E;
+  return (U + 15 * G + 15) / 16;
+}
+
+// Column tiles per weight pass: an expert never has more tokens than the batch.
+int auto_col_tiles(int B) { return B <= 16 ? 1 : 2; }
+
+WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
+  WsLayout L{};
+  (void)D;
+  const int64_t U = static_cast<int64_t>(B_max) * K;
+  const int HB = I / 32;
+  const int64_t IP = (I + 127) / 128 * 128;
+  L.max_tiles = max_tiles_for(U, E);
+  L.max_blocks = L.max_tiles * HB;
+  L.nt_cap = auto_col_tiles(B_max);
+  size_t off = 0;
+  L.calls = off;
+  off = align256(off + kMaxGrid * 4);
+  L.arrive = off;
+  off = align256(off + L.max_blocks * 4);
+  L.flags = off;
+  off = align256(off + L.max_blocks * 4);
+  L.hcodes = off;
+  off = align256(off + L.max_tiles * 16 * IP);
+  L.hscales = off;
+  off = align256(off + L.max_tiles * 16 * (IP / 32));
+  L.partials = off;
+  off = align256(off + static_cast<size_t>(kMaxGrid) * 4 * L.nt_cap * 4096);
+  L.end = off;
+  return L;
+}
+
 struct ExpArgs {
   const uint8_t* w13p;
   const uint8_t* s13p;
@@ -389,23 +420,251 @@ struct ExpArgs {
   const uint8_t* s2p;
   const uint8_t* xcodes;
   const uint8_t* xscales;
-  uint32_t* ctrl;
-  uint32_t* ready;
-  uint32_t* arrive;
   Table tbl;
+  uint32_t* calls;
+  uint32_t* arrive;
+  uint32_t* flags;
   uint8_t* hcodes;
   uint8_t* hscales;
   float* partials;
   uint16_t* out;
   uint8_t* dump_codes;
   uint8_t* dump_scales;
-  int D, I, HB, NS1, NQ1, NS2, IP, K, S, floor_rule;
+  int D, I, HB, NS1, NQ1, IP, K, floor_rule;
+  int g_cap, u_cap;  // LDS capacity of the group list and the unit rows
 };
 
-// Pair index (t*topk + s) of column `col` of an expert group, or -1 (padding).
-__device__ __forceinline__ int column_pair(const ExpArgs& a, int unit0, int nunits, int col) {
+// ------------------------------------------------------------ LDS access
+// The weight stream reaches LDS by DMA (global_load_lds); the compiler's wait-count
+// pass cannot tell those writes from other LDS data and would drain the whole stream
+// before every LDS read.  Every LDS access after the first DMA therefore goes through
+// these asm helpers, which wait for their own completion (lgkmcnt) only; the stream's
+// completion is awaited explicitly (vmcnt) where a slot is consumed.
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ uint4 lds_ld16(uint32_t addr) {
+  uint4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_ld4(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_ld2(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_u16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_st16(uint32_t addr, uint4 v) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u x = {v.x, v.y, v.z, v.w};
+  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(x) : "memory");
+}
+// Four 16-byte reads at addr + k * stride (one wait for all four).
+template <int OFF, int STRIDE>
+__device__ __forceinline__ void lds_ld16x4(uint32_t addr, uint4& v0, uint4& v1, uint4& v2, uint4& v3) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%5\n\t"
+      "ds_read_b128 %1, %4 offset:%6\n\t"
+      "ds_read_b128 %2, %4 offset:%7\n\t"
+      "ds_read_b128 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+      : "v"(addr), "n"(OFF), "n"(OFF + STRIDE), "n"(OFF + 2 * STRIDE), "n"(OFF + 3 * STRIDE)
+      : "memory");
+}
+// Four 4-byte reads at addr + k * stride.
+template <int OFF, int STRIDE>
+__device__ __forceinline__ void lds_ld4x4(uint32_t addr, uint32_t& v0, uint32_t& v1, uint32_t& v2, uint32_t& v3) {
+  asm volatile(
+      "ds_read_b32 %0, %4 offset:%5\n\t"
+      "ds_read_b32 %1, %4 offset:%6\n\t"
+      "ds_read_b32 %2, %4 offset:%7\n\t"
+      "ds_read_b32 %3, %4 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+      : "v"(addr), "n"(OFF), "n"(OFF + STRIDE), "n"(OFF + 2 * STRIDE), "n"(OFF + 3 * STRIDE)
+      : "memory");
+}
+// Two 16-byte reads and one 4-byte read (a token tile's B operand and its scale word).
+template <int OFF_LO, int OFF_HI, int OFF_S>
+__device__ __forceinline__ void lds_ld_b(uint32_t addr16, uint32_t addr4, uint4& lo, uint4& hi, uint32_t& sw) {
+  asm volatile(
+      "ds_read_b128 %0, %3 offset:%5\n\t"
+      "ds_read_b128 %1, %3 offset:%6\n\t"
+      "ds_read_b32 %2, %4 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo), "=&v"(hi), "=&v"(sw)
+      : "v"(addr16), "v"(addr4), "n"(OFF_LO), "n"(OFF_HI), "n"(OFF_S)
+      : "memory");
+}
+// Uniform (same address in every lane) LDS word, moved to a scalar register.
+__device__ __forceinline__ int lds_uni(uint32_t addr) {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(lds_ld4(addr)));
+}
+// Workgroup barrier that waits for the workgroup's own LDS traffic only (the generic
+// barrier would also wait for the in-flight weight stream).
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int VMCNT>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(VMCNT) : "memory");
+}
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)(smem + lds_off), 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)(smem + lds_off), 4, 0, 0);
+}
+__device__ __forceinline__ uint32_t lds_base() {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  return static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void*)smem));
+}
+
+// ------------------------------------------------------------ LDS layout
+// [groups: expert, unit0, nunits, tile0 (g_cap each), chunk0 (g_cap + 1)]
+// [unit rows: u_cap x 8 u16 pair indices, 0xffff = padding]
+// [red: 3 waves x 4 tiles x NT x 1 KB]  [meta: 4 waves x R x 16 B]  [ring: 4 waves x R x slot]
+template <int NT>
+struct Geo {
+  static constexpr int R = NT == 1 ? 4 : 3;                  // items in flight per wave
+  static constexpr int SLOT = 4096 + 1024 + NT * 2048 + NT * 256;
+  static constexpr int L = 8 + 3 * NT;                       // DMA instructions per item
+  static constexpr int VM = (R - 1) * L;                     // vmcnt that completes the oldest item
+  static constexpr int RED = 3 * 4 * NT * 1024;
+};
+
+struct LdsMap {
+  uint32_t expert, unit0, nunits, tile0, chunk0, urows, red, meta, ring;
+};
+
+template <int NT>
+__host__ __device__ __forceinline__ LdsMap lds_map(uint32_t g_cap, uint32_t u_cap) {
+  LdsMap t;
+  t.expert = 0;
+  t.unit0 = t.expert + g_cap * 4;
+  t.nunits = t.unit0 + g_cap * 4;
+  t.tile0 = t.nunits + g_cap * 4;
+  t.chunk0 = t.tile0 + g_cap * 4;
+  t.urows = (t.chunk0 + (g_cap + 1) * 4 + 15) & ~15u;
+  t.red = t.urows + u_cap * 16;
+  t.meta = t.red + Geo<NT>::RED;
+  t.ring = t.meta + 4 * Geo<NT>::R * 16;
+  return t;
+}
+
+template <int NT>
+inline size_t lds_bytes(int g_cap, int u_cap) {
+  const LdsMap t = lds_map<NT>(static_cast<uint32_t>(g_cap), static_cast<uint32_t>(u_cap));
+  return t.ring + 4 * static_cast<size_t>(Geo<NT>::R) * Geo<NT>::SLOT;
+}
+
+// Per-workgroup copy of the unit table: the group list, chunk0[g] = first weight-pass
+// chunk of group g (chunks of NT column tiles; chunk0[n_groups] = total), and the unit
+// rows as 16-bit pair indices.  Plain LDS stores: this runs before the first DMA.
+template <int NT>
+__device__ __forceinline__ int load_groups(const ExpArgs& a, const LdsMap& m, int n_groups, int n_units) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int* expert = reinterpret_cast<int*>(smem + m.expert);
+  int* unit0 = reinterpret_cast<int*>(smem + m.unit0);
+  int* nunits = reinterpret_cast<int*>(smem + m.nunits);
+  int* tile0 = reinterpret_cast<int*>(smem + m.tile0);
+  int* chunk0 = reinterpret_cast<int*>(smem + m.chunk0);
+  uint16_t* urows = reinterpret_cast<uint16_t*>(smem + m.urows);
+  for (int i = threadIdx.x; i < n_groups; i += kWG) {
+    expert[i] = a.tbl.g_expert[i];
+    unit0[i] = a.tbl.g_unit0[i];
+    nunits[i] = a.tbl.g_nunits[i];
+    tile0[i] = a.tbl.g_tile0[i];
+  }
+  // unit rows: int32 pair indices (-1 = padding) -> u16; four units per thread in flight
+  const int4* rows = reinterpret_cast<const int4*>(a.tbl.unit_rows);
+  for (int base = 0; base < n_units; base += 4 * kWG) {
+    int4 r[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int u = base + q * kWG + static_cast<int>(threadIdx.x);
+      if (u < n_units) {
+        r[q][0] = rows[2 * u];
+        r[q][1] = rows[2 * u + 1];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int u = base + q * kWG + static_cast<int>(threadIdx.x);
+      if (u < n_units) {
+        auto pk = [](int lo, int hi) {
+          return (static_cast<uint32_t>(lo) & 0xffffu) | (static_cast<uint32_t>(hi) << 16);
+        };
+        *reinterpret_cast<uint4*>(urows + 8 * u) = make_uint4(pk(r[q][0].x, r[q][0].y), pk(r[q][0].z, r[q][0].w),
+                                                              pk(r[q][1].x, r[q][1].y), pk(r[q][1].z, r[q][1].w));
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < n_groups; base += 64) {
+      const int g = base + lane;
+      const int v = g < n_groups ? (((nunits[g] + 1) >> 1) + NT - 1) / NT : 0;
+      int inc = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d);
+        if (lane >= d) inc += o;
+      }
+      if (g < n_groups) chunk0[g] = carry + inc - v;
+      carry += __shfl(inc, 63);
+    }
+    if (lane == 0) chunk0[n_groups] = carry;
+  }
+  __syncthreads();
+  return chunk0[n_groups];
+}
+
+struct GroupInfo {
+  int g, c0, c1, cc, e, unit0, nunits, tile0, ntiles;  // c0, c1: the group's chunks [c0, c1)
+};
+
+// Fields of group g (uniform LDS words); cc is left to the caller.
+__device__ __forceinline__ GroupInfo group_at(const LdsMap& m, uint32_t lb, int g) {
+  GroupInfo gi;
+  gi.g = g;
+  gi.c0 = lds_uni(lb + m.chunk0 + 4 * g);
+  gi.c1 = lds_uni(lb + m.chunk0 + 4 * g + 4);
+  gi.e = lds_uni(lb + m.expert + 4 * g);
+  gi.unit0 = lds_uni(lb + m.unit0 + 4 * g);
+  gi.nunits = lds_uni(lb + m.nunits + 4 * g);
+  gi.tile0 = lds_uni(lb + m.tile0 + 4 * g);
+  gi.ntiles = (gi.nunits + 1) >> 1;
+  gi.cc = 0;
+  return gi;
+}
+
+// The group of weight-pass chunk `chunk` (largest g with chunk0[g] <= chunk).
+__device__ __forceinline__ GroupInfo group_of(const LdsMap& m, uint32_t lb, int n_groups, int chunk) {
+  int lo = 0, hi = n_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (lds_uni(lb + m.chunk0 + 4 * mid) <= chunk) lo = mid; else hi = mid - 1;
+  }
+  GroupInfo gi = group_at(m, lb, lo);
+  gi.cc = chunk - gi.c0;
+  return gi;
+}
+
+// Pair index (t*topk + s) of column `col` of a group, or -1 (padding).
+__device__ __forceinline__ int column_pair(const LdsMap& m, uint32_t lb, const GroupInfo& gi, int col) {
   const int u = col >> 3;
-  return u < nunits ? a.tbl.unit_rows[(unit0 + u) * 8 + (col & 7)] : -1;
+  if (u >= gi.nunits) return -1;
+  const uint32_t v = lds_ld2(lb + m.urows + ((gi.unit0 + u) * 8 + (col & 7)) * 2);
+  return v == 0xffffu ? -1 : static_cast<int>(v);
 }
 
 // Gated activation and MXFP8 requantization of one 16-column tile of hidden block j
@@ -414,7 +673,7 @@ __device__ __forceinline__ int column_pair(const ExpArgs& a, int unit0, int nuni
 // tot[0], tot[1]: gate rows 0-15 / 16-31 of the block; tot[2], tot[3]: the matching
 // up rows.  Lane l holds column l%16, block rows 4*(l/16)+r (+16 for tot[1], tot[3]).
 // Called by one whole wave.
-__device__ void hidden_epilogue(const ExpArgs& a, const v4f (&tot)[4], int j, int gtile, int pair) {
+__device__ __forceinline__ void hidden_epilogue(const ExpArgs& a, const v4f (&tot)[4], int j, int gtile, int pair) {
   const int l = threadIdx.x & 63;
   float h[2][4];
   float amax = 0.0f;
@@ -448,316 +707,485 @@ __device__ void hidden_epilogue(const ExpArgs& a, const v4f (&tot)[4], int j, in
   }
 }
 
-// FC1 work item: hidden block j (gate and up rows: four 16-row tiles) of the item's
-// expert over the K-step groups [q_lo, q_hi) (split c of S), for every token of the
-// expert (16-column tiles, NT at a time).  Wave w takes the K steps s = 4q + w, so each
-// wave streams its own contiguous KB runs; the four waves' partial sums are reduced
-// through LDS in a fixed order.  With S > 1 the split sums meet in the workspace and
-// the last-arriving split finishes the block (deterministic: splits summed in order).
-template <int NT, int QMAX>
-__device__ void fc1_item(const ExpArgs& a, int item, float* red) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int per_g = a.HB * a.S;
-  const int g = item / per_g, rem = item - g * per_g;
-  const int j = rem / a.S, c = rem - j * a.S;
-  const int e = a.tbl.g_expert[g], unit0 = a.tbl.g_unit0[g], nunits = a.tbl.g_nunits[g];
-  const int tile0 = a.tbl.g_tile0[g];
-  const int ntiles = (nunits + 1) >> 1;
-  const int q_lo = c * a.NQ1 / a.S, q_hi = (c + 1) * a.NQ1 / a.S, nq = q_hi - q_lo;
-  const uint8_t* wbase = a.w13p + static_cast<int64_t>(e * a.HB + j) * a.NS1 * 4096 + l * 16;
-  const uint8_t* sbase = a.s13p + static_cast<int64_t>(e * a.HB + j) * a.NQ1 * 1024 + l * 4;
-  const int xrow_scales = a.D / 32;
+// ------------------------------------------------------------ work partition
+// The chunks (groups x weight passes) are split in two halves A and B.  Each workgroup
+// walks four contiguous slices, in this order: FC1 steps of A, FC1 steps of B, FC2
+// units of A, FC2 units of B (experts page, ExpertsKernel.partition: FC1(A), FC1(B),
+// FC2(A), FC2(B)), so that a hidden block is needed only well after the slices that
+// produce it ran, and the FC1->FC2 dependency costs no waiting except at the very end.
+// An FC1 step is 64 weight rows (gate rows 32j..32j+31 and the matching up rows) x 128
+// K of hidden block j of a chunk; an FC2 unit is 16 output rows x I of a chunk.
+// Global FC1 block numbers run over half A, then half B (chunk * HB + j).
 
-  for (int cb = 0; cb < ntiles; cb += NT) {
-    int tok[NT];
+// floor(n / d) for 0 <= n < 2^52, d >= 1: the rounded double quotient is within one.
+__device__ __forceinline__ int div_floor(int64_t n, int d) {
+  int64_t q = static_cast<int64_t>(static_cast<double>(n) / static_cast<double>(d));
+  const int64_t r = n - q * d;
+  if (r < 0) --q;
+  else if (r >= d) ++q;
+  return static_cast<int>(q);
+}
+
+struct Slice {
+  int lo, hi;  // this workgroup's items [lo, hi) of the list
+  int T, P;    // list length, workgroups sharing it
+  int base;    // global FC1 block / FC2 unit of the list's first item
+};
+
+// List h: 0 = FC1(A), 1 = FC1(B), 2 = FC2(A), 3 = FC2(B); slices of near-equal length.
+__device__ __forceinline__ Slice make_slice(const ExpArgs& a, int n_chunks, int h) {
+  const int cA = (n_chunks + 1) / 2;
+  const int c_lo = (h & 1) ? cA : 0, c_hi = (h & 1) ? n_chunks : cA;
+  const int per_chunk = h < 2 ? a.HB : a.D / 16;
+  const int per = h < 2 ? a.HB * a.NS1 : a.D / 16;
+  const int G = static_cast<int>(gridDim.x), p = static_cast<int>(blockIdx.x);
+  Slice s;
+  s.T = (c_hi - c_lo) * per;
+  s.base = c_lo * per_chunk;
+  s.P = s.T < G ? s.T : G;
+  s.lo = p < s.P ? div_floor(static_cast<int64_t>(p) * s.T, s.P) : 0;
+  s.hi = p < s.P ? div_floor(static_cast<int64_t>(p + 1) * s.T, s.P) : 0;
+  return s;
+}
+
+// One wave's walk over its items: FC1 steps s_lo + w, s_lo + w + 4, ... of each block
+// of the slice, then FC2 units lo + w, lo + w + 4, ...  Besides the position it tracks
+// the item's chunk, its place in the chunk and the chunk's group, incrementally.
+struct Cursor {
+  int h;              // list 0..3; 4 = done; -1 = not started
+  int lo, hi, base;   // the list's slice
+  int b;              // FC1: block of the list; FC2: unit of the list
+  int s, s_hi;        // FC1: step in the block, end of the slice in the block
+  int gidx;           // global block / unit of the item
+  int chunk, j;       // its chunk, and hidden block (FC1) / output tile (FC2) in the chunk
+  GroupInfo gi;       // the chunk's group
+};
+
+__device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
+                                            int n_chunks, Cursor& c) {
+  const int w = threadIdx.x >> 6;
+  if (c.h < 2) {
+    c.s += 4;
+    if (c.s < c.s_hi) return;  // same block
+    c.b += 1;
+  } else {
+    c.b += 4;
+  }
+  bool fresh = false;
+  for (;;) {
+    if (c.h >= 0 && c.h < 2) {
+      const int bs = c.b * a.NS1;
+      if (bs < c.hi) {
+        const int s_lo = c.lo > bs ? c.lo - bs : 0;
+        const int s_hi = c.hi - bs < a.NS1 ? c.hi - bs : a.NS1;
+        if (s_hi - s_lo > w) {
+          c.s = s_lo + w;
+          c.s_hi = s_hi;
+          break;
+        }
+        c.b += 1;
+        continue;
+      }
+    } else if (c.h >= 2 && c.h < 4) {
+      if (c.b < c.hi) break;
+    }
+    if (c.h >= 3) {
+      c.h = 4;
+      return;
+    }
+    ++c.h;
+    const Slice sl = make_slice(a, n_chunks, c.h);
+    c.lo = sl.lo;
+    c.hi = sl.hi;
+    c.base = sl.base;
+    c.b = c.h < 2 ? c.lo / a.NS1 : c.lo + w;
+    fresh = true;
+  }
+  const int per_chunk = c.h < 2 ? a.HB : a.D / 16;
+  const int gidx = c.base + c.b;
+  if (fresh) {
+    c.chunk = gidx / per_chunk;
+    c.j = gidx - c.chunk * per_chunk;
+    c.gi = group_of(m, lb, n_groups, c.chunk);
+  } else {
+    int j = c.j + gidx - c.gidx, chunk = c.chunk;
+    while (j >= per_chunk) {
+      j -= per_chunk;
+      ++chunk;
+    }
+    c.j = j;
+    if (chunk != c.chunk) {
+      int g = c.gi.g;
+      while (chunk >= lds_uni(lb + m.chunk0 + 4 * g + 4)) ++g;
+      GroupInfo gi = group_at(m, lb, g);
+      gi.cc = chunk - gi.c0;
+      c.gi = gi;
+      c.chunk = chunk;
+    }
+  }
+  c.gidx = gidx;
+}
+
+// ------------------------------------------------------------ the item stream
+// A wave's item k lives in ring slot k % R of the wave: FC1 = four 1 KB weight tiles
+// (FP4 A operands), their E8M0 words, the NT token-column B operands (FP8) and their
+// E8M0 words; FC2 = NS2 1 KB weight tiles and their E8M0 word.  Every item issues the
+// same number L of DMA instructions (FC2 and the dummies past the end pad with
+// redundant word loads), so "the oldest of R items is complete" is always
+// s_waitcnt vmcnt((R-1)*L).  The item's metadata goes to a 16-byte LDS record.
+template <int NT, int NS2>
+__device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, uint32_t lb, const Cursor& c, int k) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  using G = Geo<NT>;
+  const int slot = k % G::R;
+  const uint32_t so = m.ring + (w * G::R + slot) * G::SLOT;  // offset from the LDS base
+  uint4 meta = make_uint4(2u, 0u, 0u, 0u);                   // 2: dummy
+  int done = 0;
+  const GroupInfo& gi = c.gi;
+  if (c.h < 2) {
+    const int s = c.s, q = s >> 2;
+    const int64_t wrow = static_cast<int64_t>(gi.e) * a.HB + c.j;
+    const uint8_t* wb = a.w13p + (wrow * a.NS1 + s) * 4096 + l * 16;
+    const uint8_t* sb = a.s13p + (wrow * a.NQ1 + q) * 1024 + l * 4;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) dma16(wb + rt * 1024, so + rt * 1024);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) dma4(sb + rt * 256, so + 4096 + rt * 256);
+    uint32_t live = 0;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const int pair = (cb + n < ntiles) ? column_pair(a, unit0, nunits, (cb + n) * 16 + (l & 15)) : -1;
-      tok[n] = pair >= 0 ? pair / a.K : -1;
+      const int tcol = gi.cc * NT + n;
+      const int pair = tcol < gi.ntiles ? column_pair(m, lb, gi, tcol * 16 + (l & 15)) : -1;
+      const int t = pair >= 0 ? pair / a.K : 0;
+      live |= (pair >= 0 ? 1u : 0u) << n;
+      const uint8_t* xr = a.xcodes + static_cast<int64_t>(t) * a.D + s * 128 + 16 * (l >> 4);
+      dma16(xr, so + 5120 + n * 2048);
+      dma16(xr + 64, so + 5120 + n * 2048 + 1024);
+      dma4(a.xscales + static_cast<int64_t>(t) * (a.D / 32) + 4 * s, so + 5120 + NT * 2048 + n * 256);
     }
-    v4f acc[4][NT];
+    meta = make_uint4(0u, static_cast<uint32_t>(c.gidx), static_cast<uint32_t>(s), live);
+    done = G::L;
+  } else if (c.h < 4) {
+    const int64_t tile = static_cast<int64_t>(gi.e) * (a.D / 16) + c.j;
+    const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
+#pragma unroll
+    for (int s = 0; s < NS2; ++s) dma16(wb + s * 1024, so + s * 1024);
+    dma4(a.s2p + tile * 256 + l * 4, so + 4096);
+    meta = make_uint4(1u, static_cast<uint32_t>(c.chunk), static_cast<uint32_t>(c.j), 0u);
+    done = NS2 + 1;
+  }
+  // pad to L DMA instructions (redundant word loads into the slot's B-operand area)
+  for (int i = done; i < G::L; ++i) dma4(a.s2p + l * 4, so + 5120 + (i % 8) * 256);
+  if (l == 0) lds_st16(lb + m.meta + (w * G::R + slot) * 16, meta);
+}
+
+// End of FC1 block b for the whole workgroup (every wave calls it, in block order):
+// the four waves' sums meet in LDS (asm, fixed order); wave 0 finishes the block -- or,
+// when the block is split over several workgroups' slices, files its partial sums and
+// the last-arriving contributor adds all of them in slice order (experts page,
+// ExpertsKernel.partials) and finishes it.  Finishing = SwiGLU + MXFP8 of the hidden
+// block for every column tile of the chunk, then its flag, tagged with the call number.
+template <int NT>
+__device__ __forceinline__ void fc1_finish(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
+                                           const Slice& li, int half, int lbk, v4f (&acc)[4][NT], uint32_t gen) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int NS1 = a.NS1, HB = a.HB;
+  const int p = blockIdx.x;
+  const int b = li.base + lbk;  // global block
+  if (w > 0) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[rt][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    // K-step groups in chunks of QMAX: every load of a chunk is issued before its first
-    // MFMA (weights from HBM, activations from L2).
-    for (int qc = 0; qc < nq; qc += QMAX) {
-      const int nqc = nq - qc < QMAX ? nq - qc : QMAX;
-      uint4 A[QMAX][4];
-      uint32_t SA[QMAX][4];
-      uint4 BL[QMAX][NT], BH[QMAX][NT];
-      uint32_t SB[QMAX][NT];
-#pragma unroll
-      for (int qi = 0; qi < QMAX; ++qi) {
-        const int q = q_lo + qc + (qi < nqc ? qi : nqc - 1);
-        const int s = 4 * q + w;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          A[qi][rt] = ld16(wbase + (static_cast<int64_t>(s) * 4 + rt) * 1024);
-          SA[qi][rt] = ld4(sbase + (static_cast<int64_t>(q) * 4 + rt) * 256);
-        }
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const int t = tok[n] >= 0 ? tok[n] : 0;
-          const uint8_t* xr = a.xcodes + static_cast<int64_t>(t) * a.D + s * 128 + 16 * (l >> 4);
-          BL[qi][n] = ld16(xr);
-          BH[qi][n] = ld16(xr + 64);
-          SB[qi][n] = ld4(a.xscales + static_cast<int64_t>(t) * xrow_scales + 4 * s);
-        }
+      for (int n = 0; n < NT; ++n) {
+        const v4f v = acc[rt][n];
+        lds_st16(lb + m.red + ((((w - 1) * 4 + rt) * NT + n) * 64 + l) * 16,
+                 make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])));
       }
+  }
+  wg_barrier();
+  if (w == 0) {
 #pragma unroll
-      for (int qi = 0; qi < QMAX; ++qi) {
-        if (qi < nqc) {
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            const bool live = tok[n] >= 0;
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            const v8i b = fp8_operand(live ? BL[qi][n] : z, live ? BH[qi][n] : z);
-            const int sb = live ? static_cast<int>((SB[qi][n] >> (8 * (l >> 4))) & 0xffu) : 127;
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-              const int sa = static_cast<int>((SA[qi][rt] >> (8 * w)) & 0xffu);
-              acc[rt][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  fp4_operand(A[qi][rt]), b, acc[rt][n], 4, 0, 0, sa, 0, sb);
-            }
-          }
-        }
-      }
-    }
-    // Cross-wave reduction: waves 1..3 park their sums in LDS, wave 0 adds them in order.
-    if (w > 0) {
+    for (int ww = 0; ww < 3; ++ww)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-          *reinterpret_cast<v4f*>(red + ((((w - 1) * 4 + rt) * NT + n) * 64 + l) * 4) = acc[rt][n];
-    }
-    __syncthreads();
-    if (w == 0) {
+        for (int n = 0; n < NT; ++n) {
+          const uint4 v = lds_ld16(lb + m.red + (((ww * 4 + rt) * NT + n) * 64 + l) * 16);
+          acc[rt][n][0] += __uint_as_float(v.x);
+          acc[rt][n][1] += __uint_as_float(v.y);
+          acc[rt][n][2] += __uint_as_float(v.z);
+          acc[rt][n][3] += __uint_as_float(v.w);
+        }
+    const int bs = lbk * NS1;
+    bool finish = li.lo <= bs && bs + NS1 <= li.hi;
+    if (!finish) {
+      // contributors: the slices owning the block's first and last steps, and between
+      // (slice p holds steps [floor(pT/P), floor((p+1)T/P)); its owner of x is
+      // ceil((x+1)P/T) - 1)
+      const int T = li.T, P = li.P;
+      auto owner = [&](int x) { return div_floor(static_cast<int64_t>(x + 1) * P + T - 1, T) - 1; };
+      const int pa = owner(bs), pb = owner(bs + NS1 - 1);
+      const int k = (li.lo / NS1 == lbk) ? 0 : 1;
+      float* slot = a.partials + ((static_cast<int64_t>(p) * 2 + half) * 2 + k) * NT * 1024 + l * 4;
 #pragma unroll
-      for (int ww = 0; ww < 3; ++ww)
+      for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
+          for (int r = 0; r < 4; ++r) st_dev_u32(slot + (n * 4 + rt) * 256 + r, __float_as_uint(acc[rt][n][r]));
+      wait_stores();
+      uint32_t old = 0;
+      if (l == 0) old = __hip_atomic_fetch_add(a.arrive + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __builtin_amdgcn_readfirstlane(old);
+      finish = old == static_cast<uint32_t>(pb - pa);
+      if (finish) {
+        compiler_fence();
+        if (l == 0) st_dev_u32(a.arrive + b, 0u);  // re-arm for the next call
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[rt][n] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int pp = pa; pp <= pb; ++pp) {
+          const int kk = (div_floor(static_cast<int64_t>(pp) * T, P) / NS1 == lbk) ? 0 : 1;
+          const float* src = a.partials + ((static_cast<int64_t>(pp) * 2 + half) * 2 + kk) * NT * 1024 + l * 4;
+#pragma unroll
           for (int n = 0; n < NT; ++n)
-            acc[rt][n] += *reinterpret_cast<const v4f*>(red + (((ww * 4 + rt) * NT + n) * 64 + l) * 4);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              const uint64_t v0 = ld_dev_u64(src + (n * 4 + rt) * 256);
+              const uint64_t v1 = ld_dev_u64(src + (n * 4 + rt) * 256 + 2);
+              acc[rt][n][0] += __uint_as_float(static_cast<uint32_t>(v0));
+              acc[rt][n][1] += __uint_as_float(static_cast<uint32_t>(v0 >> 32));
+              acc[rt][n][2] += __uint_as_float(static_cast<uint32_t>(v1));
+              acc[rt][n][3] += __uint_as_float(static_cast<uint32_t>(v1 >> 32));
+            }
+        }
+      }
+    }
+    if (finish) {
+      const int chunk = b / HB, j = b - chunk * HB;
+      const GroupInfo gi = group_of(m, lb, n_groups, chunk);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        if (cb + n >= ntiles) continue;
-        const int gtile = tile0 + cb + n;
-        if (a.S == 1) {
-          const v4f tot[4] = {acc[0][n], acc[1][n], acc[2][n], acc[3][n]};
-          const int pair = column_pair(a, unit0, nunits, (cb + n) * 16 + (l & 15));
-          hidden_epilogue(a, tot, j, gtile, pair);
-        } else {
-          float* p = a.partials + ((static_cast<int64_t>(gtile) * a.HB + j) * a.S + c) * 1024 + l * 4;
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) st_dev_u32(p + rt * 256 + r, __float_as_uint(acc[rt][n][r]));
-        }
+        const int t = gi.cc * NT + n;
+        if (t >= gi.ntiles) continue;
+        const v4f tot[4] = {acc[0][n], acc[1][n], acc[2][n], acc[3][n]};
+        hidden_epilogue(a, tot, j, gi.tile0 + t, column_pair(m, lb, gi, t * 16 + (l & 15)));
       }
-    }
-    __syncthreads();
-  }
-
-  if (w != 0) return;
-  if (a.S > 1) {
-    wait_stores();
-    uint32_t old = 0;
-    if (l == 0)
-      old = __hip_atomic_fetch_add(a.arrive + g * kHBMax + j, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != static_cast<uint32_t>(a.S - 1)) return;   // another split finishes the block
-    compiler_fence();
-    if (l == 0) st_dev_u32(a.arrive + g * kHBMax + j, 0u);  // re-arm for the next call
-    for (int t = 0; t < ntiles; ++t) {
-      const int gtile = tile0 + t;
-      v4f tot[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) tot[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-      for (int cc = 0; cc < a.S; ++cc) {
-        const float* p = a.partials + ((static_cast<int64_t>(gtile) * a.HB + j) * a.S + cc) * 1024 + l * 4;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const uint64_t lo = ld_dev_u64(p + rt * 256), hi = ld_dev_u64(p + rt * 256 + 2);
-          tot[rt][0] += __uint_as_float(static_cast<uint32_t>(lo));
-          tot[rt][1] += __uint_as_float(static_cast<uint32_t>(lo >> 32));
-          tot[rt][2] += __uint_as_float(static_cast<uint32_t>(hi));
-          tot[rt][3] += __uint_as_float(static_cast<uint32_t>(hi >> 32));
-        }
-      }
-      const int pair = column_pair(a, unit0, nunits, t * 16 + (l & 15));
-      hidden_epilogue(a, tot, j, gtile, pair);
+      // Publish: the block's codes and scales are stored (sc1) before its flag.
+      wait_stores();
+      if (l == 0) st_dev_u32(a.flags + b, gen + 1);
     }
   }
-  // Publish: the hidden block's codes and scale are stored (sc1) before the count.
-  wait_stores();
-  if (l == 0) __hip_atomic_fetch_add(a.ready + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wg_barrier();
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[rt][n] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
-// FC2 work item: 256 output rows (16 tiles; wave w takes tiles w, w+4, w+8, w+12) of
-// one expert for all its tokens.  The weight loads are issued before waiting for the
-// expert's hidden, so the wait overlaps the stream.  Output: BF16 rows
-// out[pair, d] (experts page, ExpertsKernel.fc2: rows of the unit's pair indices).
-template <int NT>
-__device__ void fc2_item(const ExpArgs& a, int item) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int RB = a.D / kFC2Rows;
-  const int g = item / RB, rb = item - g * RB;
-  const int e = a.tbl.g_expert[g], unit0 = a.tbl.g_unit0[g], nunits = a.tbl.g_nunits[g];
-  const int tile0 = a.tbl.g_tile0[g];
-  const int ntiles = (nunits + 1) >> 1;
-  const int tiles_per_expert = a.D / 16;
-  uint4 A[4][4];
-  uint32_t SA[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rt2 = rb * 16 + w + 4 * i;
-    const int64_t tile = static_cast<int64_t>(e) * tiles_per_expert + rt2;
-    const uint8_t* base = a.w2p + tile * a.NS2 * 1024 + l * 16;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) A[i][s] = ld16(base + (s < a.NS2 ? s : a.NS2 - 1) * 1024);
-    SA[i] = ld4(a.s2p + tile * 256 + l * 4);
-  }
-  // Wait until every hidden block of this expert is published (FC1 items of the
-  // expert were claimed before this item, so they are running or done).
-  // The wait is bounded (seconds) so that a broken invariant can never hang the GPU:
-  // it then flags the table header (bit 2) and computes with whatever is there.
-  for (uint32_t spins = 0; ld_dev_u32(a.ready + g) < static_cast<uint32_t>(a.HB); ++spins) {
+// Wait until the HB hidden blocks of a chunk carry this call's tag.  Bounded (seconds)
+// so that a broken invariant can never hang the GPU: it then flags the unit table
+// header (bit 2) and goes on with whatever is there.
+__device__ __forceinline__ void wait_chunk(const ExpArgs& a, int chunk, uint32_t gen) {
+  const int l = threadIdx.x & 63;
+  const uint32_t want = gen + 1;
+  const uint32_t* f = a.flags + static_cast<int64_t>(chunk) * a.HB;
+  for (uint32_t spins = 0;; ++spins) {
+    const uint32_t v = l < a.HB ? ld_dev_u32(f + l) : want;
+    if (__all(v == want)) break;
     if (spins == kSpinLimit) {
-      __hip_atomic_fetch_or(a.tbl.hdr + 3, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (l == 0) __hip_atomic_fetch_or(a.tbl.hdr + 3, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
   }
   compiler_fence();
+}
 
-  for (int cb = 0; cb < ntiles; cb += NT) {
-    uint4 BL[NT][4], BH[NT][4];
-    uint32_t SB[NT][4];
-    bool live[NT];
+// FC2 B operand (the hidden of a chunk's NT column tiles, all NS2 K steps).
+template <int NT, int NS2>
+struct Fc2Hidden {
+  uint4 BL[NT][NS2], BH[NT][NS2];
+  uint32_t SB[NT][NS2];
+  int chunk;
+  GroupInfo gi;
+};
+
+template <int NT, int NS2>
+__device__ __forceinline__ void load_hidden(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups, int chunk, uint32_t gen,
+                            Fc2Hidden<NT, NS2>& hd) {
+  const int l = threadIdx.x & 63, grp = l >> 4;
+  hd.chunk = chunk;
+  hd.gi = group_of(m, lb, n_groups, chunk);
+  wait_chunk(a, chunk, gen);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      live[n] = cb + n < ntiles;
-      const int gcol = (tile0 + (live[n] ? cb + n : 0)) * 16 + (l & 15);
-      const uint8_t* hc = a.hcodes + static_cast<int64_t>(gcol) * a.IP + 16 * (l >> 4);
+  for (int n = 0; n < NT; ++n) {
+    const int t = hd.gi.cc * NT + n;
+    const int gcol = (hd.gi.tile0 + (t < hd.gi.ntiles ? t : 0)) * 16 + (l & 15);
+    const uint8_t* hc = a.hcodes + static_cast<int64_t>(gcol) * a.IP + 16 * grp;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int ss = s < a.NS2 ? s : a.NS2 - 1;
-        const uint64_t l0 = ld_dev_u64(hc + ss * 128), l1 = ld_dev_u64(hc + ss * 128 + 8);
-        const uint64_t h0 = ld_dev_u64(hc + ss * 128 + 64), h1 = ld_dev_u64(hc + ss * 128 + 72);
-        BL[n][s] = make_uint4(static_cast<uint32_t>(l0), static_cast<uint32_t>(l0 >> 32),
-                              static_cast<uint32_t>(l1), static_cast<uint32_t>(l1 >> 32));
-        BH[n][s] = make_uint4(static_cast<uint32_t>(h0), static_cast<uint32_t>(h0 >> 32),
-                              static_cast<uint32_t>(h1), static_cast<uint32_t>(h1 >> 32));
-        SB[n][s] = ld_dev_u32(a.hscales + static_cast<int64_t>(gcol) * (a.IP / 32) + 4 * ss);
-      }
-    }
-    v4f acc[4][NT];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[i][n] = v4f{0.f, 0.f, 0.f, 0.f};
-    const int grp = l >> 4;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < a.NS2) {
-        // K-blocks beyond I (I not a multiple of 128) are zero.
-        const bool lo_ok = 4 * s + (grp >> 1) < a.HB, hi_ok = 4 * s + 2 + (grp >> 1) < a.HB;
-        const bool sc_ok = 4 * s + grp < a.HB;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const uint4 z = make_uint4(0, 0, 0, 0);
-          const v8i b = fp8_operand(live[n] && lo_ok ? BL[n][s] : z, live[n] && hi_ok ? BH[n][s] : z);
-          const int sb = live[n] && sc_ok ? static_cast<int>((SB[n][s] >> (8 * grp)) & 0xffu) : 127;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int sa = static_cast<int>((SA[i] >> (8 * s)) & 0xffu);
-            acc[i][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(A[i][s]), b, acc[i][n],
-                                                                          4, 0, 0, sa, 0, sb);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      if (!live[n]) continue;
-      const int pair = column_pair(a, unit0, nunits, (cb + n) * 16 + (l & 15));
-      if (pair < 0) continue;
-      uint16_t* orow = a.out + static_cast<int64_t>(pair) * a.D;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = (rb * 16 + w + 4 * i) * 16 + 4 * grp;
-        const uint2 v = make_uint2(to_bf16_bits(acc[i][n][0]) | (to_bf16_bits(acc[i][n][1]) << 16),
-                                   to_bf16_bits(acc[i][n][2]) | (to_bf16_bits(acc[i][n][3]) << 16));
-        *reinterpret_cast<uint2*>(orow + d) = v;
-      }
+    for (int s = 0; s < NS2; ++s) {
+      const uint64_t l0 = ld_dev_u64(hc + s * 128), l1 = ld_dev_u64(hc + s * 128 + 8);
+      const uint64_t h0 = ld_dev_u64(hc + s * 128 + 64), h1 = ld_dev_u64(hc + s * 128 + 72);
+      hd.BL[n][s] = make_uint4(static_cast<uint32_t>(l0), static_cast<uint32_t>(l0 >> 32), static_cast<uint32_t>(l1),
+                               static_cast<uint32_t>(l1 >> 32));
+      hd.BH[n][s] = make_uint4(static_cast<uint32_t>(h0), static_cast<uint32_t>(h0 >> 32), static_cast<uint32_t>(h1),
+                               static_cast<uint32_t>(h1 >> 32));
+      hd.SB[n][s] = ld_dev_u32(a.hscales + static_cast<int64_t>(gcol) * (a.IP / 32) + 4 * s);
     }
   }
 }
 
 // The persistent routed-experts kernel (experts page, ExpertsKernel; runtime page,
-// PersistentExperts.run).  Items [0, G*HB*S) are FC1 splits, [G*HB*S, +G*D/256) FC2
-// row blocks, claimed in order.  The last workgroup to leave re-arms the counters.
-template <int NT, int QMAX>
+// PersistentExperts.run): one workgroup per CU, co-resident (FC2 units wait for hidden
+// blocks that other workgroups' FC1 slices produce).  Each wave streams its items --
+// FC1(A), FC1(B), FC2(A), FC2(B) -- through a private LDS ring R items deep.
+template <int NT, int NS2>
 __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
-  __shared__ float red[3 * 4 * NT * 64 * 4];
-  __shared__ int s_item, s_last;
+  using G = Geo<NT>;
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, grp = l >> 4;
+  const LdsMap m = lds_map<NT>(static_cast<uint32_t>(a.g_cap), static_cast<uint32_t>(a.u_cap));
+  const uint32_t lb = lds_base();
   const int n_groups = a.tbl.hdr[1];
-  const int n_fc1 = n_groups * a.HB * a.S;
-  const int total = n_fc1 + n_groups * (a.D / kFC2Rows);
-  for (;;) {
-    if (threadIdx.x == 0)
-      s_item = static_cast<int>(__hip_atomic_fetch_add(a.ctrl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    __syncthreads();
-    const int item = s_item;
-    __syncthreads();
-    if (item >= total) break;
-    if (item < n_fc1)
-      fc1_item<NT, QMAX>(a, item, red);
-    else
-      fc2_item<NT>(a, item - n_fc1);
-  }
-  if (threadIdx.x == 0) {
-    wait_stores();
-    const uint32_t done = __hip_atomic_fetch_add(a.ctrl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = done == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (s_last) {
-    for (int i = threadIdx.x; i < n_groups; i += kWG) st_dev_u32(a.ready + i, 0u);
-    if (threadIdx.x == 0) {
-      st_dev_u32(a.ctrl, 0u);
-      st_dev_u32(a.ctrl + 1, 0u);
+  const int n_units = a.tbl.hdr[0];
+  const uint32_t gen = a.calls[blockIdx.x];
+  const int n_chunks = load_groups<NT>(a, m, n_groups, n_units);
+
+  v4f acc[4][NT];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[rt][n] = v4f{0.f, 0.f, 0.f, 0.f};
+  // FC1 blocks are finished by the whole workgroup in order: half A's slice, then B's
+  int fin_h = 0;
+  Slice fin = make_slice(a, n_chunks, 0);
+  int fin_b = fin.lo / a.NS1, fin_last = fin.hi > fin.lo ? (fin.hi - 1) / a.NS1 : fin_b - 1;
+
+  Cursor pc;  // issue cursor, R-1 items ahead of consumption
+  pc.h = -1;
+  pc.s = pc.s_hi = 0;
+  pc.b = pc.hi = 0;
+  cursor_next(a, m, lb, n_groups, n_chunks, pc);
+  Fc2Hidden<NT, NS2> hd;
+  hd.chunk = -1;
+  int n_real = 0;  // real items issued (they precede the dummies)
+  for (int k = 0;; ++k) {
+    issue_item<NT, NS2>(a, m, lb, pc, k);
+    if (pc.h < 4) {
+      ++n_real;
+      cursor_next(a, m, lb, n_groups, n_chunks, pc);
+    }
+    const int kc = k - (G::R - 1);  // the item consumed now
+    if (kc < 0) continue;
+    const bool real = kc < n_real;
+    uint4 meta = make_uint4(3u, 0u, 0u, 0u);
+    const int slot = kc % G::R;
+    const uint32_t sa_ = lb + m.ring + (w * G::R + slot) * G::SLOT;
+    if (real) {
+      wait_vm<G::VM>();
+      meta = lds_ld16(lb + m.meta + (w * G::R + slot) * 16);
+    }
+    const int type = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.x));
+    // finish the workgroup's FC1 blocks before this item's block (all for FC2 / the end)
+    const int upto = type == 0 ? __builtin_amdgcn_readfirstlane(static_cast<int>(meta.y)) : 0x7fffffff;
+    while (fin_h < 2) {
+      if (fin_b <= fin_last) {
+        if (fin.base + fin_b >= upto) break;
+        fc1_finish<NT>(a, m, lb, n_groups, fin, fin_h, fin_b, acc, gen);
+        ++fin_b;
+      } else if (++fin_h < 2) {
+        fin = make_slice(a, n_chunks, 1);
+        fin_b = fin.lo / a.NS1;
+        fin_last = fin.hi > fin.lo ? (fin.hi - 1) / a.NS1 : fin_b - 1;
+      }
+    }
+    if (!real) break;
+    if (type == 0) {
+      const int s = static_cast<int>(meta.z);
+      const uint32_t live = meta.w;
+      uint4 av[4];
+      uint32_t saw[4];
+      lds_ld16x4<0, 1024>(sa_ + l * 16, av[0], av[1], av[2], av[3]);
+      lds_ld4x4<4096, 256>(sa_ + l * 4, saw[0], saw[1], saw[2], saw[3]);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const bool lv = (live >> n) & 1u;
+        uint4 bl, bh;
+        uint32_t sbw;
+        if (n == 0)
+          lds_ld_b<5120, 6144, 5120 + NT * 2048>(sa_ + l * 16, sa_ + l * 4, bl, bh, sbw);
+        else
+          lds_ld_b<7168, 8192, 5120 + NT * 2048 + 256>(sa_ + l * 16, sa_ + l * 4, bl, bh, sbw);
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        const v8i bop = fp8_operand(lv ? bl : z, lv ? bh : z);
+        const int sb = lv ? static_cast<int>((sbw >> (8 * grp)) & 0xffu) : 127;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int sa = static_cast<int>((saw[rt] >> (8 * (s & 3))) & 0xffu);
+          acc[rt][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(av[rt]), bop, acc[rt][n], 4, 0, 0,
+                                                                        sa, 0, sb);
+        }
+      }
+    } else if (type == 1) {
+      const int chunk = static_cast<int>(meta.y), rt2 = static_cast<int>(meta.z);
+      if (chunk != hd.chunk) load_hidden<NT, NS2>(a, m, lb, n_groups, chunk, gen, hd);
+      const uint32_t saw = lds_ld4(sa_ + 4096 + l * 4);
+      v4f o[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS2; ++s) {
+        // K-blocks beyond I (I not a multiple of 128) are zero.
+        const bool lo_ok = 4 * s + (grp >> 1) < a.HB, hi_ok = 4 * s + 2 + (grp >> 1) < a.HB;
+        const bool sc_ok = 4 * s + grp < a.HB;
+        const int sa = static_cast<int>((saw >> (8 * s)) & 0xffu);
+        const uint4 av = lds_ld16(sa_ + s * 1024 + l * 16);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          if (hd.gi.cc * NT + n >= hd.gi.ntiles) continue;
+          const uint4 z = make_uint4(0, 0, 0, 0);
+          const v8i bop = fp8_operand(lo_ok ? hd.BL[n][s] : z, hi_ok ? hd.BH[n][s] : z);
+          const int sb = sc_ok ? static_cast<int>((hd.SB[n][s] >> (8 * grp)) & 0xffu) : 127;
+          o[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(av), bop, o[n], 4, 0, 0, sa, 0, sb);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int t = hd.gi.cc * NT + n;
+        if (t >= hd.gi.ntiles) continue;
+        const int pair = column_pair(m, lb, hd.gi, t * 16 + (l & 15));
+        if (pair < 0) continue;
+        const int d = rt2 * 16 + 4 * grp;
+        const uint2 v = make_uint2(to_bf16_bits(o[n][0]) | (to_bf16_bits(o[n][1]) << 16),
+                                   to_bf16_bits(o[n][2]) | (to_bf16_bits(o[n][3]) << 16));
+        *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(pair) * a.D + d) = v;
+      }
     }
   }
+  // drain the dummy items before the workgroup ends
+  wait_vm<0>();
+  if (threadIdx.x == 0)
+    for (int q = blockIdx.x; q < kMaxGrid; q += gridDim.x) a.calls[q] = gen + 1;
 }
 
 using ExpertsFn = void (*)(ExpArgs);
 
-// Kernel variants: NT column tiles per weight pass x QMAX K-step groups held in
-// registers per wave (QMAX is capped so the preloaded operands stay in registers).
-ExpertsFn pick_kernel(int nt, int qmax) {
-  if (nt == 1) {
-    if (qmax == 1) return experts_kernel<1, 1>;
-    if (qmax == 2) return experts_kernel<1, 2>;
-    if (qmax == 4) return experts_kernel<1, 4>;
-    return experts_kernel<1, 8>;
-  }
-  if (nt == 2) {
-    if (qmax == 1) return experts_kernel<2, 1>;
-    if (qmax == 2) return experts_kernel<2, 2>;
-    return experts_kernel<2, 4>;
-  }
-  if (qmax == 1) return experts_kernel<4, 1>;
-  return experts_kernel<4, 2>;
+template <int NT>
+ExpertsFn pick_ns2(int ns2) {
+  if (ns2 == 1) return experts_kernel<NT, 1>;
+  if (ns2 == 2) return experts_kernel<NT, 2>;
+  if (ns2 == 3) return experts_kernel<NT, 3>;
+  return experts_kernel<NT, 4>;
 }
+
+// Kernel variants: NT column tiles per weight pass x NS2 = ceil(I/128) FC2 K steps.
+ExpertsFn pick_kernel(int nt, int ns2) { return nt == 1 ? pick_ns2<1>(ns2) : pick_ns2<2>(ns2); }
 
 // ------------------------------------------------------------------ host helpers
 bool shape_ok(int64_t E, int64_t D, int64_t I) {
-  return E >= 1 && E <= 1024 && D >= 512 && D <= 16384 && D % 512 == 0 && I >= 32 && I <= 512 && I % 32 == 0;
+  return E >= 1 && E <= kMaxGroups && D >= 512 && D <= 16384 && D % 512 == 0 && I >= 32 && I <= 512 &&
+         I % 32 == 0;
 }
 
 int device_cus() {
@@ -773,14 +1201,44 @@ int device_cus() {
   return cached[dev];
 }
 
-// Column tiles per weight pass: an expert never has more tokens than the batch.
-int auto_col_tiles(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
-int qmax_cap(int nt) { return nt == 1 ? 8 : (nt == 2 ? 4 : 2); }
-int max_ksplit(int B, int K, int NQ1) {
-  const int cap = static_cast<int64_t>(B) * K <= 256 ? 8 : 2;
-  return NQ1 < cap ? NQ1 : cap;
+int device_lds_limit() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
+    cached[dev] = v;
+  }
+  return cached[dev];
 }
-int pow2_at_least(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+
+// Allow the kernel variant its dynamic LDS (once per variant and size).
+bool prepare_kernel(ExpertsFn fn, size_t lds) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(lds)) == hipSuccess;
+}
+
+// Workgroups of one kernel variant that the device holds at once.
+int resident_grid(ExpertsFn fn, size_t lds) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kWG, lds) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int grid = per_cu * device_cus();
+  return grid < kMaxGrid ? grid : kMaxGrid;
+}
+
+// The largest batch a workspace of ws_bytes serves (its layout is a function of it).
+int ws_batch_capacity(int E, int D, int I, int K, size_t ws_bytes) {
+  int lo = 0, hi = 65536 / K;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (ws_layout(E, D, I, K, mid).end <= ws_bytes) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -806,16 +1264,15 @@ size_t moe_plan_bytes(int32_t B, int32_t D) {
   return static_cast<size_t>(B) * D + static_cast<size_t>(B) * (D / 32);
 }
 
+size_t moe_units_bytes(int32_t B, int32_t topk, int32_t E) {
+  if (B < 1 || topk < 1 || topk > 64 || E < 1 || E > kMaxGroups || static_cast<int64_t>(B) * topk > 65536) return 0;
+  return units_layout(B, topk, E).end;
+}
+
 size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32_t topk) {
   if (!shape_ok(E, D, I) || B_max < 1 || topk < 1 || topk > 64 || static_cast<int64_t>(B_max) * topk > 65536)
     return 0;
-  const int NQ1 = D / 512;
-  size_t best = 0;
-  for (int b = 1; b <= B_max; ++b) {
-    const size_t end = make_layout(E, b, topk, I, max_ksplit(b, topk, NQ1)).end;
-    if (end > best) best = end;
-  }
-  return best;
+  return ws_layout(E, D, I, topk, B_max).end;
 }
 
 int moe_packed_weight_bytes(int32_t E, int32_t D, int32_t I, size_t* w13_bytes, size_t* s13_bytes,
@@ -864,29 +1321,30 @@ int moe_plan(const void* x, int32_t B, int32_t D, void* plan, size_t plan_bytes,
   return launch_status();
 }
 
-int moe_group(const int32_t* ids, int32_t B, int32_t topk, int32_t E, void* ws, size_t ws_bytes, void* stream) {
-  if (!ids || !ws || B < 1 || topk < 1 || topk > 64 || E < 1 || E > 1024 ||
+int moe_group(const int32_t* ids, int32_t B, int32_t topk, int32_t E, void* units, size_t units_bytes,
+              void* stream) {
+  if (!ids || !units || B < 1 || topk < 1 || topk > 64 || E < 1 || E > kMaxGroups ||
       static_cast<int64_t>(B) * topk > 65536)
     return MOE_EINVAL;
   const int W = (B + 31) / 32;
   const size_t lds = (static_cast<size_t>(E) * W + 2 * static_cast<size_t>(E)) * 4;
   if (lds > 60 * 1024) return MOE_EINVAL;
-  const Layout L = make_layout(E, B, topk, 0, 1);
-  if (ws_bytes < L.end) return MOE_ENOSPACE;
-  const Table t = table_at(static_cast<uint8_t*>(ws), L);
+  const UnitsLayout L = units_layout(B, topk, E);
+  if (units_bytes < L.end) return MOE_ENOSPACE;
+  const Table t = table_at(static_cast<uint8_t*>(units), L);
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds, as_stream(stream), ids, B, topk, E, W, t);
   return launch_status();
 }
 
-int moe_units_export(const void* ws, size_t ws_bytes, int32_t B, int32_t topk, int32_t E, void* header,
+int moe_units_export(const void* units, size_t units_bytes, int32_t B, int32_t topk, int32_t E, void* header,
                      void* unit_expert, void* unit_rows, int32_t max_units, void* stream) {
-  if (!ws || !header || !unit_expert || !unit_rows || B < 1 || topk < 1 || E < 1 || max_units < 0)
+  if (!units || !header || !unit_expert || !unit_rows || B < 1 || topk < 1 || E < 1 || max_units < 0)
     return MOE_EINVAL;
-  const Layout L = make_layout(E, B, topk, 0, 1);
-  if (ws_bytes < L.end) return MOE_ENOSPACE;
+  const UnitsLayout L = units_layout(B, topk, E);
+  if (units_bytes < L.end) return MOE_ENOSPACE;
   const int64_t U = static_cast<int64_t>(B) * topk;
   const int64_t n = max_units < U ? max_units : U;
-  const uint8_t* base = static_cast<const uint8_t*>(ws);
+  const uint8_t* base = static_cast<const uint8_t*>(units);
   hipStream_t st = as_stream(stream);
   if (hipMemcpyAsync(header, base + L.hdr, 16, hipMemcpyDeviceToDevice, st) != hipSuccess) return MOE_EHIP;
   if (n > 0) {
@@ -898,38 +1356,40 @@ int moe_units_export(const void* ws, size_t ws_bytes, int32_t B, int32_t topk, i
   return MOE_OK;
 }
 
-int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* plan, int32_t B,
-                    int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
-  if (!wts || !plan || !ws || !out || B < 1 || topk < 1 || topk > 64 || static_cast<int64_t>(B) * topk > 65536)
+int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* plan, const void* units,
+                    size_t units_bytes, int32_t B, int32_t topk, void* ws, size_t ws_bytes, void* out,
+                    size_t out_bytes, void* stream) {
+  if (!wts || !plan || !units || !ws || !out || B < 1 || topk < 1 || topk > 64 ||
+      static_cast<int64_t>(B) * topk > 65535)  // pair indices are cached as u16, 0xffff = padding
     return MOE_EINVAL;
   const int E = wts->E, D = wts->D, I = wts->I;
   if (!shape_ok(E, D, I) || !wts->w13 || !wts->s13 || !wts->w2 || !wts->s2) return MOE_EINVAL;
   moe_run_opts_t o;
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
-  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.ksplit < 0 || o.grid < 0 || o.col_tiles < 0 ||
-      (o.fc2_rows != 0 && o.fc2_rows != kFC2Rows) ||
-      (o.col_tiles != 0 && o.col_tiles != 1 && o.col_tiles != 2 && o.col_tiles != 4) ||
+  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || o.col_tiles < 0 ||
+      (o.col_tiles != 0 && o.col_tiles != 1 && o.col_tiles != 2) ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
     return MOE_EINVAL;
   if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
-  if (ws_bytes < make_layout(E, B, topk, I, 1).end) return MOE_ENOSPACE;  // before touching the device
-
-  const int HB = I / 32, NS1 = D / 128, NQ1 = (NS1 + 3) / 4, NS2 = (I + 127) / 128;
-  const int cus = device_cus();
+  const UnitsLayout UL = units_layout(B, topk, E);
+  if (units_bytes < UL.end) return MOE_ENOSPACE;
+  const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
+  if (B_cap < B) return MOE_ENOSPACE;
+  const WsLayout L = ws_layout(E, D, I, topk, B_cap);
   const int nt = o.col_tiles ? o.col_tiles : auto_col_tiles(B);
-  const int kmax = max_ksplit(B, topk, NQ1);
-  int S = o.ksplit;
-  if (S == 0) {
-    const int64_t groups = static_cast<int64_t>(B) * topk < E ? static_cast<int64_t>(B) * topk : E;
-    const int64_t want = (3 * static_cast<int64_t>(cus) + groups * HB - 1) / (groups * HB);
-    S = static_cast<int>(want < 1 ? 1 : (want > kmax ? kmax : want));
-  }
-  if (S > kmax) return MOE_ENOSPACE;  // the workspace holds partial sums for up to kmax splits
-  int qmax = pow2_at_least((NQ1 + S - 1) / S);  // K-step groups per item, held in chunks of
-  if (qmax > qmax_cap(nt)) qmax = qmax_cap(nt);   // at most qmax_cap (register budget)
-  const Layout L = make_layout(E, B, topk, I, S);
-  if (ws_bytes < L.end) return MOE_ENOSPACE;
+  if (nt > L.nt_cap) return MOE_ENOSPACE;  // the partial-sum slots are sized for nt_cap tiles
+  const int64_t U = static_cast<int64_t>(B) * topk;
+  const int g_cap = static_cast<int>(U < E ? U : E);
+  const int64_t u_bound = g_cap + (U + 7) / 8;
+  const int u_cap = static_cast<int>(U < u_bound ? U : u_bound);
+  const size_t lds = nt == 1 ? lds_bytes<1>(g_cap, u_cap) : lds_bytes<2>(g_cap, u_cap);
+  if (lds > static_cast<size_t>(device_lds_limit())) return MOE_EINVAL;  // unit table too large for LDS
+  const ExpertsFn fn = pick_kernel(nt, (I + 127) / 128);
+  if (!prepare_kernel(fn, lds)) return MOE_EHIP;
+  const int cap = resident_grid(fn, lds);
+  if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
+  const int grid = o.grid ? o.grid : cap;
 
   uint8_t* base = static_cast<uint8_t*>(ws);
   ExpArgs a;
@@ -939,10 +1399,10 @@ int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const 
   a.s2p = static_cast<const uint8_t*>(wts->s2);
   a.xcodes = static_cast<const uint8_t*>(plan);
   a.xscales = a.xcodes + static_cast<int64_t>(B) * D;
-  a.ctrl = reinterpret_cast<uint32_t*>(base);
-  a.ready = reinterpret_cast<uint32_t*>(base + L.ready);
+  a.tbl = table_at(static_cast<uint8_t*>(const_cast<void*>(units)), UL);
+  a.calls = reinterpret_cast<uint32_t*>(base + L.calls);
   a.arrive = reinterpret_cast<uint32_t*>(base + L.arrive);
-  a.tbl = table_at(base, L);
+  a.flags = reinterpret_cast<uint32_t*>(base + L.flags);
   a.hcodes = base + L.hcodes;
   a.hscales = base + L.hscales;
   a.partials = reinterpret_cast<float*>(base + L.partials);
@@ -951,16 +1411,15 @@ int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const 
   a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
   a.D = D;
   a.I = I;
-  a.HB = HB;
-  a.NS1 = NS1;
-  a.NQ1 = NQ1;
-  a.NS2 = NS2;
-  a.IP = NS2 * 128;
+  a.HB = I / 32;
+  a.NS1 = D / 128;
+  a.NQ1 = (a.NS1 + 3) / 4;
+  a.IP = (I + 127) / 128 * 128;
+  a.g_cap = g_cap;
+  a.u_cap = u_cap;
   a.K = topk;
-  a.S = S;
   a.floor_rule = o.hidden_rule == 2 || (o.hidden_rule == 0 && I == 384);
-  const int grid = o.grid ? o.grid : 2 * cus;
-  hipLaunchKernelGGL(pick_kernel(nt, qmax), dim3(grid), dim3(kWG), 0, as_stream(stream), a);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kWG), lds, as_stream(stream), a);
   return launch_status();
 }
 

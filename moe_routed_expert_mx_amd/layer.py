@@ -39,6 +39,8 @@ class MoeLayer:
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=self.device)
         _lib.moe_workspace_init(self.ws)
         self.plan = torch.empty(_lib.moe_plan_bytes(self.B_max, self.D), dtype=torch.uint8, device=self.device)
+        self.units = torch.empty(_lib.moe_units_bytes(self.B_max, self.topk, self.E), dtype=torch.uint8,
+                                 device=self.device)
 
     def out_buffer(self, B: int) -> torch.Tensor:
         return torch.empty(B * self.topk, self.D, dtype=torch.bfloat16, device=self.device)
@@ -52,17 +54,23 @@ class MoeLayer:
         if out is None:
             out = self.out_buffer(B)
         _lib.moe_plan(x, self.plan, stream=stream)
-        _lib.moe_group(ids, self.E, self.ws, stream=stream)
-        _lib.moe_experts_run(self.structs[replica], self.plan, B, self.topk, self.ws, out, stream=stream, **opts)
+        _lib.moe_group(ids, self.E, self.units, stream=stream)
+        _lib.moe_experts_run(self.structs[replica], self.plan, self.units, B, self.topk, self.ws, out, stream=stream,
+                             **opts)
         return out
 
-    def units(self, B: int):
+    def experts(self, B: int, out: torch.Tensor, *, replica: int = 0, stream=None, **opts):
+        """The experts kernel alone, on the plan and unit table of the last forward()."""
+        _lib.moe_experts_run(self.structs[replica], self.plan, self.units, B, self.topk, self.ws, out, stream=stream,
+                             **opts)
+
+    def unit_table(self, B: int):
         """The unit table moe_group left in the workspace: (header[4], unit_expert, unit_rows)."""
         U = B * self.topk
         hdr = torch.empty(4, dtype=torch.int32, device=self.device)
         ue = torch.empty(U, dtype=torch.int32, device=self.device)
         ur = torch.empty(U, 8, dtype=torch.int32, device=self.device)
-        _lib.moe_units_export(self.ws, B, self.topk, self.E, hdr, ue, ur)
+        _lib.moe_units_export(self.units, B, self.topk, self.E, hdr, ue, ur)
         h = hdr.cpu().numpy()
         n = int(h[0])
         return h, ue[:n].cpu().numpy(), ur[:n].cpu().numpy()

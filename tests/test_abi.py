@@ -62,19 +62,29 @@ def test_host_side_argument_errors(m):
     assert L.moe_plan(fake, 2, 512, fake, 100, None) == m._lib.MOE_ENOSPACE
     assert L.moe_group(fake, 1, 0, 16, fake, 10**6, None) == m._lib.MOE_EINVAL
     assert L.moe_group(fake, 1, 4, 16, fake, 10, None) == m._lib.MOE_ENOSPACE
+    assert m.moe_units_bytes(1, 4, 16) > 0 and m.moe_units_bytes(0, 4, 16) == 0
     w = m.moe_weights_t(16, 512, 128, 0x1000, 0x1000, 0x1000, 0x1000)
     o = m.moe_run_opts_t()
-    args = lambda B, K, ws, out: (ctypes.byref(w), ctypes.byref(o), fake, B, K, fake, ws, fake, out, None)
-    assert L.moe_experts_run(*args(1, 4, 10**8, 16)) == m._lib.MOE_ENOSPACE         # output too small
-    assert L.moe_experts_run(*args(1, 4, 100, 4 * 512 * 2)) == m._lib.MOE_ENOSPACE  # workspace too small
-    assert L.moe_experts_run(*args(0, 4, 10**8, 10**8)) == m._lib.MOE_EINVAL
-    o.col_tiles = 3
-    assert L.moe_experts_run(*args(1, 4, 10**8, 10**8)) == m._lib.MOE_EINVAL
-    o.col_tiles = 0
-    o.hidden_rule = 5
-    assert L.moe_experts_run(*args(1, 4, 10**8, 10**8)) == m._lib.MOE_EINVAL
+    big = 10**9
+
+    def run(B, K, units, ws, out, opts=o, wts=w):
+        return L.moe_experts_run(ctypes.byref(wts), ctypes.byref(opts), fake, fake, units, B, K, fake, ws, fake, out,
+                                 None)
+
+    assert run(1, 4, big, big, 16) == m._lib.MOE_ENOSPACE              # output too small
+    assert run(1, 4, big, 100, big) == m._lib.MOE_ENOSPACE             # workspace too small
+    assert run(1, 4, 10, big, big) == m._lib.MOE_ENOSPACE              # unit table too small
+    assert run(0, 4, big, big, big) == m._lib.MOE_EINVAL
+    o.col_tiles = 4
+    assert run(1, 4, big, big, big) == m._lib.MOE_EINVAL
+    o.col_tiles, o.hidden_rule = 0, 5
+    assert run(1, 4, big, big, big) == m._lib.MOE_EINVAL
+    o.hidden_rule = 0
+    o.col_tiles = 2     # a workspace sized for one token holds partial sums for one tile only
+    ws1 = m.moe_workspace_bytes(16, 512, 128, 1, 4)
+    assert run(1, 4, big, ws1, big) == m._lib.MOE_ENOSPACE
     bad = m.moe_weights_t(16, 512, 100, 0x1000, 0x1000, 0x1000, 0x1000)
-    assert L.moe_experts_run(ctypes.byref(bad), None, fake, 1, 4, fake, 10**8, fake, 10**8, None) == m._lib.MOE_EINVAL
+    assert run(1, 4, big, big, big, m.moe_run_opts_t(), bad) == m._lib.MOE_EINVAL
     assert L.moe_pack_weights(16, 512, 128, None, fake, fake, fake, fake, fake, fake, fake, None) == m._lib.MOE_EINVAL
     assert L.moe_workspace_init(None, 1024, None) == m._lib.MOE_EINVAL
 

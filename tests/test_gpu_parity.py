@@ -142,7 +142,7 @@ def test_plan_special_values(lib):
 def _units_case(lib, ids, E):
     m, _ = lib
     B, K = ids.shape
-    ws = torch.zeros(m.moe_workspace_bytes(E, 512, 64, B, K), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(m.moe_units_bytes(B, K, E), dtype=torch.uint8, device=DEV)
     idd = torch.from_numpy(ids).to(DEV)
     m.moe_group(idd, E, ws)
     hdr = torch.empty(4, dtype=torch.int32, device=DEV)
@@ -210,19 +210,22 @@ SMALL = [
 ]
 
 
+# (col_tiles, grid): the default; one tile per weight pass with a small grid (long
+# slices: whole hidden blocks in one workgroup); multi-tile passes; grids that split
+# hidden blocks over many workgroups (last-arriver reductions).
+VARIANTS = [(0, 0), (1, 7), (2, 0), (2, 200), (1, 200), (2, 1)]
+
+
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-@pytest.mark.parametrize("col_tiles,ksplit", [(0, 0), (1, 1), (2, 2), (4, 1), (1, 0)])
-def test_experts_small_shapes(lib, case, col_tiles, ksplit):
+@pytest.mark.parametrize("col_tiles,grid", VARIANTS)
+def test_experts_small_shapes(lib, case, col_tiles, grid):
     name, B, E, K, D, I, routing = case
-    log(f"experts small {name} col_tiles={col_tiles} ksplit={ksplit}")
+    log(f"experts small {name} col_tiles={col_tiles} grid={grid}")
     d = workloads.generate(workloads.custom(name, B=B, E=E, K=K, D=D, I=I, routing=routing, seed=11))
-    layer = _layer(lib, d)
-    NQ1 = D // 512
-    if ksplit > NQ1:
-        pytest.skip("split larger than the K-step groups")
-    got, hc, hs = _run(layer, d, col_tiles=col_tiles, ksplit=ksplit)
+    layer = _layer(lib, d, B_max=max(B, 40))
+    got, hc, hs = _run(layer, d, col_tiles=col_tiles, grid=grid)
     ref = _oracle(d)
-    _check_all(d, got, hc, hs, ref, what=f"{name}/{col_tiles}/{ksplit}")
+    _check_all(d, got, hc, hs, ref, what=f"{name}/{col_tiles}/{grid}")
 
 
 def test_everybody_on_one_expert(lib):
@@ -273,15 +276,16 @@ def test_slot_permutation_permutes_rows(lib):
 
 
 def test_routes_independent_of_batch(lib):
-    """A route's row is the same (bit for bit, at fixed options) whether its token runs
-    alone or inside a batch that shares its expert with other tokens."""
+    """A route's row is the same (bit for bit) whether its token runs alone or inside a
+    batch that shares its expert with other tokens.  One workgroup, so that every hidden
+    block is summed whole in both runs and only the token columns differ."""
     log("route independence")
     d = workloads.generate(workloads.custom("indep", B=12, E=5, K=2, D=1024, I=128, seed=6))
     layer = _layer(lib, d)
-    full, _, _ = _run(layer, d, col_tiles=1, ksplit=1)
+    full, _, _ = _run(layer, d, col_tiles=1, grid=1)
     for t in (0, 5, 11):
         d1 = dict(d)
         d1["x"], d1["ids"] = d["x"][t:t + 1], d["ids"][t:t + 1]
         d1["workload"] = workloads.custom("one", B=1, E=5, K=2, D=1024, I=128)
-        one, _, _ = _run(layer, d1, col_tiles=1, ksplit=1)
+        one, _, _ = _run(layer, d1, col_tiles=1, grid=1)
         assert np.array_equal(one, full[t * 2:(t + 1) * 2])
