@@ -146,8 +146,11 @@ typedef struct {
   int32_t hidden_rule;
   int32_t grid;       /* persistent workgroups, at most the device's resident capacity
                          for the kernel variant (MOE_EINVAL above it); 0 = all of it */
-  int32_t col_tiles;  /* 16-token column tiles per weight pass (1 or 2), 0 = auto */
-  int32_t reserved[5];
+  int32_t col_tiles;  /* 16-token column tiles per weight pass: 0 or 1 (the kernel's only
+                         width; other values are MOE_EINVAL) */
+  int32_t ring;       /* weight items in flight per streaming wave (2..4); 0 = the deepest
+                         that fits in LDS next to the unit table */
+  int32_t reserved[4];
   void* hidden_codes_dev;  /* optional u8 [B*topk, I]: the hidden's e4m3 codes per route */
   void* hidden_scales_dev; /* optional u8 [B*topk, I/32]: its E8M0 scales */
 } moe_run_opts_t;

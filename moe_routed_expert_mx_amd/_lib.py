@@ -30,7 +30,7 @@ class moe_weights_t(ctypes.Structure):
 
 class moe_run_opts_t(ctypes.Structure):
     _fields_ = [("hidden_rule", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("col_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5),
+                ("col_tiles", ctypes.c_int32), ("ring", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4),
                 ("hidden_codes_dev", ctypes.c_void_p), ("hidden_scales_dev", ctypes.c_void_p)]
 
 
@@ -136,8 +136,8 @@ def moe_units_export(units, B, topk, E, header, unit_expert, unit_rows, stream=N
 
 
 def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, out, *, hidden_rule=0, grid=0,
-                    col_tiles=0, hidden_codes=None, hidden_scales=None, stream=None):
-    opts = moe_run_opts_t(hidden_rule, grid, col_tiles, (ctypes.c_int32 * 5)(0, 0, 0, 0, 0),
+                    col_tiles=0, ring=0, hidden_codes=None, hidden_scales=None, stream=None):
+    opts = moe_run_opts_t(hidden_rule, grid, col_tiles, ring, (ctypes.c_int32 * 4)(0, 0, 0, 0),
                           _ptr(hidden_codes), _ptr(hidden_scales))
     _check("moe_experts_run", lib.moe_experts_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(plan),
                                                   _ptr(units), _nbytes(units), B, topk, _ptr(ws), _nbytes(ws),

@@ -29,7 +29,8 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kWG = 256;          // threads per experts workgroup (4 waves)
+constexpr int kStream = 4;        // streaming waves per experts workgroup
+constexpr int kWG = 64 * (kStream + 1);  // plus one control wave
 constexpr int kGroupThreads = 1024;
 constexpr uint32_t kSpinLimit = 1u << 22;  // polls of a flag before giving up
 
@@ -100,6 +101,23 @@ __device__ __forceinline__ v8i fp4_operand(uint4 a) {
   v8i r = {static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z), static_cast<int>(a.w),
            0, 0, 0, 0};
   return r;
+}
+// Block-scaled FP4 (A, 16 rows) x FP8 (B, 16 columns) -> FP32 16x16 tile, K = 128.
+// The destination of this multi-pass MFMA must not share registers with A or B (it is
+// written while they are still read); in its VGPR-destination form the compiler does not
+// enforce that, so kernels that use it declare AGPR use (agpr_form()) and the compiler
+// gives the MFMA accumulation registers of their own.
+__device__ __forceinline__ v4f mfma_fp4_fp8(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, scale_a, 0, scale_b);
+}
+__device__ __forceinline__ void agpr_form() { asm volatile("" : : : "a0"); }
+// Extra wait states before results of the MFMA above are read by ordinary instructions:
+// the compiler's count is short for this FP4 x FP8 K = 128 form (the first result
+// register is ready, the later ones are not).  The accumulators are asm operands, so
+// no read of them can move ahead of the wait.
+__device__ __forceinline__ void mfma_settle(v4f& x) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x)); }
+__device__ __forceinline__ void mfma_settle(v4f& x0, v4f& x1, v4f& x2, v4f& x3) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3));
 }
 __device__ __forceinline__ v8i fp8_operand(uint4 lo, uint4 hi) {
   v8i r = {static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
@@ -302,25 +320,23 @@ __global__ void pack_w13_codes(const uint4* __restrict__ src, uint4* __restrict_
   dst[idx] = src[(static_cast<int64_t>(e) * 2 * I + r) * (D / 32) + kb];
 }
 
-// Packed FC1 scales: per (e, j, group q of four K steps, tile rt, lane l) one word whose
-// byte i is the E8M0 of (row, K-block 4*(4q+i) + l/16).
+// Packed FC1 scales: per (e, j, K step s, lane l) one word whose byte rt is the E8M0 of
+// (row w13_row(rt, l), K-block 4s + l/16): the A scales of one step's four row tiles.
 __global__ void pack_w13_scales(const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, int E, int D,
                                 int I) {
-  const int HB = I / 32, NS = D / 128, NQ = (NS + 3) / 4;
-  const int64_t total = static_cast<int64_t>(E) * HB * NQ * 256;
+  const int HB = I / 32, NS = D / 128;
+  const int64_t total = static_cast<int64_t>(E) * HB * NS * 64;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= total) return;
-  const int l = idx & 63, rt = (idx >> 6) & 3;
-  const int64_t rest = idx >> 8;
-  const int q = rest % NQ;
-  const int j = (rest / NQ) % HB;
-  const int e = rest / (static_cast<int64_t>(NQ) * HB);
-  const int r = w13_row(I, j, rt, l);
+  const int l = idx & 63;
+  const int64_t rest = idx >> 6;
+  const int s = rest % NS;
+  const int j = (rest / NS) % HB;
+  const int e = rest / (static_cast<int64_t>(NS) * HB);
   uint32_t word = 0;
-  for (int i = 0; i < 4; ++i) {
-    const int s = 4 * q + i;
-    const uint32_t b = s < NS ? src[(static_cast<int64_t>(e) * 2 * I + r) * (D / 32) + 4 * s + (l >> 4)] : 127u;
-    word |= b << (8 * i);
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = w13_row(I, j, rt, l);
+    word |= static_cast<uint32_t>(src[(static_cast<int64_t>(e) * 2 * I + r) * (D / 32) + 4 * s + (l >> 4)]) << (8 * rt);
   }
   dst[idx] = word;
 }
@@ -384,8 +400,6 @@ int64_t max_tiles_for(int64_t U, int E) {
   return (U + 15 * G + 15) / 16;
 }
 
-// Column tiles per weight pass: an expert never has more tokens than the batch.
-int auto_col_tiles(int B) { return B <= 16 ? 1 : 2; }
 
 WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   WsLayout L{};
@@ -395,7 +409,7 @@ WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   const int64_t IP = (I + 127) / 128 * 128;
   L.max_tiles = max_tiles_for(U, E);
   L.max_blocks = L.max_tiles * HB;
-  L.nt_cap = auto_col_tiles(B_max);
+  L.nt_cap = 1;  // one 16-column tile per weight pass
   size_t off = 0;
   L.calls = off;
   off = align256(off + kMaxGrid * 4);
@@ -430,7 +444,7 @@ struct ExpArgs {
   uint16_t* out;
   uint8_t* dump_codes;
   uint8_t* dump_scales;
-  int D, I, HB, NS1, NQ1, IP, K, floor_rule;
+  int D, I, HB, NS1, IP, K, floor_rule;
   int g_cap, u_cap;  // LDS capacity of the group list and the unit rows
 };
 
@@ -504,9 +518,6 @@ __device__ __forceinline__ void lds_ld_b(uint32_t addr16, uint32_t addr4, uint4&
 __device__ __forceinline__ int lds_uni(uint32_t addr) {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(lds_ld4(addr)));
 }
-// Workgroup barrier that waits for the workgroup's own LDS traffic only (the generic
-// barrier would also wait for the in-flight weight stream).
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int VMCNT>
 __device__ __forceinline__ void wait_vm() {
@@ -525,43 +536,73 @@ __device__ __forceinline__ uint32_t lds_base() {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   return static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void*)smem));
 }
+__device__ __forceinline__ void lds_st4(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+}
+
+// Waits (bounded, a fraction of a second) until the LDS word at addr reaches `want`
+// (>= or ==).  The waves of a workgroup hand work to each other through such words; a
+// wait that runs out sets bit 2 of the unit-table flags and goes on.
+template <bool EQ>
+__device__ __forceinline__ void lds_wait(uint32_t addr, int want, int32_t* err) {
+  for (uint32_t spins = 0;; ++spins) {
+    const int v = lds_uni(addr);
+    if (EQ ? v == want : v >= want) return;
+    if (spins == kSpinLimit) {
+      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
 
 // ------------------------------------------------------------ LDS layout
-// [groups: expert, unit0, nunits, tile0 (g_cap each), chunk0 (g_cap + 1)]
-// [unit rows: u_cap x 8 u16 pair indices, 0xffff = padding]
-// [red: 3 waves x 4 tiles x NT x 1 KB]  [meta: 4 waves x R x 16 B]  [ring: 4 waves x R x slot]
-template <int NT>
+// [groups: g_cap records {expert, unit0, nunits, tile0}]  [chunk0: g_cap + 1 words]
+// [unit rows: u_cap x 8 u16 pair indices, 0xffff = padding]  [sync words]  [red: 2 x 4 streaming waves x NT x 4 KB, later reused as the 2 hidden
+// buffers]  [meta: 4 waves x R x 16 B]  [ring: 4 waves x R x slot]
+template <int NT, int R_>
 struct Geo {
-  static constexpr int R = NT == 1 ? 4 : 3;                  // items in flight per wave
-  static constexpr int SLOT = 4096 + 1024 + NT * 2048 + NT * 256;
-  static constexpr int L = 8 + 3 * NT;                       // DMA instructions per item
-  static constexpr int VM = (R - 1) * L;                     // vmcnt that completes the oldest item
-  static constexpr int RED = 3 * 4 * NT * 1024;
+  static constexpr int R = R_;                               // items in flight per wave
+  static constexpr int SLOT = 4096 + 256 + 2048 + 256;     // the FC1 item (the larger kind)
+  static constexpr int L = 8;                                // DMA instructions per item
+  static constexpr int VM = (R - 1) * L;                     // vmcnt that completes the oldest of R items
+  static constexpr int RED = 2 * kStream * NT * 4096;  // two hand-over slots per wave
 };
+
+// Sync words (u32, offsets within the sync area): sub[w] = FC1 blocks wave w has handed
+// over; ack = blocks the control wave has taken; prog[w] = the FC2 chunk (index in the
+// workgroup's sequence) wave w works on; ready[b] = the chunk held by hidden buffer b.
+constexpr uint32_t kSyncSub = 0, kSyncAck = 16, kSyncProg = 32, kSyncReady = 48, kSyncBytes = 64;
 
 struct LdsMap {
-  uint32_t expert, unit0, nunits, tile0, chunk0, urows, red, meta, ring;
+  uint32_t grec, chunk0, urows, sync, red, hid, hid_bytes, hs, meta, ring;
 };
 
-template <int NT>
-__host__ __device__ __forceinline__ LdsMap lds_map(uint32_t g_cap, uint32_t u_cap) {
+// Hidden buffer of one FC2 chunk: NT*16 columns x (IP + 16) code bytes (padded rows),
+// then NT*16 columns x IP/32 scale bytes.  The two hidden buffers share the FC1
+// hand-over area: the control wave fills them only after it took every FC1 block.
+template <int NT, int R>
+__host__ __device__ __forceinline__ LdsMap lds_map(uint32_t g_cap, uint32_t u_cap, uint32_t IP) {
   LdsMap t;
-  t.expert = 0;
-  t.unit0 = t.expert + g_cap * 4;
-  t.nunits = t.unit0 + g_cap * 4;
-  t.tile0 = t.nunits + g_cap * 4;
-  t.chunk0 = t.tile0 + g_cap * 4;
+  t.grec = 0;
+  t.chunk0 = g_cap * 16;
   t.urows = (t.chunk0 + (g_cap + 1) * 4 + 15) & ~15u;
-  t.red = t.urows + u_cap * 16;
-  t.meta = t.red + Geo<NT>::RED;
-  t.ring = t.meta + 4 * Geo<NT>::R * 16;
+  t.sync = t.urows + u_cap * 16;
+  t.red = t.sync + kSyncBytes;
+  t.hs = IP + 16;
+  t.hid_bytes = (NT * 16 * t.hs + NT * 16 * (IP / 32) + 15) & ~15u;
+  t.hid = t.red;
+  const uint32_t area = 2 * t.hid_bytes > Geo<NT, R>::RED ? 2 * t.hid_bytes : Geo<NT, R>::RED;
+  t.meta = t.red + area;
+  t.ring = t.meta + kStream * R * 16;
   return t;
 }
 
-template <int NT>
-inline size_t lds_bytes(int g_cap, int u_cap) {
-  const LdsMap t = lds_map<NT>(static_cast<uint32_t>(g_cap), static_cast<uint32_t>(u_cap));
-  return t.ring + 4 * static_cast<size_t>(Geo<NT>::R) * Geo<NT>::SLOT;
+template <int NT, int R>
+inline size_t lds_bytes(int g_cap, int u_cap, int IP) {
+  const LdsMap t = lds_map<NT, R>(static_cast<uint32_t>(g_cap), static_cast<uint32_t>(u_cap),
+                                  static_cast<uint32_t>(IP));
+  return t.ring + kStream * static_cast<size_t>(R) * Geo<NT, R>::SLOT;
 }
 
 // Per-workgroup copy of the unit table: the group list, chunk0[g] = first weight-pass
@@ -570,18 +611,15 @@ inline size_t lds_bytes(int g_cap, int u_cap) {
 template <int NT>
 __device__ __forceinline__ int load_groups(const ExpArgs& a, const LdsMap& m, int n_groups, int n_units) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  int* expert = reinterpret_cast<int*>(smem + m.expert);
-  int* unit0 = reinterpret_cast<int*>(smem + m.unit0);
-  int* nunits = reinterpret_cast<int*>(smem + m.nunits);
-  int* tile0 = reinterpret_cast<int*>(smem + m.tile0);
+  int4* grec = reinterpret_cast<int4*>(smem + m.grec);
   int* chunk0 = reinterpret_cast<int*>(smem + m.chunk0);
   uint16_t* urows = reinterpret_cast<uint16_t*>(smem + m.urows);
-  for (int i = threadIdx.x; i < n_groups; i += kWG) {
-    expert[i] = a.tbl.g_expert[i];
-    unit0[i] = a.tbl.g_unit0[i];
-    nunits[i] = a.tbl.g_nunits[i];
-    tile0[i] = a.tbl.g_tile0[i];
+  if (threadIdx.x < kSyncBytes / 4) {
+    const int i = threadIdx.x;  // sub, ack = 0; prog, ready = -1
+    reinterpret_cast<int*>(smem + m.sync)[i] = (i * 4 >= static_cast<int>(kSyncProg)) ? -1 : 0;
   }
+  for (int i = threadIdx.x; i < n_groups; i += kWG)
+    grec[i] = make_int4(a.tbl.g_expert[i], a.tbl.g_unit0[i], a.tbl.g_nunits[i], a.tbl.g_tile0[i]);
   // unit rows: int32 pair indices (-1 = padding) -> u16; four units per thread in flight
   const int4* rows = reinterpret_cast<const int4*>(a.tbl.unit_rows);
   for (int base = 0; base < n_units; base += 4 * kWG) {
@@ -612,7 +650,7 @@ __device__ __forceinline__ int load_groups(const ExpArgs& a, const LdsMap& m, in
     int carry = 0;
     for (int base = 0; base < n_groups; base += 64) {
       const int g = base + lane;
-      const int v = g < n_groups ? (((nunits[g] + 1) >> 1) + NT - 1) / NT : 0;
+      const int v = g < n_groups ? (((grec[g].z + 1) >> 1) + NT - 1) / NT : 0;
       int inc = v;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
@@ -636,12 +674,22 @@ struct GroupInfo {
 __device__ __forceinline__ GroupInfo group_at(const LdsMap& m, uint32_t lb, int g) {
   GroupInfo gi;
   gi.g = g;
-  gi.c0 = lds_uni(lb + m.chunk0 + 4 * g);
-  gi.c1 = lds_uni(lb + m.chunk0 + 4 * g + 4);
-  gi.e = lds_uni(lb + m.expert + 4 * g);
-  gi.unit0 = lds_uni(lb + m.unit0 + 4 * g);
-  gi.nunits = lds_uni(lb + m.nunits + 4 * g);
-  gi.tile0 = lds_uni(lb + m.tile0 + 4 * g);
+  uint4 r;
+  uint32_t c0, c1;
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b32 %1, %4\n\t"
+      "ds_read_b32 %2, %4 offset:4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r), "=&v"(c0), "=&v"(c1)
+      : "v"(lb + m.grec + 16 * g), "v"(lb + m.chunk0 + 4 * g)
+      : "memory");
+  gi.c0 = __builtin_amdgcn_readfirstlane(static_cast<int>(c0));
+  gi.c1 = __builtin_amdgcn_readfirstlane(static_cast<int>(c1));
+  gi.e = __builtin_amdgcn_readfirstlane(static_cast<int>(r.x));
+  gi.unit0 = __builtin_amdgcn_readfirstlane(static_cast<int>(r.y));
+  gi.nunits = __builtin_amdgcn_readfirstlane(static_cast<int>(r.z));
+  gi.tile0 = __builtin_amdgcn_readfirstlane(static_cast<int>(r.w));
   gi.ntiles = (gi.nunits + 1) >> 1;
   gi.cc = 0;
   return gi;
@@ -758,8 +806,28 @@ struct Cursor {
   int s, s_hi;        // FC1: step in the block, end of the slice in the block
   int gidx;           // global block / unit of the item
   int chunk, j;       // its chunk, and hidden block (FC1) / output tile (FC2) in the chunk
+  int seq0, cfirst;   // FC2: index of the list's first chunk in the workgroup's chunk sequence
   GroupInfo gi;       // the chunk's group
+  int xrow, xsrow;    // FC1, per lane: offsets of its column's x codes (+ its K quarter) and scales
 };
+
+// Per lane: the x row of the column the lane holds in the chunk (group gi, tile gi.cc);
+// padded columns read row 0 (their results are never stored).
+__device__ __forceinline__ void x_rows(const ExpArgs& a, const LdsMap& m, uint32_t lb, const GroupInfo& gi,
+                                       int& xrow, int& xsrow) {
+  const int l = threadIdx.x & 63;
+  const int pair = column_pair(m, lb, gi, gi.cc * 16 + (l & 15));
+  const int t = pair >= 0 ? pair / a.K : 0;
+  xrow = t * a.D + 16 * (l >> 4);
+  xsrow = t * (a.D / 32);
+}
+
+// Chunks that the workgroup's FC2 slice S spans: [first, first + count).
+__device__ __forceinline__ int fc2_span(const ExpArgs& a, const Slice& S, int& first) {
+  const int TPE = a.D / 16;
+  first = (S.base + S.lo) / TPE;
+  return S.hi > S.lo ? (S.base + S.hi - 1) / TPE - first + 1 : 0;
+}
 
 __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
                                             int n_chunks, Cursor& c) {
@@ -799,10 +867,16 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
     c.hi = sl.hi;
     c.base = sl.base;
     c.b = c.h < 2 ? c.lo / a.NS1 : c.lo + w;
+    if (c.h >= 2) {
+      fc2_span(a, sl, c.cfirst);
+      int f2;
+      c.seq0 = c.h == 2 ? 0 : fc2_span(a, make_slice(a, n_chunks, 2), f2);
+    }
     fresh = true;
   }
   const int per_chunk = c.h < 2 ? a.HB : a.D / 16;
   const int gidx = c.base + c.b;
+  bool moved = fresh;
   if (fresh) {
     c.chunk = gidx / per_chunk;
     c.j = gidx - c.chunk * per_chunk;
@@ -821,167 +895,242 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
       gi.cc = chunk - gi.c0;
       c.gi = gi;
       c.chunk = chunk;
+      moved = true;
     }
   }
+  if (moved && c.h < 2) x_rows(a, m, lb, c.gi, c.xrow, c.xsrow);
   c.gidx = gidx;
 }
 
 // ------------------------------------------------------------ the item stream
-// A wave's item k lives in ring slot k % R of the wave: FC1 = four 1 KB weight tiles
-// (FP4 A operands), their E8M0 words, the NT token-column B operands (FP8) and their
-// E8M0 words; FC2 = NS2 1 KB weight tiles and their E8M0 word.  Every item issues the
-// same number L of DMA instructions (FC2 and the dummies past the end pad with
-// redundant word loads), so "the oldest of R items is complete" is always
-// s_waitcnt vmcnt((R-1)*L).  The item's metadata goes to a 16-byte LDS record.
-template <int NT, int NS2>
+// A wave's item k lives in ring slot k % R of the wave.  FC1 item: [A: four 1 KB FP4 row
+// tiles][A scales: one word per lane][x: the 2 KB FP8 B operand][x scales: one word per
+// lane].  FC2 item: [A: NS2 1 KB FP4 tiles][A scales: one word per lane].  Every item
+// issues the same number L of DMA instructions (FC2 items and the dummies past the end
+// pad with redundant word loads into unused bytes of their slot), so "the oldest of R
+// items has landed" is always s_waitcnt vmcnt((R-1)*L).  The item's 16-byte record goes
+// to LDS when it is issued.
+constexpr uint32_t kSlotAS = 4096, kSlotX = 4352, kSlotXS = 6400, kSlotPad = 4352;
+
+__device__ __forceinline__ void lds_st16_async(uint32_t addr, uint4 v) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u x = {v.x, v.y, v.z, v.w};
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(x) : "memory");
+}
+
+template <int NS2, int R>
 __device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, uint32_t lb, const Cursor& c, int k) {
+  using G = Geo<1, R>;
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-  using G = Geo<NT>;
-  const int slot = k % G::R;
-  const uint32_t so = m.ring + (w * G::R + slot) * G::SLOT;  // offset from the LDS base
+  const int slot = k % R;
+  const uint32_t so = m.ring + (w * R + slot) * G::SLOT;  // offset from the LDS base
   uint4 meta = make_uint4(2u, 0u, 0u, 0u);                   // 2: dummy
   int done = 0;
-  const GroupInfo& gi = c.gi;
   if (c.h < 2) {
-    const int s = c.s, q = s >> 2;
-    const int64_t wrow = static_cast<int64_t>(gi.e) * a.HB + c.j;
-    const uint8_t* wb = a.w13p + (wrow * a.NS1 + s) * 4096 + l * 16;
-    const uint8_t* sb = a.s13p + (wrow * a.NQ1 + q) * 1024 + l * 4;
+    const int64_t step = static_cast<int64_t>(c.gi.e * a.HB + c.j) * a.NS1 + c.s;
+    const uint8_t* wb = a.w13p + step * 4096 + l * 16;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) dma16(wb + rt * 1024, so + rt * 1024);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) dma4(sb + rt * 256, so + 4096 + rt * 256);
-    uint32_t live = 0;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int tcol = gi.cc * NT + n;
-      const int pair = tcol < gi.ntiles ? column_pair(m, lb, gi, tcol * 16 + (l & 15)) : -1;
-      const int t = pair >= 0 ? pair / a.K : 0;
-      live |= (pair >= 0 ? 1u : 0u) << n;
-      const uint8_t* xr = a.xcodes + static_cast<int64_t>(t) * a.D + s * 128 + 16 * (l >> 4);
-      dma16(xr, so + 5120 + n * 2048);
-      dma16(xr + 64, so + 5120 + n * 2048 + 1024);
-      dma4(a.xscales + static_cast<int64_t>(t) * (a.D / 32) + 4 * s, so + 5120 + NT * 2048 + n * 256);
-    }
-    meta = make_uint4(0u, static_cast<uint32_t>(c.gidx), static_cast<uint32_t>(s), live);
+    dma4(a.s13p + step * 256 + l * 4, so + kSlotAS);
+    const uint8_t* xr = a.xcodes + c.xrow + c.s * 128;
+    dma16(xr, so + kSlotX);
+    dma16(xr + 64, so + kSlotX + 1024);
+    dma4(a.xscales + c.xsrow + 4 * c.s, so + kSlotXS);
+    meta = make_uint4(0u, static_cast<uint32_t>(c.gidx), 0u, 0u);
     done = G::L;
   } else if (c.h < 4) {
-    const int64_t tile = static_cast<int64_t>(gi.e) * (a.D / 16) + c.j;
+    const int64_t tile = static_cast<int64_t>(c.gi.e) * (a.D / 16) + c.j;
     const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
 #pragma unroll
     for (int s = 0; s < NS2; ++s) dma16(wb + s * 1024, so + s * 1024);
-    dma4(a.s2p + tile * 256 + l * 4, so + 4096);
-    meta = make_uint4(1u, static_cast<uint32_t>(c.chunk), static_cast<uint32_t>(c.j), 0u);
+    dma4(a.s2p + tile * 256 + l * 4, so + kSlotAS);
+    meta = make_uint4(1u, static_cast<uint32_t>(c.chunk), static_cast<uint32_t>(c.j),
+                      static_cast<uint32_t>(c.seq0 + c.chunk - c.cfirst));
     done = NS2 + 1;
   }
-  // pad to L DMA instructions (redundant word loads into the slot's B-operand area)
-  for (int i = done; i < G::L; ++i) dma4(a.s2p + l * 4, so + 5120 + (i % 8) * 256);
-  if (l == 0) lds_st16(lb + m.meta + (w * G::R + slot) * 16, meta);
+  for (int i = done; i < G::L; ++i) dma4(a.s2p + l * 4, so + kSlotPad + i * 256);
+  if (l == 0) lds_st16_async(lb + m.meta + (w * R + slot) * 16, meta);
 }
 
-// End of FC1 block b for the whole workgroup (every wave calls it, in block order):
-// the four waves' sums meet in LDS (asm, fixed order); wave 0 finishes the block -- or,
-// when the block is split over several workgroups' slices, files its partial sums and
-// the last-arriving contributor adds all of them in slice order (experts page,
-// ExpertsKernel.partials) and finishes it.  Finishing = SwiGLU + MXFP8 of the hidden
-// block for every column tile of the chunk, then its flag, tagged with the call number.
+// FC2 operands of one item, read with a single LDS wait: per K step s the A tile
+// (FP4, 16 output rows, at pa + 1024 s) and the hidden's B operand halves (pb + 128 s,
+// + 64) and scale word (ps + 4 s); the A scale word (pq + 4096).
+template <int NS2>
+struct Fc2Ops {
+  uint4 a[NS2], bl[NS2], bh[NS2];
+  uint32_t bs[NS2], as;
+};
+template <int NS2>
+__device__ __forceinline__ void fc2_read(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<NS2>& o);
+
+template <>
+__device__ __forceinline__ void fc2_read<1>(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<1>& o) {
+  asm volatile(
+      "ds_read_b128 %0, %5 offset:0\n\t"
+      "ds_read_b32 %4, %6 offset:4096\n\t"
+      "ds_read_b128 %1, %7 offset:0\n\t"
+      "ds_read_b128 %2, %7 offset:64\n\t"
+      "ds_read_b32 %3, %8 offset:0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.as)
+      : "v"(pa), "v"(pq), "v"(pb), "v"(ps)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fc2_read<2>(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<2>& o) {
+  asm volatile(
+      "ds_read_b128 %0, %9 offset:0\n\t"
+      "ds_read_b128 %1, %9 offset:1024\n\t"
+      "ds_read_b32 %8, %10 offset:4096\n\t"
+      "ds_read_b128 %2, %11 offset:0\n\t"
+      "ds_read_b128 %3, %11 offset:64\n\t"
+      "ds_read_b32 %4, %12 offset:0\n\t"
+      "ds_read_b128 %5, %11 offset:128\n\t"
+      "ds_read_b128 %6, %11 offset:192\n\t"
+      "ds_read_b32 %7, %12 offset:4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1]), "=&v"(o.as)
+      : "v"(pa), "v"(pq), "v"(pb), "v"(ps)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fc2_read<3>(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<3>& o) {
+  asm volatile(
+      "ds_read_b128 %0, %13 offset:0\n\t"
+      "ds_read_b128 %1, %13 offset:1024\n\t"
+      "ds_read_b128 %2, %13 offset:2048\n\t"
+      "ds_read_b32 %12, %14 offset:4096\n\t"
+      "ds_read_b128 %3, %15 offset:0\n\t"
+      "ds_read_b128 %4, %15 offset:64\n\t"
+      "ds_read_b32 %5, %16 offset:0\n\t"
+      "ds_read_b128 %6, %15 offset:128\n\t"
+      "ds_read_b128 %7, %15 offset:192\n\t"
+      "ds_read_b32 %8, %16 offset:4\n\t"
+      "ds_read_b128 %9, %15 offset:256\n\t"
+      "ds_read_b128 %10, %15 offset:320\n\t"
+      "ds_read_b32 %11, %16 offset:8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1]), "=&v"(o.bl[2]), "=&v"(o.bh[2]), "=&v"(o.bs[2]), "=&v"(o.as)
+      : "v"(pa), "v"(pq), "v"(pb), "v"(ps)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fc2_read<4>(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<4>& o) {
+  asm volatile(
+      "ds_read_b128 %0, %17 offset:0\n\t"
+      "ds_read_b128 %1, %17 offset:1024\n\t"
+      "ds_read_b128 %2, %17 offset:2048\n\t"
+      "ds_read_b128 %3, %17 offset:3072\n\t"
+      "ds_read_b32 %16, %18 offset:4096\n\t"
+      "ds_read_b128 %4, %19 offset:0\n\t"
+      "ds_read_b128 %5, %19 offset:64\n\t"
+      "ds_read_b32 %6, %20 offset:0\n\t"
+      "ds_read_b128 %7, %19 offset:128\n\t"
+      "ds_read_b128 %8, %19 offset:192\n\t"
+      "ds_read_b32 %9, %20 offset:4\n\t"
+      "ds_read_b128 %10, %19 offset:256\n\t"
+      "ds_read_b128 %11, %19 offset:320\n\t"
+      "ds_read_b32 %12, %20 offset:8\n\t"
+      "ds_read_b128 %13, %19 offset:384\n\t"
+      "ds_read_b128 %14, %19 offset:448\n\t"
+      "ds_read_b32 %15, %20 offset:12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1]), "=&v"(o.bl[2]), "=&v"(o.bh[2]), "=&v"(o.bs[2]), "=&v"(o.bl[3]), "=&v"(o.bh[3]), "=&v"(o.bs[3]), "=&v"(o.as)
+      : "v"(pa), "v"(pq), "v"(pb), "v"(ps)
+      : "memory");
+}
+
+// The control wave's end of FC1 block lbk of list `half` (the experts page's
+// ExpertsKernel.partials and store_hidden).  acc holds the block's sums over this
+// workgroup's steps.  A block inside the slice is finished at once.  A block split over
+// several workgroups' slices is finished by the owner of its first step, for which it
+// is the slice's last block: the others (for which it is their first block) file their
+// partial sums and count in without waiting, and the finisher adds them in slice order.
+// No workgroup ever waits for a block that a wait of its own delays.  Finishing =
+// SwiGLU + MXFP8 of the hidden block for every column tile of the chunk, then its
+// flag, tagged with the call number.
 template <int NT>
-__device__ __forceinline__ void fc1_finish(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
-                                           const Slice& li, int half, int lbk, v4f (&acc)[4][NT], uint32_t gen) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ void control_block(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
+                                              const Slice& li, int half, int lbk, v4f (&acc)[4][NT],
+                                              uint32_t gen) {
+  const int l = threadIdx.x & 63;
   const int NS1 = a.NS1, HB = a.HB;
   const int p = blockIdx.x;
   const int b = li.base + lbk;  // global block
-  if (w > 0) {
+  const int bs = lbk * NS1;
+  if (li.lo > bs) {
+    // contributor: file the partial sums (device-coherent), then count in
+    float* slot = a.partials + (static_cast<int64_t>(p) * 2 + half) * NT * 1024 + l * 4;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const v4f v = acc[rt][n];
-        lds_st16(lb + m.red + ((((w - 1) * 4 + rt) * NT + n) * 64 + l) * 16,
-                 make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])));
-      }
-  }
-  wg_barrier();
-  if (w == 0) {
-#pragma unroll
-    for (int ww = 0; ww < 3; ++ww)
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const uint4 v = lds_ld16(lb + m.red + (((ww * 4 + rt) * NT + n) * 64 + l) * 16);
-          acc[rt][n][0] += __uint_as_float(v.x);
-          acc[rt][n][1] += __uint_as_float(v.y);
-          acc[rt][n][2] += __uint_as_float(v.z);
-          acc[rt][n][3] += __uint_as_float(v.w);
-        }
-    const int bs = lbk * NS1;
-    bool finish = li.lo <= bs && bs + NS1 <= li.hi;
-    if (!finish) {
-      // contributors: the slices owning the block's first and last steps, and between
-      // (slice p holds steps [floor(pT/P), floor((p+1)T/P)); its owner of x is
-      // ceil((x+1)P/T) - 1)
-      const int T = li.T, P = li.P;
-      auto owner = [&](int x) { return div_floor(static_cast<int64_t>(x + 1) * P + T - 1, T) - 1; };
-      const int pa = owner(bs), pb = owner(bs + NS1 - 1);
-      const int k = (li.lo / NS1 == lbk) ? 0 : 1;
-      float* slot = a.partials + ((static_cast<int64_t>(p) * 2 + half) * 2 + k) * NT * 1024 + l * 4;
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) st_dev_u32(slot + (n * 4 + rt) * 256 + r, __float_as_uint(acc[rt][n][r]));
-      wait_stores();
-      uint32_t old = 0;
-      if (l == 0) old = __hip_atomic_fetch_add(a.arrive + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      old = __builtin_amdgcn_readfirstlane(old);
-      finish = old == static_cast<uint32_t>(pb - pa);
-      if (finish) {
-        compiler_fence();
-        if (l == 0) st_dev_u32(a.arrive + b, 0u);  // re-arm for the next call
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-          for (int n = 0; n < NT; ++n) acc[rt][n] = v4f{0.f, 0.f, 0.f, 0.f};
-        for (int pp = pa; pp <= pb; ++pp) {
-          const int kk = (div_floor(static_cast<int64_t>(pp) * T, P) / NS1 == lbk) ? 0 : 1;
-          const float* src = a.partials + ((static_cast<int64_t>(pp) * 2 + half) * 2 + kk) * NT * 1024 + l * 4;
-#pragma unroll
-          for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-              const uint64_t v0 = ld_dev_u64(src + (n * 4 + rt) * 256);
-              const uint64_t v1 = ld_dev_u64(src + (n * 4 + rt) * 256 + 2);
-              acc[rt][n][0] += __uint_as_float(static_cast<uint32_t>(v0));
-              acc[rt][n][1] += __uint_as_float(static_cast<uint32_t>(v0 >> 32));
-              acc[rt][n][2] += __uint_as_float(static_cast<uint32_t>(v1));
-              acc[rt][n][3] += __uint_as_float(static_cast<uint32_t>(v1 >> 32));
-            }
-        }
+        for (int r = 0; r < 4; ++r) st_dev_u32(slot + (n * 4 + rt) * 256 + r, __float_as_uint(acc[rt][n][r]));
+    wait_stores();
+    if (l == 0) __hip_atomic_fetch_add(a.arrive + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (bs + NS1 > li.hi) {
+    // finisher: the block's other steps belong to slices p+1 .. pb (slice p holds steps
+    // [floor(pT/P), floor((p+1)T/P)); the owner of step x is ceil((x+1)P/T) - 1)
+    const int T = li.T, P = li.P;
+    const int pb = div_floor(static_cast<int64_t>(bs + NS1) * P + T - 1, T) - 1;
+    const uint32_t want = static_cast<uint32_t>(pb - p);
+    for (uint32_t spins = 0;; ++spins) {
+      if (ld_dev_u32(a.arrive + b) == want) break;
+      if (spins == kSpinLimit) {
+        if (l == 0) __hip_atomic_fetch_or(a.tbl.hdr + 3, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
-    if (finish) {
-      const int chunk = b / HB, j = b - chunk * HB;
-      const GroupInfo gi = group_of(m, lb, n_groups, chunk);
+    compiler_fence();
+    if (l == 0) st_dev_u32(a.arrive + b, 0u);  // re-arm for the next call
+    // up to four contributors' partials in flight at once, added in slice order
+    for (int pp0 = p + 1; pp0 <= pb; pp0 += 4) {
+      uint64_t v[4][NT * 8];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int t = gi.cc * NT + n;
-        if (t >= gi.ntiles) continue;
-        const v4f tot[4] = {acc[0][n], acc[1][n], acc[2][n], acc[3][n]};
-        hidden_epilogue(a, tot, j, gi.tile0 + t, column_pair(m, lb, gi, t * 16 + (l & 15)));
+      for (int u = 0; u < 4; ++u) {
+        if (pp0 + u > pb) continue;
+        const float* src = a.partials + (static_cast<int64_t>(pp0 + u) * 2 + half) * NT * 1024 + l * 4;
+#pragma unroll
+        for (int i = 0; i < NT * 4; ++i) {
+          v[u][2 * i] = ld_dev_u64(src + i * 256);
+          v[u][2 * i + 1] = ld_dev_u64(src + i * 256 + 2);
+        }
       }
-      // Publish: the block's codes and scales are stored (sc1) before its flag.
-      wait_stores();
-      if (l == 0) st_dev_u32(a.flags + b, gen + 1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (pp0 + u > pb) continue;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const uint64_t v0 = v[u][2 * (n * 4 + rt)], v1 = v[u][2 * (n * 4 + rt) + 1];
+            acc[rt][n][0] += __uint_as_float(static_cast<uint32_t>(v0));
+            acc[rt][n][1] += __uint_as_float(static_cast<uint32_t>(v0 >> 32));
+            acc[rt][n][2] += __uint_as_float(static_cast<uint32_t>(v1));
+            acc[rt][n][3] += __uint_as_float(static_cast<uint32_t>(v1 >> 32));
+          }
+      }
     }
   }
-  wg_barrier();
+  const int chunk = b / HB, j = b - chunk * HB;
+  const GroupInfo gi = group_of(m, lb, n_groups, chunk);
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[rt][n] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NT; ++n) {
+    const int t = gi.cc * NT + n;
+    if (t >= gi.ntiles) continue;
+    const v4f tot[4] = {acc[0][n], acc[1][n], acc[2][n], acc[3][n]};
+    hidden_epilogue(a, tot, j, gi.tile0 + t, column_pair(m, lb, gi, t * 16 + (l & 15)));
+  }
+  // Publish: the block's codes and scales are stored (sc1) before its flag.
+  wait_stores();
+  if (l == 0) st_dev_u32(a.flags + b, gen + 1);
 }
 
 // Wait until the HB hidden blocks of a chunk carry this call's tag.  Bounded (seconds)
@@ -992,8 +1141,9 @@ __device__ __forceinline__ void wait_chunk(const ExpArgs& a, int chunk, uint32_t
   const uint32_t want = gen + 1;
   const uint32_t* f = a.flags + static_cast<int64_t>(chunk) * a.HB;
   for (uint32_t spins = 0;; ++spins) {
-    const uint32_t v = l < a.HB ? ld_dev_u32(f + l) : want;
-    if (__all(v == want)) break;
+    bool ok = true;
+    for (int i = l; i < a.HB; i += 64) ok = ok && ld_dev_u32(f + i) == want;
+    if (__all(ok)) break;
     if (spins == kSpinLimit) {
       if (l == 0) __hip_atomic_fetch_or(a.tbl.hdr + 3, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
@@ -1003,184 +1153,268 @@ __device__ __forceinline__ void wait_chunk(const ExpArgs& a, int chunk, uint32_t
   compiler_fence();
 }
 
-// FC2 B operand (the hidden of a chunk's NT column tiles, all NS2 K steps).
+// The control wave's copy of one FC2 chunk's hidden (codes and scales of its NT column
+// tiles, as FC1 published them) into hidden buffer `buf`.  Per tile: 16 columns x IP
+// code bytes (IP = 128 * NS2, contiguous: 2 * NS2 16-byte pieces per lane) and 16 x
+// IP/32 scale bytes (one word per lane), all loaded in one batch.
 template <int NT, int NS2>
-struct Fc2Hidden {
-  uint4 BL[NT][NS2], BH[NT][NS2];
-  uint32_t SB[NT][NS2];
-  int chunk;
-  GroupInfo gi;
-};
-
-template <int NT, int NS2>
-__device__ __forceinline__ void load_hidden(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups, int chunk, uint32_t gen,
-                            Fc2Hidden<NT, NS2>& hd) {
-  const int l = threadIdx.x & 63, grp = l >> 4;
-  hd.chunk = chunk;
-  hd.gi = group_of(m, lb, n_groups, chunk);
-  wait_chunk(a, chunk, gen);
+__device__ __forceinline__ void control_hidden(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
+                                               int chunk, uint32_t buf) {
+  const int l = threadIdx.x & 63;
+  const GroupInfo gi = group_of(m, lb, n_groups, chunk);
+  constexpr int IP = 128 * NS2, PER_COL = IP / 16, SW = IP / 32;
+  const uint32_t hb = lb + m.hid + buf * m.hid_bytes;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const int t = hd.gi.cc * NT + n;
-    const int gcol = (hd.gi.tile0 + (t < hd.gi.ntiles ? t : 0)) * 16 + (l & 15);
-    const uint8_t* hc = a.hcodes + static_cast<int64_t>(gcol) * a.IP + 16 * grp;
+    const int t = gi.cc * NT + n;
+    if (t >= gi.ntiles) continue;
+    const int64_t gcol0 = static_cast<int64_t>(gi.tile0 + t) * 16;
+    const uint8_t* src = a.hcodes + gcol0 * IP;
+    const uint8_t* ssrc = a.hscales + gcol0 * SW;
+    uint64_t v[2 * NS2][2];
 #pragma unroll
-    for (int s = 0; s < NS2; ++s) {
-      const uint64_t l0 = ld_dev_u64(hc + s * 128), l1 = ld_dev_u64(hc + s * 128 + 8);
-      const uint64_t h0 = ld_dev_u64(hc + s * 128 + 64), h1 = ld_dev_u64(hc + s * 128 + 72);
-      hd.BL[n][s] = make_uint4(static_cast<uint32_t>(l0), static_cast<uint32_t>(l0 >> 32), static_cast<uint32_t>(l1),
-                               static_cast<uint32_t>(l1 >> 32));
-      hd.BH[n][s] = make_uint4(static_cast<uint32_t>(h0), static_cast<uint32_t>(h0 >> 32), static_cast<uint32_t>(h1),
-                               static_cast<uint32_t>(h1 >> 32));
-      hd.SB[n][s] = ld_dev_u32(a.hscales + static_cast<int64_t>(gcol) * (a.IP / 32) + 4 * s);
+    for (int u = 0; u < 2 * NS2; ++u) {
+      const int q = u * 64 + l;
+      v[u][0] = ld_dev_u64(src + q * 16);
+      v[u][1] = ld_dev_u64(src + q * 16 + 8);
     }
+    const uint32_t sw = l < 4 * SW ? ld_dev_u32(ssrc + l * 4) : 0u;
+#pragma unroll
+    for (int u = 0; u < 2 * NS2; ++u) {
+      const int q = u * 64 + l, col = q / PER_COL, off = (q - col * PER_COL) * 16;
+      lds_st16(hb + (n * 16 + col) * m.hs + off,
+               make_uint4(static_cast<uint32_t>(v[u][0]), static_cast<uint32_t>(v[u][0] >> 32),
+                          static_cast<uint32_t>(v[u][1]), static_cast<uint32_t>(v[u][1] >> 32)));
+    }
+    if (l < 4 * SW) lds_st4(hb + NT * 16 * m.hs + n * 16 * SW + l * 4, sw);
   }
 }
 
 // The persistent routed-experts kernel (experts page, ExpertsKernel; runtime page,
-// PersistentExperts.run): one workgroup per CU, co-resident (FC2 units wait for hidden
-// blocks that other workgroups' FC1 slices produce).  Each wave streams its items --
-// FC1(A), FC1(B), FC2(A), FC2(B) -- through a private LDS ring R items deep.
-template <int NT, int NS2>
+// PersistentExperts.run): one workgroup per CU, co-resident (FC2 waits for hidden
+// blocks that other workgroups' FC1 slices produce).  Waves 0-3 stream their items --
+// FC1(A), FC1(B), FC2(A), FC2(B) -- through private LDS rings R items deep and touch
+// global memory only through that DMA stream and the output stores, so no wait ever
+// drains a ring.  Wave 4, the control wave, does every cross-workgroup step: it takes
+// the streaming waves' FC1 sums of each block (LDS), files or finishes the block and
+// publishes its hidden, then polls for the hidden of each FC2 chunk the workgroup
+// needs and copies it into one of two LDS buffers.
+template <int NT, int NS2, int R>
 __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
-  using G = Geo<NT>;
+  using G = Geo<NT, R>;
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6, grp = l >> 4;
-  const LdsMap m = lds_map<NT>(static_cast<uint32_t>(a.g_cap), static_cast<uint32_t>(a.u_cap));
+  const LdsMap m = lds_map<NT, R>(static_cast<uint32_t>(a.g_cap), static_cast<uint32_t>(a.u_cap),
+                                  static_cast<uint32_t>(a.IP));
   const uint32_t lb = lds_base();
   const int n_groups = a.tbl.hdr[1];
   const int n_units = a.tbl.hdr[0];
   const uint32_t gen = a.calls[blockIdx.x];
   const int n_chunks = load_groups<NT>(a, m, n_groups, n_units);
+  const uint32_t sy = lb + m.sync;
+  agpr_form();
 
-  v4f acc[4][NT];
+  if (w == kStream) {
+    // ---------------------------------------------------------- control wave
+    v4f acc[4][NT];
+    int q = 0;  // FC1 blocks of the workgroup taken so far
+    for (int half = 0; half < 2; ++half) {
+      const Slice S = make_slice(a, n_chunks, half);
+      if (S.hi <= S.lo) continue;
+      for (int lbk = S.lo / a.NS1; lbk <= (S.hi - 1) / a.NS1; ++lbk, ++q) {
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+        for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncSub + 4 * ww, q + 1, a.tbl.hdr + 3);
+        // the streaming waves' sums, added in wave order
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[rt][n] = v4f{0.f, 0.f, 0.f, 0.f};
-  // FC1 blocks are finished by the whole workgroup in order: half A's slice, then B's
-  int fin_h = 0;
-  Slice fin = make_slice(a, n_chunks, 0);
-  int fin_b = fin.lo / a.NS1, fin_last = fin.hi > fin.lo ? (fin.hi - 1) / a.NS1 : fin_b - 1;
+        for (int ww = 0; ww < kStream; ++ww)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              const uint4 v = lds_ld16(lb + m.red + ((((q & 1) * kStream + ww) * 4 + rt) * NT + n) * 1024 + l * 16);
+              const v4f x = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+              acc[rt][n] = ww == 0 ? x : acc[rt][n] + x;
+            }
+        if (l == 0) lds_st4(sy + kSyncAck, static_cast<uint32_t>(q + 1));
+        control_block<NT>(a, m, lb, n_groups, S, half, lbk, acc, gen);
+      }
+    }
+    int i = 0;  // FC2 chunks of the workgroup loaded so far
+    for (int h = 2; h < 4; ++h) {
+      int first;
+      const int cnt = fc2_span(a, make_slice(a, n_chunks, h), first);
+      for (int c = first; c < first + cnt; ++c, ++i) {
+        wait_chunk(a, c, gen);
+        if (i >= 2)  // buffer i&1 held chunk i-2: every wave must have moved past it
+#pragma unroll
+          for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncProg + 4 * ww, i - 1, a.tbl.hdr + 3);
+        control_hidden<NT, NS2>(a, m, lb, n_groups, c, static_cast<uint32_t>(i & 1));
+        if (l == 0) lds_st4(sy + kSyncReady + 4 * (i & 1), static_cast<uint32_t>(i));
+      }
+    }
+    if (l == 0)
+      for (int qq = blockIdx.x; qq < kMaxGrid; qq += gridDim.x) a.calls[qq] = gen + 1;
+    return;
+  }
 
-  Cursor pc;  // issue cursor, R-1 items ahead of consumption
+  // ------------------------------------------------------------ streaming waves
+  static_assert(NT == 1, "one 16-column tile per weight pass");
+  v4f acc[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+  // FC1 blocks are handed over in the workgroup's order: half A's slice, then B's
+  int sub_h = 0, sub_q = 0;
+  Slice sub = make_slice(a, n_chunks, 0);
+  int sub_b = sub.lo / a.NS1, sub_last = sub.hi > sub.lo ? (sub.hi - 1) / a.NS1 : sub_b - 1;
+  // Hands the sums of the workgroup's FC1 blocks below global block `upto` to the control
+  // wave, in the workgroup's block order (zeros for blocks without steps of this wave).
+  auto hand_over = [&](int upto) {
+    while (sub_h < 2) {
+      if (sub_b <= sub_last) {
+        if (sub.base + sub_b >= upto) break;
+        lds_wait<false>(sy + kSyncAck, sub_q - 1, a.tbl.hdr + 3);  // slot sub_q&1 is free once block sub_q-2 is taken
+        mfma_settle(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const v4f v = acc[rt];
+          lds_st16(lb + m.red + (((sub_q & 1) * kStream + w) * 4 + rt) * 1024 + l * 16,
+                   make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3])));
+          acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        ++sub_q;
+        if (l == 0) lds_st4(sy + kSyncSub + 4 * w, static_cast<uint32_t>(sub_q));
+        ++sub_b;
+      } else if (++sub_h < 2) {
+        sub = make_slice(a, n_chunks, 1);
+        sub_b = sub.lo / a.NS1;
+        sub_last = sub.hi > sub.lo ? (sub.hi - 1) / a.NS1 : sub_b - 1;
+      }
+    }
+  };
+
+  Cursor pc;  // issue cursor, R items ahead of consumption
   pc.h = -1;
   pc.s = pc.s_hi = 0;
   pc.b = pc.hi = 0;
   cursor_next(a, m, lb, n_groups, n_chunks, pc);
-  Fc2Hidden<NT, NS2> hd;
-  hd.chunk = -1;
   int n_real = 0;  // real items issued (they precede the dummies)
-  for (int k = 0;; ++k) {
-    issue_item<NT, NS2>(a, m, lb, pc, k);
+  auto issue_next = [&](int k) {
+    issue_item<NS2, R>(a, m, lb, pc, k);
     if (pc.h < 4) {
       ++n_real;
       cursor_next(a, m, lb, n_groups, n_chunks, pc);
     }
-    const int kc = k - (G::R - 1);  // the item consumed now
-    if (kc < 0) continue;
+  };
+  // FC2 state of the chunk in use: per lane, its output row (or -1) and its column's
+  // places in the hidden buffer
+  int cur_seq = -1, orow = -1;
+  uint32_t hbl = 0, hbs = 0;
+  const int col = l & 15;
+  for (int k = 0; k < R; ++k) issue_next(k);  // R items in flight
+  for (int kc = 0;; ++kc) {
     const bool real = kc < n_real;
-    uint4 meta = make_uint4(3u, 0u, 0u, 0u);
-    const int slot = kc % G::R;
-    const uint32_t sa_ = lb + m.ring + (w * G::R + slot) * G::SLOT;
+    const int slot = kc % R;
+    const uint32_t sa_ = lb + m.ring + (w * R + slot) * G::SLOT;
+    // this item's and the next item's records (written at issue; no need to wait for data)
+    uint4 meta = make_uint4(3u, 0u, 0u, 0u), nm = make_uint4(3u, 0u, 0u, 0u);
     if (real) {
-      wait_vm<G::VM>();
-      meta = lds_ld16(lb + m.meta + (w * G::R + slot) * 16);
+      asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(meta), "=&v"(nm)
+                   : "v"(lb + m.meta + (w * R + slot) * 16), "v"(lb + m.meta + (w * R + (kc + 1) % R) * 16)
+                   : "memory");
+      if (kc + 1 >= n_real) nm = make_uint4(3u, 0u, 0u, 0u);
     }
     const int type = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.x));
-    // finish the workgroup's FC1 blocks before this item's block (all for FC2 / the end)
-    const int upto = type == 0 ? __builtin_amdgcn_readfirstlane(static_cast<int>(meta.y)) : 0x7fffffff;
-    while (fin_h < 2) {
-      if (fin_b <= fin_last) {
-        if (fin.base + fin_b >= upto) break;
-        fc1_finish<NT>(a, m, lb, n_groups, fin, fin_h, fin_b, acc, gen);
-        ++fin_b;
-      } else if (++fin_h < 2) {
-        fin = make_slice(a, n_chunks, 1);
-        fin_b = fin.lo / a.NS1;
-        fin_last = fin.hi > fin.lo ? (fin.hi - 1) / a.NS1 : fin_b - 1;
-      }
-    }
+    // hand over the sums of the workgroup's FC1 blocks before this item's block (all of
+    // them for an FC2 item or at the end); normally already done after the previous item
+    hand_over(type == 0 ? __builtin_amdgcn_readfirstlane(static_cast<int>(meta.y)) : 0x7fffffff);
     if (!real) break;
+    wait_vm<G::VM>();  // item kc has landed (the R-1 younger items may still be in flight)
     if (type == 0) {
-      const int s = static_cast<int>(meta.z);
-      const uint32_t live = meta.w;
-      uint4 av[4];
-      uint32_t saw[4];
-      lds_ld16x4<0, 1024>(sa_ + l * 16, av[0], av[1], av[2], av[3]);
-      lds_ld4x4<4096, 256>(sa_ + l * 4, saw[0], saw[1], saw[2], saw[3]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const bool lv = (live >> n) & 1u;
-        uint4 bl, bh;
-        uint32_t sbw;
-        if (n == 0)
-          lds_ld_b<5120, 6144, 5120 + NT * 2048>(sa_ + l * 16, sa_ + l * 4, bl, bh, sbw);
-        else
-          lds_ld_b<7168, 8192, 5120 + NT * 2048 + 256>(sa_ + l * 16, sa_ + l * 4, bl, bh, sbw);
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        const v8i bop = fp8_operand(lv ? bl : z, lv ? bh : z);
-        const int sb = lv ? static_cast<int>((sbw >> (8 * grp)) & 0xffu) : 127;
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const int sa = static_cast<int>((saw[rt] >> (8 * (s & 3))) & 0xffu);
-          acc[rt][n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(av[rt]), bop, acc[rt][n], 4, 0, 0,
-                                                                        sa, 0, sb);
-        }
-      }
+      uint4 a0, a1, a2, a3, xl, xh;
+      uint32_t saw, sbw;
+      asm volatile(
+          "ds_read_b128 %0, %8\n\t"
+          "ds_read_b128 %1, %8 offset:1024\n\t"
+          "ds_read_b128 %2, %8 offset:2048\n\t"
+          "ds_read_b128 %3, %8 offset:3072\n\t"
+          "ds_read_b32 %4, %9 offset:4096\n\t"
+          "ds_read_b128 %5, %8 offset:4352\n\t"
+          "ds_read_b128 %6, %8 offset:5376\n\t"
+          "ds_read_b32 %7, %9 offset:6400\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(saw), "=&v"(xl), "=&v"(xh), "=&v"(sbw)
+          : "v"(sa_ + l * 16), "v"(sa_ + l * 4)
+          : "memory");
+      const v8i bop = fp8_operand(xl, xh);
+      const int sb = static_cast<int>((sbw >> (8 * grp)) & 0xffu);
+      acc[0] = mfma_fp4_fp8(fp4_operand(a0), bop, acc[0], static_cast<int>(saw & 0xffu), sb);
+      acc[1] = mfma_fp4_fp8(fp4_operand(a1), bop, acc[1], static_cast<int>((saw >> 8) & 0xffu), sb);
+      acc[2] = mfma_fp4_fp8(fp4_operand(a2), bop, acc[2], static_cast<int>((saw >> 16) & 0xffu), sb);
+      acc[3] = mfma_fp4_fp8(fp4_operand(a3), bop, acc[3], static_cast<int>(saw >> 24), sb);
+      // this wave's part of the block may be complete: the next item's record tells, so
+      // the sums go to the control wave without waiting for the next item's data
+      const int ntype = __builtin_amdgcn_readfirstlane(static_cast<int>(nm.x));
+      hand_over(ntype == 0 ? __builtin_amdgcn_readfirstlane(static_cast<int>(nm.y)) : 0x7fffffff);
     } else if (type == 1) {
-      const int chunk = static_cast<int>(meta.y), rt2 = static_cast<int>(meta.z);
-      if (chunk != hd.chunk) load_hidden<NT, NS2>(a, m, lb, n_groups, chunk, gen, hd);
-      const uint32_t saw = lds_ld4(sa_ + 4096 + l * 4);
-      v4f o[NT];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
+      const int seq = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.w));
+      if (seq != cur_seq) {
+        if (l == 0) lds_st4(sy + kSyncProg + 4 * w, static_cast<uint32_t>(seq));
+        lds_wait<true>(sy + kSyncReady + 4 * (seq & 1), seq, a.tbl.hdr + 3);
+        cur_seq = seq;
+        const GroupInfo hgi = group_of(m, lb, n_groups, __builtin_amdgcn_readfirstlane(static_cast<int>(meta.y)));
+        const int pair = column_pair(m, lb, hgi, hgi.cc * 16 + col);
+        orow = pair >= 0 ? pair * a.D : -1;
+        const uint32_t hb = lb + m.hid + static_cast<uint32_t>(seq & 1) * m.hid_bytes;
+        hbl = hb + col * m.hs + 16 * grp;
+        hbs = hb + 16 * m.hs + col * (a.IP / 32);
+      }
+      Fc2Ops<NS2> op;
+      fc2_read<NS2>(sa_ + l * 16, sa_ + l * 4, hbl, hbs, op);
+      v4f o = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS2; ++s) {
-        // K-blocks beyond I (I not a multiple of 128) are zero.
+        // K-blocks beyond I (I not a multiple of 128) are zero
         const bool lo_ok = 4 * s + (grp >> 1) < a.HB, hi_ok = 4 * s + 2 + (grp >> 1) < a.HB;
         const bool sc_ok = 4 * s + grp < a.HB;
-        const int sa = static_cast<int>((saw >> (8 * s)) & 0xffu);
-        const uint4 av = lds_ld16(sa_ + s * 1024 + l * 16);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          if (hd.gi.cc * NT + n >= hd.gi.ntiles) continue;
-          const uint4 z = make_uint4(0, 0, 0, 0);
-          const v8i bop = fp8_operand(lo_ok ? hd.BL[n][s] : z, hi_ok ? hd.BH[n][s] : z);
-          const int sb = sc_ok ? static_cast<int>((hd.SB[n][s] >> (8 * grp)) & 0xffu) : 127;
-          o[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fp4_operand(av), bop, o[n], 4, 0, 0, sa, 0, sb);
-        }
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        const v8i bop = fp8_operand(lo_ok ? op.bl[s] : z, hi_ok ? op.bh[s] : z);
+        const int sb = sc_ok ? static_cast<int>((op.bs[s] >> (8 * grp)) & 0xffu) : 127;
+        o = mfma_fp4_fp8(fp4_operand(op.a[s]), bop, o, static_cast<int>((op.as >> (8 * s)) & 0xffu), sb);
       }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const int t = hd.gi.cc * NT + n;
-        if (t >= hd.gi.ntiles) continue;
-        const int pair = column_pair(m, lb, hd.gi, t * 16 + (l & 15));
-        if (pair < 0) continue;
-        const int d = rt2 * 16 + 4 * grp;
-        const uint2 v = make_uint2(to_bf16_bits(o[n][0]) | (to_bf16_bits(o[n][1]) << 16),
-                                   to_bf16_bits(o[n][2]) | (to_bf16_bits(o[n][3]) << 16));
-        *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(pair) * a.D + d) = v;
+      mfma_settle(o);
+      if (orow >= 0) {
+        const int d = static_cast<int>(meta.z) * 16 + 4 * grp;
+        const uint2 v = make_uint2(to_bf16_bits(o[0]) | (to_bf16_bits(o[1]) << 16),
+                                   to_bf16_bits(o[2]) | (to_bf16_bits(o[3]) << 16));
+        *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(orow) + d) = v;
       }
     }
+    issue_next(kc + R);  // into the slot just consumed
   }
+  if (l == 0) lds_st4(sy + kSyncProg + 4 * w, 0x7fffffffu);  // done with every FC2 chunk
   // drain the dummy items before the workgroup ends
   wait_vm<0>();
-  if (threadIdx.x == 0)
-    for (int q = blockIdx.x; q < kMaxGrid; q += gridDim.x) a.calls[q] = gen + 1;
 }
 
 using ExpertsFn = void (*)(ExpArgs);
 
-template <int NT>
+template <int R>
 ExpertsFn pick_ns2(int ns2) {
-  if (ns2 == 1) return experts_kernel<NT, 1>;
-  if (ns2 == 2) return experts_kernel<NT, 2>;
-  if (ns2 == 3) return experts_kernel<NT, 3>;
-  return experts_kernel<NT, 4>;
+  if (ns2 == 1) return experts_kernel<1, 1, R>;
+  if (ns2 == 2) return experts_kernel<1, 2, R>;
+  if (ns2 == 3) return experts_kernel<1, 3, R>;
+  return experts_kernel<1, 4, R>;
 }
 
-// Kernel variants: NT column tiles per weight pass x NS2 = ceil(I/128) FC2 K steps.
-ExpertsFn pick_kernel(int nt, int ns2) { return nt == 1 ? pick_ns2<1>(ns2) : pick_ns2<2>(ns2); }
+// Kernel variants: NS2 = ceil(I/128) FC2 K steps x ring depth R (4, else what fits).
+ExpertsFn pick_kernel(int ns2, int R) { return R >= 4 ? pick_ns2<4>(ns2) : (R == 3 ? pick_ns2<3>(ns2) : pick_ns2<2>(ns2)); }
+
+// LDS bytes of the variant with ring depth R.
+size_t lds_for(int R, int g_cap, int u_cap, int IP) {
+  return R >= 4 ? lds_bytes<1, 4>(g_cap, u_cap, IP)
+                : (R == 3 ? lds_bytes<1, 3>(g_cap, u_cap, IP) : lds_bytes<1, 2>(g_cap, u_cap, IP));
+}
 
 // ------------------------------------------------------------------ host helpers
 bool shape_ok(int64_t E, int64_t D, int64_t I) {
@@ -1290,9 +1524,9 @@ int moe_pack_weights(int32_t E, int32_t D, int32_t I, const void* w13, const voi
                      const void* s2, void* w13p, void* s13p, void* w2p, void* s2p, void* stream) {
   if (!shape_ok(E, D, I) || !w13 || !s13 || !w2 || !s2 || !w13p || !s13p || !w2p || !s2p) return MOE_EINVAL;
   hipStream_t st = as_stream(stream);
-  const int HB = I / 32, NS1 = D / 128, NQ1 = (NS1 + 3) / 4, NS2 = (I + 127) / 128, NQ2 = (NS2 + 3) / 4;
+  const int HB = I / 32, NS1 = D / 128, NS2 = (I + 127) / 128, NQ2 = (NS2 + 3) / 4;
   auto blocks = [](int64_t n) { return static_cast<unsigned>((n + 255) / 256); };
-  const int64_t n1 = static_cast<int64_t>(E) * HB * NS1 * 256, n2 = static_cast<int64_t>(E) * HB * NQ1 * 256;
+  const int64_t n1 = static_cast<int64_t>(E) * HB * NS1 * 256, n2 = static_cast<int64_t>(E) * HB * NS1 * 64;
   const int64_t n3 = static_cast<int64_t>(E) * (D / 16) * NS2 * 64, n4 = static_cast<int64_t>(E) * (D / 16) * NQ2 * 64;
   hipLaunchKernelGGL(pack_w13_codes, dim3(blocks(n1)), dim3(256), 0, st, static_cast<const uint4*>(w13),
                      static_cast<uint4*>(w13p), E, D, I);
@@ -1367,8 +1601,8 @@ int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const 
   moe_run_opts_t o;
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
-  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || o.col_tiles < 0 ||
-      (o.col_tiles != 0 && o.col_tiles != 1 && o.col_tiles != 2) ||
+  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 1) ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
     return MOE_EINVAL;
   if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
@@ -1377,15 +1611,18 @@ int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const 
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
   if (B_cap < B) return MOE_ENOSPACE;
   const WsLayout L = ws_layout(E, D, I, topk, B_cap);
-  const int nt = o.col_tiles ? o.col_tiles : auto_col_tiles(B);
-  if (nt > L.nt_cap) return MOE_ENOSPACE;  // the partial-sum slots are sized for nt_cap tiles
   const int64_t U = static_cast<int64_t>(B) * topk;
   const int g_cap = static_cast<int>(U < E ? U : E);
   const int64_t u_bound = g_cap + (U + 7) / 8;
   const int u_cap = static_cast<int>(U < u_bound ? U : u_bound);
-  const size_t lds = nt == 1 ? lds_bytes<1>(g_cap, u_cap) : lds_bytes<2>(g_cap, u_cap);
+  const int IP = (I + 127) / 128 * 128;
+  // the deepest ring that fits next to the unit table
+  int R = o.ring ? o.ring : 4;
+  if (!o.ring)
+    while (R > 2 && lds_for(R, g_cap, u_cap, IP) > static_cast<size_t>(device_lds_limit())) --R;
+  const size_t lds = lds_for(R, g_cap, u_cap, IP);
   if (lds > static_cast<size_t>(device_lds_limit())) return MOE_EINVAL;  // unit table too large for LDS
-  const ExpertsFn fn = pick_kernel(nt, (I + 127) / 128);
+  const ExpertsFn fn = pick_kernel((I + 127) / 128, R);
   if (!prepare_kernel(fn, lds)) return MOE_EHIP;
   const int cap = resident_grid(fn, lds);
   if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
@@ -1413,7 +1650,6 @@ int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const 
   a.I = I;
   a.HB = I / 32;
   a.NS1 = D / 128;
-  a.NQ1 = (a.NS1 + 3) / 4;
   a.IP = (I + 127) / 128 * 128;
   a.g_cap = g_cap;
   a.u_cap = u_cap;

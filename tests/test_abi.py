@@ -80,9 +80,15 @@ def test_host_side_argument_errors(m):
     o.col_tiles, o.hidden_rule = 0, 5
     assert run(1, 4, big, big, big) == m._lib.MOE_EINVAL
     o.hidden_rule = 0
-    o.col_tiles = 2     # a workspace sized for one token holds partial sums for one tile only
+    o.col_tiles = 2     # one 16-column tile per weight pass is the only width
+    assert run(1, 4, big, big, big) == m._lib.MOE_EINVAL
+    o.col_tiles = 1
+    for bad_ring in (1, 5, -1):
+        o.ring = bad_ring
+        assert run(1, 4, big, big, big) == m._lib.MOE_EINVAL
+    o.ring = 0
     ws1 = m.moe_workspace_bytes(16, 512, 128, 1, 4)
-    assert run(1, 4, big, ws1, big) == m._lib.MOE_ENOSPACE
+    assert run(2, 4, big, ws1, big) == m._lib.MOE_ENOSPACE          # workspace sized for one token
     bad = m.moe_weights_t(16, 512, 100, 0x1000, 0x1000, 0x1000, 0x1000)
     assert run(1, 4, big, big, big, m.moe_run_opts_t(), bad) == m._lib.MOE_EINVAL
     assert L.moe_pack_weights(16, 512, 128, None, fake, fake, fake, fake, fake, fake, fake, None) == m._lib.MOE_EINVAL

@@ -210,22 +210,23 @@ SMALL = [
 ]
 
 
-# (col_tiles, grid): the default; one tile per weight pass with a small grid (long
-# slices: whole hidden blocks in one workgroup); multi-tile passes; grids that split
-# hidden blocks over many workgroups (last-arriver reductions).
-VARIANTS = [(0, 0), (1, 7), (2, 0), (2, 200), (1, 200), (2, 1)]
+# (grid, ring): the default (one workgroup per CU, the deepest ring); a single
+# workgroup (every FC2 chunk goes through its two hidden buffers in turn); small grids
+# (long slices, whole hidden blocks in one workgroup); grids that split hidden blocks
+# over many workgroups (finisher + contributors); shallower weight rings.
+VARIANTS = [(0, 0), (1, 0), (7, 2), (33, 3), (200, 0), (0, 2)]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-@pytest.mark.parametrize("col_tiles,grid", VARIANTS)
-def test_experts_small_shapes(lib, case, col_tiles, grid):
+@pytest.mark.parametrize("grid,ring", VARIANTS)
+def test_experts_small_shapes(lib, case, grid, ring):
     name, B, E, K, D, I, routing = case
-    log(f"experts small {name} col_tiles={col_tiles} grid={grid}")
+    log(f"experts small {name} grid={grid} ring={ring}")
     d = workloads.generate(workloads.custom(name, B=B, E=E, K=K, D=D, I=I, routing=routing, seed=11))
     layer = _layer(lib, d, B_max=max(B, 40))
-    got, hc, hs = _run(layer, d, col_tiles=col_tiles, grid=grid)
+    got, hc, hs = _run(layer, d, grid=grid, ring=ring)
     ref = _oracle(d)
-    _check_all(d, got, hc, hs, ref, what=f"{name}/{col_tiles}/{grid}")
+    _check_all(d, got, hc, hs, ref, what=f"{name}/{grid}/{ring}")
 
 
 def test_everybody_on_one_expert(lib):
@@ -282,10 +283,10 @@ def test_routes_independent_of_batch(lib):
     log("route independence")
     d = workloads.generate(workloads.custom("indep", B=12, E=5, K=2, D=1024, I=128, seed=6))
     layer = _layer(lib, d)
-    full, _, _ = _run(layer, d, col_tiles=1, grid=1)
+    full, _, _ = _run(layer, d, grid=1)
     for t in (0, 5, 11):
         d1 = dict(d)
         d1["x"], d1["ids"] = d["x"][t:t + 1], d["ids"][t:t + 1]
         d1["workload"] = workloads.custom("one", B=1, E=5, K=2, D=1024, I=128)
-        one, _, _ = _run(layer, d1, col_tiles=1, grid=1)
+        one, _, _ = _run(layer, d1, grid=1)
         assert np.array_equal(one, full[t * 2:(t + 1) * 2])
