@@ -445,6 +445,9 @@ struct ExpArgs {
   uint8_t* dump_codes;
   uint8_t* dump_scales;
   int D, I, HB, NS1, IP, K, floor_rule;
+  int NSP;  // FC1 items per hidden block: pairs of 128-wide K steps (NS1 / 2)
+  uint32_t plan_bytes;  // bytes of the plan (x codes, then x scales)
+  int U2;   // FC2 items per chunk: groups of T2 16-row output tiles (D / 16 / T2)
   int g_cap, u_cap;  // LDS capacity of the group list and the unit rows
 };
 
@@ -532,6 +535,20 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_off) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __builtin_amdgcn_global_load_lds(g, (lds_void*)(smem + lds_off), 4, 0, 0);
 }
+// DMA through a buffer resource: lanes whose offset lies outside the buffer write zeros
+// and read no memory (a padded column, or a pad that only keeps the DMA count fixed).
+constexpr uint32_t kOutside = 0x80000000u;
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + lds_off), 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + lds_off), 4, voff, 0, 0, 0);
+}
+// The wave's index in its workgroup, as a scalar (uniform) value: derived from
+// threadIdx.x the compiler would keep it, and everything computed from it, per lane.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)); }
 __device__ __forceinline__ uint32_t lds_base() {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   return static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void*)smem));
@@ -563,8 +580,8 @@ __device__ __forceinline__ void lds_wait(uint32_t addr, int want, int32_t* err) 
 template <int NT, int R_>
 struct Geo {
   static constexpr int R = R_;                               // items in flight per wave
-  static constexpr int SLOT = 4096 + 256 + 2048 + 256;     // the FC1 item (the larger kind)
-  static constexpr int L = 8;                                // DMA instructions per item
+  static constexpr int SLOT = 13312;                        // the FC1 item (the larger kind)
+  static constexpr int L = 16;                               // DMA instructions per item
   static constexpr int VM = (R - 1) * L;                     // vmcnt that completes the oldest of R items
   static constexpr int RED = 2 * kStream * NT * 4096;  // two hand-over slots per wave
 };
@@ -761,8 +778,9 @@ __device__ __forceinline__ void hidden_epilogue(const ExpArgs& a, const v4f (&to
 // units of A, FC2 units of B (experts page, ExpertsKernel.partition: FC1(A), FC1(B),
 // FC2(A), FC2(B)), so that a hidden block is needed only well after the slices that
 // produce it ran, and the FC1->FC2 dependency costs no waiting except at the very end.
-// An FC1 step is 64 weight rows (gate rows 32j..32j+31 and the matching up rows) x 128
-// K of hidden block j of a chunk; an FC2 unit is 16 output rows x I of a chunk.
+// An FC1 item is 64 weight rows (gate rows 32j..32j+31 and the matching up rows) x 256
+// K (two 128-wide steps) of hidden block j of a chunk; an FC2 item is T2 tiles of 16
+// output rows x I of a chunk.
 // Global FC1 block numbers run over half A, then half B (chunk * HB + j).
 
 // floor(n / d) for 0 <= n < 2^52, d >= 1: the rounded double quotient is within one.
@@ -784,15 +802,15 @@ struct Slice {
 __device__ __forceinline__ Slice make_slice(const ExpArgs& a, int n_chunks, int h) {
   const int cA = (n_chunks + 1) / 2;
   const int c_lo = (h & 1) ? cA : 0, c_hi = (h & 1) ? n_chunks : cA;
-  const int per_chunk = h < 2 ? a.HB : a.D / 16;
-  const int per = h < 2 ? a.HB * a.NS1 : a.D / 16;
+  const int per_chunk = h < 2 ? a.HB : a.U2;
+  const int per = h < 2 ? a.HB * a.NSP : a.U2;
   const int G = static_cast<int>(gridDim.x), p = static_cast<int>(blockIdx.x);
   Slice s;
   s.T = (c_hi - c_lo) * per;
   s.base = c_lo * per_chunk;
   s.P = s.T < G ? s.T : G;
-  s.lo = p < s.P ? div_floor(static_cast<int64_t>(p) * s.T, s.P) : 0;
-  s.hi = p < s.P ? div_floor(static_cast<int64_t>(p + 1) * s.T, s.P) : 0;
+  s.lo = __builtin_amdgcn_readfirstlane(p < s.P ? div_floor(static_cast<int64_t>(p) * s.T, s.P) : 0);
+  s.hi = __builtin_amdgcn_readfirstlane(p < s.P ? div_floor(static_cast<int64_t>(p + 1) * s.T, s.P) : 0);
   return s;
 }
 
@@ -802,8 +820,8 @@ __device__ __forceinline__ Slice make_slice(const ExpArgs& a, int n_chunks, int 
 struct Cursor {
   int h;              // list 0..3; 4 = done; -1 = not started
   int lo, hi, base;   // the list's slice
-  int b;              // FC1: block of the list; FC2: unit of the list
-  int s, s_hi;        // FC1: step in the block, end of the slice in the block
+  int b;              // FC1: block of the list; FC2: item of the list
+  int s, s_hi;        // FC1: step pair in the block, end of the slice in the block
   int gidx;           // global block / unit of the item
   int chunk, j;       // its chunk, and hidden block (FC1) / output tile (FC2) in the chunk
   int seq0, cfirst;   // FC2: index of the list's first chunk in the workgroup's chunk sequence
@@ -811,27 +829,27 @@ struct Cursor {
   int xrow, xsrow;    // FC1, per lane: offsets of its column's x codes (+ its K quarter) and scales
 };
 
-// Per lane: the x row of the column the lane holds in the chunk (group gi, tile gi.cc);
-// padded columns read row 0 (their results are never stored).
+// Per lane: plan offsets of the x codes (+ the lane's K quarter) and x scales of the
+// column the lane holds in the chunk (group gi, tile gi.cc); -1 for a padded column,
+// whose loads then fall outside the plan buffer and bring zeros without touching memory.
 __device__ __forceinline__ void x_rows(const ExpArgs& a, const LdsMap& m, uint32_t lb, const GroupInfo& gi,
                                        int& xrow, int& xsrow) {
   const int l = threadIdx.x & 63;
   const int pair = column_pair(m, lb, gi, gi.cc * 16 + (l & 15));
   const int t = pair >= 0 ? pair / a.K : 0;
-  xrow = t * a.D + 16 * (l >> 4);
-  xsrow = t * (a.D / 32);
+  xrow = pair >= 0 ? t * a.D + 16 * (l >> 4) : -1;
+  xsrow = pair >= 0 ? static_cast<int>(a.plan_bytes / 33u * 32u) + t * (a.D / 32) : -1;
 }
 
 // Chunks that the workgroup's FC2 slice S spans: [first, first + count).
 __device__ __forceinline__ int fc2_span(const ExpArgs& a, const Slice& S, int& first) {
-  const int TPE = a.D / 16;
-  first = (S.base + S.lo) / TPE;
-  return S.hi > S.lo ? (S.base + S.hi - 1) / TPE - first + 1 : 0;
+  first = (S.base + S.lo) / a.U2;
+  return S.hi > S.lo ? (S.base + S.hi - 1) / a.U2 - first + 1 : 0;
 }
 
 __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
                                             int n_chunks, Cursor& c) {
-  const int w = threadIdx.x >> 6;
+  const int w = wave_id();
   if (c.h < 2) {
     c.s += 4;
     if (c.s < c.s_hi) return;  // same block
@@ -842,10 +860,10 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
   bool fresh = false;
   for (;;) {
     if (c.h >= 0 && c.h < 2) {
-      const int bs = c.b * a.NS1;
+      const int bs = c.b * a.NSP;
       if (bs < c.hi) {
         const int s_lo = c.lo > bs ? c.lo - bs : 0;
-        const int s_hi = c.hi - bs < a.NS1 ? c.hi - bs : a.NS1;
+        const int s_hi = c.hi - bs < a.NSP ? c.hi - bs : a.NSP;
         if (s_hi - s_lo > w) {
           c.s = s_lo + w;
           c.s_hi = s_hi;
@@ -866,7 +884,7 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
     c.lo = sl.lo;
     c.hi = sl.hi;
     c.base = sl.base;
-    c.b = c.h < 2 ? c.lo / a.NS1 : c.lo + w;
+    c.b = c.h < 2 ? c.lo / a.NSP : c.lo + w;
     if (c.h >= 2) {
       fc2_span(a, sl, c.cfirst);
       int f2;
@@ -874,7 +892,7 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
     }
     fresh = true;
   }
-  const int per_chunk = c.h < 2 ? a.HB : a.D / 16;
+  const int per_chunk = c.h < 2 ? a.HB : a.U2;
   const int gidx = c.base + c.b;
   bool moved = fresh;
   if (fresh) {
@@ -903,14 +921,22 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
 }
 
 // ------------------------------------------------------------ the item stream
-// A wave's item k lives in ring slot k % R of the wave.  FC1 item: [A: four 1 KB FP4 row
-// tiles][A scales: one word per lane][x: the 2 KB FP8 B operand][x scales: one word per
-// lane].  FC2 item: [A: NS2 1 KB FP4 tiles][A scales: one word per lane].  Every item
-// issues the same number L of DMA instructions (FC2 items and the dummies past the end
-// pad with redundant word loads into unused bytes of their slot), so "the oldest of R
-// items has landed" is always s_waitcnt vmcnt((R-1)*L).  The item's 16-byte record goes
-// to LDS when it is issued.
-constexpr uint32_t kSlotAS = 4096, kSlotX = 4352, kSlotXS = 6400, kSlotPad = 4352;
+// A wave's item k lives in ring slot k % R of the wave.  FC1 item (two K steps s0, s0+1
+// of one hidden block): [A: 2 x four 1 KB FP4 row tiles][A scales: 2 x one word per
+// lane][x: 2 x the 2 KB FP8 B operand][x scales: 2 x one word per lane].  FC2 item (T2
+// output tiles): [A: T2 x NS2 1 KB FP4 tiles] ... [A scales: T2 x one word per lane].
+// Every item issues the same number L of DMA instructions (FC2 items and the dummies
+// past the end pad with redundant word loads into unused bytes of their slot), so "the
+// oldest of R items has landed" is always s_waitcnt vmcnt((R-1)*L).  The item's 16-byte
+// record goes to LDS when it is issued.
+constexpr uint32_t kSlotAS = 8192, kSlotX = 8704, kSlotXS = 12800, kSlotPad = 8704;
+
+// FC2 output tiles per item, so that an FC2 item carries about as many weight bytes as
+// an FC1 item.
+template <int NS2>
+struct Fc2Tiles {
+  static constexpr int T2 = NS2 == 1 ? 8 : (NS2 == 2 ? 4 : 2);
+};
 
 __device__ __forceinline__ void lds_st16_async(uint32_t addr, uint4 v) {
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -919,127 +945,248 @@ __device__ __forceinline__ void lds_st16_async(uint32_t addr, uint4 v) {
 }
 
 template <int NS2, int R>
-__device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, uint32_t lb, const Cursor& c, int k) {
+__device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, uint32_t lb, const Cursor& c, int k,
+                                           __amdgpu_buffer_rsrc_t xr) {
   using G = Geo<1, R>;
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int T2 = Fc2Tiles<NS2>::T2;
+  const int l = threadIdx.x & 63, w = wave_id();
   const int slot = k % R;
   const uint32_t so = m.ring + (w * R + slot) * G::SLOT;  // offset from the LDS base
   uint4 meta = make_uint4(2u, 0u, 0u, 0u);                   // 2: dummy
   int done = 0;
   if (c.h < 2) {
-    const int64_t step = static_cast<int64_t>(c.gi.e * a.HB + c.j) * a.NS1 + c.s;
+    const int s0 = 2 * c.s;
+    const int64_t step = static_cast<int64_t>(c.gi.e * a.HB + c.j) * a.NS1 + s0;
     const uint8_t* wb = a.w13p + step * 4096 + l * 16;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) dma16(wb + rt * 1024, so + rt * 1024);
-    dma4(a.s13p + step * 256 + l * 4, so + kSlotAS);
-    const uint8_t* xr = a.xcodes + c.xrow + c.s * 128;
-    dma16(xr, so + kSlotX);
-    dma16(xr + 64, so + kSlotX + 1024);
-    dma4(a.xscales + c.xsrow + 4 * c.s, so + kSlotXS);
+    for (int i = 0; i < 8; ++i) dma16(wb + i * 1024, so + i * 1024);
+    const uint8_t* sb = a.s13p + step * 256 + l * 4;
+    dma4(sb, so + kSlotAS);
+    dma4(sb + 256, so + kSlotAS + 256);
+    const bool live = c.xrow >= 0;
+    const uint32_t xo = live ? static_cast<uint32_t>(c.xrow + s0 * 128) : kOutside;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bdma16(xr, live ? xo + i * 64 : kOutside, so + kSlotX + i * 1024);
+    const uint32_t xso = live ? static_cast<uint32_t>(c.xsrow + 4 * s0) : kOutside;
+    bdma4(xr, xso, so + kSlotXS);
+    bdma4(xr, live ? xso + 4 : kOutside, so + kSlotXS + 256);
     meta = make_uint4(0u, static_cast<uint32_t>(c.gidx), 0u, 0u);
     done = G::L;
   } else if (c.h < 4) {
-    const int64_t tile = static_cast<int64_t>(c.gi.e) * (a.D / 16) + c.j;
+    const int64_t tile = static_cast<int64_t>(c.gi.e) * (a.D / 16) + c.j * T2;
     const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
 #pragma unroll
-    for (int s = 0; s < NS2; ++s) dma16(wb + s * 1024, so + s * 1024);
-    dma4(a.s2p + tile * 256 + l * 4, so + kSlotAS);
+    for (int i = 0; i < T2 * NS2; ++i) dma16(wb + i * 1024, so + i * 1024);
+    const uint8_t* sb = a.s2p + tile * 256 + l * 4;
+#pragma unroll
+    for (int t = 0; t < T2; ++t) dma4(sb + t * 256, so + kSlotAS + t * 256);
     meta = make_uint4(1u, static_cast<uint32_t>(c.chunk), static_cast<uint32_t>(c.j),
                       static_cast<uint32_t>(c.seq0 + c.chunk - c.cfirst));
-    done = NS2 + 1;
+    done = T2 * NS2 + T2;
   }
-  for (int i = done; i < G::L; ++i) dma4(a.s2p + l * 4, so + kSlotPad + i * 256);
+  for (int i = done; i < G::L; ++i) bdma4(xr, kOutside, so + kSlotPad + i * 256);
   if (l == 0) lds_st16_async(lb + m.meta + (w * R + slot) * 16, meta);
 }
 
-// FC2 operands of one item, read with a single LDS wait: per K step s the A tile
-// (FP4, 16 output rows, at pa + 1024 s) and the hidden's B operand halves (pb + 128 s,
-// + 64) and scale word (ps + 4 s); the A scale word (pq + 4096).
+// ------------------------------------------------------------ item operand reads
+// Every read of an item's operands is one asm block with a single LDS wait (the DMA
+// stream must not be drained by the compiler's conservative waits).
+
+// FC1 item: A = two K steps x four row tiles (a[step*4 + rt] at pa + 4096 step + 1024 rt),
+// A scale words (as[step] at pq + 8192 + 256 step), x halves (x[step*2 + half] at
+// pa + 8704 + 2048 step + 1024 half) and x scale words (xs[step] at pq + 12800 + 256 step).
+struct Fc1Ops {
+  uint4 a[8], x[4];
+  uint32_t as[2], xs[2];
+};
+__device__ __forceinline__ void fc1_read(uint32_t pa, uint32_t pq, Fc1Ops& o) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:0\n\t"
+      "ds_read_b128 %1, %16 offset:1024\n\t"
+      "ds_read_b128 %2, %16 offset:2048\n\t"
+      "ds_read_b128 %3, %16 offset:3072\n\t"
+      "ds_read_b128 %4, %16 offset:4096\n\t"
+      "ds_read_b128 %5, %16 offset:5120\n\t"
+      "ds_read_b128 %6, %16 offset:6144\n\t"
+      "ds_read_b128 %7, %16 offset:7168\n\t"
+      "ds_read_b32 %12, %17 offset:8192\n\t"
+      "ds_read_b32 %13, %17 offset:8448\n\t"
+      "ds_read_b128 %8, %16 offset:8704\n\t"
+      "ds_read_b128 %9, %16 offset:9728\n\t"
+      "ds_read_b128 %10, %16 offset:10752\n\t"
+      "ds_read_b128 %11, %16 offset:11776\n\t"
+      "ds_read_b32 %14, %17 offset:12800\n\t"
+      "ds_read_b32 %15, %17 offset:13056\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]), "=&v"(o.a[7]), "=&v"(o.x[0]), "=&v"(o.x[1]), "=&v"(o.x[2]), "=&v"(o.x[3]), "=&v"(o.as[0]), "=&v"(o.as[1]), "=&v"(o.xs[0]), "=&v"(o.xs[1])
+      : "v"(pa), "v"(pq)
+      : "memory");
+}
+
+// FC2: the hidden's B operand of a chunk column (per K step s: halves at pb + 128 s and
+// + 64, scale word at ps + 4 s), read once per item.
 template <int NS2>
-struct Fc2Ops {
-  uint4 a[NS2], bl[NS2], bh[NS2];
-  uint32_t bs[NS2], as;
+struct HidOps {
+  uint4 bl[NS2], bh[NS2];
+  uint32_t bs[NS2];
 };
 template <int NS2>
-__device__ __forceinline__ void fc2_read(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<NS2>& o);
+__device__ __forceinline__ void hid_read(uint32_t pb, uint32_t ps, HidOps<NS2>& o);
+// FC2 item: T2 output tiles of NS2 K steps each (a[t*NS2 + s] at pa + 1024 (t NS2 + s)),
+// one A scale word per tile (as[t] at pq + 8192 + 256 t).
+template <int NS2, int T2>
+struct Fc2Ops {
+  uint4 a[T2 * NS2];
+  uint32_t as[T2];
+};
+template <int NS2, int T2>
+__device__ __forceinline__ void fc2_read(uint32_t pa, uint32_t pq, Fc2Ops<NS2, T2>& o);
 
 template <>
-__device__ __forceinline__ void fc2_read<1>(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<1>& o) {
+__device__ __forceinline__ void hid_read<1>(uint32_t pb, uint32_t ps, HidOps<1>& o) {
   asm volatile(
-      "ds_read_b128 %0, %5 offset:0\n\t"
-      "ds_read_b32 %4, %6 offset:4096\n\t"
-      "ds_read_b128 %1, %7 offset:0\n\t"
-      "ds_read_b128 %2, %7 offset:64\n\t"
-      "ds_read_b32 %3, %8 offset:0\n\t"
+      "ds_read_b128 %0, %3 offset:0\n\t"
+      "ds_read_b128 %1, %3 offset:64\n\t"
+      "ds_read_b32 %2, %4 offset:0\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o.a[0]), "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.as)
-      : "v"(pa), "v"(pq), "v"(pb), "v"(ps)
+      : "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0])
+      : "v"(pb), "v"(ps)
       : "memory");
 }
 
 template <>
-__device__ __forceinline__ void fc2_read<2>(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<2>& o) {
+__device__ __forceinline__ void hid_read<2>(uint32_t pb, uint32_t ps, HidOps<2>& o) {
+  asm volatile(
+      "ds_read_b128 %0, %6 offset:0\n\t"
+      "ds_read_b128 %1, %6 offset:64\n\t"
+      "ds_read_b32 %2, %7 offset:0\n\t"
+      "ds_read_b128 %3, %6 offset:128\n\t"
+      "ds_read_b128 %4, %6 offset:192\n\t"
+      "ds_read_b32 %5, %7 offset:4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1])
+      : "v"(pb), "v"(ps)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void hid_read<3>(uint32_t pb, uint32_t ps, HidOps<3>& o) {
   asm volatile(
       "ds_read_b128 %0, %9 offset:0\n\t"
-      "ds_read_b128 %1, %9 offset:1024\n\t"
-      "ds_read_b32 %8, %10 offset:4096\n\t"
-      "ds_read_b128 %2, %11 offset:0\n\t"
-      "ds_read_b128 %3, %11 offset:64\n\t"
-      "ds_read_b32 %4, %12 offset:0\n\t"
-      "ds_read_b128 %5, %11 offset:128\n\t"
-      "ds_read_b128 %6, %11 offset:192\n\t"
-      "ds_read_b32 %7, %12 offset:4\n\t"
+      "ds_read_b128 %1, %9 offset:64\n\t"
+      "ds_read_b32 %2, %10 offset:0\n\t"
+      "ds_read_b128 %3, %9 offset:128\n\t"
+      "ds_read_b128 %4, %9 offset:192\n\t"
+      "ds_read_b32 %5, %10 offset:4\n\t"
+      "ds_read_b128 %6, %9 offset:256\n\t"
+      "ds_read_b128 %7, %9 offset:320\n\t"
+      "ds_read_b32 %8, %10 offset:8\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1]), "=&v"(o.as)
-      : "v"(pa), "v"(pq), "v"(pb), "v"(ps)
+      : "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1]), "=&v"(o.bl[2]), "=&v"(o.bh[2]), "=&v"(o.bs[2])
+      : "v"(pb), "v"(ps)
       : "memory");
 }
 
 template <>
-__device__ __forceinline__ void fc2_read<3>(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<3>& o) {
+__device__ __forceinline__ void hid_read<4>(uint32_t pb, uint32_t ps, HidOps<4>& o) {
   asm volatile(
-      "ds_read_b128 %0, %13 offset:0\n\t"
-      "ds_read_b128 %1, %13 offset:1024\n\t"
-      "ds_read_b128 %2, %13 offset:2048\n\t"
-      "ds_read_b32 %12, %14 offset:4096\n\t"
-      "ds_read_b128 %3, %15 offset:0\n\t"
-      "ds_read_b128 %4, %15 offset:64\n\t"
-      "ds_read_b32 %5, %16 offset:0\n\t"
-      "ds_read_b128 %6, %15 offset:128\n\t"
-      "ds_read_b128 %7, %15 offset:192\n\t"
-      "ds_read_b32 %8, %16 offset:4\n\t"
-      "ds_read_b128 %9, %15 offset:256\n\t"
-      "ds_read_b128 %10, %15 offset:320\n\t"
-      "ds_read_b32 %11, %16 offset:8\n\t"
+      "ds_read_b128 %0, %12 offset:0\n\t"
+      "ds_read_b128 %1, %12 offset:64\n\t"
+      "ds_read_b32 %2, %13 offset:0\n\t"
+      "ds_read_b128 %3, %12 offset:128\n\t"
+      "ds_read_b128 %4, %12 offset:192\n\t"
+      "ds_read_b32 %5, %13 offset:4\n\t"
+      "ds_read_b128 %6, %12 offset:256\n\t"
+      "ds_read_b128 %7, %12 offset:320\n\t"
+      "ds_read_b32 %8, %13 offset:8\n\t"
+      "ds_read_b128 %9, %12 offset:384\n\t"
+      "ds_read_b128 %10, %12 offset:448\n\t"
+      "ds_read_b32 %11, %13 offset:12\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1]), "=&v"(o.bl[2]), "=&v"(o.bh[2]), "=&v"(o.bs[2]), "=&v"(o.as)
-      : "v"(pa), "v"(pq), "v"(pb), "v"(ps)
+      : "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1]), "=&v"(o.bl[2]), "=&v"(o.bh[2]), "=&v"(o.bs[2]), "=&v"(o.bl[3]), "=&v"(o.bh[3]), "=&v"(o.bs[3])
+      : "v"(pb), "v"(ps)
       : "memory");
 }
 
 template <>
-__device__ __forceinline__ void fc2_read<4>(uint32_t pa, uint32_t pq, uint32_t pb, uint32_t ps, Fc2Ops<4>& o) {
+__device__ __forceinline__ void fc2_read<1, 8>(uint32_t pa, uint32_t pq, Fc2Ops<1, 8>& o) {
   asm volatile(
-      "ds_read_b128 %0, %17 offset:0\n\t"
-      "ds_read_b128 %1, %17 offset:1024\n\t"
-      "ds_read_b128 %2, %17 offset:2048\n\t"
-      "ds_read_b128 %3, %17 offset:3072\n\t"
-      "ds_read_b32 %16, %18 offset:4096\n\t"
-      "ds_read_b128 %4, %19 offset:0\n\t"
-      "ds_read_b128 %5, %19 offset:64\n\t"
-      "ds_read_b32 %6, %20 offset:0\n\t"
-      "ds_read_b128 %7, %19 offset:128\n\t"
-      "ds_read_b128 %8, %19 offset:192\n\t"
-      "ds_read_b32 %9, %20 offset:4\n\t"
-      "ds_read_b128 %10, %19 offset:256\n\t"
-      "ds_read_b128 %11, %19 offset:320\n\t"
-      "ds_read_b32 %12, %20 offset:8\n\t"
-      "ds_read_b128 %13, %19 offset:384\n\t"
-      "ds_read_b128 %14, %19 offset:448\n\t"
-      "ds_read_b32 %15, %20 offset:12\n\t"
+      "ds_read_b128 %0, %16 offset:0\n\t"
+      "ds_read_b128 %1, %16 offset:1024\n\t"
+      "ds_read_b128 %2, %16 offset:2048\n\t"
+      "ds_read_b128 %3, %16 offset:3072\n\t"
+      "ds_read_b128 %4, %16 offset:4096\n\t"
+      "ds_read_b128 %5, %16 offset:5120\n\t"
+      "ds_read_b128 %6, %16 offset:6144\n\t"
+      "ds_read_b128 %7, %16 offset:7168\n\t"
+      "ds_read_b32 %8, %17 offset:8192\n\t"
+      "ds_read_b32 %9, %17 offset:8448\n\t"
+      "ds_read_b32 %10, %17 offset:8704\n\t"
+      "ds_read_b32 %11, %17 offset:8960\n\t"
+      "ds_read_b32 %12, %17 offset:9216\n\t"
+      "ds_read_b32 %13, %17 offset:9472\n\t"
+      "ds_read_b32 %14, %17 offset:9728\n\t"
+      "ds_read_b32 %15, %17 offset:9984\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.bl[0]), "=&v"(o.bh[0]), "=&v"(o.bs[0]), "=&v"(o.bl[1]), "=&v"(o.bh[1]), "=&v"(o.bs[1]), "=&v"(o.bl[2]), "=&v"(o.bh[2]), "=&v"(o.bs[2]), "=&v"(o.bl[3]), "=&v"(o.bh[3]), "=&v"(o.bs[3]), "=&v"(o.as)
-      : "v"(pa), "v"(pq), "v"(pb), "v"(ps)
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]), "=&v"(o.a[7]), "=&v"(o.as[0]), "=&v"(o.as[1]), "=&v"(o.as[2]), "=&v"(o.as[3]), "=&v"(o.as[4]), "=&v"(o.as[5]), "=&v"(o.as[6]), "=&v"(o.as[7])
+      : "v"(pa), "v"(pq)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fc2_read<2, 4>(uint32_t pa, uint32_t pq, Fc2Ops<2, 4>& o) {
+  asm volatile(
+      "ds_read_b128 %0, %12 offset:0\n\t"
+      "ds_read_b128 %1, %12 offset:1024\n\t"
+      "ds_read_b128 %2, %12 offset:2048\n\t"
+      "ds_read_b128 %3, %12 offset:3072\n\t"
+      "ds_read_b128 %4, %12 offset:4096\n\t"
+      "ds_read_b128 %5, %12 offset:5120\n\t"
+      "ds_read_b128 %6, %12 offset:6144\n\t"
+      "ds_read_b128 %7, %12 offset:7168\n\t"
+      "ds_read_b32 %8, %13 offset:8192\n\t"
+      "ds_read_b32 %9, %13 offset:8448\n\t"
+      "ds_read_b32 %10, %13 offset:8704\n\t"
+      "ds_read_b32 %11, %13 offset:8960\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]), "=&v"(o.a[7]), "=&v"(o.as[0]), "=&v"(o.as[1]), "=&v"(o.as[2]), "=&v"(o.as[3])
+      : "v"(pa), "v"(pq)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fc2_read<3, 2>(uint32_t pa, uint32_t pq, Fc2Ops<3, 2>& o) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:0\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b32 %6, %9 offset:8192\n\t"
+      "ds_read_b32 %7, %9 offset:8448\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.as[0]), "=&v"(o.as[1])
+      : "v"(pa), "v"(pq)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void fc2_read<4, 2>(uint32_t pa, uint32_t pq, Fc2Ops<4, 2>& o) {
+  asm volatile(
+      "ds_read_b128 %0, %10 offset:0\n\t"
+      "ds_read_b128 %1, %10 offset:1024\n\t"
+      "ds_read_b128 %2, %10 offset:2048\n\t"
+      "ds_read_b128 %3, %10 offset:3072\n\t"
+      "ds_read_b128 %4, %10 offset:4096\n\t"
+      "ds_read_b128 %5, %10 offset:5120\n\t"
+      "ds_read_b128 %6, %10 offset:6144\n\t"
+      "ds_read_b128 %7, %10 offset:7168\n\t"
+      "ds_read_b32 %8, %11 offset:8192\n\t"
+      "ds_read_b32 %9, %11 offset:8448\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]), "=&v"(o.a[7]), "=&v"(o.as[0]), "=&v"(o.as[1])
+      : "v"(pa), "v"(pq)
       : "memory");
 }
 
@@ -1057,7 +1204,7 @@ __device__ __forceinline__ void control_block(const ExpArgs& a, const LdsMap& m,
                                               const Slice& li, int half, int lbk, v4f (&acc)[4][NT],
                                               uint32_t gen) {
   const int l = threadIdx.x & 63;
-  const int NS1 = a.NS1, HB = a.HB;
+  const int NS1 = a.NSP, HB = a.HB;  // block length in FC1 items (step pairs)
   const int p = blockIdx.x;
   const int b = li.base + lbk;  // global block
   const int bs = lbk * NS1;
@@ -1202,7 +1349,7 @@ __device__ __forceinline__ void control_hidden(const ExpArgs& a, const LdsMap& m
 template <int NT, int NS2, int R>
 __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   using G = Geo<NT, R>;
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6, grp = l >> 4;
+  const int l = threadIdx.x & 63, w = wave_id(), grp = l >> 4;
   const LdsMap m = lds_map<NT, R>(static_cast<uint32_t>(a.g_cap), static_cast<uint32_t>(a.u_cap),
                                   static_cast<uint32_t>(a.IP));
   const uint32_t lb = lds_base();
@@ -1220,7 +1367,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
     for (int half = 0; half < 2; ++half) {
       const Slice S = make_slice(a, n_chunks, half);
       if (S.hi <= S.lo) continue;
-      for (int lbk = S.lo / a.NS1; lbk <= (S.hi - 1) / a.NS1; ++lbk, ++q) {
+      for (int lbk = S.lo / a.NSP; lbk <= (S.hi - 1) / a.NSP; ++lbk, ++q) {
 #pragma unroll
         for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncSub + 4 * ww, q + 1, a.tbl.hdr + 3);
         // the streaming waves' sums, added in wave order
@@ -1264,7 +1411,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   // FC1 blocks are handed over in the workgroup's order: half A's slice, then B's
   int sub_h = 0, sub_q = 0;
   Slice sub = make_slice(a, n_chunks, 0);
-  int sub_b = sub.lo / a.NS1, sub_last = sub.hi > sub.lo ? (sub.hi - 1) / a.NS1 : sub_b - 1;
+  int sub_b = sub.lo / a.NSP, sub_last = sub.hi > sub.lo ? (sub.hi - 1) / a.NSP : sub_b - 1;
   // Hands the sums of the workgroup's FC1 blocks below global block `upto` to the control
   // wave, in the workgroup's block order (zeros for blocks without steps of this wave).
   auto hand_over = [&](int upto) {
@@ -1286,12 +1433,15 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
         ++sub_b;
       } else if (++sub_h < 2) {
         sub = make_slice(a, n_chunks, 1);
-        sub_b = sub.lo / a.NS1;
-        sub_last = sub.hi > sub.lo ? (sub.hi - 1) / a.NS1 : sub_b - 1;
+        sub_b = sub.lo / a.NSP;
+        sub_last = sub.hi > sub.lo ? (sub.hi - 1) / a.NSP : sub_b - 1;
       }
     }
   };
 
+  // the plan (x codes and scales) as a buffer: padded columns and pads load zeros from outside it
+  const __amdgpu_buffer_rsrc_t xrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.xcodes), static_cast<short>(0), a.plan_bytes, 0x00020000);
   Cursor pc;  // issue cursor, R items ahead of consumption
   pc.h = -1;
   pc.s = pc.s_hi = 0;
@@ -1299,7 +1449,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   cursor_next(a, m, lb, n_groups, n_chunks, pc);
   int n_real = 0;  // real items issued (they precede the dummies)
   auto issue_next = [&](int k) {
-    issue_item<NS2, R>(a, m, lb, pc, k);
+    issue_item<NS2, R>(a, m, lb, pc, k, xrsrc);
     if (pc.h < 4) {
       ++n_real;
       cursor_next(a, m, lb, n_groups, n_chunks, pc);
@@ -1331,32 +1481,23 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
     if (!real) break;
     wait_vm<G::VM>();  // item kc has landed (the R-1 younger items may still be in flight)
     if (type == 0) {
-      uint4 a0, a1, a2, a3, xl, xh;
-      uint32_t saw, sbw;
-      asm volatile(
-          "ds_read_b128 %0, %8\n\t"
-          "ds_read_b128 %1, %8 offset:1024\n\t"
-          "ds_read_b128 %2, %8 offset:2048\n\t"
-          "ds_read_b128 %3, %8 offset:3072\n\t"
-          "ds_read_b32 %4, %9 offset:4096\n\t"
-          "ds_read_b128 %5, %8 offset:4352\n\t"
-          "ds_read_b128 %6, %8 offset:5376\n\t"
-          "ds_read_b32 %7, %9 offset:6400\n\t"
-          "s_waitcnt lgkmcnt(0)"
-          : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(saw), "=&v"(xl), "=&v"(xh), "=&v"(sbw)
-          : "v"(sa_ + l * 16), "v"(sa_ + l * 4)
-          : "memory");
-      const v8i bop = fp8_operand(xl, xh);
-      const int sb = static_cast<int>((sbw >> (8 * grp)) & 0xffu);
-      acc[0] = mfma_fp4_fp8(fp4_operand(a0), bop, acc[0], static_cast<int>(saw & 0xffu), sb);
-      acc[1] = mfma_fp4_fp8(fp4_operand(a1), bop, acc[1], static_cast<int>((saw >> 8) & 0xffu), sb);
-      acc[2] = mfma_fp4_fp8(fp4_operand(a2), bop, acc[2], static_cast<int>((saw >> 16) & 0xffu), sb);
-      acc[3] = mfma_fp4_fp8(fp4_operand(a3), bop, acc[3], static_cast<int>(saw >> 24), sb);
+      Fc1Ops op;
+      fc1_read(sa_ + l * 16, sa_ + l * 4, op);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const v8i bop = fp8_operand(op.x[2 * st], op.x[2 * st + 1]);
+        const int sb = static_cast<int>((op.xs[st] >> (8 * grp)) & 0xffu);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          acc[rt] = mfma_fp4_fp8(fp4_operand(op.a[4 * st + rt]), bop, acc[rt],
+                                 static_cast<int>((op.as[st] >> (8 * rt)) & 0xffu), sb);
+      }
       // this wave's part of the block may be complete: the next item's record tells, so
       // the sums go to the control wave without waiting for the next item's data
       const int ntype = __builtin_amdgcn_readfirstlane(static_cast<int>(nm.x));
       hand_over(ntype == 0 ? __builtin_amdgcn_readfirstlane(static_cast<int>(nm.y)) : 0x7fffffff);
     } else if (type == 1) {
+      constexpr int T2 = Fc2Tiles<NS2>::T2;
       const int seq = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.w));
       if (seq != cur_seq) {
         if (l == 0) lds_st4(sy + kSyncProg + 4 * w, static_cast<uint32_t>(seq));
@@ -1369,25 +1510,40 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
         hbl = hb + col * m.hs + 16 * grp;
         hbs = hb + 16 * m.hs + col * (a.IP / 32);
       }
-      Fc2Ops<NS2> op;
-      fc2_read<NS2>(sa_ + l * 16, sa_ + l * 4, hbl, hbs, op);
-      v4f o = v4f{0.f, 0.f, 0.f, 0.f};
+      HidOps<NS2> hop;
+      hid_read<NS2>(hbl, hbs, hop);
+      Fc2Ops<NS2, T2> op;
+      fc2_read<NS2, T2>(sa_ + l * 16, sa_ + l * 4, op);
+      v8i bop[NS2];
+      int sb[NS2];
 #pragma unroll
       for (int s = 0; s < NS2; ++s) {
         // K-blocks beyond I (I not a multiple of 128) are zero
         const bool lo_ok = 4 * s + (grp >> 1) < a.HB, hi_ok = 4 * s + 2 + (grp >> 1) < a.HB;
         const bool sc_ok = 4 * s + grp < a.HB;
         const uint4 z = make_uint4(0, 0, 0, 0);
-        const v8i bop = fp8_operand(lo_ok ? op.bl[s] : z, hi_ok ? op.bh[s] : z);
-        const int sb = sc_ok ? static_cast<int>((op.bs[s] >> (8 * grp)) & 0xffu) : 127;
-        o = mfma_fp4_fp8(fp4_operand(op.a[s]), bop, o, static_cast<int>((op.as >> (8 * s)) & 0xffu), sb);
+        bop[s] = fp8_operand(lo_ok ? hop.bl[s] : z, hi_ok ? hop.bh[s] : z);
+        sb[s] = sc_ok ? static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu) : 127;
       }
-      mfma_settle(o);
+      v4f o[T2];
+#pragma unroll
+      for (int t = 0; t < T2; ++t) {
+        o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS2; ++s)
+          o[t] = mfma_fp4_fp8(fp4_operand(op.a[t * NS2 + s]), bop[s], o[t],
+                              static_cast<int>((op.as[t] >> (8 * s)) & 0xffu), sb[s]);
+      }
+#pragma unroll
+      for (int t = 0; t < T2; ++t) mfma_settle(o[t]);
       if (orow >= 0) {
-        const int d = static_cast<int>(meta.z) * 16 + 4 * grp;
-        const uint2 v = make_uint2(to_bf16_bits(o[0]) | (to_bf16_bits(o[1]) << 16),
-                                   to_bf16_bits(o[2]) | (to_bf16_bits(o[3]) << 16));
-        *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(orow) + d) = v;
+        const int d0 = static_cast<int>(meta.z) * T2 * 16 + 4 * grp;
+#pragma unroll
+        for (int t = 0; t < T2; ++t) {
+          const uint2 v = make_uint2(to_bf16_bits(o[t][0]) | (to_bf16_bits(o[t][1]) << 16),
+                                     to_bf16_bits(o[t][2]) | (to_bf16_bits(o[t][3]) << 16));
+          *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(orow) + d0 + 16 * t) = v;
+        }
       }
     }
     issue_next(kc + R);  // into the slot just consumed
@@ -1636,6 +1792,7 @@ int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const 
   a.s2p = static_cast<const uint8_t*>(wts->s2);
   a.xcodes = static_cast<const uint8_t*>(plan);
   a.xscales = a.xcodes + static_cast<int64_t>(B) * D;
+  a.plan_bytes = static_cast<uint32_t>(static_cast<int64_t>(B) * D / 32 * 33);
   a.tbl = table_at(static_cast<uint8_t*>(const_cast<void*>(units)), UL);
   a.calls = reinterpret_cast<uint32_t*>(base + L.calls);
   a.arrive = reinterpret_cast<uint32_t*>(base + L.arrive);
@@ -1650,6 +1807,11 @@ int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const 
   a.I = I;
   a.HB = I / 32;
   a.NS1 = D / 128;
+  a.NSP = a.NS1 / 2;
+  {
+    const int ns2 = (I + 127) / 128, t2 = ns2 == 1 ? 8 : (ns2 == 2 ? 4 : 2);
+    a.U2 = D / 16 / t2;
+  }
   a.IP = (I + 127) / 128 * 128;
   a.g_cap = g_cap;
   a.u_cap = u_cap;
