@@ -27,6 +27,42 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+KERNEL_SRC = os.path.join(ROOT, "moe_routed_expert_mx_amd", "csrc", "moe_mx.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "experts_kernel_traffic.json")
+
+
+def kernel_hash() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM-side bytes per experts-kernel launch from the committed rocprofv3 PMC summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or None when there
+    is none for this workload or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else w.get("bytes_per_launch")
+
+
+def copy_calibration(mb: int) -> None:
+    """A plain device copy of `mb` MiB (a torch elementwise kernel), three times: the
+    known-size reference that scales the PMC byte counters."""
+    import torch
+    n = mb << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), file=sys.stderr)
 
 
 def _unique_weight_bytes(ids, w) -> int:
@@ -36,7 +72,7 @@ def _unique_weight_bytes(ids, w) -> int:
     return n * workloads.expert_weight_bytes(w.D, w.I)
 
 
-def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 24, log=print) -> dict:
+def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager: bool = False, log=print) -> dict:
     import numpy as np
     import torch
 
@@ -51,45 +87,53 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 24, log=pr
     x = torch.from_numpy(d["x"]).cuda()
     ids = torch.from_numpy(d["ids"]).cuda()
     out = layer.out_buffer(w.B)
-    G = max(graph_steps // R, 1) * R
+    # steps per graph: the largest divisor of `steps` up to graph_steps, so that exactly
+    # `steps` steps are timed
+    G = max(gs for gs in range(1, min(graph_steps, steps) + 1) if steps % gs == 0)
 
     for i in range(warmup):
         layer.forward(x, ids, out, replica=i % R)
     torch.cuda.synchronize()
 
-    # whole step (plan + units + experts), captured G steps per graph
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(G):
-            layer.forward(x, ids, out, replica=i % R)
-    for _ in range(2):
-        g.replay()
-    torch.cuda.synchronize()
-    reps = max(1, math.ceil(steps / G))
+    reps = steps // G
     stream = torch.cuda.current_stream()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(reps):
-        g.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    step_us = t0.elapsed_time(t1) * 1e3 / (reps * G)
+    g = ge = None
+    if not eager:
+        # whole step (plan + units + experts), captured G steps per graph
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(G):
+                layer.forward(x, ids, out, replica=i % R)
+        # the dominant kernel alone: the experts kernel on the plan/units of the last step
+        ge = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ge):
+            for i in range(G):
+                layer.experts(w.B, out, replica=i % R)
+        for _ in range(2):
+            g.replay()
+            ge.replay()
+        layer.forward(x, ids, out)  # plan and units of this batch for the experts-only graph
+        torch.cuda.synchronize()
 
-    # dominant kernel alone: the experts kernel on the plan/units of the last step
-    ge = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(ge):
-        for i in range(G):
+    def timed(run_all) -> float:
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        run_all()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / (reps * G)
+
+    def steps_eager():
+        for i in range(reps * G):
+            layer.forward(x, ids, out, replica=i % R)
+
+    def experts_eager():
+        for i in range(reps * G):
             layer.experts(w.B, out, replica=i % R)
-    ge.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        ge.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    experts_us = e0.elapsed_time(e1) * 1e3 / (reps * G)
+
+    step_us = timed(steps_eager if eager else (lambda: [g.replay() for _ in range(reps)]))
+    experts_us = timed(experts_eager if eager else (lambda: [ge.replay() for _ in range(reps)]))
 
     uniq = _unique_weight_bytes(d["ids"], w)
     io_bytes = w.B * w.D * 2 + w.B * w.K * 4 + w.B * w.K * w.D * 2  # x, ids, out
@@ -137,7 +181,7 @@ def cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
                        want_hidden=False)
         runs += 1
         el = time.perf_counter() - t_start
-        if el >= budget_s or runs >= 1000:
+        if el >= budget_s:
             break
     per_route_s = el / (runs * n_routes)
     layer_us = per_route_s * R * 1e6
@@ -155,6 +199,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time the other four workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying HIP graphs")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -167,8 +214,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_mb > 0:
+        copy_calibration(args.copy_mb)
     names = workloads.ORDER if args.all else [args.workload]
-    results = {n: measure(n, args.steps, args.warmup) for n in names}
+    results = {n: measure(n, args.steps, args.warmup, eager=args.eager) for n in names}
     main_res = results[args.workload]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_budget)
     line = {
@@ -184,6 +233,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4xfp8->f32",
         "data": "synthetic",
+        "timing": "eager launches" if args.eager else "HIP graph replays",
         "config": {"workload": args.workload, "B": main_res["B"], "E": main_res["E"], "topk": main_res["topk"],
                    "D": main_res["D"], "I": main_res["I"], "parallelism": "single GPU (one TP shard)"},
         "routes_per_s": round(main_res["routes_per_s"], 1),
@@ -196,8 +246,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(main_res["experts_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "avg_us": round(main_res["experts_us"], 3),
+            "alg_bytes": main_res["experts_alg_bytes"],
         },
         "cpu_baseline": cpu,
     }
