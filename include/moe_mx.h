@@ -171,6 +171,20 @@ int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
                     int32_t topk, void* ws_dev, size_t ws_bytes, void* out_dev, size_t out_bytes,
                     void* stream);
 
+/* ------------------------------------------------------------- combine ---- */
+
+/* Weighted top-k combine of the output rows (experts page, ExpertsKernel.finalize, the
+ * arithmetic without the cross-rank multicast):
+ *     out[t, d] = sum over s < topk of weights[t, s] * rows[t*topk + s, d]
+ * accumulated in FP32 with fused multiply-adds in slot order s = 0, 1, ..., rounded
+ * once to BF16 (round to nearest even).
+ *   rows_dev    BF16 [B*topk, D], as written by moe_experts_run (rows_bytes >= B*topk*D*2)
+ *   weights_dev FP32 [B, topk], the routing weights in the caller's top-k order
+ *   out_dev     BF16 [B, D] (out_bytes >= B*D*2); must not overlap rows_dev
+ * D must be a multiple of 8.  Returns MOE_EINVAL / MOE_ENOSPACE as the other calls. */
+int moe_combine(const void* rows_dev, size_t rows_bytes, const float* weights_dev, int32_t B, int32_t topk,
+                int32_t D, void* out_dev, size_t out_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

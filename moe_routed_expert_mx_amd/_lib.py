@@ -54,6 +54,7 @@ def _load():
                                        c.c_int32, P]),
         "moe_experts_run": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_size_t,
                                       c.c_int32, c.c_int32, P, c.c_size_t, P, c.c_size_t, P]),
+        "moe_combine": (c.c_int, [P, c.c_size_t, P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -64,7 +65,7 @@ def _load():
 lib = _load()
 EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_units_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
             "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_units_export",
-            "moe_experts_run")
+            "moe_experts_run", "moe_combine")
 
 
 def status_string(status: int) -> str:
@@ -142,3 +143,11 @@ def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, 
     _check("moe_experts_run", lib.moe_experts_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(plan),
                                                   _ptr(units), _nbytes(units), B, topk, _ptr(ws), _nbytes(ws),
                                                   _ptr(out), _nbytes(out), _stream(stream)))
+
+
+def moe_combine(rows, weights, out, stream=None):
+    """rows: BF16 [B*topk, D] (or uint16 bits), weights: FP32 [B, topk], out: BF16 [B, D]."""
+    B, K = weights.shape
+    D = rows.shape[-1]
+    _check("moe_combine", lib.moe_combine(_ptr(rows), _nbytes(rows), _ptr(weights), B, K, D, _ptr(out), _nbytes(out),
+                                          _stream(stream)))

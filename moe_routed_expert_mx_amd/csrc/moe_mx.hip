@@ -161,6 +161,35 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ x
   scales[idx] = static_cast<uint8_t>(e + 127);
 }
 
+// ------------------------------------------------------------------ combine
+// Weighted top-k combine (experts page, ExpertsKernel.finalize without the multicast):
+// out[t, d] = sum over s of w[t, s] * y[t*K + s, d], FP32 fused multiply-adds in slot
+// order, rounded once to BF16.  One thread per 8 consecutive d of one token (16-byte
+// row reads and one 16-byte store).
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ rows, const float* __restrict__ w,
+                                                      int B, int K, int D, uint16_t* __restrict__ out) {
+  const int per = D / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(B) * per) return;
+  const int t = static_cast<int>(i / per), c = static_cast<int>(i - static_cast<int64_t>(t) * per);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint16_t* r = rows + static_cast<int64_t>(t) * K * D + c * 8;
+  for (int s = 0; s < K; ++s) {
+    const float ws = w[static_cast<int64_t>(t) * K + s];
+    const uint4 v = *reinterpret_cast<const uint4*>(r + static_cast<int64_t>(s) * D);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = fmaf(ws, __uint_as_float(u[q] << 16), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(ws, __uint_as_float(u[q] & 0xffff0000u), acc[2 * q + 1]);
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = to_bf16_bits(acc[2 * q]) | (to_bf16_bits(acc[2 * q + 1]) << 16);
+  *reinterpret_cast<uint4*>(out + static_cast<int64_t>(t) * D + c * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // ------------------------------------------------------------------ units buffer
 // The unit table lives in its own caller buffer: header, per-unit expert and eight
 // pair indices, then the distinct experts ("groups") with their first unit, unit count
@@ -1708,6 +1737,17 @@ int moe_plan(const void* x, int32_t B, int32_t D, void* plan, size_t plan_bytes,
   hipLaunchKernelGGL(plan_kernel, dim3(static_cast<unsigned>((nblocks + 255) / 256)), dim3(256), 0,
                      as_stream(stream), static_cast<const uint8_t*>(x), nblocks, codes,
                      codes + static_cast<int64_t>(B) * D);
+  return launch_status();
+}
+
+int moe_combine(const void* rows, size_t rows_bytes, const float* weights, int32_t B, int32_t topk, int32_t D,
+                void* out, size_t out_bytes, void* stream) {
+  if (!rows || !weights || !out || B < 1 || topk < 1 || D < 8 || D % 8) return MOE_EINVAL;
+  if (rows_bytes < static_cast<size_t>(B) * topk * D * 2 || out_bytes < static_cast<size_t>(B) * D * 2)
+    return MOE_ENOSPACE;
+  const int64_t n = static_cast<int64_t>(B) * (D / 8);
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint16_t*>(rows), weights, B, topk, D, static_cast<uint16_t*>(out));
   return launch_status();
 }
 

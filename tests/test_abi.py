@@ -108,3 +108,17 @@ def test_product_does_not_reach_the_oracle():
         if f.endswith((".py", ".c")):
             src = open(os.path.join(ROOT, "oracle", f)).read()
             assert "moe_routed_expert_mx_amd" not in src and "moe_mx.h" not in src
+
+
+def test_combine_argument_checks():
+    """moe_combine rejects bad arguments on the host, before any launch."""
+    import ctypes
+    import moe_routed_expert_mx_amd as m
+    L = m._lib.lib
+    fake = ctypes.c_void_p(0x1000)
+    big = 1 << 40
+    assert L.moe_combine(None, big, fake, 1, 4, 512, fake, big, None) == m._lib.MOE_EINVAL
+    assert L.moe_combine(fake, big, fake, 1, 4, 500, fake, big, None) == m._lib.MOE_EINVAL   # D % 8
+    assert L.moe_combine(fake, big, fake, 0, 4, 512, fake, big, None) == m._lib.MOE_EINVAL
+    assert L.moe_combine(fake, 4 * 512 * 2 - 1, fake, 1, 4, 512, fake, big, None) == m._lib.MOE_ENOSPACE
+    assert L.moe_combine(fake, big, fake, 1, 4, 512, fake, 512 * 2 - 1, None) == m._lib.MOE_ENOSPACE
