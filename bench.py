@@ -2,8 +2,10 @@
 """Benchmark of the routed-experts MoE decode step on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input: the MXFP8
-plan of x (moe_plan), the unit table (moe_group) and the persistent experts kernel
-(moe_experts_run: FC1 -> SwiGLU -> hidden requant -> FC2 -> BF16 rows).  Inputs are
+plan of x, the unit table and the persistent experts kernel (FC1 -> SwiGLU -> hidden
+requant -> FC2 -> BF16 rows).  For B <= 8 that is one moe_decode_run launch (the
+kernel quantizes and routes the batch itself); for larger batches three calls,
+moe_plan + moe_group + moe_experts_run.  Inputs are
 resident in HBM before the timed region starts.  Each step reads a different weight
 replica (>= 1 GiB rotated) so the 256 MB Infinity Cache cannot serve repeated weights.
 Steps are captured in a HIP graph (torch.cuda.CUDAGraph) and replayed; the timed
@@ -11,8 +13,10 @@ region is bracketed by synchronizations and HIP events on the launch stream.
 
 Prints ONE JSON line (rank 0): µs per layer of the named workload, plus the roofline
 of the dominant kernel (experts: algorithmic bytes / its average duration measured
-with HIP events over graph replays of that kernel alone) and the CPU oracle timed on
-the host cores on a bounded sample of the same workload.
+with HIP events over graph replays of that kernel alone), the CPU oracle timed on
+the host cores on a bounded sample of the same workload, and the weighted top-k
+combine (moe_combine) of the step's rows timed alone (it follows the step; it is not
+part of it).
 """
 from __future__ import annotations
 
@@ -72,7 +76,8 @@ def _unique_weight_bytes(ids, w) -> int:
     return n * workloads.expert_weight_bytes(w.D, w.I)
 
 
-def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager: bool = False, log=print) -> dict:
+def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager: bool = False, path: str = "auto",
+            log=print) -> dict:
     import numpy as np
     import torch
 
@@ -86,33 +91,47 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
     layer = MoeLayer(d["w13"], d["s13"], d["w2"], d["s2"], B_max=w.B, topk=w.K, device="cuda", replicas=R)
     x = torch.from_numpy(d["x"]).cuda()
     ids = torch.from_numpy(d["ids"]).cuda()
+    rw = torch.from_numpy(d["weights"]).cuda()
     out = layer.out_buffer(w.B)
+    y = torch.empty(w.B, w.D, dtype=torch.bfloat16, device="cuda")
     # steps per graph: the largest divisor of `steps` up to graph_steps, so that exactly
     # `steps` steps are timed
     G = max(gs for gs in range(1, min(graph_steps, steps) + 1) if steps % gs == 0)
+    decode = path == "decode" or (path == "auto" and MoeLayer.AUTO_DECODE and w.B <= MoeLayer.DECODE_MAX)
+    form = "decode" if decode else "grouped"
 
     for i in range(warmup):
-        layer.forward(x, ids, out, replica=i % R)
+        layer.forward(x, ids, out, replica=i % R, path=form)
     torch.cuda.synchronize()
 
     reps = steps // G
     stream = torch.cuda.current_stream()
-    g = ge = None
+    g = ge = gc = None
     if not eager:
         # whole step (plan + units + experts), captured G steps per graph
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(G):
-                layer.forward(x, ids, out, replica=i % R)
+                layer.forward(x, ids, out, replica=i % R, path=form)
         # the dominant kernel alone: the experts kernel on the plan/units of the last step
+        # (the decode form's step is that one kernel)
         ge = torch.cuda.CUDAGraph()
         with torch.cuda.graph(ge):
             for i in range(G):
-                layer.experts(w.B, out, replica=i % R)
+                if decode:
+                    layer.forward(x, ids, out, replica=i % R, path=form)
+                else:
+                    layer.experts(w.B, out, replica=i % R)
+        # the weighted top-k combine of the step's rows (outside the step)
+        gc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gc):
+            for i in range(G):
+                layer.combine(out, rw, y)
         for _ in range(2):
             g.replay()
             ge.replay()
-        layer.forward(x, ids, out)  # plan and units of this batch for the experts-only graph
+            gc.replay()
+        layer.forward(x, ids, out, path=form)  # plan and units of this batch for the experts-only graph
         torch.cuda.synchronize()
 
     def timed(run_all) -> float:
@@ -126,21 +145,33 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
 
     def steps_eager():
         for i in range(reps * G):
-            layer.forward(x, ids, out, replica=i % R)
+            layer.forward(x, ids, out, replica=i % R, path=form)
 
     def experts_eager():
         for i in range(reps * G):
-            layer.experts(w.B, out, replica=i % R)
+            if decode:
+                layer.forward(x, ids, out, replica=i % R, path=form)
+            else:
+                layer.experts(w.B, out, replica=i % R)
+
+    def combine_eager():
+        for i in range(reps * G):
+            layer.combine(out, rw, y)
 
     step_us = timed(steps_eager if eager else (lambda: [g.replay() for _ in range(reps)]))
     experts_us = timed(experts_eager if eager else (lambda: [ge.replay() for _ in range(reps)]))
+    combine_us = timed(combine_eager if eager else (lambda: [gc.replay() for _ in range(reps)]))
+    combine_bytes = w.B * w.K * w.D * 2 + w.B * w.K * 4 + w.B * w.D * 2  # rows, weights, y
 
     uniq = _unique_weight_bytes(d["ids"], w)
     io_bytes = w.B * w.D * 2 + w.B * w.K * 4 + w.B * w.K * w.D * 2  # x, ids, out
     plan_bytes = w.B * w.D * 33 // 32
-    experts_bytes = uniq + plan_bytes + w.B * w.K * w.D * 2          # weights + plan read + out
+    # weights + the activations the kernel reads (the plan, or x and ids in the decode
+    # form) + output rows
+    act_bytes = w.B * w.D * 2 + w.B * w.K * 4 if decode else plan_bytes
+    experts_bytes = uniq + act_bytes + w.B * w.K * w.D * 2
     res = {
-        "workload": name, "B": w.B, "E": w.E, "topk": w.K, "D": w.D, "I": w.I,
+        "workload": name, "form": form, "B": w.B, "E": w.E, "topk": w.K, "D": w.D, "I": w.I,
         "distinct_experts": int(len(np.unique(d["ids"]))), "replicas": R, "graph_steps": G,
         "step_us": step_us, "experts_us": experts_us,
         "routes_per_s": w.B * w.K / (step_us * 1e-6),
@@ -148,9 +179,11 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
         "experts_alg_bytes": experts_bytes,
         "step_gbs": uniq / (step_us * 1e-6) / 1e9,
         "experts_gbs": experts_bytes / (experts_us * 1e-6) / 1e9,
+        "combine_us": combine_us, "combine_alg_bytes": combine_bytes,
+        "combine_gbs": combine_bytes / (combine_us * 1e-6) / 1e9,
     }
     log(json.dumps({"config_detail": res}), file=sys.stderr)
-    del g, ge, layer
+    del g, ge, gc, layer
     torch.cuda.empty_cache()
     return res
 
@@ -200,6 +233,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying HIP graphs")
+    ap.add_argument("--path", default="auto", choices=("auto", "decode", "grouped"),
+                    help="step form: one decode launch (B <= 8), the three-call grouped form, or auto")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()
@@ -217,7 +252,7 @@ def main():
     if args.copy_mb > 0:
         copy_calibration(args.copy_mb)
     names = workloads.ORDER if args.all else [args.workload]
-    results = {n: measure(n, args.steps, args.warmup, eager=args.eager) for n in names}
+    results = {n: measure(n, args.steps, args.warmup, eager=args.eager, path=args.path) for n in names}
     main_res = results[args.workload]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_budget)
     line = {
@@ -234,14 +269,14 @@ def main():
         "dtype": "fp4xfp8->f32",
         "data": "synthetic",
         "timing": "eager launches" if args.eager else "HIP graph replays",
-        "config": {"workload": args.workload, "B": main_res["B"], "E": main_res["E"], "topk": main_res["topk"],
+        "config": {"workload": args.workload, "form": main_res["form"], "B": main_res["B"], "E": main_res["E"], "topk": main_res["topk"],
                    "D": main_res["D"], "I": main_res["I"], "parallelism": "single GPU (one TP shard)"},
         "routes_per_s": round(main_res["routes_per_s"], 1),
         "hbm_gbs_unique_weights": round(main_res["step_gbs"], 1),
         "hbm_frac_of_peak": round(main_res["step_gbs"] / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "experts_kernel",
+            "kernel": "experts_kernel (decode form)" if main_res["form"] == "decode" else "experts_kernel",
             "achieved": round(main_res["experts_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -251,9 +286,14 @@ def main():
             "alg_bytes": main_res["experts_alg_bytes"],
         },
         "cpu_baseline": cpu,
+        "combine": {"kernel": "combine_kernel", "us": round(main_res["combine_us"], 3),
+                    "alg_bytes": main_res["combine_alg_bytes"], "gbs": round(main_res["combine_gbs"], 1),
+                    "note": "weighted top-k combine of the step's rows into [B, D]; not part of the step"},
     }
     if args.all:
-        line["per_workload"] = {n: {"us": round(r["step_us"], 3), "experts_us": round(r["experts_us"], 3),
+        line["per_workload"] = {n: {"form": r["form"], "us": round(r["step_us"], 3),
+                                    "experts_us": round(r["experts_us"], 3),
+                                    "combine_us": round(r["combine_us"], 3),
                                     "routes_per_s": round(r["routes_per_s"], 1),
                                     "gbs_unique": round(r["step_gbs"], 1),
                                     "frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4)} for n, r in results.items()}

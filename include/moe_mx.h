@@ -153,6 +153,14 @@ typedef struct {
   int32_t reserved[4];
   void* hidden_codes_dev;  /* optional u8 [B*topk, I]: the hidden's e4m3 codes per route */
   void* hidden_scales_dev; /* optional u8 [B*topk, I/32]: its E8M0 scales */
+  /* moe_decode_run only (MOE_EINVAL for moe_experts_run when set): */
+  void* plan_dev;          /* optional: the MXFP8 plan of x the call computed, in the moe_plan
+                              layout (B*D codes, then B*D/32 scales) */
+  size_t plan_bytes;       /* size of plan_dev (>= B*D/32*33, else MOE_ENOSPACE) */
+  int32_t* status_dev;     /* optional i32 status word the call ORs flags into: bit 0 an id out
+                              of range (skipped), bit 1 an id repeated within a token (one of
+                              its routes is lost), bit 2 a wait gave up (never expected).
+                              NULL: the flags go to a word of the workspace. */
 } moe_run_opts_t;
 
 /* The routed experts (experts page, ExpertsKernel; runtime page, PersistentExperts.run):
@@ -170,6 +178,21 @@ int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
                     const void* plan_dev, const void* units_dev, size_t units_bytes, int32_t B,
                     int32_t topk, void* ws_dev, size_t ws_bytes, void* out_dev, size_t out_bytes,
                     void* stream);
+
+/* The whole step of a small batch in one launch (B <= 8): the experts kernel also
+ * quantizes x and routes the batch itself (experts page, the capacity <= 8 path of
+ * ExpertsKernel, which skips the plan and group kernels: one unit per distinct expert,
+ * its tokens in token order, the same table moe_group writes for such a batch).
+ * Inputs x_dev BF16 [B, D] and ids_dev i32 [B, topk]; outputs as moe_experts_run
+ * (out_dev BF16 [B*topk, D], top-k order; optional hidden dump), plus the optional plan
+ * and status word of moe_run_opts_t.  The FC1 -> FC2 exchange goes through call-tagged
+ * FC1 partial sums in the workspace (moe_workspace_bytes sizes them), which each FC2
+ * workgroup reduces itself.  Ids out of range are skipped and flagged (status bit 0).
+ * Errors: MOE_EINVAL for B > 8 or the cases of moe_experts_run; MOE_ENOSPACE likewise.
+ * The same residency and no-overlap rules as moe_experts_run apply. */
+int moe_decode_run(const moe_weights_t* weights, const moe_run_opts_t* opts, const void* x_dev,
+                   const int32_t* ids_dev, int32_t B, int32_t topk, void* ws_dev, size_t ws_bytes,
+                   void* out_dev, size_t out_bytes, void* stream);
 
 /* ------------------------------------------------------------- combine ---- */
 

@@ -31,7 +31,8 @@ class moe_weights_t(ctypes.Structure):
 class moe_run_opts_t(ctypes.Structure):
     _fields_ = [("hidden_rule", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("col_tiles", ctypes.c_int32), ("ring", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4),
-                ("hidden_codes_dev", ctypes.c_void_p), ("hidden_scales_dev", ctypes.c_void_p)]
+                ("hidden_codes_dev", ctypes.c_void_p), ("hidden_scales_dev", ctypes.c_void_p),
+                ("plan_dev", ctypes.c_void_p), ("plan_bytes", ctypes.c_size_t), ("status_dev", ctypes.c_void_p)]
 
 
 def _load():
@@ -54,6 +55,8 @@ def _load():
                                        c.c_int32, P]),
         "moe_experts_run": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_size_t,
                                       c.c_int32, c.c_int32, P, c.c_size_t, P, c.c_size_t, P]),
+        "moe_decode_run": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_int32,
+                                     c.c_int32, P, c.c_size_t, P, c.c_size_t, P]),
         "moe_combine": (c.c_int, [P, c.c_size_t, P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
     }
     for name, (res, args) in sig.items():
@@ -65,7 +68,7 @@ def _load():
 lib = _load()
 EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_units_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
             "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_units_export",
-            "moe_experts_run", "moe_combine")
+            "moe_experts_run", "moe_decode_run", "moe_combine")
 
 
 def status_string(status: int) -> str:
@@ -136,13 +139,29 @@ def moe_units_export(units, B, topk, E, header, unit_expert, unit_rows, stream=N
                                                     _stream(stream)))
 
 
+def _opts(hidden_rule, grid, col_tiles, ring, hidden_codes, hidden_scales, plan=None, status=None):
+    return moe_run_opts_t(hidden_rule, grid, col_tiles, ring, (ctypes.c_int32 * 4)(0, 0, 0, 0),
+                          _ptr(hidden_codes), _ptr(hidden_scales), _ptr(plan), 0 if plan is None else _nbytes(plan),
+                          _ptr(status))
+
+
 def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, out, *, hidden_rule=0, grid=0,
                     col_tiles=0, ring=0, hidden_codes=None, hidden_scales=None, stream=None):
-    opts = moe_run_opts_t(hidden_rule, grid, col_tiles, ring, (ctypes.c_int32 * 4)(0, 0, 0, 0),
-                          _ptr(hidden_codes), _ptr(hidden_scales))
+    opts = _opts(hidden_rule, grid, col_tiles, ring, hidden_codes, hidden_scales)
     _check("moe_experts_run", lib.moe_experts_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(plan),
                                                   _ptr(units), _nbytes(units), B, topk, _ptr(ws), _nbytes(ws),
                                                   _ptr(out), _nbytes(out), _stream(stream)))
+
+
+def moe_decode_run(weights: moe_weights_t, x, ids, ws, out, *, hidden_rule=0, grid=0, ring=0, hidden_codes=None,
+                   hidden_scales=None, plan=None, status=None, stream=None):
+    """The whole step of a batch of B <= 8 tokens in one launch: x BF16 [B, D] (or uint16
+    bits), ids int32 [B, topk] -> out BF16 [B*topk, D]; optional plan (u8, the moe_plan
+    layout) and status (int32 [1]) outputs."""
+    B, K = ids.shape
+    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status)
+    _check("moe_decode_run", lib.moe_decode_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(x), _ptr(ids), B, K,
+                                                _ptr(ws), _nbytes(ws), _ptr(out), _nbytes(out), _stream(stream)))
 
 
 def moe_combine(rows, weights, out, stream=None):

@@ -88,6 +88,9 @@ __device__ __forceinline__ uint64_t ld_dev_u64(const void* p) {
 __device__ __forceinline__ void st_dev_u32(void* p, uint32_t v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev_u64(void* p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_dev_u8(void* p, uint8_t v) {
   __hip_atomic_store(reinterpret_cast<uint8_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -417,10 +420,14 @@ constexpr int kMaxGrid = 2048;     // workgroups of the persistent grid (call co
 constexpr int kMaxGroups = 1024;   // distinct experts per call (E <= 1024)
 
 struct WsLayout {
-  size_t calls, arrive, flags, hcodes, hscales, partials, end;
+  size_t calls, status, arrive, flags, hcodes, hscales, partials, end;
   int64_t max_tiles, max_blocks;
+  int64_t dec_slots;  // decode-form partial-sum slots (512 tagged pairs each)
   int nt_cap;
 };
+
+// Decode form (B <= kDecodeMax): at most 8 token columns per expert.
+constexpr int kDecodeMax = 8;
 
 // 16-column tiles of all expert groups of a batch: sum_g ceil(n_g / 16) with
 // sum_g n_g = U over at most min(E, U) groups.
@@ -442,6 +449,8 @@ WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   size_t off = 0;
   L.calls = off;
   off = align256(off + kMaxGrid * 4);
+  L.status = off;  // the decode form's status word (when the caller passes none)
+  off = align256(off + 4);
   L.arrive = off;
   off = align256(off + L.max_blocks * 4);
   L.flags = off;
@@ -450,8 +459,15 @@ WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   off = align256(off + L.max_tiles * 16 * IP);
   L.hscales = off;
   off = align256(off + L.max_tiles * 16 * (IP / 32));
+  // FC1 partial sums: the grouped form's per-workgroup slots, or the decode form's
+  // tagged slots -- at most (blocks of a call) + 4 * grid of them
+  const int64_t Bd = B_max < kDecodeMax ? B_max : kDecodeMax;
+  const int64_t Gd = Bd * K < E ? Bd * K : E;
+  L.dec_slots = Gd * HB + 4 * static_cast<int64_t>(kMaxGrid) + 4;
+  const size_t grouped = static_cast<size_t>(kMaxGrid) * 4 * L.nt_cap * 4096;
+  const size_t dec = static_cast<size_t>(L.dec_slots) * 4096;
   L.partials = off;
-  off = align256(off + static_cast<size_t>(kMaxGrid) * 4 * L.nt_cap * 4096);
+  off = align256(off + (grouped > dec ? grouped : dec));
   L.end = off;
   return L;
 }
@@ -478,6 +494,15 @@ struct ExpArgs {
   uint32_t plan_bytes;  // bytes of the plan (x codes, then x scales)
   int U2;   // FC2 items per chunk: groups of T2 16-row output tiles (D / 16 / T2)
   int g_cap, u_cap;  // LDS capacity of the group list and the unit rows
+  int32_t* err;      // status word: bit 0 id out of range, bit 1 id repeated in a token,
+                     // bit 2 a wait gave up (never expected)
+  // decode form (B <= 8): routing and the MXFP8 plan of x happen in the kernel
+  const uint16_t* x;     // BF16 [B, D]
+  const int32_t* ids;    // [B, K]
+  uint8_t* plan_dump;    // optional: the plan of x in the moe_plan layout (workgroup 0)
+  uint64_t* dpart;       // call-tagged FC1 partial sums: (float bits, call + 1) pairs
+  int B, E;
+  int qmin;  // decode form: least FC1 items per workgroup slice (0: grouped form)
 };
 
 // ------------------------------------------------------------ LDS access
@@ -591,6 +616,7 @@ __device__ __forceinline__ void lds_st4(uint32_t addr, uint32_t v) {
 // wait that runs out sets bit 2 of the unit-table flags and goes on.
 template <bool EQ>
 __device__ __forceinline__ void lds_wait(uint32_t addr, int want, int32_t* err) {
+  #pragma unroll 1
   for (uint32_t spins = 0;; ++spins) {
     const int v = lds_uni(addr);
     if (EQ ? v == want : v >= want) return;
@@ -606,11 +632,26 @@ __device__ __forceinline__ void lds_wait(uint32_t addr, int want, int32_t* err) 
 // [groups: g_cap records {expert, unit0, nunits, tile0}]  [chunk0: g_cap + 1 words]
 // [unit rows: u_cap x 8 u16 pair indices, 0xffff = padding]  [sync words]  [red: 2 x 4 streaming waves x NT x 4 KB, later reused as the 2 hidden
 // buffers]  [meta: 4 waves x R x 16 B]  [ring: 4 waves x R x slot]
-template <int NT, int R_>
+// FC2 output tiles per item, so that an FC2 item carries about as many weight bytes as
+// an FC1 item.
+template <int NS2>
+struct Fc2Tiles {
+  static constexpr int T2 = NS2 == 1 ? 8 : (NS2 == 2 ? 4 : 2);
+};
+
+// Ring geometry.  Grouped form: an FC1 item carries its x operand (13 KB slot).  Decode
+// form (DEC): x sits in LDS for the whole call, so a slot holds only weights: the FC1
+// item (8.5 KB) or the FC2 item (A codes, then its scale words from byte 8192).  Items
+// that issue fewer than L DMA instructions pad with zero-filling word loads from
+// outside a buffer into the slot's pad area, which nothing reads.
+template <int NT, int R_, int NS2, bool DEC>
 struct Geo {
   static constexpr int R = R_;                               // items in flight per wave
-  static constexpr int SLOT = 13312;                        // the FC1 item (the larger kind)
-  static constexpr int L = 16;                               // DMA instructions per item
+  static constexpr int T2 = Fc2Tiles<NS2>::T2;
+  static constexpr int FC2_END = 8192 + T2 * 256;            // end of an FC2 item's scale words
+  static constexpr int SLOT = DEC ? (FC2_END > 8704 ? FC2_END : 8704) + 256 : 13312;
+  static constexpr int PAD = DEC ? SLOT - 256 : 12800;
+  static constexpr int L = DEC ? (T2 * NS2 + T2 > 10 ? T2 * NS2 + T2 : 10) : 16;  // DMA instructions per item
   static constexpr int VM = (R - 1) * L;                     // vmcnt that completes the oldest of R items
   static constexpr int RED = 2 * kStream * NT * 4096;  // two hand-over slots per wave
 };
@@ -622,13 +663,24 @@ constexpr uint32_t kSyncSub = 0, kSyncAck = 16, kSyncProg = 32, kSyncReady = 48,
 
 struct LdsMap {
   uint32_t grec, chunk0, urows, sync, red, hid, hid_bytes, hs, meta, ring;
+  uint32_t xq, xs, xstr, xss;  // decode form: x codes [B + 1 rows of xstr], x scales [B + 1 rows of xss]
+  uint32_t scr;                // decode form: the hidden builder's staging area (in red)
 };
+
+// Decode form: the hidden builder stages up to kRound tagged partial sums per lane.
+constexpr int kRound = 16;
 
 // Hidden buffer of one FC2 chunk: NT*16 columns x (IP + 16) code bytes (padded rows),
 // then NT*16 columns x IP/32 scale bytes.  The two hidden buffers share the FC1
 // hand-over area: the control wave fills them only after it took every FC1 block.
-template <int NT, int R>
-__host__ __device__ __forceinline__ LdsMap lds_map(uint32_t g_cap, uint32_t u_cap, uint32_t IP) {
+// Decode form: x codes rows are D + 16 bytes apart (the rows of different tokens then
+// start in different LDS banks), scale rows D/32 + 4; row B is all zeros and stands in
+// for padded columns.  In red, after the two hidden buffers: the hidden builder's
+// staging area (kRound x 64 words) and its per-chunk table (96 words).
+template <int NT, int R, int NS2, bool DEC>
+__host__ __device__ __forceinline__ LdsMap lds_map(uint32_t g_cap, uint32_t u_cap, uint32_t IP, uint32_t B,
+                                                   uint32_t D) {
+  using G = Geo<NT, R, NS2, DEC>;
   LdsMap t;
   t.grec = 0;
   t.chunk0 = g_cap * 16;
@@ -638,17 +690,24 @@ __host__ __device__ __forceinline__ LdsMap lds_map(uint32_t g_cap, uint32_t u_ca
   t.hs = IP + 16;
   t.hid_bytes = (NT * 16 * t.hs + NT * 16 * (IP / 32) + 15) & ~15u;
   t.hid = t.red;
-  const uint32_t area = 2 * t.hid_bytes > Geo<NT, R>::RED ? 2 * t.hid_bytes : Geo<NT, R>::RED;
-  t.meta = t.red + area;
-  t.ring = t.meta + kStream * R * 16;
+  t.scr = t.red + 2 * t.hid_bytes;
+  const uint32_t need = DEC ? 2 * t.hid_bytes + kRound * 256 + 384 : 2 * t.hid_bytes;
+  const uint32_t area = need > static_cast<uint32_t>(G::RED) ? need : static_cast<uint32_t>(G::RED);
+  t.meta = t.red + ((area + 15) & ~15u);
+  t.xq = t.meta + kStream * R * 16;
+  t.xstr = D + 16;
+  t.xss = D / 32 + 4;
+  t.xs = t.xq + (DEC ? (B + 1) * t.xstr : 0);
+  t.ring = (t.xs + (DEC ? (B + 1) * t.xss : 0) + 15) & ~15u;
   return t;
 }
 
-template <int NT, int R>
-inline size_t lds_bytes(int g_cap, int u_cap, int IP) {
-  const LdsMap t = lds_map<NT, R>(static_cast<uint32_t>(g_cap), static_cast<uint32_t>(u_cap),
-                                  static_cast<uint32_t>(IP));
-  return t.ring + kStream * static_cast<size_t>(R) * Geo<NT, R>::SLOT;
+template <int NT, int R, int NS2, bool DEC>
+inline size_t lds_bytes(int g_cap, int u_cap, int IP, int B, int D) {
+  const LdsMap t = lds_map<NT, R, NS2, DEC>(static_cast<uint32_t>(g_cap), static_cast<uint32_t>(u_cap),
+                                            static_cast<uint32_t>(IP), static_cast<uint32_t>(B),
+                                            static_cast<uint32_t>(D));
+  return t.ring + kStream * static_cast<size_t>(R) * Geo<NT, R, NS2, DEC>::SLOT;
 }
 
 // Per-workgroup copy of the unit table: the group list, chunk0[g] = first weight-pass
@@ -710,6 +769,167 @@ __device__ __forceinline__ int load_groups(const ExpArgs& a, const LdsMap& m, in
   }
   __syncthreads();
   return chunk0[n_groups];
+}
+
+// Exclusive scan of v over the kWG threads of a workgroup (wtot: kWG/64 LDS words);
+// `total` gets the sum.  Contains a workgroup barrier.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* wtot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWG / 64; ++ww) {
+    const int t = wtot[ww];
+    if (ww < wave) base += t;
+    total += t;
+  }
+  return base + inc - v;
+}
+
+// MXFP8 of one 32-element BF16 block (w: its 16 words): 8 code words; returns the
+// E8M0 exponent (experts page, mx_block; the same arithmetic as plan_kernel).
+__device__ __forceinline__ int mx_block32(const uint32_t (&w)[16], uint32_t (&c)[8]) {
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+  }
+  const int e = mx_exponent(amax, false);
+  const float s = exp2_neg(e);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    c[k] = to_e4m3(v[4 * k] * s) | (to_e4m3(v[4 * k + 1] * s) << 8) | (to_e4m3(v[4 * k + 2] * s) << 16) |
+           (to_e4m3(v[4 * k + 3] * s) << 24);
+  return e;
+}
+
+// Decode form prologue, all waves, before the first weight DMA.  Every workgroup builds
+// in its own LDS the unit table of the batch (B <= 8; experts page, the capacity <= 8
+// path: one unit per distinct expert, experts ascending, its tokens in token order --
+// the table moe_group writes for such a batch) and the MXFP8 plan of x (the moe_plan
+// arithmetic), so the whole step is one launch.  Returns the number of distinct experts.
+__device__ __forceinline__ int dec_prologue(const ExpArgs& a, const LdsMap& m, uint32_t ring_bytes) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x;
+  const int U = a.B * a.K, E = a.E, D = a.D, nkb = D / 32, nxb = a.B * nkb;
+  // scratch in the ring, which no DMA has touched yet: per-expert token masks (a byte
+  // per expert), expert -> group rank, wave totals
+  uint32_t* mk = reinterpret_cast<uint32_t*>(smem + m.ring);          // [ceil(E / 4)]
+  uint16_t* rk = reinterpret_cast<uint16_t*>(smem + m.ring + 1024);   // [E]
+  int* wtot = reinterpret_cast<int*>(smem + m.ring + 3072);           // [kWG / 64]
+  uint16_t* urows = reinterpret_cast<uint16_t*>(smem + m.urows);
+  int4* grec = reinterpret_cast<int4*>(smem + m.grec);
+  int* chunk0 = reinterpret_cast<int*>(smem + m.chunk0);
+  // the ids (U <= 512: at most 2 per thread)
+  int id[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = tid + q * kWG;
+    id[q] = r < U ? a.ids[r] : -1;
+  }
+  for (int i = tid; i < (E + 3) / 4; i += kWG) mk[i] = 0u;
+  for (int i = tid; i < a.u_cap * 8; i += kWG) urows[i] = 0xffffu;
+  if (tid < kSyncBytes / 4)  // sub, ack = 0; prog, ready = -1
+    reinterpret_cast<int*>(smem + m.sync)[tid] = (tid * 4 >= static_cast<int>(kSyncProg)) ? -1 : 0;
+  for (int i = tid; i < D / 16; i += kWG)
+    *reinterpret_cast<uint4*>(smem + m.xq + a.B * m.xstr + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < static_cast<int>(m.xss) / 4; i += kWG)
+    *reinterpret_cast<uint32_t*>(smem + m.xs + a.B * m.xss + 4 * i) = 0u;
+  __syncthreads();
+  // token masks; an id repeated within a token finds its bit already set
+  int flags = 0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = tid + q * kWG;
+    if (r >= U) continue;
+    const int e = id[q];
+    if (e < 0 || e >= E) {
+      flags |= 1;
+      continue;
+    }
+    const uint32_t bit = 1u << ((e & 3) * 8 + r / a.K);
+    if (atomicOr(&mk[e >> 2], bit) & bit) flags |= 2;
+  }
+  __syncthreads();
+  // group ranks: thread i takes experts 4i .. 4i+3 (E <= 1024 -> 256 threads)
+  const uint32_t mw = tid < (E + 3) / 4 ? mk[tid] : 0u;
+  int cnt = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) cnt += ((mw >> (8 * b)) & 0xffu) != 0u;
+  int n_groups = 0;
+  int g = wg_exclusive_scan(cnt, wtot, n_groups);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (((mw >> (8 * b)) & 0xffu) == 0u) continue;
+    const int e = 4 * tid + b;
+    rk[e] = static_cast<uint16_t>(g);
+    grec[g] = make_int4(e, g, 1, g);  // one unit, one column tile per expert
+    chunk0[g] = g;
+    ++g;
+  }
+  if (tid == 0) chunk0[n_groups] = n_groups;
+  __syncthreads();
+  // unit rows: pair r of token t at t's rank among the expert's tokens
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = tid + q * kWG;
+    const int e = id[q];
+    if (r >= U || e < 0 || e >= E) continue;
+    const int t = r / a.K;
+    const uint32_t tm = (mk[e >> 2] >> ((e & 3) * 8)) & 0xffu;
+    urows[rk[e] * 8 + __popc(tm & ((1u << t) - 1u))] = static_cast<uint16_t>(r);
+  }
+  if (flags && blockIdx.x == 0) __hip_atomic_fetch_or(a.err, flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the plan of x into LDS (and the optional dump, workgroup 0): the BF16 rows come in
+  // by DMA, 1 KB per instruction, into the ring behind the routing scratch, as many as
+  // fit per pass; then one thread per 32-element block
+  const int pieces = a.B * D * 2 / 1024, per_pass = static_cast<int>(ring_bytes - 4096) / 1024;
+  const int w = wave_id(), l = threadIdx.x & 63;
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
+#pragma unroll 1
+  for (int p0 = 0; p0 < pieces; p0 += per_pass) {
+    const int np = pieces - p0 < per_pass ? pieces - p0 : per_pass;
+#pragma unroll 1
+    for (int i = w; i < np; i += kWG / 64) dma16(xb + (p0 + i) * 1024 + l * 16, m.ring + 4096 + i * 1024);
+    wait_vm<0>();
+    __syncthreads();
+#pragma unroll 1
+    for (int blk = p0 * 16 + tid; blk < (p0 + np) * 16; blk += kWG) {
+      const uint4* src = reinterpret_cast<const uint4*>(smem + m.ring + 4096 + (blk - p0 * 16) * 64);
+      uint32_t xw[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = src[i];
+        xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+      }
+      uint32_t c[8];
+      const int e = mx_block32(xw, c);
+      const int t = blk / nkb, kb = blk - t * nkb;
+      uint4* dst = reinterpret_cast<uint4*>(smem + m.xq + t * m.xstr + 32 * kb);
+      dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+      dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+      smem[m.xs + t * m.xss + kb] = static_cast<unsigned char>(e + 127);
+      if (a.plan_dump != nullptr && blockIdx.x == 0) {
+        uint4* pd = reinterpret_cast<uint4*>(a.plan_dump + static_cast<int64_t>(blk) * 32);
+        pd[0] = make_uint4(c[0], c[1], c[2], c[3]);
+        pd[1] = make_uint4(c[4], c[5], c[6], c[7]);
+        a.plan_dump[static_cast<int64_t>(nxb) * 32 + blk] = static_cast<uint8_t>(e + 127);
+      }
+    }
+    __syncthreads();
+  }
+  return n_groups;
 }
 
 struct GroupInfo {
@@ -838,9 +1058,36 @@ __device__ __forceinline__ Slice make_slice(const ExpArgs& a, int n_chunks, int 
   s.T = (c_hi - c_lo) * per;
   s.base = c_lo * per_chunk;
   s.P = s.T < G ? s.T : G;
+  if (h < 2 && a.qmin > 0 && s.T > 0) {
+    // decode form: FC1 slices of at least qmin items, so a hidden block has at most
+    // four owners (qmin = ceil(NSP / 3))
+    const int q = s.T / a.qmin;
+    s.P = q < 1 ? 1 : (q < s.P ? q : s.P);
+  }
   s.lo = __builtin_amdgcn_readfirstlane(p < s.P ? div_floor(static_cast<int64_t>(p) * s.T, s.P) : 0);
   s.hi = __builtin_amdgcn_readfirstlane(p < s.P ? div_floor(static_cast<int64_t>(p + 1) * s.T, s.P) : 0);
   return s;
+}
+
+// Decode form: the partial-sum slots (512 tagged pairs each) of FC1 list h.  A slice of
+// at most ceil(T/P) items touches at most (ceil(T/P) - 1) / NSP + 2 hidden blocks, so
+// workgroup p's slots of list h are p * SPW_h + (local block); list 1's follow list 0's.
+__device__ __forceinline__ int dec_spw(const Slice& S, int NSP) {
+  return S.P > 0 ? ((S.T + S.P - 1) / S.P - 1) / NSP + 2 : 0;
+}
+// Slot of workgroup p's share of list-local FC1 block bl of list h (S = that list).
+__device__ __forceinline__ uint32_t dec_slot(const ExpArgs& a, int n_chunks, int h, const Slice& S, int p, int bl) {
+  uint32_t off = 0;
+  if (h == 1) {
+    const Slice S0 = make_slice(a, n_chunks, 0);
+    off = static_cast<uint32_t>(S0.P * dec_spw(S0, a.NSP));
+  }
+  const int lo = div_floor(static_cast<int64_t>(p) * S.T, S.P);
+  return off + static_cast<uint32_t>(p * dec_spw(S, a.NSP) + (bl - lo / a.NSP));
+}
+// Owner of item x of a list of T items split over P slices: ceil((x + 1) P / T) - 1.
+__device__ __forceinline__ int slice_owner(int x, int T, int P) {
+  return div_floor(static_cast<int64_t>(x + 1) * P + T - 1, T) - 1;
 }
 
 // One wave's walk over its items: FC1 steps s_lo + w, s_lo + w + 4, ... of each block
@@ -876,6 +1123,7 @@ __device__ __forceinline__ int fc2_span(const ExpArgs& a, const Slice& S, int& f
   return S.hi > S.lo ? (S.base + S.hi - 1) / a.U2 - first + 1 : 0;
 }
 
+template <bool DEC>
 __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
                                             int n_chunks, Cursor& c) {
   const int w = wave_id();
@@ -945,7 +1193,7 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
       moved = true;
     }
   }
-  if (moved && c.h < 2) x_rows(a, m, lb, c.gi, c.xrow, c.xsrow);
+  if (!DEC && moved && c.h < 2) x_rows(a, m, lb, c.gi, c.xrow, c.xsrow);
   c.gidx = gidx;
 }
 
@@ -958,14 +1206,7 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
 // past the end pad with redundant word loads into unused bytes of their slot), so "the
 // oldest of R items has landed" is always s_waitcnt vmcnt((R-1)*L).  The item's 16-byte
 // record goes to LDS when it is issued.
-constexpr uint32_t kSlotAS = 8192, kSlotX = 8704, kSlotXS = 12800, kSlotPad = 8704;
-
-// FC2 output tiles per item, so that an FC2 item carries about as many weight bytes as
-// an FC1 item.
-template <int NS2>
-struct Fc2Tiles {
-  static constexpr int T2 = NS2 == 1 ? 8 : (NS2 == 2 ? 4 : 2);
-};
+constexpr uint32_t kSlotAS = 8192, kSlotX = 8704, kSlotXS = 12800;
 
 __device__ __forceinline__ void lds_st16_async(uint32_t addr, uint4 v) {
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -973,10 +1214,10 @@ __device__ __forceinline__ void lds_st16_async(uint32_t addr, uint4 v) {
   asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(x) : "memory");
 }
 
-template <int NS2, int R>
+template <int NS2, int R, bool DEC>
 __device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, uint32_t lb, const Cursor& c, int k,
                                            __amdgpu_buffer_rsrc_t xr) {
-  using G = Geo<1, R>;
+  using G = Geo<1, R, NS2, DEC>;
   constexpr int T2 = Fc2Tiles<NS2>::T2;
   const int l = threadIdx.x & 63, w = wave_id();
   const int slot = k % R;
@@ -992,15 +1233,22 @@ __device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, ui
     const uint8_t* sb = a.s13p + step * 256 + l * 4;
     dma4(sb, so + kSlotAS);
     dma4(sb + 256, so + kSlotAS + 256);
-    const bool live = c.xrow >= 0;
-    const uint32_t xo = live ? static_cast<uint32_t>(c.xrow + s0 * 128) : kOutside;
+    if constexpr (DEC) {
+      // x is in LDS: the record names the chunk and the step pair instead
+      meta = make_uint4(0u, static_cast<uint32_t>(c.gidx), static_cast<uint32_t>(c.chunk),
+                        static_cast<uint32_t>(c.s));
+      done = 10;
+    } else {
+      const bool live = c.xrow >= 0;
+      const uint32_t xo = live ? static_cast<uint32_t>(c.xrow + s0 * 128) : kOutside;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bdma16(xr, live ? xo + i * 64 : kOutside, so + kSlotX + i * 1024);
-    const uint32_t xso = live ? static_cast<uint32_t>(c.xsrow + 4 * s0) : kOutside;
-    bdma4(xr, xso, so + kSlotXS);
-    bdma4(xr, live ? xso + 4 : kOutside, so + kSlotXS + 256);
-    meta = make_uint4(0u, static_cast<uint32_t>(c.gidx), 0u, 0u);
-    done = G::L;
+      for (int i = 0; i < 4; ++i) bdma16(xr, live ? xo + i * 64 : kOutside, so + kSlotX + i * 1024);
+      const uint32_t xso = live ? static_cast<uint32_t>(c.xsrow + 4 * s0) : kOutside;
+      bdma4(xr, xso, so + kSlotXS);
+      bdma4(xr, live ? xso + 4 : kOutside, so + kSlotXS + 256);
+      meta = make_uint4(0u, static_cast<uint32_t>(c.gidx), 0u, 0u);
+      done = G::L;
+    }
   } else if (c.h < 4) {
     const int64_t tile = static_cast<int64_t>(c.gi.e) * (a.D / 16) + c.j * T2;
     const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
@@ -1013,7 +1261,7 @@ __device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, ui
                       static_cast<uint32_t>(c.seq0 + c.chunk - c.cfirst));
     done = T2 * NS2 + T2;
   }
-  for (int i = done; i < G::L; ++i) bdma4(xr, kOutside, so + kSlotPad + i * 256);
+  for (int i = done; i < G::L; ++i) bdma4(xr, kOutside, so + G::PAD);
   if (l == 0) lds_st16_async(lb + m.meta + (w * R + slot) * 16, meta);
 }
 
@@ -1049,6 +1297,33 @@ __device__ __forceinline__ void fc1_read(uint32_t pa, uint32_t pq, Fc1Ops& o) {
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]), "=&v"(o.a[7]), "=&v"(o.x[0]), "=&v"(o.x[1]), "=&v"(o.x[2]), "=&v"(o.x[3]), "=&v"(o.as[0]), "=&v"(o.as[1]), "=&v"(o.xs[0]), "=&v"(o.xs[1])
       : "v"(pa), "v"(pq)
+      : "memory");
+}
+
+// Decode form FC1 item: A and its scale words from the slot (as fc1_read), the x operand
+// from the LDS plan: px = the column's codes at the item's first K step (+ 16 per lane
+// group), halves at +0/+64 (step 0) and +128/+192 (step 1); pxs = its scale words.
+__device__ __forceinline__ void fc1_read_dec(uint32_t pa, uint32_t pq, uint32_t px, uint32_t pxs, Fc1Ops& o) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:0\n\t"
+      "ds_read_b128 %1, %16 offset:1024\n\t"
+      "ds_read_b128 %2, %16 offset:2048\n\t"
+      "ds_read_b128 %3, %16 offset:3072\n\t"
+      "ds_read_b128 %4, %16 offset:4096\n\t"
+      "ds_read_b128 %5, %16 offset:5120\n\t"
+      "ds_read_b128 %6, %16 offset:6144\n\t"
+      "ds_read_b128 %7, %16 offset:7168\n\t"
+      "ds_read_b32 %12, %17 offset:8192\n\t"
+      "ds_read_b32 %13, %17 offset:8448\n\t"
+      "ds_read_b128 %8, %18 offset:0\n\t"
+      "ds_read_b128 %9, %18 offset:64\n\t"
+      "ds_read_b128 %10, %18 offset:128\n\t"
+      "ds_read_b128 %11, %18 offset:192\n\t"
+      "ds_read_b32 %14, %19 offset:0\n\t"
+      "ds_read_b32 %15, %19 offset:4\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o.a[0]), "=&v"(o.a[1]), "=&v"(o.a[2]), "=&v"(o.a[3]), "=&v"(o.a[4]), "=&v"(o.a[5]), "=&v"(o.a[6]), "=&v"(o.a[7]), "=&v"(o.x[0]), "=&v"(o.x[1]), "=&v"(o.x[2]), "=&v"(o.x[3]), "=&v"(o.as[0]), "=&v"(o.as[1]), "=&v"(o.xs[0]), "=&v"(o.xs[1])
+      : "v"(pa), "v"(pq), "v"(px), "v"(pxs)
       : "memory");
 }
 
@@ -1256,10 +1531,11 @@ __device__ __forceinline__ void control_block(const ExpArgs& a, const LdsMap& m,
     const int T = li.T, P = li.P;
     const int pb = div_floor(static_cast<int64_t>(bs + NS1) * P + T - 1, T) - 1;
     const uint32_t want = static_cast<uint32_t>(pb - p);
+    #pragma unroll 1
     for (uint32_t spins = 0;; ++spins) {
       if (ld_dev_u32(a.arrive + b) == want) break;
       if (spins == kSpinLimit) {
-        if (l == 0) __hip_atomic_fetch_or(a.tbl.hdr + 3, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -1316,12 +1592,13 @@ __device__ __forceinline__ void wait_chunk(const ExpArgs& a, int chunk, uint32_t
   const int l = threadIdx.x & 63;
   const uint32_t want = gen + 1;
   const uint32_t* f = a.flags + static_cast<int64_t>(chunk) * a.HB;
+  #pragma unroll 1
   for (uint32_t spins = 0;; ++spins) {
     bool ok = true;
     for (int i = l; i < a.HB; i += 64) ok = ok && ld_dev_u32(f + i) == want;
     if (__all(ok)) break;
     if (spins == kSpinLimit) {
-      if (l == 0) __hip_atomic_fetch_or(a.tbl.hdr + 3, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -1366,6 +1643,234 @@ __device__ __forceinline__ void control_hidden(const ExpArgs& a, const LdsMap& m
   }
 }
 
+// ------------------------------------------------------------ decode form exchange
+// FC1 block sums cross workgroups as call-tagged (float bits, call + 1) pairs that the
+// FC2 side reduces itself: one store and one load between a block's last FC1 step and
+// FC2, where a finished-block scheme needs a count, a finisher's loads, the hidden's
+// stores and a flag.
+
+__device__ __forceinline__ void lds_st1(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b8 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_st4_nw(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_settle() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Real token columns of a decode-form group (its one unit's non-padding entries).
+__device__ __forceinline__ int unit_cols(const LdsMap& m, uint32_t lb, const GroupInfo& gi) {
+  const int l = threadIdx.x & 63;
+  const uint32_t v = lds_ld2(lb + m.urows + (gi.unit0 * 8 + (l & 7)) * 2);
+  return __popcll(__ballot(l < 8 && v != 0xffffu));
+}
+
+// File the workgroup's sum of list-local FC1 block lbk of list h (the four streaming
+// waves' sums in hand-over slot q & 1, added in wave order): lane l = block row l (gate
+// rows 0-31, up rows 32-63), one 64-pair run per real column.  No wait.
+__device__ __forceinline__ void dec_publish(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
+                                            int n_chunks, const Slice& S, int h, int lbk, int q, uint32_t gen) {
+  const int l = threadIdx.x & 63;
+  const int chunk = (S.base + lbk) / a.HB;
+  const GroupInfo gi = group_of(m, lb, n_groups, chunk);
+  const int ncols = unit_cols(m, lb, gi);
+  uint64_t* dst = a.dpart + static_cast<size_t>(dec_slot(a, n_chunks, h, S, blockIdx.x, lbk)) * 512 + l;
+  // element (row l, column c) of tile rt = l / 16 sits in lane 16 ((l % 16) / 4) + c,
+  // register l % 4 of the MFMA result
+  const int rt = l >> 4, rr = l & 15;
+  const uint32_t src = lb + m.red + ((q & 1) * kStream * 4 + rt) * 1024 + 256 * (rr >> 2) + 4 * (rr & 3);
+  const uint64_t tag = static_cast<uint64_t>(gen + 1) << 32;
+  static_assert(kStream == 4, "four streaming waves' sums");
+  for (int c = 0; c < ncols; ++c) {
+    uint32_t x0, x1, x2, x3;
+    lds_ld4x4<0, 4096>(src + 16 * c, x0, x1, x2, x3);
+    const float v = ((__uint_as_float(x0) + __uint_as_float(x1)) + __uint_as_float(x2)) + __uint_as_float(x3);
+    st_dev_u64(dst + 64 * c, tag | __float_as_uint(v));
+  }
+}
+
+// The hidden of FC2 chunk `chunk` (one expert, up to 8 token columns) into hidden buffer
+// buf, from the tagged FC1 partials: per hidden block j and column c, the owners' sums
+// added in slice order, then SwiGLU and MXFP8 (experts page, store_hidden: FP32 hidden,
+// one E8M0 exponent per 32 values; the arithmetic of hidden_epilogue).
+// The partial pairs are taken in (block, column, owner) order, kRound per lane at a time:
+// lane s works out where pair s of a round lives (from a per-chunk table in LDS) and
+// whether it opens or closes a (block, column) sum; the loads take those addresses by
+// lane broadcasts.  Before loading, it polls one probe pair per (block, owner) -- the last
+// pair each owner stores; a round whose tags are not all this call's is loaded again
+// (bounded).  Finished sums are staged in LDS and completed two at a time, one per
+// half-wave.  The workgroup owning the chunk's first FC2 item writes the optional dump.
+__device__ __forceinline__ void dec_hidden(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
+                                           int n_chunks, int chunk, uint32_t buf, bool dump, uint32_t gen) {
+  const int l = threadIdx.x & 63, half = l >> 5, hl = l & 31;
+  const GroupInfo gi = group_of(m, lb, n_groups, chunk);
+  const int ncols = unit_cols(m, lb, gi);
+  const int HB = a.HB, NSP = a.NSP;
+  const uint32_t want = gen + 1;
+  // lane 4j + k: owner k (< 4) of hidden block j and its slot; the table: cum[16] (first
+  // pair of block j in the chunk's order), nown[16], slot[64]
+  const uint32_t tb = lb + m.scr + kRound * 256;
+  int total;
+  {
+    const int h = chunk < (n_chunks + 1) / 2 ? 0 : 1;
+    const Slice S = make_slice(a, n_chunks, h);
+    const int j = l >> 2, k = l & 3;
+    int nown = 0;
+    uint32_t sidx = 0;
+    if (j < HB) {
+      const int bl = chunk * HB + j - S.base;
+      const int p0 = slice_owner(bl * NSP, S.T, S.P), p1 = slice_owner(bl * NSP + NSP - 1, S.T, S.P);
+      nown = p1 - p0 + 1;
+      if (k < nown) sidx = dec_slot(a, n_chunks, h, S, p0 + k, bl);
+    }
+    const int v = k == 0 ? nown * ncols : 0;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(inc, d);
+      if (l >= d) inc += o;
+    }
+    total = __builtin_amdgcn_readlane(inc, 63);
+    if (k == 0 && j < 16) {
+      lds_st4_nw(tb + 4 * j, static_cast<uint32_t>(j < HB ? inc - v : total));
+      lds_st4_nw(tb + 64 + 4 * j, static_cast<uint32_t>(nown));
+    }
+    lds_st4_nw(tb + 128 + 4 * l, sidx);
+    lds_settle();
+    const bool probe = j < HB && k < nown;
+    const uint64_t* pp = a.dpart + static_cast<size_t>(sidx) * 512 + 64 * (ncols - 1) + 63;
+#pragma unroll 1
+    for (uint32_t spins = 0;; ++spins) {
+      const bool ok = !probe || static_cast<uint32_t>(ld_dev_u64(pp) >> 32) == want;
+      if (__all(ok)) break;
+      if (spins == kSpinLimit) {
+        if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  const uint32_t hb = lb + m.hid + buf * m.hid_bytes;
+  int fj = 0, fc = 0;  // first unfinished (block, column)
+  float sum = 0.0f;
+#pragma unroll 1
+  for (int done = 0; done < total; done += kRound) {
+    const int nb = total - done < kRound ? total - done : kRound;
+    // lane s: pair done + s -> block j (the last with cum[j] <= f), column, owner
+    uint64_t addr = 0;
+    bool first = false, last = false;
+    {
+      const int f = done + l;
+      uint4 c4[4];
+      asm volatile(
+          "ds_read_b128 %0, %4 offset:0\n\t"
+          "ds_read_b128 %1, %4 offset:16\n\t"
+          "ds_read_b128 %2, %4 offset:32\n\t"
+          "ds_read_b128 %3, %4 offset:48\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(c4[0]), "=&v"(c4[1]), "=&v"(c4[2]), "=&v"(c4[3])
+          : "v"(tb)
+          : "memory");
+      int j = -1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        j += (static_cast<int>(c4[q].x) <= f) + (static_cast<int>(c4[q].y) <= f) + (static_cast<int>(c4[q].z) <= f) +
+             (static_cast<int>(c4[q].w) <= f);
+      }
+      j = j < HB - 1 ? j : HB - 1;  // blocks past HB carry cum = total
+      if (l < nb) {
+        const int cum = static_cast<int>(lds_ld4(tb + 4 * j));
+        const int n = static_cast<int>(lds_ld4(tb + 64 + 4 * j));
+        const int r = f - cum, c = r / n, k = r - c * n;
+        const uint32_t sl = lds_ld4(tb + 128 + 4 * (4 * j + k));
+        addr = reinterpret_cast<uint64_t>(a.dpart + static_cast<size_t>(sl) * 512 + 64 * c);
+        first = k == 0;
+        last = k == n - 1;
+      }
+    }
+    const uint64_t fm = __ballot(first), lm = __ballot(last);
+    const uint32_t alo = static_cast<uint32_t>(addr), ahi = static_cast<uint32_t>(addr >> 32);
+    uint64_t v[kRound];
+#pragma unroll 1
+    for (uint32_t spins = 0;; ++spins) {
+#pragma unroll
+      for (int s = 0; s < kRound; ++s) {
+        if (s < nb) {
+          // slot s's address, broadcast through a VGPR (no scalar registers held per slot)
+          const uint64_t base = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl(static_cast<int>(ahi), s))) << 32) |
+                                static_cast<uint32_t>(__shfl(static_cast<int>(alo), s));
+          v[s] = ld_dev_u64(reinterpret_cast<const uint64_t*>(base) + l);
+        }
+      }
+      bool ok = true;
+#pragma unroll
+      for (int s = 0; s < kRound; ++s) ok = ok && (s >= nb || static_cast<uint32_t>(v[s] >> 32) == want);
+      if (__all(ok)) break;
+      if (spins == kSpinLimit) {
+        if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    // owners' sums in registers; each finished (block, column) sum goes to the staging area
+    int nf = 0;
+#pragma unroll
+    for (int s = 0; s < kRound; ++s) {
+      if (s < nb) {
+        const float x = __uint_as_float(static_cast<uint32_t>(v[s]));
+        sum = ((fm >> s) & 1) ? x : sum + x;
+        if ((lm >> s) & 1) {
+          lds_st4_nw(lb + m.scr + nf * 256 + l * 4, __float_as_uint(sum));
+          ++nf;
+        }
+      }
+    }
+    lds_settle();
+    // complete the finished sums two at a time: half-wave 0 takes (fj, fc), half-wave 1
+    // the next; lane hl of a half is hidden row 32 fj + hl (its gate and up rows sit in
+    // lanes hl and hl + 32 of the staged sums)
+#pragma unroll 1
+    for (int f = 0; f < nf; f += 2) {
+      const bool two = f + 1 < nf;
+      const float sA = __uint_as_float(lds_ld4(lb + m.scr + f * 256 + l * 4));
+      const float sB = two ? __uint_as_float(lds_ld4(lb + m.scr + (f + 1) * 256 + l * 4)) : 0.0f;
+      const float xA = __shfl_xor(sA, 32), xB = __shfl_xor(sB, 32);
+      const float g = half == 0 ? sA : xB, u = half == 0 ? xA : sB;
+      const bool live = half == 0 || two;
+      const float hv = live ? g / (1.0f + expf(-g)) * u : 0.0f;
+      float amax = fabsf(hv);
+#pragma unroll
+      for (int d = 1; d < 32; d <<= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+      const int e = mx_exponent(amax, a.floor_rule != 0);
+      const uint32_t code = to_e4m3(hv * exp2_neg(e));
+      int jB = fj, cB = fc + 1;
+      if (cB == ncols) {
+        cB = 0;
+        ++jB;
+      }
+      const int jj = half == 0 ? fj : jB, c2 = half == 0 ? fc : cB;
+      if (live) {
+        lds_st1(hb + c2 * m.hs + 32 * jj + hl, code);
+        if (hl == 0) lds_st1(hb + 16 * m.hs + c2 * (a.IP / 32) + jj, static_cast<uint32_t>(e + 127));
+        if (dump && a.dump_codes != nullptr) {
+          const int pair = column_pair(m, lb, gi, c2);
+          if (pair >= 0) {
+            a.dump_codes[static_cast<int64_t>(pair) * a.I + 32 * jj + hl] = static_cast<uint8_t>(code);
+            if (hl == 0) a.dump_scales[static_cast<int64_t>(pair) * (a.I / 32) + jj] = static_cast<uint8_t>(e + 127);
+          }
+        }
+      }
+      // advance past the entries just completed (one or two)
+      fj = jB;
+      fc = cB;
+      if (two && ++fc == ncols) {
+        fc = 0;
+        ++fj;
+      }
+    }
+    lds_settle();
+  }
+}
+
 // The persistent routed-experts kernel (experts page, ExpertsKernel; runtime page,
 // PersistentExperts.run): one workgroup per CU, co-resident (FC2 waits for hidden
 // blocks that other workgroups' FC1 slices produce).  Waves 0-3 stream their items --
@@ -1375,17 +1880,23 @@ __device__ __forceinline__ void control_hidden(const ExpArgs& a, const LdsMap& m
 // the streaming waves' FC1 sums of each block (LDS), files or finishes the block and
 // publishes its hidden, then polls for the hidden of each FC2 chunk the workgroup
 // needs and copies it into one of two LDS buffers.
-template <int NT, int NS2, int R>
+template <int NT, int NS2, int R, bool DEC>
 __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
-  using G = Geo<NT, R>;
+  using G = Geo<NT, R, NS2, DEC>;
   const int l = threadIdx.x & 63, w = wave_id(), grp = l >> 4;
-  const LdsMap m = lds_map<NT, R>(static_cast<uint32_t>(a.g_cap), static_cast<uint32_t>(a.u_cap),
-                                  static_cast<uint32_t>(a.IP));
+  const LdsMap m = lds_map<NT, R, NS2, DEC>(static_cast<uint32_t>(a.g_cap), static_cast<uint32_t>(a.u_cap),
+                                            static_cast<uint32_t>(a.IP), static_cast<uint32_t>(a.B),
+                                            static_cast<uint32_t>(a.D));
   const uint32_t lb = lds_base();
-  const int n_groups = a.tbl.hdr[1];
-  const int n_units = a.tbl.hdr[0];
   const uint32_t gen = a.calls[blockIdx.x];
-  const int n_chunks = load_groups<NT>(a, m, n_groups, n_units);
+  int n_groups, n_chunks;
+  if constexpr (DEC) {
+    n_groups = dec_prologue(a, m, kStream * R * G::SLOT);
+    n_chunks = n_groups;  // one column tile per expert
+  } else {
+    n_groups = a.tbl.hdr[1];
+    n_chunks = load_groups<NT>(a, m, n_groups, a.tbl.hdr[0]);
+  }
   const uint32_t sy = lb + m.sync;
   agpr_form();
 
@@ -1398,10 +1909,10 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
       if (S.hi <= S.lo) continue;
       for (int lbk = S.lo / a.NSP; lbk <= (S.hi - 1) / a.NSP; ++lbk, ++q) {
 #pragma unroll
-        for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncSub + 4 * ww, q + 1, a.tbl.hdr + 3);
+        for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncSub + 4 * ww, q + 1, a.err);
         // the streaming waves' sums, added in wave order
 #pragma unroll
-        for (int ww = 0; ww < kStream; ++ww)
+        for (int ww = 0; ww < (DEC ? 0 : kStream); ++ww)
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -1410,20 +1921,30 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
               const v4f x = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
               acc[rt][n] = ww == 0 ? x : acc[rt][n] + x;
             }
-        if (l == 0) lds_st4(sy + kSyncAck, static_cast<uint32_t>(q + 1));
-        control_block<NT>(a, m, lb, n_groups, S, half, lbk, acc, gen);
+        if constexpr (DEC) {
+          dec_publish(a, m, lb, n_groups, n_chunks, S, half, lbk, q, gen);
+          if (l == 0) lds_st4(sy + kSyncAck, static_cast<uint32_t>(q + 1));
+        } else {
+          if (l == 0) lds_st4(sy + kSyncAck, static_cast<uint32_t>(q + 1));
+          control_block<NT>(a, m, lb, n_groups, S, half, lbk, acc, gen);
+        }
       }
     }
     int i = 0;  // FC2 chunks of the workgroup loaded so far
     for (int h = 2; h < 4; ++h) {
       int first;
-      const int cnt = fc2_span(a, make_slice(a, n_chunks, h), first);
+      const Slice S2 = make_slice(a, n_chunks, h);
+      const int cnt = fc2_span(a, S2, first);
+      const int c_lo = h == 2 ? 0 : (n_chunks + 1) / 2;
       for (int c = first; c < first + cnt; ++c, ++i) {
-        wait_chunk(a, c, gen);
+        if (!DEC) wait_chunk(a, c, gen);
         if (i >= 2)  // buffer i&1 held chunk i-2: every wave must have moved past it
 #pragma unroll
-          for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncProg + 4 * ww, i - 1, a.tbl.hdr + 3);
-        control_hidden<NT, NS2>(a, m, lb, n_groups, c, static_cast<uint32_t>(i & 1));
+          for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncProg + 4 * ww, i - 1, a.err);
+        if constexpr (DEC)
+          dec_hidden(a, m, lb, n_groups, n_chunks, c, static_cast<uint32_t>(i & 1), S2.lo <= (c - c_lo) * a.U2, gen);
+        else
+          control_hidden<NT, NS2>(a, m, lb, n_groups, c, static_cast<uint32_t>(i & 1));
         if (l == 0) lds_st4(sy + kSyncReady + 4 * (i & 1), static_cast<uint32_t>(i));
       }
     }
@@ -1447,7 +1968,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
     while (sub_h < 2) {
       if (sub_b <= sub_last) {
         if (sub.base + sub_b >= upto) break;
-        lds_wait<false>(sy + kSyncAck, sub_q - 1, a.tbl.hdr + 3);  // slot sub_q&1 is free once block sub_q-2 is taken
+        lds_wait<false>(sy + kSyncAck, sub_q - 1, a.err);  // slot sub_q&1 is free once block sub_q-2 is taken
         mfma_settle(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -1468,20 +1989,22 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
     }
   };
 
-  // the plan (x codes and scales) as a buffer: padded columns and pads load zeros from outside it
-  const __amdgpu_buffer_rsrc_t xrsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.xcodes), static_cast<short>(0), a.plan_bytes, 0x00020000);
+  // the plan (x codes and scales) as a buffer: padded columns and pads load zeros from
+  // outside it (decode form: an empty buffer, for the pads)
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      DEC ? static_cast<void*>(a.out) : const_cast<uint8_t*>(a.xcodes), static_cast<short>(0),
+      DEC ? 0u : a.plan_bytes, 0x00020000);
   Cursor pc;  // issue cursor, R items ahead of consumption
   pc.h = -1;
   pc.s = pc.s_hi = 0;
   pc.b = pc.hi = 0;
-  cursor_next(a, m, lb, n_groups, n_chunks, pc);
+  cursor_next<DEC>(a, m, lb, n_groups, n_chunks, pc);
   int n_real = 0;  // real items issued (they precede the dummies)
   auto issue_next = [&](int k) {
-    issue_item<NS2, R>(a, m, lb, pc, k, xrsrc);
+    issue_item<NS2, R, DEC>(a, m, lb, pc, k, xrsrc);
     if (pc.h < 4) {
       ++n_real;
-      cursor_next(a, m, lb, n_groups, n_chunks, pc);
+      cursor_next<DEC>(a, m, lb, n_groups, n_chunks, pc);
     }
   };
   // FC2 state of the chunk in use: per lane, its output row (or -1) and its column's
@@ -1489,6 +2012,10 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   int cur_seq = -1, orow = -1;
   uint32_t hbl = 0, hbs = 0;
   const int col = l & 15;
+  // decode form, FC1: the chunk whose x rows the lane's column addresses hold
+  int x_chunk = -1;
+  uint32_t pxl = 0, pxsl = 0;
+#pragma unroll 1
   for (int k = 0; k < R; ++k) issue_next(k);  // R items in flight
   for (int kc = 0;; ++kc) {
     const bool real = kc < n_real;
@@ -1511,7 +2038,21 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
     wait_vm<G::VM>();  // item kc has landed (the R-1 younger items may still be in flight)
     if (type == 0) {
       Fc1Ops op;
-      fc1_read(sa_ + l * 16, sa_ + l * 4, op);
+      if constexpr (DEC) {
+        const int xc = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.z));
+        const int xsp = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.w));
+        if (xc != x_chunk) {
+          x_chunk = xc;
+          const GroupInfo xgi = group_of(m, lb, n_groups, xc);
+          const int pair = column_pair(m, lb, xgi, xgi.cc * 16 + col);
+          const int t = pair >= 0 ? pair / a.K : a.B;  // padded columns read the zero row
+          pxl = lb + m.xq + t * m.xstr + 16 * grp;
+          pxsl = lb + m.xs + t * m.xss;
+        }
+        fc1_read_dec(sa_ + l * 16, sa_ + l * 4, pxl + 256 * xsp, pxsl + 8 * xsp, op);
+      } else {
+        fc1_read(sa_ + l * 16, sa_ + l * 4, op);
+      }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const v8i bop = fp8_operand(op.x[2 * st], op.x[2 * st + 1]);
@@ -1530,7 +2071,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
       const int seq = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.w));
       if (seq != cur_seq) {
         if (l == 0) lds_st4(sy + kSyncProg + 4 * w, static_cast<uint32_t>(seq));
-        lds_wait<true>(sy + kSyncReady + 4 * (seq & 1), seq, a.tbl.hdr + 3);
+        lds_wait<true>(sy + kSyncReady + 4 * (seq & 1), seq, a.err);
         cur_seq = seq;
         const GroupInfo hgi = group_of(m, lb, n_groups, __builtin_amdgcn_readfirstlane(static_cast<int>(meta.y)));
         const int pair = column_pair(m, lb, hgi, hgi.cc * 16 + col);
@@ -1584,21 +2125,33 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
 
 using ExpertsFn = void (*)(ExpArgs);
 
-template <int R>
+template <int R, bool DEC>
 ExpertsFn pick_ns2(int ns2) {
-  if (ns2 == 1) return experts_kernel<1, 1, R>;
-  if (ns2 == 2) return experts_kernel<1, 2, R>;
-  if (ns2 == 3) return experts_kernel<1, 3, R>;
-  return experts_kernel<1, 4, R>;
+  if (ns2 == 1) return experts_kernel<1, 1, R, DEC>;
+  if (ns2 == 2) return experts_kernel<1, 2, R, DEC>;
+  if (ns2 == 3) return experts_kernel<1, 3, R, DEC>;
+  return experts_kernel<1, 4, R, DEC>;
 }
 
-// Kernel variants: NS2 = ceil(I/128) FC2 K steps x ring depth R (4, else what fits).
-ExpertsFn pick_kernel(int ns2, int R) { return R >= 4 ? pick_ns2<4>(ns2) : (R == 3 ? pick_ns2<3>(ns2) : pick_ns2<2>(ns2)); }
+// Kernel variants: form (grouped / decode) x NS2 = ceil(I/128) FC2 K steps x ring depth
+// R (4, else what fits).
+template <bool DEC>
+ExpertsFn pick_kernel(int ns2, int R) {
+  return R >= 4 ? pick_ns2<4, DEC>(ns2) : (R == 3 ? pick_ns2<3, DEC>(ns2) : pick_ns2<2, DEC>(ns2));
+}
 
-// LDS bytes of the variant with ring depth R.
-size_t lds_for(int R, int g_cap, int u_cap, int IP) {
-  return R >= 4 ? lds_bytes<1, 4>(g_cap, u_cap, IP)
-                : (R == 3 ? lds_bytes<1, 3>(g_cap, u_cap, IP) : lds_bytes<1, 2>(g_cap, u_cap, IP));
+// LDS bytes of a variant (B, D: decode form's x plan).
+template <int R, bool DEC>
+size_t lds_ns2(int ns2, int g_cap, int u_cap, int IP, int B, int D) {
+  if (ns2 == 1) return lds_bytes<1, R, 1, DEC>(g_cap, u_cap, IP, B, D);
+  if (ns2 == 2) return lds_bytes<1, R, 2, DEC>(g_cap, u_cap, IP, B, D);
+  if (ns2 == 3) return lds_bytes<1, R, 3, DEC>(g_cap, u_cap, IP, B, D);
+  return lds_bytes<1, R, 4, DEC>(g_cap, u_cap, IP, B, D);
+}
+template <bool DEC>
+size_t lds_for(int R, int ns2, int g_cap, int u_cap, int IP, int B, int D) {
+  return R >= 4 ? lds_ns2<4, DEC>(ns2, g_cap, u_cap, IP, B, D)
+                : (R == 3 ? lds_ns2<3, DEC>(ns2, g_cap, u_cap, IP, B, D) : lds_ns2<2, DEC>(ns2, g_cap, u_cap, IP, B, D));
 }
 
 // ------------------------------------------------------------------ host helpers
@@ -1662,6 +2215,95 @@ int ws_batch_capacity(int E, int D, int I, int K, size_t ws_bytes) {
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+// Checks, kernel variant, grid and arguments shared by both forms; enqueues one launch.
+template <bool DEC>
+int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* plan, const void* units,
+                size_t units_bytes, const void* x, const int32_t* ids, int32_t B, int32_t topk, void* ws,
+                size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
+  if (!wts || !ws || !out || B < 1 || topk < 1 || topk > 64 ||
+      static_cast<int64_t>(B) * topk > 65535)  // pair indices are cached as u16, 0xffff = padding
+    return MOE_EINVAL;
+  const int E = wts->E, D = wts->D, I = wts->I;
+  if (!shape_ok(E, D, I) || !wts->w13 || !wts->s13 || !wts->w2 || !wts->s2) return MOE_EINVAL;
+  moe_run_opts_t o;
+  std::memset(&o, 0, sizeof(o));
+  if (opts) o = *opts;
+  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 1) ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) ||
+      ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
+    return MOE_EINVAL;
+  if (!DEC && (o.plan_dev != nullptr || o.status_dev != nullptr)) return MOE_EINVAL;  // decode-form options
+  if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
+  if (!DEC && units_bytes < units_layout(B, topk, E).end) return MOE_ENOSPACE;
+  if (DEC && o.plan_bytes != 0 && o.plan_dev == nullptr) return MOE_EINVAL;
+  if (DEC && o.plan_dev != nullptr && o.plan_bytes < static_cast<size_t>(B) * D / 32 * 33) return MOE_ENOSPACE;
+  const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
+  if (B_cap < B) return MOE_ENOSPACE;
+  const WsLayout L = ws_layout(E, D, I, topk, B_cap);
+  const int64_t U = static_cast<int64_t>(B) * topk;
+  const int g_cap = static_cast<int>(U < E ? U : E);
+  const int64_t u_bound = g_cap + (U + 7) / 8;
+  const int u_cap = DEC ? g_cap : static_cast<int>(U < u_bound ? U : u_bound);
+  const int IP = (I + 127) / 128 * 128, ns2 = IP / 128;
+  // the deepest ring that fits next to the unit table (and the decode form's x plan)
+  int R = o.ring ? o.ring : 4;
+  if (!o.ring)
+    while (R > 2 && lds_for<DEC>(R, ns2, g_cap, u_cap, IP, B, D) > static_cast<size_t>(device_lds_limit())) --R;
+  const size_t lds = lds_for<DEC>(R, ns2, g_cap, u_cap, IP, B, D);
+  if (lds > static_cast<size_t>(device_lds_limit())) return MOE_EINVAL;  // unit table too large for LDS
+  const ExpertsFn fn = pick_kernel<DEC>(ns2, R);
+  if (!prepare_kernel(fn, lds)) return MOE_EHIP;
+  const int cap = resident_grid(fn, lds);
+  if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
+  const int grid = o.grid ? o.grid : cap;
+
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  ExpArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.w13p = static_cast<const uint8_t*>(wts->w13);
+  a.s13p = static_cast<const uint8_t*>(wts->s13);
+  a.w2p = static_cast<const uint8_t*>(wts->w2);
+  a.s2p = static_cast<const uint8_t*>(wts->s2);
+  if (DEC) {
+    a.x = static_cast<const uint16_t*>(x);
+    a.ids = ids;
+    a.plan_dump = static_cast<uint8_t*>(o.plan_dev);
+    a.err = o.status_dev ? static_cast<int32_t*>(o.status_dev) : reinterpret_cast<int32_t*>(base + L.status);
+    a.dpart = reinterpret_cast<uint64_t*>(base + L.partials);
+  } else {
+    a.xcodes = static_cast<const uint8_t*>(plan);
+    a.xscales = a.xcodes + static_cast<int64_t>(B) * D;
+    a.plan_bytes = static_cast<uint32_t>(static_cast<int64_t>(B) * D / 32 * 33);
+    a.tbl = table_at(static_cast<uint8_t*>(const_cast<void*>(units)), units_layout(B, topk, E));
+    a.err = a.tbl.hdr + 3;
+  }
+  a.calls = reinterpret_cast<uint32_t*>(base + L.calls);
+  a.arrive = reinterpret_cast<uint32_t*>(base + L.arrive);
+  a.flags = reinterpret_cast<uint32_t*>(base + L.flags);
+  a.hcodes = base + L.hcodes;
+  a.hscales = base + L.hscales;
+  a.partials = reinterpret_cast<float*>(base + L.partials);
+  a.out = static_cast<uint16_t*>(out);
+  a.dump_codes = static_cast<uint8_t*>(o.hidden_codes_dev);
+  a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
+  a.D = D;
+  a.I = I;
+  a.HB = I / 32;
+  a.NS1 = D / 128;
+  a.NSP = a.NS1 / 2;
+  a.U2 = D / 16 / (ns2 == 1 ? 8 : (ns2 == 2 ? 4 : 2));
+  a.IP = IP;
+  a.g_cap = g_cap;
+  a.u_cap = u_cap;
+  a.K = topk;
+  a.B = B;
+  a.E = E;
+  a.qmin = DEC ? (a.NSP + 2) / 3 : 0;
+  a.floor_rule = o.hidden_rule == 2 || (o.hidden_rule == 0 && I == 384);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kWG), lds, as_stream(stream), a);
+  return launch_status();
+}
 
 }  // namespace
 
@@ -1789,76 +2431,15 @@ int moe_units_export(const void* units, size_t units_bytes, int32_t B, int32_t t
 int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* plan, const void* units,
                     size_t units_bytes, int32_t B, int32_t topk, void* ws, size_t ws_bytes, void* out,
                     size_t out_bytes, void* stream) {
-  if (!wts || !plan || !units || !ws || !out || B < 1 || topk < 1 || topk > 64 ||
-      static_cast<int64_t>(B) * topk > 65535)  // pair indices are cached as u16, 0xffff = padding
-    return MOE_EINVAL;
-  const int E = wts->E, D = wts->D, I = wts->I;
-  if (!shape_ok(E, D, I) || !wts->w13 || !wts->s13 || !wts->w2 || !wts->s2) return MOE_EINVAL;
-  moe_run_opts_t o;
-  std::memset(&o, 0, sizeof(o));
-  if (opts) o = *opts;
-  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 1) ||
-      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) ||
-      ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
-    return MOE_EINVAL;
-  if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
-  const UnitsLayout UL = units_layout(B, topk, E);
-  if (units_bytes < UL.end) return MOE_ENOSPACE;
-  const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
-  if (B_cap < B) return MOE_ENOSPACE;
-  const WsLayout L = ws_layout(E, D, I, topk, B_cap);
-  const int64_t U = static_cast<int64_t>(B) * topk;
-  const int g_cap = static_cast<int>(U < E ? U : E);
-  const int64_t u_bound = g_cap + (U + 7) / 8;
-  const int u_cap = static_cast<int>(U < u_bound ? U : u_bound);
-  const int IP = (I + 127) / 128 * 128;
-  // the deepest ring that fits next to the unit table
-  int R = o.ring ? o.ring : 4;
-  if (!o.ring)
-    while (R > 2 && lds_for(R, g_cap, u_cap, IP) > static_cast<size_t>(device_lds_limit())) --R;
-  const size_t lds = lds_for(R, g_cap, u_cap, IP);
-  if (lds > static_cast<size_t>(device_lds_limit())) return MOE_EINVAL;  // unit table too large for LDS
-  const ExpertsFn fn = pick_kernel((I + 127) / 128, R);
-  if (!prepare_kernel(fn, lds)) return MOE_EHIP;
-  const int cap = resident_grid(fn, lds);
-  if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
-  const int grid = o.grid ? o.grid : cap;
+  if (!plan || !units) return MOE_EINVAL;
+  return run_experts<false>(wts, opts, plan, units, units_bytes, nullptr, nullptr, B, topk, ws, ws_bytes, out,
+                            out_bytes, stream);
+}
 
-  uint8_t* base = static_cast<uint8_t*>(ws);
-  ExpArgs a;
-  a.w13p = static_cast<const uint8_t*>(wts->w13);
-  a.s13p = static_cast<const uint8_t*>(wts->s13);
-  a.w2p = static_cast<const uint8_t*>(wts->w2);
-  a.s2p = static_cast<const uint8_t*>(wts->s2);
-  a.xcodes = static_cast<const uint8_t*>(plan);
-  a.xscales = a.xcodes + static_cast<int64_t>(B) * D;
-  a.plan_bytes = static_cast<uint32_t>(static_cast<int64_t>(B) * D / 32 * 33);
-  a.tbl = table_at(static_cast<uint8_t*>(const_cast<void*>(units)), UL);
-  a.calls = reinterpret_cast<uint32_t*>(base + L.calls);
-  a.arrive = reinterpret_cast<uint32_t*>(base + L.arrive);
-  a.flags = reinterpret_cast<uint32_t*>(base + L.flags);
-  a.hcodes = base + L.hcodes;
-  a.hscales = base + L.hscales;
-  a.partials = reinterpret_cast<float*>(base + L.partials);
-  a.out = static_cast<uint16_t*>(out);
-  a.dump_codes = static_cast<uint8_t*>(o.hidden_codes_dev);
-  a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
-  a.D = D;
-  a.I = I;
-  a.HB = I / 32;
-  a.NS1 = D / 128;
-  a.NSP = a.NS1 / 2;
-  {
-    const int ns2 = (I + 127) / 128, t2 = ns2 == 1 ? 8 : (ns2 == 2 ? 4 : 2);
-    a.U2 = D / 16 / t2;
-  }
-  a.IP = (I + 127) / 128 * 128;
-  a.g_cap = g_cap;
-  a.u_cap = u_cap;
-  a.K = topk;
-  a.floor_rule = o.hidden_rule == 2 || (o.hidden_rule == 0 && I == 384);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kWG), lds, as_stream(stream), a);
-  return launch_status();
+int moe_decode_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* x, const int32_t* ids,
+                   int32_t B, int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
+  if (!x || !ids || B > kDecodeMax) return MOE_EINVAL;
+  return run_experts<true>(wts, opts, nullptr, nullptr, 0, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
 }
 
 }  // extern "C"

@@ -2,9 +2,10 @@
 
 ``MoeLayer`` uploads canonical FP4/E8M0 weights once, packs them with
 ``moe_pack_weights`` (the canonical copies are freed), owns the workspace and the
-plan buffer, and runs one decode step as the three ABI calls the runtime page's
-PersistentExperts.run makes: plan (MXFP8 of x), units (moe_group), experts.
-torch only allocates memory and supplies the stream.
+plan buffer, and runs one decode step, either as one moe_decode_run launch (B <= 8: the
+experts kernel quantizes and routes the batch itself) or as the three ABI calls the
+runtime page's PersistentExperts.run makes: plan (MXFP8 of x), units (moe_group),
+experts.  torch only allocates memory and supplies the stream.
 """
 from __future__ import annotations
 
@@ -45,14 +46,24 @@ class MoeLayer:
     def out_buffer(self, B: int) -> torch.Tensor:
         return torch.empty(B * self.topk, self.D, dtype=torch.bfloat16, device=self.device)
 
+    DECODE_MAX = 8  # largest batch of the one-launch decode form
+    AUTO_DECODE = False  # "auto" picks the decode form for B <= DECODE_MAX only when set
+
     def forward(self, x: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None, *, replica: int = 0,
-                stream=None, **opts) -> torch.Tensor:
-        """x: BF16 [B, D] (or its uint16 bits), ids: int32 [B, topk], both on the device."""
+                stream=None, path: str = "auto", **opts) -> torch.Tensor:
+        """x: BF16 [B, D] (or its uint16 bits), ids: int32 [B, topk], both on the device.
+        path: "decode" (one launch, B <= 8), "grouped" (plan + units + experts) or "auto"
+        (the decode form for B <= 8 when AUTO_DECODE is set, else grouped)."""
         B = x.shape[0]
         if B > self.B_max or ids.shape != (B, self.topk):
             raise ValueError("batch larger than B_max or ids of the wrong shape")
+        if path not in ("auto", "decode", "grouped"):
+            raise ValueError(f"unknown path {path!r}")
         if out is None:
             out = self.out_buffer(B)
+        if path == "decode" or (path == "auto" and self.AUTO_DECODE and B <= self.DECODE_MAX):
+            _lib.moe_decode_run(self.structs[replica], x, ids, self.ws, out, stream=stream, **opts)
+            return out
         _lib.moe_plan(x, self.plan, stream=stream)
         _lib.moe_group(ids, self.E, self.units, stream=stream)
         _lib.moe_experts_run(self.structs[replica], self.plan, self.units, B, self.topk, self.ws, out, stream=stream,
@@ -63,6 +74,15 @@ class MoeLayer:
         """The experts kernel alone, on the plan and unit table of the last forward()."""
         _lib.moe_experts_run(self.structs[replica], self.plan, self.units, B, self.topk, self.ws, out, stream=stream,
                              **opts)
+
+    def combine(self, rows: torch.Tensor, weights: torch.Tensor, y: torch.Tensor | None = None, *, stream=None):
+        """Weighted top-k combine of the BF16 rows [B*topk, D] with FP32 weights [B, topk]
+        into BF16 y [B, D]."""
+        B = weights.shape[0]
+        if y is None:
+            y = torch.empty(B, self.D, dtype=torch.bfloat16, device=self.device)
+        _lib.moe_combine(rows, weights, y, stream=stream)
+        return y
 
     def unit_table(self, B: int):
         """The unit table moe_group left in the workspace: (header[4], unit_expert, unit_rows)."""

@@ -122,3 +122,35 @@ def test_combine_argument_checks():
     assert L.moe_combine(fake, big, fake, 0, 4, 512, fake, big, None) == m._lib.MOE_EINVAL
     assert L.moe_combine(fake, 4 * 512 * 2 - 1, fake, 1, 4, 512, fake, big, None) == m._lib.MOE_ENOSPACE
     assert L.moe_combine(fake, big, fake, 1, 4, 512, fake, 512 * 2 - 1, None) == m._lib.MOE_ENOSPACE
+
+
+def test_decode_run_argument_checks(m):
+    """moe_decode_run (the one-launch form for B <= 8) checks its arguments on the host;
+    the decode-only options are refused by moe_experts_run."""
+    L = m._lib.lib
+    fake = ctypes.c_void_p(0x1000)
+    big = 10**9
+    w = m.moe_weights_t(16, 512, 128, 0x1000, 0x1000, 0x1000, 0x1000)
+
+    def dec(B, K, ws=big, out=big, opts=None, x=fake, ids=fake):
+        o = opts if opts is not None else m.moe_run_opts_t()
+        return L.moe_decode_run(ctypes.byref(w), ctypes.byref(o), x, ids, B, K, fake, ws, fake, out, None)
+
+    assert dec(9, 4) == m._lib.MOE_EINVAL                    # more than 8 tokens
+    assert dec(0, 4) == m._lib.MOE_EINVAL
+    assert dec(1, 0) == m._lib.MOE_EINVAL
+    assert dec(1, 4, x=None) == m._lib.MOE_EINVAL
+    assert dec(1, 4, ids=None) == m._lib.MOE_EINVAL
+    assert dec(2, 4, out=2 * 4 * 512 * 2 - 1) == m._lib.MOE_ENOSPACE
+    assert dec(2, 4, ws=100) == m._lib.MOE_ENOSPACE
+    o = m.moe_run_opts_t()
+    o.plan_dev, o.plan_bytes = 0x1000, 2 * 512 // 32 * 33 - 1  # plan dump too small
+    assert dec(2, 4, opts=o) == m._lib.MOE_ENOSPACE
+    o.plan_dev, o.plan_bytes = None, 64                        # a size without a buffer
+    assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL
+    o = m.moe_run_opts_t()
+    o.status_dev = 0x1000
+    assert L.moe_experts_run(ctypes.byref(w), ctypes.byref(o), fake, fake, big, 1, 4, fake, big, fake, big,
+                             None) == m._lib.MOE_EINVAL
+    # a workspace sized for decode batches serves every B <= B_max of the form
+    assert m.moe_workspace_bytes(160, 3584, 384, 8, 16) >= m.moe_workspace_bytes(160, 3584, 384, 1, 16)

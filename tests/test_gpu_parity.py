@@ -180,10 +180,11 @@ def test_units_edge_cases(lib):
 # --------------------------------------------------------------------------- experts
 @pytest.mark.parametrize("name", ["tiny", "decode_b1", "decode_b8", "grouped_b64"])
 def test_experts_full(lib, name):
+    """The three-call form (plan, units, experts kernel) on the full workloads."""
     log(f"experts {name}")
     d = workloads.generate(name)
     layer = _layer(lib, d)
-    got, hc, hs = _run(layer, d)
+    got, hc, hs = _run(layer, d, path="grouped")
     ref = _oracle(d)
     _check_all(d, got, hc, hs, ref, what=name)
 
@@ -290,3 +291,109 @@ def test_routes_independent_of_batch(lib):
         d1["workload"] = workloads.custom("one", B=1, E=5, K=2, D=1024, I=128)
         one, _, _ = _run(layer, d1, grid=1)
         assert np.array_equal(one, full[t * 2:(t + 1) * 2])
+
+
+# --------------------------------------------------------------------------- decode form
+def _decode_run(lib, layer, d, **opts):
+    """moe_decode_run on d's batch: rows, hidden dump, the plan it computed, status."""
+    m, _ = lib
+    w = d["workload"]
+    plan = torch.zeros(m.moe_plan_bytes(w.B, w.D), dtype=torch.uint8, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got, hc, hs = _run(layer, d, path="decode", plan=plan, status=status, **opts)
+    return got, hc, hs, plan.cpu().numpy(), int(status.cpu().numpy()[0])
+
+
+def _check_plan(d, p):
+    B, D = d["x"].shape
+    codes, scales = oracle.plan(d["x"])
+    assert np.array_equal(p[:B * D].reshape(B, D), codes), "plan codes"
+    assert np.array_equal(p[B * D:B * D * 33 // 32].reshape(B, D // 32), scales), "plan scales"
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode_b1", "decode_b8"])
+def test_decode_form_full(lib, name):
+    """The one-launch form (routing and the MXFP8 plan inside the experts kernel, FC1
+    partials reduced by the FC2 side) on the full decode workloads."""
+    log(f"decode form {name}")
+    d = workloads.generate(name)
+    layer = _layer(lib, d)
+    got, hc, hs, plan, status = _decode_run(lib, layer, d)
+    assert status == 0
+    _check_plan(d, plan)
+    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/{name}")
+
+
+DEC_SMALL = [
+    # (name, B, E, K, D, I, routing)
+    ("one_token", 1, 8, 3, 512, 64, "uniform"),
+    ("b8_ragged_I", 8, 12, 6, 1024, 96, "zipf"),      # I % 128 != 0, shared experts
+    ("b5_topk16", 5, 40, 16, 1536, 160, "zipf"),
+    ("b3_k1", 3, 6, 1, 512, 128, "uniform"),
+]
+# (grid, ring): default; one workgroup (it reduces its own partials); small grids (long
+# slices); grids that split hidden blocks over several owners; shallower rings
+DEC_VARIANTS = [(0, 0), (1, 0), (7, 2), (33, 2), (200, 0)]
+
+
+@pytest.mark.parametrize("case", DEC_SMALL, ids=[c[0] for c in DEC_SMALL])
+@pytest.mark.parametrize("grid,ring", DEC_VARIANTS)
+def test_decode_form_small_shapes(lib, case, grid, ring):
+    name, B, E, K, D, I, routing = case
+    log(f"decode form small {name} grid={grid} ring={ring}")
+    d = workloads.generate(workloads.custom(name, B=B, E=E, K=K, D=D, I=I, routing=routing, seed=12))
+    layer = _layer(lib, d, B_max=8)
+    got, hc, hs, plan, status = _decode_run(lib, layer, d, grid=grid, ring=ring)
+    assert status == 0
+    _check_plan(d, plan)
+    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/{name}/{grid}/{ring}")
+
+
+@pytest.mark.parametrize("grid", [0, 1, 40])
+def test_decode_form_eight_tokens_one_expert(lib, grid):
+    """All 8 tokens on one expert at the full decode shape: 8 token columns, 12 hidden
+    blocks of 14 FC1 items each split over up to four owners."""
+    log(f"decode form 8 tokens x 1 expert grid={grid}")
+    d = workloads.generate(workloads.custom("one_expert", B=8, E=160, K=1, D=3584, I=384, scale_lo=-9, scale_hi=-5,
+                                            seed=13))
+    d["ids"][:] = 77
+    layer = _layer(lib, d)
+    got, hc, hs, plan, status = _decode_run(lib, layer, d, grid=grid)
+    assert status == 0
+    _check_plan(d, plan)
+    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/one_expert/{grid}")
+
+
+def test_decode_form_flags_bad_ids(lib):
+    """An id out of range is skipped and an id repeated within a token loses one of its
+    routes; both are flagged in the status word, and every other route is exact."""
+    log("decode form bad ids")
+    d = workloads.generate(workloads.custom("bad", B=2, E=10, K=4, D=512, I=64, seed=14))
+    good = np.array([[1, 3, 9, 5], [2, 4, 7, 0]], np.int32)
+    d["ids"] = good.copy()
+    bad = good.copy()
+    bad[0, 2] = 12      # out of range
+    bad[1, 1] = 2       # token 1 names expert 2 twice
+    layer = _layer(lib, d)
+    db = dict(d)
+    db["ids"] = bad
+    got, hc, hs, plan, status = _decode_run(lib, layer, db)
+    assert status == 3
+    _check_plan(d, plan)
+    keep = np.array([0, 1, 3, 6, 7], np.int32)     # routes (0,0) (0,1) (0,3) (1,2) (1,3)
+    _check_all(d, got, hc, hs, _oracle(d, routes=keep), routes=keep, what="decode/bad_ids")
+
+
+def test_decode_form_matches_grouped_form_repeatedly(lib):
+    """Decode-form calls re-arm the workspace like grouped ones: a decode call, a grouped
+    B=64 call and a decode call of another size in between, then the same decode call
+    again gives the same rows bit for bit."""
+    log("decode form repeat")
+    d = workloads.generate("decode_b8")
+    layer = _layer(lib, d, B_max=64)
+    a, _, _, _, _ = _decode_run(lib, layer, d)
+    d64 = workloads.generate("grouped_b64", with_weights=False)
+    layer.forward(torch.from_numpy(d64["x"]).to(DEV), torch.from_numpy(d64["ids"] % d["workload"].E).to(DEV))
+    layer.forward(torch.from_numpy(d["x"][:3]).to(DEV), torch.from_numpy(d["ids"][:3]).to(DEV), path="decode")
+    b, _, _, _, _ = _decode_run(lib, layer, d)
+    assert np.array_equal(a, b)
