@@ -97,7 +97,7 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
     # steps per graph: the largest divisor of `steps` up to graph_steps, so that exactly
     # `steps` steps are timed
     G = max(gs for gs in range(1, min(graph_steps, steps) + 1) if steps % gs == 0)
-    decode = path == "decode" or (path == "auto" and MoeLayer.AUTO_DECODE and w.B <= MoeLayer.DECODE_MAX)
+    decode = w.B <= MoeLayer.DECODE_MAX and (path == "decode" or (path == "auto" and MoeLayer.AUTO_DECODE))
     form = "decode" if decode else "grouped"
 
     for i in range(warmup):
@@ -234,7 +234,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying HIP graphs")
     ap.add_argument("--path", default="auto", choices=("auto", "decode", "grouped"),
-                    help="step form: one decode launch (B <= 8), the three-call grouped form, or auto")
+                    help="step form for B <= 8: one decode launch, the three-call grouped form, or auto "
+                         "(larger batches always use the grouped form)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
     args = ap.parse_args()

@@ -150,7 +150,12 @@ typedef struct {
                          width; other values are MOE_EINVAL) */
   int32_t ring;       /* weight items in flight per streaming wave (2..4); 0 = the deepest
                          that fits in LDS next to the unit table */
-  int32_t reserved[4];
+  int32_t exchange;   /* moe_decode_run only: how FC1 results reach FC2 -- 0 = finished
+                         hidden blocks (the owner of a block's first step adds the other
+                         owners' partial sums, applies SwiGLU and MXFP8, publishes codes and
+                         a call-tagged flag), 1 = call-tagged FC1 partial sums that every
+                         FC2 workgroup reduces itself; other values MOE_EINVAL */
+  int32_t reserved[3];
   void* hidden_codes_dev;  /* optional u8 [B*topk, I]: the hidden's e4m3 codes per route */
   void* hidden_scales_dev; /* optional u8 [B*topk, I/32]: its E8M0 scales */
   /* moe_decode_run only (MOE_EINVAL for moe_experts_run when set): */
@@ -185,9 +190,10 @@ int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
  * its tokens in token order, the same table moe_group writes for such a batch).
  * Inputs x_dev BF16 [B, D] and ids_dev i32 [B, topk]; outputs as moe_experts_run
  * (out_dev BF16 [B*topk, D], top-k order; optional hidden dump), plus the optional plan
- * and status word of moe_run_opts_t.  The FC1 -> FC2 exchange goes through call-tagged
- * FC1 partial sums in the workspace (moe_workspace_bytes sizes them), which each FC2
- * workgroup reduces itself.  Ids out of range are skipped and flagged (status bit 0).
+ * and status word of moe_run_opts_t.  The FC1 -> FC2 exchange is chosen by
+ * opts->exchange (finished hidden blocks by default, or call-tagged partial sums; the
+ * workspace from moe_workspace_bytes holds either).  Ids out of range are skipped and
+ * flagged (status bit 0).
  * Errors: MOE_EINVAL for B > 8 or the cases of moe_experts_run; MOE_ENOSPACE likewise.
  * The same residency and no-overlap rules as moe_experts_run apply. */
 int moe_decode_run(const moe_weights_t* weights, const moe_run_opts_t* opts, const void* x_dev,

@@ -30,7 +30,8 @@ class moe_weights_t(ctypes.Structure):
 
 class moe_run_opts_t(ctypes.Structure):
     _fields_ = [("hidden_rule", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("col_tiles", ctypes.c_int32), ("ring", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4),
+                ("col_tiles", ctypes.c_int32), ("ring", ctypes.c_int32), ("exchange", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3),
                 ("hidden_codes_dev", ctypes.c_void_p), ("hidden_scales_dev", ctypes.c_void_p),
                 ("plan_dev", ctypes.c_void_p), ("plan_bytes", ctypes.c_size_t), ("status_dev", ctypes.c_void_p)]
 
@@ -139,8 +140,8 @@ def moe_units_export(units, B, topk, E, header, unit_expert, unit_rows, stream=N
                                                     _stream(stream)))
 
 
-def _opts(hidden_rule, grid, col_tiles, ring, hidden_codes, hidden_scales, plan=None, status=None):
-    return moe_run_opts_t(hidden_rule, grid, col_tiles, ring, (ctypes.c_int32 * 4)(0, 0, 0, 0),
+def _opts(hidden_rule, grid, col_tiles, ring, hidden_codes, hidden_scales, plan=None, status=None, exchange=0):
+    return moe_run_opts_t(hidden_rule, grid, col_tiles, ring, exchange, (ctypes.c_int32 * 3)(0, 0, 0),
                           _ptr(hidden_codes), _ptr(hidden_scales), _ptr(plan), 0 if plan is None else _nbytes(plan),
                           _ptr(status))
 
@@ -153,13 +154,14 @@ def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, 
                                                   _ptr(out), _nbytes(out), _stream(stream)))
 
 
-def moe_decode_run(weights: moe_weights_t, x, ids, ws, out, *, hidden_rule=0, grid=0, ring=0, hidden_codes=None,
-                   hidden_scales=None, plan=None, status=None, stream=None):
+def moe_decode_run(weights: moe_weights_t, x, ids, ws, out, *, hidden_rule=0, grid=0, ring=0, exchange=0,
+                   hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
     """The whole step of a batch of B <= 8 tokens in one launch: x BF16 [B, D] (or uint16
     bits), ids int32 [B, topk] -> out BF16 [B*topk, D]; optional plan (u8, the moe_plan
-    layout) and status (int32 [1]) outputs."""
+    layout) and status (int32 [1]) outputs; exchange 0 (finished hidden blocks) or 1
+    (tagged partial sums)."""
     B, K = ids.shape
-    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status)
+    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, exchange)
     _check("moe_decode_run", lib.moe_decode_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(x), _ptr(ids), B, K,
                                                 _ptr(ws), _nbytes(ws), _ptr(out), _nbytes(out), _stream(stream)))
 

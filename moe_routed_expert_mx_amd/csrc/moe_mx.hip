@@ -1756,7 +1756,7 @@ __device__ __forceinline__ void dec_hidden(const ExpArgs& a, const LdsMap& m, ui
   for (int done = 0; done < total; done += kRound) {
     const int nb = total - done < kRound ? total - done : kRound;
     // lane s: pair done + s -> block j (the last with cum[j] <= f), column, owner
-    uint64_t addr = 0;
+    uint32_t poff = 0;  // pair offset of the lane's slot (global loads index a.dpart with it)
     bool first = false, last = false;
     {
       const int f = done + l;
@@ -1782,23 +1782,22 @@ __device__ __forceinline__ void dec_hidden(const ExpArgs& a, const LdsMap& m, ui
         const int n = static_cast<int>(lds_ld4(tb + 64 + 4 * j));
         const int r = f - cum, c = r / n, k = r - c * n;
         const uint32_t sl = lds_ld4(tb + 128 + 4 * (4 * j + k));
-        addr = reinterpret_cast<uint64_t>(a.dpart + static_cast<size_t>(sl) * 512 + 64 * c);
+        poff = sl * 512 + 64 * c;
         first = k == 0;
         last = k == n - 1;
       }
     }
     const uint64_t fm = __ballot(first), lm = __ballot(last);
-    const uint32_t alo = static_cast<uint32_t>(addr), ahi = static_cast<uint32_t>(addr >> 32);
     uint64_t v[kRound];
 #pragma unroll 1
     for (uint32_t spins = 0;; ++spins) {
 #pragma unroll
       for (int s = 0; s < kRound; ++s) {
         if (s < nb) {
-          // slot s's address, broadcast through a VGPR (no scalar registers held per slot)
-          const uint64_t base = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl(static_cast<int>(ahi), s))) << 32) |
-                                static_cast<uint32_t>(__shfl(static_cast<int>(alo), s));
-          v[s] = ld_dev_u64(reinterpret_cast<const uint64_t*>(base) + l);
+          // slot s's pair offset from lane s; the load stays a global one (a generic one
+          // would also count against the LDS counter, and the waits would serialize them)
+          const uint32_t o = __builtin_amdgcn_readlane(poff, s);
+          v[s] = ld_dev_u64(a.dpart + o + l);
         }
       }
       bool ok = true;
@@ -1880,8 +1879,11 @@ __device__ __forceinline__ void dec_hidden(const ExpArgs& a, const LdsMap& m, ui
 // the streaming waves' FC1 sums of each block (LDS), files or finishes the block and
 // publishes its hidden, then polls for the hidden of each FC2 chunk the workgroup
 // needs and copies it into one of two LDS buffers.
-template <int NT, int NS2, int R, bool DEC>
+// DEC: the decode form's prologue and LDS plan of x; TAG (decode form only): the FC1 ->
+// FC2 exchange through tagged partial sums instead of finished hidden blocks.
+template <int NT, int NS2, int R, bool DEC, bool TAG>
 __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
+  static_assert(DEC || !TAG, "the tagged exchange belongs to the decode form");
   using G = Geo<NT, R, NS2, DEC>;
   const int l = threadIdx.x & 63, w = wave_id(), grp = l >> 4;
   const LdsMap m = lds_map<NT, R, NS2, DEC>(static_cast<uint32_t>(a.g_cap), static_cast<uint32_t>(a.u_cap),
@@ -1912,7 +1914,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
         for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncSub + 4 * ww, q + 1, a.err);
         // the streaming waves' sums, added in wave order
 #pragma unroll
-        for (int ww = 0; ww < (DEC ? 0 : kStream); ++ww)
+        for (int ww = 0; ww < (TAG ? 0 : kStream); ++ww)
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -1921,7 +1923,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
               const v4f x = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
               acc[rt][n] = ww == 0 ? x : acc[rt][n] + x;
             }
-        if constexpr (DEC) {
+        if constexpr (TAG) {
           dec_publish(a, m, lb, n_groups, n_chunks, S, half, lbk, q, gen);
           if (l == 0) lds_st4(sy + kSyncAck, static_cast<uint32_t>(q + 1));
         } else {
@@ -1937,11 +1939,11 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
       const int cnt = fc2_span(a, S2, first);
       const int c_lo = h == 2 ? 0 : (n_chunks + 1) / 2;
       for (int c = first; c < first + cnt; ++c, ++i) {
-        if (!DEC) wait_chunk(a, c, gen);
+        if (!TAG) wait_chunk(a, c, gen);
         if (i >= 2)  // buffer i&1 held chunk i-2: every wave must have moved past it
 #pragma unroll
           for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(sy + kSyncProg + 4 * ww, i - 1, a.err);
-        if constexpr (DEC)
+        if constexpr (TAG)
           dec_hidden(a, m, lb, n_groups, n_chunks, c, static_cast<uint32_t>(i & 1), S2.lo <= (c - c_lo) * a.U2, gen);
         else
           control_hidden<NT, NS2>(a, m, lb, n_groups, c, static_cast<uint32_t>(i & 1));
@@ -2125,19 +2127,19 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
 
 using ExpertsFn = void (*)(ExpArgs);
 
-template <int R, bool DEC>
+template <int R, bool DEC, bool TAG>
 ExpertsFn pick_ns2(int ns2) {
-  if (ns2 == 1) return experts_kernel<1, 1, R, DEC>;
-  if (ns2 == 2) return experts_kernel<1, 2, R, DEC>;
-  if (ns2 == 3) return experts_kernel<1, 3, R, DEC>;
-  return experts_kernel<1, 4, R, DEC>;
+  if (ns2 == 1) return experts_kernel<1, 1, R, DEC, TAG>;
+  if (ns2 == 2) return experts_kernel<1, 2, R, DEC, TAG>;
+  if (ns2 == 3) return experts_kernel<1, 3, R, DEC, TAG>;
+  return experts_kernel<1, 4, R, DEC, TAG>;
 }
 
-// Kernel variants: form (grouped / decode) x NS2 = ceil(I/128) FC2 K steps x ring depth
-// R (4, else what fits).
-template <bool DEC>
+// Kernel variants: form (grouped / decode, and the decode form's exchange) x NS2 =
+// ceil(I/128) FC2 K steps x ring depth R (4, else what fits).
+template <bool DEC, bool TAG>
 ExpertsFn pick_kernel(int ns2, int R) {
-  return R >= 4 ? pick_ns2<4, DEC>(ns2) : (R == 3 ? pick_ns2<3, DEC>(ns2) : pick_ns2<2, DEC>(ns2));
+  return R >= 4 ? pick_ns2<4, DEC, TAG>(ns2) : (R == 3 ? pick_ns2<3, DEC, TAG>(ns2) : pick_ns2<2, DEC, TAG>(ns2));
 }
 
 // LDS bytes of a variant (B, D: decode form's x plan).
@@ -2233,7 +2235,9 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
       (o.ring != 0 && (o.ring < 2 || o.ring > 4)) ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
     return MOE_EINVAL;
-  if (!DEC && (o.plan_dev != nullptr || o.status_dev != nullptr)) return MOE_EINVAL;  // decode-form options
+  if (!DEC && (o.plan_dev != nullptr || o.status_dev != nullptr || o.exchange != 0))
+    return MOE_EINVAL;  // decode-form options
+  if (o.exchange < 0 || o.exchange > 1) return MOE_EINVAL;
   if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
   if (!DEC && units_bytes < units_layout(B, topk, E).end) return MOE_ENOSPACE;
   if (DEC && o.plan_bytes != 0 && o.plan_dev == nullptr) return MOE_EINVAL;
@@ -2252,7 +2256,8 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
     while (R > 2 && lds_for<DEC>(R, ns2, g_cap, u_cap, IP, B, D) > static_cast<size_t>(device_lds_limit())) --R;
   const size_t lds = lds_for<DEC>(R, ns2, g_cap, u_cap, IP, B, D);
   if (lds > static_cast<size_t>(device_lds_limit())) return MOE_EINVAL;  // unit table too large for LDS
-  const ExpertsFn fn = pick_kernel<DEC>(ns2, R);
+  const bool tag = DEC && o.exchange == 1;
+  const ExpertsFn fn = tag ? pick_kernel<DEC, DEC>(ns2, R) : pick_kernel<DEC, false>(ns2, R);
   if (!prepare_kernel(fn, lds)) return MOE_EHIP;
   const int cap = resident_grid(fn, lds);
   if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
@@ -2299,7 +2304,7 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   a.K = topk;
   a.B = B;
   a.E = E;
-  a.qmin = DEC ? (a.NSP + 2) / 3 : 0;
+  a.qmin = tag ? (a.NSP + 2) / 3 : 0;
   a.floor_rule = o.hidden_rule == 2 || (o.hidden_rule == 0 && I == 384);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kWG), lds, as_stream(stream), a);
   return launch_status();

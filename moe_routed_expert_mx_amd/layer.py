@@ -47,7 +47,7 @@ class MoeLayer:
         return torch.empty(B * self.topk, self.D, dtype=torch.bfloat16, device=self.device)
 
     DECODE_MAX = 8  # largest batch of the one-launch decode form
-    AUTO_DECODE = False  # "auto" picks the decode form for B <= DECODE_MAX only when set
+    AUTO_DECODE = True  # "auto" picks the decode form for B <= DECODE_MAX (faster at B = 1 and 8)
 
     def forward(self, x: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None, *, replica: int = 0,
                 stream=None, path: str = "auto", **opts) -> torch.Tensor:

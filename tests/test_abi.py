@@ -149,6 +149,13 @@ def test_decode_run_argument_checks(m):
     o.plan_dev, o.plan_bytes = None, 64                        # a size without a buffer
     assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL
     o = m.moe_run_opts_t()
+    o.exchange = 2
+    assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # no such exchange
+    o = m.moe_run_opts_t()
+    o.exchange = 1                                             # a decode-form option
+    assert L.moe_experts_run(ctypes.byref(w), ctypes.byref(o), fake, fake, big, 1, 4, fake, big, fake, big,
+                             None) == m._lib.MOE_EINVAL
+    o = m.moe_run_opts_t()
     o.status_dev = 0x1000
     assert L.moe_experts_run(ctypes.byref(w), ctypes.byref(o), fake, fake, big, 1, 4, fake, big, fake, big,
                              None) == m._lib.MOE_EINVAL

@@ -311,17 +311,21 @@ def _check_plan(d, p):
     assert np.array_equal(p[B * D:B * D * 33 // 32].reshape(B, D // 32), scales), "plan scales"
 
 
+EXCHANGES = [0, 1]  # finished hidden blocks; tagged partial sums reduced by the FC2 side
+
+
+@pytest.mark.parametrize("exchange", EXCHANGES)
 @pytest.mark.parametrize("name", ["tiny", "decode_b1", "decode_b8"])
-def test_decode_form_full(lib, name):
-    """The one-launch form (routing and the MXFP8 plan inside the experts kernel, FC1
-    partials reduced by the FC2 side) on the full decode workloads."""
-    log(f"decode form {name}")
+def test_decode_form_full(lib, name, exchange):
+    """The one-launch form (routing and the MXFP8 plan inside the experts kernel) with
+    either FC1 -> FC2 exchange, on the full decode workloads."""
+    log(f"decode form {name} exchange={exchange}")
     d = workloads.generate(name)
     layer = _layer(lib, d)
-    got, hc, hs, plan, status = _decode_run(lib, layer, d)
+    got, hc, hs, plan, status = _decode_run(lib, layer, d, exchange=exchange)
     assert status == 0
     _check_plan(d, plan)
-    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/{name}")
+    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/{name}/x{exchange}")
 
 
 DEC_SMALL = [
@@ -336,32 +340,34 @@ DEC_SMALL = [
 DEC_VARIANTS = [(0, 0), (1, 0), (7, 2), (33, 2), (200, 0)]
 
 
+@pytest.mark.parametrize("exchange", EXCHANGES)
 @pytest.mark.parametrize("case", DEC_SMALL, ids=[c[0] for c in DEC_SMALL])
 @pytest.mark.parametrize("grid,ring", DEC_VARIANTS)
-def test_decode_form_small_shapes(lib, case, grid, ring):
+def test_decode_form_small_shapes(lib, case, grid, ring, exchange):
     name, B, E, K, D, I, routing = case
-    log(f"decode form small {name} grid={grid} ring={ring}")
+    log(f"decode form small {name} grid={grid} ring={ring} exchange={exchange}")
     d = workloads.generate(workloads.custom(name, B=B, E=E, K=K, D=D, I=I, routing=routing, seed=12))
     layer = _layer(lib, d, B_max=8)
-    got, hc, hs, plan, status = _decode_run(lib, layer, d, grid=grid, ring=ring)
+    got, hc, hs, plan, status = _decode_run(lib, layer, d, grid=grid, ring=ring, exchange=exchange)
     assert status == 0
     _check_plan(d, plan)
-    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/{name}/{grid}/{ring}")
+    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/{name}/{grid}/{ring}/x{exchange}")
 
 
+@pytest.mark.parametrize("exchange", EXCHANGES)
 @pytest.mark.parametrize("grid", [0, 1, 40])
-def test_decode_form_eight_tokens_one_expert(lib, grid):
+def test_decode_form_eight_tokens_one_expert(lib, grid, exchange):
     """All 8 tokens on one expert at the full decode shape: 8 token columns, 12 hidden
     blocks of 14 FC1 items each split over up to four owners."""
-    log(f"decode form 8 tokens x 1 expert grid={grid}")
+    log(f"decode form 8 tokens x 1 expert grid={grid} exchange={exchange}")
     d = workloads.generate(workloads.custom("one_expert", B=8, E=160, K=1, D=3584, I=384, scale_lo=-9, scale_hi=-5,
                                             seed=13))
     d["ids"][:] = 77
     layer = _layer(lib, d)
-    got, hc, hs, plan, status = _decode_run(lib, layer, d, grid=grid)
+    got, hc, hs, plan, status = _decode_run(lib, layer, d, grid=grid, exchange=exchange)
     assert status == 0
     _check_plan(d, plan)
-    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/one_expert/{grid}")
+    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/one_expert/{grid}/x{exchange}")
 
 
 def test_decode_form_flags_bad_ids(lib):
@@ -392,8 +398,11 @@ def test_decode_form_matches_grouped_form_repeatedly(lib):
     d = workloads.generate("decode_b8")
     layer = _layer(lib, d, B_max=64)
     a, _, _, _, _ = _decode_run(lib, layer, d)
+    t, _, _, _, _ = _decode_run(lib, layer, d, exchange=1)
     d64 = workloads.generate("grouped_b64", with_weights=False)
     layer.forward(torch.from_numpy(d64["x"]).to(DEV), torch.from_numpy(d64["ids"] % d["workload"].E).to(DEV))
-    layer.forward(torch.from_numpy(d["x"][:3]).to(DEV), torch.from_numpy(d["ids"][:3]).to(DEV), path="decode")
+    layer.forward(torch.from_numpy(d["x"][:3]).to(DEV), torch.from_numpy(d["ids"][:3]).to(DEV), path="decode",
+                  exchange=1)
     b, _, _, _, _ = _decode_run(lib, layer, d)
-    assert np.array_equal(a, b)
+    u, _, _, _, _ = _decode_run(lib, layer, d, exchange=1)
+    assert np.array_equal(a, b) and np.array_equal(t, u)
