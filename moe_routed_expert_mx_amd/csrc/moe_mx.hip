@@ -630,7 +630,7 @@ __device__ __forceinline__ void lds_wait(uint32_t addr, int want, int32_t* err) 
 
 // ------------------------------------------------------------ LDS layout
 // [groups: g_cap records {expert, unit0, nunits, tile0}]  [chunk0: g_cap + 1 words]
-// [unit rows: u_cap x 8 u16 pair indices, 0xffff = padding]  [sync words]  [red: 2 x 4 streaming waves x NT x 4 KB, later reused as the 2 hidden
+// [unit rows: u_cap x 8 u16 pair indices, 0xffff = padding]  [sync words]  [slice table]  [red: 2 x 4 streaming waves x NT x 4 KB, later reused as the 2 hidden
 // buffers]  [meta: 4 waves x R x 16 B]  [ring: 4 waves x R x slot]
 // FC2 output tiles per item, so that an FC2 item carries about as many weight bytes as
 // an FC1 item.
@@ -662,7 +662,7 @@ struct Geo {
 constexpr uint32_t kSyncSub = 0, kSyncAck = 16, kSyncProg = 32, kSyncReady = 48, kSyncBytes = 64;
 
 struct LdsMap {
-  uint32_t grec, chunk0, urows, sync, red, hid, hid_bytes, hs, meta, ring;
+  uint32_t grec, chunk0, urows, sync, slt, red, hid, hid_bytes, hs, meta, ring;
   uint32_t xq, xs, xstr, xss;  // decode form: x codes [B + 1 rows of xstr], x scales [B + 1 rows of xss]
   uint32_t scr;                // decode form: the hidden builder's staging area (in red)
 };
@@ -686,7 +686,8 @@ __host__ __device__ __forceinline__ LdsMap lds_map(uint32_t g_cap, uint32_t u_ca
   t.chunk0 = g_cap * 16;
   t.urows = (t.chunk0 + (g_cap + 1) * 4 + 15) & ~15u;
   t.sync = t.urows + u_cap * 16;
-  t.red = t.sync + kSyncBytes;
+  t.slt = t.sync + kSyncBytes;  // the workgroup's four slices, 32 bytes each
+  t.red = t.slt + 128;
   t.hs = IP + 16;
   t.hid_bytes = (NT * 16 * t.hs + NT * 16 * (IP / 32) + 15) & ~15u;
   t.hid = t.red;
@@ -814,6 +815,8 @@ __device__ __forceinline__ int mx_block32(const uint32_t (&w)[16], uint32_t (&c)
   return e;
 }
 
+__device__ __forceinline__ void fill_slices(const ExpArgs& a, const LdsMap& m, int n_groups, int n_chunks);
+
 // Decode form prologue, all waves, before the first weight DMA.  Every workgroup builds
 // in its own LDS the unit table of the batch (B <= 8; experts page, the capacity <= 8
 // path: one unit per distinct expert, experts ascending, its tokens in token order --
@@ -880,6 +883,7 @@ __device__ __forceinline__ int dec_prologue(const ExpArgs& a, const LdsMap& m, u
   }
   if (tid == 0) chunk0[n_groups] = n_groups;
   __syncthreads();
+  fill_slices(a, m, n_groups, n_groups);  // one chunk per group; read after the barriers below
   // unit rows: pair r of token t at t's rank among the expert's tokens
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -1048,6 +1052,8 @@ struct Slice {
 };
 
 // List h: 0 = FC1(A), 1 = FC1(B), 2 = FC2(A), 3 = FC2(B); slices of near-equal length.
+// Computed per lane (h may differ between lanes: fill_slices takes one list per lane);
+// the kernel reads the results through the slice table (slice_at), as scalars.
 __device__ __forceinline__ Slice make_slice(const ExpArgs& a, int n_chunks, int h) {
   const int cA = (n_chunks + 1) / 2;
   const int c_lo = (h & 1) ? cA : 0, c_hi = (h & 1) ? n_chunks : cA;
@@ -1064,9 +1070,63 @@ __device__ __forceinline__ Slice make_slice(const ExpArgs& a, int n_chunks, int 
     const int q = s.T / a.qmin;
     s.P = q < 1 ? 1 : (q < s.P ? q : s.P);
   }
-  s.lo = __builtin_amdgcn_readfirstlane(p < s.P ? div_floor(static_cast<int64_t>(p) * s.T, s.P) : 0);
-  s.hi = __builtin_amdgcn_readfirstlane(p < s.P ? div_floor(static_cast<int64_t>(p + 1) * s.T, s.P) : 0);
+  s.lo = p < s.P ? div_floor(static_cast<int64_t>(p) * s.T, s.P) : 0;
+  s.hi = p < s.P ? div_floor(static_cast<int64_t>(p + 1) * s.T, s.P) : 0;
   return s;
+}
+
+// Chunks that the workgroup's FC2 slice S spans: [first, first + count).
+__device__ __forceinline__ int fc2_span(const ExpArgs& a, const Slice& S, int& first) {
+  first = (S.base + S.lo) / a.U2;
+  return S.hi > S.lo ? (S.base + S.hi - 1) / a.U2 - first + 1 : 0;
+}
+
+// The workgroup's four slices, computed once (threads 0-3, once the group list is in
+// LDS) into the slice table: per list {lo, hi, T, P, base, FC2 span first / count, group
+// of the chunk of the slice's first item}.  Readers take them with two LDS loads
+// instead of the divisions.
+struct SliceExtra {
+  int span_first, span_count, g0;
+};
+__device__ __forceinline__ void fill_slices(const ExpArgs& a, const LdsMap& m, int n_groups, int n_chunks) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int h = threadIdx.x;
+  if (h >= 4) return;
+  const Slice S = make_slice(a, n_chunks, h);
+  int first = 0, cnt = 0, g0 = 0;
+  if (h >= 2) cnt = fc2_span(a, S, first);
+  // group of the chunk holding the slice's first item (largest g with chunk0[g] <= c)
+  const int per_chunk = h < 2 ? a.HB : a.U2, per_item = h < 2 ? a.NSP : 1;
+  const int c = S.hi > S.lo ? (S.base + S.lo / per_item) / per_chunk : 0;
+  const int* chunk0 = reinterpret_cast<const int*>(smem + m.chunk0);
+  int lo = 0, hi = n_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk0[mid] <= c) lo = mid; else hi = mid - 1;
+  }
+  g0 = lo;
+  int4* t = reinterpret_cast<int4*>(smem + m.slt + 32 * h);
+  t[0] = make_int4(S.lo, S.hi, S.T, S.P);
+  t[1] = make_int4(S.base, first, cnt, g0);
+}
+__device__ __forceinline__ Slice slice_at(const LdsMap& m, uint32_t lb, int h, SliceExtra* x = nullptr) {
+  uint4 u, v;
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(u), "=&v"(v)
+               : "v"(lb + m.slt + 32 * h)
+               : "memory");
+  Slice S;
+  S.lo = __builtin_amdgcn_readfirstlane(static_cast<int>(u.x));
+  S.hi = __builtin_amdgcn_readfirstlane(static_cast<int>(u.y));
+  S.T = __builtin_amdgcn_readfirstlane(static_cast<int>(u.z));
+  S.P = __builtin_amdgcn_readfirstlane(static_cast<int>(u.w));
+  S.base = __builtin_amdgcn_readfirstlane(static_cast<int>(v.x));
+  if (x) {
+    x->span_first = __builtin_amdgcn_readfirstlane(static_cast<int>(v.y));
+    x->span_count = __builtin_amdgcn_readfirstlane(static_cast<int>(v.z));
+    x->g0 = __builtin_amdgcn_readfirstlane(static_cast<int>(v.w));
+  }
+  return S;
 }
 
 // Decode form: the partial-sum slots (512 tagged pairs each) of FC1 list h.  A slice of
@@ -1076,12 +1136,9 @@ __device__ __forceinline__ int dec_spw(const Slice& S, int NSP) {
   return S.P > 0 ? ((S.T + S.P - 1) / S.P - 1) / NSP + 2 : 0;
 }
 // Slot of workgroup p's share of list-local FC1 block bl of list h (S = that list).
-__device__ __forceinline__ uint32_t dec_slot(const ExpArgs& a, int n_chunks, int h, const Slice& S, int p, int bl) {
-  uint32_t off = 0;
-  if (h == 1) {
-    const Slice S0 = make_slice(a, n_chunks, 0);
-    off = static_cast<uint32_t>(S0.P * dec_spw(S0, a.NSP));
-  }
+__device__ __forceinline__ uint32_t dec_slot(const ExpArgs& a, const Slice& S0, int h, const Slice& S, int p,
+                                              int bl) {
+  const uint32_t off = h == 1 ? static_cast<uint32_t>(S0.P * dec_spw(S0, a.NSP)) : 0u;
   const int lo = div_floor(static_cast<int64_t>(p) * S.T, S.P);
   return off + static_cast<uint32_t>(p * dec_spw(S, a.NSP) + (bl - lo / a.NSP));
 }
@@ -1115,12 +1172,6 @@ __device__ __forceinline__ void x_rows(const ExpArgs& a, const LdsMap& m, uint32
   const int t = pair >= 0 ? pair / a.K : 0;
   xrow = pair >= 0 ? t * a.D + 16 * (l >> 4) : -1;
   xsrow = pair >= 0 ? static_cast<int>(a.plan_bytes / 33u * 32u) + t * (a.D / 32) : -1;
-}
-
-// Chunks that the workgroup's FC2 slice S spans: [first, first + count).
-__device__ __forceinline__ int fc2_span(const ExpArgs& a, const Slice& S, int& first) {
-  first = (S.base + S.lo) / a.U2;
-  return S.hi > S.lo ? (S.base + S.hi - 1) / a.U2 - first + 1 : 0;
 }
 
 template <bool DEC>
@@ -1157,15 +1208,21 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
       return;
     }
     ++c.h;
-    const Slice sl = make_slice(a, n_chunks, c.h);
+    SliceExtra sx;
+    const Slice sl = slice_at(m, lb, c.h, &sx);
     c.lo = sl.lo;
     c.hi = sl.hi;
     c.base = sl.base;
     c.b = c.h < 2 ? c.lo / a.NSP : c.lo + w;
+    c.gi.g = sx.g0;  // group of the slice's first chunk: the scan below starts there
     if (c.h >= 2) {
-      fc2_span(a, sl, c.cfirst);
-      int f2;
-      c.seq0 = c.h == 2 ? 0 : fc2_span(a, make_slice(a, n_chunks, 2), f2);
+      c.cfirst = sx.span_first;
+      c.seq0 = 0;
+      if (c.h == 3) {
+        SliceExtra s2;
+        slice_at(m, lb, 2, &s2);
+        c.seq0 = s2.span_count;
+      }
     }
     fresh = true;
   }
@@ -1175,7 +1232,11 @@ __device__ __forceinline__ void cursor_next(const ExpArgs& a, const LdsMap& m, u
   if (fresh) {
     c.chunk = gidx / per_chunk;
     c.j = gidx - c.chunk * per_chunk;
-    c.gi = group_of(m, lb, n_groups, c.chunk);
+    int g = c.gi.g;
+    while (g + 1 < n_groups && c.chunk >= lds_uni(lb + m.chunk0 + 4 * g + 4)) ++g;
+    GroupInfo gi = group_at(m, lb, g);
+    gi.cc = c.chunk - gi.c0;
+    c.gi = gi;
   } else {
     int j = c.j + gidx - c.gidx, chunk = c.chunk;
     while (j >= per_chunk) {
@@ -1224,7 +1285,11 @@ __device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, ui
   const uint32_t so = m.ring + (w * R + slot) * G::SLOT;  // offset from the LDS base
   uint4 meta = make_uint4(2u, 0u, 0u, 0u);                   // 2: dummy
   int done = 0;
-  if (c.h < 2) {
+  // an expert index outside [0, E) can only come from a broken invariant: issue nothing
+  // from it (the item turns into a dummy) and flag it, rather than load out of bounds
+  const bool sane = c.gi.e >= 0 && c.gi.e < a.E;
+  if (c.h < 4 && !sane && l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (c.h < 2 && sane) {
     const int s0 = 2 * c.s;
     const int64_t step = static_cast<int64_t>(c.gi.e * a.HB + c.j) * a.NS1 + s0;
     const uint8_t* wb = a.w13p + step * 4096 + l * 16;
@@ -1249,7 +1314,7 @@ __device__ __forceinline__ void issue_item(const ExpArgs& a, const LdsMap& m, ui
       meta = make_uint4(0u, static_cast<uint32_t>(c.gidx), 0u, 0u);
       done = G::L;
     }
-  } else if (c.h < 4) {
+  } else if (c.h < 4 && sane) {
     const int64_t tile = static_cast<int64_t>(c.gi.e) * (a.D / 16) + c.j * T2;
     const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
 #pragma unroll
@@ -1673,7 +1738,7 @@ __device__ __forceinline__ void dec_publish(const ExpArgs& a, const LdsMap& m, u
   const int chunk = (S.base + lbk) / a.HB;
   const GroupInfo gi = group_of(m, lb, n_groups, chunk);
   const int ncols = unit_cols(m, lb, gi);
-  uint64_t* dst = a.dpart + static_cast<size_t>(dec_slot(a, n_chunks, h, S, blockIdx.x, lbk)) * 512 + l;
+  uint64_t* dst = a.dpart + static_cast<size_t>(dec_slot(a, slice_at(m, lb, 0), h, S, blockIdx.x, lbk)) * 512 + l;
   // element (row l, column c) of tile rt = l / 16 sits in lane 16 ((l % 16) / 4) + c,
   // register l % 4 of the MFMA result
   const int rt = l >> 4, rr = l & 15;
@@ -1712,7 +1777,7 @@ __device__ __forceinline__ void dec_hidden(const ExpArgs& a, const LdsMap& m, ui
   int total;
   {
     const int h = chunk < (n_chunks + 1) / 2 ? 0 : 1;
-    const Slice S = make_slice(a, n_chunks, h);
+    const Slice S = slice_at(m, lb, h), S0 = slice_at(m, lb, 0);
     const int j = l >> 2, k = l & 3;
     int nown = 0;
     uint32_t sidx = 0;
@@ -1720,7 +1785,7 @@ __device__ __forceinline__ void dec_hidden(const ExpArgs& a, const LdsMap& m, ui
       const int bl = chunk * HB + j - S.base;
       const int p0 = slice_owner(bl * NSP, S.T, S.P), p1 = slice_owner(bl * NSP + NSP - 1, S.T, S.P);
       nown = p1 - p0 + 1;
-      if (k < nown) sidx = dec_slot(a, n_chunks, h, S, p0 + k, bl);
+      if (k < nown) sidx = dec_slot(a, S0, h, S, p0 + k, bl);
     }
     const int v = k == 0 ? nown * ncols : 0;
     int inc = v;
@@ -1898,6 +1963,8 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   } else {
     n_groups = a.tbl.hdr[1];
     n_chunks = load_groups<NT>(a, m, n_groups, a.tbl.hdr[0]);
+    fill_slices(a, m, n_groups, n_chunks);
+    __syncthreads();
   }
   const uint32_t sy = lb + m.sync;
   agpr_form();
@@ -1907,7 +1974,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
     v4f acc[4][NT];
     int q = 0;  // FC1 blocks of the workgroup taken so far
     for (int half = 0; half < 2; ++half) {
-      const Slice S = make_slice(a, n_chunks, half);
+      const Slice S = slice_at(m, lb, half);
       if (S.hi <= S.lo) continue;
       for (int lbk = S.lo / a.NSP; lbk <= (S.hi - 1) / a.NSP; ++lbk, ++q) {
 #pragma unroll
@@ -1934,9 +2001,9 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
     }
     int i = 0;  // FC2 chunks of the workgroup loaded so far
     for (int h = 2; h < 4; ++h) {
-      int first;
-      const Slice S2 = make_slice(a, n_chunks, h);
-      const int cnt = fc2_span(a, S2, first);
+      SliceExtra sx;
+      const Slice S2 = slice_at(m, lb, h, &sx);
+      const int first = sx.span_first, cnt = sx.span_count;
       const int c_lo = h == 2 ? 0 : (n_chunks + 1) / 2;
       for (int c = first; c < first + cnt; ++c, ++i) {
         if (!TAG) wait_chunk(a, c, gen);
@@ -1962,7 +2029,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
   // FC1 blocks are handed over in the workgroup's order: half A's slice, then B's
   int sub_h = 0, sub_q = 0;
-  Slice sub = make_slice(a, n_chunks, 0);
+  Slice sub = slice_at(m, lb, 0);
   int sub_b = sub.lo / a.NSP, sub_last = sub.hi > sub.lo ? (sub.hi - 1) / a.NSP : sub_b - 1;
   // Hands the sums of the workgroup's FC1 blocks below global block `upto` to the control
   // wave, in the workgroup's block order (zeros for blocks without steps of this wave).
@@ -1984,7 +2051,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
         if (l == 0) lds_st4(sy + kSyncSub + 4 * w, static_cast<uint32_t>(sub_q));
         ++sub_b;
       } else if (++sub_h < 2) {
-        sub = make_slice(a, n_chunks, 1);
+        sub = slice_at(m, lb, 1);
         sub_b = sub.lo / a.NSP;
         sub_last = sub.hi > sub.lo ? (sub.hi - 1) / a.NSP : sub_b - 1;
       }
