@@ -607,6 +607,7 @@ __device__ __forceinline__ uint32_t lds_base() {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   return static_cast<uint32_t>(reinterpret_cast<size_t>((lds_void*)smem));
 }
+__device__ __forceinline__ void lds_settle_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_st4(uint32_t addr, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
 }
@@ -658,8 +659,9 @@ struct Geo {
 
 // Sync words (u32, offsets within the sync area): sub[w] = FC1 blocks wave w has handed
 // over; ack = blocks the control wave has taken; prog[w] = the FC2 chunk (index in the
-// workgroup's sequence) wave w works on; ready[b] = the chunk held by hidden buffer b.
-constexpr uint32_t kSyncSub = 0, kSyncAck = 16, kSyncProg = 32, kSyncReady = 48, kSyncBytes = 64;
+// workgroup's sequence) wave w works on; ready[b] = the chunk held by hidden buffer b;
+// x = 1 once the decode form's plan of x is in LDS.
+constexpr uint32_t kSyncSub = 0, kSyncAck = 16, kSyncProg = 32, kSyncReady = 48, kSyncX = 56, kSyncBytes = 64;
 
 struct LdsMap {
   uint32_t grec, chunk0, urows, sync, slt, red, hid, hid_bytes, hs, meta, ring;
@@ -817,16 +819,36 @@ __device__ __forceinline__ int mx_block32(const uint32_t (&w)[16], uint32_t (&c)
 
 __device__ __forceinline__ void fill_slices(const ExpArgs& a, const LdsMap& m, int n_groups, int n_chunks);
 
+// Plans of x up to this many 32-element blocks are the control wave's alone (dec_plan_x,
+// while the streaming waves start); larger ones are quantized by all waves in the
+// prologue.
+constexpr int kPlanByControl = 256;
+
 // Decode form prologue, all waves, before the first weight DMA.  Every workgroup builds
 // in its own LDS the unit table of the batch (B <= 8; experts page, the capacity <= 8
 // path: one unit per distinct expert, experts ascending, its tokens in token order --
-// the table moe_group writes for such a batch) and the MXFP8 plan of x (the moe_plan
-// arithmetic), so the whole step is one launch.  Returns the number of distinct experts.
-__device__ __forceinline__ int dec_prologue(const ExpArgs& a, const LdsMap& m, uint32_t ring_bytes) {
+// the table moe_group writes for such a batch) and its slice table, so the whole step is
+// one launch.  A plan of x larger than kPlanByControl blocks is made here too, by all
+// waves (the moe_plan arithmetic; its raw rows come in by DMA into the ring, issued
+// first so they travel with the ids); a smaller one is dec_plan_x's.  Returns the number
+// of distinct experts.
+__device__ __forceinline__ int dec_route(const ExpArgs& a, const LdsMap& m, uint32_t ring_bytes) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int tid = threadIdx.x;
   const int U = a.B * a.K, E = a.E, D = a.D, nkb = D / 32, nxb = a.B * nkb;
-  // scratch in the ring, which no DMA has touched yet: per-expert token masks (a byte
+  const bool plan_here = nxb > kPlanByControl;
+  // raw rows of x into the ring behind the routing scratch, as many 1 KB pieces as fit
+  // per pass (the first pass is issued before anything waits)
+  const int pieces = a.B * D * 2 / 1024, per_pass = static_cast<int>(ring_bytes - 4096) / 1024;
+  const int w = wave_id(), l = threadIdx.x & 63;
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
+  auto stage_x = [&](int p0) {
+    const int np = pieces - p0 < per_pass ? pieces - p0 : per_pass;
+#pragma unroll 1
+    for (int i = w; i < np; i += kWG / 64) dma16(xb + (p0 + i) * 1024 + l * 16, m.ring + 4096 + i * 1024);
+  };
+  if (plan_here) stage_x(0);
+  // scratch in the ring, which no weight DMA has touched yet: per-expert token masks (a byte
   // per expert), expert -> group rank, wave totals
   uint32_t* mk = reinterpret_cast<uint32_t*>(smem + m.ring);          // [ceil(E / 4)]
   uint16_t* rk = reinterpret_cast<uint16_t*>(smem + m.ring + 1024);   // [E]
@@ -895,22 +917,67 @@ __device__ __forceinline__ int dec_prologue(const ExpArgs& a, const LdsMap& m, u
     urows[rk[e] * 8 + __popc(tm & ((1u << t) - 1u))] = static_cast<uint16_t>(r);
   }
   if (flags && blockIdx.x == 0) __hip_atomic_fetch_or(a.err, flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // the plan of x into LDS (and the optional dump, workgroup 0): the BF16 rows come in
-  // by DMA, 1 KB per instruction, into the ring behind the routing scratch, as many as
-  // fit per pass; then one thread per 32-element block
-  const int pieces = a.B * D * 2 / 1024, per_pass = static_cast<int>(ring_bytes - 4096) / 1024;
-  const int w = wave_id(), l = threadIdx.x & 63;
+  if (plan_here) {
+#pragma unroll 1
+    for (int p0 = 0; p0 < pieces; p0 += per_pass) {
+      const int np = pieces - p0 < per_pass ? pieces - p0 : per_pass;
+      if (p0 > 0) stage_x(p0);
+      wait_vm<0>();
+      __syncthreads();
+#pragma unroll 1
+      for (int blk = p0 * 16 + tid; blk < (p0 + np) * 16; blk += kWG) {
+        const uint4* src = reinterpret_cast<const uint4*>(smem + m.ring + 4096 + (blk - p0 * 16) * 64);
+        uint32_t xw[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = src[i];
+          xw[4 * i] = v.x; xw[4 * i + 1] = v.y; xw[4 * i + 2] = v.z; xw[4 * i + 3] = v.w;
+        }
+        uint32_t c[8];
+        const int e = mx_block32(xw, c);
+        const int t = blk / nkb, kb = blk - t * nkb;
+        uint4* dst = reinterpret_cast<uint4*>(smem + m.xq + t * m.xstr + 32 * kb);
+        dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+        dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+        smem[m.xs + t * m.xss + kb] = static_cast<unsigned char>(e + 127);
+        if (a.plan_dump != nullptr && blockIdx.x == 0) {
+          uint4* pd = reinterpret_cast<uint4*>(a.plan_dump + static_cast<int64_t>(blk) * 32);
+          pd[0] = make_uint4(c[0], c[1], c[2], c[3]);
+          pd[1] = make_uint4(c[4], c[5], c[6], c[7]);
+          a.plan_dump[static_cast<int64_t>(nxb) * 32 + blk] = static_cast<uint8_t>(e + 127);
+        }
+      }
+      __syncthreads();
+    }
+    if (tid == 0) reinterpret_cast<uint32_t*>(smem + m.sync)[kSyncX / 4] = 1u;  // x plan ready
+  }
+  __syncthreads();  // the unit rows (and the plan) are in place; the ring's scratch is free
+  return n_groups;
+}
+
+
+// Decode form, the control wave: the MXFP8 plan of x (the moe_plan arithmetic) into LDS,
+// and the optional plan dump (workgroup 0).  The BF16 rows come in by DMA, 1 KB per
+// instruction, into the FC1 hand-over area -- idle until the first FC1 block is handed
+// over, which needs this plan first -- 32 KB per pass; one lane per 32-element block.
+// The streaming waves meanwhile start their weight streams; the kSyncX word tells them
+// the plan is there.
+__device__ __forceinline__ void dec_plan_x(const ExpArgs& a, const LdsMap& m, uint32_t sy) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int l = threadIdx.x & 63;
+  const int D = a.D, nkb = D / 32, nxb = a.B * nkb;
+  constexpr int kPass = 32;  // KB of raw rows per pass: the hand-over area
+  const int pieces = a.B * D * 2 / 1024;
   const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
 #pragma unroll 1
-  for (int p0 = 0; p0 < pieces; p0 += per_pass) {
-    const int np = pieces - p0 < per_pass ? pieces - p0 : per_pass;
+  for (int p0 = 0; p0 < pieces; p0 += kPass) {
+    const int np = pieces - p0 < kPass ? pieces - p0 : kPass;
 #pragma unroll 1
-    for (int i = w; i < np; i += kWG / 64) dma16(xb + (p0 + i) * 1024 + l * 16, m.ring + 4096 + i * 1024);
+    for (int i = 0; i < np; ++i) dma16(xb + (p0 + i) * 1024 + l * 16, m.red + i * 1024);
     wait_vm<0>();
-    __syncthreads();
 #pragma unroll 1
-    for (int blk = p0 * 16 + tid; blk < (p0 + np) * 16; blk += kWG) {
-      const uint4* src = reinterpret_cast<const uint4*>(smem + m.ring + 4096 + (blk - p0 * 16) * 64);
+    for (int blk = p0 * 16 + l; blk < (p0 + np) * 16; blk += 64) {
+      const uint4* src = reinterpret_cast<const uint4*>(smem + m.red + (blk - p0 * 16) * 64);
       uint32_t xw[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -931,9 +998,10 @@ __device__ __forceinline__ int dec_prologue(const ExpArgs& a, const LdsMap& m, u
         a.plan_dump[static_cast<int64_t>(nxb) * 32 + blk] = static_cast<uint8_t>(e + 127);
       }
     }
-    __syncthreads();
+    lds_settle_all();  // this pass's reads of the staged rows are done before the next DMA
   }
-  return n_groups;
+  lds_settle_all();
+  if (l == 0) lds_st4(sy + kSyncX, 1u);
 }
 
 struct GroupInfo {
@@ -1958,7 +2026,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   const uint32_t gen = a.calls[blockIdx.x];
   int n_groups, n_chunks;
   if constexpr (DEC) {
-    n_groups = dec_prologue(a, m, kStream * R * G::SLOT);
+    n_groups = dec_route(a, m, kStream * R * G::SLOT);
     n_chunks = n_groups;  // one column tile per expert
   } else {
     n_groups = a.tbl.hdr[1];
@@ -1971,6 +2039,8 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
 
   if (w == kStream) {
     // ---------------------------------------------------------- control wave
+    if constexpr (DEC)
+      if (a.B * (a.D / 32) <= kPlanByControl) dec_plan_x(a, m, sy);
     v4f acc[4][NT];
     int q = 0;  // FC1 blocks of the workgroup taken so far
     for (int half = 0; half < 2; ++half) {
@@ -2027,6 +2097,15 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   v4f acc[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+  // decode form: the control wave's plan of x is in LDS (it also frees the hand-over
+  // area, its staging buffer); waited for before the first FC1 item or hand-over write
+  bool x_ok = !DEC;
+  auto wait_x = [&]() {
+    if (!x_ok) {
+      lds_wait<false>(sy + kSyncX, 1, a.err);
+      x_ok = true;
+    }
+  };
   // FC1 blocks are handed over in the workgroup's order: half A's slice, then B's
   int sub_h = 0, sub_q = 0;
   Slice sub = slice_at(m, lb, 0);
@@ -2037,6 +2116,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
     while (sub_h < 2) {
       if (sub_b <= sub_last) {
         if (sub.base + sub_b >= upto) break;
+        wait_x();
         lds_wait<false>(sy + kSyncAck, sub_q - 1, a.err);  // slot sub_q&1 is free once block sub_q-2 is taken
         mfma_settle(acc[0], acc[1], acc[2], acc[3]);
 #pragma unroll
@@ -2110,6 +2190,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
       if constexpr (DEC) {
         const int xc = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.z));
         const int xsp = __builtin_amdgcn_readfirstlane(static_cast<int>(meta.w));
+        wait_x();
         if (xc != x_chunk) {
           x_chunk = xc;
           const GroupInfo xgi = group_of(m, lb, n_groups, xc);
