@@ -847,7 +847,14 @@ __device__ __forceinline__ int dec_route(const ExpArgs& a, const LdsMap& m, uint
 #pragma unroll 1
     for (int i = w; i < np; i += kWG / 64) dma16(xb + (p0 + i) * 1024 + l * 16, m.ring + 4096 + i * 1024);
   };
-  if (plan_here) stage_x(0);
+  if (plan_here) {
+    stage_x(0);
+  } else if (w == kStream) {
+    // small plan: the control wave's (dec_plan_x); its raw rows go out now, ahead of
+    // the weight streams in the memory pipeline, into the idle FC1 hand-over area
+#pragma unroll 1
+    for (int i = 0; i < pieces; ++i) dma16(xb + i * 1024 + l * 16, m.red + i * 1024);
+  }
   // scratch in the ring, which no weight DMA has touched yet: per-expert token masks (a byte
   // per expert), expert -> group rank, wave totals
   uint32_t* mk = reinterpret_cast<uint32_t*>(smem + m.ring);          // [ceil(E / 4)]
@@ -956,25 +963,20 @@ __device__ __forceinline__ int dec_route(const ExpArgs& a, const LdsMap& m, uint
 }
 
 
-// Decode form, the control wave: the MXFP8 plan of x (the moe_plan arithmetic) into LDS,
-// and the optional plan dump (workgroup 0).  The BF16 rows come in by DMA, 1 KB per
-// instruction, into the FC1 hand-over area -- idle until the first FC1 block is handed
-// over, which needs this plan first -- 32 KB per pass; one lane per 32-element block.
-// The streaming waves meanwhile start their weight streams; the kSyncX word tells them
-// the plan is there.
+// Decode form, the control wave: the MXFP8 plan of x (the moe_plan arithmetic; at most
+// kPlanByControl blocks, i.e. 16 KB of raw rows) into LDS, and the optional plan dump
+// (workgroup 0).  dec_route already had the BF16 rows DMA'd into the FC1 hand-over area
+// (idle until the first FC1 block is handed over, which needs this plan first); one
+// lane per 32-element block.  The streaming waves meanwhile start their weight streams;
+// the kSyncX word tells them the plan is there.
 __device__ __forceinline__ void dec_plan_x(const ExpArgs& a, const LdsMap& m, uint32_t sy) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int l = threadIdx.x & 63;
   const int D = a.D, nkb = D / 32, nxb = a.B * nkb;
-  constexpr int kPass = 32;  // KB of raw rows per pass: the hand-over area
-  const int pieces = a.B * D * 2 / 1024;
-  const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
-#pragma unroll 1
-  for (int p0 = 0; p0 < pieces; p0 += kPass) {
-    const int np = pieces - p0 < kPass ? pieces - p0 : kPass;
-#pragma unroll 1
-    for (int i = 0; i < np; ++i) dma16(xb + (p0 + i) * 1024 + l * 16, m.red + i * 1024);
-    wait_vm<0>();
+  static_assert(kPlanByControl * 64 <= 32 * 1024, "the raw rows fit the hand-over area");
+  wait_vm<0>();
+  {
+    const int p0 = 0, np = a.B * D * 2 / 1024;
 #pragma unroll 1
     for (int blk = p0 * 16 + l; blk < (p0 + np) * 16; blk += 64) {
       const uint4* src = reinterpret_cast<const uint4*>(smem + m.red + (blk - p0 * 16) * 64);
@@ -998,7 +1000,6 @@ __device__ __forceinline__ void dec_plan_x(const ExpArgs& a, const LdsMap& m, ui
         a.plan_dump[static_cast<int64_t>(nxb) * 32 + blk] = static_cast<uint8_t>(e + 127);
       }
     }
-    lds_settle_all();  // this pass's reads of the staged rows are done before the next DMA
   }
   lds_settle_all();
   if (l == 0) lds_st4(sy + kSyncX, 1u);
