@@ -1082,10 +1082,12 @@ __device__ __forceinline__ void hidden_epilogue(const ExpArgs& a, const v4f (&to
     word[half] = to_e4m3(h[half][0] * s) | (to_e4m3(h[half][1] * s) << 8) |
                  (to_e4m3(h[half][2] * s) << 16) | (to_e4m3(h[half][3] * s) << 24);
   const int gcol = gtile * 16 + (l & 15);
-  uint8_t* hc = a.hcodes + static_cast<int64_t>(gcol) * a.IP + 32 * j + 4 * (l >> 4);
-  st_dev_u32(hc, word[0]);
-  st_dev_u32(hc + 16, word[1]);
-  if (l < 16) st_dev_u8(a.hscales + static_cast<int64_t>(gcol) * (a.IP / 32) + j, static_cast<uint8_t>(e + 127));
+  if (pair >= 0) {  // padded columns: nothing reads their hidden
+    uint8_t* hc = a.hcodes + static_cast<int64_t>(gcol) * a.IP + 32 * j + 4 * (l >> 4);
+    st_dev_u32(hc, word[0]);
+    st_dev_u32(hc + 16, word[1]);
+    if (l < 16) st_dev_u8(a.hscales + static_cast<int64_t>(gcol) * (a.IP / 32) + j, static_cast<uint8_t>(e + 127));
+  }
   if (a.dump_codes != nullptr && pair >= 0) {
     uint8_t* dc = a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 4 * (l >> 4);
     *reinterpret_cast<uint32_t*>(dc) = word[0];
@@ -1641,20 +1643,30 @@ template <int NT>
 __device__ __forceinline__ void control_block(const ExpArgs& a, const LdsMap& m, uint32_t lb, int n_groups,
                                               const Slice& li, int half, int lbk, v4f (&acc)[4][NT],
                                               uint32_t gen) {
+  static_assert(NT == 1, "one column tile per block");
   const int l = threadIdx.x & 63;
   const int NS1 = a.NSP, HB = a.HB;  // block length in FC1 items (step pairs)
   const int p = blockIdx.x;
   const int b = li.base + lbk;  // global block
   const int bs = lbk * NS1;
+  const int chunk = b / HB, j = b - chunk * HB;
+  const GroupInfo gi = group_of(m, lb, n_groups, chunk);
+  // the lane's column holds a route (padded columns are neither filed nor summed: every
+  // FC2 output column depends on its own hidden column only, and padded rows are never
+  // stored)
+  const int pair = column_pair(m, lb, gi, gi.cc * 16 + (l & 15));
+  const bool live = pair >= 0;
   if (li.lo > bs) {
-    // contributor: file the partial sums (device-coherent), then count in
+    // contributor: file the partial sums (device-coherent, two floats per store), then
+    // count in
     float* slot = a.partials + (static_cast<int64_t>(p) * 2 + half) * NT * 1024 + l * 4;
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
+    if (live)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st_dev_u32(slot + (n * 4 + rt) * 256 + r, __float_as_uint(acc[rt][n][r]));
+        for (int r = 0; r < 4; r += 2)
+          st_dev_u64(slot + rt * 256 + r, (static_cast<uint64_t>(__float_as_uint(acc[rt][0][r + 1])) << 32) |
+                                              __float_as_uint(acc[rt][0][r]));
     wait_stores();
     if (l == 0) __hip_atomic_fetch_add(a.arrive + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
@@ -1681,7 +1693,7 @@ __device__ __forceinline__ void control_block(const ExpArgs& a, const LdsMap& m,
       uint64_t v[4][NT * 8];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (pp0 + u > pb) continue;
+        if (pp0 + u > pb || !live) continue;
         const float* src = a.partials + (static_cast<int64_t>(pp0 + u) * 2 + half) * NT * 1024 + l * 4;
 #pragma unroll
         for (int i = 0; i < NT * 4; ++i) {
@@ -1691,7 +1703,7 @@ __device__ __forceinline__ void control_block(const ExpArgs& a, const LdsMap& m,
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (pp0 + u > pb) continue;
+        if (pp0 + u > pb || !live) continue;
 #pragma unroll
         for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -1705,14 +1717,9 @@ __device__ __forceinline__ void control_block(const ExpArgs& a, const LdsMap& m,
       }
     }
   }
-  const int chunk = b / HB, j = b - chunk * HB;
-  const GroupInfo gi = group_of(m, lb, n_groups, chunk);
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int t = gi.cc * NT + n;
-    if (t >= gi.ntiles) continue;
-    const v4f tot[4] = {acc[0][n], acc[1][n], acc[2][n], acc[3][n]};
-    hidden_epilogue(a, tot, j, gi.tile0 + t, column_pair(m, lb, gi, t * 16 + (l & 15)));
+  {
+    const v4f tot[4] = {acc[0][0], acc[1][0], acc[2][0], acc[3][0]};
+    hidden_epilogue(a, tot, j, gi.tile0 + gi.cc, pair);
   }
   // Publish: the block's codes and scales are stored (sc1) before its flag.
   wait_stores();
