@@ -6,17 +6,20 @@
 //   [runtime]  "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.moe.experts_runtime"
 // The pages' engine (TMA producer warp, TMEM accumulators, mbarriers, clusters) is
 // NVIDIA-specific; this file keeps the method (MXFP8 plan, (expert, <=8 token) units,
-// FC1 -> gated activation -> hidden requant -> FC2, rows in top-k order, claim-based
-// work distribution) and maps it onto CDNA4:
-//   * weights stream from HBM once per distinct expert per call with 128-bit loads
-//     straight into the operand registers of v_mfma_scale_f32_16x16x128_f8f6f4
-//     (FP4 A operand = a 16-row weight tile, FP8 B operand = 16 token columns);
-//   * block scales go to the MFMA as E8M0 operands (no dequantization pass);
-//   * one persistent kernel claims work items in order from a device-wide counter:
-//     FC1 items first, then FC2 items that wait on their expert's hidden, which only
-//     earlier-claimed FC1 items produce -- no co-residency is needed;
-//   * the FC1->FC2 hidden exchange and the FC1 split-K partial sums cross XCDs
-//     through device-coherent (sc1) stores/loads plus agent-scope atomics.
+// FC1 -> gated activation -> hidden requant -> FC2, rows in top-k order, contiguous
+// work slices) and maps it onto CDNA4:
+//   * weights stream from HBM once per distinct expert per call, through per-wave LDS
+//     DMA rings (global_load_lds, 16 bytes per lane), as the operands of
+//     v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 A operand = a 16-row weight tile, FP8 B
+//     operand = 16 token columns); block scales go to the MFMA as E8M0 operands;
+//   * one persistent, co-resident kernel: every workgroup takes a contiguous slice of
+//     the FC1 work, then of the FC2 work; four streaming waves per workgroup only
+//     stream and multiply, one control wave does every cross-workgroup step;
+//   * the FC1 -> FC2 hidden exchange and the split-block FC1 partial sums cross XCDs
+//     through device-coherent (sc1) stores and loads, call-tagged flags and
+//     agent-scope counters;
+//   * for B <= 8 the same kernel also routes the batch and quantizes x (the decode
+//     form), so the step is one launch.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
