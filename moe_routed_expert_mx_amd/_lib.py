@@ -38,7 +38,7 @@ class moe_run_opts_t(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python -m moe_routed_expert_mx_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built: run `python moe_routed_expert_mx_amd/build.py` "
                           "(or __graft_entry__.build()) first")
     L = ctypes.CDLL(LIB_PATH)
     c, P = ctypes, ctypes.c_void_p
