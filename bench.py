@@ -77,7 +77,7 @@ def _unique_weight_bytes(ids, w) -> int:
 
 
 def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager: bool = False, path: str = "auto",
-            log=print) -> dict:
+            exchange: int | None = None, log=print) -> dict:
     import numpy as np
     import torch
 
@@ -99,9 +99,10 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
     G = max(gs for gs in range(1, min(graph_steps, steps) + 1) if steps % gs == 0)
     decode = w.B <= MoeLayer.DECODE_MAX and (path == "decode" or (path == "auto" and MoeLayer.AUTO_DECODE))
     form = "decode" if decode else "grouped"
+    xo = {"exchange": exchange} if (decode and exchange is not None) else {}
 
     for i in range(warmup):
-        layer.forward(x, ids, out, replica=i % R, path=form)
+        layer.forward(x, ids, out, replica=i % R, path=form, **xo)
     torch.cuda.synchronize()
 
     reps = steps // G
@@ -112,14 +113,14 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(G):
-                layer.forward(x, ids, out, replica=i % R, path=form)
+                layer.forward(x, ids, out, replica=i % R, path=form, **xo)
         # the dominant kernel alone: the experts kernel on the plan/units of the last step
         # (the decode form's step is that one kernel)
         ge = torch.cuda.CUDAGraph()
         with torch.cuda.graph(ge):
             for i in range(G):
                 if decode:
-                    layer.forward(x, ids, out, replica=i % R, path=form)
+                    layer.forward(x, ids, out, replica=i % R, path=form, **xo)
                 else:
                     layer.experts(w.B, out, replica=i % R)
         # the weighted top-k combine of the step's rows (outside the step)
@@ -131,7 +132,7 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
             g.replay()
             ge.replay()
             gc.replay()
-        layer.forward(x, ids, out, path=form)  # plan and units of this batch for the experts-only graph
+        layer.forward(x, ids, out, path=form, **xo)  # plan and units of this batch for the experts-only graph
         torch.cuda.synchronize()
 
     def timed(run_all) -> float:
@@ -145,12 +146,12 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
 
     def steps_eager():
         for i in range(reps * G):
-            layer.forward(x, ids, out, replica=i % R, path=form)
+            layer.forward(x, ids, out, replica=i % R, path=form, **xo)
 
     def experts_eager():
         for i in range(reps * G):
             if decode:
-                layer.forward(x, ids, out, replica=i % R, path=form)
+                layer.forward(x, ids, out, replica=i % R, path=form, **xo)
             else:
                 layer.experts(w.B, out, replica=i % R)
 
@@ -233,6 +234,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying HIP graphs")
+    ap.add_argument("--exchange", type=int, default=None,
+                    help="decode form: FC1 -> FC2 exchange variant (moe_run_opts_t.exchange); default: the library's")
     ap.add_argument("--path", default="auto", choices=("auto", "decode", "grouped"),
                     help="step form for B <= 8: one decode launch, the three-call grouped form, or auto "
                          "(larger batches always use the grouped form)")
@@ -253,7 +256,8 @@ def main():
     if args.copy_mb > 0:
         copy_calibration(args.copy_mb)
     names = workloads.ORDER if args.all else [args.workload]
-    results = {n: measure(n, args.steps, args.warmup, eager=args.eager, path=args.path) for n in names}
+    results = {n: measure(n, args.steps, args.warmup, eager=args.eager, path=args.path, exchange=args.exchange)
+               for n in names}
     main_res = results[args.workload]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_budget)
     line = {

@@ -423,7 +423,9 @@ constexpr int kMaxGrid = 2048;     // workgroups of the persistent grid (call co
 constexpr int kMaxGroups = 1024;   // distinct experts per call (E <= 1024)
 
 struct WsLayout {
-  size_t calls, status, arrive, flags, hcodes, hscales, partials, end;
+  size_t calls, status, arrive, flags, hcodes, hscales, partials;
+  size_t qcalls, qflags, qhcodes, qhscales;  // decode form with whole-K FC1 blocks
+  size_t end;
   int64_t max_tiles, max_blocks;
   int64_t dec_slots;  // decode-form partial-sum slots (512 tagged pairs each)
   int nt_cap;
@@ -471,6 +473,16 @@ WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   const size_t dec = static_cast<size_t>(L.dec_slots) * 4096;
   L.partials = off;
   off = align256(off + (grouped > dec ? grouped : dec));
+  // decode form with whole-K FC1 blocks: its own call counters, block flags and hidden
+  // (at most 128 distinct experts x 8 token columns)
+  L.qcalls = off;
+  off = align256(off + kMaxGrid * 4);
+  L.qflags = off;
+  off = align256(off + 128 * 16 * 4);
+  L.qhcodes = off;
+  off = align256(off + static_cast<size_t>(128) * 8 * IP);
+  L.qhscales = off;
+  off = align256(off + 128 * 8 * 16);
   L.end = off;
   return L;
 }
@@ -2284,6 +2296,515 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
   wait_vm<0>();
 }
 
+// =================================================================== decode form, whole-K FC1 blocks
+// moe_decode_run with exchange == 2.  A variant of the decode form in which no hidden
+// block is ever split between workgroups:
+//   * an FC1 item is one hidden block (distinct expert g, block j of 32 hidden values):
+//     the 64 weight rows gate 32j..32j+31 and the matching up rows over the whole of K.
+//     The workgroup's four streaming waves take every fourth 128-wide K step of it; the
+//     control wave adds their four partial tiles in wave order, applies SwiGLU and the
+//     MXFP8 requantization (experts page, ExpertsKernel.store_hidden) and publishes the
+//     block with a call-tagged flag.  No FC1 partial sum leaves the workgroup.
+//   * FC2 is dealt as 16-row output tiles, a contiguous run of them (in expert-major
+//     order) per workgroup, so a workgroup's FC2 touches one or two experts; the tiles of
+//     one expert wait for that expert's block flags only.
+//   * FC1 items go round-robin too (item i to workgroup i mod grid); the workgroups with
+//     one item fewer take proportionally more FC2 tiles, so every workgroup streams about
+//     the same number of weight bytes (experts page, ExpertsKernel.partition, contiguous
+//     near-equal shares of the weight stream).
+// The weight stream of a streaming wave is one sequence of equal slots (an FC1 K step:
+// four 1 KB row tiles and their scale words; or an FC2 tile: NS2 1 KB K steps and its
+// scale words), R in flight through LDS DMA, so "the oldest slot has landed" is always
+// the same vmcnt.
+
+constexpr int kQSlot = 4096 + 256;  // slot bytes
+constexpr int kQOps = 5;            // DMA instructions per slot (pads keep it fixed)
+constexpr int kQGMax = 128;         // distinct experts per call
+constexpr int kQXBlk = 4;           // 32-element x blocks per thread held in the prologue
+constexpr int kQHB = 16;            // flag and scale words per (expert, column): HB <= 16
+
+// LDS: sync words and the routing tables of the batch (byte offsets from the LDS base).
+constexpr uint32_t kQProg = 0;      // [4] FC1 items whose partial tiles wave w has written
+constexpr uint32_t kQCons = 16;     // FC1 items whose partial tiles the control wave has read
+constexpr uint32_t kQProg2 = 32;    // [4] wave w is done with every FC2 hidden sequence < value
+constexpr uint32_t kQReady = 48;    // FC2 hidden sequences loaded into the two hidden buffers
+constexpr uint32_t kQXDone = 52;    // waves that have written their share of the x plan
+constexpr uint32_t kQGCount = 56;   // distinct experts of the batch
+constexpr uint32_t kQEmask = 64;    // [32] expert bitmask (E <= 1024)
+constexpr uint32_t kQPre = 192;     // [32] popcount prefix of the bitmask words
+constexpr uint32_t kQExp = 320;     // [kQGMax] expert id of group g (ascending)
+constexpr uint32_t kQTok = 832;     // [kQGMax] token bitmask of group g
+constexpr uint32_t kQRow = 1344;    // [kQGMax][8] u16: pair t*K+s of group g's column c
+constexpr uint32_t kQTables = 3456;
+
+struct QArgs {
+  const uint8_t* w13p;
+  const uint8_t* s13p;
+  const uint8_t* w2p;
+  const uint8_t* s2p;
+  const uint16_t* x;      // BF16 [B, D]
+  const int32_t* ids;     // [B, K]
+  uint16_t* out;          // BF16 [B*K, D]
+  uint8_t* hcodes;        // [kQGMax][8][IP] hidden codes of this call
+  uint8_t* hscales;       // [kQGMax][8][kQHB] hidden scales
+  uint32_t* flags;        // [kQGMax][kQHB] call-tagged block flags
+  uint32_t* calls;        // [kMaxGrid] per-workgroup call counters
+  int32_t* err;           // status word (bit 0 id out of range, bit 1 repeated id, bit 2 a wait gave up)
+  uint8_t* dump_codes;    // optional [B*K, I]
+  uint8_t* dump_scales;   // optional [B*K, I/32]
+  uint8_t* plan_dump;     // optional plan of x (moe_plan layout), written by workgroup 0
+  int B, K, E, D, I, HB, NS1, IP, floor_rule;
+  uint32_t o_red, o_hid, o_xq, o_xs, o_ring;  // LDS offsets
+  uint32_t xstr, xsstr, hid_bytes;            // x code row stride, x scale row stride, one hidden buffer
+};
+
+__device__ __forceinline__ void lds_add4(uint32_t addr, uint32_t v) {
+  asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_st1_async(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b8 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// The workgroup's share of the work (the same on every lane; all workgroups agree).
+struct QWork {
+  int n1;      // FC1 items: i = c + k * grid, k < n1
+  int m1;      // this wave's K steps per FC1 item (steps w, w + 4, ...)
+  int n2;      // FC2 tiles: the contiguous run first2 .. first2 + n2 - 1 (expert-major order)
+  int first2;
+  int TPE, nwg, c;
+};
+
+__device__ __forceinline__ int q_tile(const QWork& q, int k) { return q.first2 + k; }
+
+__device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int NS2, int D, int nwg, int c, int w) {
+  QWork q;
+  const int N1 = G * HB;
+  q.nwg = nwg;
+  q.c = c;
+  q.TPE = D / 16;
+  const int N2 = G * q.TPE;
+  const int r1 = N1 % nwg;  // workgroups c < r1 hold one FC1 item more
+  q.n1 = N1 / nwg + (c < r1 ? 1 : 0);
+  q.m1 = (NS1 - w + 3) / 4;
+  int cap;
+  if (r1 == 0) {
+    cap = (N2 + nwg - 1) / nwg;
+    q.first2 = c * cap;
+  } else {
+    // the workgroups with an FC1 item more take dlt FC2 tiles fewer (dlt tiles stream
+    // about the bytes of one FC1 item)
+    const int b1 = NS1 * kQSlot, b2 = NS2 * 1024 + 256;
+    const int dlt = (b1 + b2 / 2) / b2;
+    const int v = N2 - (nwg - r1) * dlt;
+    const int cap_hi = v <= 0 ? 0 : (v + nwg - 1) / nwg;
+    const int rest = N2 - r1 * cap_hi;
+    const int cap_lo = rest <= 0 ? 0 : (rest + (nwg - r1) - 1) / (nwg - r1);
+    cap = c < r1 ? cap_hi : cap_lo;
+    q.first2 = c < r1 ? c * cap_hi : r1 * cap_hi + (c - r1) * cap_lo;
+  }
+  int n2 = N2 - q.first2;
+  q.n2 = n2 < 0 ? 0 : (n2 > cap ? cap : n2);
+  return q;
+}
+
+// Issues slot `k` of wave w's stream (a dummy past its end: out-of-range loads that
+// write zeros and read no memory, so the vmcnt of a slot stays fixed).
+template <int NS2, int R>
+__device__ __forceinline__ void q_issue(const QArgs& a, const QWork& q, uint32_t lb, int w, int k, int n_el,
+                                        __amdgpu_buffer_rsrc_t none) {
+  const int l = threadIdx.x & 63;
+  const uint32_t so = a.o_ring + static_cast<uint32_t>((w * R + k % R) * kQSlot);
+  if (k < q.n1 * q.m1) {
+    const int item = k / q.m1, s = w + 4 * (k - item * q.m1);
+    const int i = q.c + item * q.nwg, g = i / a.HB, j = i - g * a.HB;
+    const int e = lds_uni(lb + kQExp + 4 * g);
+    const int64_t step = (static_cast<int64_t>(e) * a.HB + j) * a.NS1 + s;
+    const uint8_t* wb = a.w13p + step * 4096 + l * 16;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(wb + t * 1024, so + t * 1024);
+    dma4(a.s13p + step * 256 + l * 4, so + 4096);
+  } else if (k < n_el) {
+    const int k2 = w + 4 * (k - q.n1 * q.m1);
+    const int t = q_tile(q, k2), g = t / q.TPE, rt = t - g * q.TPE;
+    const int e = lds_uni(lb + kQExp + 4 * g);
+    const int64_t tile = static_cast<int64_t>(e) * q.TPE + rt;
+    const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
+#pragma unroll
+    for (int s = 0; s < NS2; ++s) dma16(wb + s * 1024, so + s * 1024);
+#pragma unroll
+    for (int s = NS2; s < 4; ++s) bdma16(none, kOutside, so + s * 1024);
+    dma4(a.s2p + tile * 256 + l * 4, so + 4096);
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) bdma16(none, kOutside, so + s * 1024);
+    bdma4(none, kOutside, so + 4096);
+  }
+}
+
+template <int NS2, int R>
+__global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  agpr_form();
+  const int tid = threadIdx.x, l = tid & 63, w = wave_id();
+  const int grp = l >> 4, col = l & 15;
+  const uint32_t lb = lds_base();
+  const int nwg = gridDim.x, c = blockIdx.x;
+  const int D = a.D, HB = a.HB, NS1 = a.NS1, K = a.K, IP = a.IP;
+  const int nkb = D / 32, nxb = a.B * nkb, nroutes = a.B * K;
+  uint32_t* sw = reinterpret_cast<uint32_t*>(smem);
+
+  // ---- prologue: ids, raw x rows and the call number in flight together
+  if (tid < 16) sw[tid] = 0u;
+  if (tid < 32) sw[kQEmask / 4 + tid] = 0u;
+  if (tid < kQGMax) sw[kQTok / 4 + tid] = 0u;
+  int myid = -1;
+  if (tid < nroutes) myid = a.ids[tid];
+  uint32_t xw[kQXBlk][16];
+#pragma unroll
+  for (int i = 0; i < kQXBlk; ++i) {
+    const int blk = tid + i * kWG;
+    if (blk < nxb) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(blk) * 32);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 u = src[v];
+        xw[i][4 * v] = u.x; xw[i][4 * v + 1] = u.y; xw[i][4 * v + 2] = u.z; xw[i][4 * v + 3] = u.w;
+      }
+    }
+  }
+  uint32_t call = 0;
+  if (w == kStream && l == 0) {
+    call = ld_dev_u32(a.calls + c) + 1u;
+    st_dev_u32(a.calls + c, call);
+  }
+  __syncthreads();
+
+  // ---- routing (experts page, the capacity <= 8 path: one unit per distinct expert,
+  // experts ascending, tokens in token order)
+  const bool valid = myid >= 0 && myid < a.E;
+  if (tid < nroutes) {
+    if (!valid) __hip_atomic_fetch_or(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else atomicOr(sw + kQEmask / 4 + (myid >> 5), 1u << (myid & 31));
+  }
+  __syncthreads();
+  if (tid < 32) {
+    const int pc = __popc(sw[kQEmask / 4 + tid]);
+    int inc = pc;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int o = __shfl_up(inc, d);
+      if (l >= d) inc += o;
+    }
+    sw[kQPre / 4 + tid] = static_cast<uint32_t>(inc - pc);
+    if (tid == 31) sw[kQGCount / 4] = static_cast<uint32_t>(inc);
+  }
+  __syncthreads();
+  int g_mine = -1;
+  if (tid < nroutes && valid) {
+    const uint32_t word = sw[kQEmask / 4 + (myid >> 5)];
+    g_mine = static_cast<int>(sw[kQPre / 4 + (myid >> 5)]) + __popc(word & ((1u << (myid & 31)) - 1u));
+    const int t = tid / K;
+    const uint32_t old = atomicOr(sw + kQTok / 4 + g_mine, 1u << t);
+    if (old & (1u << t)) __hip_atomic_fetch_or(a.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sw[kQExp / 4 + g_mine] = static_cast<uint32_t>(myid);
+  }
+  __syncthreads();
+  if (g_mine >= 0) {
+    const int t = tid / K;
+    const int cc = __popc(sw[kQTok / 4 + g_mine] & ((1u << t) - 1u));
+    reinterpret_cast<uint16_t*>(smem + kQRow)[g_mine * 8 + cc] = static_cast<uint16_t>(tid);
+  }
+  const int G = __builtin_amdgcn_readfirstlane(static_cast<int>(sw[kQGCount / 4]));
+  __syncthreads();
+
+  const QWork q = q_work(G, HB, NS1, NS2, D, nwg, c, w < kStream ? w : 0);
+  const __amdgpu_buffer_rsrc_t none =
+      __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
+
+  // ---- streaming waves start their weight streams; the x plan does not gate them
+  const int n2w = q.n2 > w ? (q.n2 - w + 3) / 4 : 0;
+  const int n_el = w < kStream ? q.n1 * q.m1 + n2w : 0;
+  if (w < kStream) {
+#pragma unroll 1
+    for (int k = 0; k < R; ++k) q_issue<NS2, R>(a, q, lb, w, k, n_el, none);
+  }
+
+  // ---- the MXFP8 plan of x (experts page, plan_chunk / mx_block), all waves, into LDS
+#pragma unroll
+  for (int i = 0; i < kQXBlk; ++i) {
+    const int blk = tid + i * kWG;
+    if (blk < nxb) {
+      uint32_t cw[8];
+      const int e = mx_block32(xw[i], cw);
+      const int t = blk / nkb, kb = blk - t * nkb;
+      const uint32_t dst = lb + a.o_xq + t * a.xstr + 32 * kb;
+      lds_st16_async(dst, make_uint4(cw[0], cw[1], cw[2], cw[3]));
+      lds_st16_async(dst + 16, make_uint4(cw[4], cw[5], cw[6], cw[7]));
+      lds_st1_async(lb + a.o_xs + t * a.xsstr + kb, static_cast<uint32_t>(e + 127));
+      if (a.plan_dump != nullptr && c == 0) {
+        uint4* pd = reinterpret_cast<uint4*>(a.plan_dump + static_cast<int64_t>(blk) * 32);
+        pd[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+        pd[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+        a.plan_dump[static_cast<int64_t>(nxb) * 32 + blk] = static_cast<uint8_t>(e + 127);
+      }
+    }
+  }
+  lds_settle_all();
+  if (l == 0) lds_add4(lb + kQXDone, 1u);
+
+  if (w < kStream) {
+    // =============================================================== streaming wave
+    v4f acc[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+    int cur_item = -1;
+    uint32_t px = 0, pxs = 0;  // the lane's x column (FC1)
+    bool xlive = false;
+    // FC2: the walk over the workgroup's tiles that numbers its experts (sequences)
+    int sc_k = -1, sc_g = -1, sc_seq = -1, cur_seq = -1;
+    int orow = -1;
+    uint32_t hbl = 0, hbs = 0;
+    const int n1el = q.n1 * q.m1;
+    if (n1el > 0) lds_wait<false>(lb + kQXDone, kStream + 1, a.err);
+#pragma unroll 1
+    for (int k = 0; k < n_el; ++k) {
+      wait_vm<(R - 1) * kQOps>();  // slot k has landed (the R - 1 younger ones may be in flight)
+      const uint32_t sa = lb + a.o_ring + static_cast<uint32_t>((w * R + k % R) * kQSlot);
+      if (k < n1el) {
+        const int item = k / q.m1, s = w + 4 * (k - item * q.m1);
+        if (item != cur_item) {
+          cur_item = item;
+          const int i = q.c + item * q.nwg, g = i / HB;
+          const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
+          const int ng = __popc(tok);
+          xlive = col < ng;
+          int t = 0;
+          if (xlive) t = static_cast<int>(lds_ld2(lb + kQRow + 2 * (g * 8 + col))) / K;
+          px = lb + a.o_xq + t * a.xstr + 16 * grp;
+          pxs = lb + a.o_xs + t * a.xsstr;
+        }
+        uint4 a0, a1, a2, a3, xl, xh;
+        uint32_t as, xs;
+        asm volatile(
+            "ds_read_b128 %0, %8 offset:0\n\t"
+            "ds_read_b128 %1, %8 offset:1024\n\t"
+            "ds_read_b128 %2, %8 offset:2048\n\t"
+            "ds_read_b128 %3, %8 offset:3072\n\t"
+            "ds_read_b32 %4, %9 offset:4096\n\t"
+            "ds_read_b128 %5, %10 offset:0\n\t"
+            "ds_read_b128 %6, %10 offset:64\n\t"
+            "ds_read_b32 %7, %11 offset:0\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(as), "=&v"(xl), "=&v"(xh), "=&v"(xs)
+            : "v"(sa + l * 16), "v"(sa + l * 4), "v"(px + 128 * s), "v"(pxs + 4 * s)
+            : "memory");
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        const v8i bop = fp8_operand(xlive ? xl : z, xlive ? xh : z);
+        const int sb = xlive ? static_cast<int>((xs >> (8 * grp)) & 0xffu) : 127;
+        acc[0] = mfma_fp4_fp8(fp4_operand(a0), bop, acc[0], static_cast<int>(as & 0xffu), sb);
+        acc[1] = mfma_fp4_fp8(fp4_operand(a1), bop, acc[1], static_cast<int>((as >> 8) & 0xffu), sb);
+        acc[2] = mfma_fp4_fp8(fp4_operand(a2), bop, acc[2], static_cast<int>((as >> 16) & 0xffu), sb);
+        acc[3] = mfma_fp4_fp8(fp4_operand(a3), bop, acc[3], static_cast<int>(as >> 24), sb);
+        if (s + 4 >= NS1) {
+          // the wave's part of the block is done: hand its partial tiles to the control
+          // wave once it has taken the previous block's
+          mfma_settle(acc[0], acc[1], acc[2], acc[3]);
+          lds_wait<false>(lb + kQCons, item, a.err);
+          const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(w * 4096 + l * 16);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            lds_st16_async(rd + rt * 1024, make_uint4(__float_as_uint(acc[rt][0]), __float_as_uint(acc[rt][1]),
+                                                      __float_as_uint(acc[rt][2]), __float_as_uint(acc[rt][3])));
+            acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+          }
+          lds_settle_all();
+          if (l == 0) lds_st4(lb + kQProg + 4 * w, static_cast<uint32_t>(item + 1));
+        }
+      } else {
+        const int k2 = w + 4 * (k - n1el);
+#pragma unroll 1
+        while (sc_k < k2) {
+          ++sc_k;
+          const int gg = q_tile(q, sc_k) / q.TPE;
+          if (gg != sc_g) { sc_g = gg; ++sc_seq; }
+        }
+        const int t = q_tile(q, k2), rt2 = t - sc_g * q.TPE;
+        if (sc_seq != cur_seq) {
+          cur_seq = sc_seq;
+          if (l == 0) lds_st4(lb + kQProg2 + 4 * w, static_cast<uint32_t>(cur_seq));
+          lds_wait<false>(lb + kQReady, cur_seq + 1, a.err);
+          const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * sc_g));
+          orow = -1;
+          if (col < __popc(tok)) orow = static_cast<int>(lds_ld2(lb + kQRow + 2 * (sc_g * 8 + col))) * D;
+          const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(cur_seq & 1) * a.hid_bytes;
+          const int hcol = orow >= 0 ? col : 0;  // other lanes read column 0 and use zeros
+          hbl = hb + hcol * IP + 16 * grp;
+          hbs = hb + 8 * IP + hcol * kQHB;
+        }
+        uint4 wa0, wa1, wa2, wa3;
+        uint32_t was;
+        asm volatile(
+            "ds_read_b128 %0, %5 offset:0\n\t"
+            "ds_read_b128 %1, %5 offset:1024\n\t"
+            "ds_read_b128 %2, %5 offset:2048\n\t"
+            "ds_read_b128 %3, %5 offset:3072\n\t"
+            "ds_read_b32 %4, %6 offset:4096\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(wa0), "=&v"(wa1), "=&v"(wa2), "=&v"(wa3), "=&v"(was)
+            : "v"(sa + l * 16), "v"(sa + l * 4)
+            : "memory");
+        const uint4 wa[4] = {wa0, wa1, wa2, wa3};
+        HidOps<NS2> hop;
+        hid_read<NS2>(hbl, hbs, hop);
+        const bool live = orow >= 0;
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        v4f o = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS2; ++s) {
+          // K-blocks at or beyond I (I not a multiple of 128) are zero: the weights are
+          // zero-padded there and the hidden holds no codes
+          const bool lo_ok = live && 4 * s + (grp >> 1) < HB, hi_ok = live && 4 * s + 2 + (grp >> 1) < HB;
+          const bool sc_ok = live && 4 * s + grp < HB;
+          o = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(lo_ok ? hop.bl[s] : z, hi_ok ? hop.bh[s] : z), o,
+                           static_cast<int>((was >> (8 * s)) & 0xffu),
+                           sc_ok ? static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu) : 127);
+        }
+        mfma_settle(o);
+        if (orow >= 0) {
+          const uint2 v = make_uint2(to_bf16_bits(o[0]) | (to_bf16_bits(o[1]) << 16),
+                                     to_bf16_bits(o[2]) | (to_bf16_bits(o[3]) << 16));
+          *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(orow) + 16 * rt2 + 4 * grp) = v;
+        }
+      }
+      q_issue<NS2, R>(a, q, lb, w, k + R, n_el, none);  // into the slot just consumed
+    }
+    if (l == 0) lds_st4(lb + kQProg2 + 4 * w, 0x7fffffffu);
+    wait_vm<0>();  // the dummy slots land before the workgroup ends
+    return;
+  }
+
+  // ================================================================= control wave
+  call = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(__shfl(call, 0))));
+  // FC1: finish the workgroup's hidden blocks in order
+#pragma unroll 1
+  for (int k = 0; k < q.n1; ++k) {
+    const int i = q.c + k * q.nwg, g = i / HB, j = i - g * HB;
+#pragma unroll 1
+    for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(lb + kQProg + 4 * ww, k + 1, a.err);
+    v4f tot[4];
+    {
+      const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(l * 16);
+      uint4 p[4][4];
+#pragma unroll
+      for (int ww = 0; ww < kStream; ++ww)
+        lds_ld16x4<0, 1024>(rd + ww * 4096, p[ww][0], p[ww][1], p[ww][2], p[ww][3]);
+      if (l == 0) lds_st4(lb + kQCons, static_cast<uint32_t>(k + 1));
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        tot[rt] = v4f{__uint_as_float(p[0][rt].x), __uint_as_float(p[0][rt].y), __uint_as_float(p[0][rt].z),
+                      __uint_as_float(p[0][rt].w)};
+#pragma unroll
+        for (int ww = 1; ww < kStream; ++ww) {
+          tot[rt][0] += __uint_as_float(p[ww][rt].x);
+          tot[rt][1] += __uint_as_float(p[ww][rt].y);
+          tot[rt][2] += __uint_as_float(p[ww][rt].z);
+          tot[rt][3] += __uint_as_float(p[ww][rt].w);
+        }
+      }
+    }
+    // SwiGLU and MXFP8 of the block (experts page, store_hidden): lane (col, grp) holds
+    // hidden values 32j + 4grp + r (tile 0) and 32j + 16 + 4grp + r (tile 1) of column col
+    float h[2][4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gv = tot[half][r], uv = tot[2 + half][r];
+        h[half][r] = gv / (1.0f + expf(-gv)) * uv;
+        amax = fmaxf(amax, fabsf(h[half][r]));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int e = mx_exponent(amax, a.floor_rule != 0);
+    const float sc = exp2_neg(e);
+    uint32_t word[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      word[half] = to_e4m3(h[half][0] * sc) | (to_e4m3(h[half][1] * sc) << 8) | (to_e4m3(h[half][2] * sc) << 16) |
+                   (to_e4m3(h[half][3] * sc) << 24);
+    const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
+    if (col < __popc(tok)) {
+      uint8_t* hc = a.hcodes + (static_cast<int64_t>(g) * 8 + col) * IP + 32 * j + 4 * grp;
+      st_dev_u32(hc, word[0]);
+      st_dev_u32(hc + 16, word[1]);
+      if (grp == 0) st_dev_u8(a.hscales + (static_cast<int64_t>(g) * 8 + col) * kQHB + j, static_cast<uint8_t>(e + 127));
+      if (a.dump_codes != nullptr) {
+        const int pair = static_cast<int>(lds_ld2(lb + kQRow + 2 * (g * 8 + col)));
+        uint8_t* dc = a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 4 * grp;
+        *reinterpret_cast<uint32_t*>(dc) = word[0];
+        *reinterpret_cast<uint32_t*>(dc + 16) = word[1];
+        if (grp == 0) a.dump_scales[static_cast<int64_t>(pair) * HB + j] = static_cast<uint8_t>(e + 127);
+      }
+    }
+    // publish: the block's codes and scales are stored (sc1) before its flag
+    wait_stores();
+    if (l == 0) st_dev_u32(a.flags + g * kQHB + j, call);
+  }
+
+  // FC2: for each expert of the workgroup's tiles, in order, wait for its blocks and copy
+  // its hidden into one of the two LDS hidden buffers
+  int seq = -1, prev_g = -1;
+#pragma unroll 1
+  for (int k2 = 0; k2 < q.n2; ++k2) {
+    const int g = q_tile(q, k2) / q.TPE;
+    if (g == prev_g) continue;
+    prev_g = g;
+    ++seq;
+    if (seq >= 2) {
+#pragma unroll 1
+      for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(lb + kQProg2 + 4 * ww, seq - 1, a.err);
+    }
+#pragma unroll 1
+    for (uint32_t spins = 0;; ++spins) {
+      const bool ok = l >= HB || ld_dev_u32(a.flags + g * kQHB + l) == call;
+      if (__all(ok)) break;
+      if (spins == kSpinLimit) {
+        if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    compiler_fence();
+    const int ng = __popc(static_cast<int>(lds_ld4(lb + kQTok + 4 * g)));
+    const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(seq & 1) * a.hid_bytes;
+    const uint8_t* src = a.hcodes + static_cast<int64_t>(g) * 8 * IP;
+    const int nq = ng * IP / 8;  // 8-byte words of codes
+    uint64_t v[8];
+#pragma unroll 1
+    for (int base = 0; base < nq; base += 8 * 64) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * 64 + l;
+        v[u] = idx < nq ? ld_dev_u64(src + static_cast<int64_t>(idx) * 8) : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * 64 + l;
+        if (idx < nq) {
+          asm volatile("ds_write_b64 %0, %1" : : "v"(hb + idx * 8), "v"(v[u]) : "memory");
+        }
+      }
+    }
+    if (l < ng * kQHB / 8) {
+      const uint64_t s8 = ld_dev_u64(a.hscales + static_cast<int64_t>(g) * 8 * kQHB + l * 8);
+      asm volatile("ds_write_b64 %0, %1" : : "v"(hb + 8 * IP + l * 8), "v"(s8) : "memory");
+    }
+    lds_settle_all();
+    if (l == 0) lds_st4(lb + kQReady, static_cast<uint32_t>(seq + 1));
+  }
+}
+
 using ExpertsFn = void (*)(ExpArgs);
 
 template <int R, bool DEC, bool TAG>
@@ -2377,6 +2898,9 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids, int32_t B,
+                     int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream);
+
 // Checks, kernel variant, grid and arguments shared by both forms; enqueues one launch.
 template <bool DEC>
 int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* plan, const void* units,
@@ -2391,16 +2915,18 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
   if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 1) ||
-      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > ((DEC && o.exchange == 2) ? 7 : 4))) ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
     return MOE_EINVAL;
   if (!DEC && (o.plan_dev != nullptr || o.status_dev != nullptr || o.exchange != 0))
     return MOE_EINVAL;  // decode-form options
-  if (o.exchange < 0 || o.exchange > 1) return MOE_EINVAL;
+  if (o.exchange < 0 || o.exchange > (DEC ? 2 : 0)) return MOE_EINVAL;
   if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
   if (!DEC && units_bytes < units_layout(B, topk, E).end) return MOE_ENOSPACE;
   if (DEC && o.plan_bytes != 0 && o.plan_dev == nullptr) return MOE_EINVAL;
   if (DEC && o.plan_dev != nullptr && o.plan_bytes < static_cast<size_t>(B) * D / 32 * 33) return MOE_ENOSPACE;
+  if (DEC && o.exchange == 2)
+    return run_decode_whole(wts, o, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
   if (B_cap < B) return MOE_ENOSPACE;
   const WsLayout L = ws_layout(E, D, I, topk, B_cap);
@@ -2469,6 +2995,120 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   return launch_status();
 }
 
+
+// ------------------------------------------------- decode form, whole-K FC1 blocks (host)
+using QFn = void (*)(QArgs);
+template <int NS2>
+QFn pick_q_r(int R) {
+  switch (R) {
+    case 3: return decode_whole_kernel<NS2, 3>;
+    case 4: return decode_whole_kernel<NS2, 4>;
+    case 5: return decode_whole_kernel<NS2, 5>;
+    case 6: return decode_whole_kernel<NS2, 6>;
+    default: return decode_whole_kernel<NS2, 7>;
+  }
+}
+QFn pick_q(int ns2, int R) {
+  switch (ns2) {
+    case 1: return pick_q_r<1>(R);
+    case 2: return pick_q_r<2>(R);
+    case 3: return pick_q_r<3>(R);
+    default: return pick_q_r<4>(R);
+  }
+}
+
+struct QLds {
+  uint32_t o_red, o_hid, o_xq, o_xs, o_ring, xstr, xsstr, hid_bytes;
+  size_t bytes(int R) const { return o_ring + static_cast<size_t>(4) * R * kQSlot; }
+};
+QLds q_lds(int B, int D, int IP) {
+  QLds m;
+  auto a16 = [](uint32_t v) { return (v + 15u) & ~15u; };
+  m.o_red = a16(kQTables);
+  m.hid_bytes = 8u * IP + 8u * kQHB;
+  m.o_hid = m.o_red + kStream * 4096u;
+  m.xstr = static_cast<uint32_t>(D) + 16u;
+  m.xsstr = static_cast<uint32_t>(D) / 32u;
+  m.o_xq = a16(m.o_hid + 2u * m.hid_bytes);
+  m.o_xs = a16(m.o_xq + static_cast<uint32_t>(B) * m.xstr);
+  m.o_ring = a16(m.o_xs + static_cast<uint32_t>(B) * m.xsstr);
+  return m;
+}
+
+// The decode form with whole-K FC1 blocks (moe_run_opts_t.exchange == 2).  Returns
+// MOE_EINVAL for shapes outside its limits: at most 128 distinct experts, B*topk <= 320
+// routes and B*D/32 <= 4 * 320 blocks of x.
+int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids, int32_t B,
+                     int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
+  const int E = wts->E, D = wts->D, I = wts->I;
+  const int64_t routes = static_cast<int64_t>(B) * topk;
+  const int64_t gmax = routes < E ? routes : E;
+  if (I > 512 || gmax > kQGMax || routes > kWG ||
+      static_cast<int64_t>(B) * D / 32 > static_cast<int64_t>(kQXBlk) * kWG)
+    return MOE_EINVAL;
+  const int IP = (I + 127) / 128 * 128, ns2 = IP / 128;
+  const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
+  if (B_cap < B) return MOE_ENOSPACE;
+  const WsLayout L = ws_layout(E, D, I, topk, B_cap);
+  const QLds m = q_lds(B, D, IP);
+  const size_t limit = static_cast<size_t>(device_lds_limit());
+  int R = 7;
+  if (o.ring) R = o.ring < 3 ? 3 : (o.ring > 7 ? 7 : o.ring);
+  while (R > 3 && m.bytes(R) > limit) --R;
+  if (m.bytes(R) > limit) return MOE_EINVAL;
+  const size_t lds = m.bytes(R);
+  const QFn fn = pick_q(ns2, R);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(lds)) != hipSuccess)
+    return MOE_EHIP;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kWG, lds) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  int cap = per_cu * device_cus();
+  if (cap > kMaxGrid) cap = kMaxGrid;
+  if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
+  const int grid = o.grid ? o.grid : cap;
+
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  QArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.w13p = static_cast<const uint8_t*>(wts->w13);
+  a.s13p = static_cast<const uint8_t*>(wts->s13);
+  a.w2p = static_cast<const uint8_t*>(wts->w2);
+  a.s2p = static_cast<const uint8_t*>(wts->s2);
+  a.x = static_cast<const uint16_t*>(x);
+  a.ids = ids;
+  a.out = static_cast<uint16_t*>(out);
+  a.hcodes = base + L.qhcodes;
+  a.hscales = base + L.qhscales;
+  a.flags = reinterpret_cast<uint32_t*>(base + L.qflags);
+  a.calls = reinterpret_cast<uint32_t*>(base + L.qcalls);
+  a.err = o.status_dev ? static_cast<int32_t*>(o.status_dev) : reinterpret_cast<int32_t*>(base + L.status);
+  a.dump_codes = static_cast<uint8_t*>(o.hidden_codes_dev);
+  a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
+  a.plan_dump = static_cast<uint8_t*>(o.plan_dev);
+  a.B = B;
+  a.K = topk;
+  a.E = E;
+  a.D = D;
+  a.I = I;
+  a.HB = I / 32;
+  a.NS1 = D / 128;
+  a.IP = IP;
+  a.floor_rule = o.hidden_rule == 2 || (o.hidden_rule == 0 && I == 384);
+  a.o_red = m.o_red;
+  a.o_hid = m.o_hid;
+  a.o_xq = m.o_xq;
+  a.o_xs = m.o_xs;
+  a.o_ring = m.o_ring;
+  a.xstr = m.xstr;
+  a.xsstr = m.xsstr;
+  a.hid_bytes = m.hid_bytes;
+  (void)out_bytes;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kWG), lds, as_stream(stream), a);
+  return launch_status();
+}
 }  // namespace
 
 // ====================================================================== C ABI

@@ -311,7 +311,7 @@ def _check_plan(d, p):
     assert np.array_equal(p[B * D:B * D * 33 // 32].reshape(B, D // 32), scales), "plan scales"
 
 
-EXCHANGES = [0, 1]  # finished hidden blocks; tagged partial sums reduced by the FC2 side
+EXCHANGES = [0, 1, 2]  # finished hidden blocks; tagged partial sums reduced by the FC2 side; whole-K blocks
 
 
 @pytest.mark.parametrize("exchange", EXCHANGES)
