@@ -424,7 +424,7 @@ constexpr int kMaxGroups = 1024;   // distinct experts per call (E <= 1024)
 
 struct WsLayout {
   size_t calls, status, arrive, flags, hcodes, hscales, partials;
-  size_t qcalls, qflags, qhcodes, qhscales;  // decode form with whole-K FC1 blocks
+  size_t qcalls, qhq;  // decode form with whole-K FC1 blocks
   size_t end;
   int64_t max_tiles, max_blocks;
   int64_t dec_slots;  // decode-form partial-sum slots (512 tagged pairs each)
@@ -473,16 +473,12 @@ WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   const size_t dec = static_cast<size_t>(L.dec_slots) * 4096;
   L.partials = off;
   off = align256(off + (grouped > dec ? grouped : dec));
-  // decode form with whole-K FC1 blocks: its own call counters, block flags and hidden
-  // (at most 128 distinct experts x 8 token columns)
+  // decode form with whole-K FC1 blocks: its own call counters and the hidden as
+  // (data, call) pairs (at most 128 distinct experts x 8 token columns x (IP/4 + 16))
   L.qcalls = off;
   off = align256(off + kMaxGrid * 4);
-  L.qflags = off;
-  off = align256(off + 128 * 16 * 4);
-  L.qhcodes = off;
-  off = align256(off + static_cast<size_t>(128) * 8 * IP);
-  L.qhscales = off;
-  off = align256(off + 128 * 8 * 16);
+  L.qhq = off;
+  off = align256(off + static_cast<size_t>(128) * 8 * (IP / 4 + 16) * 8);
   L.end = off;
   return L;
 }
@@ -829,6 +825,33 @@ __device__ __forceinline__ int mx_block32(const uint32_t (&w)[16], uint32_t (&c)
   for (int k = 0; k < 8; ++k)
     c[k] = to_e4m3(v[4 * k] * s) | (to_e4m3(v[4 * k + 1] * s) << 8) | (to_e4m3(v[4 * k + 2] * s) << 16) |
            (to_e4m3(v[4 * k + 3] * s) << 24);
+  return e;
+}
+
+// Four binary32 values to four e4m3 codes (byte i = value i) with gfx950's packed
+// conversion.  It rounds to nearest even like to_e4m3; inputs must lie in [-448, 448]
+// (callers clamp or know it), where the two agree on every value (checked exhaustively
+// on the device, both signs).
+__device__ __forceinline__ uint32_t cvt4_e4m3(float v0, float v1, float v2, float v3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true));
+}
+
+// mx_block32 with the packed conversion: the default exponent rule bounds every scaled
+// value by 448, so no clamp is needed.
+__device__ __forceinline__ int mx_block32_hw(const uint32_t (&w)[16], uint32_t (&c)[8]) {
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+  }
+  const int e = mx_exponent(amax, false);
+  const float s = exp2_neg(e);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = cvt4_e4m3(v[4 * k] * s, v[4 * k + 1] * s, v[4 * k + 2] * s, v[4 * k + 3] * s);
   return e;
 }
 
@@ -2321,21 +2344,25 @@ constexpr int kQSlot = 4096 + 256;  // slot bytes
 constexpr int kQOps = 5;            // DMA instructions per slot (pads keep it fixed)
 constexpr int kQGMax = 128;         // distinct experts per call
 constexpr int kQXBlk = 4;           // 32-element x blocks per thread held in the prologue
-constexpr int kQHB = 16;            // flag and scale words per (expert, column): HB <= 16
+constexpr int kQHB = 16;            // hidden scale slots per token column (HB <= 16)
+
+constexpr int kQStream = 8;                  // streaming waves per workgroup
+constexpr int kQWG = 64 * (kQStream + 1);    // plus one control wave
 
 // LDS: sync words and the routing tables of the batch (byte offsets from the LDS base).
-constexpr uint32_t kQProg = 0;      // [4] FC1 items whose partial tiles wave w has written
-constexpr uint32_t kQCons = 16;     // FC1 items whose partial tiles the control wave has read
-constexpr uint32_t kQProg2 = 32;    // [4] wave w is done with every FC2 hidden sequence < value
-constexpr uint32_t kQReady = 48;    // FC2 hidden sequences loaded into the two hidden buffers
-constexpr uint32_t kQXDone = 52;    // waves that have written their share of the x plan
-constexpr uint32_t kQGCount = 56;   // distinct experts of the batch
-constexpr uint32_t kQEmask = 64;    // [32] expert bitmask (E <= 1024)
-constexpr uint32_t kQPre = 192;     // [32] popcount prefix of the bitmask words
-constexpr uint32_t kQExp = 320;     // [kQGMax] expert id of group g (ascending)
-constexpr uint32_t kQTok = 832;     // [kQGMax] token bitmask of group g
-constexpr uint32_t kQRow = 1344;    // [kQGMax][8] u16: pair t*K+s of group g's column c
+constexpr uint32_t kQProg = 0;      // [8] FC1 items whose partial tiles wave w has written
+constexpr uint32_t kQProg2 = 32;    // [8] wave w is done with every FC2 hidden sequence < value
+constexpr uint32_t kQCons = 64;     // FC1 items whose partial tiles the control wave has read
+constexpr uint32_t kQReady = 68;    // FC2 hidden sequences loaded into the two hidden buffers
+constexpr uint32_t kQXDone = 72;    // waves that have written their share of the x plan
+constexpr uint32_t kQGCount = 76;   // distinct experts of the batch
+constexpr uint32_t kQEmask = 128;   // [32] expert bitmask (E <= 1024)
+constexpr uint32_t kQPre = 256;     // [32] popcount prefix of the bitmask words
+constexpr uint32_t kQExp = 384;     // [kQGMax] expert id of group g (ascending)
+constexpr uint32_t kQTok = 896;     // [kQGMax] token bitmask of group g
+constexpr uint32_t kQRow = 1408;    // [kQGMax][8] u16: pair t*K+s of group g's column c
 constexpr uint32_t kQTables = 3456;
+constexpr uint32_t kQRedWave = 2048;  // one wave's partial tiles: 4 tiles x 8 columns x 16 rows x FP32
 
 struct QArgs {
   const uint8_t* w13p;
@@ -2345,15 +2372,14 @@ struct QArgs {
   const uint16_t* x;      // BF16 [B, D]
   const int32_t* ids;     // [B, K]
   uint16_t* out;          // BF16 [B*K, D]
-  uint8_t* hcodes;        // [kQGMax][8][IP] hidden codes of this call
-  uint8_t* hscales;       // [kQGMax][8][kQHB] hidden scales
-  uint32_t* flags;        // [kQGMax][kQHB] call-tagged block flags
+  uint64_t* hq;           // [kQGMax][8][hq_words] the hidden as (data, call) pairs: per
+                          // column I/4 code words, then HB scale words
   uint32_t* calls;        // [kMaxGrid] per-workgroup call counters
   int32_t* err;           // status word (bit 0 id out of range, bit 1 repeated id, bit 2 a wait gave up)
   uint8_t* dump_codes;    // optional [B*K, I]
   uint8_t* dump_scales;   // optional [B*K, I/32]
   uint8_t* plan_dump;     // optional plan of x (moe_plan layout), written by workgroup 0
-  int B, K, E, D, I, HB, NS1, IP, floor_rule;
+  int B, K, E, D, I, HB, NS1, IP, floor_rule, hq_words;
   uint32_t o_red, o_hid, o_xq, o_xs, o_ring;  // LDS offsets
   uint32_t xstr, xsstr, hid_bytes;            // x code row stride, x scale row stride, one hidden buffer
 };
@@ -2368,15 +2394,13 @@ __device__ __forceinline__ void lds_st1_async(uint32_t addr, uint32_t v) {
 // The workgroup's share of the work (the same on every lane; all workgroups agree).
 struct QWork {
   int n1;      // FC1 items: i = c + k * grid, k < n1
-  int m1;      // this wave's K steps per FC1 item (steps w, w + 4, ...)
+  int m1;      // this wave's K steps per FC1 item (steps w, w + 8, ...; 0 for w >= NS1)
   int n2;      // FC2 tiles: the contiguous run first2 .. first2 + n2 - 1 (expert-major order)
   int first2;
   int TPE, nwg, c;
 };
 
-__device__ __forceinline__ int q_tile(const QWork& q, int k) { return q.first2 + k; }
-
-__device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int NS2, int D, int nwg, int c, int w) {
+__device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int D, int nwg, int c, int w) {
   QWork q;
   const int N1 = G * HB;
   q.nwg = nwg;
@@ -2385,64 +2409,80 @@ __device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int NS2, int D, 
   const int N2 = G * q.TPE;
   const int r1 = N1 % nwg;  // workgroups c < r1 hold one FC1 item more
   q.n1 = N1 / nwg + (c < r1 ? 1 : 0);
-  q.m1 = (NS1 - w + 3) / 4;
-  int cap;
-  if (r1 == 0) {
-    cap = (N2 + nwg - 1) / nwg;
-    q.first2 = c * cap;
-  } else {
-    // the workgroups with an FC1 item more take dlt FC2 tiles fewer (dlt tiles stream
-    // about the bytes of one FC1 item)
-    const int b1 = NS1 * kQSlot, b2 = NS2 * 1024 + 256;
-    const int dlt = (b1 + b2 / 2) / b2;
-    const int v = N2 - (nwg - r1) * dlt;
-    const int cap_hi = v <= 0 ? 0 : (v + nwg - 1) / nwg;
-    const int rest = N2 - r1 * cap_hi;
-    const int cap_lo = rest <= 0 ? 0 : (rest + (nwg - r1) - 1) / (nwg - r1);
-    cap = c < r1 ? cap_hi : cap_lo;
-    q.first2 = c < r1 ? c * cap_hi : r1 * cap_hi + (c - r1) * cap_lo;
-  }
-  int n2 = N2 - q.first2;
+  q.m1 = w < NS1 ? (NS1 - w + kQStream - 1) / kQStream : 0;
+  // FC2 tiles: equal contiguous runs.  A workgroup with an FC1 item more streams its
+  // FC2 weights while the hidden blocks are exchanged, which takes about as long.
+  const int cap = (N2 + nwg - 1) / nwg;
+  q.first2 = c * cap;
+  const int n2 = N2 - q.first2;
   q.n2 = n2 < 0 ? 0 : (n2 > cap ? cap : n2);
   return q;
 }
 
-// Issues slot `k` of wave w's stream (a dummy past its end: out-of-range loads that
-// write zeros and read no memory, so the vmcnt of a slot stays fixed).
+// The issue side of a streaming wave's slot sequence: its FC1 K steps (item by item),
+// then its FC2 tiles (w, w + 8, ... of the workgroup's run), then dummies (out-of-range
+// loads that write zeros and read no memory, so the vmcnt of a slot stays fixed).
+struct QIssue {
+  int k;          // slots issued
+  int item, si;   // next FC1 step: item of the workgroup, step index (s = w + 8 si)
+  int64_t step;   // its packed step index ((e * HB + j) * NS1 + s)
+  int g2, rt2;    // next FC2 tile: group and 16-row tile of its expert
+  int e2;         // expert of group g2 (cached)
+};
+
 template <int NS2, int R>
-__device__ __forceinline__ void q_issue(const QArgs& a, const QWork& q, uint32_t lb, int w, int k, int n_el,
-                                        __amdgpu_buffer_rsrc_t none) {
+__device__ __forceinline__ void q_issue(const QArgs& a, const QWork& q, uint32_t lb, int w, int n1el, int n_el,
+                                        QIssue& is, __amdgpu_buffer_rsrc_t none) {
   const int l = threadIdx.x & 63;
-  const uint32_t so = a.o_ring + static_cast<uint32_t>((w * R + k % R) * kQSlot);
-  if (k < q.n1 * q.m1) {
-    const int item = k / q.m1, s = w + 4 * (k - item * q.m1);
-    const int i = q.c + item * q.nwg, g = i / a.HB, j = i - g * a.HB;
-    const int e = lds_uni(lb + kQExp + 4 * g);
-    const int64_t step = (static_cast<int64_t>(e) * a.HB + j) * a.NS1 + s;
-    const uint8_t* wb = a.w13p + step * 4096 + l * 16;
+  const uint32_t so = a.o_ring + static_cast<uint32_t>((w * R + is.k % R) * kQSlot);
+  if (is.k < n1el) {
+    if (is.si == 0) {
+      const int i = q.c + is.item * q.nwg, g = i / a.HB, j = i - g * a.HB;
+      const int e = lds_uni(lb + kQExp + 4 * g);
+      is.step = (static_cast<int64_t>(e) * a.HB + j) * a.NS1 + w;
+    }
+    const uint8_t* wb = a.w13p + is.step * 4096 + l * 16;
 #pragma unroll
     for (int t = 0; t < 4; ++t) dma16(wb + t * 1024, so + t * 1024);
-    dma4(a.s13p + step * 256 + l * 4, so + 4096);
-  } else if (k < n_el) {
-    const int k2 = w + 4 * (k - q.n1 * q.m1);
-    const int t = q_tile(q, k2), g = t / q.TPE, rt = t - g * q.TPE;
-    const int e = lds_uni(lb + kQExp + 4 * g);
-    const int64_t tile = static_cast<int64_t>(e) * q.TPE + rt;
+    dma4(a.s13p + is.step * 256 + l * 4, so + 4096);
+    is.step += kQStream;
+    if (++is.si == q.m1) {
+      is.si = 0;
+      ++is.item;
+    }
+  } else if (is.k < n_el) {
+    if (is.k == n1el) {  // first FC2 tile of this wave
+      const int t = q.first2 + w;
+      is.g2 = t / q.TPE;
+      is.rt2 = t - is.g2 * q.TPE;
+      is.e2 = lds_uni(lb + kQExp + 4 * is.g2);
+    }
+    const int64_t tile = static_cast<int64_t>(is.e2) * q.TPE + is.rt2;
     const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
 #pragma unroll
     for (int s = 0; s < NS2; ++s) dma16(wb + s * 1024, so + s * 1024);
 #pragma unroll
     for (int s = NS2; s < 4; ++s) bdma16(none, kOutside, so + s * 1024);
     dma4(a.s2p + tile * 256 + l * 4, so + 4096);
+    is.rt2 += kQStream;
+    if (is.rt2 >= q.TPE && is.k + 1 < n_el) {
+#pragma unroll 1
+      while (is.rt2 >= q.TPE) {
+        is.rt2 -= q.TPE;
+        ++is.g2;
+      }
+      is.e2 = lds_uni(lb + kQExp + 4 * is.g2);
+    }
   } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) bdma16(none, kOutside, so + s * 1024);
     bdma4(none, kOutside, so + 4096);
   }
+  ++is.k;
 }
 
 template <int NS2, int R>
-__global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
+__global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   agpr_form();
   const int tid = threadIdx.x, l = tid & 63, w = wave_id();
@@ -2454,7 +2494,7 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
   uint32_t* sw = reinterpret_cast<uint32_t*>(smem);
 
   // ---- prologue: ids, raw x rows and the call number in flight together
-  if (tid < 16) sw[tid] = 0u;
+  if (tid < 20) sw[tid] = 0u;
   if (tid < 32) sw[kQEmask / 4 + tid] = 0u;
   if (tid < kQGMax) sw[kQTok / 4 + tid] = 0u;
   int myid = -1;
@@ -2462,7 +2502,7 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
   uint32_t xw[kQXBlk][16];
 #pragma unroll
   for (int i = 0; i < kQXBlk; ++i) {
-    const int blk = tid + i * kWG;
+    const int blk = tid + i * kQWG;
     if (blk < nxb) {
       const uint4* src = reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(blk) * 32);
 #pragma unroll
@@ -2473,7 +2513,7 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
     }
   }
   uint32_t call = 0;
-  if (w == kStream && l == 0) {
+  if (w == kQStream && l == 0) {
     call = ld_dev_u32(a.calls + c) + 1u;
     st_dev_u32(a.calls + c, call);
   }
@@ -2517,25 +2557,32 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
   const int G = __builtin_amdgcn_readfirstlane(static_cast<int>(sw[kQGCount / 4]));
   __syncthreads();
 
-  const QWork q = q_work(G, HB, NS1, NS2, D, nwg, c, w < kStream ? w : 0);
+  const QWork q = q_work(G, HB, NS1, D, nwg, c, w < kQStream ? w : 0);
   const __amdgpu_buffer_rsrc_t none =
       __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
+  const int nw1 = NS1 < kQStream ? NS1 : kQStream;  // waves that take FC1 steps
 
   // ---- streaming waves start their weight streams; the x plan does not gate them
-  const int n2w = q.n2 > w ? (q.n2 - w + 3) / 4 : 0;
-  const int n_el = w < kStream ? q.n1 * q.m1 + n2w : 0;
-  if (w < kStream) {
+  const int n1el = w < kQStream ? q.n1 * q.m1 : 0;
+  const int n2w = q.n2 > w ? (q.n2 - w + kQStream - 1) / kQStream : 0;
+  const int n_el = w < kQStream ? n1el + n2w : 0;
+  QIssue is;
+  is.k = 0;
+  is.item = is.si = 0;
+  is.step = 0;
+  is.g2 = is.rt2 = is.e2 = 0;
+  if (w < kQStream) {
 #pragma unroll 1
-    for (int k = 0; k < R; ++k) q_issue<NS2, R>(a, q, lb, w, k, n_el, none);
+    for (int k = 0; k < R; ++k) q_issue<NS2, R>(a, q, lb, w, n1el, n_el, is, none);
   }
 
   // ---- the MXFP8 plan of x (experts page, plan_chunk / mx_block), all waves, into LDS
 #pragma unroll
   for (int i = 0; i < kQXBlk; ++i) {
-    const int blk = tid + i * kWG;
+    const int blk = tid + i * kQWG;
     if (blk < nxb) {
       uint32_t cw[8];
-      const int e = mx_block32(xw[i], cw);
+      const int e = mx_block32_hw(xw[i], cw);
       const int t = blk / nkb, kb = blk - t * nkb;
       const uint32_t dst = lb + a.o_xq + t * a.xstr + 32 * kb;
       lds_st16_async(dst, make_uint4(cw[0], cw[1], cw[2], cw[3]));
@@ -2552,37 +2599,33 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
   lds_settle_all();
   if (l == 0) lds_add4(lb + kQXDone, 1u);
 
-  if (w < kStream) {
+  const int g0 = q.first2 / q.TPE;  // expert of the workgroup's first FC2 tile (sequence 0)
+
+  if (w < kQStream) {
     // =============================================================== streaming wave
-    v4f acc[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-    int cur_item = -1;
-    uint32_t px = 0, pxs = 0;  // the lane's x column (FC1)
-    bool xlive = false;
-    // FC2: the walk over the workgroup's tiles that numbers its experts (sequences)
-    int sc_k = -1, sc_g = -1, sc_seq = -1, cur_seq = -1;
-    int orow = -1;
-    uint32_t hbl = 0, hbs = 0;
-    const int n1el = q.n1 * q.m1;
-    if (n1el > 0) lds_wait<false>(lb + kQXDone, kStream + 1, a.err);
+    int k = 0;
+    if (n1el > 0) lds_wait<false>(lb + kQXDone, kQStream + 1, a.err);
+    // ---- FC1: this wave's K steps of each of the workgroup's hidden blocks
 #pragma unroll 1
-    for (int k = 0; k < n_el; ++k) {
-      wait_vm<(R - 1) * kQOps>();  // slot k has landed (the R - 1 younger ones may be in flight)
-      const uint32_t sa = lb + a.o_ring + static_cast<uint32_t>((w * R + k % R) * kQSlot);
-      if (k < n1el) {
-        const int item = k / q.m1, s = w + 4 * (k - item * q.m1);
-        if (item != cur_item) {
-          cur_item = item;
-          const int i = q.c + item * q.nwg, g = i / HB;
-          const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
-          const int ng = __popc(tok);
-          xlive = col < ng;
-          int t = 0;
-          if (xlive) t = static_cast<int>(lds_ld2(lb + kQRow + 2 * (g * 8 + col))) / K;
-          px = lb + a.o_xq + t * a.xstr + 16 * grp;
-          pxs = lb + a.o_xs + t * a.xsstr;
-        }
+    for (int item = 0; item < q.n1 && q.m1 > 0; ++item) {
+      uint32_t px, pxs;
+      bool xlive;
+      {
+        const int i = q.c + item * q.nwg, g = i / HB;
+        const int ng = __popc(static_cast<int>(lds_ld4(lb + kQTok + 4 * g)));
+        xlive = col < ng;
+        int t = 0;
+        if (xlive) t = static_cast<int>(lds_ld2(lb + kQRow + 2 * (g * 8 + col))) / K;
+        px = lb + a.o_xq + t * a.xstr + 16 * grp + 128 * w;
+        pxs = lb + a.o_xs + t * a.xsstr + 4 * w;
+      }
+      v4f acc[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+      for (int si = 0; si < q.m1; ++si, ++k) {
+        wait_vm<(R - 1) * kQOps>();  // slot k has landed (the R - 1 younger ones may be in flight)
+        const uint32_t sa = lb + a.o_ring + static_cast<uint32_t>((w * R + k % R) * kQSlot);
         uint4 a0, a1, a2, a3, xl, xh;
         uint32_t as, xs;
         asm volatile(
@@ -2596,7 +2639,7 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
             "ds_read_b32 %7, %11 offset:0\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(as), "=&v"(xl), "=&v"(xh), "=&v"(xs)
-            : "v"(sa + l * 16), "v"(sa + l * 4), "v"(px + 128 * s), "v"(pxs + 4 * s)
+            : "v"(sa + l * 16), "v"(sa + l * 4), "v"(px + 1024 * si), "v"(pxs + 32 * si)
             : "memory");
         const uint4 z = make_uint4(0u, 0u, 0u, 0u);
         const v8i bop = fp8_operand(xlive ? xl : z, xlive ? xh : z);
@@ -2605,78 +2648,90 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
         acc[1] = mfma_fp4_fp8(fp4_operand(a1), bop, acc[1], static_cast<int>((as >> 8) & 0xffu), sb);
         acc[2] = mfma_fp4_fp8(fp4_operand(a2), bop, acc[2], static_cast<int>((as >> 16) & 0xffu), sb);
         acc[3] = mfma_fp4_fp8(fp4_operand(a3), bop, acc[3], static_cast<int>(as >> 24), sb);
-        if (s + 4 >= NS1) {
-          // the wave's part of the block is done: hand its partial tiles to the control
-          // wave once it has taken the previous block's
-          mfma_settle(acc[0], acc[1], acc[2], acc[3]);
-          lds_wait<false>(lb + kQCons, item, a.err);
-          const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(w * 4096 + l * 16);
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            lds_st16_async(rd + rt * 1024, make_uint4(__float_as_uint(acc[rt][0]), __float_as_uint(acc[rt][1]),
-                                                      __float_as_uint(acc[rt][2]), __float_as_uint(acc[rt][3])));
-            acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-          }
-          lds_settle_all();
-          if (l == 0) lds_st4(lb + kQProg + 4 * w, static_cast<uint32_t>(item + 1));
-        }
-      } else {
-        const int k2 = w + 4 * (k - n1el);
-#pragma unroll 1
-        while (sc_k < k2) {
-          ++sc_k;
-          const int gg = q_tile(q, sc_k) / q.TPE;
-          if (gg != sc_g) { sc_g = gg; ++sc_seq; }
-        }
-        const int t = q_tile(q, k2), rt2 = t - sc_g * q.TPE;
-        if (sc_seq != cur_seq) {
-          cur_seq = sc_seq;
-          if (l == 0) lds_st4(lb + kQProg2 + 4 * w, static_cast<uint32_t>(cur_seq));
-          lds_wait<false>(lb + kQReady, cur_seq + 1, a.err);
-          const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * sc_g));
-          orow = -1;
-          if (col < __popc(tok)) orow = static_cast<int>(lds_ld2(lb + kQRow + 2 * (sc_g * 8 + col))) * D;
-          const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(cur_seq & 1) * a.hid_bytes;
-          const int hcol = orow >= 0 ? col : 0;  // other lanes read column 0 and use zeros
-          hbl = hb + hcol * IP + 16 * grp;
-          hbs = hb + 8 * IP + hcol * kQHB;
-        }
-        uint4 wa0, wa1, wa2, wa3;
-        uint32_t was;
-        asm volatile(
-            "ds_read_b128 %0, %5 offset:0\n\t"
-            "ds_read_b128 %1, %5 offset:1024\n\t"
-            "ds_read_b128 %2, %5 offset:2048\n\t"
-            "ds_read_b128 %3, %5 offset:3072\n\t"
-            "ds_read_b32 %4, %6 offset:4096\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(wa0), "=&v"(wa1), "=&v"(wa2), "=&v"(wa3), "=&v"(was)
-            : "v"(sa + l * 16), "v"(sa + l * 4)
-            : "memory");
-        const uint4 wa[4] = {wa0, wa1, wa2, wa3};
-        HidOps<NS2> hop;
-        hid_read<NS2>(hbl, hbs, hop);
-        const bool live = orow >= 0;
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        v4f o = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < NS2; ++s) {
-          // K-blocks at or beyond I (I not a multiple of 128) are zero: the weights are
-          // zero-padded there and the hidden holds no codes
-          const bool lo_ok = live && 4 * s + (grp >> 1) < HB, hi_ok = live && 4 * s + 2 + (grp >> 1) < HB;
-          const bool sc_ok = live && 4 * s + grp < HB;
-          o = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(lo_ok ? hop.bl[s] : z, hi_ok ? hop.bh[s] : z), o,
-                           static_cast<int>((was >> (8 * s)) & 0xffu),
-                           sc_ok ? static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu) : 127);
-        }
-        mfma_settle(o);
-        if (orow >= 0) {
-          const uint2 v = make_uint2(to_bf16_bits(o[0]) | (to_bf16_bits(o[1]) << 16),
-                                     to_bf16_bits(o[2]) | (to_bf16_bits(o[3]) << 16));
-          *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(orow) + 16 * rt2 + 4 * grp) = v;
-        }
+        q_issue<NS2, R>(a, q, lb, w, n1el, n_el, is, none);  // into the slot just consumed
       }
-      q_issue<NS2, R>(a, q, lb, w, k + R, n_el, none);  // into the slot just consumed
+      // the wave's part of the block is done: hand its partial tiles (the 8 columns a
+      // batch of <= 8 tokens can use) to the control wave once it has taken the last ones
+      mfma_settle(acc[0], acc[1], acc[2], acc[3]);
+      lds_wait<false>(lb + kQCons, item, a.err);
+      if (col < 8) {
+        const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(w * kQRedWave + (grp * 8 + col) * 16);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          lds_st16_async(rd + rt * 512, make_uint4(__float_as_uint(acc[rt][0]), __float_as_uint(acc[rt][1]),
+                                                   __float_as_uint(acc[rt][2]), __float_as_uint(acc[rt][3])));
+      }
+      lds_settle_all();
+      if (l == 0) lds_st4(lb + kQProg + 4 * w, static_cast<uint32_t>(item + 1));
+    }
+
+    // ---- FC2: this wave's tiles of the workgroup's run (w, w + 8, ...)
+    int cur_seq = -1, orow = -1;
+    uint32_t hbl = 0, hbs = 0;
+    int g = 0, rt2 = 0;
+    if (k < n_el) {
+      const int t = q.first2 + w;
+      g = t / q.TPE;
+      rt2 = t - g * q.TPE;
+    }
+#pragma unroll 1
+    for (; k < n_el; ++k) {
+      wait_vm<(R - 1) * kQOps>();
+      const uint32_t sa = lb + a.o_ring + static_cast<uint32_t>((w * R + k % R) * kQSlot);
+      const int seq = g - g0;
+      if (seq != cur_seq) {
+        cur_seq = seq;
+        if (l == 0) lds_st4(lb + kQProg2 + 4 * w, static_cast<uint32_t>(cur_seq));
+        lds_wait<false>(lb + kQReady, cur_seq + 1, a.err);
+        const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
+        orow = -1;
+        if (col < __popc(tok)) orow = static_cast<int>(lds_ld2(lb + kQRow + 2 * (g * 8 + col))) * D;
+        const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(cur_seq & 1) * a.hid_bytes;
+        const int hcol = orow >= 0 ? col : 0;  // other lanes read column 0 and use zeros
+        hbl = hb + hcol * IP + 16 * grp;
+        hbs = hb + 8 * IP + hcol * kQHB;
+      }
+      uint4 wa0, wa1, wa2, wa3;
+      uint32_t was;
+      asm volatile(
+          "ds_read_b128 %0, %5 offset:0\n\t"
+          "ds_read_b128 %1, %5 offset:1024\n\t"
+          "ds_read_b128 %2, %5 offset:2048\n\t"
+          "ds_read_b128 %3, %5 offset:3072\n\t"
+          "ds_read_b32 %4, %6 offset:4096\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(wa0), "=&v"(wa1), "=&v"(wa2), "=&v"(wa3), "=&v"(was)
+          : "v"(sa + l * 16), "v"(sa + l * 4)
+          : "memory");
+      const uint4 wa[4] = {wa0, wa1, wa2, wa3};
+      HidOps<NS2> hop;
+      hid_read<NS2>(hbl, hbs, hop);
+      const bool live = orow >= 0;
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      v4f o = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS2; ++s) {
+        // K-blocks at or beyond I (I not a multiple of 128) are zero: the weights are
+        // zero-padded there and the hidden holds no codes
+        const bool lo_ok = live && 4 * s + (grp >> 1) < HB, hi_ok = live && 4 * s + 2 + (grp >> 1) < HB;
+        const bool sc_ok = live && 4 * s + grp < HB;
+        o = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(lo_ok ? hop.bl[s] : z, hi_ok ? hop.bh[s] : z), o,
+                         static_cast<int>((was >> (8 * s)) & 0xffu),
+                         sc_ok ? static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu) : 127);
+      }
+      mfma_settle(o);
+      if (live) {
+        const uint2 v = make_uint2(to_bf16_bits(o[0]) | (to_bf16_bits(o[1]) << 16),
+                                   to_bf16_bits(o[2]) | (to_bf16_bits(o[3]) << 16));
+        *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(orow) + 16 * rt2 + 4 * grp) = v;
+      }
+      q_issue<NS2, R>(a, q, lb, w, n1el, n_el, is, none);
+      rt2 += kQStream;
+#pragma unroll 1
+      while (rt2 >= q.TPE) {
+        rt2 -= q.TPE;
+        ++g;
+      }
     }
     if (l == 0) lds_st4(lb + kQProg2 + 4 * w, 0x7fffffffu);
     wait_vm<0>();  // the dummy slots land before the workgroup ends
@@ -2690,28 +2745,27 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
   for (int k = 0; k < q.n1; ++k) {
     const int i = q.c + k * q.nwg, g = i / HB, j = i - g * HB;
 #pragma unroll 1
-    for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(lb + kQProg + 4 * ww, k + 1, a.err);
+    for (int ww = 0; ww < nw1; ++ww) lds_wait<false>(lb + kQProg + 4 * ww, k + 1, a.err);
     v4f tot[4];
-    {
-      const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(l * 16);
-      uint4 p[4][4];
 #pragma unroll
-      for (int ww = 0; ww < kStream; ++ww)
-        lds_ld16x4<0, 1024>(rd + ww * 4096, p[ww][0], p[ww][1], p[ww][2], p[ww][3]);
-      if (l == 0) lds_st4(lb + kQCons, static_cast<uint32_t>(k + 1));
+    for (int rt = 0; rt < 4; ++rt) tot[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (col < 8) {
+      const uint32_t rd = lb + a.o_red + static_cast<uint32_t>((grp * 8 + col) * 16);
+#pragma unroll 1
+      for (int ww = 0; ww < nw1; ++ww) {  // partial tiles added in wave order
+        uint4 p0, p1, p2, p3;
+        lds_ld16x4<0, 512>(rd + ww * kQRedWave, p0, p1, p2, p3);
+        const uint4 p[4] = {p0, p1, p2, p3};
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        tot[rt] = v4f{__uint_as_float(p[0][rt].x), __uint_as_float(p[0][rt].y), __uint_as_float(p[0][rt].z),
-                      __uint_as_float(p[0][rt].w)};
-#pragma unroll
-        for (int ww = 1; ww < kStream; ++ww) {
-          tot[rt][0] += __uint_as_float(p[ww][rt].x);
-          tot[rt][1] += __uint_as_float(p[ww][rt].y);
-          tot[rt][2] += __uint_as_float(p[ww][rt].z);
-          tot[rt][3] += __uint_as_float(p[ww][rt].w);
+        for (int rt = 0; rt < 4; ++rt) {
+          tot[rt][0] += __uint_as_float(p[rt].x);
+          tot[rt][1] += __uint_as_float(p[rt].y);
+          tot[rt][2] += __uint_as_float(p[rt].z);
+          tot[rt][3] += __uint_as_float(p[rt].w);
         }
       }
     }
+    if (l == 0) lds_st4(lb + kQCons, static_cast<uint32_t>(k + 1));
     // SwiGLU and MXFP8 of the block (experts page, store_hidden): lane (col, grp) holds
     // hidden values 32j + 4grp + r (tile 0) and 32j + 16 + 4grp + r (tile 1) of column col
     float h[2][4];
@@ -2729,16 +2783,20 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
     const int e = mx_exponent(amax, a.floor_rule != 0);
     const float sc = exp2_neg(e);
     uint32_t word[2];
+    auto clampf = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };  // the floor rule saturates
 #pragma unroll
     for (int half = 0; half < 2; ++half)
-      word[half] = to_e4m3(h[half][0] * sc) | (to_e4m3(h[half][1] * sc) << 8) | (to_e4m3(h[half][2] * sc) << 16) |
-                   (to_e4m3(h[half][3] * sc) << 24);
+      word[half] = cvt4_e4m3(clampf(h[half][0] * sc), clampf(h[half][1] * sc), clampf(h[half][2] * sc),
+                             clampf(h[half][3] * sc));
     const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
     if (col < __popc(tok)) {
-      uint8_t* hc = a.hcodes + (static_cast<int64_t>(g) * 8 + col) * IP + 32 * j + 4 * grp;
-      st_dev_u32(hc, word[0]);
-      st_dev_u32(hc + 16, word[1]);
-      if (grp == 0) st_dev_u8(a.hscales + (static_cast<int64_t>(g) * 8 + col) * kQHB + j, static_cast<uint8_t>(e + 127));
+      // (data, call) pairs: one 8-byte device-coherent store carries a word and its tag,
+      // so no flag and no wait for the stores are needed
+      uint64_t* hq = a.hq + (static_cast<int64_t>(g) * 8 + col) * a.hq_words;
+      const uint64_t tag = static_cast<uint64_t>(call) << 32;
+      st_dev_u64(hq + 8 * j + grp, tag | word[0]);
+      st_dev_u64(hq + 8 * j + 4 + grp, tag | word[1]);
+      if (grp == 0) st_dev_u64(hq + a.I / 4 + j, tag | static_cast<uint32_t>(e + 127));
       if (a.dump_codes != nullptr) {
         const int pair = static_cast<int>(lds_ld2(lb + kQRow + 2 * (g * 8 + col)));
         uint8_t* dc = a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 4 * grp;
@@ -2747,58 +2805,54 @@ __global__ __launch_bounds__(kWG) void decode_whole_kernel(QArgs a) {
         if (grp == 0) a.dump_scales[static_cast<int64_t>(pair) * HB + j] = static_cast<uint8_t>(e + 127);
       }
     }
-    // publish: the block's codes and scales are stored (sc1) before its flag
-    wait_stores();
-    if (l == 0) st_dev_u32(a.flags + g * kQHB + j, call);
   }
 
-  // FC2: for each expert of the workgroup's tiles, in order, wait for its blocks and copy
-  // its hidden into one of the two LDS hidden buffers
-  int seq = -1, prev_g = -1;
+  // FC2: for each expert of the workgroup's run, in order, wait for its hidden and copy it
+  // into one of the two LDS hidden buffers
+  const int nseq = q.n2 > 0 ? (q.first2 + q.n2 - 1) / q.TPE - g0 + 1 : 0;
 #pragma unroll 1
-  for (int k2 = 0; k2 < q.n2; ++k2) {
-    const int g = q_tile(q, k2) / q.TPE;
-    if (g == prev_g) continue;
-    prev_g = g;
-    ++seq;
+  for (int seq = 0; seq < nseq; ++seq) {
+    const int g = g0 + seq;
     if (seq >= 2) {
 #pragma unroll 1
-      for (int ww = 0; ww < kStream; ++ww) lds_wait<false>(lb + kQProg2 + 4 * ww, seq - 1, a.err);
+      for (int ww = 0; ww < kQStream; ++ww) lds_wait<false>(lb + kQProg2 + 4 * ww, seq - 1, a.err);
     }
-#pragma unroll 1
-    for (uint32_t spins = 0;; ++spins) {
-      const bool ok = l >= HB || ld_dev_u32(a.flags + g * kQHB + l) == call;
-      if (__all(ok)) break;
-      if (spins == kSpinLimit) {
-        if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    compiler_fence();
+    // load the expert's (data, call) pairs until every one carries this call's tag
     const int ng = __popc(static_cast<int>(lds_ld4(lb + kQTok + 4 * g)));
     const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(seq & 1) * a.hid_bytes;
-    const uint8_t* src = a.hcodes + static_cast<int64_t>(g) * 8 * IP;
-    const int nq = ng * IP / 8;  // 8-byte words of codes
-    uint64_t v[8];
+    const uint64_t* src = a.hq + static_cast<int64_t>(g) * 8 * a.hq_words;
+    const int per_col = a.I / 4 + HB;  // pairs a column holds: code words, then scales
+    const int n = ng * per_col;
 #pragma unroll 1
-    for (int base = 0; base < nq; base += 8 * 64) {
+    for (int base = 0; base < n; base += 8 * 64) {
+      uint64_t v[8];
+#pragma unroll 1
+      for (uint32_t spins = 0;; ++spins) {
+        bool ok = true;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * 64 + l;
-        v[u] = idx < nq ? ld_dev_u64(src + static_cast<int64_t>(idx) * 8) : 0ull;
+        for (int u = 0; u < 8; ++u) {
+          const int idx = base + u * 64 + l;
+          const int cc = idx / per_col, r = idx - cc * per_col;
+          v[u] = idx < n ? ld_dev_u64(src + static_cast<int64_t>(cc) * a.hq_words + r) : 0ull;
+          ok = ok && (idx >= n || static_cast<uint32_t>(v[u] >> 32) == call);
+        }
+        if (__all(ok)) break;
+        if (spins == kSpinLimit) {
+          if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int idx = base + u * 64 + l;
-        if (idx < nq) {
-          asm volatile("ds_write_b64 %0, %1" : : "v"(hb + idx * 8), "v"(v[u]) : "memory");
+        if (idx < n) {
+          const int cc = idx / per_col, r = idx - cc * per_col;
+          const uint32_t d = static_cast<uint32_t>(v[u]);
+          if (r < a.I / 4) lds_st4_nw(hb + cc * IP + 4 * r, d);
+          else lds_st1(hb + 8 * IP + cc * kQHB + (r - a.I / 4), d);
         }
       }
-    }
-    if (l < ng * kQHB / 8) {
-      const uint64_t s8 = ld_dev_u64(a.hscales + static_cast<int64_t>(g) * 8 * kQHB + l * 8);
-      asm volatile("ds_write_b64 %0, %1" : : "v"(hb + 8 * IP + l * 8), "v"(s8) : "memory");
     }
     lds_settle_all();
     if (l == 0) lds_st4(lb + kQReady, static_cast<uint32_t>(seq + 1));
@@ -2915,7 +2969,7 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
   if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 1) ||
-      (o.ring != 0 && (o.ring < 2 || o.ring > ((DEC && o.exchange == 2) ? 7 : 4))) ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
     return MOE_EINVAL;
   if (!DEC && (o.plan_dev != nullptr || o.status_dev != nullptr || o.exchange != 0))
@@ -3001,11 +3055,9 @@ using QFn = void (*)(QArgs);
 template <int NS2>
 QFn pick_q_r(int R) {
   switch (R) {
+    case 2: return decode_whole_kernel<NS2, 2>;
     case 3: return decode_whole_kernel<NS2, 3>;
-    case 4: return decode_whole_kernel<NS2, 4>;
-    case 5: return decode_whole_kernel<NS2, 5>;
-    case 6: return decode_whole_kernel<NS2, 6>;
-    default: return decode_whole_kernel<NS2, 7>;
+    default: return decode_whole_kernel<NS2, 4>;
   }
 }
 QFn pick_q(int ns2, int R) {
@@ -3019,14 +3071,14 @@ QFn pick_q(int ns2, int R) {
 
 struct QLds {
   uint32_t o_red, o_hid, o_xq, o_xs, o_ring, xstr, xsstr, hid_bytes;
-  size_t bytes(int R) const { return o_ring + static_cast<size_t>(4) * R * kQSlot; }
+  size_t bytes(int R) const { return o_ring + static_cast<size_t>(kQStream) * R * kQSlot; }
 };
 QLds q_lds(int B, int D, int IP) {
   QLds m;
   auto a16 = [](uint32_t v) { return (v + 15u) & ~15u; };
   m.o_red = a16(kQTables);
   m.hid_bytes = 8u * IP + 8u * kQHB;
-  m.o_hid = m.o_red + kStream * 4096u;
+  m.o_hid = m.o_red + kQStream * kQRedWave;
   m.xstr = static_cast<uint32_t>(D) + 16u;
   m.xsstr = static_cast<uint32_t>(D) / 32u;
   m.o_xq = a16(m.o_hid + 2u * m.hid_bytes);
@@ -3043,8 +3095,8 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   const int E = wts->E, D = wts->D, I = wts->I;
   const int64_t routes = static_cast<int64_t>(B) * topk;
   const int64_t gmax = routes < E ? routes : E;
-  if (I > 512 || gmax > kQGMax || routes > kWG ||
-      static_cast<int64_t>(B) * D / 32 > static_cast<int64_t>(kQXBlk) * kWG)
+  if (I > 512 || gmax > kQGMax || routes > kQWG ||
+      static_cast<int64_t>(B) * D / 32 > static_cast<int64_t>(kQXBlk) * kQWG)
     return MOE_EINVAL;
   const int IP = (I + 127) / 128 * 128, ns2 = IP / 128;
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
@@ -3052,9 +3104,9 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   const WsLayout L = ws_layout(E, D, I, topk, B_cap);
   const QLds m = q_lds(B, D, IP);
   const size_t limit = static_cast<size_t>(device_lds_limit());
-  int R = 7;
-  if (o.ring) R = o.ring < 3 ? 3 : (o.ring > 7 ? 7 : o.ring);
-  while (R > 3 && m.bytes(R) > limit) --R;
+  int R = 4;
+  if (o.ring) R = o.ring < 2 ? 2 : (o.ring > 4 ? 4 : o.ring);
+  while (R > 2 && m.bytes(R) > limit) --R;
   if (m.bytes(R) > limit) return MOE_EINVAL;
   const size_t lds = m.bytes(R);
   const QFn fn = pick_q(ns2, R);
@@ -3062,7 +3114,7 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
                           static_cast<int>(lds)) != hipSuccess)
     return MOE_EHIP;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kWG, lds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kQWG, lds) !=
           hipSuccess || per_cu < 1)
     per_cu = 1;
   int cap = per_cu * device_cus();
@@ -3080,9 +3132,8 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   a.x = static_cast<const uint16_t*>(x);
   a.ids = ids;
   a.out = static_cast<uint16_t*>(out);
-  a.hcodes = base + L.qhcodes;
-  a.hscales = base + L.qhscales;
-  a.flags = reinterpret_cast<uint32_t*>(base + L.qflags);
+  a.hq = reinterpret_cast<uint64_t*>(base + L.qhq);
+  a.hq_words = IP / 4 + kQHB;
   a.calls = reinterpret_cast<uint32_t*>(base + L.qcalls);
   a.err = o.status_dev ? static_cast<int32_t*>(o.status_dev) : reinterpret_cast<int32_t*>(base + L.status);
   a.dump_codes = static_cast<uint8_t*>(o.hidden_codes_dev);
@@ -3106,7 +3157,7 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   a.xsstr = m.xsstr;
   a.hid_bytes = m.hid_bytes;
   (void)out_bytes;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kWG), lds, as_stream(stream), a);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kQWG), lds, as_stream(stream), a);
   return launch_status();
 }
 }  // namespace
