@@ -150,11 +150,18 @@ typedef struct {
                          width; other values are MOE_EINVAL) */
   int32_t ring;       /* weight items in flight per streaming wave (2..4); 0 = the deepest
                          that fits in LDS next to the unit table */
-  int32_t exchange;   /* moe_decode_run only: how FC1 results reach FC2 -- 0 = finished
-                         hidden blocks (the owner of a block's first step adds the other
-                         owners' partial sums, applies SwiGLU and MXFP8, publishes codes and
-                         a call-tagged flag), 1 = call-tagged FC1 partial sums that every
-                         FC2 workgroup reduces itself; other values MOE_EINVAL */
+  int32_t exchange;   /* moe_decode_run only: how FC1 results reach FC2 --
+                         0 = whole-K blocks (default): a hidden block's FC1 runs over all of
+                         K in one workgroup, which applies SwiGLU and MXFP8 and publishes the
+                         block as call-tagged (code word, call) pairs; batches beyond its
+                         limits (more than 128 distinct experts, more than 576 routes, I >
+                         512, B*D/32 > 2304) fall back to 2;
+                         1 = call-tagged FC1 partial sums that every FC2 workgroup reduces
+                         itself;
+                         2 = finished split blocks (the owner of a block's first step adds
+                         the other owners' partial sums, applies SwiGLU and MXFP8, publishes
+                         codes and a call-tagged flag);
+                         other values MOE_EINVAL */
   int32_t reserved[3];
   void* hidden_codes_dev;  /* optional u8 [B*topk, I]: the hidden's e4m3 codes per route */
   void* hidden_scales_dev; /* optional u8 [B*topk, I/32]: its E8M0 scales */

@@ -158,8 +158,8 @@ def moe_decode_run(weights: moe_weights_t, x, ids, ws, out, *, hidden_rule=0, gr
                    hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
     """The whole step of a batch of B <= 8 tokens in one launch: x BF16 [B, D] (or uint16
     bits), ids int32 [B, topk] -> out BF16 [B*topk, D]; optional plan (u8, the moe_plan
-    layout) and status (int32 [1]) outputs; exchange 0 (finished hidden blocks) or 1
-    (tagged partial sums)."""
+    layout) and status (int32 [1]) outputs; exchange 0 (whole-K hidden blocks, the
+    default), 1 (tagged partial sums) or 2 (finished split blocks)."""
     B, K = ids.shape
     opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, exchange)
     _check("moe_decode_run", lib.moe_decode_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(x), _ptr(ids), B, K,

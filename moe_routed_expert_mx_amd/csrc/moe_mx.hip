@@ -2320,7 +2320,7 @@ __global__ __launch_bounds__(kWG) void experts_kernel(ExpArgs a) {
 }
 
 // =================================================================== decode form, whole-K FC1 blocks
-// moe_decode_run with exchange == 2.  A variant of the decode form in which no hidden
+// moe_decode_run's default exchange.  A variant of the decode form in which no hidden
 // block is ever split between workgroups:
 //   * an FC1 item is one hidden block (distinct expert g, block j of 32 hidden values):
 //     the 64 weight rows gate 32j..32j+31 and the matching up rows over the whole of K.
@@ -2383,6 +2383,35 @@ struct QArgs {
   uint32_t o_red, o_hid, o_xq, o_xs, o_ring;  // LDS offsets
   uint32_t xstr, xsstr, hid_bytes;            // x code row stride, x scale row stride, one hidden buffer
 };
+
+// Sixteen 16-byte reads, one wait: p[u][rt] at addr + u * kQRedWave + rt * 512 (four
+// waves' partial tiles; the fourth wave's slot may be past the last participating wave,
+// still inside the partial-tile area).
+__device__ __forceinline__ void lds_ld16x16(uint32_t addr, uint4 (&p)[4][4]) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:0\n\t"
+      "ds_read_b128 %1, %16 offset:512\n\t"
+      "ds_read_b128 %2, %16 offset:1024\n\t"
+      "ds_read_b128 %3, %16 offset:1536\n\t"
+      "ds_read_b128 %4, %16 offset:2048\n\t"
+      "ds_read_b128 %5, %16 offset:2560\n\t"
+      "ds_read_b128 %6, %16 offset:3072\n\t"
+      "ds_read_b128 %7, %16 offset:3584\n\t"
+      "ds_read_b128 %8, %16 offset:4096\n\t"
+      "ds_read_b128 %9, %16 offset:4608\n\t"
+      "ds_read_b128 %10, %16 offset:5120\n\t"
+      "ds_read_b128 %11, %16 offset:5632\n\t"
+      "ds_read_b128 %12, %16 offset:6144\n\t"
+      "ds_read_b128 %13, %16 offset:6656\n\t"
+      "ds_read_b128 %14, %16 offset:7168\n\t"
+      "ds_read_b128 %15, %16 offset:7680\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(p[0][0]), "=&v"(p[0][1]), "=&v"(p[0][2]), "=&v"(p[0][3]), "=&v"(p[1][0]), "=&v"(p[1][1]),
+        "=&v"(p[1][2]), "=&v"(p[1][3]), "=&v"(p[2][0]), "=&v"(p[2][1]), "=&v"(p[2][2]), "=&v"(p[2][3]),
+        "=&v"(p[3][0]), "=&v"(p[3][1]), "=&v"(p[3][2]), "=&v"(p[3][3])
+      : "v"(addr)
+      : "memory");
+}
 
 __device__ __forceinline__ void lds_add4(uint32_t addr, uint32_t v) {
   asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
@@ -2750,18 +2779,22 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) tot[rt] = v4f{0.f, 0.f, 0.f, 0.f};
     if (col < 8) {
+      // the partial tiles of four waves per batch of reads (one wait), added in wave order
       const uint32_t rd = lb + a.o_red + static_cast<uint32_t>((grp * 8 + col) * 16);
 #pragma unroll 1
-      for (int ww = 0; ww < nw1; ++ww) {  // partial tiles added in wave order
-        uint4 p0, p1, p2, p3;
-        lds_ld16x4<0, 512>(rd + ww * kQRedWave, p0, p1, p2, p3);
-        const uint4 p[4] = {p0, p1, p2, p3};
+      for (int w0 = 0; w0 < nw1; w0 += 4) {
+        uint4 p[4][4];
+        lds_ld16x16(rd + w0 * kQRedWave, p);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          tot[rt][0] += __uint_as_float(p[rt].x);
-          tot[rt][1] += __uint_as_float(p[rt].y);
-          tot[rt][2] += __uint_as_float(p[rt].z);
-          tot[rt][3] += __uint_as_float(p[rt].w);
+        for (int u = 0; u < 4; ++u) {
+          if (w0 + u >= nw1) break;
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            tot[rt][0] += __uint_as_float(p[u][rt].x);
+            tot[rt][1] += __uint_as_float(p[u][rt].y);
+            tot[rt][2] += __uint_as_float(p[u][rt].z);
+            tot[rt][3] += __uint_as_float(p[u][rt].w);
+          }
         }
       }
     }
@@ -2954,6 +2987,7 @@ int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP
 
 int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids, int32_t B,
                      int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream);
+bool whole_fits(const moe_weights_t* wts, int32_t B, int32_t topk);
 
 // Checks, kernel variant, grid and arguments shared by both forms; enqueues one launch.
 template <bool DEC>
@@ -2979,7 +3013,9 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   if (!DEC && units_bytes < units_layout(B, topk, E).end) return MOE_ENOSPACE;
   if (DEC && o.plan_bytes != 0 && o.plan_dev == nullptr) return MOE_EINVAL;
   if (DEC && o.plan_dev != nullptr && o.plan_bytes < static_cast<size_t>(B) * D / 32 * 33) return MOE_ENOSPACE;
-  if (DEC && o.exchange == 2)
+  // the decode form's default exchange: whole-K blocks where the batch fits its limits,
+  // else finished split blocks
+  if (DEC && o.exchange == 0 && whole_fits(wts, B, topk))
     return run_decode_whole(wts, o, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
   if (B_cap < B) return MOE_ENOSPACE;
@@ -3087,17 +3123,21 @@ QLds q_lds(int B, int D, int IP) {
   return m;
 }
 
-// The decode form with whole-K FC1 blocks (moe_run_opts_t.exchange == 2).  Returns
-// MOE_EINVAL for shapes outside its limits: at most 128 distinct experts, B*topk <= 320
-// routes and B*D/32 <= 4 * 320 blocks of x.
+// The limits of the decode form with whole-K FC1 blocks: at most 128 distinct experts,
+// B*topk <= 576 routes, B*D/32 <= 4 * 576 blocks of x, I <= 512.
+bool whole_fits(const moe_weights_t* wts, int32_t B, int32_t topk) {
+  const int64_t routes = static_cast<int64_t>(B) * topk;
+  const int64_t gmax = routes < wts->E ? routes : wts->E;
+  return wts->I <= 512 && gmax <= kQGMax && routes <= kQWG &&
+         static_cast<int64_t>(B) * wts->D / 32 <= static_cast<int64_t>(kQXBlk) * kQWG;
+}
+
+// The decode form with whole-K FC1 blocks (moe_run_opts_t.exchange == 0, the default,
+// for batches within whole_fits).
 int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids, int32_t B,
                      int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
   const int E = wts->E, D = wts->D, I = wts->I;
-  const int64_t routes = static_cast<int64_t>(B) * topk;
-  const int64_t gmax = routes < E ? routes : E;
-  if (I > 512 || gmax > kQGMax || routes > kQWG ||
-      static_cast<int64_t>(B) * D / 32 > static_cast<int64_t>(kQXBlk) * kQWG)
-    return MOE_EINVAL;
+  if (!whole_fits(wts, B, topk)) return MOE_EINVAL;
   const int IP = (I + 127) / 128 * 128, ns2 = IP / 128;
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
   if (B_cap < B) return MOE_ENOSPACE;

@@ -149,7 +149,7 @@ def test_decode_run_argument_checks(m):
     o.plan_dev, o.plan_bytes = None, 64                        # a size without a buffer
     assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL
     o = m.moe_run_opts_t()
-    o.exchange = 2
+    o.exchange = 3
     assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # no such exchange
     o = m.moe_run_opts_t()
     o.exchange = 1                                             # a decode-form option

@@ -311,7 +311,7 @@ def _check_plan(d, p):
     assert np.array_equal(p[B * D:B * D * 33 // 32].reshape(B, D // 32), scales), "plan scales"
 
 
-EXCHANGES = [0, 1, 2]  # finished hidden blocks; tagged partial sums reduced by the FC2 side; whole-K blocks
+EXCHANGES = [0, 1, 2]  # whole-K blocks; tagged partial sums reduced by the FC2 side; finished split blocks
 
 
 @pytest.mark.parametrize("exchange", EXCHANGES)
@@ -399,10 +399,13 @@ def test_decode_form_matches_grouped_form_repeatedly(lib):
     layer = _layer(lib, d, B_max=64)
     a, _, _, _, _ = _decode_run(lib, layer, d)
     t, _, _, _, _ = _decode_run(lib, layer, d, exchange=1)
+    f, _, _, _, _ = _decode_run(lib, layer, d, exchange=2)
     d64 = workloads.generate("grouped_b64", with_weights=False)
     layer.forward(torch.from_numpy(d64["x"]).to(DEV), torch.from_numpy(d64["ids"] % d["workload"].E).to(DEV))
-    layer.forward(torch.from_numpy(d["x"][:3]).to(DEV), torch.from_numpy(d["ids"][:3]).to(DEV), path="decode",
-                  exchange=1)
+    for ex in EXCHANGES:  # a smaller batch (other experts, fewer columns) in between
+        layer.forward(torch.from_numpy(d["x"][:3]).to(DEV), torch.from_numpy(d["ids"][:3]).to(DEV), path="decode",
+                      exchange=ex)
     b, _, _, _, _ = _decode_run(lib, layer, d)
     u, _, _, _, _ = _decode_run(lib, layer, d, exchange=1)
-    assert np.array_equal(a, b) and np.array_equal(t, u)
+    g, _, _, _, _ = _decode_run(lib, layer, d, exchange=2)
+    assert np.array_equal(a, b) and np.array_equal(t, u) and np.array_equal(f, g)
