@@ -171,8 +171,13 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
     # form) + output rows
     act_bytes = w.B * w.D * 2 + w.B * w.K * 4 if decode else plan_bytes
     experts_bytes = uniq + act_bytes + w.B * w.K * w.D * 2
+    # the decode form's default exchange runs decode_whole_kernel (whole-K hidden blocks)
+    # for batches within its limits (at most 128 distinct experts); the others run
+    # experts_kernel
+    whole = decode and exchange in (None, 0) and min(w.E, w.B * w.K) <= 128
     res = {
-        "workload": name, "form": form, "B": w.B, "E": w.E, "topk": w.K, "D": w.D, "I": w.I,
+        "workload": name, "form": form,
+        "kernel": "decode_whole_kernel" if whole else ("experts_kernel (decode form)" if decode else "experts_kernel"), "B": w.B, "E": w.E, "topk": w.K, "D": w.D, "I": w.I,
         "distinct_experts": int(len(np.unique(d["ids"]))), "replicas": R, "graph_steps": G,
         "step_us": step_us, "experts_us": experts_us,
         "routes_per_s": w.B * w.K / (step_us * 1e-6),
@@ -281,7 +286,7 @@ def main():
         "hbm_frac_of_peak": round(main_res["step_gbs"] / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "experts_kernel (decode form)" if main_res["form"] == "decode" else "experts_kernel",
+            "kernel": main_res["kernel"],
             "achieved": round(main_res["experts_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
