@@ -191,16 +191,18 @@ int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
                     int32_t topk, void* ws_dev, size_t ws_bytes, void* out_dev, size_t out_bytes,
                     void* stream);
 
-/* The whole step of a small batch in one launch (B <= 8): the experts kernel also
- * quantizes x and routes the batch itself (experts page, the capacity <= 8 path of
- * ExpertsKernel, which skips the plan and group kernels: one unit per distinct expert,
- * its tokens in token order, the same table moe_group writes for such a batch).
+/* The whole step of a small batch in one launch (B <= 8): the kernel also quantizes x
+ * and routes the batch itself (experts page, the capacity <= 8 path of ExpertsKernel,
+ * which skips the plan and group kernels: one unit per distinct expert, its tokens in
+ * token order, the same table moe_group writes for such a batch).
  * Inputs x_dev BF16 [B, D] and ids_dev i32 [B, topk]; outputs as moe_experts_run
  * (out_dev BF16 [B*topk, D], top-k order; optional hidden dump), plus the optional plan
  * and status word of moe_run_opts_t.  The FC1 -> FC2 exchange is chosen by
- * opts->exchange (finished hidden blocks by default, or call-tagged partial sums; the
- * workspace from moe_workspace_bytes holds either).  Ids out of range are skipped and
- * flagged (status bit 0).
+ * opts->exchange: by default (0) each hidden block's FC1 runs over the whole of K in one
+ * workgroup, which publishes the finished block as call-tagged words; 1 and 2 are the
+ * split-block variants of the experts kernel (the workspace from moe_workspace_bytes
+ * holds any of them).  The FP32 sums of one call are summed in a fixed order, so repeated
+ * calls give identical rows.  Ids out of range are skipped and flagged (status bit 0).
  * Errors: MOE_EINVAL for B > 8 or the cases of moe_experts_run; MOE_ENOSPACE likewise.
  * The same residency and no-overlap rules as moe_experts_run apply. */
 int moe_decode_run(const moe_weights_t* weights, const moe_run_opts_t* opts, const void* x_dev,
