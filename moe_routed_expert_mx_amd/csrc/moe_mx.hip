@@ -2347,7 +2347,9 @@ constexpr int kQXBlk = 4;           // 32-element x blocks per thread held in th
 constexpr int kQHB = 16;            // hidden scale slots per token column (HB <= 16)
 
 constexpr int kQStream = 8;                  // streaming waves per workgroup
-constexpr int kQWG = 64 * (kQStream + 1);    // plus one control wave
+constexpr int kQFin = kQStream;             // the finisher wave: FC1 blocks' epilogues
+constexpr int kQLoad = kQStream + 1;         // the loader wave: FC2's hidden, polled and copied
+constexpr int kQWG = 64 * (kQStream + 2);
 
 // LDS: sync words and the routing tables of the batch (byte offsets from the LDS base).
 constexpr uint32_t kQProg = 0;      // [8] FC1 items whose partial tiles wave w has written
@@ -2356,6 +2358,7 @@ constexpr uint32_t kQCons = 64;     // FC1 items whose partial tiles the control
 constexpr uint32_t kQReady = 68;    // FC2 hidden sequences loaded into the two hidden buffers
 constexpr uint32_t kQXDone = 72;    // waves that have written their share of the x plan
 constexpr uint32_t kQGCount = 76;   // distinct experts of the batch
+constexpr uint32_t kQCall = 80;     // this call's number (tag of the published hidden)
 constexpr uint32_t kQEmask = 128;   // [32] expert bitmask (E <= 1024)
 constexpr uint32_t kQPre = 256;     // [32] popcount prefix of the bitmask words
 constexpr uint32_t kQExp = 384;     // [kQGMax] expert id of group g (ascending)
@@ -2541,10 +2544,10 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
       }
     }
   }
-  uint32_t call = 0;
-  if (w == kQStream && l == 0) {
-    call = ld_dev_u32(a.calls + c) + 1u;
-    st_dev_u32(a.calls + c, call);
+  if (w == kQFin && l == 0) {
+    const uint32_t cn = ld_dev_u32(a.calls + c) + 1u;
+    st_dev_u32(a.calls + c, cn);
+    sw[kQCall / 4] = cn;
   }
   __syncthreads();
 
@@ -2633,7 +2636,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   if (w < kQStream) {
     // =============================================================== streaming wave
     int k = 0;
-    if (n1el > 0) lds_wait<false>(lb + kQXDone, kQStream + 1, a.err);
+    if (n1el > 0) lds_wait<false>(lb + kQXDone, kQStream + 2, a.err);
     // ---- FC1: this wave's K steps of each of the workgroup's hidden blocks
 #pragma unroll 1
     for (int item = 0; item < q.n1 && q.m1 > 0; ++item) {
@@ -2683,7 +2686,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
       // batch of <= 8 tokens can use) to the control wave once it has taken the last ones
       mfma_settle(acc[0], acc[1], acc[2], acc[3]);
       lds_wait<false>(lb + kQCons, item, a.err);
-      if (col < 8) {
+      if (xlive) {  // the live token columns (col < ng <= 8)
         const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(w * kQRedWave + (grp * 8 + col) * 16);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
@@ -2711,7 +2714,6 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
       if (seq != cur_seq) {
         cur_seq = seq;
         if (l == 0) lds_st4(lb + kQProg2 + 4 * w, static_cast<uint32_t>(cur_seq));
-        lds_wait<false>(lb + kQReady, cur_seq + 1, a.err);
         const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
         orow = -1;
         if (col < __popc(tok)) orow = static_cast<int>(lds_ld2(lb + kQRow + 2 * (g * 8 + col))) * D;
@@ -2719,6 +2721,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
         const int hcol = orow >= 0 ? col : 0;  // other lanes read column 0 and use zeros
         hbl = hb + hcol * IP + 16 * grp;
         hbs = hb + 8 * IP + hcol * kQHB;
+        lds_wait<false>(lb + kQReady, cur_seq + 1, a.err);
       }
       uint4 wa0, wa1, wa2, wa3;
       uint32_t was;
@@ -2767,9 +2770,10 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     return;
   }
 
-  // ================================================================= control wave
-  call = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(__shfl(call, 0))));
-  // FC1: finish the workgroup's hidden blocks in order
+  const uint32_t call = static_cast<uint32_t>(lds_uni(lb + kQCall));
+  if (w == kQFin) {
+    // =============================================================== finisher wave
+    // FC1: finish the workgroup's hidden blocks in order
 #pragma unroll 1
   for (int k = 0; k < q.n1; ++k) {
     const int i = q.c + k * q.nwg, g = i / HB, j = i - g * HB;
@@ -2778,7 +2782,9 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     v4f tot[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) tot[rt] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (col < 8) {
+    const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
+    const bool live = col < __popc(tok);  // the block's token columns
+    if (live) {
       // the partial tiles of four waves per batch of reads (one wait), added in wave order
       const uint32_t rd = lb + a.o_red + static_cast<uint32_t>((grp * 8 + col) * 16);
 #pragma unroll 1
@@ -2821,8 +2827,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     for (int half = 0; half < 2; ++half)
       word[half] = cvt4_e4m3(clampf(h[half][0] * sc), clampf(h[half][1] * sc), clampf(h[half][2] * sc),
                              clampf(h[half][3] * sc));
-    const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
-    if (col < __popc(tok)) {
+    if (live) {
       // (data, call) pairs: one 8-byte device-coherent store carries a word and its tag,
       // so no flag and no wait for the stores are needed
       uint64_t* hq = a.hq + (static_cast<int64_t>(g) * 8 + col) * a.hq_words;
@@ -2840,8 +2845,12 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     }
   }
 
-  // FC2: for each expert of the workgroup's run, in order, wait for its hidden and copy it
-  // into one of the two LDS hidden buffers
+    return;
+  }
+  // ================================================================= loader wave
+  static_assert(kQLoad == kQStream + 1 && kQWG == 64 * (kQLoad + 1), "the loader is the last wave");
+  // FC2: for each expert of the workgroup's run, in order, wait for its hidden (polling
+  // from the start of the call) and copy it into one of the two LDS hidden buffers
   const int nseq = q.n2 > 0 ? (q.first2 + q.n2 - 1) / q.TPE - g0 + 1 : 0;
 #pragma unroll 1
   for (int seq = 0; seq < nseq; ++seq) {
