@@ -2387,35 +2387,6 @@ struct QArgs {
   uint32_t xstr, xsstr, hid_bytes;            // x code row stride, x scale row stride, one hidden buffer
 };
 
-// Sixteen 16-byte reads, one wait: p[u][rt] at addr + u * kQRedWave + rt * 512 (four
-// waves' partial tiles; the fourth wave's slot may be past the last participating wave,
-// still inside the partial-tile area).
-__device__ __forceinline__ void lds_ld16x16(uint32_t addr, uint4 (&p)[4][4]) {
-  asm volatile(
-      "ds_read_b128 %0, %16 offset:0\n\t"
-      "ds_read_b128 %1, %16 offset:512\n\t"
-      "ds_read_b128 %2, %16 offset:1024\n\t"
-      "ds_read_b128 %3, %16 offset:1536\n\t"
-      "ds_read_b128 %4, %16 offset:2048\n\t"
-      "ds_read_b128 %5, %16 offset:2560\n\t"
-      "ds_read_b128 %6, %16 offset:3072\n\t"
-      "ds_read_b128 %7, %16 offset:3584\n\t"
-      "ds_read_b128 %8, %16 offset:4096\n\t"
-      "ds_read_b128 %9, %16 offset:4608\n\t"
-      "ds_read_b128 %10, %16 offset:5120\n\t"
-      "ds_read_b128 %11, %16 offset:5632\n\t"
-      "ds_read_b128 %12, %16 offset:6144\n\t"
-      "ds_read_b128 %13, %16 offset:6656\n\t"
-      "ds_read_b128 %14, %16 offset:7168\n\t"
-      "ds_read_b128 %15, %16 offset:7680\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(p[0][0]), "=&v"(p[0][1]), "=&v"(p[0][2]), "=&v"(p[0][3]), "=&v"(p[1][0]), "=&v"(p[1][1]),
-        "=&v"(p[1][2]), "=&v"(p[1][3]), "=&v"(p[2][0]), "=&v"(p[2][1]), "=&v"(p[2][2]), "=&v"(p[2][3]),
-        "=&v"(p[3][0]), "=&v"(p[3][1]), "=&v"(p[3][2]), "=&v"(p[3][3])
-      : "v"(addr)
-      : "memory");
-}
-
 __device__ __forceinline__ void lds_add4(uint32_t addr, uint32_t v) {
   asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
 }
@@ -2526,7 +2497,14 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   uint32_t* sw = reinterpret_cast<uint32_t*>(smem);
 
   // ---- prologue: ids, raw x rows and the call number in flight together
-  if (tid < 20) sw[tid] = 0u;
+  if (tid < 21) sw[tid] = 0u;  // sync words and the call number
+  // the two hidden buffers start as zero codes with unit scales: the K-blocks past I (I
+  // not a multiple of 128) then multiply zero-padded weights by zero, and the token
+  // columns past a group's count hold finite values (their outputs are never stored)
+  for (int v = tid; v < static_cast<int>(a.hid_bytes / 2); v += kQWG) {
+    const uint32_t off = 4u * static_cast<uint32_t>(v), in_buf = off % a.hid_bytes;
+    sw[(a.o_hid + off) / 4] = in_buf < 8u * static_cast<uint32_t>(IP) ? 0u : 0x7f7f7f7fu;
+  }
   if (tid < 32) sw[kQEmask / 4 + tid] = 0u;
   if (tid < kQGMax) sw[kQTok / 4 + tid] = 0u;
   int myid = -1;
@@ -2673,9 +2651,9 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
             : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(as), "=&v"(xl), "=&v"(xh), "=&v"(xs)
             : "v"(sa + l * 16), "v"(sa + l * 4), "v"(px + 1024 * si), "v"(pxs + 32 * si)
             : "memory");
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        const v8i bop = fp8_operand(xlive ? xl : z, xlive ? xh : z);
-        const int sb = xlive ? static_cast<int>((xs >> (8 * grp)) & 0xffu) : 127;
+        // columns past the group's tokens read token 0's row: their sums are never used
+        const v8i bop = fp8_operand(xl, xh);
+        const int sb = static_cast<int>((xs >> (8 * grp)) & 0xffu);
         acc[0] = mfma_fp4_fp8(fp4_operand(a0), bop, acc[0], static_cast<int>(as & 0xffu), sb);
         acc[1] = mfma_fp4_fp8(fp4_operand(a1), bop, acc[1], static_cast<int>((as >> 8) & 0xffu), sb);
         acc[2] = mfma_fp4_fp8(fp4_operand(a2), bop, acc[2], static_cast<int>((as >> 16) & 0xffu), sb);
@@ -2739,18 +2717,13 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
       HidOps<NS2> hop;
       hid_read<NS2>(hbl, hbs, hop);
       const bool live = orow >= 0;
-      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
       v4f o = v4f{0.f, 0.f, 0.f, 0.f};
+      // K-blocks past I hold zero codes (weights and hidden); columns past the group's
+      // tokens read column 0 and are not stored
 #pragma unroll
-      for (int s = 0; s < NS2; ++s) {
-        // K-blocks at or beyond I (I not a multiple of 128) are zero: the weights are
-        // zero-padded there and the hidden holds no codes
-        const bool lo_ok = live && 4 * s + (grp >> 1) < HB, hi_ok = live && 4 * s + 2 + (grp >> 1) < HB;
-        const bool sc_ok = live && 4 * s + grp < HB;
-        o = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(lo_ok ? hop.bl[s] : z, hi_ok ? hop.bh[s] : z), o,
-                         static_cast<int>((was >> (8 * s)) & 0xffu),
-                         sc_ok ? static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu) : 127);
-      }
+      for (int s = 0; s < NS2; ++s)
+        o = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(hop.bl[s], hop.bh[s]), o,
+                         static_cast<int>((was >> (8 * s)) & 0xffu), static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu));
       mfma_settle(o);
       if (live) {
         const uint2 v = make_uint2(to_bf16_bits(o[0]) | (to_bf16_bits(o[1]) << 16),
@@ -2777,30 +2750,26 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
 #pragma unroll 1
   for (int k = 0; k < q.n1; ++k) {
     const int i = q.c + k * q.nwg, g = i / HB, j = i - g * HB;
-#pragma unroll 1
-    for (int ww = 0; ww < nw1; ++ww) lds_wait<false>(lb + kQProg + 4 * ww, k + 1, a.err);
     v4f tot[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) tot[rt] = v4f{0.f, 0.f, 0.f, 0.f};
     const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
     const bool live = col < __popc(tok);  // the block's token columns
-    if (live) {
-      // the partial tiles of four waves per batch of reads (one wait), added in wave order
-      const uint32_t rd = lb + a.o_red + static_cast<uint32_t>((grp * 8 + col) * 16);
+    const uint32_t rd = lb + a.o_red + static_cast<uint32_t>((grp * 8 + col) * 16);
+    // each wave's partial tiles are added (in wave order) as soon as that wave posts them
 #pragma unroll 1
-      for (int w0 = 0; w0 < nw1; w0 += 4) {
-        uint4 p[4][4];
-        lds_ld16x16(rd + w0 * kQRedWave, p);
+    for (int ww = 0; ww < nw1; ++ww) {
+      lds_wait<false>(lb + kQProg + 4 * ww, k + 1, a.err);
+      if (live) {
+        uint4 p0, p1, p2, p3;
+        lds_ld16x4<0, 512>(rd + ww * kQRedWave, p0, p1, p2, p3);
+        const uint4 p[4] = {p0, p1, p2, p3};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (w0 + u >= nw1) break;
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            tot[rt][0] += __uint_as_float(p[u][rt].x);
-            tot[rt][1] += __uint_as_float(p[u][rt].y);
-            tot[rt][2] += __uint_as_float(p[u][rt].z);
-            tot[rt][3] += __uint_as_float(p[u][rt].w);
-          }
+        for (int rt = 0; rt < 4; ++rt) {
+          tot[rt][0] += __uint_as_float(p[rt].x);
+          tot[rt][1] += __uint_as_float(p[rt].y);
+          tot[rt][2] += __uint_as_float(p[rt].z);
+          tot[rt][3] += __uint_as_float(p[rt].w);
         }
       }
     }
@@ -2814,7 +2783,9 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float gv = tot[half][r], uv = tot[2 + half][r];
-        h[half][r] = gv / (1.0f + expf(-gv)) * uv;
+        // SwiGLU with the hardware exponential and reciprocal (a few ulp in FP32; the
+        // hidden is then rounded to 3 mantissa bits)
+        h[half][r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
         amax = fmaxf(amax, fabsf(h[half][r]));
       }
     amax = fmaxf(amax, __shfl_xor(amax, 16));
