@@ -370,6 +370,19 @@ def test_decode_form_eight_tokens_one_expert(lib, grid, exchange):
     _check_all(d, got, hc, hs, _oracle(d), what=f"decode/one_expert/{grid}/x{exchange}")
 
 
+def test_decode_form_many_experts_falls_back(lib):
+    """More distinct experts than the whole-K form holds (128): the default exchange runs
+    the split-block kernel instead, with the same results."""
+    log("decode form beyond the whole-K limits")
+    d = workloads.generate(workloads.custom("many", B=8, E=400, K=40, D=512, I=64, seed=15))
+    assert len(np.unique(d["ids"])) > 128
+    layer = _layer(lib, d)
+    got, hc, hs, plan, status = _decode_run(lib, layer, d)
+    assert status == 0
+    _check_plan(d, plan)
+    _check_all(d, got, hc, hs, _oracle(d), what="decode/many_experts")
+
+
 def test_decode_form_flags_bad_ids(lib):
     """An id out of range is skipped and an id repeated within a token loses one of its
     routes; both are flagged in the status word, and every other route is exact."""
