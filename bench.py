@@ -36,9 +36,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "experts_kernel_traffic.json")
 
 
 def kernel_hash() -> str:
+    """sha256[:16] of the kernel source's code: line comments and blank lines are left
+    out, so that a change of comments alone keeps the recorded traffic valid."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in f)
+        code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload: str):

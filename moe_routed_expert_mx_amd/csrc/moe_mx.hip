@@ -18,8 +18,10 @@
 //   * the FC1 -> FC2 hidden exchange and the split-block FC1 partial sums cross XCDs
 //     through device-coherent (sc1) stores and loads, call-tagged flags and
 //     agent-scope counters;
-//   * for B <= 8 the same kernel also routes the batch and quantizes x (the decode
-//     form), so the step is one launch.
+//   * for B <= 8 the step is one launch that also routes the batch and quantizes x (the
+//     decode form): by default decode_whole_kernel, where each hidden block's FC1 runs
+//     over the whole of K inside one workgroup and only the finished MXFP8 hidden
+//     crosses workgroups, as call-tagged words; or the experts kernel's decode form.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
