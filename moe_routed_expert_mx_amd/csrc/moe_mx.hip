@@ -2389,6 +2389,13 @@ struct QArgs {
   uint32_t xstr, xsstr, hid_bytes;            // x code row stride, x scale row stride, one hidden buffer
 };
 
+// Two binary32 values to two BF16 (low half = a), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+}
+
 __device__ __forceinline__ void lds_add4(uint32_t addr, uint32_t v) {
   asm volatile("ds_add_u32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
 }
@@ -2524,11 +2531,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
       }
     }
   }
-  if (w == kQFin && l == 0) {
-    const uint32_t cn = ld_dev_u32(a.calls + c) + 1u;
-    st_dev_u32(a.calls + c, cn);
-    sw[kQCall / 4] = cn;
-  }
+  if (w == kQFin && l == 0) sw[kQCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
   __syncthreads();
 
   // ---- routing (experts page, the capacity <= 8 path: one unit per distinct expert,
@@ -2728,8 +2731,8 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
                          static_cast<int>((was >> (8 * s)) & 0xffu), static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu));
       mfma_settle(o);
       if (live) {
-        const uint2 v = make_uint2(to_bf16_bits(o[0]) | (to_bf16_bits(o[1]) << 16),
-                                   to_bf16_bits(o[2]) | (to_bf16_bits(o[3]) << 16));
+        // FP32 -> BF16 round to nearest even with gfx950's packed conversion
+        const uint2 v = make_uint2(bf16_pair(o[0], o[1]), bf16_pair(o[2], o[3]));
         *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(orow) + 16 * rt2 + 4 * grp) = v;
       }
       q_issue<NS2, R>(a, q, lb, w, n1el, n_el, is, none);
@@ -2818,6 +2821,9 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     }
   }
 
+    // the workgroup's call counter, for the next call (which starts after this kernel
+    // has ended, so nothing waits on the store)
+    if (l == 0) st_dev_u32(a.calls + c, call);
     return;
   }
   // ================================================================= loader wave
