@@ -2367,7 +2367,6 @@ constexpr uint32_t kQExp = 384;     // [kQGMax] expert id of group g (ascending)
 constexpr uint32_t kQTok = 896;     // [kQGMax] token bitmask of group g
 constexpr uint32_t kQRow = 1408;    // [kQGMax][8] u16: pair t*K+s of group g's column c
 constexpr uint32_t kQTables = 3456;
-constexpr uint32_t kQRedWave = 2048;  // one wave's partial tiles: 4 tiles x 8 columns x 16 rows x FP32
 
 struct QArgs {
   const uint8_t* w13p;
@@ -2387,7 +2386,23 @@ struct QArgs {
   int B, K, E, D, I, HB, NS1, IP, floor_rule, hq_words;
   uint32_t o_red, o_hid, o_xq, o_xs, o_ring;  // LDS offsets
   uint32_t xstr, xsstr, hid_bytes;            // x code row stride, x scale row stride, one hidden buffer
+  int cb;                 // token columns a group can have: min(B, 8); sizes the LDS areas below
+  uint32_t red_wave;      // one wave's partial tiles: 4 tiles x cb columns x 16 rows x FP32
 };
+
+// Four 16-byte LDS reads at four addresses, one wait.
+__device__ __forceinline__ void lds_ld16x4v(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint4& v0, uint4& v1,
+                                            uint4& v2, uint4& v3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
 
 // Two binary32 values to two BF16 (low half = a), round to nearest even
 // (v_cvt_pk_bf16_f32).
@@ -2512,7 +2527,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   // columns past a group's count hold finite values (their outputs are never stored)
   for (int v = tid; v < static_cast<int>(a.hid_bytes / 2); v += kQWG) {
     const uint32_t off = 4u * static_cast<uint32_t>(v), in_buf = off % a.hid_bytes;
-    sw[(a.o_hid + off) / 4] = in_buf < 8u * static_cast<uint32_t>(IP) ? 0u : 0x7f7f7f7fu;
+    sw[(a.o_hid + off) / 4] = in_buf < static_cast<uint32_t>(a.cb * IP) ? 0u : 0x7f7f7f7fu;
   }
   if (tid < 32) sw[kQEmask / 4 + tid] = 0u;
   if (tid < kQGMax) sw[kQTok / 4 + tid] = 0u;
@@ -2665,15 +2680,15 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
         acc[3] = mfma_fp4_fp8(fp4_operand(a3), bop, acc[3], static_cast<int>(as >> 24), sb);
         q_issue<NS2, R>(a, q, lb, w, n1el, n_el, is, none);  // into the slot just consumed
       }
-      // the wave's part of the block is done: hand its partial tiles (the 8 columns a
-      // batch of <= 8 tokens can use) to the control wave once it has taken the last ones
+      // the wave's part of the block is done: hand its partial tiles (the block's token
+      // columns) to the finisher once it has taken the last ones
       mfma_settle(acc[0], acc[1], acc[2], acc[3]);
       lds_wait<false>(lb + kQCons, item, a.err);
-      if (xlive) {  // the live token columns (col < ng <= 8)
-        const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(w * kQRedWave + (grp * 8 + col) * 16);
+      if (xlive) {  // the live token columns (col < ng <= cb)
+        const uint32_t rd = lb + a.o_red + w * a.red_wave + static_cast<uint32_t>((grp * a.cb + col) * 16);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
-          lds_st16_async(rd + rt * 512, make_uint4(__float_as_uint(acc[rt][0]), __float_as_uint(acc[rt][1]),
+          lds_st16_async(rd + rt * 64 * a.cb, make_uint4(__float_as_uint(acc[rt][0]), __float_as_uint(acc[rt][1]),
                                                    __float_as_uint(acc[rt][2]), __float_as_uint(acc[rt][3])));
       }
       lds_settle_all();
@@ -2703,7 +2718,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
         const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(cur_seq & 1) * a.hid_bytes;
         const int hcol = orow >= 0 ? col : 0;  // other lanes read column 0 and use zeros
         hbl = hb + hcol * IP + 16 * grp;
-        hbs = hb + 8 * IP + hcol * kQHB;
+        hbs = hb + a.cb * IP + hcol * kQHB;
         lds_wait<false>(lb + kQReady, cur_seq + 1, a.err);
       }
       uint4 wa0, wa1, wa2, wa3;
@@ -2760,14 +2775,15 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     for (int rt = 0; rt < 4; ++rt) tot[rt] = v4f{0.f, 0.f, 0.f, 0.f};
     const int tok = static_cast<int>(lds_ld4(lb + kQTok + 4 * g));
     const bool live = col < __popc(tok);  // the block's token columns
-    const uint32_t rd = lb + a.o_red + static_cast<uint32_t>((grp * 8 + col) * 16);
+    const uint32_t rd = lb + a.o_red + static_cast<uint32_t>((grp * a.cb + col) * 16);
     // each wave's partial tiles are added (in wave order) as soon as that wave posts them
 #pragma unroll 1
     for (int ww = 0; ww < nw1; ++ww) {
       lds_wait<false>(lb + kQProg + 4 * ww, k + 1, a.err);
       if (live) {
         uint4 p0, p1, p2, p3;
-        lds_ld16x4<0, 512>(rd + ww * kQRedWave, p0, p1, p2, p3);
+        const uint32_t rw = rd + ww * a.red_wave, ts = 64u * a.cb;
+        lds_ld16x4v(rw, rw + ts, rw + 2 * ts, rw + 3 * ts, p0, p1, p2, p3);
         const uint4 p[4] = {p0, p1, p2, p3};
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
@@ -2871,7 +2887,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
           const int cc = idx / per_col, r = idx - cc * per_col;
           const uint32_t d = static_cast<uint32_t>(v[u]);
           if (r < a.I / 4) lds_st4_nw(hb + cc * IP + 4 * r, d);
-          else lds_st1(hb + 8 * IP + cc * kQHB + (r - a.I / 4), d);
+          else lds_st1(hb + a.cb * IP + cc * kQHB + (r - a.I / 4), d);
         }
       }
     }
@@ -3094,15 +3110,18 @@ QFn pick_q(int ns2, int R) {
 }
 
 struct QLds {
-  uint32_t o_red, o_hid, o_xq, o_xs, o_ring, xstr, xsstr, hid_bytes;
+  uint32_t o_red, o_hid, o_xq, o_xs, o_ring, xstr, xsstr, hid_bytes, red_wave;
+  int cb;
   size_t bytes(int R) const { return o_ring + static_cast<size_t>(kQStream) * R * kQSlot; }
 };
 QLds q_lds(int B, int D, int IP) {
   QLds m;
   auto a16 = [](uint32_t v) { return (v + 15u) & ~15u; };
+  m.cb = B < 8 ? B : 8;  // token columns of a group
+  m.red_wave = 256u * static_cast<uint32_t>(m.cb);
   m.o_red = a16(kQTables);
-  m.hid_bytes = 8u * IP + 8u * kQHB;
-  m.o_hid = m.o_red + kQStream * kQRedWave;
+  m.hid_bytes = static_cast<uint32_t>(m.cb) * (static_cast<uint32_t>(IP) + kQHB);
+  m.o_hid = m.o_red + kQStream * m.red_wave;
   m.xstr = static_cast<uint32_t>(D) + 16u;
   m.xsstr = static_cast<uint32_t>(D) / 32u;
   m.o_xq = a16(m.o_hid + 2u * m.hid_bytes);
@@ -3132,7 +3151,9 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   const WsLayout L = ws_layout(E, D, I, topk, B_cap);
   const QLds m = q_lds(B, D, IP);
   const size_t limit = static_cast<size_t>(device_lds_limit());
-  int R = 4;
+  // three slots per wave by default (measured faster than four at B = 1, where a deeper
+  // ring only brings the FC2 prefetch forward into FC1's critical stream)
+  int R = 3;
   if (o.ring) R = o.ring < 2 ? 2 : (o.ring > 4 ? 4 : o.ring);
   while (R > 2 && m.bytes(R) > limit) --R;
   if (m.bytes(R) > limit) return MOE_EINVAL;
@@ -3184,6 +3205,8 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   a.xstr = m.xstr;
   a.xsstr = m.xsstr;
   a.hid_bytes = m.hid_bytes;
+  a.cb = m.cb;
+  a.red_wave = m.red_wave;
   (void)out_bytes;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kQWG), lds, as_stream(stream), a);
   return launch_status();
