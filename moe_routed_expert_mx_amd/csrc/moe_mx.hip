@@ -3151,9 +3151,11 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   const WsLayout L = ws_layout(E, D, I, topk, B_cap);
   const QLds m = q_lds(B, D, IP);
   const size_t limit = static_cast<size_t>(device_lds_limit());
-  // three slots per wave by default (measured faster than four at B = 1, where a deeper
-  // ring only brings the FC2 prefetch forward into FC1's critical stream)
-  int R = 3;
+  // two slots per wave by default: measured fastest at the decode sizes (B = 1: 13.9 us
+  // with two, 14.5 with three, 15.0 with four; B = 8: 35.7, 37.4, -).  More requests in
+  // flight only lengthen each one's latency, and a deeper ring brings FC2 prefetch
+  // forward into FC1's critical stream.
+  int R = 2;
   if (o.ring) R = o.ring < 2 ? 2 : (o.ring > 4 ? 4 : o.ring);
   while (R > 2 && m.bytes(R) > limit) --R;
   if (m.bytes(R) > limit) return MOE_EINVAL;
