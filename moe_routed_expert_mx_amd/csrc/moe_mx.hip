@@ -2837,9 +2837,11 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     }
   }
 
-    // the workgroup's call counter, for the next call (which starts after this kernel
-    // has ended, so nothing waits on the store)
-    if (l == 0) st_dev_u32(a.calls + c, call);
+    // the call counters for the next call (which starts after this kernel has ended, so
+    // nothing waits on the stores): every counter c, c + grid, c + 2 grid, ... below
+    // kMaxGrid, so all of them stay equal whatever grid the next call uses
+#pragma unroll 1
+    for (int m = c + l * nwg; m < kMaxGrid; m += 64 * nwg) st_dev_u32(a.calls + m, call);
     return;
   }
   // ================================================================= loader wave

@@ -383,6 +383,19 @@ def test_decode_form_many_experts_falls_back(lib):
     _check_all(d, got, hc, hs, _oracle(d), what="decode/many_experts")
 
 
+def test_decode_form_grid_changes_between_calls(lib):
+    """Calls with different grids on one workspace: the call numbers that tag the
+    published hidden stay in step, so every call's rows are the same."""
+    log("decode form, grid changes between calls")
+    d = workloads.generate(workloads.custom("grids", B=4, E=24, K=4, D=1024, I=128, routing="zipf", seed=16))
+    layer = _layer(lib, d)
+    ref = _oracle(d)
+    for grid in (40, 57, 0, 3, 57):
+        got, hc, hs, _, status = _decode_run(lib, layer, d, grid=grid)
+        assert status == 0, (grid, status)  # bit 2: a wait gave up (tags out of step)
+        _check_all(d, got, hc, hs, ref, what=f"decode/grid{grid}")
+
+
 def test_decode_form_flags_bad_ids(lib):
     """An id out of range is skipped and an id repeated within a token loses one of its
     routes; both are flagged in the status word, and every other route is exact."""
