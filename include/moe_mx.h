@@ -128,6 +128,14 @@ int moe_plan(const void* x_dev, int32_t B, int32_t D, void* plan_dev, size_t pla
 int moe_group(const int32_t* ids_dev, int32_t B, int32_t topk, int32_t E, void* units_dev,
               size_t units_bytes, void* stream);
 
+/* moe_plan and moe_group of one batch in a single launch (the same outputs, bit for bit):
+ * x_dev BF16 [B, D] -> plan_dev (moe_plan layout), ids_dev i32 [B, topk] -> units_dev
+ * (moe_group layout).  One workgroup builds the unit table while the others quantize x,
+ * which saves a launch per step of the grouped form.  Arguments and errors as the two
+ * calls. */
+int moe_plan_group(const void* x_dev, const int32_t* ids_dev, int32_t B, int32_t D, int32_t topk, int32_t E,
+                   void* plan_dev, size_t plan_bytes, void* units_dev, size_t units_bytes, void* stream);
+
 /* Copy the unit table that moe_group wrote into caller device buffers (for
  * inspection): header_dev i32[4] = {n_units, n_groups, n_column_tiles, flags (bit 0: an
  * id was out of range, bit 1: an id repeated within a token, bit 2: an experts call gave

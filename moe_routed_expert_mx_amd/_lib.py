@@ -52,6 +52,8 @@ def _load():
         "moe_workspace_init": (c.c_int, [P, c.c_size_t, P]),
         "moe_plan": (c.c_int, [P, c.c_int32, c.c_int32, P, c.c_size_t, P]),
         "moe_group": (c.c_int, [P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
+        "moe_plan_group": (c.c_int, [P, P, c.c_int32, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P, c.c_size_t,
+                                     P]),
         "moe_units_export": (c.c_int, [P, c.c_size_t, c.c_int32, c.c_int32, c.c_int32, P, P, P,
                                        c.c_int32, P]),
         "moe_experts_run": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_size_t,
@@ -68,7 +70,7 @@ def _load():
 
 lib = _load()
 EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_units_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
-            "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_units_export",
+            "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_plan_group", "moe_units_export",
             "moe_experts_run", "moe_decode_run", "moe_combine")
 
 
@@ -132,6 +134,14 @@ def moe_plan(x, plan, stream=None):
 def moe_group(ids, E: int, units, stream=None):
     B, K = ids.shape
     _check("moe_group", lib.moe_group(_ptr(ids), B, K, E, _ptr(units), _nbytes(units), _stream(stream)))
+
+
+def moe_plan_group(x, ids, E: int, plan, units, stream=None):
+    """moe_plan and moe_group in one launch."""
+    B, D = x.shape
+    K = ids.shape[1]
+    _check("moe_plan_group", lib.moe_plan_group(_ptr(x), _ptr(ids), B, D, K, E, _ptr(plan), _nbytes(plan),
+                                                _ptr(units), _nbytes(units), _stream(stream)))
 
 
 def moe_units_export(units, B, topk, E, header, unit_expert, unit_rows, stream=None):

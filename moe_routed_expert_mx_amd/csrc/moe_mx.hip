@@ -136,11 +136,8 @@ __device__ __forceinline__ v8i fp8_operand(uint4 lo, uint4 hi) {
 // ------------------------------------------------------------------ plan
 // One thread per 32-element block of a token row (experts page, plan_chunk: the same
 // quantization as mx_block).  x: BF16 [B, D]; codes [B, D]; scales [B, D/32].
-__global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ x, int64_t nblocks,
-                                                   uint8_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= nblocks) return;
+__device__ __forceinline__ void plan_block(const uint8_t* __restrict__ x, int64_t idx, uint8_t* __restrict__ codes,
+                                           uint8_t* __restrict__ scales) {
   const uint8_t* src = x + idx * 64;
   uint32_t w[16];
 #pragma unroll
@@ -167,6 +164,13 @@ __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ x
   dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
   dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
   scales[idx] = static_cast<uint8_t>(e + 127);
+}
+
+__global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ x, int64_t nblocks,
+                                                   uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx < nblocks) plan_block(x, idx, codes, scales);
 }
 
 // ------------------------------------------------------------------ combine
@@ -276,8 +280,7 @@ __device__ I3 block_scan3(I3 v, I3* wave_tot) {
 // ExpertsGroupKernel): per-expert token bitmasks, ceil(n/8) units per expert numbered
 // in expert order, unit rows holding pair indices in token order (-1 padded), and the
 // list of distinct experts with their first unit and 16-column tile offset.
-__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids, int B,
-                                                              int K, int E, int W, Table tbl) {
+__device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int B, int K, int E, int W, Table tbl) {
   extern __shared__ uint32_t lds[];
   uint32_t* masks = lds;                                        // [E, W]
   int* routes = reinterpret_cast<int*>(masks + static_cast<size_t>(E) * W);  // [E] route counts
@@ -331,6 +334,26 @@ __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __r
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(m[w]);
     tbl.unit_rows[(unit0[e] + (rank >> 3)) * 8 + (rank & 7)] = r;
   }
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids, int B,
+                                                              int K, int E, int W, Table tbl) {
+  group_body(ids, B, K, E, W, tbl);
+}
+
+// The plan and the unit table of a batch in one launch (moe_plan_group): workgroup 0
+// builds the unit table, the others quantize x, kGroupThreads 32-element blocks each.
+__global__ __launch_bounds__(kGroupThreads) void plan_group_kernel(const uint8_t* __restrict__ x, int64_t nblocks,
+                                                                   uint8_t* __restrict__ codes,
+                                                                   uint8_t* __restrict__ scales,
+                                                                   const int32_t* __restrict__ ids, int B, int K,
+                                                                   int E, int W, Table tbl) {
+  if (blockIdx.x == 0) {
+    group_body(ids, B, K, E, W, tbl);
+    return;
+  }
+  const int64_t idx = static_cast<int64_t>(blockIdx.x - 1) * kGroupThreads + threadIdx.x;
+  if (idx < nblocks) plan_block(x, idx, codes, scales);
 }
 
 // ------------------------------------------------------------------ packing
@@ -3315,6 +3338,27 @@ int moe_group(const int32_t* ids, int32_t B, int32_t topk, int32_t E, void* unit
   if (units_bytes < L.end) return MOE_ENOSPACE;
   const Table t = table_at(static_cast<uint8_t*>(units), L);
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds, as_stream(stream), ids, B, topk, E, W, t);
+  return launch_status();
+}
+
+int moe_plan_group(const void* x, const int32_t* ids, int32_t B, int32_t D, int32_t topk, int32_t E, void* plan,
+                   size_t plan_bytes, void* units, size_t units_bytes, void* stream) {
+  if (!x || !plan || !ids || !units || B < 1 || D < 32 || D % 32 || topk < 1 || topk > 64 || E < 1 ||
+      E > kMaxGroups || static_cast<int64_t>(B) * topk > 65536)
+    return MOE_EINVAL;
+  if (plan_bytes < moe_plan_bytes(B, D)) return MOE_ENOSPACE;
+  const int W = (B + 31) / 32;
+  const size_t lds = (static_cast<size_t>(E) * W + 2 * static_cast<size_t>(E)) * 4;
+  if (lds > 60 * 1024) return MOE_EINVAL;
+  const UnitsLayout L = units_layout(B, topk, E);
+  if (units_bytes < L.end) return MOE_ENOSPACE;
+  const Table t = table_at(static_cast<uint8_t*>(units), L);
+  const int64_t nblocks = static_cast<int64_t>(B) * (D / 32);
+  uint8_t* codes = static_cast<uint8_t*>(plan);
+  const unsigned grid = 1u + static_cast<unsigned>((nblocks + kGroupThreads - 1) / kGroupThreads);
+  hipLaunchKernelGGL(plan_group_kernel, dim3(grid), dim3(kGroupThreads), lds, as_stream(stream),
+                     static_cast<const uint8_t*>(x), nblocks, codes, codes + static_cast<int64_t>(B) * D, ids, B,
+                     topk, E, W, t);
   return launch_status();
 }
 

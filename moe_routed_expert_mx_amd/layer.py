@@ -64,8 +64,7 @@ class MoeLayer:
         if path == "decode" or (path == "auto" and self.AUTO_DECODE and B <= self.DECODE_MAX):
             _lib.moe_decode_run(self.structs[replica], x, ids, self.ws, out, stream=stream, **opts)
             return out
-        _lib.moe_plan(x, self.plan, stream=stream)
-        _lib.moe_group(ids, self.E, self.units, stream=stream)
+        _lib.moe_plan_group(x, ids, self.E, self.plan, self.units, stream=stream)
         _lib.moe_experts_run(self.structs[replica], self.plan, self.units, B, self.topk, self.ws, out, stream=stream,
                              **opts)
         return out

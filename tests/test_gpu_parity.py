@@ -167,6 +167,37 @@ def test_units_bitexact(lib, name):
     _units_case(lib, d["ids"], d["workload"].E)
 
 
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_plan_group_one_launch(lib, name):
+    """moe_plan_group writes the same plan and unit table as moe_plan + moe_group."""
+    m, _ = lib
+    log(f"plan + units in one launch {name}")
+    d = workloads.generate(name, with_weights=False)
+    E = d["workload"].E
+    x = torch.from_numpy(d["x"]).to(DEV)
+    ids = torch.from_numpy(d["ids"]).to(DEV)
+    B, D = x.shape
+    K = ids.shape[1]
+    plan_a = torch.full((m.moe_plan_bytes(B, D),), 0xAB, dtype=torch.uint8, device=DEV)
+    plan_b = torch.full_like(plan_a, 0xCD)
+    units_a = torch.zeros(m.moe_units_bytes(B, K, E), dtype=torch.uint8, device=DEV)
+    units_b = torch.full_like(units_a, 0x5A)
+    m.moe_plan(x, plan_a)
+    m.moe_group(ids, E, units_a)
+    m.moe_plan_group(x, ids, E, plan_b, units_b)
+    assert torch.equal(plan_a, plan_b)
+    outs = []
+    for u in (units_a, units_b):
+        hdr = torch.empty(4, dtype=torch.int32, device=DEV)
+        ue = torch.empty(B * K, dtype=torch.int32, device=DEV)
+        ur = torch.empty(B * K, 8, dtype=torch.int32, device=DEV)
+        m.moe_units_export(u, B, K, E, hdr, ue, ur)
+        n = int(hdr[0].item())
+        outs.append((hdr.cpu().numpy(), ue[:n].cpu().numpy(), ur[:n].cpu().numpy()))
+    for a_, b_ in zip(*outs):
+        assert np.array_equal(a_, b_)
+
+
 def test_units_edge_cases(lib):
     log("units edge cases")
     _units_case(lib, np.zeros((1, 1), np.int32), 1)                     # one route
