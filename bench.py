@@ -4,8 +4,8 @@
 A step is one pass of the whole hot path over one batch of synthetic input: the MXFP8
 plan of x, the unit table and the persistent experts kernel (FC1 -> SwiGLU -> hidden
 requant -> FC2 -> BF16 rows).  For B <= 8 that is one moe_decode_run launch (the
-kernel quantizes and routes the batch itself); for larger batches three calls,
-moe_plan + moe_group + moe_experts_run.  Inputs are
+kernel quantizes and routes the batch itself); for larger batches two calls,
+moe_plan_group (the plan of x and the unit table) + moe_experts_run.  Inputs are
 resident in HBM before the timed region starts.  Each step reads a different weight
 replica (>= 1 GiB rotated) so the 256 MB Infinity Cache cannot serve repeated weights.
 Steps are captured in a HIP graph (torch.cuda.CUDAGraph) and replayed; the timed
@@ -247,7 +247,7 @@ def main():
     ap.add_argument("--exchange", type=int, default=None,
                     help="decode form: FC1 -> FC2 exchange variant (moe_run_opts_t.exchange); default: the library's")
     ap.add_argument("--path", default="auto", choices=("auto", "decode", "grouped"),
-                    help="step form for B <= 8: one decode launch, the three-call grouped form, or auto "
+                    help="step form for B <= 8: one decode launch, the two-call grouped form, or auto "
                          "(larger batches always use the grouped form)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")

@@ -52,7 +52,7 @@ class MoeLayer:
     def forward(self, x: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None, *, replica: int = 0,
                 stream=None, path: str = "auto", **opts) -> torch.Tensor:
         """x: BF16 [B, D] (or its uint16 bits), ids: int32 [B, topk], both on the device.
-        path: "decode" (one launch, B <= 8), "grouped" (plan + units + experts) or "auto"
+        path: "decode" (one launch, B <= 8), "grouped" (plan and units in one launch, then experts) or "auto"
         (the decode form for B <= 8 when AUTO_DECODE is set, else grouped)."""
         B = x.shape[0]
         if B > self.B_max or ids.shape != (B, self.topk):
