@@ -10,6 +10,11 @@ from __future__ import annotations
 import ctypes
 import os
 
+# PyTorch first: the library runs on torch's streams and memory, so it must bind to the
+# HIP runtime torch has loaded.  Loaded the other way round, the process holds two HIP
+# runtimes and launches on torch's streams fail.
+import torch  # noqa: F401
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mx.so")
 
