@@ -2450,7 +2450,7 @@ struct QWork {
   int TPE, nwg, c;
 };
 
-__device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int D, int nwg, int c, int w) {
+__device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int D, int nwg, int c, int w, int item) {
   QWork q;
   const int N1 = G * HB;
   q.nwg = nwg;
@@ -2460,12 +2460,39 @@ __device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int D, int nwg, 
   const int r1 = N1 % nwg;  // workgroups c < r1 hold one FC1 item more
   q.n1 = N1 / nwg + (c < r1 ? 1 : 0);
   q.m1 = w < NS1 ? (NS1 - w + kQStream - 1) / kQStream : 0;
-  // FC2 tiles: equal contiguous runs.  A workgroup with an FC1 item more streams its
-  // FC2 weights while the hidden blocks are exchanged, which takes about as long.
-  const int cap = (N2 + nwg - 1) / nwg;
-  q.first2 = c * cap;
-  const int n2 = N2 - q.first2;
-  q.n2 = n2 < 0 ? 0 : (n2 > cap ? cap : n2);
+  // FC2 tiles: contiguous runs in expert-major order.  When every workgroup has FC1
+  // items and some have one more, those come last with `item` tiles fewer (an FC1 item
+  // streams as long as that many FC2 tiles): they take the experts that finish last,
+  // their own last items among them.  Otherwise (no FC1 item for some workgroups, or
+  // the same count for all) the runs are equal: no FC2 tile can start before the last
+  // round's hidden is there.
+  int first, n2;
+  if (N1 >= nwg && r1 > 0) {
+    const int M0 = nwg - r1;  // workgroups with the fewer items: the first runs
+    int cn = (N2 + r1 * item + nwg - 1) / nwg, ce = cn - item;
+    if (ce <= 0) {
+      cn = (N2 + M0 - 1) / M0;
+      ce = 0;
+    }
+    // the workgroups with one item more take the last r1 * ce tiles, the others the
+    // rest (M0 * cn covers it)
+    const int e0 = N2 - r1 * ce > 0 ? N2 - r1 * ce : 0;
+    if (c >= r1) {
+      first = (c - r1) * cn < e0 ? (c - r1) * cn : e0;
+      n2 = e0 - first < cn ? e0 - first : cn;
+    } else {
+      const int a0 = N2 - (r1 - c) * ce, a1 = N2 - (r1 - c - 1) * ce;
+      first = a0 > 0 ? a0 : 0;
+      n2 = (a1 > 0 ? a1 : 0) - first;
+    }
+  } else {
+    const int cap = (N2 + nwg - 1) / nwg;
+    first = c * cap;
+    n2 = cap;
+  }
+  q.first2 = first < N2 ? first : N2;
+  n2 = N2 - q.first2 < n2 ? N2 - q.first2 : n2;
+  q.n2 = n2 < 0 ? 0 : n2;
   return q;
 }
 
@@ -2610,7 +2637,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   const int G = __builtin_amdgcn_readfirstlane(static_cast<int>(sw[kQGCount / 4]));
   __syncthreads();
 
-  const QWork q = q_work(G, HB, NS1, D, nwg, c, w < kQStream ? w : 0);
+  const QWork q = q_work(G, HB, NS1, D, nwg, c, w < kQStream ? w : 0, 34 * D / (NS2 * 1024 + 256));
   const __amdgpu_buffer_rsrc_t none =
       __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
   const int nw1 = NS1 < kQStream ? NS1 : kQStream;  // waves that take FC1 steps
