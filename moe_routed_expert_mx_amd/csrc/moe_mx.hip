@@ -2374,6 +2374,7 @@ constexpr int kQHB = 16;            // hidden scale slots per token column (HB <
 constexpr int kQStream = 8;                  // streaming waves per workgroup
 constexpr int kQFin = kQStream;             // the finisher wave: FC1 blocks' epilogues
 constexpr int kQLoad = kQStream + 1;         // the loader wave: FC2's hidden, polled and copied
+constexpr int kQPoll = 18;  // hidden pairs per loader lane, one-pass poll: 8 x (512 / 4 + 16) / 64
 constexpr int kQWG = 64 * (kQStream + 2);
 
 // LDS: sync words and the routing tables of the batch (byte offsets from the LDS base).
@@ -2558,7 +2559,7 @@ __device__ __forceinline__ void q_issue(const QArgs& a, const QWork& q, uint32_t
   ++is.k;
 }
 
-template <int NS2, int R>
+template <int NS2, int R, bool WIDE>
 __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   agpr_form();
@@ -2912,19 +2913,33 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     const uint64_t* src = a.hq + static_cast<int64_t>(g) * 8 * a.hq_words;
     const int per_col = a.I / 4 + HB;  // pairs a column holds: code words, then scales
     const int n = ng * per_col;
-#pragma unroll 1
-    for (int base = 0; base < n; base += 8 * 64) {
-      uint64_t v[8];
-#pragma unroll 1
+    if constexpr (WIDE) {
+      // lane l holds pairs l, l + 64, ...: all of them are polled in each round, so an
+      // expert of many tokens costs one round trip, not one per 512 pairs (a separate
+      // variant: the longer loop slows the small batches, whose experts fit one round); the pair's
+      // column and word advance by 64 = q64 columns + r64 words per step
+      const int nu = (n + 63) >> 6;  // steps that hold pairs (uniform)
+      const int q64 = 64 / per_col, r64 = 64 - q64 * per_col;
+      const int c0 = l / per_col, w0 = l - c0 * per_col;
+      uint64_t v[kQPoll];
+  #pragma unroll 1
       for (uint32_t spins = 0;; ++spins) {
-        bool ok = true;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int idx = base + u * 64 + l;
-          const int cc = idx / per_col, r = idx - cc * per_col;
-          v[u] = idx < n ? ld_dev_u64(src + static_cast<int64_t>(cc) * a.hq_words + r) : 0ull;
-          ok = ok && (idx >= n || static_cast<uint32_t>(v[u] >> 32) == call);
+        int cc = c0, r = w0;
+  #pragma unroll
+        for (int u = 0; u < kQPoll; ++u) {
+          v[u] = 0ull;
+          if (u < nu) {  // uniform: the steps past the expert's pairs are skipped
+            if (u * 64 + l < n) v[u] = ld_dev_u64(src + static_cast<int64_t>(cc) * a.hq_words + r);
+            r += r64;
+            cc += q64;
+            const bool wrap = r >= per_col;
+            r = wrap ? r - per_col : r;
+            cc = wrap ? cc + 1 : cc;
+          }
         }
+        bool ok = true;
+  #pragma unroll
+        for (int u = 0; u < kQPoll; ++u) ok = ok && (u * 64 + l >= n || static_cast<uint32_t>(v[u] >> 32) == call);
         if (__all(ok)) break;
         if (spins == kSpinLimit) {
           if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2932,14 +2947,54 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
         }
         __builtin_amdgcn_s_sleep(1);
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * 64 + l;
-        if (idx < n) {
-          const int cc = idx / per_col, r = idx - cc * per_col;
-          const uint32_t d = static_cast<uint32_t>(v[u]);
-          if (r < a.I / 4) lds_st4_nw(hb + cc * IP + 4 * r, d);
-          else lds_st1(hb + a.cb * IP + cc * kQHB + (r - a.I / 4), d);
+      {
+        int cc = c0, r = w0;
+  #pragma unroll
+        for (int u = 0; u < kQPoll; ++u) {
+          if (u < nu) {
+            if (u * 64 + l < n) {
+              const uint32_t d = static_cast<uint32_t>(v[u]);
+              if (r < a.I / 4) lds_st4_nw(hb + cc * IP + 4 * r, d);
+              else lds_st1(hb + a.cb * IP + cc * kQHB + (r - a.I / 4), d);
+            }
+            r += r64;
+            cc += q64;
+            const bool wrap = r >= per_col;
+            r = wrap ? r - per_col : r;
+            cc = wrap ? cc + 1 : cc;
+          }
+        }
+      }
+    } else {
+  #pragma unroll 1
+      for (int base = 0; base < n; base += 8 * 64) {
+        uint64_t v[8];
+  #pragma unroll 1
+        for (uint32_t spins = 0;; ++spins) {
+          bool ok = true;
+  #pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int idx = base + u * 64 + l;
+            const int cc = idx / per_col, r = idx - cc * per_col;
+            v[u] = idx < n ? ld_dev_u64(src + static_cast<int64_t>(cc) * a.hq_words + r) : 0ull;
+            ok = ok && (idx >= n || static_cast<uint32_t>(v[u] >> 32) == call);
+          }
+          if (__all(ok)) break;
+          if (spins == kSpinLimit) {
+            if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+  #pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = base + u * 64 + l;
+          if (idx < n) {
+            const int cc = idx / per_col, r = idx - cc * per_col;
+            const uint32_t d = static_cast<uint32_t>(v[u]);
+            if (r < a.I / 4) lds_st4_nw(hb + cc * IP + 4 * r, d);
+            else lds_st1(hb + a.cb * IP + cc * kQHB + (r - a.I / 4), d);
+          }
         }
       }
     }
@@ -3144,20 +3199,22 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
 
 // ------------------------------------------------- decode form, whole-K FC1 blocks (host)
 using QFn = void (*)(QArgs);
+// wide: an expert's hidden can exceed 512 pairs (more than four tokens at I = 384), so
+// the loader polls it in one pass (two slots per wave only)
 template <int NS2>
-QFn pick_q_r(int R) {
+QFn pick_q_r(int R, bool wide) {
   switch (R) {
-    case 2: return decode_whole_kernel<NS2, 2>;
-    case 3: return decode_whole_kernel<NS2, 3>;
-    default: return decode_whole_kernel<NS2, 4>;
+    case 2: return wide ? decode_whole_kernel<NS2, 2, true> : decode_whole_kernel<NS2, 2, false>;
+    case 3: return decode_whole_kernel<NS2, 3, false>;
+    default: return decode_whole_kernel<NS2, 4, false>;
   }
 }
-QFn pick_q(int ns2, int R) {
+QFn pick_q(int ns2, int R, bool wide) {
   switch (ns2) {
-    case 1: return pick_q_r<1>(R);
-    case 2: return pick_q_r<2>(R);
-    case 3: return pick_q_r<3>(R);
-    default: return pick_q_r<4>(R);
+    case 1: return pick_q_r<1>(R, wide);
+    case 2: return pick_q_r<2>(R, wide);
+    case 3: return pick_q_r<3>(R, wide);
+    default: return pick_q_r<4>(R, wide);
   }
 }
 
@@ -3212,7 +3269,7 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   while (R > 2 && m.bytes(R) > limit) --R;
   if (m.bytes(R) > limit) return MOE_EINVAL;
   const size_t lds = m.bytes(R);
-  const QFn fn = pick_q(ns2, R);
+  const QFn fn = pick_q(ns2, R, m.cb * (I / 4 + I / 32) > 8 * 64);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(lds)) != hipSuccess)
     return MOE_EHIP;
