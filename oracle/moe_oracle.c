@@ -20,7 +20,9 @@
  * Parity pins: every function here is pinned by a `-m "not gpu"` test (decode against
  * torch's own float8/float4 decoders, encode against a brute-force nearest search,
  * block exponents against closed forms, FC1/FC2 against dense FP64 matmuls of
- * independently decoded operands, routing invariants).  No function is unpinned.
+ * independently decoded operands, the gated activation against closed-form values
+ * g*u/(1+e^-g) of hand-set asymmetric gate/up pairs and against torch's SiLU,
+ * routing invariants).  No function is unpinned.
  */
 #include <math.h>
 #include <pthread.h>
@@ -235,6 +237,7 @@ typedef struct {
   uint16_t* out;
   float* out_f32;
   float* fc1;
+  float* hidden; /* optional: the FP32 hidden before its requantization */
   uint8_t *hcodes, *hscales;
   double *e2m1, *e4m3, *e8m0; /* decode tables (plain lookups of the decoders above) */
 } oracle_job;
@@ -296,6 +299,7 @@ static int64_t oracle_route(const oracle_job* j, int out_row, int route) {
     if (j->out_f32) j->out_f32[(size_t)out_row * D + d] = (float)acc;
   }
   if (j->fc1) memcpy(j->fc1 + (size_t)out_row * 2 * I, a, sizeof(float) * 2 * I);
+  if (j->hidden) memcpy(j->hidden + (size_t)out_row * I, h, sizeof(float) * I);
   if (j->hcodes) memcpy(j->hcodes + (size_t)out_row * I, hq, I);
   if (j->hscales) memcpy(j->hscales + (size_t)out_row * (I / 32), hs, I / 32);
   free(a);
@@ -321,7 +325,9 @@ static void* oracle_worker_main(void* arg) {
 
 /* Runs the routes listed in `routes` (NULL: all B*K routes, in pair order) and writes
  * output row i for the i-th listed route (`out_f32`, optional: the same rows before
- * their BF16 rounding, i.e. the exact FC2 sums rounded once to FP32).  Routes are independent of each other, so
+ * their BF16 rounding, i.e. the exact FC2 sums rounded once to FP32; `fc1`, `hidden`,
+ * `hcodes`, `hscales`, optional: the route's FC1 values [2I], FP32 hidden [I] and its
+ * MXFP8 codes [I] and scales [I/32]).  Routes are independent of each other, so
  * they are spread over `nthreads` threads.  `inexact` (optional) receives the number
  * of FP64 additions that rounded (0 certifies the FC1/FC2 sums as exact).
  * Returns 0, or -1 on invalid arguments / ids. */
@@ -329,8 +335,8 @@ ORACLE_API int oracle_experts(int E, int D, int I, const uint8_t* w13, const uin
                               const uint8_t* w2, const uint8_t* s2, const uint8_t* xcodes,
                               const uint8_t* xscales, const int32_t* ids, int B, int K,
                               const int32_t* routes, int n_routes, int hidden_floor,
-                              uint16_t* out, float* out_f32, float* fc1, uint8_t* hcodes,
-                              uint8_t* hscales, int nthreads, int64_t* inexact) {
+                              uint16_t* out, float* out_f32, float* fc1, float* hidden,
+                              uint8_t* hcodes, uint8_t* hscales, int nthreads, int64_t* inexact) {
   if (E <= 0 || D <= 0 || I <= 0 || D % 32 || I % 32 || B < 0 || K <= 0) return -1;
   for (int r = 0; r < B * K; ++r)
     if (ids[r] < 0 || ids[r] >= E) return -1;
@@ -342,7 +348,7 @@ ORACLE_API int oracle_experts(int E, int D, int I, const uint8_t* w13, const uin
   for (int c = 0; c < 256; ++c) e4m3[c] = oracle_e4m3_value((unsigned)c);
   for (int c = 0; c < 256; ++c) e8m0[c] = oracle_e8m0_value((unsigned)c);
   oracle_job job = {E, D, I, hidden_floor, w13, s13, w2, s2, xcodes, xscales, ids, B, K,
-                    routes, n_routes, out, out_f32, fc1, hcodes, hscales, e2m1, e4m3, e8m0};
+                    routes, n_routes, out, out_f32, fc1, hidden, hcodes, hscales, e2m1, e4m3, e8m0};
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   oracle_worker workers[256];

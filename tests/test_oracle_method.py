@@ -220,6 +220,86 @@ def test_all_ones_weights_sum_x(orc):
         assert np.all(res["fc1"][t] == np.float32(X[t].sum()))
 
 
+def _golden_swiglu():
+    rows = []
+    with open(os.path.join(GOLDEN, "swiglu.txt")) as f:
+        for ln in f:
+            if ln.strip() and not ln.startswith("#"):
+                g, u, h = ln.split()[:3]
+                rows.append((float(g), float(u), h))
+    return rows
+
+
+def _fp4_code_and_exponent(v):
+    """v = FP4(code) * 2^k with code's magnitude in the OCP table: the (code, k) pair
+    with the smallest |k| (found by search over the table, not by any oracle code)."""
+    if v == 0:
+        return 0, 0
+    for k in sorted(range(-12, 13), key=abs):
+        m = abs(v) / 2.0 ** k
+        hit = np.flatnonzero(FP4[:8] == m)
+        if hit.size:
+            return int(hit[0]) | (8 if v < 0 else 0), k
+    raise ValueError(v)
+
+
+def test_swiglu_closed_forms(orc):
+    """The gated activation on exact FC1 values (tests/golden/swiglu.txt): x = e_0
+    quantizes exactly to 1.0, so FC1 row r is the hand-set weight W13[0, r, 0] and
+    gate i / up i take the golden pair (g_i, u_i).  The oracle's FP32 hidden must equal
+    the closed form g*u/(1+e^-g) rounded to FP32 -- a swapped gate/up half or a flipped
+    sign inside the sigmoid changes almost every row."""
+    gold = _golden_swiglu()
+    I, D = 32, 64
+    assert len(gold) == I
+    w13 = np.zeros((1, 2 * I, D // 2), np.uint8)
+    s13 = np.full((1, 2 * I, D // 32), 127, np.uint8)
+    for i, (g, u, _) in enumerate(gold):
+        for r, v in ((i, g), (I + i, u)):
+            code, k = _fp4_code_and_exponent(v)
+            w13[0, r, 0] = code                       # low nibble = k index 0
+            s13[0, r, 0] = 127 + k
+    w2 = np.zeros((1, D, I // 2), np.uint8)
+    s2 = np.full((1, D, I // 32), 127, np.uint8)
+    x = np.zeros((1, D), np.float32)
+    x[0, 0] = 1.0
+    codes, scales = orc.plan(bf16_bits(x))
+    res = orc.experts(w13, s13, w2, s2, codes, scales, np.zeros((1, 1), np.int32), hidden_floor=False,
+                      want_fc1=True, want_hidden_f32=True)
+    # the FC1 values are exactly the pairs (the construction is right)
+    assert np.array_equal(res["fc1"][0, :I], np.array([g for g, _, _ in gold], np.float32))
+    assert np.array_equal(res["fc1"][0, I:], np.array([u for _, u, _ in gold], np.float32))
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    for i, (g, u, lit) in enumerate(gold):
+        # the literal is the closed form (re-derived here at 50 digits as a typo guard)
+        exact = Decimal(repr(g)) / (1 + (-Decimal(repr(g))).exp()) * Decimal(repr(u))
+        assert abs(Decimal(lit) - exact) <= abs(exact) * Decimal("1e-25"), (i, lit, exact)
+        assert res["hidden"][0, i] == np.float32(float(lit)), (i, g, u, res["hidden"][0, i], lit)
+    swapped = [np.float32(u / (1 + np.exp(-u)) * g) for g, u, _ in gold]
+    flipped = [np.float32(g / (1 + np.exp(g)) * u) for g, u, _ in gold]
+    assert np.sum(res["hidden"][0] != swapped) >= 20 and np.sum(res["hidden"][0] != flipped) >= 20
+
+
+def test_swiglu_matches_torch_silu(orc):
+    """On a random layer, the oracle's FP32 hidden is torch's SiLU (its own FP64
+    implementation) of the gate times the up value, rounded once to FP32."""
+    d = small(seed=21, B=4, E=5, K=3, I=96)
+    codes, scales = orc.plan(d["x"])
+    res = orc.experts(d["w13"], d["s13"], d["w2"], d["s2"], codes, scales, d["ids"], hidden_floor=False,
+                      want_fc1=True, want_hidden_f32=True)
+    I = d["workload"].I
+    g = torch.from_numpy(res["fc1"][:, :I].astype(np.float64))
+    u = torch.from_numpy(res["fc1"][:, I:].astype(np.float64))
+    ref = (torch.nn.functional.silu(g) * u).to(torch.float32).numpy()
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert np.all(np.abs(res["hidden"] - ref) <= ulp)      # at most one FP32 rounding apart
+    assert np.mean(res["hidden"] == ref) >= 0.999
+    # and the hidden codes are the MXFP8 of exactly that FP32 hidden
+    c2, s2 = orc.quantize_blocks(res["hidden"], floor_rule=False)
+    assert np.array_equal(c2, res["hcodes"]) and np.array_equal(s2, res["hscales"])
+
+
 def test_zero_gate_gives_zero_hidden_and_output(orc):
     d = small(seed=8, B=2, E=3, K=2, D=256, I=64)
     d["w13"][:, :64] = 0                              # gate rows -> g = 0 -> h = 0
