@@ -6,17 +6,20 @@ plan of x, the unit table and the persistent experts kernel (FC1 -> SwiGLU -> hi
 requant -> FC2 -> BF16 rows).  For B <= 8 that is one moe_decode_run launch (the
 kernel quantizes and routes the batch itself); for larger batches two calls,
 moe_plan_group (the plan of x and the unit table) + moe_experts_run.  Inputs are
-resident in HBM before the timed region starts.  Each step reads a different weight
-replica (>= 1 GiB rotated) so the 256 MB Infinity Cache cannot serve repeated weights.
-Steps are captured in a HIP graph (torch.cuda.CUDAGraph) and replayed; the timed
-region is bracketed by synchronizations and HIP events on the launch stream.
+resident in HBM before the timed region starts.  Step i reads replica i % R of the
+weights, with R * (weight bytes a step touches) >= 1 GiB, so the 256 MB Infinity Cache
+cannot serve a weight byte twice.  The steps are captured in one HIP graph
+(torch.cuda.CUDAGraph) and replayed; the timed region is bracketed by synchronizations
+and HIP events on the launch stream.
 
-Prints ONE JSON line (rank 0): µs per layer of the named workload, plus the roofline
-of the dominant kernel (experts: algorithmic bytes / its average duration measured
-with HIP events over graph replays of that kernel alone), the CPU oracle timed on
-the host cores on a bounded sample of the same workload, and the weighted top-k
-combine (moe_combine) of the step's rows timed alone (it follows the step; it is not
-part of it).
+By default all five workloads are timed.  Prints ONE JSON line: `value` is µs per layer
+of the headline workload (wide_b256, B = 256, the largest the metric names; --workload
+picks another), `roofline` is its dominant kernel (algorithmic bytes / the kernel's
+average duration, HIP events over graph replays of that kernel alone), `cpu_baseline`
+the oracle on the host cores (best of 3), and `per_workload` the same figures for
+every workload, with the oracle also on one thread for the three smallest, and the
+weighted top-k combine (moe_combine) of the step's rows timed alone (it follows the
+step; it is not part of it).
 """
 from __future__ import annotations
 
@@ -81,27 +84,29 @@ def _unique_weight_bytes(ids, w) -> int:
     return n * workloads.expert_weight_bytes(w.D, w.I)
 
 
-def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager: bool = False, path: str = "auto",
+ROTATE_BYTES = 1 << 30  # bytes a step sequence touches before it reads a replica again
+
+
+def measure(d: dict, steps: int, warmup: int, *, eager: bool = False, path: str = "auto",
             exchange: int | None = None, log=print) -> dict:
+    """Times `steps` steps of workload d on the GPU (inputs resident in HBM).  Step i reads
+    replica i % R of the expert weights, R = ceil(1 GiB / weight bytes a step touches),
+    so no weight byte is read again before 1 GiB of others: the 256 MB Infinity Cache
+    cannot serve it."""
     import numpy as np
     import torch
 
-    import workloads
     from moe_routed_expert_mx_amd.layer import MoeLayer
 
-    d = workloads.generate(name)
     w = d["workload"]
-    per_expert = workloads.expert_weight_bytes(w.D, w.I)
-    R = max(2, math.ceil((1 << 30) / (w.E * per_expert)))
+    uniq = _unique_weight_bytes(d["ids"], w)
+    R = max(2, math.ceil(ROTATE_BYTES / uniq))
     layer = MoeLayer(d["w13"], d["s13"], d["w2"], d["s2"], B_max=w.B, topk=w.K, device="cuda", replicas=R)
     x = torch.from_numpy(d["x"]).cuda()
     ids = torch.from_numpy(d["ids"]).cuda()
     rw = torch.from_numpy(d["weights"]).cuda()
     out = layer.out_buffer(w.B)
     y = torch.empty(w.B, w.D, dtype=torch.bfloat16, device="cuda")
-    # steps per graph: the largest divisor of `steps` up to graph_steps, so that exactly
-    # `steps` steps are timed
-    G = max(gs for gs in range(1, min(graph_steps, steps) + 1) if steps % gs == 0)
     decode = w.B <= MoeLayer.DECODE_MAX and (path == "decode" or (path == "auto" and MoeLayer.AUTO_DECODE))
     form = "decode" if decode else "grouped"
     xo = {"exchange": exchange} if (decode and exchange is not None) else {}
@@ -110,139 +115,134 @@ def measure(name: str, steps: int, warmup: int, *, graph_steps: int = 48, eager:
         layer.forward(x, ids, out, replica=i % R, path=form, **xo)
     torch.cuda.synchronize()
 
-    reps = steps // G
     stream = torch.cuda.current_stream()
-    g = ge = gc = None
+
+    def step(i):
+        layer.forward(x, ids, out, replica=i % R, path=form, **xo)
+
+    def kernel(i):  # the dominant kernel alone (the decode form's step is that kernel)
+        if decode:
+            step(i)
+        else:
+            layer.experts(w.B, out, replica=i % R)
+
+    def comb(i):
+        layer.combine(out, rw, y)
+
+    graphs = {}
     if not eager:
-        # whole step (plan + units + experts), captured G steps per graph
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(G):
-                layer.forward(x, ids, out, replica=i % R, path=form, **xo)
-        # the dominant kernel alone: the experts kernel on the plan/units of the last step
-        # (the decode form's step is that one kernel)
-        ge = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(ge):
-            for i in range(G):
-                if decode:
-                    layer.forward(x, ids, out, replica=i % R, path=form, **xo)
-                else:
-                    layer.experts(w.B, out, replica=i % R)
-        # the weighted top-k combine of the step's rows (outside the step)
-        gc = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gc):
-            for i in range(G):
-                layer.combine(out, rw, y)
-        for _ in range(2):
+        # one graph of all `steps` steps for each timed sequence: exactly `steps` steps
+        # are timed, each on its own replica
+        for key, fn in (("step", step), ("kernel", kernel), ("combine", comb)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    fn(i)
+            graphs[key] = g
+        for g in graphs.values():
             g.replay()
-            ge.replay()
-            gc.replay()
-        layer.forward(x, ids, out, path=form, **xo)  # plan and units of this batch for the experts-only graph
+        layer.forward(x, ids, out, path=form, **xo)  # plan and units of this batch for the kernel-only graph
         torch.cuda.synchronize()
 
-    def timed(run_all) -> float:
+    def timed(key, fn) -> float:
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record(stream)
-        run_all()
+        if eager:
+            for i in range(steps):
+                fn(i)
+        else:
+            graphs[key].replay()
         t1.record(stream)
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) * 1e3 / (reps * G)
+        return t0.elapsed_time(t1) * 1e3 / steps
 
-    def steps_eager():
-        for i in range(reps * G):
-            layer.forward(x, ids, out, replica=i % R, path=form, **xo)
-
-    def experts_eager():
-        for i in range(reps * G):
-            if decode:
-                layer.forward(x, ids, out, replica=i % R, path=form, **xo)
-            else:
-                layer.experts(w.B, out, replica=i % R)
-
-    def combine_eager():
-        for i in range(reps * G):
-            layer.combine(out, rw, y)
-
-    step_us = timed(steps_eager if eager else (lambda: [g.replay() for _ in range(reps)]))
-    experts_us = timed(experts_eager if eager else (lambda: [ge.replay() for _ in range(reps)]))
-    combine_us = timed(combine_eager if eager else (lambda: [gc.replay() for _ in range(reps)]))
+    step_us = timed("step", step)
+    kernel_us = timed("kernel", kernel)
+    combine_us = timed("combine", comb)
     combine_bytes = w.B * w.K * w.D * 2 + w.B * w.K * 4 + w.B * w.D * 2  # rows, weights, y
 
-    uniq = _unique_weight_bytes(d["ids"], w)
     io_bytes = w.B * w.D * 2 + w.B * w.K * 4 + w.B * w.K * w.D * 2  # x, ids, out
     plan_bytes = w.B * w.D * 33 // 32
     # weights + the activations the kernel reads (the plan, or x and ids in the decode
     # form) + output rows
     act_bytes = w.B * w.D * 2 + w.B * w.K * 4 if decode else plan_bytes
-    experts_bytes = uniq + act_bytes + w.B * w.K * w.D * 2
-    # the decode form's default exchange runs decode_whole_kernel (whole-K hidden blocks)
-    # for batches within its limits (at most 128 distinct experts); the others run
-    # experts_kernel
-    whole = decode and exchange in (None, 0) and min(w.E, w.B * w.K) <= 128
+    kernel_bytes = uniq + act_bytes + w.B * w.K * w.D * 2
     res = {
-        "workload": name, "form": form,
-        "kernel": "decode_whole_kernel" if whole else ("experts_kernel (decode form)" if decode else "experts_kernel"), "B": w.B, "E": w.E, "topk": w.K, "D": w.D, "I": w.I,
-        "distinct_experts": int(len(np.unique(d["ids"]))), "replicas": R, "graph_steps": G,
-        "step_us": step_us, "experts_us": experts_us,
+        "workload": w.name, "form": form, "kernel": layer.kernel_name(w.B, path=form, **xo),
+        "B": w.B, "E": w.E, "topk": w.K, "D": w.D, "I": w.I,
+        "distinct_experts": int(len(np.unique(d["ids"]))), "replicas": R, "rotated_bytes": R * uniq,
+        "step_us": step_us, "kernel_us": kernel_us,
         "routes_per_s": w.B * w.K / (step_us * 1e-6),
         "unique_weight_bytes": uniq, "step_bytes": uniq + io_bytes,
-        "experts_alg_bytes": experts_bytes,
+        "kernel_alg_bytes": kernel_bytes,
         "step_gbs": uniq / (step_us * 1e-6) / 1e9,
-        "experts_gbs": experts_bytes / (experts_us * 1e-6) / 1e9,
+        "kernel_gbs": kernel_bytes / (kernel_us * 1e-6) / 1e9,
+        "flops": 6 * w.I * w.D * w.B * w.K,
         "combine_us": combine_us, "combine_alg_bytes": combine_bytes,
         "combine_gbs": combine_bytes / (combine_us * 1e-6) / 1e9,
     }
     log(json.dumps({"config_detail": res}), file=sys.stderr)
-    del g, ge, gc, layer
+    del graphs, layer
     torch.cuda.empty_cache()
     return res
 
 
-def cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
-    """The oracle (plan + per-route experts) on the host cores, repeated over the whole
-    layer until `budget_s` of wall time; a bounded sample for the big layers."""
+def cpu_baseline(d: dict, threads: int, max_routes: int | None, repeats: int = 3) -> dict:
+    """The oracle (plan + per-route FC1/SwiGLU/requant/FC2 in FP64) on `threads` host
+    threads, best of `repeats` runs, on the whole layer or a seeded sample of at most
+    `max_routes` routes (then scaled to the layer by route count: routes are independent
+    and cost the same)."""
     import numpy as np
 
     import oracle
-    import workloads
 
-    d = workloads.generate(name)
     w = d["workload"]
-    threads = max(1, len(os.sched_getaffinity(0)))
     R = w.B * w.K
-    # one route takes ~6*I*D flops in FP64 with exactness checks; sample <= 256 routes
     routes = None
-    if R > 256:
-        routes = np.random.default_rng(0).choice(R, 256, replace=False).astype(np.int32)
+    if max_routes is not None and R > max_routes:
+        routes = np.random.default_rng(0).choice(R, max_routes, replace=False).astype(np.int32)
     n_routes = R if routes is None else len(routes)
-    runs = 0
-    t_start = time.perf_counter()
-    while True:
+    best = float("inf")
+    for _ in range(repeats):
+        t0 = time.perf_counter()
         codes, scales = oracle.plan(d["x"])
         oracle.experts(d["w13"], d["s13"], d["w2"], d["s2"], codes, scales, d["ids"],
                        hidden_floor=oracle.default_hidden_floor(w.I), routes=routes, nthreads=threads,
                        want_hidden=False)
-        runs += 1
-        el = time.perf_counter() - t_start
-        if el >= budget_s:
-            break
-    per_route_s = el / (runs * n_routes)
-    layer_us = per_route_s * R * 1e6
-    sample = (f"{runs} oracle run(s) of plan + {n_routes} of {R} routes "
-              f"({'all' if routes is None else 'a seeded random sample'}), {el:.1f} s wall, scaled to the layer")
+        best = min(best, time.perf_counter() - t0)
+    layer_us = best / n_routes * R * 1e6
+    sample = (f"best of {repeats} oracle runs (plan + {n_routes} of {R} routes, "
+              f"{'all' if routes is None else 'a seeded random sample'}) on {threads} thread(s): "
+              f"{best:.3f} s, scaled to the layer")
     return {"value": layer_us, "unit": "us", "cores": threads, "kind": "oracle", "sample": sample}
+
+
+def kernel_roofline(r: dict) -> dict:
+    return {
+        "bound": "hbm",
+        "kernel": r["kernel"],
+        "achieved": round(r["kernel_gbs"], 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(r["kernel_gbs"] / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(r["workload"]),
+        "avg_us": round(r["kernel_us"], 3),
+        "alg_bytes": r["kernel_alg_bytes"],
+    }
+
+
+HEADLINE = "wide_b256"  # the largest configuration the metric names (B = 256)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_b1")
-    ap.add_argument("--all", action="store_true", help="also time the other four workloads")
+    ap.add_argument("--workload", default=None,
+                    help="time only this workload (default: all five; the headline is wide_b256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--eager", action="store_true", help="launch kernels directly instead of replaying HIP graphs")
     ap.add_argument("--exchange", type=int, default=None,
                     help="decode form: FC1 -> FC2 exchange variant (moe_run_opts_t.exchange); default: the library's")
@@ -265,11 +265,21 @@ def main():
         sys.exit(1)
     if args.copy_mb > 0:
         copy_calibration(args.copy_mb)
-    names = workloads.ORDER if args.all else [args.workload]
-    results = {n: measure(n, args.steps, args.warmup, eager=args.eager, path=args.path, exchange=args.exchange)
-               for n in names}
-    main_res = results[args.workload]
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, args.cpu_budget)
+    names = [args.workload] if args.workload else list(workloads.ORDER)
+    head = args.workload or HEADLINE
+    threads = max(1, len(os.sched_getaffinity(0)))
+    results, cpu = {}, {}
+    for n in names:
+        d = workloads.generate(n)
+        print(f"bench: {n}", file=sys.stderr, flush=True)
+        results[n] = measure(d, args.steps, args.warmup, eager=args.eager, path=args.path, exchange=args.exchange)
+        if not args.no_cpu_baseline:
+            big = d["workload"].B * d["workload"].K > 256
+            cpu[n] = {"threads": cpu_baseline(d, threads, 512 if big else None)}
+            if n in ("tiny", "decode_b1", "decode_b8"):
+                cpu[n]["one_thread"] = cpu_baseline(d, 1, None)
+        del d
+    main_res = results[head]
     line = {
         "metric": "us per MoE layer & achieved HBM GB/s (% of peak), B=1..256",
         "value": round(main_res["step_us"], 3),
@@ -283,35 +293,30 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4xfp8->f32",
         "data": "synthetic",
-        "timing": "eager launches" if args.eager else "HIP graph replays",
-        "config": {"workload": args.workload, "form": main_res["form"], "B": main_res["B"], "E": main_res["E"], "topk": main_res["topk"],
-                   "D": main_res["D"], "I": main_res["I"], "parallelism": "single GPU (one TP shard)"},
+        "timing": "eager launches" if args.eager else "HIP graph replays, one replica per step (cold)",
+        "config": {"workload": head, "form": main_res["form"], "B": main_res["B"], "E": main_res["E"],
+                   "topk": main_res["topk"], "D": main_res["D"], "I": main_res["I"],
+                   "parallelism": "single GPU (one TP shard)"},
         "routes_per_s": round(main_res["routes_per_s"], 1),
         "hbm_gbs_unique_weights": round(main_res["step_gbs"], 1),
         "hbm_frac_of_peak": round(main_res["step_gbs"] / HBM_PEAK_GBS, 4),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": main_res["kernel"],
-            "achieved": round(main_res["experts_gbs"], 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(main_res["experts_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload),
-            "avg_us": round(main_res["experts_us"], 3),
-            "alg_bytes": main_res["experts_alg_bytes"],
-        },
-        "cpu_baseline": cpu,
-        "combine": {"kernel": "combine_kernel", "us": round(main_res["combine_us"], 3),
-                    "alg_bytes": main_res["combine_alg_bytes"], "gbs": round(main_res["combine_gbs"], 1),
-                    "note": "weighted top-k combine of the step's rows into [B, D]; not part of the step"},
+        "roofline": kernel_roofline(main_res),
+        "cpu_baseline": cpu.get(head, {}).get("threads"),
+        "per_workload": {},
     }
-    if args.all:
-        line["per_workload"] = {n: {"form": r["form"], "us": round(r["step_us"], 3),
-                                    "experts_us": round(r["experts_us"], 3),
-                                    "combine_us": round(r["combine_us"], 3),
-                                    "routes_per_s": round(r["routes_per_s"], 1),
-                                    "gbs_unique": round(r["step_gbs"], 1),
-                                    "frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4)} for n, r in results.items()}
+    for n, r in results.items():
+        line["per_workload"][n] = {
+            "form": r["form"], "us": round(r["step_us"], 3), "routes_per_s": round(r["routes_per_s"], 1),
+            "gbs_unique": round(r["step_gbs"], 1), "frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
+            "distinct_experts": r["distinct_experts"], "replicas": r["replicas"],
+            "rotated_bytes": r["rotated_bytes"], "tflops": round(r["flops"] / (r["step_us"] * 1e-6) / 1e12, 2),
+            "roofline": kernel_roofline(r),
+            "combine": {"kernel": "combine_kernel", "us": round(r["combine_us"], 3),
+                        "alg_bytes": r["combine_alg_bytes"], "gbs": round(r["combine_gbs"], 1),
+                        "note": "weighted top-k combine of the step's rows into [B, D]; not part of the step"},
+            "cpu_baseline": {k: {"us": round(v["value"], 1), "cores": v["cores"], "sample": v["sample"]}
+                             for k, v in cpu.get(n, {}).items()},
+        }
     print(json.dumps(line), flush=True)
 
 

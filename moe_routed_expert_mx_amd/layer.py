@@ -69,6 +69,18 @@ class MoeLayer:
                              **opts)
         return out
 
+    def kernel_name(self, B: int, path: str = "auto", exchange: int | None = None) -> str:
+        """Name of the kernel that does a step's FC1/FC2 work (for reports): the decode form
+        runs decode_whole_kernel for batches within its limits (at most 128 distinct
+        experts, B*topk <= 640, B*D/32 <= 2560, I <= 512) unless another exchange is asked
+        for; everything else runs experts_kernel."""
+        decode = path == "decode" or (path == "auto" and self.AUTO_DECODE and B <= self.DECODE_MAX)
+        routes = B * self.topk
+        whole = (min(self.E, routes) <= 128 and routes <= 640 and B * self.D // 32 <= 2560 and self.I <= 512)
+        if decode and exchange in (None, 0) and whole:
+            return "decode_whole_kernel"
+        return "experts_kernel (decode form)" if decode else "experts_kernel"
+
     def experts(self, B: int, out: torch.Tensor, *, replica: int = 0, stream=None, **opts):
         """The experts kernel alone, on the plan and unit table of the last forward()."""
         _lib.moe_experts_run(self.structs[replica], self.plan, self.units, B, self.topk, self.ws, out, stream=stream,

@@ -63,7 +63,7 @@ def lib():
         L.oracle_group.argtypes = [P, c.c_int, c.c_int, c.c_int, P, P]
         L.oracle_experts.restype = c.c_int
         L.oracle_experts.argtypes = [c.c_int, c.c_int, c.c_int, P, P, P, P, P, P, P, c.c_int,
-                                     c.c_int, P, c.c_int, c.c_int, P, P, P, P, P, P, c.c_int, P]
+                                     c.c_int, P, c.c_int, c.c_int, P, P, P, P, P, P, P, c.c_int, P]
         L.oracle_combine.restype = c.c_int
         L.oracle_combine.argtypes = [P, P, c.c_int, c.c_int, c.c_int, P]
         _lib = L
@@ -147,13 +147,13 @@ def group(ids: np.ndarray, E: int):
 
 def experts(w13, s13, w2, s2, codes, scales, ids, *, hidden_floor: bool, routes=None,
             nthreads: int = 1, want_fc1: bool = False, want_hidden: bool = True,
-            want_hidden_f32: bool = False):
+            want_hidden_f32: bool = False, want_fc1_abs: bool = False):
     """Per-route FC1 -> SwiGLU -> MXFP8 requant -> FC2.  Canonical weight layouts:
     w13 [E, 2I, D/2], s13 [E, 2I, D/32], w2 [E, D, I/2], s2 [E, D, I/32].
 
     Returns dict(out=BF16 bits [n, D], out_f32=[n, D] (the rows before BF16 rounding),
-    fc1=[n, 2I] f32 | None, hidden=[n, I] f32 (the gated activation before its
-    requantization) | None, hcodes=[n, I], hscales=[n, I/32], inexact=int)."""
+    fc1=[n, 2I] f32 | None, fc1_abs=[n, 2I] f64 (sum of |w*x| of each FC1 row) | None,
+    hidden=[n, I] f32 (the gated activation before its requantization) | None, hcodes=[n, I], hscales=[n, I/32], inexact=int)."""
     w13, s13, w2, s2 = (_c(a, np.uint8) for a in (w13, s13, w2, s2))
     codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
     ids = _c(ids, np.int32)
@@ -166,16 +166,17 @@ def experts(w13, s13, w2, s2, codes, scales, ids, *, hidden_floor: bool, routes=
     out32 = np.empty((n, D), np.float32)
     fc1 = np.empty((n, 2 * I), np.float32) if want_fc1 else None
     hf = np.empty((n, I), np.float32) if want_hidden_f32 else None
+    fa = np.empty((n, 2 * I), np.float64) if want_fc1_abs else None
     hc = np.empty((n, I), np.uint8) if want_hidden else None
     hs = np.empty((n, I // 32), np.uint8) if want_hidden else None
     inexact = ctypes.c_int64(0)
     rc = lib().oracle_experts(E, D, I, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), _ptr(codes),
                               _ptr(scales), _ptr(ids), B, K, _ptr(r), n, int(hidden_floor),
-                              _ptr(out), _ptr(out32), _ptr(fc1), _ptr(hf), _ptr(hc), _ptr(hs), int(nthreads),
+                              _ptr(out), _ptr(out32), _ptr(fc1), _ptr(fa), _ptr(hf), _ptr(hc), _ptr(hs), int(nthreads),
                               ctypes.byref(inexact))
     if rc:
         raise ValueError("oracle_experts: invalid arguments")
-    return {"out": out, "out_f32": out32, "fc1": fc1, "hidden": hf, "hcodes": hc, "hscales": hs,
+    return {"out": out, "out_f32": out32, "fc1": fc1, "fc1_abs": fa, "hidden": hf, "hcodes": hc, "hscales": hs,
             "inexact": inexact.value}
 
 

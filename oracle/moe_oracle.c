@@ -238,6 +238,7 @@ typedef struct {
   float* out_f32;
   float* fc1;
   float* hidden; /* optional: the FP32 hidden before its requantization */
+  double* fc1_abs; /* optional: sum over k of |w * x| per FC1 row (the sum's condition) */
   uint8_t *hcodes, *hscales;
   double *e2m1, *e4m3, *e8m0; /* decode tables (plain lookups of the decoders above) */
 } oracle_job;
@@ -270,13 +271,15 @@ static int64_t oracle_route(const oracle_job* j, int out_row, int route) {
   for (int r = 0; r < 2 * I; ++r) {
     const uint8_t* wrow = j->w13 + ((size_t)e * 2 * I + r) * (D / 2);
     const uint8_t* srow = j->s13 + ((size_t)e * 2 * I + r) * (D / 32);
-    double acc = 0.0;
+    double acc = 0.0, mag = 0.0;
     for (int k = 0; k < D; ++k) {
       double w = fp4_at(j, wrow, k) * j->e8m0[srow[k / 32]];
       double x = j->e4m3[xc[k]] * j->e8m0[xs[k / 32]];
       acc = two_sum(acc, w * x, &inexact);
+      mag += fabs(w * x);
     }
     a[r] = (float)acc;
+    if (j->fc1_abs) j->fc1_abs[(size_t)out_row * 2 * I + r] = mag;
   }
   /* SwiGLU, FP32 hidden (no BF16 rounding before the requantization) */
   for (int i = 0; i < I; ++i) {
@@ -325,9 +328,11 @@ static void* oracle_worker_main(void* arg) {
 
 /* Runs the routes listed in `routes` (NULL: all B*K routes, in pair order) and writes
  * output row i for the i-th listed route (`out_f32`, optional: the same rows before
- * their BF16 rounding, i.e. the exact FC2 sums rounded once to FP32; `fc1`, `hidden`,
- * `hcodes`, `hscales`, optional: the route's FC1 values [2I], FP32 hidden [I] and its
- * MXFP8 codes [I] and scales [I/32]).  Routes are independent of each other, so
+ * their BF16 rounding, i.e. the exact FC2 sums rounded once to FP32; `fc1`, `fc1_abs`,
+ * `hidden`, `hcodes`, `hscales`, optional: the route's FC1 values [2I], the sums of
+ * their terms' magnitudes [2I] (in FP64: they bound how far an FP32 summation in any
+ * order can land from the exact value), FP32 hidden [I] and its MXFP8 codes [I] and
+ * scales [I/32]).  Routes are independent of each other, so
  * they are spread over `nthreads` threads.  `inexact` (optional) receives the number
  * of FP64 additions that rounded (0 certifies the FC1/FC2 sums as exact).
  * Returns 0, or -1 on invalid arguments / ids. */
@@ -335,7 +340,7 @@ ORACLE_API int oracle_experts(int E, int D, int I, const uint8_t* w13, const uin
                               const uint8_t* w2, const uint8_t* s2, const uint8_t* xcodes,
                               const uint8_t* xscales, const int32_t* ids, int B, int K,
                               const int32_t* routes, int n_routes, int hidden_floor,
-                              uint16_t* out, float* out_f32, float* fc1, float* hidden,
+                              uint16_t* out, float* out_f32, float* fc1, double* fc1_abs, float* hidden,
                               uint8_t* hcodes, uint8_t* hscales, int nthreads, int64_t* inexact) {
   if (E <= 0 || D <= 0 || I <= 0 || D % 32 || I % 32 || B < 0 || K <= 0) return -1;
   for (int r = 0; r < B * K; ++r)
@@ -348,7 +353,7 @@ ORACLE_API int oracle_experts(int E, int D, int I, const uint8_t* w13, const uin
   for (int c = 0; c < 256; ++c) e4m3[c] = oracle_e4m3_value((unsigned)c);
   for (int c = 0; c < 256; ++c) e8m0[c] = oracle_e8m0_value((unsigned)c);
   oracle_job job = {E, D, I, hidden_floor, w13, s13, w2, s2, xcodes, xscales, ids, B, K,
-                    routes, n_routes, out, out_f32, fc1, hidden, hcodes, hscales, e2m1, e4m3, e8m0};
+                    routes, n_routes, out, out_f32, fc1, hidden, fc1_abs, hcodes, hscales, e2m1, e4m3, e8m0};
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   oracle_worker workers[256];

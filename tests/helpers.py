@@ -68,6 +68,16 @@ def check_rows(got_u16: np.ndarray, ref_u16, what: str = ""):
     return float(rel.max()), float((mx / np.maximum(rms, 1e-300))[~zero].max() if (~zero).any() else 0.0)
 
 
+def record_stats(stats: dict):
+    """Append one parity record (JSON line) to gpurun_out/parity_stats.jsonl when that
+    folder exists (GPU runs collect them; elsewhere nothing is written)."""
+    import json
+    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+    if os.path.isdir(d):
+        with open(os.path.join(d, "parity_stats.jsonl"), "a") as f:
+            f.write(json.dumps(stats) + "\n")
+
+
 def log(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()

@@ -157,6 +157,14 @@ def test_experts_match_dense_fp64(orc, which):
     fc1, out = _dense_reference(d, codes, scales, res, floor)
     assert np.array_equal(res["fc1"], fc1)
     assert np.array_equal(res["out"], out)
+    # the sums of the FC1 terms' magnitudes: dense |W13| @ |X| of the same operands
+    res2 = orc.experts(d["w13"], d["s13"], d["w2"], d["s2"], codes, scales, d["ids"],
+                       hidden_floor=floor, want_fc1_abs=True, nthreads=2)
+    X = np.abs(dq_fp8(codes, scales))
+    for r in range(d["workload"].B * d["workload"].K):
+        e = d["ids"].ravel()[r]
+        mag = np.abs(dq_fp4(d["w13"][e], d["s13"][e])) @ X[r // d["workload"].K]
+        assert np.allclose(res2["fc1_abs"][r], mag, rtol=1e-12, atol=0)
     # SwiGLU + requant of the FP32 FC1 values (torch's cast, exponent rule pinned in
     # test_oracle_formats): at least 99.9% identical, the rest one code apart
     g, u = fc1[:, : d["workload"].I].astype(np.float64), fc1[:, d["workload"].I:].astype(np.float64)
