@@ -53,6 +53,7 @@ enum moe_status {
   MOE_EINVAL = -1,       /* null pointer, bad size or unsupported shape */
   MOE_ENOSPACE = -2,     /* plan, workspace or output buffer too small */
   MOE_EHIP = -3,         /* a HIP call or kernel launch failed */
+  MOE_ELIMIT = -4,       /* moe_decode_run_noalloc: the batch needs more than its fixed scratch */
 };
 
 /* Human-readable name of a moe_status value (static string). */
@@ -216,6 +217,24 @@ int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
 int moe_decode_run(const moe_weights_t* weights, const moe_run_opts_t* opts, const void* x_dev,
                    const int32_t* ids_dev, int32_t B, int32_t topk, void* ws_dev, size_t ws_bytes,
                    void* out_dev, size_t out_bytes, void* stream);
+
+/* moe_decode_run for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same step, the same
+ * kernel and the same rows bit for bit, with no workspace argument.  What moe_decode_run
+ * keeps in the workspace (the call counters, the default status word and the call-tagged
+ * hidden exchange) lives in a fixed scratch inside the library: one copy per device,
+ * 1,188,096 bytes, zero when the library's code is loaded on that device and held until
+ * the process ends.  The first call on a device looks up that device's copy
+ * (hipGetSymbolAddress); no call allocates, frees or clears memory.
+ * Limits (MOE_ELIMIT beyond them): the whole-K decode form only -- B <= 8, at most 128
+ * distinct experts in the batch, B*topk <= 640, B*D/32 <= 2560, I <= 512; opts->exchange
+ * must be 0.  Other arguments, options and errors as moe_decode_run.
+ * All calls on one device share its scratch: calls that overlap in time on one device
+ * (different streams without ordering, or several host threads) race and give wrong
+ * rows; order them on one stream.  Calls on different devices are independent. */
+int moe_decode_run_noalloc(const moe_weights_t* weights, const moe_run_opts_t* opts, const void* x_dev,
+                           const int32_t* ids_dev, int32_t B, int32_t topk, void* out_dev, size_t out_bytes,
+                           void* stream);
 
 /* ------------------------------------------------------------- combine ---- */
 

@@ -18,7 +18,7 @@ import torch  # noqa: F401
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_mx.so")
 
-MOE_OK, MOE_EINVAL, MOE_ENOSPACE, MOE_EHIP = 0, -1, -2, -3
+MOE_OK, MOE_EINVAL, MOE_ENOSPACE, MOE_EHIP, MOE_ELIMIT = 0, -1, -2, -3, -4
 
 
 class MoeError(RuntimeError):
@@ -65,6 +65,8 @@ def _load():
                                       c.c_int32, c.c_int32, P, c.c_size_t, P, c.c_size_t, P]),
         "moe_decode_run": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_int32,
                                      c.c_int32, P, c.c_size_t, P, c.c_size_t, P]),
+        "moe_decode_run_noalloc": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_int32,
+                                             c.c_int32, P, c.c_size_t, P]),
         "moe_combine": (c.c_int, [P, c.c_size_t, P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
     }
     for name, (res, args) in sig.items():
@@ -76,7 +78,7 @@ def _load():
 lib = _load()
 EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_units_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
             "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_plan_group", "moe_units_export",
-            "moe_experts_run", "moe_decode_run", "moe_combine")
+            "moe_experts_run", "moe_decode_run", "moe_decode_run_noalloc", "moe_combine")
 
 
 def status_string(status: int) -> str:
@@ -179,6 +181,17 @@ def moe_decode_run(weights: moe_weights_t, x, ids, ws, out, *, hidden_rule=0, gr
     opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, exchange)
     _check("moe_decode_run", lib.moe_decode_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(x), _ptr(ids), B, K,
                                                 _ptr(ws), _nbytes(ws), _ptr(out), _nbytes(out), _stream(stream)))
+
+
+def moe_decode_run_noalloc(weights: moe_weights_t, x, ids, out, *, hidden_rule=0, grid=0, ring=0,
+                           hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
+    """moe_decode_run with the library's fixed per-device scratch instead of a workspace
+    (no allocation; the whole-K decode form only, MOE_ELIMIT beyond its limits)."""
+    B, K = ids.shape
+    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, 0)
+    _check("moe_decode_run_noalloc", lib.moe_decode_run_noalloc(ctypes.byref(weights), ctypes.byref(opts), _ptr(x),
+                                                                _ptr(ids), B, K, _ptr(out), _nbytes(out),
+                                                                _stream(stream)))
 
 
 def moe_combine(rows, weights, out, stream=None):

@@ -26,6 +26,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "moe_mx.h"
 
@@ -3248,16 +3249,35 @@ bool whole_fits(const moe_weights_t* wts, int32_t B, int32_t topk) {
          static_cast<int64_t>(B) * wts->D / 32 <= static_cast<int64_t>(kQXBlk) * kQWG;
 }
 
+// The decode form with whole-K FC1 blocks on the given workspace areas: the call
+// counters [kMaxGrid], the default status word and the hidden exchange [kQGMax][8][IP/4 +
+// kQHB] pairs (from a caller's workspace, or from the allocation-free entry point's
+// fixed scratch).
+int launch_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids,
+                        int32_t B, int32_t topk, uint32_t* calls, int32_t* status, uint64_t* hq, void* out,
+                        void* stream);
+
 // The decode form with whole-K FC1 blocks (moe_run_opts_t.exchange == 0, the default,
 // for batches within whole_fits).
 int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids, int32_t B,
                      int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
   const int E = wts->E, D = wts->D, I = wts->I;
   if (!whole_fits(wts, B, topk)) return MOE_EINVAL;
-  const int IP = (I + 127) / 128 * 128, ns2 = IP / 128;
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
   if (B_cap < B) return MOE_ENOSPACE;
   const WsLayout L = ws_layout(E, D, I, topk, B_cap);
+  (void)out_bytes;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  return launch_decode_whole(wts, o, x, ids, B, topk, reinterpret_cast<uint32_t*>(base + L.qcalls),
+                             reinterpret_cast<int32_t*>(base + L.status), reinterpret_cast<uint64_t*>(base + L.qhq),
+                             out, stream);
+}
+
+int launch_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids,
+                        int32_t B, int32_t topk, uint32_t* calls, int32_t* status, uint64_t* hq, void* out,
+                        void* stream) {
+  const int E = wts->E, D = wts->D, I = wts->I;
+  const int IP = (I + 127) / 128 * 128, ns2 = IP / 128;
   const QLds m = q_lds(B, D, IP);
   const size_t limit = static_cast<size_t>(device_lds_limit());
   // two slots per wave by default: measured fastest at the decode sizes (B = 1: 13.9 us
@@ -3282,7 +3302,6 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
   const int grid = o.grid ? o.grid : cap;
 
-  uint8_t* base = static_cast<uint8_t*>(ws);
   QArgs a;
   std::memset(&a, 0, sizeof(a));
   a.w13p = static_cast<const uint8_t*>(wts->w13);
@@ -3292,10 +3311,10 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   a.x = static_cast<const uint16_t*>(x);
   a.ids = ids;
   a.out = static_cast<uint16_t*>(out);
-  a.hq = reinterpret_cast<uint64_t*>(base + L.qhq);
+  a.hq = hq;
   a.hq_words = IP / 4 + kQHB;
-  a.calls = reinterpret_cast<uint32_t*>(base + L.qcalls);
-  a.err = o.status_dev ? static_cast<int32_t*>(o.status_dev) : reinterpret_cast<int32_t*>(base + L.status);
+  a.calls = calls;
+  a.err = o.status_dev ? static_cast<int32_t*>(o.status_dev) : status;
   a.dump_codes = static_cast<uint8_t*>(o.hidden_codes_dev);
   a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
   a.plan_dump = static_cast<uint8_t*>(o.plan_dev);
@@ -3318,9 +3337,39 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   a.hid_bytes = m.hid_bytes;
   a.cb = m.cb;
   a.red_wave = m.red_wave;
-  (void)out_bytes;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kQWG), lds, as_stream(stream), a);
   return launch_status();
+}
+
+// ------------------------------------------- the allocation-free entry point's scratch
+// moe_decode_run_noalloc keeps what moe_decode_run keeps in the caller's workspace --
+// the call counters, the status word and the call-tagged hidden exchange -- in this
+// file-scope array instead: one copy per device, zero when the code object is loaded,
+// kept until the process ends.  Every quantity in it is tagged with call numbers, so
+// no call clears anything.  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchCalls = 0;                                  // u32 [kMaxGrid]
+constexpr size_t kScratchStatus = kScratchCalls + kMaxGrid * 4;      // i32 status word
+constexpr size_t kScratchHq = kScratchStatus + 256;                  // u64 [kQGMax][8][512 / 4 + kQHB]
+constexpr size_t kScratchBytes = kScratchHq + static_cast<size_t>(kQGMax) * 8 * (512 / 4 + kQHB) * 8;
+static_assert(kScratchHq % 256 == 0, "aligned areas");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// The device address of this device's copy of `scratch` (nullptr if it cannot be had).
+uint8_t* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev] = p;
+  }
+  return static_cast<uint8_t*>(ptrs[dev]);
 }
 }  // namespace
 
@@ -3333,6 +3382,7 @@ const char* moe_status_string(int status) {
     case MOE_EINVAL: return "invalid argument or unsupported shape";
     case MOE_ENOSPACE: return "buffer too small";
     case MOE_EHIP: return "HIP launch or runtime error";
+    case MOE_ELIMIT: return "batch beyond the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -3478,6 +3528,31 @@ int moe_decode_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const v
                    int32_t B, int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
   if (!x || !ids || B > kDecodeMax) return MOE_EINVAL;
   return run_experts<true>(wts, opts, nullptr, nullptr, 0, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
+}
+
+int moe_decode_run_noalloc(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* x, const int32_t* ids,
+                           int32_t B, int32_t topk, void* out, size_t out_bytes, void* stream) {
+  if (!wts || !x || !ids || !out || B < 1 || B > kDecodeMax || topk < 1 || topk > 64) return MOE_EINVAL;
+  const int E = wts->E, D = wts->D, I = wts->I;
+  if (!shape_ok(E, D, I) || !wts->w13 || !wts->s13 || !wts->w2 || !wts->s2) return MOE_EINVAL;
+  moe_run_opts_t o;
+  std::memset(&o, 0, sizeof(o));
+  if (opts) o = *opts;
+  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 1) ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.exchange != 0 ||
+      ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)) ||
+      (o.plan_bytes != 0 && o.plan_dev == nullptr))
+    return MOE_EINVAL;
+  if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
+  if (o.plan_dev != nullptr && o.plan_bytes < static_cast<size_t>(B) * D / 32 * 33) return MOE_ENOSPACE;
+  // the scratch holds the whole-K form's exchange for at most kQGMax distinct experts of
+  // at most 8 token columns and I <= 512; the kernel's own limits are the same
+  if (!whole_fits(wts, B, topk)) return MOE_ELIMIT;
+  uint8_t* base = scratch_ptr();
+  if (base == nullptr) return MOE_EHIP;
+  return launch_decode_whole(wts, o, x, ids, B, topk, reinterpret_cast<uint32_t*>(base + kScratchCalls),
+                             reinterpret_cast<int32_t*>(base + kScratchStatus),
+                             reinterpret_cast<uint64_t*>(base + kScratchHq), out, stream);
 }
 
 }  // extern "C"

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(m):
 
 def test_status_strings(m):
     assert m.status_string(0) == "ok"
-    for s in (-1, -2, -3):
+    for s in (-1, -2, -3, -4):
         assert m.status_string(s) != "unknown status"
 
 
@@ -161,3 +161,24 @@ def test_decode_run_argument_checks(m):
                              None) == m._lib.MOE_EINVAL
     # a workspace sized for decode batches serves every B <= B_max of the form
     assert m.moe_workspace_bytes(160, 3584, 384, 8, 16) >= m.moe_workspace_bytes(160, 3584, 384, 1, 16)
+
+
+def test_noalloc_host_side_limits(m):
+    """The allocation-free entry point checks its limits on the host before any HIP call:
+    B > 8 or an exchange other than 0 is MOE_EINVAL; a batch whose whole-K exchange would
+    not fit its fixed scratch (here more than 128 distinct experts) is MOE_ELIMIT."""
+    L = m._lib.lib
+    fake = ctypes.c_void_p(0x1000)
+    w = m.moe_weights_t(400, 512, 64, fake, fake, fake, fake)
+    o = m.moe_run_opts_t()
+    big = 8 * 40 * 512 * 2
+    assert L.moe_decode_run_noalloc(ctypes.byref(w), ctypes.byref(o), fake, fake, 9, 4, fake, big, None) \
+        == m._lib.MOE_EINVAL
+    assert L.moe_decode_run_noalloc(ctypes.byref(w), ctypes.byref(o), fake, fake, 8, 40, fake, big, None) \
+        == m._lib.MOE_ELIMIT
+    o.exchange = 2
+    assert L.moe_decode_run_noalloc(ctypes.byref(w), ctypes.byref(o), fake, fake, 2, 4, fake, big, None) \
+        == m._lib.MOE_EINVAL
+    o.exchange = 0
+    assert L.moe_decode_run_noalloc(ctypes.byref(w), ctypes.byref(o), fake, fake, 2, 4, fake, 16, None) \
+        == m._lib.MOE_ENOSPACE
