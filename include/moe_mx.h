@@ -36,7 +36,8 @@
  *   out      BF16  [B*topk, D]
  * Supported shapes: 512 <= D <= 16384 with D % 512 == 0, 32 <= I <= 512 with
  * I % 32 == 0, 1 <= E <= 1024, 1 <= topk <= 64, 1 <= B*topk <= 65536; moe_group also
- * needs E * ceil(B/32) + 2E <= 15360 (its per-expert token bitmasks live in LDS).
+ * needs E * ceil(B/32) + 3E <= 15360 (its per-expert token bitmasks and counts live
+ * in LDS).
  */
 #ifndef MOE_MX_H
 #define MOE_MX_H
@@ -66,7 +67,10 @@ const char* moe_status_string(int status);
 size_t moe_plan_bytes(int32_t B, int32_t D);
 
 /* Bytes of the unit-table buffer of a batch of B tokens with topk routes each over E
- * experts (header, per-unit expert and pair rows, the distinct-expert list). */
+ * experts (experts page, ExpertsKernel.group: the per-batch grouping of routes by
+ * expert): header, per-unit expert and pair rows, the distinct-expert list and the
+ * 32-column chunk table.  Sized for the worst case of the batch, so one buffer serves
+ * any ids.  0 on invalid sizes. */
 size_t moe_units_bytes(int32_t B, int32_t topk, int32_t E);
 
 /* Bytes of the caller-owned workspace of the experts kernel for calls with up to B_max
@@ -76,10 +80,12 @@ size_t moe_units_bytes(int32_t B, int32_t topk, int32_t E);
  * the B_max it was sized for.  0 on invalid sizes. */
 size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32_t topk);
 
-/* Bytes of the four packed weight buffers written by moe_pack_weights.  They equal
- * the canonical sizes (the packing only reorders 16-byte code runs and scale bytes),
- * except that FC2 codes and scales are padded to a multiple of 128 along I.
- * Returns MOE_OK or MOE_EINVAL. */
+/* Bytes of the four packed weight buffers written by moe_pack_weights (experts page,
+ * ExpertsKernel.schedule / produce: the weights stream tile by tile, 128 K at a time).
+ * They equal the canonical sizes (the packing only reorders 16-byte code runs and scale
+ * bytes), except that FC2 codes and scales are padded to a multiple of 128 along I.
+ * The four size_t outputs are host pointers (any may be NULL).  Returns MOE_OK or
+ * MOE_EINVAL for an unsupported shape. */
 int moe_packed_weight_bytes(int32_t E, int32_t D, int32_t I, size_t* w13_bytes,
                             size_t* s13_bytes, size_t* w2_bytes, size_t* s2_bytes);
 
@@ -123,13 +129,16 @@ int moe_plan(const void* x_dev, int32_t B, int32_t D, void* plan_dev, size_t pla
  * ExpertsGroupKernel): expert e's routes, in token order, fill ceil(n_e / 8) units
  * numbered in ascending expert order; each unit row holds eight pair indices
  * t*topk + s, -1 where padded.  Also lists the distinct experts ("groups") with their
- * first unit, unit count and first 16-column tile, which the experts kernel walks.
+ * first unit, unit count and first 16-column tile, and cuts each expert's routes, in the
+ * same order, into chunks of 32 (the grouped kernel's weight-pass width): per chunk its
+ * expert and 32 pair indices (-1 padded), in ascending expert order.
  * Written into `units_dev` (moe_units_bytes(B, topk, E) bytes); run it before
  * moe_experts_run on the same stream. */
 int moe_group(const int32_t* ids_dev, int32_t B, int32_t topk, int32_t E, void* units_dev,
               size_t units_bytes, void* stream);
 
-/* moe_plan and moe_group of one batch in a single launch (the same outputs, bit for bit):
+/* moe_plan and moe_group of one batch in a single launch (experts page, plan_chunk and
+ * ExpertsKernel.group; the same outputs, bit for bit):
  * x_dev BF16 [B, D] -> plan_dev (moe_plan layout), ids_dev i32 [B, topk] -> units_dev
  * (moe_group layout).  One workgroup builds the unit table while the others quantize x,
  * which saves a launch per step of the grouped form.  Arguments and errors as the two
@@ -137,8 +146,8 @@ int moe_group(const int32_t* ids_dev, int32_t B, int32_t topk, int32_t E, void* 
 int moe_plan_group(const void* x_dev, const int32_t* ids_dev, int32_t B, int32_t D, int32_t topk, int32_t E,
                    void* plan_dev, size_t plan_bytes, void* units_dev, size_t units_bytes, void* stream);
 
-/* Copy the unit table that moe_group wrote into caller device buffers (for
- * inspection): header_dev i32[4] = {n_units, n_groups, n_column_tiles, flags (bit 0: an
+/* Copy the unit table that moe_group wrote (experts page, ExpertsKernel.group) into
+ * caller device buffers (for inspection): header_dev i32[4] = {n_units, n_groups, n_column_tiles, flags (bit 0: an
  * id was out of range, bit 1: an id repeated within a token, bit 2: an experts call gave
  * up waiting for a hidden block -- never expected)}, unit_expert_dev i32[max_units],
  * unit_rows_dev i32[max_units, 8].  Enqueued device-to-device copies. */
@@ -155,10 +164,16 @@ typedef struct {
   int32_t hidden_rule;
   int32_t grid;       /* persistent workgroups, at most the device's resident capacity
                          for the kernel variant (MOE_EINVAL above it); 0 = all of it */
-  int32_t col_tiles;  /* 16-token column tiles per weight pass: 0 or 1 (the kernel's only
-                         width; other values are MOE_EINVAL) */
-  int32_t ring;       /* weight items in flight per streaming wave (2..4); 0 = the deepest
-                         that fits in LDS next to the unit table */
+  int32_t col_tiles;  /* moe_experts_run: 16-token column tiles per weight pass.
+                         0 = default: the grouped kernel (two tiles, 32-route chunks) when
+                         the batch fits its limits (I <= 512, at most 1024 chunks and 32
+                         FC1 blocks per workgroup), else 1;
+                         1 = the one-tile experts kernel (any batch);
+                         2 = the grouped kernel only (MOE_EINVAL beyond its limits);
+                         moe_decode_run: 0 or 1; other values MOE_EINVAL */
+  int32_t ring;       /* weight items in flight per streaming wave (2..4) of the one-tile
+                         and decode kernels; 0 = the deepest that fits in LDS next to the
+                         unit table (the grouped kernel always keeps three) */
   int32_t exchange;   /* moe_decode_run only: how FC1 results reach FC2 --
                          0 = whole-K blocks (default): a hidden block's FC1 runs over all of
                          K in one workgroup, which applies SwiGLU and MXFP8 and publishes the
@@ -189,9 +204,13 @@ typedef struct {
  * tokens, SwiGLU, MXFP8 requantization of the hidden, FC2 against the packed w2, BF16
  * rows into out_dev [B*topk, D] in the caller's top-k order.  Reads the plan written by
  * moe_plan and the unit table written by moe_group (same B and topk).
- * One persistent, co-resident kernel: every workgroup takes an equal contiguous slice
- * of the FC1 weight stream, then of the FC2 weight stream; FC2 waits, per expert, for
- * the hidden blocks that FC1 slices publish (device-coherent stores, call-tagged flags).
+ * One persistent, co-resident kernel.  By default (col_tiles 0) the grouped kernel: an
+ * FC1 work item is one 32-wide hidden block of one 32-route chunk over the whole of K,
+ * so one workgroup applies SwiGLU and MXFP8 to it and publishes it (device-coherent
+ * stores, a call-tagged flag); FC2 tiles are dealt as contiguous runs, and each chunk's
+ * FC2 waits for its hidden blocks.  The one-tile experts kernel (col_tiles 1) instead
+ * gives every workgroup an equal contiguous slice of the FC1 weight stream, then of the
+ * FC2 weight stream, and FC2 waits per expert for the split blocks FC1 slices publish.
  * The grid is sized from the kernel's occupancy so that it is resident at once; do not
  * run other kernels on the device concurrently with it.  Calls that share a workspace
  * must not overlap (one stream, or ordered streams). */

@@ -34,6 +34,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kStream = 4;        // streaming waves per experts workgroup
 constexpr int kWG = 64 * (kStream + 1);  // plus one control wave
@@ -209,25 +210,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 // and first 16-column tile.
 struct Table {
   int32_t* hdr;          // [16]: n_units, n_groups, n_tiles, flags (1: id out of range,
-                         //        2: id repeated in a token, 4: a hidden wait timed out)
+                         //        2: id repeated in a token, 4: a hidden wait timed out),
+                         //        n_chunks
   int32_t* unit_expert;  // [U]
   int32_t* unit_rows;    // [U, 8]
   int32_t* g_expert;     // [G]
   int32_t* g_unit0;      // [G]
   int32_t* g_nunits;     // [G]
   int32_t* g_tile0;      // [G]
+  // chunks of the grouped kernel: each expert's routes, in token order, cut into runs of
+  // kChunkCols token columns (one weight pass of that expert each)
+  int32_t* c_expert;     // [C]
+  int32_t* c_ncols;      // [C] real columns (1..kChunkCols)
+  int32_t* c_pairs;      // [C, kChunkCols] pair indices t*K + s, -1 where padded
 };
+constexpr int kChunkCols = 32;  // token columns per chunk: two 16-column MFMA tiles
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct UnitsLayout {
-  size_t hdr, unit_expert, unit_rows, g_expert, g_unit0, g_nunits, g_tile0, end;
+  size_t hdr, unit_expert, unit_rows, g_expert, g_unit0, g_nunits, g_tile0, c_expert, c_ncols, c_pairs, end;
+  int64_t max_chunks;
 };
+
+// Chunks of a batch of U routes over at most G experts: sum_g ceil(n_g / 32) with
+// sum_g n_g = U.
+int64_t max_chunks_for(int64_t U, int64_t G) { return G + (U + kChunkCols - 1) / kChunkCols; }
 
 UnitsLayout units_layout(int B, int K, int E) {
   UnitsLayout L{};
   const int64_t U = static_cast<int64_t>(B) * K;
   const int64_t G = U < E ? U : E;
+  L.max_chunks = max_chunks_for(U, G);
   size_t off = 0;
   L.hdr = off;
   off += 64;
@@ -243,6 +257,12 @@ UnitsLayout units_layout(int B, int K, int E) {
   off += G * 4;
   L.g_tile0 = off;
   off += G * 4;
+  L.c_expert = align256(off);
+  off = L.c_expert + L.max_chunks * 4;
+  L.c_ncols = off;
+  off += L.max_chunks * 4;
+  L.c_pairs = align256(off);
+  off = L.c_pairs + L.max_chunks * kChunkCols * 4;
   L.end = align256(off);
   return L;
 }
@@ -256,24 +276,29 @@ Table table_at(uint8_t* base, const UnitsLayout& L) {
   t.g_unit0 = reinterpret_cast<int32_t*>(base + L.g_unit0);
   t.g_nunits = reinterpret_cast<int32_t*>(base + L.g_nunits);
   t.g_tile0 = reinterpret_cast<int32_t*>(base + L.g_tile0);
+  t.c_expert = reinterpret_cast<int32_t*>(base + L.c_expert);
+  t.c_ncols = reinterpret_cast<int32_t*>(base + L.c_ncols);
+  t.c_pairs = reinterpret_cast<int32_t*>(base + L.c_pairs);
   return t;
 }
 
 // ------------------------------------------------------------------ group
-// Inclusive scan of three counters over the 1024 threads of the group kernel.
-struct I3 { int a, b, c; };
+// Inclusive scan of four counters over the 1024 threads of the group kernel.
+struct I3 { int a, b, c, d; };
 __device__ I3 block_scan3(I3 v, I3* wave_tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int a = __shfl_up(v.a, d), b = __shfl_up(v.b, d), c = __shfl_up(v.c, d);
-    if (lane >= d) { v.a += a; v.b += b; v.c += c; }
+    const int a = __shfl_up(v.a, d), b = __shfl_up(v.b, d), c = __shfl_up(v.c, d), e = __shfl_up(v.d, d);
+    if (lane >= d) { v.a += a; v.b += b; v.c += c; v.d += e; }
   }
   if (lane == 63) wave_tot[wave] = v;
   __syncthreads();
-  I3 base = {0, 0, 0};
-  for (int w = 0; w < wave; ++w) { base.a += wave_tot[w].a; base.b += wave_tot[w].b; base.c += wave_tot[w].c; }
-  v.a += base.a; v.b += base.b; v.c += base.c;
+  I3 base = {0, 0, 0, 0};
+  for (int w = 0; w < wave; ++w) {
+    base.a += wave_tot[w].a; base.b += wave_tot[w].b; base.c += wave_tot[w].c; base.d += wave_tot[w].d;
+  }
+  v.a += base.a; v.b += base.b; v.c += base.c; v.d += base.d;
   return v;
 }
 
@@ -286,6 +311,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
   uint32_t* masks = lds;                                        // [E, W]
   int* routes = reinterpret_cast<int*>(masks + static_cast<size_t>(E) * W);  // [E] route counts
   int* unit0 = routes + E;                                      // [E]
+  int* chunk0 = unit0 + E;                                      // [E]
   __shared__ I3 wave_tot[kGroupThreads / 64];
   __shared__ int flags;
   const int tid = threadIdx.x;
@@ -307,10 +333,14 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
     for (int w = 0; w < W; ++w) cnt += __popc(masks[tid * W + w]);
   if (tid < E && cnt != routes[tid]) atomicOr(&flags, 2);      // an id repeated in a token
   const int units = (cnt + 7) >> 3;
-  I3 v = {units, cnt > 0 ? 1 : 0, (units + 1) >> 1};
+  const int chunks = (cnt + kChunkCols - 1) / kChunkCols;
+  I3 v = {units, cnt > 0 ? 1 : 0, (units + 1) >> 1, chunks};
   const I3 inc = block_scan3(v, wave_tot);
-  const int u0 = inc.a - v.a, gi = inc.b - v.b, t0 = inc.c - v.c;
-  if (tid < E) unit0[tid] = u0;
+  const int u0 = inc.a - v.a, gi = inc.b - v.b, t0 = inc.c - v.c, c0 = inc.d - v.d;
+  if (tid < E) {
+    unit0[tid] = u0;
+    chunk0[tid] = c0;
+  }
   if (tid < E && cnt > 0) {
     tbl.g_expert[gi] = tid;
     tbl.g_unit0[gi] = u0;
@@ -318,6 +348,12 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
     tbl.g_tile0[gi] = t0;
     for (int u = 0; u < units; ++u) tbl.unit_expert[u0 + u] = tid;
     for (int s = cnt & 7; s != 0 && s < 8; ++s) tbl.unit_rows[(u0 + units - 1) * 8 + s] = -1;
+    for (int q = 0; q < chunks; ++q) {
+      tbl.c_expert[c0 + q] = tid;
+      tbl.c_ncols[c0 + q] = cnt - q * kChunkCols < kChunkCols ? cnt - q * kChunkCols : kChunkCols;
+    }
+    for (int col = cnt - (chunks - 1) * kChunkCols; col < kChunkCols; ++col)
+      tbl.c_pairs[(c0 + chunks - 1) * kChunkCols + col] = -1;
   }
   __syncthreads();
   if (tid == kGroupThreads - 1) {
@@ -325,6 +361,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
     tbl.hdr[1] = inc.b;
     tbl.hdr[2] = inc.c;
     tbl.hdr[3] = flags;
+    tbl.hdr[4] = inc.d;
   }
   for (int r = tid; r < U; r += kGroupThreads) {
     const int e = ids[r];
@@ -334,6 +371,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
     int rank = __popc(m[t >> 5] & ((1u << (t & 31)) - 1u));
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(m[w]);
     tbl.unit_rows[(unit0[e] + (rank >> 3)) * 8 + (rank & 7)] = r;
+    tbl.c_pairs[(chunk0[e] + rank / kChunkCols) * kChunkCols + rank % kChunkCols] = r;
   }
 }
 
@@ -451,6 +489,7 @@ constexpr int kMaxGroups = 1024;   // distinct experts per call (E <= 1024)
 struct WsLayout {
   size_t calls, status, arrive, flags, hcodes, hscales, partials;
   size_t qcalls, qhq;  // decode form with whole-K FC1 blocks
+  size_t gcalls, gflags, ghid;  // grouped form with whole-K FC1 blocks
   size_t end;
   int64_t max_tiles, max_blocks;
   int64_t dec_slots;  // decode-form partial-sum slots (512 tagged pairs each)
@@ -505,6 +544,16 @@ WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   off = align256(off + kMaxGrid * 4);
   L.qhq = off;
   off = align256(off + static_cast<size_t>(128) * 8 * (IP / 4 + 16) * 8);
+  // grouped form with whole-K FC1 blocks: its call counters, a call-tagged flag per
+  // (chunk, hidden block) and the published hidden, [chunk][32 columns][IP + 16] (plus 1
+  // KB that the loader's 1 KB DMA pieces may read past the last chunk)
+  const int64_t chunks = max_chunks_for(U, U < E ? U : E);
+  L.gcalls = off;
+  off = align256(off + kMaxGrid * 4);
+  L.gflags = off;
+  off = align256(off + static_cast<size_t>(chunks) * HB * 4);
+  L.ghid = off;
+  off = align256(off + static_cast<size_t>(chunks) * kChunkCols * (IP + 16) + 1024);
   L.end = off;
   return L;
 }
@@ -2452,7 +2501,8 @@ struct QWork {
   int TPE, nwg, c;
 };
 
-__device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int D, int nwg, int c, int w, int item) {
+__device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int D, int nwg, int c, int w, int item,
+                                        int nst = kQStream) {
   QWork q;
   const int N1 = G * HB;
   q.nwg = nwg;
@@ -2461,7 +2511,7 @@ __device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int D, int nwg, 
   const int N2 = G * q.TPE;
   const int r1 = N1 % nwg;  // workgroups c < r1 hold one FC1 item more
   q.n1 = N1 / nwg + (c < r1 ? 1 : 0);
-  q.m1 = w < NS1 ? (NS1 - w + kQStream - 1) / kQStream : 0;
+  q.m1 = w < NS1 ? (NS1 - w + nst - 1) / nst : 0;
   // FC2 tiles: contiguous runs in expert-major order.  When every workgroup has FC1
   // items and some have one more, those come last with `item` tiles fewer (an FC1 item
   // streams as long as that many FC2 tiles): they take the experts that finish last,
@@ -3004,6 +3054,653 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   }
 }
 
+// =================================================================== grouped form, whole-K FC1 blocks
+// moe_experts_run's default.  The unit table cuts each expert's routes, in token order,
+// into chunks of kChunkCols = 32 token columns (two MFMA column tiles); one weight pass
+// of an expert serves a whole chunk.  One persistent, co-resident workgroup per CU:
+// four streaming waves, a finisher wave and a loader wave.
+//   * an FC1 item is one hidden block of one chunk: the 64 weight rows gate 32j.. and up
+//     I + 32j.. over the whole of K, against the chunk's token columns.  Items are dealt
+//     round-robin over the workgroups, numbered so that the blocks of one chunk land on
+//     workgroups of one XCD (whose L2 then serves the chunk's x to all of them);
+//     streaming wave w takes the K steps w, w + 4, ... of each and keeps FP32 partial
+//     tiles for it.  The finisher adds the four waves' tiles in wave order, applies SwiGLU
+//     and the MXFP8 requantization (experts page, ExpertsKernel.store_hidden), stores the
+//     block's codes and scales device-coherently and then raises the block's flag with the
+//     call number.  No FC1 partial sum leaves the workgroup.
+//   * FC2 is dealt as 16-row output tiles, a contiguous run per workgroup in chunk order
+//     (experts page, ExpertsKernel.partition: contiguous near-equal shares of the weight
+//     stream; workgroups with one FC1 item more take fewer, last tiles).  The loader
+//     waits for a chunk's HB flags and copies its hidden into LDS by device-coherent DMA.
+//   * each streaming wave has one LDS DMA ring of three 8.5 KB slots: an FC1 K step (four
+//     1 KB row tiles and their scale word, then the x operands of the chunk's two column
+//     tiles, gathered per lane from the plan) or two FC2 tiles (NS2 1 KB K steps and a
+//     scale word each).  Every slot is ten DMA instructions (out-of-range ones write
+//     zeros and read no memory), so the wait before a slot depends only on how many of the
+//     last three slots stored output rows.
+constexpr int kGTiles = kChunkCols / 16;  // column tiles of a chunk
+constexpr int kGStream = 4;               // streaming waves
+constexpr int kGR = 3;                    // slots per streaming wave
+constexpr int kGHalf = 4096 + 256;        // half a slot: four 1 KB pieces and a scale word
+constexpr int kGSlot = 2 * kGHalf;
+constexpr int kGOps = 10;                 // DMA instructions per slot
+constexpr int kGStores = 4;               // row stores after an FC2 slot (2 tiles x 2 column tiles)
+constexpr int kGFin = kGStream;           // the finisher wave
+constexpr int kGLoad = kGStream + 1;      // the loader wave
+constexpr int kGWG = 64 * (kGStream + 2);
+constexpr int kGItems = 32;               // FC1 items per workgroup (LDS token table)
+constexpr int kGChunks = 1024;            // chunks per call (LDS expert table)
+
+constexpr uint32_t kGProg = 0;     // [kGStream] FC1 items whose partial tiles wave w has written
+constexpr uint32_t kGProg2 = 32;   // [kGStream] wave w is done with every FC2 chunk sequence < value
+constexpr uint32_t kGCons = 64;    // FC1 items whose partial tiles the finisher has read
+constexpr uint32_t kGReady = 68;   // FC2 chunk sequences loaded into the hidden buffers
+constexpr uint32_t kGCall = 72;    // this call's number
+constexpr uint32_t kGExp = 128;    // [kGChunks] u16 expert of chunk ch
+constexpr uint32_t kGTok = kGExp + 2 * kGChunks;  // [kGItems][32] u16 token of item k's column (0xffff: padded)
+constexpr uint32_t kGTables = kGTok + 2 * kGItems * kChunkCols;
+
+struct GArgs {
+  const uint8_t* w13p;
+  const uint8_t* s13p;
+  const uint8_t* w2p;
+  const uint8_t* s2p;
+  const uint8_t* plan;      // x codes [B, D], then scales [B, D/32]
+  const int32_t* hdr;       // unit table header (n_chunks at [4])
+  const int32_t* c_expert;  // [max_chunks]
+  const int32_t* c_pairs;   // [max_chunks][32]
+  uint16_t* out;            // BF16 [B*K, D]
+  uint8_t* hid;             // [max_chunks][32 columns][IP + 16]: IP code bytes, then HB scales
+  uint32_t* flags;          // [max_chunks * HB] call-tagged
+  uint32_t* calls;          // [kMaxGrid] per-workgroup call counters
+  int32_t* err;             // status word (bit 2: a wait gave up)
+  uint8_t* dump_codes;      // optional [B*K, I]
+  uint8_t* dump_scales;     // optional [B*K, I/32]
+  int B, K, D, I, HB, NS1, IP, floor_rule, max_chunks;
+  uint32_t plan_bytes;      // bytes of the plan (x codes, then x scales)
+  uint32_t out_bytes;       // bytes of the output rows
+  uint32_t colb;            // bytes of one hidden column (IP + 16)
+  uint32_t o_ring, o_red, o_hid, hid_bytes, hid_code_bytes;  // LDS: ring, partial tiles, hidden buffers
+};
+
+__device__ __forceinline__ int lds_u16(uint32_t addr) {
+  return static_cast<int>(lds_ld2(addr) & 0xffffu);
+}
+
+// FC1 item i -> (chunk, hidden block).  The HB items of a chunk get indices congruent mod
+// 8 (in the chunk groups of eight; the last, partial group is interleaved), so that with
+// item i dealt to workgroup i mod grid they run on workgroups of one XCD (workgroup c runs
+// on XCD c mod 8).
+__device__ __forceinline__ void g_item(int i, int n_chunks, int HB, int& ch, int& j) {
+  const int full = (n_chunks >> 3) * 8 * HB;
+  if (i < full) {
+    const int g = i / (8 * HB), r = i - g * 8 * HB;
+    j = r >> 3;
+    ch = 8 * g + (r & 7);
+  } else {
+    const int rem = n_chunks & 7, i2 = i - full;
+    j = i2 / rem;
+    ch = (n_chunks & ~7) + (i2 - j * rem);
+  }
+}
+
+// Bounded LDS wait of the streaming waves.  They wait only on words that their own
+// workgroup's finisher and loader post, whose own waits are bounded, so it reads no
+// global memory (a global read would wait for the wave's ring); its own bound (~1 s) is a
+// last resort.
+__device__ __forceinline__ void g_wait_lds(uint32_t addr, int want, int32_t* err) {
+#pragma unroll 1
+  for (uint32_t spins = 0;; ++spins) {
+    if (lds_uni(addr) >= want) return;
+    if (spins == (1u << 24)) {
+      if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Bounded LDS wait of the finisher and the loader: gives up (status bit 2) after ~0.1 s,
+// or soon after another wave of the call has given up.
+__device__ __forceinline__ void g_wait(uint32_t addr, int want, int32_t* err) {
+#pragma unroll 1
+  for (uint32_t spins = 0;; ++spins) {
+    if (lds_uni(addr) >= want) return;
+    if ((spins & 1023u) == 1023u) {
+      const bool stop = spins >= (1u << 20) || (ld_dev_u32(err) & 4u) != 0;
+      if (stop) {
+        if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// A cursor over a streaming wave's slot sequence: its FC1 K steps item by item, then its
+// FC2 tiles two per slot (tiles w, w + 4, ... of the workgroup's run), then the end.
+struct GCursor {
+  int k;            // slot index
+  int item, si;     // FC1: item of the workgroup, this wave's step index within it
+  int e, j;         // FC1: expert and hidden block of the current item
+  int t0, t1;       // FC1 (issue side): the lane's token in column tile 0 / 1 (-1: padded)
+  int ti;           // FC2: the wave's tile index of the slot's first tile
+  int chunk, rt2;   // FC2: chunk and 16-row tile of that tile
+};
+
+__device__ __forceinline__ void g_cursor_init(GCursor& c) {
+  c.k = c.item = c.si = c.e = c.j = c.ti = 0;
+  c.t0 = c.t1 = -1;
+  c.chunk = c.rt2 = 0;
+}
+
+// The tile kGStream positions further in the workgroup's run.
+__device__ __forceinline__ void g_next_tile(int TPE, int& chunk, int& rt2) {
+  rt2 += kGStream;
+#pragma unroll 1
+  while (rt2 >= TPE) {
+    rt2 -= TPE;
+    ++chunk;
+  }
+}
+
+// Moves the cursor to its next slot, reading the per-item state (the chunk's expert and
+// the block; the issue side also the lane's tokens) when it enters an FC1 item.  Every
+// field is computed into a local and stored once (stores to different fields in
+// different branches would otherwise be merged through a pointer, which puts the cursor
+// in scratch memory).
+__device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t lb, int w, int m1, int n1el,
+                                       int n_el, int n_chunks, GCursor& c, bool tokens) {
+  const int l = threadIdx.x & 63;
+  int k = c.k + 1, item = c.item, si = c.si, e = c.e, j = c.j, t0 = c.t0, t1 = c.t1, ti = c.ti;
+  int chunk = c.chunk, rt2 = c.rt2;
+  if (c.k < n1el) {
+    if (++si == m1) {
+      si = 0;
+      ++item;
+    }
+  } else if (c.k < n_el) {
+    ti += 2;
+    g_next_tile(q.TPE, chunk, rt2);
+    g_next_tile(q.TPE, chunk, rt2);
+  }
+  if (k < n1el && si == 0) {  // entering an FC1 item
+    int ch;
+    g_item(q.c + item * q.nwg, n_chunks, a.HB, ch, j);
+    e = __builtin_amdgcn_readfirstlane(lds_u16(lb + kGExp + 2 * ch));
+    if (tokens) {
+      const uint32_t tb = lb + kGTok + static_cast<uint32_t>(item * kChunkCols * 2);
+      const int u0 = lds_u16(tb + 2 * (l & 15)), u1 = lds_u16(tb + 2 * (16 + (l & 15)));
+      t0 = u0 == 0xffff ? -1 : u0;
+      t1 = u1 == 0xffff ? -1 : u1;
+    }
+  } else if (k == n1el && k < n_el) {  // entering the FC2 run
+    const int t = q.first2 + w;
+    ti = 0;
+    chunk = t / q.TPE;
+    rt2 = t - chunk * q.TPE;
+  }
+  c.k = k;
+  c.item = item;
+  c.si = si;
+  c.e = e;
+  c.j = j;
+  c.t0 = t0;
+  c.t1 = t1;
+  c.ti = ti;
+  c.chunk = chunk;
+  c.rt2 = rt2;
+}
+
+// Sets the cursor on slot 0 (the same per-item reads as g_step).
+__device__ __forceinline__ void g_start(const GArgs& a, const QWork& q, uint32_t lb, int w, int n1el, int n_el,
+                                        int n_chunks, GCursor& c, bool tokens) {
+  const int l = threadIdx.x & 63;
+  g_cursor_init(c);
+  if (0 < n1el) {
+    int ch;
+    g_item(q.c, n_chunks, a.HB, ch, c.j);
+    c.e = __builtin_amdgcn_readfirstlane(lds_u16(lb + kGExp + 2 * ch));
+    if (tokens) {
+      const int u0 = lds_u16(lb + kGTok + 2 * (l & 15)), u1 = lds_u16(lb + kGTok + 2 * (16 + (l & 15)));
+      c.t0 = u0 == 0xffff ? -1 : u0;
+      c.t1 = u1 == 0xffff ? -1 : u1;
+    }
+  } else if (0 < n_el) {
+    const int t = q.first2 + w;
+    c.chunk = t / q.TPE;
+    c.rt2 = t - c.chunk * q.TPE;
+  }
+}
+
+// The slot at cursor c: always kGOps DMA instructions.
+template <int NS2>
+__device__ __forceinline__ void g_issue(const GArgs& a, const QWork& q, uint32_t lb, int w, int n1el, int n_el,
+                                        int n2w, const GCursor& c, __amdgpu_buffer_rsrc_t rx,
+                                        __amdgpu_buffer_rsrc_t none) {
+  const int l = threadIdx.x & 63, g = l >> 4;
+  const uint32_t so = a.o_ring + static_cast<uint32_t>((w * kGR + c.k % kGR) * kGSlot);
+  if (c.k < n1el) {
+    // four row tiles and their scale word ...
+    const int s = w + kGStream * c.si;
+    const int64_t step = (static_cast<int64_t>(c.e) * a.HB + c.j) * a.NS1 + s;
+    const uint8_t* wb = a.w13p + step * 4096 + l * 16;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(wb + t * 1024, so + t * 1024);
+    dma4(a.s13p + step * 256 + l * 4, so + 4096);
+    // ... then the x operands: codes of column l % 16 at K 16g.. and 64 + 16g.. of the
+    // step for column tiles 0 and 1, and the scale word of column l (lanes 0-31; the tokens
+    // of columns l & 15 and 16 + (l & 15) are this lane's t0 and t1)
+    const int t0 = c.t0, t1 = c.t1;
+    const uint32_t x0 = t0 >= 0 ? static_cast<uint32_t>(t0 * a.D + 128 * s + 16 * g) : kOutside;
+    const uint32_t x1 = t1 >= 0 ? static_cast<uint32_t>(t1 * a.D + 128 * s + 16 * g) : kOutside;
+    const int lo = l < 16 ? 1 : 0;
+    const int tcol = lo * t0 + (1 - lo) * t1;
+    const uint32_t xs = l < 32 && tcol >= 0 ? static_cast<uint32_t>(a.B * a.D + tcol * (a.D / 32) + 4 * s) : kOutside;
+    bdma16(rx, x0, so + kGHalf);
+    bdma16(rx, x0 == kOutside ? kOutside : x0 + 64, so + kGHalf + 1024);
+    bdma16(rx, x1, so + kGHalf + 2048);
+    bdma16(rx, x1 == kOutside ? kOutside : x1 + 64, so + kGHalf + 3072);
+    bdma4(rx, xs, so + kGHalf + 4096);
+  } else if (c.k < n_el) {
+    // two FC2 tiles of the wave's sequence (the second may lie past it: nothing loaded)
+    int chunk = c.chunk, rt2 = c.rt2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t sh = so + h * kGHalf;
+      if (c.ti + h < n2w) {
+        const int e = __builtin_amdgcn_readfirstlane(lds_u16(lb + kGExp + 2 * chunk));
+        const int64_t tile = static_cast<int64_t>(e) * q.TPE + rt2;
+        const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
+#pragma unroll
+        for (int ks = 0; ks < NS2; ++ks) dma16(wb + ks * 1024, sh + ks * 1024);
+#pragma unroll
+        for (int ks = NS2; ks < 4; ++ks) bdma16(none, kOutside, sh + ks * 1024);
+        dma4(a.s2p + tile * 256 + l * 4, sh + 4096);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) bdma16(none, kOutside, sh + ks * 1024);
+        bdma4(none, kOutside, sh + 4096);
+      }
+      g_next_tile(q.TPE, chunk, rt2);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) bdma16(none, kOutside, so + h * kGHalf + ks * 1024);
+      bdma4(none, kOutside, so + h * kGHalf + 4096);
+    }
+  }
+}
+
+// The BF16 row pieces of one FC2 tile, stored after the slot's refill is issued.
+struct GRows {
+  uint2 v0, v1;        // column tile 0 / 1: four BF16 values of the lane's output row
+  uint32_t off0, off1; // their byte offsets in the output (out of range: not written)
+};
+
+__device__ __forceinline__ void g_store_rows(const GRows& r, __amdgpu_buffer_rsrc_t rout) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, r.v0), rout, static_cast<int>(r.off0), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, r.v1), rout, static_cast<int>(r.off1), 0, 0);
+}
+
+// One FC2 tile from half a slot against the hidden of its chunk: 16 output rows x the
+// chunk's two column tiles (the second skipped for a chunk of <= 16 columns).  Past the
+// wave's sequence it computes nothing and both row offsets are out of range.
+template <int NS2>
+__device__ __forceinline__ GRows g_fc2_tile(const GArgs& a, uint32_t lb, int w, int g0, bool live_tile, int chunk,
+                                            int rt2, uint32_t sh, int& seq_cur, uint32_t& hbl, uint32_t& hbs,
+                                            int& orow0, int& orow1) {
+  const int l = threadIdx.x & 63, grp = l >> 4, col = l & 15;
+  v4f o0 = v4f{0.f, 0.f, 0.f, 0.f}, o1 = v4f{0.f, 0.f, 0.f, 0.f};
+  bool second = false;
+  if (live_tile) {
+    const int seq = chunk - g0;
+    if (seq != seq_cur) {
+      seq_cur = seq;
+      if (l == 0) lds_st4(lb + kGProg2 + 4 * w, static_cast<uint32_t>(seq));
+      g_wait_lds(lb + kGReady, seq + 1, a.err);
+      const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(seq & 1) * a.hid_bytes;
+      hbl = hb + col * a.colb + 16 * grp;
+      hbs = hb + col * a.colb + a.IP;
+      const int p0 = static_cast<int>(lds_ld4(hb + a.hid_code_bytes + 4 * col));
+      const int p1 = static_cast<int>(lds_ld4(hb + a.hid_code_bytes + 4 * (16 + col)));
+      orow0 = p0 >= 0 ? p0 * a.D : -1;
+      orow1 = p1 >= 0 ? p1 * a.D : -1;
+    }
+    uint4 wa0, wa1, wa2, wa3;
+    uint32_t was;
+    asm volatile(
+        "ds_read_b128 %0, %5 offset:0\n\t"
+        "ds_read_b128 %1, %5 offset:1024\n\t"
+        "ds_read_b128 %2, %5 offset:2048\n\t"
+        "ds_read_b128 %3, %5 offset:3072\n\t"
+        "ds_read_b32 %4, %6 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(wa0), "=&v"(wa1), "=&v"(wa2), "=&v"(wa3), "=&v"(was)
+        : "v"(sh + l * 16), "v"(sh + l * 4)
+        : "memory");
+    const uint4 wa[4] = {wa0, wa1, wa2, wa3};
+    {
+      HidOps<NS2> hop;
+      hid_read<NS2>(hbl, hbs, hop);
+      // K-blocks past I hold zero codes (weights and hidden)
+#pragma unroll
+      for (int s = 0; s < NS2; ++s)
+        o0 = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(hop.bl[s], hop.bh[s]), o0,
+                          static_cast<int>((was >> (8 * s)) & 0xffu), static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu));
+    }
+    second = __any(orow1 >= 0);  // a chunk of <= 16 columns skips its second column tile
+    if (second) {
+      HidOps<NS2> hop;
+      hid_read<NS2>(hbl + 16 * a.colb, hbs + 16 * a.colb, hop);
+#pragma unroll
+      for (int s = 0; s < NS2; ++s)
+        o1 = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(hop.bl[s], hop.bh[s]), o1,
+                          static_cast<int>((was >> (8 * s)) & 0xffu), static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu));
+    }
+    mfma_settle(o0);
+    mfma_settle(o1);
+  }
+  const uint32_t ro = static_cast<uint32_t>(16 * rt2 + 4 * grp) * 2;
+  GRows r;
+  r.off0 = live_tile && orow0 >= 0 ? static_cast<uint32_t>(orow0) * 2 + ro : kOutside;
+  r.off1 = live_tile && second && orow1 >= 0 ? static_cast<uint32_t>(orow1) * 2 + ro : kOutside;
+  r.v0 = make_uint2(bf16_pair(o0[0], o0[1]), bf16_pair(o0[2], o0[3]));
+  r.v1 = make_uint2(bf16_pair(o1[0], o1[1]), bf16_pair(o1[2], o1[3]));
+  return r;
+}
+
+template <int NS2>
+__global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  agpr_form();
+  const int tid = threadIdx.x, l = tid & 63, w = wave_id();
+  const int grp = l >> 4, col = l & 15;
+  const uint32_t lb = lds_base();
+  const int nwg = gridDim.x, c = blockIdx.x;
+  const int HB = a.HB, NS1 = a.NS1;
+  uint32_t* sw = reinterpret_cast<uint32_t*>(smem);
+
+  // ---- prologue: the chunk count, the chunks' experts and the token columns of this
+  // workgroup's FC1 items, all requested at once (read for every possible chunk: the
+  // table holds max_chunks records, and the item numbering depends on the chunk count)
+  if (tid < 32) sw[tid] = 0u;
+  const int n_chunks = a.hdr[4];
+  for (int ch = tid; ch < a.max_chunks && ch < kGChunks; ch += kGWG)
+    reinterpret_cast<uint16_t*>(smem + kGExp)[ch] = static_cast<uint16_t>(a.c_expert[ch]);
+  const int n1_cap = (n_chunks * HB - c + nwg - 1) / nwg;  // this workgroup's FC1 items
+  for (int idx = tid; idx < n1_cap * kChunkCols && idx < kGItems * kChunkCols; idx += kGWG) {
+    const int k = idx / kChunkCols, cl = idx - k * kChunkCols;
+    int ch, jj;
+    g_item(c + k * nwg, n_chunks, HB, ch, jj);
+    const int pr = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
+    reinterpret_cast<uint16_t*>(smem + kGTok)[idx] = static_cast<uint16_t>(pr >= 0 ? pr / a.K : 0xffff);
+  }
+  if (tid == 0) sw[kGCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
+  __syncthreads();
+
+  const int item_tiles = 34 * a.D / (NS2 * 1024 + 256);  // FC2 tiles that stream as long as one FC1 item
+  const QWork q = q_work(n_chunks, HB, NS1, a.D, nwg, c, w < kGStream ? w : 0, item_tiles, kGStream);
+  const int nw1 = NS1 < kGStream ? NS1 : kGStream;  // waves that take FC1 steps
+  const int g0 = q.first2 / q.TPE;  // chunk of the workgroup's first FC2 tile (sequence 0)
+  const __amdgpu_buffer_rsrc_t none =
+      __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
+
+  if (w < kGStream) {
+    // =============================================================== streaming wave
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.plan), static_cast<short>(0), static_cast<int>(a.plan_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<void*>(a.out), static_cast<short>(0), static_cast<int>(a.out_bytes), 0x00020000);
+    const int m1 = q.m1;
+    const int n1el = q.n1 * m1;
+    const int n2w = q.n2 > w ? (q.n2 - w + kGStream - 1) / kGStream : 0;  // the wave's FC2 tiles
+    const int n_el = n1el + (n2w + 1) / 2;                                 // two per slot
+    GCursor ic, cs;  // issue side (three slots ahead), consume side
+    g_start(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
+    g_start(a, q, lb, w, n1el, n_el, n_chunks, cs, false);
+    static_assert(kGR == 3, "the wait counts below assume three slots");
+#pragma unroll 1
+    for (int p = 0; p < kGR; ++p) {
+      g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
+      g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, ic, true);
+    }
+    v4f acc[4][kGTiles];
+    int ncc = 1, seq_cur = -1;
+    uint32_t hbl = 0, hbs = 0;
+    int orow0 = -1, orow1 = -1;
+#pragma unroll 1
+    for (int k = 0; k < n_el; ++k) {
+      // slot k has landed: younger are the two later slots and the row stores of the
+      // last three consumed slots (kGStores after each FC2 slot)
+      const int nf = k - n1el < 0 ? 0 : (k - n1el > 3 ? 3 : k - n1el);
+      if (nf == 0) wait_vm<2 * kGOps>();
+      else if (nf == 1) wait_vm<2 * kGOps + kGStores>();
+      else if (nf == 2) wait_vm<2 * kGOps + 2 * kGStores>();
+      else wait_vm<2 * kGOps + 3 * kGStores>();
+      const uint32_t sa = lb + a.o_ring + static_cast<uint32_t>((w * kGR + k % kGR) * kGSlot);
+      if (k < n1el) {
+        // ---- FC1 step: four row tiles x the chunk's column tiles
+        if (cs.si == 0) {
+          ncc = lds_u16(lb + kGTok + static_cast<uint32_t>((cs.item * kChunkCols + 16) * 2)) == 0xffff ? 1 : 2;
+          ncc = __builtin_amdgcn_readfirstlane(ncc);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int cc = 0; cc < kGTiles; ++cc) acc[rt][cc] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        const uint32_t sb = sa + kGHalf;
+        uint4 a0, a1, a2, a3, xl, xh;
+        uint32_t as, xs;
+        asm volatile(
+            "ds_read_b128 %0, %8 offset:0\n\t"
+            "ds_read_b128 %1, %8 offset:1024\n\t"
+            "ds_read_b128 %2, %8 offset:2048\n\t"
+            "ds_read_b128 %3, %8 offset:3072\n\t"
+            "ds_read_b32 %4, %9 offset:4096\n\t"
+            "ds_read_b128 %5, %10 offset:0\n\t"
+            "ds_read_b128 %6, %10 offset:1024\n\t"
+            "ds_read_b32 %7, %11 offset:4096\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(as), "=&v"(xl), "=&v"(xh), "=&v"(xs)
+            : "v"(sa + l * 16), "v"(sa + l * 4), "v"(sb + l * 16), "v"(sb + col * 4)
+            : "memory");
+        const uint4 av[4] = {a0, a1, a2, a3};
+        {
+          const v8i b = fp8_operand(xl, xh);
+          const int sbv = static_cast<int>((xs >> (8 * grp)) & 0xffu);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+            acc[rt][0] = mfma_fp4_fp8(fp4_operand(av[rt]), b, acc[rt][0], static_cast<int>((as >> (8 * rt)) & 0xffu), sbv);
+        }
+        if (ncc > 1) {
+          uint4 yl, yh;
+          uint32_t ys;
+          asm volatile(
+              "ds_read_b128 %0, %3 offset:2048\n\t"
+              "ds_read_b128 %1, %3 offset:3072\n\t"
+              "ds_read_b32 %2, %4 offset:4160\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(yl), "=&v"(yh), "=&v"(ys)
+              : "v"(sb + l * 16), "v"(sb + col * 4)
+              : "memory");
+          const v8i b = fp8_operand(yl, yh);
+          const int sbv = static_cast<int>((ys >> (8 * grp)) & 0xffu);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+            acc[rt][1] = mfma_fp4_fp8(fp4_operand(av[rt]), b, acc[rt][1], static_cast<int>((as >> (8 * rt)) & 0xffu), sbv);
+        }
+        // refill the slot just consumed (three slots ahead)
+        g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
+        g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, ic, true);
+        if (cs.si == m1 - 1) {
+          // the wave's part of the item is done: hand its partial tiles to the finisher once
+          // it has taken the previous ones
+#pragma unroll
+          for (int cc = 0; cc < kGTiles; ++cc) mfma_settle(acc[0][cc], acc[1][cc], acc[2][cc], acc[3][cc]);
+          g_wait_lds(lb + kGCons, cs.item, a.err);
+          const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(w * 4 * kGTiles * 1024 + l * 16);
+#pragma unroll
+          for (int cc = 0; cc < kGTiles; ++cc)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+              lds_st16_async(rd + (cc * 4 + rt) * 1024,
+                             make_uint4(__float_as_uint(acc[rt][cc][0]), __float_as_uint(acc[rt][cc][1]),
+                                        __float_as_uint(acc[rt][cc][2]), __float_as_uint(acc[rt][cc][3])));
+          lds_settle_all();
+          if (l == 0) lds_st4(lb + kGProg + 4 * w, static_cast<uint32_t>(cs.item + 1));
+        }
+      } else {
+        // ---- two FC2 tiles, computed before the refill overwrites the slot; the refill
+        // is issued first, then the four row stores
+        const int ti = cs.ti, chunk0 = cs.chunk, rt20 = cs.rt2;
+        int chunk1 = chunk0, rt21 = rt20;
+        g_next_tile(q.TPE, chunk1, rt21);
+        const GRows r0 = g_fc2_tile<NS2>(a, lb, w, g0, ti < n2w, chunk0, rt20, sa, seq_cur, hbl, hbs, orow0, orow1);
+        const GRows r1 =
+            g_fc2_tile<NS2>(a, lb, w, g0, ti + 1 < n2w, chunk1, rt21, sa + kGHalf, seq_cur, hbl, hbs, orow0, orow1);
+        g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
+        g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, ic, true);
+        g_store_rows(r0, rout);
+        g_store_rows(r1, rout);
+      }
+      g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, cs, false);
+    }
+    if (l == 0) lds_st4(lb + kGProg2 + 4 * w, 0x7fffffffu);
+    wait_vm<0>();  // the dummy slots land before the wave ends
+    return;
+  }
+
+  const uint32_t call = static_cast<uint32_t>(lds_uni(lb + kGCall));
+  if (w == kGFin) {
+    // =============================================================== finisher wave
+#pragma unroll 1
+    for (int k = 0; k < q.n1; ++k) {
+      int ch, j;
+      g_item(q.c + k * q.nwg, n_chunks, HB, ch, j);
+      const int ncc = lds_u16(lb + kGTok + static_cast<uint32_t>((k * kChunkCols + 16) * 2)) == 0xffff ? 1 : 2;
+      v4f tot[kGTiles][4];
+#pragma unroll
+      for (int cc = 0; cc < kGTiles; ++cc)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) tot[cc][rt] = v4f{0.f, 0.f, 0.f, 0.f};
+      // each wave's partial tiles are added (in wave order) as soon as it posts them
+#pragma unroll 1
+      for (int ww = 0; ww < nw1; ++ww) {
+        g_wait(lb + kGProg + 4 * ww, k + 1, a.err);
+        const uint32_t rw = lb + a.o_red + static_cast<uint32_t>(ww * 4 * kGTiles * 1024 + l * 16);
+#pragma unroll
+        for (int cc = 0; cc < kGTiles; ++cc) {
+          if (cc < ncc) {
+            uint4 p0, p1, p2, p3;
+            lds_ld16x4v(rw + cc * 4096, rw + cc * 4096 + 1024, rw + cc * 4096 + 2048, rw + cc * 4096 + 3072, p0, p1,
+                        p2, p3);
+            const uint4 p[4] = {p0, p1, p2, p3};
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              tot[cc][rt][0] += __uint_as_float(p[rt].x);
+              tot[cc][rt][1] += __uint_as_float(p[rt].y);
+              tot[cc][rt][2] += __uint_as_float(p[rt].z);
+              tot[cc][rt][3] += __uint_as_float(p[rt].w);
+            }
+          }
+        }
+      }
+      if (l == 0) lds_st4(lb + kGCons, static_cast<uint32_t>(k + 1));
+      // SwiGLU and MXFP8 of the block (experts page, store_hidden): lane (col, grp) holds
+      // hidden values 32j + 4grp + r (tile 0) and 32j + 16 + 4grp + r (tile 1) of column col
+#pragma unroll
+      for (int cc = 0; cc < kGTiles; ++cc) {
+        if (cc >= ncc) continue;
+        float h[2][4];
+        float amax = 0.0f;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gv = tot[cc][half][r], uv = tot[cc][2 + half][r];
+            // SwiGLU with the hardware exponential and reciprocal (a few ulp in FP32; the
+            // hidden is then rounded to 3 mantissa bits)
+            h[half][r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+            amax = fmaxf(amax, fabsf(h[half][r]));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int e = mx_exponent(amax, a.floor_rule != 0);
+        const float sc = exp2_neg(e);
+        uint32_t word[2];
+        auto clampf = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };  // the floor rule saturates
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          word[half] = cvt4_e4m3(clampf(h[half][0] * sc), clampf(h[half][1] * sc), clampf(h[half][2] * sc),
+                                 clampf(h[half][3] * sc));
+        const int cl = cc * 16 + col;
+        uint8_t* dst = a.hid + (static_cast<int64_t>(ch) * kChunkCols + cl) * a.colb;
+        st_dev_u32(dst + 32 * j + 4 * grp, word[0]);
+        st_dev_u32(dst + 32 * j + 16 + 4 * grp, word[1]);
+        if (grp == 0) st_dev_u8(dst + a.IP + j, static_cast<uint8_t>(e + 127));
+        if (a.dump_codes != nullptr) {
+          const int pair = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
+          if (pair >= 0) {
+            uint8_t* dc = a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 4 * grp;
+            *reinterpret_cast<uint32_t*>(dc) = word[0];
+            *reinterpret_cast<uint32_t*>(dc + 16) = word[1];
+            if (grp == 0) a.dump_scales[static_cast<int64_t>(pair) * HB + j] = static_cast<uint8_t>(e + 127);
+          }
+        }
+      }
+      // publish: the block's codes and scales (sc1) before its flag
+      wait_stores();
+      if (l == 0) st_dev_u32(a.flags + static_cast<int64_t>(ch) * HB + j, call);
+    }
+    // the call counters for the next call (every counter c, c + grid, ... below kMaxGrid,
+    // so that all stay equal whatever grid the next call uses)
+#pragma unroll 1
+    for (int m = c + l * nwg; m < kMaxGrid; m += 64 * nwg) st_dev_u32(a.calls + m, call);
+    return;
+  }
+  // ================================================================= loader wave
+  // FC2: for each chunk of the workgroup's run, in order: wait for its HB block flags,
+  // then copy its hidden (codes and scales, device-coherent DMA) and its columns' pair
+  // indices into one of the two LDS hidden buffers.  The buffers share LDS with the FC1
+  // partial tiles, so the first copy waits until the finisher has read the last of them.
+  const int nseq = q.n2 > 0 ? (q.first2 + q.n2 - 1) / q.TPE - g0 + 1 : 0;
+  if (nseq > 0) g_wait(lb + kGCons, q.n1, a.err);
+#pragma unroll 1
+  for (int seq = 0; seq < nseq; ++seq) {
+    const int ch = g0 + seq;
+    if (seq >= 2) {
+#pragma unroll 1
+      for (int ww = 0; ww < kGStream; ++ww) g_wait(lb + kGProg2 + 4 * ww, seq - 1, a.err);
+    }
+    const uint32_t* f = a.flags + static_cast<int64_t>(ch) * HB;
+#pragma unroll 1
+    for (uint32_t spins = 0;; ++spins) {
+      const bool ok = l >= HB || ld_dev_u32(f + l) == call;
+      if (__all(ok)) break;
+      if ((spins & 255u) == 255u && (spins >= (1u << 16) || (ld_dev_u32(a.err) & 4u) != 0)) {
+        if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    compiler_fence();
+    const uint32_t hb = a.o_hid + static_cast<uint32_t>(seq & 1) * a.hid_bytes;  // offset from smem
+    const uint8_t* src = a.hid + static_cast<int64_t>(ch) * kChunkCols * a.colb;
+    for (uint32_t off = 0; off < a.hid_code_bytes; off += 1024)
+      __builtin_amdgcn_global_load_lds(src + off + l * 16, (lds_void*)(smem + hb + off), 16, 0, 16 /* sc1 */);
+    if (l < kChunkCols) {
+      const int pr = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + l];
+      lds_st4(lb + hb + a.hid_code_bytes + 4 * l, static_cast<uint32_t>(pr));
+    }
+    wait_vm<0>();
+    lds_settle_all();
+    if (l == 0) lds_st4(lb + kGReady, static_cast<uint32_t>(seq + 1));
+  }
+}
+
 using ExpertsFn = void (*)(ExpArgs);
 
 template <int R, bool DEC, bool TAG>
@@ -3100,6 +3797,9 @@ int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP
 int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids, int32_t B,
                      int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream);
 bool whole_fits(const moe_weights_t* wts, int32_t B, int32_t topk);
+bool grouped_fits(int E, int I, int B, int K, int grid);
+int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, int32_t B,
+                int32_t topk, void* ws, size_t ws_bytes, void* out, void* stream);
 
 // Checks, kernel variant, grid and arguments shared by both forms; enqueues one launch.
 template <bool DEC>
@@ -3114,7 +3814,7 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   moe_run_opts_t o;
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
-  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 1) ||
+  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || o.col_tiles < 0 || o.col_tiles > (DEC ? 1 : 2) ||
       (o.ring != 0 && (o.ring < 2 || o.ring > 4)) ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
     return MOE_EINVAL;
@@ -3129,6 +3829,11 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   // else finished split blocks
   if (DEC && o.exchange == 0 && whole_fits(wts, B, topk))
     return run_decode_whole(wts, o, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
+  // the grouped form's default: whole-K FC1 blocks over 32-column chunks (col_tiles 0 or 2)
+  // where the batch fits its tables; col_tiles 1 asks for the split-block kernel
+  if (!DEC && o.col_tiles != 1 && grouped_fits(E, I, B, topk, o.grid ? o.grid : device_cus()))
+    return run_grouped(wts, o, plan, units, B, topk, ws, ws_bytes, out, stream);
+  if (!DEC && o.col_tiles == 2) return MOE_EINVAL;
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
   if (B_cap < B) return MOE_ENOSPACE;
   const WsLayout L = ws_layout(E, D, I, topk, B_cap);
@@ -3197,6 +3902,97 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   return launch_status();
 }
 
+
+// ------------------------------------------------- grouped form, whole-K FC1 blocks (host)
+using GFn = void (*)(GArgs);
+GFn pick_g(int ns2) {
+  switch (ns2) {
+    case 1: return grouped_kernel<1>;
+    case 2: return grouped_kernel<2>;
+    case 3: return grouped_kernel<3>;
+    default: return grouped_kernel<4>;
+  }
+}
+
+// The grouped kernel's limits: its LDS tables hold kGChunks chunks and kGItems FC1 items
+// per workgroup; I <= 512.
+bool grouped_fits(int E, int I, int B, int K, int grid) {
+  const int64_t U = static_cast<int64_t>(B) * K;
+  const int64_t chunks = max_chunks_for(U, U < E ? U : E);
+  const int64_t items = (chunks * (I / 32) + grid - 1) / grid;
+  return I <= 512 && chunks <= kGChunks && items <= kGItems;
+}
+
+int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, int32_t B,
+                int32_t topk, void* ws, size_t ws_bytes, void* out, void* stream) {
+  const int E = wts->E, D = wts->D, I = wts->I;
+  const int IP = (I + 127) / 128 * 128, ns2 = IP / 128, HB = I / 32, NS1 = D / 128;
+  const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
+  if (B_cap < B) return MOE_ENOSPACE;
+  const WsLayout L = ws_layout(E, D, I, topk, B_cap);
+  const UnitsLayout UL = units_layout(B, topk, E);
+  const uint32_t colb = static_cast<uint32_t>(IP + 16);
+  const uint32_t code_bytes = (kChunkCols * colb + 1023u) / 1024u * 1024u;
+  const uint32_t hid_bytes = code_bytes + 4u * kChunkCols;
+  const uint32_t o_ring = (kGTables + 15u) / 16u * 16u;
+  const uint32_t o_red = o_ring + kGStream * kGR * kGSlot;
+  const uint32_t o_hid = o_red;  // FC1's partial tiles, then FC2's hidden buffers
+  const uint32_t red_bytes = kGStream * 4 * kGTiles * 1024;
+  const size_t lds = o_hid + (2u * hid_bytes > red_bytes ? 2u * hid_bytes : red_bytes);
+  if (lds > static_cast<size_t>(device_lds_limit())) return MOE_EINVAL;
+  const GFn fn = pick_g(ns2);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(lds)) != hipSuccess)
+    return MOE_EHIP;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kGWG, lds) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  int cap = per_cu * device_cus();
+  if (cap > kMaxGrid) cap = kMaxGrid;
+  if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
+  const int grid = o.grid ? o.grid : cap;
+  if (!grouped_fits(E, I, B, topk, grid)) return MOE_EINVAL;
+
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint8_t* ub = static_cast<uint8_t*>(const_cast<void*>(units));
+  GArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.w13p = static_cast<const uint8_t*>(wts->w13);
+  a.s13p = static_cast<const uint8_t*>(wts->s13);
+  a.w2p = static_cast<const uint8_t*>(wts->w2);
+  a.s2p = static_cast<const uint8_t*>(wts->s2);
+  a.plan = static_cast<const uint8_t*>(plan);
+  a.hdr = reinterpret_cast<const int32_t*>(ub + UL.hdr);
+  a.c_expert = reinterpret_cast<const int32_t*>(ub + UL.c_expert);
+  a.c_pairs = reinterpret_cast<const int32_t*>(ub + UL.c_pairs);
+  a.out = static_cast<uint16_t*>(out);
+  a.hid = base + L.ghid;
+  a.flags = reinterpret_cast<uint32_t*>(base + L.gflags);
+  a.calls = reinterpret_cast<uint32_t*>(base + L.gcalls);
+  a.err = reinterpret_cast<int32_t*>(ub + UL.hdr) + 3;
+  a.dump_codes = static_cast<uint8_t*>(o.hidden_codes_dev);
+  a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
+  a.B = B;
+  a.K = topk;
+  a.D = D;
+  a.I = I;
+  a.HB = HB;
+  a.NS1 = NS1;
+  a.IP = IP;
+  a.floor_rule = o.hidden_rule == 2 || (o.hidden_rule == 0 && I == 384);
+  a.max_chunks = static_cast<int>(UL.max_chunks);
+  a.plan_bytes = static_cast<uint32_t>(static_cast<int64_t>(B) * D / 32 * 33);
+  a.out_bytes = static_cast<uint32_t>(static_cast<int64_t>(B) * topk * D * 2);
+  a.colb = colb;
+  a.o_ring = o_ring;
+  a.o_red = o_red;
+  a.o_hid = o_hid;
+  a.hid_bytes = hid_bytes;
+  a.hid_code_bytes = code_bytes;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kGWG), lds, as_stream(stream), a);
+  return launch_status();
+}
 
 // ------------------------------------------------- decode form, whole-K FC1 blocks (host)
 using QFn = void (*)(QArgs);
@@ -3466,7 +4262,7 @@ int moe_group(const int32_t* ids, int32_t B, int32_t topk, int32_t E, void* unit
       static_cast<int64_t>(B) * topk > 65536)
     return MOE_EINVAL;
   const int W = (B + 31) / 32;
-  const size_t lds = (static_cast<size_t>(E) * W + 2 * static_cast<size_t>(E)) * 4;
+  const size_t lds = (static_cast<size_t>(E) * W + 3 * static_cast<size_t>(E)) * 4;
   if (lds > 60 * 1024) return MOE_EINVAL;
   const UnitsLayout L = units_layout(B, topk, E);
   if (units_bytes < L.end) return MOE_ENOSPACE;
@@ -3482,7 +4278,7 @@ int moe_plan_group(const void* x, const int32_t* ids, int32_t B, int32_t D, int3
     return MOE_EINVAL;
   if (plan_bytes < moe_plan_bytes(B, D)) return MOE_ENOSPACE;
   const int W = (B + 31) / 32;
-  const size_t lds = (static_cast<size_t>(E) * W + 2 * static_cast<size_t>(E)) * 4;
+  const size_t lds = (static_cast<size_t>(E) * W + 3 * static_cast<size_t>(E)) * 4;
   if (lds > 60 * 1024) return MOE_EINVAL;
   const UnitsLayout L = units_layout(B, topk, E);
   if (units_bytes < L.end) return MOE_ENOSPACE;
@@ -3538,7 +4334,7 @@ int moe_decode_run_noalloc(const moe_weights_t* wts, const moe_run_opts_t* opts,
   moe_run_opts_t o;
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
-  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 1) ||
+  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || o.col_tiles < 0 || o.col_tiles > 1 ||
       (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.exchange != 0 ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)) ||
       (o.plan_bytes != 0 && o.plan_dev == nullptr))

@@ -69,17 +69,24 @@ class MoeLayer:
                              **opts)
         return out
 
-    def kernel_name(self, B: int, path: str = "auto", exchange: int | None = None) -> str:
-        """Name of the kernel that does a step's FC1/FC2 work (for reports): the decode form
-        runs decode_whole_kernel for batches within its limits (at most 128 distinct
+    def kernel_name(self, B: int, path: str = "auto", exchange: int | None = None, col_tiles: int = 0,
+                    grid: int = 0) -> str:
+        """Name of the kernel that does a step's FC1/FC2 work (for reports).  The decode
+        form runs decode_whole_kernel for batches within its limits (at most 128 distinct
         experts, B*topk <= 640, B*D/32 <= 2560, I <= 512) unless another exchange is asked
-        for; everything else runs experts_kernel."""
+        for.  The grouped form runs grouped_kernel where the batch fits its tables (I <=
+        512, at most 1024 chunks of 32 routes and 32 FC1 blocks per workgroup, with one
+        workgroup per compute unit unless a grid is given) unless col_tiles is 1.  Everything
+        else runs experts_kernel."""
         decode = path == "decode" or (path == "auto" and self.AUTO_DECODE and B <= self.DECODE_MAX)
         routes = B * self.topk
-        whole = (min(self.E, routes) <= 128 and routes <= 640 and B * self.D // 32 <= 2560 and self.I <= 512)
-        if decode and exchange in (None, 0) and whole:
-            return "decode_whole_kernel"
-        return "experts_kernel (decode form)" if decode else "experts_kernel"
+        if decode:
+            whole = (min(self.E, routes) <= 128 and routes <= 640 and B * self.D // 32 <= 2560 and self.I <= 512)
+            return "decode_whole_kernel" if exchange in (None, 0) and whole else "experts_kernel (decode form)"
+        chunks = min(self.E, routes) + (routes + 31) // 32
+        g = grid or min(torch.cuda.get_device_properties(self.device).multi_processor_count, 2048)
+        fits = self.I <= 512 and chunks <= 1024 and (chunks * (self.I // 32) + g - 1) // g <= 32
+        return "grouped_kernel" if col_tiles != 1 and fits else "experts_kernel"
 
     def experts(self, B: int, out: torch.Tensor, *, replica: int = 0, stream=None, **opts):
         """The experts kernel alone, on the plan and unit table of the last forward()."""

@@ -80,7 +80,7 @@ def test_host_side_argument_errors(m):
     o.col_tiles, o.hidden_rule = 0, 5
     assert run(1, 4, big, big, big) == m._lib.MOE_EINVAL
     o.hidden_rule = 0
-    o.col_tiles = 2     # one 16-column tile per weight pass is the only width
+    o.col_tiles = 3     # 0 (default), 1 (one-tile kernel) or 2 (grouped kernel only)
     assert run(1, 4, big, big, big) == m._lib.MOE_EINVAL
     o.col_tiles = 1
     for bad_ring in (1, 5, -1):
@@ -151,6 +151,11 @@ def test_decode_run_argument_checks(m):
     o = m.moe_run_opts_t()
     o.exchange = 3
     assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # no such exchange
+    o = m.moe_run_opts_t()
+    o.col_tiles = 2
+    assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # the grouped kernel is not a decode form
+    assert L.moe_decode_run_noalloc(ctypes.byref(w), ctypes.byref(o), fake, fake, 2, 4, fake, big,
+                                    None) == m._lib.MOE_EINVAL
     o = m.moe_run_opts_t()
     o.exchange = 1                                             # a decode-form option
     assert L.moe_experts_run(ctypes.byref(w), ctypes.byref(o), fake, fake, big, 1, 4, fake, big, fake, big,
