@@ -36,8 +36,8 @@
  *   out      BF16  [B*topk, D]
  * Supported shapes: 512 <= D <= 16384 with D % 512 == 0, 32 <= I <= 512 with
  * I % 32 == 0, 1 <= E <= 1024, 1 <= topk <= 64, 1 <= B*topk <= 65536; moe_group also
- * needs E * ceil(B/32) + 3E <= 15360 (its per-expert token bitmasks and counts live
- * in LDS).
+ * needs E * ceil(B/32) + 3E + C <= 15360 with C = min(E, B*topk) + ceil(B*topk/32)
+ * (its per-expert token bitmasks and counts and its per-chunk column counts live in LDS).
  */
 #ifndef MOE_MX_H
 #define MOE_MX_H

@@ -136,43 +136,40 @@ __device__ __forceinline__ v8i fp8_operand(uint4 lo, uint4 hi) {
 }
 
 // ------------------------------------------------------------------ plan
-// One thread per 32-element block of a token row (experts page, plan_chunk: the same
-// quantization as mx_block).  x: BF16 [B, D]; codes [B, D]; scales [B, D/32].
-__device__ __forceinline__ void plan_block(const uint8_t* __restrict__ x, int64_t idx, uint8_t* __restrict__ codes,
-                                           uint8_t* __restrict__ scales) {
-  const uint8_t* src = x + idx * 64;
-  uint32_t w[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 q = ld16(src + 16 * i);
-    w[4 * i + 0] = q.x; w[4 * i + 1] = q.y; w[4 * i + 2] = q.z; w[4 * i + 3] = q.w;
-  }
-  float v[32];
+// MXFP8 quantization of x (experts page, plan_chunk: the same quantization as mx_block),
+// four lanes per 32-element block of a token row: one 16-byte load and one 8-byte store
+// each, the block's amax combined across the four lanes.  x: BF16 [B, D]; codes [B, D];
+// scales [B, D/32]; idx4 = 4 * block + quarter.
+__device__ __forceinline__ void plan_quarter(const uint8_t* __restrict__ x, int64_t idx4, uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales) {
+  const uint4 q = ld16(x + idx4 * 16);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float v[8];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 4; ++i) {
     v[2 * i] = __uint_as_float(w[i] << 16);
     v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
   }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
   const int e = mx_exponent(amax, false);
-  const float s = exp2_neg(e);
-  uint32_t c[8];
+  const float sc = exp2_neg(e);
+  uint32_t c[2];
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    c[k] = to_e4m3(v[4 * k] * s) | (to_e4m3(v[4 * k + 1] * s) << 8) |
-           (to_e4m3(v[4 * k + 2] * s) << 16) | (to_e4m3(v[4 * k + 3] * s) << 24);
-  uint4* dst = reinterpret_cast<uint4*>(codes + idx * 32);
-  dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
-  dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
-  scales[idx] = static_cast<uint8_t>(e + 127);
+  for (int k = 0; k < 2; ++k)
+    c[k] = to_e4m3(v[4 * k] * sc) | (to_e4m3(v[4 * k + 1] * sc) << 8) | (to_e4m3(v[4 * k + 2] * sc) << 16) |
+           (to_e4m3(v[4 * k + 3] * sc) << 24);
+  *reinterpret_cast<uint2*>(codes + idx4 * 8) = make_uint2(c[0], c[1]);
+  if ((idx4 & 3) == 0) scales[idx4 >> 2] = static_cast<uint8_t>(e + 127);
 }
 
 __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ x, int64_t nblocks,
                                                    uint8_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx < nblocks) plan_block(x, idx, codes, scales);
+  const int64_t idx4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx4 < 4 * nblocks) plan_quarter(x, idx4, codes, scales);
 }
 
 // ------------------------------------------------------------------ combine
@@ -283,116 +280,213 @@ Table table_at(uint8_t* base, const UnitsLayout& L) {
 }
 
 // ------------------------------------------------------------------ group
-// Inclusive scan of four counters over the 1024 threads of the group kernel.
-struct I3 { int a, b, c, d; };
-__device__ I3 block_scan3(I3 v, I3* wave_tot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+constexpr int kGroupParts = 8;  // workgroups that build the unit table together
+
+// Inclusive scan over a wave (64 lanes).
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int a = __shfl_up(v.a, d), b = __shfl_up(v.b, d), c = __shfl_up(v.c, d), e = __shfl_up(v.d, d);
-    if (lane >= d) { v.a += a; v.b += b; v.c += c; v.d += e; }
+    const uint32_t o = __shfl_up(v, d);
+    if (lane >= d) v += o;
   }
-  if (lane == 63) wave_tot[wave] = v;
-  __syncthreads();
-  I3 base = {0, 0, 0, 0};
-  for (int w = 0; w < wave; ++w) {
-    base.a += wave_tot[w].a; base.b += wave_tot[w].b; base.c += wave_tot[w].c; base.d += wave_tot[w].d;
-  }
-  v.a += base.a; v.b += base.b; v.c += base.c; v.d += base.d;
   return v;
 }
 
-// One workgroup builds the unit table (experts page, ExpertsKernel.group /
-// ExpertsGroupKernel): per-expert token bitmasks, ceil(n/8) units per expert numbered
-// in expert order, unit rows holding pair indices in token order (-1 padded), and the
-// list of distinct experts with their first unit and 16-column tile offset.
-__device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int B, int K, int E, int W, Table tbl) {
+// LDS words of the unit-table build: per-expert token bitmasks (word-major, [W][E]),
+// route counts, first unit and first chunk per expert, and the column count of every
+// chunk.
+size_t group_lds_words(int B, int K, int E) {
+  const int64_t U = static_cast<int64_t>(B) * K;
+  return static_cast<size_t>(E) * ((B + 31) / 32) + 3 * static_cast<size_t>(E) +
+         static_cast<size_t>(max_chunks_for(U, U < E ? U : E));
+}
+
+// The unit table (experts page, ExpertsKernel.group / ExpertsGroupKernel): per-expert
+// token bitmasks, ceil(n/8) units per expert numbered in expert order, unit rows holding
+// pair indices in token order (-1 padded), the list of distinct experts with their first
+// unit and 16-column tile offset, and the 32-route chunks.  Built by `parts` workgroups
+// of kGroupThreads: every one counts all routes and scans all experts (E <= 1024: thread
+// e holds expert e), then writes the per-expert entries of the experts [lo, hi) and the
+// unit-row and chunk entries of the routes [r_lo, r_hi), so that each issues 1/parts of
+// the table's scattered stores.
+__device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int B, int K, int E, int W, Table tbl,
+                                           int part, int parts) {
   extern __shared__ uint32_t lds[];
-  uint32_t* masks = lds;                                        // [E, W]
-  int* routes = reinterpret_cast<int*>(masks + static_cast<size_t>(E) * W);  // [E] route counts
-  int* unit0 = routes + E;                                      // [E]
-  int* chunk0 = unit0 + E;                                      // [E]
-  __shared__ I3 wave_tot[kGroupThreads / 64];
-  __shared__ int flags;
-  const int tid = threadIdx.x;
+  constexpr int kPer = 8;  // routes per thread held in registers (all of them for U <= 8192)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int U = B * K;
+  const int lo = static_cast<int>(static_cast<int64_t>(part) * E / parts);
+  const int hi = static_cast<int>(static_cast<int64_t>(part + 1) * E / parts);
+  const int r_lo = static_cast<int>(static_cast<int64_t>(part) * U / parts);
+  const int r_hi = static_cast<int>(static_cast<int64_t>(part + 1) * U / parts);
+  int ev[kPer];  // requested before anything else
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r = tid + i * kGroupThreads;
+    ev[i] = r < U ? ids[r] : -1;
+  }
+  uint32_t* masks = lds;                                                     // [W][E]
+  int* routes = reinterpret_cast<int*>(masks + static_cast<size_t>(E) * W);  // [E] route counts
+  int* unit0 = routes + E;                                                   // [E]
+  int* chunk0 = unit0 + E;                                                   // [E]
+  int* ncols = chunk0 + E;                                                   // [chunks]
+  __shared__ uint32_t wsum[2][kGroupThreads / 64];
+  __shared__ uint32_t s_tot[2];
+  __shared__ int flags, s_c_lo, s_c_hi;
   for (int i = tid; i < E * W; i += kGroupThreads) masks[i] = 0;
   for (int i = tid; i < E; i += kGroupThreads) routes[i] = 0;
   if (tid == 0) flags = 0;
   __syncthreads();
-  for (int r = tid; r < U; r += kGroupThreads) {
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r = tid + i * kGroupThreads;
+    if (r < U) {
+      const int e = ev[i];
+      if (e < 0 || e >= E) {
+        bad = 1;
+      } else {
+        const int t = r / K;
+        atomicOr(&masks[(t >> 5) * E + e], 1u << (t & 31));
+        atomicAdd(&routes[e], 1);
+      }
+    }
+  }
+  for (int r = tid + kPer * kGroupThreads; r < U; r += kGroupThreads) {
     const int e = ids[r];
-    if (e < 0 || e >= E) { atomicOr(&flags, 1); continue; }
+    if (e < 0 || e >= E) {
+      bad = 1;
+      continue;
+    }
     const int t = r / K;
-    atomicOr(&masks[e * W + (t >> 5)], 1u << (t & 31));
+    atomicOr(&masks[(t >> 5) * E + e], 1u << (t & 31));
     atomicAdd(&routes[e], 1);
   }
+  if (bad) atomicOr(&flags, 1);
   __syncthreads();
-  int cnt = 0;
-  if (tid < E)
-    for (int w = 0; w < W; ++w) cnt += __popc(masks[tid * W + w]);
-  if (tid < E && cnt != routes[tid]) atomicOr(&flags, 2);      // an id repeated in a token
-  const int units = (cnt + 7) >> 3;
-  const int chunks = (cnt + kChunkCols - 1) / kChunkCols;
-  I3 v = {units, cnt > 0 ? 1 : 0, (units + 1) >> 1, chunks};
-  const I3 inc = block_scan3(v, wave_tot);
-  const int u0 = inc.a - v.a, gi = inc.b - v.b, t0 = inc.c - v.c, c0 = inc.d - v.d;
-  if (tid < E) {
-    unit0[tid] = u0;
-    chunk0[tid] = c0;
-  }
-  if (tid < E && cnt > 0) {
-    tbl.g_expert[gi] = tid;
-    tbl.g_unit0[gi] = u0;
-    tbl.g_nunits[gi] = units;
-    tbl.g_tile0[gi] = t0;
-    for (int u = 0; u < units; ++u) tbl.unit_expert[u0 + u] = tid;
-    for (int s = cnt & 7; s != 0 && s < 8; ++s) tbl.unit_rows[(u0 + units - 1) * 8 + s] = -1;
-    for (int q = 0; q < chunks; ++q) {
-      tbl.c_expert[c0 + q] = tid;
-      tbl.c_ncols[c0 + q] = cnt - q * kChunkCols < kChunkCols ? cnt - q * kChunkCols : kChunkCols;
+  // thread e: expert e's route count (token bits; a repeated id sets one bit twice), its
+  // units, chunks and 32-column tiles, scanned over the expert waves in two words of two
+  // 16-bit fields (units <= E + U/8 and chunks <= E + U/32 stay below 2^16, so no field
+  // carries into the next)
+  const int ew = (E + 63) >> 6;
+  int cnt = 0, units = 0, chunks = 0, grp = 0, tiles = 0;
+  uint32_t s0 = 0, s1 = 0;
+  if (wave < ew) {
+    if (tid < E) {
+      int c0 = 0, c1 = 0, c2 = 0, c3 = 0, w = 0;
+      for (; w + 4 <= W; w += 4) {
+        c0 += __popc(masks[w * E + tid]);
+        c1 += __popc(masks[(w + 1) * E + tid]);
+        c2 += __popc(masks[(w + 2) * E + tid]);
+        c3 += __popc(masks[(w + 3) * E + tid]);
+      }
+      for (; w < W; ++w) c0 += __popc(masks[w * E + tid]);
+      cnt = c0 + c1 + c2 + c3;
+      if (cnt != routes[tid]) atomicOr(&flags, 2);  // an id repeated within a token
     }
-    for (int col = cnt - (chunks - 1) * kChunkCols; col < kChunkCols; ++col)
-      tbl.c_pairs[(c0 + chunks - 1) * kChunkCols + col] = -1;
+    units = (cnt + 7) >> 3;
+    chunks = (cnt + kChunkCols - 1) / kChunkCols;
+    grp = cnt > 0 ? 1 : 0;
+    tiles = (units + 1) >> 1;
+    s0 = wave_scan_u32(static_cast<uint32_t>(units) | (static_cast<uint32_t>(grp) << 16));
+    s1 = wave_scan_u32(static_cast<uint32_t>(tiles) | (static_cast<uint32_t>(chunks) << 16));
+    if (lane == 63) {
+      wsum[0][wave] = s0;
+      wsum[1][wave] = s1;
+    }
   }
   __syncthreads();
-  if (tid == kGroupThreads - 1) {
-    tbl.hdr[0] = inc.a;
-    tbl.hdr[1] = inc.b;
-    tbl.hdr[2] = inc.c;
-    tbl.hdr[3] = flags;
-    tbl.hdr[4] = inc.d;
+  if (wave < ew) {
+    for (int w = 0; w < wave; ++w) {
+      s0 += wsum[0][w];
+      s1 += wsum[1][w];
+    }
+    const int iu = static_cast<int>(s0 & 0xffffu), ig = static_cast<int>(s0 >> 16);
+    const int it = static_cast<int>(s1 & 0xffffu), ic = static_cast<int>(s1 >> 16);
+    const int u0 = iu - units, gi = ig - grp, t0 = it - tiles, c0 = ic - chunks;
+    if (tid < E) {
+      unit0[tid] = u0;
+      chunk0[tid] = c0;
+    }
+    if (tid == E - 1) {
+      s_tot[0] = s0;
+      s_tot[1] = s1;
+    }
+    if (tid == lo) s_c_lo = c0;
+    if (tid == hi - 1) s_c_hi = ic;
+    if (tid >= lo && tid < hi) {
+      for (int q = 0; q < chunks; ++q) {
+        const int nc = cnt - q * kChunkCols < kChunkCols ? cnt - q * kChunkCols : kChunkCols;
+        ncols[c0 + q] = nc;
+        tbl.c_expert[c0 + q] = tid;
+        tbl.c_ncols[c0 + q] = nc;
+      }
+      if (cnt > 0) {
+        tbl.g_expert[gi] = tid;
+        tbl.g_unit0[gi] = u0;
+        tbl.g_nunits[gi] = units;
+        tbl.g_tile0[gi] = t0;
+        for (int u = 0; u < units; ++u) tbl.unit_expert[u0 + u] = tid;
+        for (int sl = cnt & 7; sl != 0 && sl < 8; ++sl) tbl.unit_rows[(u0 + units - 1) * 8 + sl] = -1;
+      }
+    }
   }
-  for (int r = tid; r < U; r += kGroupThreads) {
-    const int e = ids[r];
-    if (e < 0 || e >= E) continue;
-    const int t = r / K;
-    const uint32_t* m = masks + e * W;
-    int rank = __popc(m[t >> 5] & ((1u << (t & 31)) - 1u));
-    for (int w = 0; w < (t >> 5); ++w) rank += __popc(m[w]);
+  __syncthreads();
+  if (part == 0 && tid == 0) {
+    tbl.hdr[0] = static_cast<int>(s_tot[0] & 0xffffu);
+    tbl.hdr[1] = static_cast<int>(s_tot[0] >> 16);
+    tbl.hdr[2] = static_cast<int>(s_tot[1] & 0xffffu);
+    tbl.hdr[3] = flags;
+    tbl.hdr[4] = static_cast<int>(s_tot[1] >> 16);
+  }
+  // unit-row and chunk entries of the routes [r_lo, r_hi): rank = the route's position
+  // among its expert's routes in token order
+  auto place = [&](int r, int e) {
+    if (e < 0 || e >= E) return;
+    const int t = r / K, tw = t >> 5;
+    int rank = __popc(masks[tw * E + e] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < tw; ++w) rank += __popc(masks[w * E + e]);
     tbl.unit_rows[(unit0[e] + (rank >> 3)) * 8 + (rank & 7)] = r;
     tbl.c_pairs[(chunk0[e] + rank / kChunkCols) * kChunkCols + rank % kChunkCols] = r;
+  };
+  if (U <= kPer * kGroupThreads) {  // every route is in a thread's registers
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = tid + i * kGroupThreads;
+      if (r >= r_lo && r < r_hi) place(r, ev[i]);
+    }
+  } else {
+    for (int r = r_lo + tid; r < r_hi; r += kGroupThreads) place(r, ids[r]);
+  }
+  // chunk pads of the experts [lo, hi): their chunks are contiguous
+  if (lo < hi) {
+    const int c_lo = s_c_lo, c_hi = s_c_hi;
+    for (int idx = c_lo * kChunkCols + tid; idx < c_hi * kChunkCols; idx += kGroupThreads)
+      if ((idx & (kChunkCols - 1)) >= ncols[idx / kChunkCols]) tbl.c_pairs[idx] = -1;
   }
 }
 
 __global__ __launch_bounds__(kGroupThreads) void group_kernel(const int32_t* __restrict__ ids, int B,
                                                               int K, int E, int W, Table tbl) {
-  group_body(ids, B, K, E, W, tbl);
+  group_body(ids, B, K, E, W, tbl, blockIdx.x, gridDim.x);
 }
 
-// The plan and the unit table of a batch in one launch (moe_plan_group): workgroup 0
-// builds the unit table, the others quantize x, kGroupThreads 32-element blocks each.
+// The plan and the unit table of a batch in one launch (moe_plan_group): the first
+// kGroupParts workgroups build the unit table, the others quantize x, kGroupThreads / 4
+// 32-element blocks each.
 __global__ __launch_bounds__(kGroupThreads) void plan_group_kernel(const uint8_t* __restrict__ x, int64_t nblocks,
                                                                    uint8_t* __restrict__ codes,
                                                                    uint8_t* __restrict__ scales,
                                                                    const int32_t* __restrict__ ids, int B, int K,
                                                                    int E, int W, Table tbl) {
-  if (blockIdx.x == 0) {
-    group_body(ids, B, K, E, W, tbl);
+  if (blockIdx.x < kGroupParts) {
+    group_body(ids, B, K, E, W, tbl, blockIdx.x, kGroupParts);
     return;
   }
-  const int64_t idx = static_cast<int64_t>(blockIdx.x - 1) * kGroupThreads + threadIdx.x;
-  if (idx < nblocks) plan_block(x, idx, codes, scales);
+  // four lanes per block: a block's lanes are in one wave, and all four are in range or none
+  const int64_t idx4 = static_cast<int64_t>(blockIdx.x - kGroupParts) * kGroupThreads + threadIdx.x;
+  if (idx4 < 4 * nblocks) plan_quarter(x, idx4, codes, scales);
 }
 
 // ------------------------------------------------------------------ packing
@@ -4239,7 +4333,7 @@ int moe_plan(const void* x, int32_t B, int32_t D, void* plan, size_t plan_bytes,
   if (plan_bytes < moe_plan_bytes(B, D)) return MOE_ENOSPACE;
   const int64_t nblocks = static_cast<int64_t>(B) * (D / 32);
   uint8_t* codes = static_cast<uint8_t*>(plan);
-  hipLaunchKernelGGL(plan_kernel, dim3(static_cast<unsigned>((nblocks + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(plan_kernel, dim3(static_cast<unsigned>((4 * nblocks + 255) / 256)), dim3(256), 0,
                      as_stream(stream), static_cast<const uint8_t*>(x), nblocks, codes,
                      codes + static_cast<int64_t>(B) * D);
   return launch_status();
@@ -4262,12 +4356,13 @@ int moe_group(const int32_t* ids, int32_t B, int32_t topk, int32_t E, void* unit
       static_cast<int64_t>(B) * topk > 65536)
     return MOE_EINVAL;
   const int W = (B + 31) / 32;
-  const size_t lds = (static_cast<size_t>(E) * W + 3 * static_cast<size_t>(E)) * 4;
+  const size_t lds = group_lds_words(B, topk, E) * 4;
   if (lds > 60 * 1024) return MOE_EINVAL;
   const UnitsLayout L = units_layout(B, topk, E);
   if (units_bytes < L.end) return MOE_ENOSPACE;
   const Table t = table_at(static_cast<uint8_t*>(units), L);
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(kGroupThreads), lds, as_stream(stream), ids, B, topk, E, W, t);
+  hipLaunchKernelGGL(group_kernel, dim3(kGroupParts), dim3(kGroupThreads), lds, as_stream(stream), ids, B, topk, E,
+                     W, t);
   return launch_status();
 }
 
@@ -4278,14 +4373,14 @@ int moe_plan_group(const void* x, const int32_t* ids, int32_t B, int32_t D, int3
     return MOE_EINVAL;
   if (plan_bytes < moe_plan_bytes(B, D)) return MOE_ENOSPACE;
   const int W = (B + 31) / 32;
-  const size_t lds = (static_cast<size_t>(E) * W + 3 * static_cast<size_t>(E)) * 4;
+  const size_t lds = group_lds_words(B, topk, E) * 4;
   if (lds > 60 * 1024) return MOE_EINVAL;
   const UnitsLayout L = units_layout(B, topk, E);
   if (units_bytes < L.end) return MOE_ENOSPACE;
   const Table t = table_at(static_cast<uint8_t*>(units), L);
   const int64_t nblocks = static_cast<int64_t>(B) * (D / 32);
   uint8_t* codes = static_cast<uint8_t*>(plan);
-  const unsigned grid = 1u + static_cast<unsigned>((nblocks + kGroupThreads - 1) / kGroupThreads);
+  const unsigned grid = kGroupParts + static_cast<unsigned>((4 * nblocks + kGroupThreads - 1) / kGroupThreads);
   hipLaunchKernelGGL(plan_group_kernel, dim3(grid), dim3(kGroupThreads), lds, as_stream(stream),
                      static_cast<const uint8_t*>(x), nblocks, codes, codes + static_cast<int64_t>(B) * D, ids, B,
                      topk, E, W, t);
