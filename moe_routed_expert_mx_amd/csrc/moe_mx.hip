@@ -769,6 +769,18 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_off) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __builtin_amdgcn_global_load_lds(g, (lds_void*)(smem + lds_off), 4, 0, 0);
 }
+// The same with the non-temporal hint (cache policy NT): for data read exactly once
+// (the weight stream), so that its lines are the first the L2 evicts and do not push
+// out data that other workgroups read again.
+constexpr int kNT = 2;
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)(smem + lds_off), 16, 0, kNT);
+}
+__device__ __forceinline__ void dma4_nt(const void* g, uint32_t lds_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)(smem + lds_off), 4, 0, kNT);
+}
 // DMA through a buffer resource: lanes whose offset lies outside the buffer write zeros
 // and read no memory (a padded column, or a pad that only keeps the DMA count fixed).
 constexpr uint32_t kOutside = 0x80000000u;
@@ -780,6 +792,25 @@ __device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + lds_off), 4, voff, 0, 0, 0);
 }
+// DMA through a buffer resource with the lane's offset `voff` (a loop-invariant register)
+// and a scalar offset `soff`: a stream of such loads needs no vector address arithmetic
+// between them (a vector register that a load has not yet read holds up the instruction
+// that would overwrite it).  A lane whose voff lies outside the buffer writes zeros.
+template <int AUX = 0>
+__device__ __forceinline__ void sdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + lds_off), 16, voff, soff, 0, AUX);
+}
+template <int AUX = 0>
+__device__ __forceinline__ void sdma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lds_off) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(smem + lds_off), 4, voff, soff, 0, AUX);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
 // The wave's index in its workgroup, as a scalar (uniform) value: derived from
 // threadIdx.x the compiler would keep it, and everything computed from it, per lane.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)); }
@@ -3182,6 +3213,7 @@ constexpr int kGStores = 4;               // row stores after an FC2 slot (2 til
 constexpr int kGFin = kGStream;           // the finisher wave
 constexpr int kGLoad = kGStream + 1;      // the loader wave
 constexpr int kGWG = 64 * (kGStream + 2);
+static_assert(kGLoad + 1 == kGWG / 64, "the loader is the last wave");
 constexpr int kGItems = 32;               // FC1 items per workgroup (LDS token table)
 constexpr int kGChunks = 1024;            // chunks per call (LDS expert table)
 
@@ -3190,6 +3222,7 @@ constexpr uint32_t kGProg2 = 32;   // [kGStream] wave w is done with every FC2 c
 constexpr uint32_t kGCons = 64;    // FC1 items whose partial tiles the finisher has read
 constexpr uint32_t kGReady = 68;   // FC2 chunk sequences loaded into the hidden buffers
 constexpr uint32_t kGCall = 72;    // this call's number
+constexpr uint32_t kGXs = 76;      // FC1 items whose x scales are in their x-scale buffer
 constexpr uint32_t kGExp = 128;    // [kGChunks] u16 expert of chunk ch
 constexpr uint32_t kGTok = kGExp + 2 * kGChunks;  // [kGItems][32] u16 token of item k's column (0xffff: padded)
 constexpr uint32_t kGTables = kGTok + 2 * kGItems * kChunkCols;
@@ -3215,6 +3248,7 @@ struct GArgs {
   uint32_t out_bytes;       // bytes of the output rows
   uint32_t colb;            // bytes of one hidden column (IP + 16)
   uint32_t o_ring, o_red, o_hid, hid_bytes, hid_code_bytes;  // LDS: ring, partial tiles, hidden buffers
+  uint32_t o_xs, xs_bytes, xs_stride;  // LDS: two x-scale buffers of xs_bytes, one column per xs_stride bytes
 };
 
 __device__ __forceinline__ int lds_u16(uint32_t addr) {
@@ -3277,14 +3311,15 @@ struct GCursor {
   int k;            // slot index
   int item, si;     // FC1: item of the workgroup, this wave's step index within it
   int e, j;         // FC1: expert and hidden block of the current item
-  int t0, t1;       // FC1 (issue side): the lane's token in column tile 0 / 1 (-1: padded)
+  uint32_t xo0, xo1, xo2, xo3;  // FC1 (issue side): the lane's x code offsets in the four x
+                                // DMAs at K step 0 (kOutside: a padded column)
   int ti;           // FC2: the wave's tile index of the slot's first tile
   int chunk, rt2;   // FC2: chunk and 16-row tile of that tile
 };
 
 __device__ __forceinline__ void g_cursor_init(GCursor& c) {
   c.k = c.item = c.si = c.e = c.j = c.ti = 0;
-  c.t0 = c.t1 = -1;
+  c.xo0 = c.xo1 = c.xo2 = c.xo3 = kOutside;
   c.chunk = c.rt2 = 0;
 }
 
@@ -3298,6 +3333,29 @@ __device__ __forceinline__ void g_next_tile(int TPE, int& chunk, int& rt2) {
   }
 }
 
+// The x code offsets of item `item` for this lane: the four x DMAs of an FC1 slot fetch
+// whole 128-byte lines, DMA i holding columns 8i .. 8i + 7 (eight lanes per column); lane
+// l fetches part (l & 7) ^ (col & 7) of column 8i + (l >> 3), so that the slot holds
+// column c's line at c * 128 with its 16-byte parts XOR-swizzled by c & 7 (the MFMA reads
+// then spread over the LDS banks).
+__device__ __forceinline__ void g_xoffsets(const GArgs& a, uint32_t lb, int item, uint32_t& x0, uint32_t& x1,
+                                           uint32_t& x2, uint32_t& x3) {
+  const int l = threadIdx.x & 63;
+  const uint32_t tb = lb + kGTok + static_cast<uint32_t>(item * kChunkCols * 2);
+  uint32_t xo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int col = 8 * i + (l >> 3);
+    const int tok = lds_u16(tb + 2 * col);
+    const int part = (l & 7) ^ (col & 7);
+    xo[i] = tok == 0xffff ? kOutside : static_cast<uint32_t>(tok * a.D + 16 * part);
+  }
+  x0 = xo[0];
+  x1 = xo[1];
+  x2 = xo[2];
+  x3 = xo[3];
+}
+
 // Moves the cursor to its next slot, reading the per-item state (the chunk's expert and
 // the block; the issue side also the lane's tokens) when it enters an FC1 item.  Every
 // field is computed into a local and stored once (stores to different fields in
@@ -3305,8 +3363,8 @@ __device__ __forceinline__ void g_next_tile(int TPE, int& chunk, int& rt2) {
 // in scratch memory).
 __device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t lb, int w, int m1, int n1el,
                                        int n_el, int n_chunks, GCursor& c, bool tokens) {
-  const int l = threadIdx.x & 63;
-  int k = c.k + 1, item = c.item, si = c.si, e = c.e, j = c.j, t0 = c.t0, t1 = c.t1, ti = c.ti;
+  int k = c.k + 1, item = c.item, si = c.si, e = c.e, j = c.j, ti = c.ti;
+  uint32_t xo0 = c.xo0, xo1 = c.xo1, xo2 = c.xo2, xo3 = c.xo3;
   int chunk = c.chunk, rt2 = c.rt2;
   if (c.k < n1el) {
     if (++si == m1) {
@@ -3322,12 +3380,7 @@ __device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t 
     int ch;
     g_item(q.c + item * q.nwg, n_chunks, a.HB, ch, j);
     e = __builtin_amdgcn_readfirstlane(lds_u16(lb + kGExp + 2 * ch));
-    if (tokens) {
-      const uint32_t tb = lb + kGTok + static_cast<uint32_t>(item * kChunkCols * 2);
-      const int u0 = lds_u16(tb + 2 * (l & 15)), u1 = lds_u16(tb + 2 * (16 + (l & 15)));
-      t0 = u0 == 0xffff ? -1 : u0;
-      t1 = u1 == 0xffff ? -1 : u1;
-    }
+    if (tokens) g_xoffsets(a, lb, item, xo0, xo1, xo2, xo3);
   } else if (k == n1el && k < n_el) {  // entering the FC2 run
     const int t = q.first2 + w;
     ti = 0;
@@ -3339,8 +3392,10 @@ __device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t 
   c.si = si;
   c.e = e;
   c.j = j;
-  c.t0 = t0;
-  c.t1 = t1;
+  c.xo0 = xo0;
+  c.xo1 = xo1;
+  c.xo2 = xo2;
+  c.xo3 = xo3;
   c.ti = ti;
   c.chunk = chunk;
   c.rt2 = rt2;
@@ -3349,17 +3404,12 @@ __device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t 
 // Sets the cursor on slot 0 (the same per-item reads as g_step).
 __device__ __forceinline__ void g_start(const GArgs& a, const QWork& q, uint32_t lb, int w, int n1el, int n_el,
                                         int n_chunks, GCursor& c, bool tokens) {
-  const int l = threadIdx.x & 63;
   g_cursor_init(c);
   if (0 < n1el) {
     int ch;
     g_item(q.c, n_chunks, a.HB, ch, c.j);
     c.e = __builtin_amdgcn_readfirstlane(lds_u16(lb + kGExp + 2 * ch));
-    if (tokens) {
-      const int u0 = lds_u16(lb + kGTok + 2 * (l & 15)), u1 = lds_u16(lb + kGTok + 2 * (16 + (l & 15)));
-      c.t0 = u0 == 0xffff ? -1 : u0;
-      c.t1 = u1 == 0xffff ? -1 : u1;
-    }
+    if (tokens) g_xoffsets(a, lb, 0, c.xo0, c.xo1, c.xo2, c.xo3);
   } else if (0 < n_el) {
     const int t = q.first2 + w;
     c.chunk = t / q.TPE;
@@ -3372,49 +3422,48 @@ template <int NS2>
 __device__ __forceinline__ void g_issue(const GArgs& a, const QWork& q, uint32_t lb, int w, int n1el, int n_el,
                                         int n2w, const GCursor& c, __amdgpu_buffer_rsrc_t rx,
                                         __amdgpu_buffer_rsrc_t none) {
-  const int l = threadIdx.x & 63, g = l >> 4;
+  const uint32_t l = threadIdx.x & 63;
+  const uint32_t v16 = 16 * l, v4 = 4 * l, vout = kOutside;
   const uint32_t so = a.o_ring + static_cast<uint32_t>((w * kGR + c.k % kGR) * kGSlot);
   if (c.k < n1el) {
-    // four row tiles and their scale word ...
+    // four row tiles and their scale word (the expert's packed w13 as one buffer) ...
     const int s = w + kGStream * c.si;
-    const int64_t step = (static_cast<int64_t>(c.e) * a.HB + c.j) * a.NS1 + s;
-    const uint8_t* wb = a.w13p + step * 4096 + l * 16;
+    const uint32_t per = static_cast<uint32_t>(a.HB * a.NS1);  // K steps of an expert
+    const uint32_t st = static_cast<uint32_t>(c.j * a.NS1 + s);
+    const __amdgpu_buffer_rsrc_t rw = rsrc(a.w13p + static_cast<int64_t>(c.e) * per * 4096, per * 4096);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(a.s13p + static_cast<int64_t>(c.e) * per * 256, per * 256);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dma16(wb + t * 1024, so + t * 1024);
-    dma4(a.s13p + step * 256 + l * 4, so + 4096);
-    // ... then the x operands: codes of column l % 16 at K 16g.. and 64 + 16g.. of the
-    // step for column tiles 0 and 1, and the scale word of column l (lanes 0-31; the tokens
-    // of columns l & 15 and 16 + (l & 15) are this lane's t0 and t1)
-    const int t0 = c.t0, t1 = c.t1;
-    const uint32_t x0 = t0 >= 0 ? static_cast<uint32_t>(t0 * a.D + 128 * s + 16 * g) : kOutside;
-    const uint32_t x1 = t1 >= 0 ? static_cast<uint32_t>(t1 * a.D + 128 * s + 16 * g) : kOutside;
-    const int lo = l < 16 ? 1 : 0;
-    const int tcol = lo * t0 + (1 - lo) * t1;
-    const uint32_t xs = l < 32 && tcol >= 0 ? static_cast<uint32_t>(a.B * a.D + tcol * (a.D / 32) + 4 * s) : kOutside;
-    bdma16(rx, x0, so + kGHalf);
-    bdma16(rx, x0 == kOutside ? kOutside : x0 + 64, so + kGHalf + 1024);
-    bdma16(rx, x1, so + kGHalf + 2048);
-    bdma16(rx, x1 == kOutside ? kOutside : x1 + 64, so + kGHalf + 3072);
-    bdma4(rx, xs, so + kGHalf + 4096);
+    for (int t = 0; t < 4; ++t) sdma16<kNT>(rw, v16, st * 4096 + t * 1024, so + t * 1024);
+    sdma4<kNT>(rs, v4, st * 256, so + 4096);
+    // ... then the x codes of the step: the chunk's 32 columns as whole lines (the x
+    // scales of the item are in LDS already), and one empty DMA that keeps the count
+    const uint32_t ks = static_cast<uint32_t>(128 * s);
+    sdma16(rx, c.xo0, ks, so + kGHalf);
+    sdma16(rx, c.xo1, ks, so + kGHalf + 1024);
+    sdma16(rx, c.xo2, ks, so + kGHalf + 2048);
+    sdma16(rx, c.xo3, ks, so + kGHalf + 3072);
+    sdma4(none, vout, 0, so + kGHalf + 4096);
   } else if (c.k < n_el) {
     // two FC2 tiles of the wave's sequence (the second may lie past it: nothing loaded)
     int chunk = c.chunk, rt2 = c.rt2;
+    const uint32_t per = static_cast<uint32_t>(q.TPE);  // 16-row tiles of an expert
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t sh = so + h * kGHalf;
       if (c.ti + h < n2w) {
         const int e = __builtin_amdgcn_readfirstlane(lds_u16(lb + kGExp + 2 * chunk));
-        const int64_t tile = static_cast<int64_t>(e) * q.TPE + rt2;
-        const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
+        const __amdgpu_buffer_rsrc_t rw = rsrc(a.w2p + static_cast<int64_t>(e) * per * NS2 * 1024, per * NS2 * 1024);
+        const __amdgpu_buffer_rsrc_t rs = rsrc(a.s2p + static_cast<int64_t>(e) * per * 256, per * 256);
+        const uint32_t t0 = static_cast<uint32_t>(rt2);
 #pragma unroll
-        for (int ks = 0; ks < NS2; ++ks) dma16(wb + ks * 1024, sh + ks * 1024);
+        for (int ks = 0; ks < NS2; ++ks) sdma16<kNT>(rw, v16, (t0 * NS2 + ks) * 1024, sh + ks * 1024);
 #pragma unroll
-        for (int ks = NS2; ks < 4; ++ks) bdma16(none, kOutside, sh + ks * 1024);
-        dma4(a.s2p + tile * 256 + l * 4, sh + 4096);
+        for (int ks = NS2; ks < 4; ++ks) sdma16(none, vout, 0, sh + ks * 1024);
+        sdma4<kNT>(rs, v4, t0 * 256, sh + 4096);
       } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) bdma16(none, kOutside, sh + ks * 1024);
-        bdma4(none, kOutside, sh + 4096);
+        for (int ks = 0; ks < 4; ++ks) sdma16(none, vout, 0, sh + ks * 1024);
+        sdma4(none, vout, 0, sh + 4096);
       }
       g_next_tile(q.TPE, chunk, rt2);
     }
@@ -3422,10 +3471,43 @@ __device__ __forceinline__ void g_issue(const GArgs& a, const QWork& q, uint32_t
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bdma16(none, kOutside, so + h * kGHalf + ks * 1024);
-      bdma4(none, kOutside, so + h * kGHalf + 4096);
+      for (int ks = 0; ks < 4; ++ks) sdma16(none, vout, 0, so + h * kGHalf + ks * 1024);
+      sdma4(none, vout, 0, so + h * kGHalf + 4096);
     }
   }
+}
+
+// The hidden operands of one FC2 column tile for up to four K steps, as named members (an
+// array member kept across loop iterations would be placed in scratch memory).
+struct HidCache {
+  uint4 l0, h0, l1, h1, l2, h2, l3, h3;
+  uint32_t s0, s1, s2, s3;
+};
+template <int NS2>
+__device__ __forceinline__ HidCache hid_cache(const HidOps<NS2>& o) {
+  HidCache c;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  c.l0 = o.bl[0];
+  c.h0 = o.bh[0];
+  c.s0 = o.bs[0];
+  c.l1 = NS2 > 1 ? o.bl[NS2 > 1 ? 1 : 0] : z;
+  c.h1 = NS2 > 1 ? o.bh[NS2 > 1 ? 1 : 0] : z;
+  c.s1 = NS2 > 1 ? o.bs[NS2 > 1 ? 1 : 0] : 0u;
+  c.l2 = NS2 > 2 ? o.bl[NS2 > 2 ? 2 : 0] : z;
+  c.h2 = NS2 > 2 ? o.bh[NS2 > 2 ? 2 : 0] : z;
+  c.s2 = NS2 > 2 ? o.bs[NS2 > 2 ? 2 : 0] : 0u;
+  c.l3 = NS2 > 3 ? o.bl[NS2 > 3 ? 3 : 0] : z;
+  c.h3 = NS2 > 3 ? o.bh[NS2 > 3 ? 3 : 0] : z;
+  c.s3 = NS2 > 3 ? o.bs[NS2 > 3 ? 3 : 0] : 0u;
+  return c;
+}
+// Operands of K step s (a constant after unrolling).
+__device__ __forceinline__ v8i hid_b(const HidCache& c, int s) {
+  return s == 0 ? fp8_operand(c.l0, c.h0) : s == 1 ? fp8_operand(c.l1, c.h1) : s == 2 ? fp8_operand(c.l2, c.h2)
+                                                                                 : fp8_operand(c.l3, c.h3);
+}
+__device__ __forceinline__ uint32_t hid_s(const HidCache& c, int s) {
+  return s == 0 ? c.s0 : s == 1 ? c.s1 : s == 2 ? c.s2 : c.s3;
 }
 
 // The BF16 row pieces of one FC2 tile, stored after the slot's refill is issued.
@@ -3440,15 +3522,16 @@ __device__ __forceinline__ void g_store_rows(const GRows& r, __amdgpu_buffer_rsr
 }
 
 // One FC2 tile from half a slot against the hidden of its chunk: 16 output rows x the
-// chunk's two column tiles (the second skipped for a chunk of <= 16 columns).  Past the
-// wave's sequence it computes nothing and both row offsets are out of range.
+// chunk's two column tiles (the second skipped for a chunk of <= 16 columns).  The chunk's
+// hidden operands (both column tiles) are read from LDS when the chunk changes and kept in
+// registers (hop0, hop1).  Past the wave's sequence it computes nothing and both row
+// offsets are out of range.
 template <int NS2>
 __device__ __forceinline__ GRows g_fc2_tile(const GArgs& a, uint32_t lb, int w, int g0, bool live_tile, int chunk,
-                                            int rt2, uint32_t sh, int& seq_cur, uint32_t& hbl, uint32_t& hbs,
-                                            int& orow0, int& orow1) {
+                                            int rt2, uint32_t sh, int& seq_cur, HidCache& hop0, HidCache& hop1,
+                                            bool& second, int& orow0, int& orow1) {
   const int l = threadIdx.x & 63, grp = l >> 4, col = l & 15;
   v4f o0 = v4f{0.f, 0.f, 0.f, 0.f}, o1 = v4f{0.f, 0.f, 0.f, 0.f};
-  bool second = false;
   if (live_tile) {
     const int seq = chunk - g0;
     if (seq != seq_cur) {
@@ -3456,12 +3539,18 @@ __device__ __forceinline__ GRows g_fc2_tile(const GArgs& a, uint32_t lb, int w, 
       if (l == 0) lds_st4(lb + kGProg2 + 4 * w, static_cast<uint32_t>(seq));
       g_wait_lds(lb + kGReady, seq + 1, a.err);
       const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(seq & 1) * a.hid_bytes;
-      hbl = hb + col * a.colb + 16 * grp;
-      hbs = hb + col * a.colb + a.IP;
+      const uint32_t hbl = hb + col * a.colb + 16 * grp;
+      const uint32_t hbs = hb + col * a.colb + a.IP;
       const int p0 = static_cast<int>(lds_ld4(hb + a.hid_code_bytes + 4 * col));
       const int p1 = static_cast<int>(lds_ld4(hb + a.hid_code_bytes + 4 * (16 + col)));
       orow0 = p0 >= 0 ? p0 * a.D : -1;
       orow1 = p1 >= 0 ? p1 * a.D : -1;
+      second = __any(orow1 >= 0);  // a chunk of <= 16 columns skips its second column tile
+      HidOps<NS2> t0, t1;
+      hid_read<NS2>(hbl, hbs, t0);
+      hid_read<NS2>(hbl + 16 * a.colb, hbs + 16 * a.colb, t1);  // (zero codes for a chunk of <= 16 columns)
+      hop0 = hid_cache<NS2>(t0);
+      hop1 = hid_cache<NS2>(t1);
     }
     uint4 wa0, wa1, wa2, wa3;
     uint32_t was;
@@ -3476,23 +3565,16 @@ __device__ __forceinline__ GRows g_fc2_tile(const GArgs& a, uint32_t lb, int w, 
         : "v"(sh + l * 16), "v"(sh + l * 4)
         : "memory");
     const uint4 wa[4] = {wa0, wa1, wa2, wa3};
-    {
-      HidOps<NS2> hop;
-      hid_read<NS2>(hbl, hbs, hop);
-      // K-blocks past I hold zero codes (weights and hidden)
+    // K-blocks past I hold zero codes (weights and hidden)
 #pragma unroll
-      for (int s = 0; s < NS2; ++s)
-        o0 = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(hop.bl[s], hop.bh[s]), o0,
-                          static_cast<int>((was >> (8 * s)) & 0xffu), static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu));
-    }
-    second = __any(orow1 >= 0);  // a chunk of <= 16 columns skips its second column tile
+    for (int s = 0; s < NS2; ++s)
+      o0 = mfma_fp4_fp8(fp4_operand(wa[s]), hid_b(hop0, s), o0, static_cast<int>((was >> (8 * s)) & 0xffu),
+                        static_cast<int>((hid_s(hop0, s) >> (8 * grp)) & 0xffu));
     if (second) {
-      HidOps<NS2> hop;
-      hid_read<NS2>(hbl + 16 * a.colb, hbs + 16 * a.colb, hop);
 #pragma unroll
       for (int s = 0; s < NS2; ++s)
-        o1 = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(hop.bl[s], hop.bh[s]), o1,
-                          static_cast<int>((was >> (8 * s)) & 0xffu), static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu));
+        o1 = mfma_fp4_fp8(fp4_operand(wa[s]), hid_b(hop1, s), o1, static_cast<int>((was >> (8 * s)) & 0xffu),
+                          static_cast<int>((hid_s(hop1, s) >> (8 * grp)) & 0xffu));
     }
     mfma_settle(o0);
     mfma_settle(o1);
@@ -3562,8 +3644,10 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
       g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, ic, true);
     }
     v4f acc[4][kGTiles];
+    const uint32_t xq_lo = static_cast<uint32_t>(col * 128 + 16 * (grp ^ (col & 7)));
     int ncc = 1, seq_cur = -1;
-    uint32_t hbl = 0, hbs = 0;
+    HidCache hop0, hop1;  // the current FC2 chunk's hidden operands (column tiles 0, 1)
+    bool second = false;
     int orow0 = -1, orow1 = -1;
 #pragma unroll 1
     for (int k = 0; k < n_el; ++k) {
@@ -3580,26 +3664,38 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
         if (cs.si == 0) {
           ncc = lds_u16(lb + kGTok + static_cast<uint32_t>((cs.item * kChunkCols + 16) * 2)) == 0xffff ? 1 : 2;
           ncc = __builtin_amdgcn_readfirstlane(ncc);
+          g_wait_lds(lb + kGXs, cs.item + 1, a.err);  // the item's x scales are in LDS
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int cc = 0; cc < kGTiles; ++cc) acc[rt][cc] = v4f{0.f, 0.f, 0.f, 0.f};
         }
+        // x codes of column col: K 16 grp.. (part grp) and 64 + 16 grp.. (part 4 + grp) of its
+        // swizzled line; its scale word of the step from the item's x-scale buffer
         const uint32_t sb = sa + kGHalf;
-        uint4 a0, a1, a2, a3, xl, xh;
-        uint32_t as, xs;
+        const uint32_t xlo = sb + xq_lo, xhi = sb + (xq_lo ^ 64u);
+        const uint32_t xsa = lb + a.o_xs + static_cast<uint32_t>(cs.item & 1) * a.xs_bytes + col * a.xs_stride +
+                             4u * static_cast<uint32_t>(w + kGStream * cs.si);
+        // (the second column tile's operands are read too, one wait for all: for a chunk of
+        // <= 16 columns they are zeros and unused)
+        uint4 a0, a1, a2, a3, xl, xh, yl, yh;
+        uint32_t as, xs, ys;
         asm volatile(
-            "ds_read_b128 %0, %8 offset:0\n\t"
-            "ds_read_b128 %1, %8 offset:1024\n\t"
-            "ds_read_b128 %2, %8 offset:2048\n\t"
-            "ds_read_b128 %3, %8 offset:3072\n\t"
-            "ds_read_b32 %4, %9 offset:4096\n\t"
-            "ds_read_b128 %5, %10 offset:0\n\t"
-            "ds_read_b128 %6, %10 offset:1024\n\t"
-            "ds_read_b32 %7, %11 offset:4096\n\t"
+            "ds_read_b128 %0, %11 offset:0\n\t"
+            "ds_read_b128 %1, %11 offset:1024\n\t"
+            "ds_read_b128 %2, %11 offset:2048\n\t"
+            "ds_read_b128 %3, %11 offset:3072\n\t"
+            "ds_read_b32 %4, %12 offset:4096\n\t"
+            "ds_read_b128 %5, %13 offset:0\n\t"
+            "ds_read_b128 %6, %14 offset:0\n\t"
+            "ds_read_b32 %7, %15 offset:0\n\t"
+            "ds_read_b128 %8, %13 offset:2048\n\t"
+            "ds_read_b128 %9, %14 offset:2048\n\t"
+            "ds_read_b32 %10, %16 offset:0\n\t"
             "s_waitcnt lgkmcnt(0)"
-            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(as), "=&v"(xl), "=&v"(xh), "=&v"(xs)
-            : "v"(sa + l * 16), "v"(sa + l * 4), "v"(sb + l * 16), "v"(sb + col * 4)
+            : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(as), "=&v"(xl), "=&v"(xh), "=&v"(xs), "=&v"(yl),
+              "=&v"(yh), "=&v"(ys)
+            : "v"(sa + l * 16), "v"(sa + l * 4), "v"(xlo), "v"(xhi), "v"(xsa), "v"(xsa + 16 * a.xs_stride)
             : "memory");
         const uint4 av[4] = {a0, a1, a2, a3};
         {
@@ -3610,16 +3706,6 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
             acc[rt][0] = mfma_fp4_fp8(fp4_operand(av[rt]), b, acc[rt][0], static_cast<int>((as >> (8 * rt)) & 0xffu), sbv);
         }
         if (ncc > 1) {
-          uint4 yl, yh;
-          uint32_t ys;
-          asm volatile(
-              "ds_read_b128 %0, %3 offset:2048\n\t"
-              "ds_read_b128 %1, %3 offset:3072\n\t"
-              "ds_read_b32 %2, %4 offset:4160\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(yl), "=&v"(yh), "=&v"(ys)
-              : "v"(sb + l * 16), "v"(sb + col * 4)
-              : "memory");
           const v8i b = fp8_operand(yl, yh);
           const int sbv = static_cast<int>((ys >> (8 * grp)) & 0xffu);
 #pragma unroll
@@ -3652,9 +3738,10 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
         const int ti = cs.ti, chunk0 = cs.chunk, rt20 = cs.rt2;
         int chunk1 = chunk0, rt21 = rt20;
         g_next_tile(q.TPE, chunk1, rt21);
-        const GRows r0 = g_fc2_tile<NS2>(a, lb, w, g0, ti < n2w, chunk0, rt20, sa, seq_cur, hbl, hbs, orow0, orow1);
-        const GRows r1 =
-            g_fc2_tile<NS2>(a, lb, w, g0, ti + 1 < n2w, chunk1, rt21, sa + kGHalf, seq_cur, hbl, hbs, orow0, orow1);
+        const GRows r0 =
+            g_fc2_tile<NS2>(a, lb, w, g0, ti < n2w, chunk0, rt20, sa, seq_cur, hop0, hop1, second, orow0, orow1);
+        const GRows r1 = g_fc2_tile<NS2>(a, lb, w, g0, ti + 1 < n2w, chunk1, rt21, sa + kGHalf, seq_cur, hop0, hop1,
+                                         second, orow0, orow1);
         g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
         g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, ic, true);
         g_store_rows(r0, rout);
@@ -3756,6 +3843,36 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
     return;
   }
   // ================================================================= loader wave
+  // FC1: the x scales of the workgroup's items (32 columns x D/32 bytes, column c at
+  // c * xs_stride) into the two x-scale buffers, item k into buffer k & 1 once every FC1
+  // wave has finished item k - 2 with it.
+  {
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.plan), static_cast<short>(0), static_cast<int>(a.plan_bytes), 0x00020000);
+    const int pc = static_cast<int>(a.xs_stride / 16), parts = a.D / 512;  // 16-byte parts per column: slot, real
+    const int n_dma = static_cast<int>(a.xs_bytes / 1024);
+#pragma unroll 1
+    for (int k = 0; k < q.n1; ++k) {
+      if (k >= 2) {
+#pragma unroll 1
+        for (int ww = 0; ww < nw1; ++ww) g_wait(lb + kGProg + 4 * ww, k - 1, a.err);
+      }
+      const uint32_t dst = a.o_xs + static_cast<uint32_t>(k & 1) * a.xs_bytes;
+      const uint32_t tb = lb + kGTok + static_cast<uint32_t>(k * kChunkCols * 2);
+#pragma unroll 1
+      for (int i = 0; i < n_dma; ++i) {
+        const int L = 64 * i + l, col = L / pc, part = L - col * pc;
+        const int tok = col < kChunkCols ? lds_u16(tb + 2 * col) : 0xffff;
+        const uint32_t off = tok != 0xffff && part < parts
+                                 ? static_cast<uint32_t>(a.B * a.D + tok * (a.D / 32) + 16 * part)
+                                 : kOutside;
+        bdma16(rx, off, dst + 1024u * static_cast<uint32_t>(i));
+      }
+      wait_vm<0>();
+      lds_settle_all();
+      if (l == 0) lds_st4(lb + kGXs, static_cast<uint32_t>(k + 1));
+    }
+  }
   // FC2: for each chunk of the workgroup's run, in order: wait for its HB block flags,
   // then copy its hidden (codes and scales, device-coherent DMA) and its columns' pair
   // indices into one of the two LDS hidden buffers.  The buffers share LDS with the FC1
@@ -3891,7 +4008,7 @@ int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP
 int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids, int32_t B,
                      int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream);
 bool whole_fits(const moe_weights_t* wts, int32_t B, int32_t topk);
-bool grouped_fits(int E, int I, int B, int K, int grid);
+bool grouped_fits(int E, int D, int I, int B, int K, int grid);
 int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, int32_t B,
                 int32_t topk, void* ws, size_t ws_bytes, void* out, void* stream);
 
@@ -3925,7 +4042,7 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
     return run_decode_whole(wts, o, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
   // the grouped form's default: whole-K FC1 blocks over 32-column chunks (col_tiles 0 or 2)
   // where the batch fits its tables; col_tiles 1 asks for the split-block kernel
-  if (!DEC && o.col_tiles != 1 && grouped_fits(E, I, B, topk, o.grid ? o.grid : device_cus()))
+  if (!DEC && o.col_tiles != 1 && grouped_fits(E, D, I, B, topk, o.grid ? o.grid : device_cus()))
     return run_grouped(wts, o, plan, units, B, topk, ws, ws_bytes, out, stream);
   if (!DEC && o.col_tiles == 2) return MOE_EINVAL;
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
@@ -4008,13 +4125,39 @@ GFn pick_g(int ns2) {
   }
 }
 
+// LDS layout of the grouped kernel for (D, I).
+struct GLds {
+  uint32_t colb, code_bytes, hid_bytes;   // hidden column bytes; a hidden buffer's codes, and all of it
+  uint32_t o_ring, o_xs, xs_bytes, xs_stride, o_red, o_hid;
+  size_t total;
+};
+GLds grouped_lds(int D, int I) {
+  GLds g;
+  const int IP = (I + 127) / 128 * 128;
+  g.colb = static_cast<uint32_t>(IP + 16);
+  g.code_bytes = (kChunkCols * g.colb + 1023u) / 1024u * 1024u;
+  g.hid_bytes = g.code_bytes + 4u * kChunkCols;
+  g.o_ring = (kGTables + 15u) / 16u * 16u;
+  // x scales: a column's D/32 bytes at a stride with bit 4 set (an odd number of 16-byte
+  // units), so that the 16 columns of a read fall in different LDS banks
+  g.xs_stride = static_cast<uint32_t>(D / 32) | 16u;
+  g.xs_bytes = (kChunkCols * g.xs_stride + 1023u) / 1024u * 1024u;
+  g.o_xs = g.o_ring + kGStream * kGR * kGSlot;
+  g.o_red = g.o_xs + 2u * g.xs_bytes;
+  g.o_hid = g.o_red;  // FC1's partial tiles, then FC2's hidden buffers
+  const uint32_t red_bytes = kGStream * 4 * kGTiles * 1024;
+  g.total = g.o_hid + (2u * g.hid_bytes > red_bytes ? 2u * g.hid_bytes : red_bytes);
+  return g;
+}
+constexpr size_t kGLdsMax = 160 * 1024;  // LDS of a gfx950 workgroup
+
 // The grouped kernel's limits: its LDS tables hold kGChunks chunks and kGItems FC1 items
-// per workgroup; I <= 512.
-bool grouped_fits(int E, int I, int B, int K, int grid) {
+// per workgroup; I <= 512; its LDS layout fits.
+bool grouped_fits(int E, int D, int I, int B, int K, int grid) {
   const int64_t U = static_cast<int64_t>(B) * K;
   const int64_t chunks = max_chunks_for(U, U < E ? U : E);
   const int64_t items = (chunks * (I / 32) + grid - 1) / grid;
-  return I <= 512 && chunks <= kGChunks && items <= kGItems;
+  return I <= 512 && chunks <= kGChunks && items <= kGItems && grouped_lds(D, I).total <= kGLdsMax;
 }
 
 int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, int32_t B,
@@ -4025,14 +4168,8 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   if (B_cap < B) return MOE_ENOSPACE;
   const WsLayout L = ws_layout(E, D, I, topk, B_cap);
   const UnitsLayout UL = units_layout(B, topk, E);
-  const uint32_t colb = static_cast<uint32_t>(IP + 16);
-  const uint32_t code_bytes = (kChunkCols * colb + 1023u) / 1024u * 1024u;
-  const uint32_t hid_bytes = code_bytes + 4u * kChunkCols;
-  const uint32_t o_ring = (kGTables + 15u) / 16u * 16u;
-  const uint32_t o_red = o_ring + kGStream * kGR * kGSlot;
-  const uint32_t o_hid = o_red;  // FC1's partial tiles, then FC2's hidden buffers
-  const uint32_t red_bytes = kGStream * 4 * kGTiles * 1024;
-  const size_t lds = o_hid + (2u * hid_bytes > red_bytes ? 2u * hid_bytes : red_bytes);
+  const GLds G = grouped_lds(D, I);
+  const size_t lds = G.total;
   if (lds > static_cast<size_t>(device_lds_limit())) return MOE_EINVAL;
   const GFn fn = pick_g(ns2);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -4046,7 +4183,7 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   if (cap > kMaxGrid) cap = kMaxGrid;
   if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
   const int grid = o.grid ? o.grid : cap;
-  if (!grouped_fits(E, I, B, topk, grid)) return MOE_EINVAL;
+  if (!grouped_fits(E, D, I, B, topk, grid)) return MOE_EINVAL;
 
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* ub = static_cast<uint8_t*>(const_cast<void*>(units));
@@ -4078,12 +4215,15 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   a.max_chunks = static_cast<int>(UL.max_chunks);
   a.plan_bytes = static_cast<uint32_t>(static_cast<int64_t>(B) * D / 32 * 33);
   a.out_bytes = static_cast<uint32_t>(static_cast<int64_t>(B) * topk * D * 2);
-  a.colb = colb;
-  a.o_ring = o_ring;
-  a.o_red = o_red;
-  a.o_hid = o_hid;
-  a.hid_bytes = hid_bytes;
-  a.hid_code_bytes = code_bytes;
+  a.colb = G.colb;
+  a.o_ring = G.o_ring;
+  a.o_red = G.o_red;
+  a.o_hid = G.o_hid;
+  a.hid_bytes = G.hid_bytes;
+  a.hid_code_bytes = G.code_bytes;
+  a.o_xs = G.o_xs;
+  a.xs_bytes = G.xs_bytes;
+  a.xs_stride = G.xs_stride;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kGWG), lds, as_stream(stream), a);
   return launch_status();
 }
