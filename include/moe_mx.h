@@ -166,7 +166,7 @@ typedef struct {
                          for the kernel variant (MOE_EINVAL above it); 0 = all of it */
   int32_t col_tiles;  /* moe_experts_run: 16-token column tiles per weight pass.
                          0 = default: the grouped kernel (two tiles, 32-route chunks) when
-                         the batch fits its limits (I <= 512, at most 1024 chunks and 32
+                         the batch fits its limits (I <= 384, at most 1024 chunks and 32
                          FC1 blocks per workgroup), else 1;
                          1 = the one-tile experts kernel (any batch);
                          2 = the grouped kernel only (MOE_EINVAL beyond its limits);

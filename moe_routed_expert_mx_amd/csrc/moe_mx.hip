@@ -3183,46 +3183,49 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
 // moe_experts_run's default.  The unit table cuts each expert's routes, in token order,
 // into chunks of kChunkCols = 32 token columns (two MFMA column tiles); one weight pass
 // of an expert serves a whole chunk.  One persistent, co-resident workgroup per CU:
-// four streaming waves, a finisher wave and a loader wave.
+// eight streaming waves, each with its own FC1 items, FC2 tiles and DMA ring, and a
+// loader wave.
 //   * an FC1 item is one hidden block of one chunk: the 64 weight rows gate 32j.. and up
 //     I + 32j.. over the whole of K, against the chunk's token columns.  Items are dealt
 //     round-robin over the workgroups, numbered so that the blocks of one chunk land on
-//     workgroups of one XCD (whose L2 then serves the chunk's x to all of them);
-//     streaming wave w takes the K steps w, w + 4, ... of each and keeps FP32 partial
-//     tiles for it.  The finisher adds the four waves' tiles in wave order, applies SwiGLU
-//     and the MXFP8 requantization (experts page, ExpertsKernel.store_hidden), stores the
-//     block's codes and scales device-coherently and then raises the block's flag with the
-//     call number.  No FC1 partial sum leaves the workgroup.
-//   * FC2 is dealt as 16-row output tiles, a contiguous run per workgroup in chunk order
-//     (experts page, ExpertsKernel.partition: contiguous near-equal shares of the weight
-//     stream; workgroups with one FC1 item more take fewer, last tiles).  The loader
+//     workgroups of one XCD (whose L2 then serves the chunk's x to all of them); within a
+//     workgroup, item k goes to streaming wave k mod 8, which runs all of its K steps, so
+//     no FC1 partial sum leaves the wave.  The wave then applies SwiGLU and the MXFP8
+//     requantization (experts page, ExpertsKernel.store_hidden) and stages the block's
+//     codes and scales in LDS; the loader stores them device-coherently and raises the
+//     block's flag with the call number.
+//   * FC2 is dealt as 16-row output tiles, an equal contiguous run per workgroup in chunk
+//     order (experts page, ExpertsKernel.partition: contiguous near-equal shares of the
+//     weight stream); streaming wave w takes tiles w, w + 8, ... of the run.  The loader
 //     waits for a chunk's HB flags and copies its hidden into LDS by device-coherent DMA.
-//   * each streaming wave has one LDS DMA ring of three 8.5 KB slots: an FC1 K step (four
-//     1 KB row tiles and their scale word, then the x operands of the chunk's two column
-//     tiles, gathered per lane from the plan) or two FC2 tiles (NS2 1 KB K steps and a
-//     scale word each).  Every slot is ten DMA instructions (out-of-range ones write
-//     zeros and read no memory), so the wait before a slot depends only on how many of the
-//     last three slots stored output rows.
+//   * each streaming wave has a ring of two 8.5 KB LDS slots: an FC1 K step (four 1 KB
+//     row tiles and their scale word, the x codes of the chunk's 32 columns as whole
+//     lines, their scale words) or two FC2 tiles (NS2 1 KB K steps and a scale word
+//     each).  A wave issues at most about one LDS DMA per 90 cycles, so eight independent
+//     waves (two per SIMD) let one wave's issue overlap another's LDS reads and MFMAs.
+//     Every slot is ten DMA instructions (out-of-range ones write zeros and read no
+//     memory), so the wait before a slot depends only on how many of the last two slots
+//     stored output rows.
 constexpr int kGTiles = kChunkCols / 16;  // column tiles of a chunk
-constexpr int kGStream = 4;               // streaming waves
-constexpr int kGR = 3;                    // slots per streaming wave
-constexpr int kGHalf = 4096 + 256;        // half a slot: four 1 KB pieces and a scale word
+constexpr int kGStream = 8;               // streaming waves
+constexpr int kGR = 2;                    // slots per streaming wave
+constexpr int kGHalf = 4096 + 256;        // half a slot: four 1 KB pieces and a scale area
 constexpr int kGSlot = 2 * kGHalf;
 constexpr int kGOps = 10;                 // DMA instructions per slot
 constexpr int kGStores = 4;               // row stores after an FC2 slot (2 tiles x 2 column tiles)
-constexpr int kGFin = kGStream;           // the finisher wave
-constexpr int kGLoad = kGStream + 1;      // the loader wave
-constexpr int kGWG = 64 * (kGStream + 2);
+constexpr int kGLoad = kGStream;          // the loader wave
+constexpr int kGWG = 64 * (kGStream + 1);
 static_assert(kGLoad + 1 == kGWG / 64, "the loader is the last wave");
 constexpr int kGItems = 32;               // FC1 items per workgroup (LDS token table)
 constexpr int kGChunks = 1024;            // chunks per call (LDS expert table)
+constexpr uint32_t kGStage = 1152;        // LDS bytes of a staged hidden block (32 x 32 codes, 32 scale words)
 
-constexpr uint32_t kGProg = 0;     // [kGStream] FC1 items whose partial tiles wave w has written
-constexpr uint32_t kGProg2 = 32;   // [kGStream] wave w is done with every FC2 chunk sequence < value
-constexpr uint32_t kGCons = 64;    // FC1 items whose partial tiles the finisher has read
-constexpr uint32_t kGReady = 68;   // FC2 chunk sequences loaded into the hidden buffers
-constexpr uint32_t kGCall = 72;    // this call's number
-constexpr uint32_t kGXs = 76;      // FC1 items whose x scales are in their x-scale buffer
+constexpr uint32_t kGStaged = 0;   // [kGStream] FC1 items wave w has staged
+constexpr uint32_t kGPub = 32;     // [kGStream] staged items of wave w the loader has published
+constexpr uint32_t kGProg2 = 64;   // [kGStream] wave w is done with every FC2 chunk sequence < value
+constexpr uint32_t kGReady = 96;   // FC2 chunk sequences loaded into the hidden buffer
+constexpr uint32_t kGCall = 100;   // this call's number
+constexpr uint32_t kGWords = 128;  // bytes of the words above (cleared at the start)
 constexpr uint32_t kGExp = 128;    // [kGChunks] u16 expert of chunk ch
 constexpr uint32_t kGTok = kGExp + 2 * kGChunks;  // [kGItems][32] u16 token of item k's column (0xffff: padded)
 constexpr uint32_t kGTables = kGTok + 2 * kGItems * kChunkCols;
@@ -3247,8 +3250,7 @@ struct GArgs {
   uint32_t plan_bytes;      // bytes of the plan (x codes, then x scales)
   uint32_t out_bytes;       // bytes of the output rows
   uint32_t colb;            // bytes of one hidden column (IP + 16)
-  uint32_t o_ring, o_red, o_hid, hid_bytes, hid_code_bytes;  // LDS: ring, partial tiles, hidden buffers
-  uint32_t o_xs, xs_bytes, xs_stride;  // LDS: two x-scale buffers of xs_bytes, one column per xs_stride bytes
+  uint32_t o_ring, o_hid, hid_code_bytes;  // LDS: rings; hidden buffer (FC1: staging), its code bytes
 };
 
 __device__ __forceinline__ int lds_u16(uint32_t addr) {
@@ -3273,9 +3275,8 @@ __device__ __forceinline__ void g_item(int i, int n_chunks, int HB, int& ch, int
 }
 
 // Bounded LDS wait of the streaming waves.  They wait only on words that their own
-// workgroup's finisher and loader post, whose own waits are bounded, so it reads no
-// global memory (a global read would wait for the wave's ring); its own bound (~1 s) is a
-// last resort.
+// workgroup's loader posts, whose own waits are bounded, so it reads no global memory (a
+// global read would wait for the wave's ring); its own bound (~1 s) is a last resort.
 __device__ __forceinline__ void g_wait_lds(uint32_t addr, int want, int32_t* err) {
 #pragma unroll 1
   for (uint32_t spins = 0;; ++spins) {
@@ -3288,8 +3289,8 @@ __device__ __forceinline__ void g_wait_lds(uint32_t addr, int want, int32_t* err
   }
 }
 
-// Bounded LDS wait of the finisher and the loader: gives up (status bit 2) after ~0.1 s,
-// or soon after another wave of the call has given up.
+// Bounded LDS wait of the loader: gives up (status bit 2) after ~0.1 s, or soon after
+// another wave of the call has given up.
 __device__ __forceinline__ void g_wait(uint32_t addr, int want, int32_t* err) {
 #pragma unroll 1
   for (uint32_t spins = 0;; ++spins) {
@@ -3305,21 +3306,21 @@ __device__ __forceinline__ void g_wait(uint32_t addr, int want, int32_t* err) {
   }
 }
 
-// A cursor over a streaming wave's slot sequence: its FC1 K steps item by item, then its
-// FC2 tiles two per slot (tiles w, w + 4, ... of the workgroup's run), then the end.
+// A cursor over a streaming wave's slot sequence: the K steps of its FC1 items, then its
+// FC2 tiles two per slot (tiles w, w + 8, ... of the workgroup's run), then the end.
 struct GCursor {
   int k;            // slot index
-  int item, si;     // FC1: item of the workgroup, this wave's step index within it
-  int e, j;         // FC1: expert and hidden block of the current item
-  uint32_t xo0, xo1, xo2, xo3;  // FC1 (issue side): the lane's x code offsets in the four x
-                                // DMAs at K step 0 (kOutside: a padded column)
+  int item, si;     // FC1: the wave's item (workgroup item w + 8 * item), its K step
+  int e, j, ch;     // FC1: expert, hidden block and chunk of the current item
+  uint32_t xo0, xo1, xo2, xo3, xso;  // FC1 (issue side): the lane's offsets in the x code
+                                     // DMAs and the x scale DMA at K step 0 (kOutside: none)
   int ti;           // FC2: the wave's tile index of the slot's first tile
   int chunk, rt2;   // FC2: chunk and 16-row tile of that tile
 };
 
 __device__ __forceinline__ void g_cursor_init(GCursor& c) {
-  c.k = c.item = c.si = c.e = c.j = c.ti = 0;
-  c.xo0 = c.xo1 = c.xo2 = c.xo3 = kOutside;
+  c.k = c.item = c.si = c.e = c.j = c.ch = c.ti = 0;
+  c.xo0 = c.xo1 = c.xo2 = c.xo3 = c.xso = kOutside;
   c.chunk = c.rt2 = 0;
 }
 
@@ -3333,15 +3334,16 @@ __device__ __forceinline__ void g_next_tile(int TPE, int& chunk, int& rt2) {
   }
 }
 
-// The x code offsets of item `item` for this lane: the four x DMAs of an FC1 slot fetch
-// whole 128-byte lines, DMA i holding columns 8i .. 8i + 7 (eight lanes per column); lane
-// l fetches part (l & 7) ^ (col & 7) of column 8i + (l >> 3), so that the slot holds
+// The x offsets of workgroup item `wi` for this lane.  The four x code DMAs of an FC1 slot
+// fetch whole 128-byte lines, DMA i holding columns 8i .. 8i + 7 (eight lanes per column);
+// lane l fetches part (l & 7) ^ (col & 7) of column 8i + (l >> 3), so that the slot holds
 // column c's line at c * 128 with its 16-byte parts XOR-swizzled by c & 7 (the MFMA reads
-// then spread over the LDS banks).
-__device__ __forceinline__ void g_xoffsets(const GArgs& a, uint32_t lb, int item, uint32_t& x0, uint32_t& x1,
-                                           uint32_t& x2, uint32_t& x3) {
+// then spread over the LDS banks).  The x scale DMA fetches column l's scale word (lanes
+// 0 .. 31).
+__device__ __forceinline__ void g_xoffsets(const GArgs& a, uint32_t lb, int wi, uint32_t& x0, uint32_t& x1,
+                                           uint32_t& x2, uint32_t& x3, uint32_t& xs) {
   const int l = threadIdx.x & 63;
-  const uint32_t tb = lb + kGTok + static_cast<uint32_t>(item * kChunkCols * 2);
+  const uint32_t tb = lb + kGTok + static_cast<uint32_t>(wi * kChunkCols * 2);
   uint32_t xo[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -3350,24 +3352,26 @@ __device__ __forceinline__ void g_xoffsets(const GArgs& a, uint32_t lb, int item
     const int part = (l & 7) ^ (col & 7);
     xo[i] = tok == 0xffff ? kOutside : static_cast<uint32_t>(tok * a.D + 16 * part);
   }
+  const int ts = l < kChunkCols ? lds_u16(tb + 2 * l) : 0xffff;
   x0 = xo[0];
   x1 = xo[1];
   x2 = xo[2];
   x3 = xo[3];
+  xs = ts == 0xffff ? kOutside : static_cast<uint32_t>(a.B * a.D + ts * (a.D / 32));
 }
 
 // Moves the cursor to its next slot, reading the per-item state (the chunk's expert and
-// the block; the issue side also the lane's tokens) when it enters an FC1 item.  Every
+// the block; the issue side also the lane's x offsets) when it enters an FC1 item.  Every
 // field is computed into a local and stored once (stores to different fields in
 // different branches would otherwise be merged through a pointer, which puts the cursor
 // in scratch memory).
-__device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t lb, int w, int m1, int n1el,
-                                       int n_el, int n_chunks, GCursor& c, bool tokens) {
-  int k = c.k + 1, item = c.item, si = c.si, e = c.e, j = c.j, ti = c.ti;
-  uint32_t xo0 = c.xo0, xo1 = c.xo1, xo2 = c.xo2, xo3 = c.xo3;
+__device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t lb, int w, int n1el, int n_el,
+                                       int n_chunks, GCursor& c, bool tokens) {
+  int k = c.k + 1, item = c.item, si = c.si, e = c.e, j = c.j, ch = c.ch, ti = c.ti;
+  uint32_t xo0 = c.xo0, xo1 = c.xo1, xo2 = c.xo2, xo3 = c.xo3, xso = c.xso;
   int chunk = c.chunk, rt2 = c.rt2;
   if (c.k < n1el) {
-    if (++si == m1) {
+    if (++si == a.NS1) {
       si = 0;
       ++item;
     }
@@ -3377,10 +3381,10 @@ __device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t 
     g_next_tile(q.TPE, chunk, rt2);
   }
   if (k < n1el && si == 0) {  // entering an FC1 item
-    int ch;
-    g_item(q.c + item * q.nwg, n_chunks, a.HB, ch, j);
+    const int wi = w + kGStream * item;
+    g_item(q.c + wi * q.nwg, n_chunks, a.HB, ch, j);
     e = __builtin_amdgcn_readfirstlane(lds_u16(lb + kGExp + 2 * ch));
-    if (tokens) g_xoffsets(a, lb, item, xo0, xo1, xo2, xo3);
+    if (tokens) g_xoffsets(a, lb, wi, xo0, xo1, xo2, xo3, xso);
   } else if (k == n1el && k < n_el) {  // entering the FC2 run
     const int t = q.first2 + w;
     ti = 0;
@@ -3392,10 +3396,12 @@ __device__ __forceinline__ void g_step(const GArgs& a, const QWork& q, uint32_t 
   c.si = si;
   c.e = e;
   c.j = j;
+  c.ch = ch;
   c.xo0 = xo0;
   c.xo1 = xo1;
   c.xo2 = xo2;
   c.xo3 = xo3;
+  c.xso = xso;
   c.ti = ti;
   c.chunk = chunk;
   c.rt2 = rt2;
@@ -3406,10 +3412,12 @@ __device__ __forceinline__ void g_start(const GArgs& a, const QWork& q, uint32_t
                                         int n_chunks, GCursor& c, bool tokens) {
   g_cursor_init(c);
   if (0 < n1el) {
-    int ch;
-    g_item(q.c, n_chunks, a.HB, ch, c.j);
+    int ch, j;
+    g_item(q.c + w * q.nwg, n_chunks, a.HB, ch, j);
+    c.ch = ch;
+    c.j = j;
     c.e = __builtin_amdgcn_readfirstlane(lds_u16(lb + kGExp + 2 * ch));
-    if (tokens) g_xoffsets(a, lb, 0, c.xo0, c.xo1, c.xo2, c.xo3);
+    if (tokens) g_xoffsets(a, lb, w, c.xo0, c.xo1, c.xo2, c.xo3, c.xso);
   } else if (0 < n_el) {
     const int t = q.first2 + w;
     c.chunk = t / q.TPE;
@@ -3426,8 +3434,9 @@ __device__ __forceinline__ void g_issue(const GArgs& a, const QWork& q, uint32_t
   const uint32_t v16 = 16 * l, v4 = 4 * l, vout = kOutside;
   const uint32_t so = a.o_ring + static_cast<uint32_t>((w * kGR + c.k % kGR) * kGSlot);
   if (c.k < n1el) {
-    // four row tiles and their scale word (the expert's packed w13 as one buffer) ...
-    const int s = w + kGStream * c.si;
+    // four row tiles and their scale word (the expert's packed w13 as one buffer), then the
+    // x codes of the step (the chunk's 32 columns as whole lines) and their scale words
+    const int s = c.si;
     const uint32_t per = static_cast<uint32_t>(a.HB * a.NS1);  // K steps of an expert
     const uint32_t st = static_cast<uint32_t>(c.j * a.NS1 + s);
     const __amdgpu_buffer_rsrc_t rw = rsrc(a.w13p + static_cast<int64_t>(c.e) * per * 4096, per * 4096);
@@ -3435,14 +3444,12 @@ __device__ __forceinline__ void g_issue(const GArgs& a, const QWork& q, uint32_t
 #pragma unroll
     for (int t = 0; t < 4; ++t) sdma16<kNT>(rw, v16, st * 4096 + t * 1024, so + t * 1024);
     sdma4<kNT>(rs, v4, st * 256, so + 4096);
-    // ... then the x codes of the step: the chunk's 32 columns as whole lines (the x
-    // scales of the item are in LDS already), and one empty DMA that keeps the count
     const uint32_t ks = static_cast<uint32_t>(128 * s);
     sdma16(rx, c.xo0, ks, so + kGHalf);
     sdma16(rx, c.xo1, ks, so + kGHalf + 1024);
     sdma16(rx, c.xo2, ks, so + kGHalf + 2048);
     sdma16(rx, c.xo3, ks, so + kGHalf + 3072);
-    sdma4(none, vout, 0, so + kGHalf + 4096);
+    sdma4(rx, c.xso, static_cast<uint32_t>(4 * s), so + kGHalf + 4096);
   } else if (c.k < n_el) {
     // two FC2 tiles of the wave's sequence (the second may lie past it: nothing loaded)
     int chunk = c.chunk, rt2 = c.rt2;
@@ -3477,39 +3484,6 @@ __device__ __forceinline__ void g_issue(const GArgs& a, const QWork& q, uint32_t
   }
 }
 
-// The hidden operands of one FC2 column tile for up to four K steps, as named members (an
-// array member kept across loop iterations would be placed in scratch memory).
-struct HidCache {
-  uint4 l0, h0, l1, h1, l2, h2, l3, h3;
-  uint32_t s0, s1, s2, s3;
-};
-template <int NS2>
-__device__ __forceinline__ HidCache hid_cache(const HidOps<NS2>& o) {
-  HidCache c;
-  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-  c.l0 = o.bl[0];
-  c.h0 = o.bh[0];
-  c.s0 = o.bs[0];
-  c.l1 = NS2 > 1 ? o.bl[NS2 > 1 ? 1 : 0] : z;
-  c.h1 = NS2 > 1 ? o.bh[NS2 > 1 ? 1 : 0] : z;
-  c.s1 = NS2 > 1 ? o.bs[NS2 > 1 ? 1 : 0] : 0u;
-  c.l2 = NS2 > 2 ? o.bl[NS2 > 2 ? 2 : 0] : z;
-  c.h2 = NS2 > 2 ? o.bh[NS2 > 2 ? 2 : 0] : z;
-  c.s2 = NS2 > 2 ? o.bs[NS2 > 2 ? 2 : 0] : 0u;
-  c.l3 = NS2 > 3 ? o.bl[NS2 > 3 ? 3 : 0] : z;
-  c.h3 = NS2 > 3 ? o.bh[NS2 > 3 ? 3 : 0] : z;
-  c.s3 = NS2 > 3 ? o.bs[NS2 > 3 ? 3 : 0] : 0u;
-  return c;
-}
-// Operands of K step s (a constant after unrolling).
-__device__ __forceinline__ v8i hid_b(const HidCache& c, int s) {
-  return s == 0 ? fp8_operand(c.l0, c.h0) : s == 1 ? fp8_operand(c.l1, c.h1) : s == 2 ? fp8_operand(c.l2, c.h2)
-                                                                                 : fp8_operand(c.l3, c.h3);
-}
-__device__ __forceinline__ uint32_t hid_s(const HidCache& c, int s) {
-  return s == 0 ? c.s0 : s == 1 ? c.s1 : s == 2 ? c.s2 : c.s3;
-}
-
 // The BF16 row pieces of one FC2 tile, stored after the slot's refill is issued.
 struct GRows {
   uint2 v0, v1;        // column tile 0 / 1: four BF16 values of the lane's output row
@@ -3522,35 +3496,28 @@ __device__ __forceinline__ void g_store_rows(const GRows& r, __amdgpu_buffer_rsr
 }
 
 // One FC2 tile from half a slot against the hidden of its chunk: 16 output rows x the
-// chunk's two column tiles (the second skipped for a chunk of <= 16 columns).  The chunk's
-// hidden operands (both column tiles) are read from LDS when the chunk changes and kept in
-// registers (hop0, hop1).  Past the wave's sequence it computes nothing and both row
-// offsets are out of range.
+// chunk's two column tiles (the second skipped for a chunk of <= 16 columns).  Past the
+// wave's sequence it computes nothing and both row offsets are out of range.
 template <int NS2>
 __device__ __forceinline__ GRows g_fc2_tile(const GArgs& a, uint32_t lb, int w, int g0, bool live_tile, int chunk,
-                                            int rt2, uint32_t sh, int& seq_cur, HidCache& hop0, HidCache& hop1,
-                                            bool& second, int& orow0, int& orow1) {
+                                            int rt2, uint32_t sh, int& seq_cur, uint32_t& hbl, uint32_t& hbs,
+                                            int& orow0, int& orow1) {
   const int l = threadIdx.x & 63, grp = l >> 4, col = l & 15;
   v4f o0 = v4f{0.f, 0.f, 0.f, 0.f}, o1 = v4f{0.f, 0.f, 0.f, 0.f};
+  bool second = false;
   if (live_tile) {
     const int seq = chunk - g0;
     if (seq != seq_cur) {
       seq_cur = seq;
       if (l == 0) lds_st4(lb + kGProg2 + 4 * w, static_cast<uint32_t>(seq));
       g_wait_lds(lb + kGReady, seq + 1, a.err);
-      const uint32_t hb = lb + a.o_hid + static_cast<uint32_t>(seq & 1) * a.hid_bytes;
-      const uint32_t hbl = hb + col * a.colb + 16 * grp;
-      const uint32_t hbs = hb + col * a.colb + a.IP;
+      const uint32_t hb = lb + a.o_hid;
+      hbl = hb + col * a.colb + 16 * grp;
+      hbs = hb + col * a.colb + a.IP;
       const int p0 = static_cast<int>(lds_ld4(hb + a.hid_code_bytes + 4 * col));
       const int p1 = static_cast<int>(lds_ld4(hb + a.hid_code_bytes + 4 * (16 + col)));
       orow0 = p0 >= 0 ? p0 * a.D : -1;
       orow1 = p1 >= 0 ? p1 * a.D : -1;
-      second = __any(orow1 >= 0);  // a chunk of <= 16 columns skips its second column tile
-      HidOps<NS2> t0, t1;
-      hid_read<NS2>(hbl, hbs, t0);
-      hid_read<NS2>(hbl + 16 * a.colb, hbs + 16 * a.colb, t1);  // (zero codes for a chunk of <= 16 columns)
-      hop0 = hid_cache<NS2>(t0);
-      hop1 = hid_cache<NS2>(t1);
     }
     uint4 wa0, wa1, wa2, wa3;
     uint32_t was;
@@ -3565,16 +3532,23 @@ __device__ __forceinline__ GRows g_fc2_tile(const GArgs& a, uint32_t lb, int w, 
         : "v"(sh + l * 16), "v"(sh + l * 4)
         : "memory");
     const uint4 wa[4] = {wa0, wa1, wa2, wa3};
-    // K-blocks past I hold zero codes (weights and hidden)
-#pragma unroll
-    for (int s = 0; s < NS2; ++s)
-      o0 = mfma_fp4_fp8(fp4_operand(wa[s]), hid_b(hop0, s), o0, static_cast<int>((was >> (8 * s)) & 0xffu),
-                        static_cast<int>((hid_s(hop0, s) >> (8 * grp)) & 0xffu));
-    if (second) {
+    {
+      HidOps<NS2> hop;
+      hid_read<NS2>(hbl, hbs, hop);
+      // K-blocks past I hold zero codes (weights and hidden)
 #pragma unroll
       for (int s = 0; s < NS2; ++s)
-        o1 = mfma_fp4_fp8(fp4_operand(wa[s]), hid_b(hop1, s), o1, static_cast<int>((was >> (8 * s)) & 0xffu),
-                          static_cast<int>((hid_s(hop1, s) >> (8 * grp)) & 0xffu));
+        o0 = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(hop.bl[s], hop.bh[s]), o0,
+                          static_cast<int>((was >> (8 * s)) & 0xffu), static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu));
+    }
+    second = __any(orow1 >= 0);  // a chunk of <= 16 columns skips its second column tile
+    if (second) {
+      HidOps<NS2> hop;
+      hid_read<NS2>(hbl + 16 * a.colb, hbs + 16 * a.colb, hop);
+#pragma unroll
+      for (int s = 0; s < NS2; ++s)
+        o1 = mfma_fp4_fp8(fp4_operand(wa[s]), fp8_operand(hop.bl[s], hop.bh[s]), o1,
+                          static_cast<int>((was >> (8 * s)) & 0xffu), static_cast<int>((hop.bs[s] >> (8 * grp)) & 0xffu));
     }
     mfma_settle(o0);
     mfma_settle(o1);
@@ -3586,6 +3560,45 @@ __device__ __forceinline__ GRows g_fc2_tile(const GArgs& a, uint32_t lb, int w, 
   r.v0 = make_uint2(bf16_pair(o0[0], o0[1]), bf16_pair(o0[2], o0[3]));
   r.v1 = make_uint2(bf16_pair(o1[0], o1[1]), bf16_pair(o1[2], o1[3]));
   return r;
+}
+
+// SwiGLU and MXFP8 of a finished FC1 item (experts page, store_hidden), staged in LDS at
+// `stg` for the loader: column c's 32 codes at c * 32, its scale (E8M0 byte, as a word) at
+// 1024 + 4c.  Lane
+// (col, grp) holds hidden values 32j + 4grp + r (row tile 0 over 1) and 32j + 16 + 4grp + r
+// of column col of each column tile.
+__device__ __forceinline__ void g_finish(const GArgs& a, v4f (&acc)[4][kGTiles], int ncc, uint32_t stg) {
+  const int l = threadIdx.x & 63, grp = l >> 4, col = l & 15;
+#pragma unroll
+  for (int cc = 0; cc < kGTiles; ++cc) {
+    if (cc >= ncc) continue;
+    float h[2][4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float gv = acc[half][cc][r], uv = acc[2 + half][cc][r];
+        // SwiGLU with the hardware exponential and reciprocal (a few ulp in FP32; the
+        // hidden is then rounded to 3 mantissa bits)
+        h[half][r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+        amax = fmaxf(amax, fabsf(h[half][r]));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int e = mx_exponent(amax, a.floor_rule != 0);
+    const float sc = exp2_neg(e);
+    auto clampf = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };  // the floor rule saturates
+    uint32_t word[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      word[half] = cvt4_e4m3(clampf(h[half][0] * sc), clampf(h[half][1] * sc), clampf(h[half][2] * sc),
+                             clampf(h[half][3] * sc));
+    const uint32_t cl = static_cast<uint32_t>(cc * 16 + col);
+    lds_st4(stg + cl * 32 + 4 * grp, word[0]);
+    lds_st4(stg + cl * 32 + 16 + 4 * grp, word[1]);
+    if (grp == 0) lds_st4(stg + 1024 + 4 * cl, static_cast<uint32_t>(e + 127));
+  }
 }
 
 template <int NS2>
@@ -3602,7 +3615,7 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
   // ---- prologue: the chunk count, the chunks' experts and the token columns of this
   // workgroup's FC1 items, all requested at once (read for every possible chunk: the
   // table holds max_chunks records, and the item numbering depends on the chunk count)
-  if (tid < 32) sw[tid] = 0u;
+  if (tid < static_cast<int>(kGWords / 4)) sw[tid] = 0u;
   const int n_chunks = a.hdr[4];
   for (int ch = tid; ch < a.max_chunks && ch < kGChunks; ch += kGWG)
     reinterpret_cast<uint16_t*>(smem + kGExp)[ch] = static_cast<uint16_t>(a.c_expert[ch]);
@@ -3617,9 +3630,20 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
   if (tid == 0) sw[kGCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
   __syncthreads();
 
-  const int item_tiles = 34 * a.D / (NS2 * 1024 + 256);  // FC2 tiles that stream as long as one FC1 item
-  const QWork q = q_work(n_chunks, HB, NS1, a.D, nwg, c, w < kGStream ? w : 0, item_tiles, kGStream);
-  const int nw1 = NS1 < kGStream ? NS1 : kGStream;  // waves that take FC1 steps
+  // FC1 items i = c + k * grid; FC2 tiles: equal contiguous runs in chunk order (every
+  // workgroup's FC1 items run side by side in its waves, so all finish at about the same
+  // time)
+  QWork q;
+  q.nwg = nwg;
+  q.c = c;
+  q.TPE = a.D / 16;
+  q.m1 = NS1;
+  {
+    const int N1 = n_chunks * HB, N2 = n_chunks * q.TPE, cap = (N2 + nwg - 1) / nwg;
+    q.n1 = N1 / nwg + (c < N1 % nwg ? 1 : 0);
+    q.first2 = c * cap < N2 ? c * cap : N2;
+    q.n2 = N2 - q.first2 < cap ? N2 - q.first2 : cap;
+  }
   const int g0 = q.first2 / q.TPE;  // chunk of the workgroup's first FC2 tile (sequence 0)
   const __amdgpu_buffer_rsrc_t none =
       __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
@@ -3630,54 +3654,50 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
         const_cast<uint8_t*>(a.plan), static_cast<short>(0), static_cast<int>(a.plan_bytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<void*>(a.out), static_cast<short>(0), static_cast<int>(a.out_bytes), 0x00020000);
-    const int m1 = q.m1;
-    const int n1el = q.n1 * m1;
+    const int n1w = q.n1 > w ? (q.n1 - w + kGStream - 1) / kGStream : 0;  // the wave's FC1 items
+    const int n1el = n1w * NS1;
     const int n2w = q.n2 > w ? (q.n2 - w + kGStream - 1) / kGStream : 0;  // the wave's FC2 tiles
     const int n_el = n1el + (n2w + 1) / 2;                                 // two per slot
-    GCursor ic, cs;  // issue side (three slots ahead), consume side
+    const uint32_t stg = lb + a.o_hid + static_cast<uint32_t>(w) * kGStage;  // the wave's staging
+    GCursor ic, cs;  // issue side (two slots ahead), consume side
     g_start(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
     g_start(a, q, lb, w, n1el, n_el, n_chunks, cs, false);
-    static_assert(kGR == 3, "the wait counts below assume three slots");
+    static_assert(kGR == 2, "the wait counts below assume two slots");
 #pragma unroll 1
     for (int p = 0; p < kGR; ++p) {
       g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
-      g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, ic, true);
+      g_step(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
     }
     v4f acc[4][kGTiles];
     const uint32_t xq_lo = static_cast<uint32_t>(col * 128 + 16 * (grp ^ (col & 7)));
     int ncc = 1, seq_cur = -1;
-    HidCache hop0, hop1;  // the current FC2 chunk's hidden operands (column tiles 0, 1)
-    bool second = false;
+    uint32_t hbl = 0, hbs = 0;
     int orow0 = -1, orow1 = -1;
 #pragma unroll 1
     for (int k = 0; k < n_el; ++k) {
-      // slot k has landed: younger are the two later slots and the row stores of the
-      // last three consumed slots (kGStores after each FC2 slot)
-      const int nf = k - n1el < 0 ? 0 : (k - n1el > 3 ? 3 : k - n1el);
-      if (nf == 0) wait_vm<2 * kGOps>();
-      else if (nf == 1) wait_vm<2 * kGOps + kGStores>();
-      else if (nf == 2) wait_vm<2 * kGOps + 2 * kGStores>();
-      else wait_vm<2 * kGOps + 3 * kGStores>();
+      // slot k has landed: younger are the next slot and the row stores of the last two
+      // consumed slots (kGStores after each FC2 slot)
+      const int nf = k - n1el < 0 ? 0 : (k - n1el > 2 ? 2 : k - n1el);
+      if (nf == 0) wait_vm<kGOps>();
+      else if (nf == 1) wait_vm<kGOps + kGStores>();
+      else wait_vm<kGOps + 2 * kGStores>();
       const uint32_t sa = lb + a.o_ring + static_cast<uint32_t>((w * kGR + k % kGR) * kGSlot);
       if (k < n1el) {
         // ---- FC1 step: four row tiles x the chunk's column tiles
         if (cs.si == 0) {
-          ncc = lds_u16(lb + kGTok + static_cast<uint32_t>((cs.item * kChunkCols + 16) * 2)) == 0xffff ? 1 : 2;
+          const int wi = w + kGStream * cs.item;
+          ncc = lds_u16(lb + kGTok + static_cast<uint32_t>((wi * kChunkCols + 16) * 2)) == 0xffff ? 1 : 2;
           ncc = __builtin_amdgcn_readfirstlane(ncc);
-          g_wait_lds(lb + kGXs, cs.item + 1, a.err);  // the item's x scales are in LDS
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int cc = 0; cc < kGTiles; ++cc) acc[rt][cc] = v4f{0.f, 0.f, 0.f, 0.f};
         }
         // x codes of column col: K 16 grp.. (part grp) and 64 + 16 grp.. (part 4 + grp) of its
-        // swizzled line; its scale word of the step from the item's x-scale buffer
+        // swizzled line, and its scale word of the step; both column tiles with one wait (for
+        // a chunk of <= 16 columns the second is zeros and unused)
         const uint32_t sb = sa + kGHalf;
         const uint32_t xlo = sb + xq_lo, xhi = sb + (xq_lo ^ 64u);
-        const uint32_t xsa = lb + a.o_xs + static_cast<uint32_t>(cs.item & 1) * a.xs_bytes + col * a.xs_stride +
-                             4u * static_cast<uint32_t>(w + kGStream * cs.si);
-        // (the second column tile's operands are read too, one wait for all: for a chunk of
-        // <= 16 columns they are zeros and unused)
         uint4 a0, a1, a2, a3, xl, xh, yl, yh;
         uint32_t as, xs, ys;
         asm volatile(
@@ -3688,14 +3708,14 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
             "ds_read_b32 %4, %12 offset:4096\n\t"
             "ds_read_b128 %5, %13 offset:0\n\t"
             "ds_read_b128 %6, %14 offset:0\n\t"
-            "ds_read_b32 %7, %15 offset:0\n\t"
+            "ds_read_b32 %7, %15 offset:4096\n\t"
             "ds_read_b128 %8, %13 offset:2048\n\t"
             "ds_read_b128 %9, %14 offset:2048\n\t"
-            "ds_read_b32 %10, %16 offset:0\n\t"
+            "ds_read_b32 %10, %15 offset:4160\n\t"
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(as), "=&v"(xl), "=&v"(xh), "=&v"(xs), "=&v"(yl),
               "=&v"(yh), "=&v"(ys)
-            : "v"(sa + l * 16), "v"(sa + l * 4), "v"(xlo), "v"(xhi), "v"(xsa), "v"(xsa + 16 * a.xs_stride)
+            : "v"(sa + l * 16), "v"(sa + l * 4), "v"(xlo), "v"(xhi), "v"(sb + col * 4)
             : "memory");
         const uint4 av[4] = {a0, a1, a2, a3};
         {
@@ -3712,25 +3732,17 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
           for (int rt = 0; rt < 4; ++rt)
             acc[rt][1] = mfma_fp4_fp8(fp4_operand(av[rt]), b, acc[rt][1], static_cast<int>((as >> (8 * rt)) & 0xffu), sbv);
         }
-        // refill the slot just consumed (three slots ahead)
+        // refill the slot just consumed (two slots ahead)
         g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
-        g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, ic, true);
-        if (cs.si == m1 - 1) {
-          // the wave's part of the item is done: hand its partial tiles to the finisher once
-          // it has taken the previous ones
+        g_step(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
+        if (cs.si == NS1 - 1) {
+          // the item is done: SwiGLU and MXFP8 into the wave's staging area, once the loader
+          // has published the wave's previous item from it
 #pragma unroll
           for (int cc = 0; cc < kGTiles; ++cc) mfma_settle(acc[0][cc], acc[1][cc], acc[2][cc], acc[3][cc]);
-          g_wait_lds(lb + kGCons, cs.item, a.err);
-          const uint32_t rd = lb + a.o_red + static_cast<uint32_t>(w * 4 * kGTiles * 1024 + l * 16);
-#pragma unroll
-          for (int cc = 0; cc < kGTiles; ++cc)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-              lds_st16_async(rd + (cc * 4 + rt) * 1024,
-                             make_uint4(__float_as_uint(acc[rt][cc][0]), __float_as_uint(acc[rt][cc][1]),
-                                        __float_as_uint(acc[rt][cc][2]), __float_as_uint(acc[rt][cc][3])));
-          lds_settle_all();
-          if (l == 0) lds_st4(lb + kGProg + 4 * w, static_cast<uint32_t>(cs.item + 1));
+          g_wait_lds(lb + kGPub + 4 * w, cs.item, a.err);
+          g_finish(a, acc, ncc, stg);
+          if (l == 0) lds_st4(lb + kGStaged + 4 * w, static_cast<uint32_t>(cs.item + 1));
         }
       } else {
         // ---- two FC2 tiles, computed before the refill overwrites the slot; the refill
@@ -3738,153 +3750,62 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
         const int ti = cs.ti, chunk0 = cs.chunk, rt20 = cs.rt2;
         int chunk1 = chunk0, rt21 = rt20;
         g_next_tile(q.TPE, chunk1, rt21);
-        const GRows r0 =
-            g_fc2_tile<NS2>(a, lb, w, g0, ti < n2w, chunk0, rt20, sa, seq_cur, hop0, hop1, second, orow0, orow1);
-        const GRows r1 = g_fc2_tile<NS2>(a, lb, w, g0, ti + 1 < n2w, chunk1, rt21, sa + kGHalf, seq_cur, hop0, hop1,
-                                         second, orow0, orow1);
+        const GRows r0 = g_fc2_tile<NS2>(a, lb, w, g0, ti < n2w, chunk0, rt20, sa, seq_cur, hbl, hbs, orow0, orow1);
+        const GRows r1 =
+            g_fc2_tile<NS2>(a, lb, w, g0, ti + 1 < n2w, chunk1, rt21, sa + kGHalf, seq_cur, hbl, hbs, orow0, orow1);
         g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
-        g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, ic, true);
+        g_step(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
         g_store_rows(r0, rout);
         g_store_rows(r1, rout);
       }
-      g_step(a, q, lb, w, m1, n1el, n_el, n_chunks, cs, false);
+      g_step(a, q, lb, w, n1el, n_el, n_chunks, cs, false);
     }
     if (l == 0) lds_st4(lb + kGProg2 + 4 * w, 0x7fffffffu);
     wait_vm<0>();  // the dummy slots land before the wave ends
     return;
   }
 
-  const uint32_t call = static_cast<uint32_t>(lds_uni(lb + kGCall));
-  if (w == kGFin) {
-    // =============================================================== finisher wave
-#pragma unroll 1
-    for (int k = 0; k < q.n1; ++k) {
-      int ch, j;
-      g_item(q.c + k * q.nwg, n_chunks, HB, ch, j);
-      const int ncc = lds_u16(lb + kGTok + static_cast<uint32_t>((k * kChunkCols + 16) * 2)) == 0xffff ? 1 : 2;
-      v4f tot[kGTiles][4];
-#pragma unroll
-      for (int cc = 0; cc < kGTiles; ++cc)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) tot[cc][rt] = v4f{0.f, 0.f, 0.f, 0.f};
-      // each wave's partial tiles are added (in wave order) as soon as it posts them
-#pragma unroll 1
-      for (int ww = 0; ww < nw1; ++ww) {
-        g_wait(lb + kGProg + 4 * ww, k + 1, a.err);
-        const uint32_t rw = lb + a.o_red + static_cast<uint32_t>(ww * 4 * kGTiles * 1024 + l * 16);
-#pragma unroll
-        for (int cc = 0; cc < kGTiles; ++cc) {
-          if (cc < ncc) {
-            uint4 p0, p1, p2, p3;
-            lds_ld16x4v(rw + cc * 4096, rw + cc * 4096 + 1024, rw + cc * 4096 + 2048, rw + cc * 4096 + 3072, p0, p1,
-                        p2, p3);
-            const uint4 p[4] = {p0, p1, p2, p3};
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-              tot[cc][rt][0] += __uint_as_float(p[rt].x);
-              tot[cc][rt][1] += __uint_as_float(p[rt].y);
-              tot[cc][rt][2] += __uint_as_float(p[rt].z);
-              tot[cc][rt][3] += __uint_as_float(p[rt].w);
-            }
-          }
-        }
-      }
-      if (l == 0) lds_st4(lb + kGCons, static_cast<uint32_t>(k + 1));
-      // SwiGLU and MXFP8 of the block (experts page, store_hidden): lane (col, grp) holds
-      // hidden values 32j + 4grp + r (tile 0) and 32j + 16 + 4grp + r (tile 1) of column col
-#pragma unroll
-      for (int cc = 0; cc < kGTiles; ++cc) {
-        if (cc >= ncc) continue;
-        float h[2][4];
-        float amax = 0.0f;
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gv = tot[cc][half][r], uv = tot[cc][2 + half][r];
-            // SwiGLU with the hardware exponential and reciprocal (a few ulp in FP32; the
-            // hidden is then rounded to 3 mantissa bits)
-            h[half][r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-            amax = fmaxf(amax, fabsf(h[half][r]));
-          }
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const int e = mx_exponent(amax, a.floor_rule != 0);
-        const float sc = exp2_neg(e);
-        uint32_t word[2];
-        auto clampf = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };  // the floor rule saturates
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-          word[half] = cvt4_e4m3(clampf(h[half][0] * sc), clampf(h[half][1] * sc), clampf(h[half][2] * sc),
-                                 clampf(h[half][3] * sc));
-        const int cl = cc * 16 + col;
-        uint8_t* dst = a.hid + (static_cast<int64_t>(ch) * kChunkCols + cl) * a.colb;
-        st_dev_u32(dst + 32 * j + 4 * grp, word[0]);
-        st_dev_u32(dst + 32 * j + 16 + 4 * grp, word[1]);
-        if (grp == 0) st_dev_u8(dst + a.IP + j, static_cast<uint8_t>(e + 127));
-        if (a.dump_codes != nullptr) {
-          const int pair = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
-          if (pair >= 0) {
-            uint8_t* dc = a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 4 * grp;
-            *reinterpret_cast<uint32_t*>(dc) = word[0];
-            *reinterpret_cast<uint32_t*>(dc + 16) = word[1];
-            if (grp == 0) a.dump_scales[static_cast<int64_t>(pair) * HB + j] = static_cast<uint8_t>(e + 127);
-          }
-        }
-      }
-      // publish: the block's codes and scales (sc1) before its flag
-      wait_stores();
-      if (l == 0) st_dev_u32(a.flags + static_cast<int64_t>(ch) * HB + j, call);
-    }
-    // the call counters for the next call (every counter c, c + grid, ... below kMaxGrid,
-    // so that all stay equal whatever grid the next call uses)
-#pragma unroll 1
-    for (int m = c + l * nwg; m < kMaxGrid; m += 64 * nwg) st_dev_u32(a.calls + m, call);
-    return;
-  }
   // ================================================================= loader wave
-  // FC1: the x scales of the workgroup's items (32 columns x D/32 bytes, column c at
-  // c * xs_stride) into the two x-scale buffers, item k into buffer k & 1 once every FC1
-  // wave has finished item k - 2 with it.
-  {
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.plan), static_cast<short>(0), static_cast<int>(a.plan_bytes), 0x00020000);
-    const int pc = static_cast<int>(a.xs_stride / 16), parts = a.D / 512;  // 16-byte parts per column: slot, real
-    const int n_dma = static_cast<int>(a.xs_bytes / 1024);
+  const uint32_t call = static_cast<uint32_t>(lds_uni(lb + kGCall));
+  // FC1: publish the staged hidden blocks in the workgroup's item order (item k is wave
+  // k mod 8's (k / 8)-th): codes and scale of each column (device-coherent stores), then
+  // the block's flag with the call number
 #pragma unroll 1
-    for (int k = 0; k < q.n1; ++k) {
-      if (k >= 2) {
-#pragma unroll 1
-        for (int ww = 0; ww < nw1; ++ww) g_wait(lb + kGProg + 4 * ww, k - 1, a.err);
+  for (int k = 0; k < q.n1; ++k) {
+    const int ww = k % kGStream, m = k / kGStream;
+    g_wait(lb + kGStaged + 4 * ww, m + 1, a.err);
+    int ch, j;
+    g_item(c + k * nwg, n_chunks, HB, ch, j);
+    const uint32_t stg = lb + a.o_hid + static_cast<uint32_t>(ww) * kGStage;
+    const int cl = l >> 1, part = l & 1;  // lane: 16 code bytes of column cl
+    const uint4 v = lds_ld16(stg + static_cast<uint32_t>(cl * 32 + 16 * part));
+    const uint32_t sc = lds_ld4(stg + 1024 + 4 * static_cast<uint32_t>(cl));
+    uint8_t* dst = a.hid + (static_cast<int64_t>(ch) * kChunkCols + cl) * a.colb;
+    st_dev_u64(dst + 32 * j + 16 * part, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
+    st_dev_u64(dst + 32 * j + 16 * part + 8, static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32));
+    if (part == 0) st_dev_u8(dst + a.IP + j, static_cast<uint8_t>(sc));
+    if (a.dump_codes != nullptr) {
+      const int pair = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
+      if (pair >= 0) {
+        *reinterpret_cast<uint4*>(a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 16 * part) = v;
+        if (part == 0) a.dump_scales[static_cast<int64_t>(pair) * HB + j] = static_cast<uint8_t>(sc);
       }
-      const uint32_t dst = a.o_xs + static_cast<uint32_t>(k & 1) * a.xs_bytes;
-      const uint32_t tb = lb + kGTok + static_cast<uint32_t>(k * kChunkCols * 2);
-#pragma unroll 1
-      for (int i = 0; i < n_dma; ++i) {
-        const int L = 64 * i + l, col = L / pc, part = L - col * pc;
-        const int tok = col < kChunkCols ? lds_u16(tb + 2 * col) : 0xffff;
-        const uint32_t off = tok != 0xffff && part < parts
-                                 ? static_cast<uint32_t>(a.B * a.D + tok * (a.D / 32) + 16 * part)
-                                 : kOutside;
-        bdma16(rx, off, dst + 1024u * static_cast<uint32_t>(i));
-      }
-      wait_vm<0>();
-      lds_settle_all();
-      if (l == 0) lds_st4(lb + kGXs, static_cast<uint32_t>(k + 1));
     }
+    wait_stores();
+    if (l == 0) st_dev_u32(a.flags + static_cast<int64_t>(ch) * HB + j, call);
+    if (l == 0) lds_st4(lb + kGPub + 4 * ww, static_cast<uint32_t>(m + 1));
   }
   // FC2: for each chunk of the workgroup's run, in order: wait for its HB block flags,
   // then copy its hidden (codes and scales, device-coherent DMA) and its columns' pair
-  // indices into one of the two LDS hidden buffers.  The buffers share LDS with the FC1
-  // partial tiles, so the first copy waits until the finisher has read the last of them.
+  // indices into the LDS hidden buffer (which held the staging areas during FC1), once
+  // every streaming wave is done with the previous chunk.
   const int nseq = q.n2 > 0 ? (q.first2 + q.n2 - 1) / q.TPE - g0 + 1 : 0;
-  if (nseq > 0) g_wait(lb + kGCons, q.n1, a.err);
 #pragma unroll 1
   for (int seq = 0; seq < nseq; ++seq) {
     const int ch = g0 + seq;
-    if (seq >= 2) {
+    if (seq >= 1) {
 #pragma unroll 1
-      for (int ww = 0; ww < kGStream; ++ww) g_wait(lb + kGProg2 + 4 * ww, seq - 1, a.err);
+      for (int ww = 0; ww < kGStream; ++ww) g_wait(lb + kGProg2 + 4 * ww, seq, a.err);
     }
     const uint32_t* f = a.flags + static_cast<int64_t>(ch) * HB;
 #pragma unroll 1
@@ -3898,7 +3819,7 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
       __builtin_amdgcn_s_sleep(1);
     }
     compiler_fence();
-    const uint32_t hb = a.o_hid + static_cast<uint32_t>(seq & 1) * a.hid_bytes;  // offset from smem
+    const uint32_t hb = a.o_hid;  // offset from smem
     const uint8_t* src = a.hid + static_cast<int64_t>(ch) * kChunkCols * a.colb;
     for (uint32_t off = 0; off < a.hid_code_bytes; off += 1024)
       __builtin_amdgcn_global_load_lds(src + off + l * 16, (lds_void*)(smem + hb + off), 16, 0, 16 /* sc1 */);
@@ -3910,6 +3831,10 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
     lds_settle_all();
     if (l == 0) lds_st4(lb + kGReady, static_cast<uint32_t>(seq + 1));
   }
+  // the call counters for the next call (every counter c, c + grid, ... below kMaxGrid,
+  // so that all stay equal whatever grid the next call uses)
+#pragma unroll 1
+  for (int m = c + l * nwg; m < kMaxGrid; m += 64 * nwg) st_dev_u32(a.calls + m, call);
 }
 
 using ExpertsFn = void (*)(ExpArgs);
@@ -4120,44 +4045,39 @@ GFn pick_g(int ns2) {
   switch (ns2) {
     case 1: return grouped_kernel<1>;
     case 2: return grouped_kernel<2>;
-    case 3: return grouped_kernel<3>;
-    default: return grouped_kernel<4>;
+    default: return grouped_kernel<3>;
   }
 }
 
 // LDS layout of the grouped kernel for (D, I).
 struct GLds {
-  uint32_t colb, code_bytes, hid_bytes;   // hidden column bytes; a hidden buffer's codes, and all of it
-  uint32_t o_ring, o_xs, xs_bytes, xs_stride, o_red, o_hid;
+  uint32_t colb, code_bytes, hid_bytes;   // hidden column bytes; the hidden buffer's codes, and all of it
+  uint32_t o_ring, o_hid;
   size_t total;
 };
 GLds grouped_lds(int D, int I) {
+  (void)D;
   GLds g;
   const int IP = (I + 127) / 128 * 128;
   g.colb = static_cast<uint32_t>(IP + 16);
   g.code_bytes = (kChunkCols * g.colb + 1023u) / 1024u * 1024u;
   g.hid_bytes = g.code_bytes + 4u * kChunkCols;
   g.o_ring = (kGTables + 15u) / 16u * 16u;
-  // x scales: a column's D/32 bytes at a stride with bit 4 set (an odd number of 16-byte
-  // units), so that the 16 columns of a read fall in different LDS banks
-  g.xs_stride = static_cast<uint32_t>(D / 32) | 16u;
-  g.xs_bytes = (kChunkCols * g.xs_stride + 1023u) / 1024u * 1024u;
-  g.o_xs = g.o_ring + kGStream * kGR * kGSlot;
-  g.o_red = g.o_xs + 2u * g.xs_bytes;
-  g.o_hid = g.o_red;  // FC1's partial tiles, then FC2's hidden buffers
-  const uint32_t red_bytes = kGStream * 4 * kGTiles * 1024;
-  g.total = g.o_hid + (2u * g.hid_bytes > red_bytes ? 2u * g.hid_bytes : red_bytes);
+  g.o_hid = g.o_ring + kGStream * kGR * kGSlot;  // FC1's staging areas, then FC2's hidden buffer
+  const uint32_t stage = kGStream * kGStage;
+  g.total = g.o_hid + (g.hid_bytes > stage ? g.hid_bytes : stage);
   return g;
 }
 constexpr size_t kGLdsMax = 160 * 1024;  // LDS of a gfx950 workgroup
 
 // The grouped kernel's limits: its LDS tables hold kGChunks chunks and kGItems FC1 items
-// per workgroup; I <= 512; its LDS layout fits.
+// per workgroup; I <= 384 (three FC2 K steps: nine waves share a SIMD's registers, and
+// a fourth K step would not fit them); its LDS layout fits.
 bool grouped_fits(int E, int D, int I, int B, int K, int grid) {
   const int64_t U = static_cast<int64_t>(B) * K;
   const int64_t chunks = max_chunks_for(U, U < E ? U : E);
   const int64_t items = (chunks * (I / 32) + grid - 1) / grid;
-  return I <= 512 && chunks <= kGChunks && items <= kGItems && grouped_lds(D, I).total <= kGLdsMax;
+  return I <= 384 && chunks <= kGChunks && items <= kGItems && grouped_lds(D, I).total <= kGLdsMax;
 }
 
 int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, int32_t B,
@@ -4217,13 +4137,8 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   a.out_bytes = static_cast<uint32_t>(static_cast<int64_t>(B) * topk * D * 2);
   a.colb = G.colb;
   a.o_ring = G.o_ring;
-  a.o_red = G.o_red;
   a.o_hid = G.o_hid;
-  a.hid_bytes = G.hid_bytes;
   a.hid_code_bytes = G.code_bytes;
-  a.o_xs = G.o_xs;
-  a.xs_bytes = G.xs_bytes;
-  a.xs_stride = G.xs_stride;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kGWG), lds, as_stream(stream), a);
   return launch_status();
 }

@@ -75,7 +75,7 @@ class MoeLayer:
         form runs decode_whole_kernel for batches within its limits (at most 128 distinct
         experts, B*topk <= 640, B*D/32 <= 2560, I <= 512) unless another exchange is asked
         for.  The grouped form runs grouped_kernel where the batch fits its tables (I <=
-        512, at most 1024 chunks of 32 routes and 32 FC1 blocks per workgroup, with one
+        384, at most 1024 chunks of 32 routes and 32 FC1 blocks per workgroup, with one
         workgroup per compute unit unless a grid is given) unless col_tiles is 1.  Everything
         else runs experts_kernel."""
         decode = path == "decode" or (path == "auto" and self.AUTO_DECODE and B <= self.DECODE_MAX)
@@ -85,7 +85,7 @@ class MoeLayer:
             return "decode_whole_kernel" if exchange in (None, 0) and whole else "experts_kernel (decode form)"
         chunks = min(self.E, routes) + (routes + 31) // 32
         g = grid or min(torch.cuda.get_device_properties(self.device).multi_processor_count, 2048)
-        fits = self.I <= 512 and chunks <= 1024 and (chunks * (self.I // 32) + g - 1) // g <= 32
+        fits = self.I <= 384 and chunks <= 1024 and (chunks * (self.I // 32) + g - 1) // g <= 32
         return "grouped_kernel" if col_tiles != 1 and fits else "experts_kernel"
 
     def experts(self, B: int, out: torch.Tensor, *, replica: int = 0, stream=None, **opts):
