@@ -80,6 +80,22 @@ size_t moe_units_bytes(int32_t B, int32_t topk, int32_t E);
  * the B_max it was sized for.  0 on invalid sizes. */
 size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32_t topk);
 
+/* The static work split of one experts launch, evaluated on the host (no device call;
+ * for checking schedules on any machine).  It is the persistent grid's division of the
+ * work among its workgroups (experts page, ExpertsKernel: each CTA's FC1 blocks and
+ * its FC2 tile range).  form 0: the decode form's whole-K kernel, `groups` distinct
+ * experts (<= 128, I <= 512); form 1: the grouped form, `groups` chunks of up to 32
+ * routes of one expert (<= 1024).  An FC1 item is one 32-wide hidden block of one group;
+ * there are groups * I/32 of them, and item i goes to workgroup i mod grid.  FC2 tiles
+ * are the 16-row output tiles, groups * D/16 of them in group-major order.
+ * Outputs are host pointers:
+ *   split i32 [grid, 4]: per workgroup {FC1 items, first FC2 tile, FC2 tiles, streaming
+ *     waves per workgroup};
+ *   items i32 [groups * I/32, 2] (may be NULL): (group, hidden block) of item i.
+ * MOE_EINVAL for a bad form, shape, group count or grid (1..2048). */
+int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t grid, int32_t* split,
+                   int32_t* items);
+
 /* Bytes of the four packed weight buffers written by moe_pack_weights (experts page,
  * ExpertsKernel.schedule / produce: the weights stream tile by tile, 128 K at a time).
  * They equal the canonical sizes (the packing only reorders 16-byte code runs and scale
@@ -140,8 +156,8 @@ int moe_group(const int32_t* ids_dev, int32_t B, int32_t topk, int32_t E, void* 
 /* moe_plan and moe_group of one batch in a single launch (experts page, plan_chunk and
  * ExpertsKernel.group; the same outputs, bit for bit):
  * x_dev BF16 [B, D] -> plan_dev (moe_plan layout), ids_dev i32 [B, topk] -> units_dev
- * (moe_group layout).  One workgroup builds the unit table while the others quantize x,
- * which saves a launch per step of the grouped form.  Arguments and errors as the two
+ * (moe_group layout).  Eight workgroups build the unit table while the others quantize
+ * x, which saves a launch per step of the grouped form.  Arguments and errors as the two
  * calls. */
 int moe_plan_group(const void* x_dev, const int32_t* ids_dev, int32_t B, int32_t D, int32_t topk, int32_t E,
                    void* plan_dev, size_t plan_bytes, void* units_dev, size_t units_bytes, void* stream);

@@ -68,6 +68,7 @@ def _load():
         "moe_decode_run_noalloc": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_int32,
                                              c.c_int32, P, c.c_size_t, P]),
         "moe_combine": (c.c_int, [P, c.c_size_t, P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
+        "moe_work_split": (c.c_int, [c.c_int32] * 5 + [P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -78,7 +79,7 @@ def _load():
 lib = _load()
 EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_units_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
             "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_plan_group", "moe_units_export",
-            "moe_experts_run", "moe_decode_run", "moe_decode_run_noalloc", "moe_combine")
+            "moe_experts_run", "moe_decode_run", "moe_decode_run_noalloc", "moe_combine", "moe_work_split")
 
 
 def status_string(status: int) -> str:
@@ -122,6 +123,16 @@ def moe_packed_weight_bytes(E: int, D: int, I: int):
     out = [ctypes.c_size_t(0) for _ in range(4)]
     _check("moe_packed_weight_bytes", lib.moe_packed_weight_bytes(E, D, I, *[ctypes.byref(o) for o in out]))
     return tuple(o.value for o in out)
+
+
+def moe_work_split(form: int, groups: int, D: int, I: int, grid: int):
+    """Host-side static split of an experts launch: (split [grid, 4], items [groups*I/32, 2])
+    as numpy int32 arrays (no device call)."""
+    import numpy as np
+    split = np.zeros((grid, 4), np.int32)
+    items = np.zeros((max(groups * (I // 32), 1), 2), np.int32)
+    _check("moe_work_split", lib.moe_work_split(form, groups, D, I, grid, split.ctypes.data, items.ctypes.data))
+    return split, items[:groups * (I // 32)]
 
 
 def moe_pack_weights(E, D, I, w13, s13, w2, s2, w13p, s13p, w2p, s2p, stream=None):

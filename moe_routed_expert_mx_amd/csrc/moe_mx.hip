@@ -39,7 +39,11 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 constexpr int kStream = 4;        // streaming waves per experts workgroup
 constexpr int kWG = 64 * (kStream + 1);  // plus one control wave
 constexpr int kGroupThreads = 1024;
-constexpr uint32_t kSpinLimit = 1u << 22;  // polls of a flag before giving up
+// Bounds of the waits on other waves' progress: far beyond any legitimate wait (a launch
+// lasts well under a millisecond), short enough that a broken invariant ends the launch
+// within tens of milliseconds.
+constexpr uint32_t kSpinLimit = 1u << 19;  // polls of an LDS word (~40 ms)
+constexpr uint32_t kPollLimit = 1u << 16;  // polls of a global flag (15-60 ms)
 
 // ------------------------------------------------------------------ formats
 // E8M0 exponent of an MX block from its absolute maximum (experts page, mx_block and
@@ -97,6 +101,14 @@ __device__ __forceinline__ void st_dev_u32(void* p, uint32_t v) {
 }
 __device__ __forceinline__ void st_dev_u64(void* p, uint64_t v) {
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Give-up test of a bounded wait on flags in global memory: true after kPollLimit polls
+// (tens of milliseconds), or, checked every 256 polls, once any wave of the launch has
+// given up and set bit 2 of the status word, so that one broken wait ends the others
+// within about a millisecond instead of each running out its own bound.
+__device__ __forceinline__ bool poll_expired(uint32_t spins, const int32_t* err) {
+  return (spins & 255u) == 255u && (spins >= kPollLimit || (ld_dev_u32(err) & 4u) != 0);
 }
 __device__ __forceinline__ void st_dev_u8(void* p, uint8_t v) {
   __hip_atomic_store(reinterpret_cast<uint8_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -823,7 +835,7 @@ __device__ __forceinline__ void lds_st4(uint32_t addr, uint32_t v) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(v) : "memory");
 }
 
-// Waits (bounded, a fraction of a second) until the LDS word at addr reaches `want`
+// Waits (bounded, tens of milliseconds) until the LDS word at addr reaches `want`
 // (>= or ==).  The waves of a workgroup hand work to each other through such words; a
 // wait that runs out sets bit 2 of the unit-table flags and goes on.
 template <bool EQ>
@@ -1918,7 +1930,7 @@ __device__ __forceinline__ void control_block(const ExpArgs& a, const LdsMap& m,
     #pragma unroll 1
     for (uint32_t spins = 0;; ++spins) {
       if (ld_dev_u32(a.arrive + b) == want) break;
-      if (spins == kSpinLimit) {
+      if (poll_expired(spins, a.err)) {
         if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -1976,7 +1988,7 @@ __device__ __forceinline__ void wait_chunk(const ExpArgs& a, int chunk, uint32_t
     bool ok = true;
     for (int i = l; i < a.HB; i += 64) ok = ok && ld_dev_u32(f + i) == want;
     if (__all(ok)) break;
-    if (spins == kSpinLimit) {
+    if (poll_expired(spins, a.err)) {
       if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
@@ -2121,7 +2133,7 @@ __device__ __forceinline__ void dec_hidden(const ExpArgs& a, const LdsMap& m, ui
     for (uint32_t spins = 0;; ++spins) {
       const bool ok = !probe || static_cast<uint32_t>(ld_dev_u64(pp) >> 32) == want;
       if (__all(ok)) break;
-      if (spins == kSpinLimit) {
+      if (poll_expired(spins, a.err)) {
         if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -2183,7 +2195,7 @@ __device__ __forceinline__ void dec_hidden(const ExpArgs& a, const LdsMap& m, ui
 #pragma unroll
       for (int s = 0; s < kRound; ++s) ok = ok && (s >= nb || static_cast<uint32_t>(v[s] >> 32) == want);
       if (__all(ok)) break;
-      if (spins == kSpinLimit) {
+      if (poll_expired(spins, a.err)) {
         if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -2626,7 +2638,12 @@ struct QWork {
   int TPE, nwg, c;
 };
 
-__device__ __forceinline__ QWork q_work(int G, int HB, int NS1, int D, int nwg, int c, int w, int item,
+// FC2 tiles that stream as long as one FC1 item (34 / (NS2 + 1/4) per 1024 columns of D:
+// an item's K steps against a tile's NS2 steps plus its scales).
+__host__ __device__ inline int q_item_tiles(int D, int NS2) { return 34 * D / (NS2 * 1024 + 256); }
+
+// Callable on the host too (moe_work_split evaluates it there for schedule checks).
+__host__ __device__ inline QWork q_work(int G, int HB, int NS1, int D, int nwg, int c, int w, int item,
                                         int nst = kQStream) {
   QWork q;
   const int N1 = G * HB;
@@ -2814,7 +2831,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   const int G = __builtin_amdgcn_readfirstlane(static_cast<int>(sw[kQGCount / 4]));
   __syncthreads();
 
-  const QWork q = q_work(G, HB, NS1, D, nwg, c, w < kQStream ? w : 0, 34 * D / (NS2 * 1024 + 256));
+  const QWork q = q_work(G, HB, NS1, D, nwg, c, w < kQStream ? w : 0, q_item_tiles(D, NS2));
   const __amdgpu_buffer_rsrc_t none =
       __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
   const int nw1 = NS1 < kQStream ? NS1 : kQStream;  // waves that take FC1 steps
@@ -3117,7 +3134,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   #pragma unroll
         for (int u = 0; u < kQPoll; ++u) ok = ok && (u * 64 + l >= n || static_cast<uint32_t>(v[u] >> 32) == call);
         if (__all(ok)) break;
-        if (spins == kSpinLimit) {
+        if (poll_expired(spins, a.err)) {
           if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
@@ -3156,7 +3173,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
             ok = ok && (idx >= n || static_cast<uint32_t>(v[u] >> 32) == call);
           }
           if (__all(ok)) break;
-          if (spins == kSpinLimit) {
+          if (poll_expired(spins, a.err)) {
             if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
@@ -3261,7 +3278,7 @@ __device__ __forceinline__ int lds_u16(uint32_t addr) {
 // 8 (in the chunk groups of eight; the last, partial group is interleaved), so that with
 // item i dealt to workgroup i mod grid they run on workgroups of one XCD (workgroup c runs
 // on XCD c mod 8).
-__device__ __forceinline__ void g_item(int i, int n_chunks, int HB, int& ch, int& j) {
+__host__ __device__ inline void g_item(int i, int n_chunks, int HB, int& ch, int& j) {
   const int full = (n_chunks >> 3) * 8 * HB;
   if (i < full) {
     const int g = i / (8 * HB), r = i - g * 8 * HB;
@@ -3274,14 +3291,32 @@ __device__ __forceinline__ void g_item(int i, int n_chunks, int HB, int& ch, int
   }
 }
 
+// The grouped form's split of a launch (callable on the host too): FC1 items i = c + k *
+// grid (each a whole hidden block of one chunk), and FC2 tiles in equal contiguous runs
+// in chunk order (every workgroup's FC1 items run side by side in its waves, so all
+// finish at about the same time).
+__host__ __device__ inline QWork g_work(int n_chunks, int HB, int NS1, int D, int nwg, int c) {
+  QWork q;
+  q.nwg = nwg;
+  q.c = c;
+  q.TPE = D / 16;
+  q.m1 = NS1;
+  const int N1 = n_chunks * HB, N2 = n_chunks * q.TPE, cap = (N2 + nwg - 1) / nwg;
+  q.n1 = N1 / nwg + (c < N1 % nwg ? 1 : 0);
+  q.first2 = c * cap < N2 ? c * cap : N2;
+  q.n2 = N2 - q.first2 < cap ? N2 - q.first2 : cap;
+  return q;
+}
+
 // Bounded LDS wait of the streaming waves.  They wait only on words that their own
 // workgroup's loader posts, whose own waits are bounded, so it reads no global memory (a
-// global read would wait for the wave's ring); its own bound (~1 s) is a last resort.
+// global read would wait for the wave's ring); its own bound, twice the loader's, is a
+// last resort.
 __device__ __forceinline__ void g_wait_lds(uint32_t addr, int want, int32_t* err) {
 #pragma unroll 1
   for (uint32_t spins = 0;; ++spins) {
     if (lds_uni(addr) >= want) return;
-    if (spins == (1u << 24)) {
+    if (spins == 2 * kSpinLimit) {
       if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
@@ -3289,14 +3324,14 @@ __device__ __forceinline__ void g_wait_lds(uint32_t addr, int want, int32_t* err
   }
 }
 
-// Bounded LDS wait of the loader: gives up (status bit 2) after ~0.1 s, or soon after
-// another wave of the call has given up.
+// Bounded LDS wait of the loader: gives up (status bit 2) after kSpinLimit polls, or
+// soon after another wave of the call has given up.
 __device__ __forceinline__ void g_wait(uint32_t addr, int want, int32_t* err) {
 #pragma unroll 1
   for (uint32_t spins = 0;; ++spins) {
     if (lds_uni(addr) >= want) return;
     if ((spins & 1023u) == 1023u) {
-      const bool stop = spins >= (1u << 20) || (ld_dev_u32(err) & 4u) != 0;
+      const bool stop = spins >= kSpinLimit || (ld_dev_u32(err) & 4u) != 0;
       if (stop) {
         if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_or(err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
@@ -3630,20 +3665,7 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
   if (tid == 0) sw[kGCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
   __syncthreads();
 
-  // FC1 items i = c + k * grid; FC2 tiles: equal contiguous runs in chunk order (every
-  // workgroup's FC1 items run side by side in its waves, so all finish at about the same
-  // time)
-  QWork q;
-  q.nwg = nwg;
-  q.c = c;
-  q.TPE = a.D / 16;
-  q.m1 = NS1;
-  {
-    const int N1 = n_chunks * HB, N2 = n_chunks * q.TPE, cap = (N2 + nwg - 1) / nwg;
-    q.n1 = N1 / nwg + (c < N1 % nwg ? 1 : 0);
-    q.first2 = c * cap < N2 ? c * cap : N2;
-    q.n2 = N2 - q.first2 < cap ? N2 - q.first2 : cap;
-  }
+  const QWork q = g_work(n_chunks, HB, NS1, a.D, nwg, c);
   const int g0 = q.first2 / q.TPE;  // chunk of the workgroup's first FC2 tile (sequence 0)
   const __amdgpu_buffer_rsrc_t none =
       __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
@@ -3812,7 +3834,7 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
     for (uint32_t spins = 0;; ++spins) {
       const bool ok = l >= HB || ld_dev_u32(f + l) == call;
       if (__all(ok)) break;
-      if ((spins & 255u) == 255u && (spins >= (1u << 16) || (ld_dev_u32(a.err) & 4u) != 0)) {
+      if (poll_expired(spins, a.err)) {
         if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -4346,6 +4368,33 @@ size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32
   if (!shape_ok(E, D, I) || B_max < 1 || topk < 1 || topk > 64 || static_cast<int64_t>(B_max) * topk > 65536)
     return 0;
   return ws_layout(E, D, I, topk, B_max).end;
+}
+
+int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t grid, int32_t* split,
+                   int32_t* items) {
+  if ((form != 0 && form != 1) || groups < 0 || !shape_ok(1, D, I) || grid < 1 || grid > kMaxGrid ||
+      split == nullptr)
+    return MOE_EINVAL;
+  const int HB = I / 32, NS1 = D / 128, NS2 = (I + 127) / 128;
+  if (form == 0 && (groups > kQGMax || HB > kQHB)) return MOE_EINVAL;
+  if (form == 1 && groups > kGChunks) return MOE_EINVAL;
+  for (int c = 0; c < grid; ++c) {
+    const QWork q = form == 0 ? q_work(groups, HB, NS1, D, grid, c, 0, q_item_tiles(D, NS2))
+                              : g_work(groups, HB, NS1, D, grid, c);
+    split[4 * c] = q.n1;
+    split[4 * c + 1] = q.first2;
+    split[4 * c + 2] = q.n2;
+    split[4 * c + 3] = form == 0 ? kQStream : kGStream;
+  }
+  if (items != nullptr) {
+    for (int i = 0; i < groups * HB; ++i) {
+      int g = i / HB, j = i - (i / HB) * HB;
+      if (form == 1) g_item(i, groups, HB, g, j);
+      items[2 * i] = g;
+      items[2 * i + 1] = j;
+    }
+  }
+  return MOE_OK;
 }
 
 int moe_packed_weight_bytes(int32_t E, int32_t D, int32_t I, size_t* w13_bytes, size_t* s13_bytes,

@@ -94,8 +94,19 @@ def test_combine_edge_shapes(B, K, D):
 @pytest.mark.gpu
 @pytest.mark.parametrize("name", ["tiny", "decode_b8"])
 def test_combine_after_experts(name):
-    """End to end: the experts kernel's rows, combined on the GPU, against the oracle's
-    rows combined by the oracle (rows are within the output tolerance of each other)."""
+    """End to end: the experts kernel's rows, combined on the GPU.
+
+    Two bars.  (1) The combine itself, on the kernel's own rows: the _check bar above.
+    (2) Against the oracle's rows combined by the oracle: per token, rel-L2 <= 1e-2, and
+    each element within the route bar carried through the weighted sum.  A route's bar is
+    max-abs <= 2e-2 x RMS of its oracle row plus half a BF16 ulp of its largest element;
+    a route with a hidden code that FP32 summation order flipped may exceed it (the
+    experts parity tests bound each such route by its flip's FC2 image), so such routes
+    are counted (at most 1 %) and carry their own measured deviation.  The combine adds
+    K route errors with weights w[t, s], so the token's bound is sum_s w[t, s] x (route
+    bar), plus the FP32 accumulation bound and half a BF16 ulp of each combined row.  A
+    bar scaled by the combined row's own RMS would not hold: the errors add linearly,
+    while the RMS of a weighted sum of K nearly independent rows adds in quadrature."""
     from moe_routed_expert_mx_amd.layer import MoeLayer
     m = _lib()
     d = workloads.generate(name)
@@ -105,15 +116,38 @@ def test_combine_after_experts(name):
     x = torch.from_numpy(d["x"]).to(DEV)
     ids = torch.from_numpy(d["ids"]).to(DEV)
     rows = layer.forward(x, ids)
+    weights = d["weights"].astype(np.float32)
     out = torch.empty(w.B, w.D, dtype=torch.bfloat16, device=DEV)
-    m.moe_combine(rows, torch.from_numpy(d["weights"].astype(np.float32)).to(DEV), out)
+    m.moe_combine(rows, torch.from_numpy(weights).to(DEV), out)
     torch.cuda.synchronize()
+    got16 = out.view(torch.uint16).cpu().numpy()
+    _check(rows.view(torch.uint16).cpu().numpy(), weights, got16)
     codes, scales = oracle.plan(d["x"])
     ref_rows = oracle.experts(d["w13"], d["s13"], d["w2"], d["s2"], codes, scales, d["ids"],
                               hidden_floor=oracle.default_hidden_floor(w.I))["out"]
-    ref = bf16_to_f64(oracle.combine(ref_rows, d["weights"].astype(np.float32), w.B, w.K))
-    got = bf16_to_f64(out.view(torch.uint16).cpu().numpy())
+    ref = bf16_to_f64(oracle.combine(ref_rows, weights, w.B, w.K))
+    got = bf16_to_f64(got16)
     rel = np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
-    rms = np.sqrt(np.mean(ref * ref, axis=1))
     assert np.all(rel <= 1e-2), rel.max()
-    assert np.all(np.abs(got - ref).max(axis=1) <= 2e-2 * rms * 4)
+    r = bf16_to_f64(ref_rows).reshape(w.B, w.K, w.D)
+    y = bf16_to_f64(rows.view(torch.uint16).cpu().numpy()).reshape(w.B, w.K, w.D)
+    plain = 2e-2 * np.sqrt(np.mean(r * r, axis=2)) + _half_ulp(np.abs(r).max(axis=2))
+    dev = np.abs(y - r).max(axis=2)
+    n_over = int((dev > plain).sum())
+    assert n_over <= max(1, w.B * w.K // 100), f"{n_over} routes over the plain route bar"
+    route_bar = np.maximum(plain, dev)
+    wt = weights.astype(np.float64)
+    acc = (w.K + 1) * 2.0 ** -24 * (np.abs(wt)[:, :, None] * np.abs(y)).sum(axis=1).max(axis=1)
+    # both combined rows are rounded to BF16 once: half an ulp each
+    bound = (np.abs(wt) * route_bar).sum(axis=1) + acc + _half_ulp(np.abs(ref).max(axis=1)) + \
+        _half_ulp(np.abs(got).max(axis=1))
+    worst = np.abs(got - ref).max(axis=1)
+    assert np.all(worst <= bound), f"max-abs over the carried bar: {(worst / bound).max()}"
+    log(f"  routes over the plain bar: {n_over}")
+    log(f"  max-abs / carried bar: {(worst / bound).max():.3f}")
+
+
+def _half_ulp(a):
+    """Half a BF16 ulp at magnitude a (normal range)."""
+    ex = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (ex - 8), 0.0)

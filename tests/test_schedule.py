@@ -1,0 +1,287 @@
+"""The experts launches' static work split and their waves' wait protocol, checked on
+the CPU.
+
+The split comes from the library itself (moe_work_split evaluates the kernels' own
+split functions on the host), so these tests check the code that runs, not a copy.
+
+* Cover: every FC1 item (one 32-wide hidden block of one group) goes to exactly one
+  workgroup, and the FC2 runs partition the output tiles.
+* Protocol: each workgroup's waves are modelled as ordered lists of posts and waits on
+  their workgroup's LDS words, and on global block flags, in the order the kernels take
+  them (experts page, ExpertsKernel: a co-resident grid whose CTAs wait on other CTAs'
+  hidden blocks).  Running every wave as far as its waits allow must finish every wave:
+  no wait cycle, for every split tested.
+* Give-up: with one published block missing, the bounded waits end every wave, and the
+  global waits end within one status poll period of the first give-up (each reads the
+  status word every 256 polls).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+INF = 1 << 30
+QSTREAM = 8          # streaming waves of either form (returned by moe_work_split too)
+
+
+@pytest.fixture(scope="module")
+def m():
+    import moe_routed_expert_mx_amd as pkg
+    return pkg
+
+
+def _cases():
+    shapes = [(3584, 384), (7168, 256), (512, 32), (1024, 96), (2048, 512), (7168, 384)]
+    groups = [0, 1, 2, 3, 7, 13, 65, 128]
+    grids = [1, 2, 7, 8, 33, 64, 256, 257]
+    return shapes, groups, grids
+
+
+# ---------------------------------------------------------------------------- cover
+@pytest.mark.parametrize("form", [0, 1])
+def test_split_covers_items_and_tiles(m, form):
+    shapes, groups, grids = _cases()
+    for (D, I), G, grid in itertools.product(shapes, groups, grids):
+        if form == 1 and I > 384:
+            continue
+        HB, TPE = I // 32, D // 16
+        split, items = m.moe_work_split(form, G, D, I, grid)
+        n1, first2, n2 = split[:, 0], split[:, 1], split[:, 2]
+        assert (split[:, 3] == QSTREAM).all()
+        # FC1: item i to workgroup i mod grid, n1[c] of them
+        assert n1.sum() == G * HB
+        for c in range(grid):
+            assert n1[c] == len(range(c, G * HB, grid)), (form, D, I, G, grid, c)
+        # items are a bijection onto (group, block)
+        pairs = set(map(tuple, items.tolist()))
+        assert len(pairs) == G * HB
+        assert pairs == {(g, j) for g in range(G) for j in range(HB)}
+        # FC2 runs partition [0, G * TPE)
+        assert (n2 >= 0).all() and n2.sum() == G * TPE
+        live = np.flatnonzero(n2 > 0)
+        order = live[np.argsort(first2[live], kind="stable")]
+        pos = 0
+        for c in order:
+            assert first2[c] == pos, (form, D, I, G, grid, c)
+            pos += n2[c]
+        assert pos == G * TPE
+
+
+def test_grouped_items_of_a_chunk_share_an_xcd(m):
+    """Grouped form: with a grid that is a multiple of eight, the blocks of a chunk in a
+    full group of eight chunks go to workgroups congruent mod 8 (one XCD: workgroup c
+    runs on XCD c mod 8), so its hidden is exchanged within one L2."""
+    for G, grid, (D, I) in itertools.product([8, 16, 61, 300], [8, 64, 256], [(7168, 256), (3584, 384)]):
+        HB = I // 32
+        _, items = m.moe_work_split(1, G, D, I, grid)
+        xcd = {}
+        for i, (ch, j) in enumerate(items.tolist()):
+            if ch < G // 8 * 8:
+                xcd.setdefault(ch, set()).add((i % grid) % 8)
+        assert all(len(v) == 1 for v in xcd.values()), (G, grid, D, I)
+
+
+def test_split_rejects_bad_arguments(m):
+    L = m._lib.lib
+    buf = np.zeros((4, 4), np.int32)
+    assert L.moe_work_split(2, 1, 3584, 384, 4, buf.ctypes.data, None) == m._lib.MOE_EINVAL
+    assert L.moe_work_split(0, 129, 3584, 384, 4, buf.ctypes.data, None) == m._lib.MOE_EINVAL
+    assert L.moe_work_split(1, 1025, 3584, 384, 4, buf.ctypes.data, None) == m._lib.MOE_EINVAL
+    assert L.moe_work_split(0, 1, 3584, 384, 0, buf.ctypes.data, None) == m._lib.MOE_EINVAL
+    assert L.moe_work_split(0, 1, 3584, 384, 2049, buf.ctypes.data, None) == m._lib.MOE_EINVAL
+    assert L.moe_work_split(0, 1, 3000, 384, 4, buf.ctypes.data, None) == m._lib.MOE_EINVAL
+    assert L.moe_work_split(0, 1, 3584, 384, 4, None, None) == m._lib.MOE_EINVAL
+
+
+# ------------------------------------------------------------------------ protocol
+def _wave_tiles(first2, n2, w):
+    """FC2 tiles of streaming wave w: w, w + 8, ... of the workgroup's run."""
+    return [first2 + t for t in range(w, n2, QSTREAM)]
+
+
+def _fc2_ops(first2, n2, w, TPE, c):
+    """A streaming wave's FC2 part: on entering a new hidden sequence (the run's groups,
+    in order) it posts that it is done with the earlier ones, then waits for the
+    loader's copy; at the end it posts that it is done with all."""
+    ops, cur = [], None
+    g0 = first2 // TPE
+    for t in _wave_tiles(first2, n2, w):
+        seq = t // TPE - g0
+        if seq != cur:
+            cur = seq
+            ops += [("post", (c, "prog2", w), seq), ("wait", (c, "ready"), seq + 1)]
+    ops.append(("post", (c, "prog2", w), INF))
+    return ops
+
+
+def _nseq(first2, n2, TPE):
+    return (first2 + n2 - 1) // TPE - first2 // TPE + 1 if n2 > 0 else 0
+
+
+def _decode_actors(split, items, D, I):
+    """decode_whole_kernel: eight streaming waves (FC1 K steps w, w + 8, ... of each of
+    the workgroup's items, then FC2 tiles), the finisher (adds the waves' partial tiles
+    of each item, SwiGLU, publishes the block) and the loader (per hidden sequence: waits
+    until the waves are done with the buffer it reuses, two back, then for the group's
+    blocks, then copies)."""
+    NS1, HB, TPE = D // 128, I // 32, D // 16
+    grid = split.shape[0]
+    actors = []
+    for c in range(grid):
+        n1, first2, n2 = (int(v) for v in split[c, :3])
+        nw1 = min(NS1, QSTREAM)
+        for w in range(QSTREAM):
+            m1 = -(-(NS1 - w) // QSTREAM) if w < NS1 else 0
+            ops = [("add", (c, "xdone"))]
+            if n1 * m1 > 0:
+                ops.append(("wait", (c, "xdone"), QSTREAM + 2))
+            if m1 > 0:
+                for k in range(n1):
+                    ops += [("wait", (c, "cons"), k), ("post", (c, "prog", w), k + 1)]
+            actors.append(ops + _fc2_ops(first2, n2, w, TPE, c))
+        fin = [("add", (c, "xdone"))]
+        for k in range(n1):
+            fin += [("wait", (c, "prog", ww), k + 1) for ww in range(nw1)]
+            fin.append(("post", (c, "cons"), k + 1))
+            fin.append(("gpost", tuple(items[c + k * grid])))
+        actors.append(fin)
+        ld = [("add", (c, "xdone"))]
+        g0 = first2 // TPE
+        for seq in range(_nseq(first2, n2, TPE)):
+            if seq >= 2:
+                ld += [("wait", (c, "prog2", ww), seq - 1) for ww in range(QSTREAM)]
+            ld += [("gwait", (g0 + seq, j)) for j in range(HB)]
+            ld.append(("post", (c, "ready"), seq + 1))
+        actors.append(ld)
+    return actors
+
+
+def _grouped_actors(split, items, D, I):
+    """grouped_kernel: eight streaming waves (wave w runs the workgroup's items w, w + 8,
+    ... whole, stages each finished block once the loader has published its previous
+    one, then its FC2 tiles) and the loader (publishes the staged blocks in item order,
+    then per hidden sequence: waits until every wave is done with the one buffer, then
+    for the chunk's blocks, then copies)."""
+    HB, TPE = I // 32, D // 16
+    grid = split.shape[0]
+    actors = []
+    for c in range(grid):
+        n1, first2, n2 = (int(v) for v in split[c, :3])
+        for w in range(QSTREAM):
+            n1w = -(-(n1 - w) // QSTREAM) if n1 > w else 0
+            ops = []
+            for mm in range(n1w):
+                ops += [("wait", (c, "pub", w), mm), ("post", (c, "staged", w), mm + 1)]
+            actors.append(ops + _fc2_ops(first2, n2, w, TPE, c))
+        ld = []
+        for k in range(n1):
+            ww, mm = k % QSTREAM, k // QSTREAM
+            ld += [("wait", (c, "staged", ww), mm + 1), ("gpost", tuple(items[c + k * grid])),
+                   ("post", (c, "pub", ww), mm + 1)]
+        g0 = first2 // TPE
+        for seq in range(_nseq(first2, n2, TPE)):
+            if seq >= 1:
+                ld += [("wait", (c, "prog2", ww), seq) for ww in range(QSTREAM)]
+            ld += [("gwait", (g0 + seq, j)) for j in range(HB)]
+            ld.append(("post", (c, "ready"), seq + 1))
+        actors.append(ld)
+    return actors
+
+
+def _run(actors, drop=None, bounded=False, lds_limit=64, poll_limit=4096, period=256):
+    """Runs the waves.  Unbounded: every wave advances while its next wait holds; returns
+    the waves left blocked (none means no wait cycle).  Bounded (a time-stepped model of
+    the kernels' bounded waits, one poll per step): an LDS wait gives up after lds_limit
+    polls; a global wait after poll_limit polls, or at a multiple of `period` polls once
+    any wait has given up.  Returns (blocked waves, step of the first give-up, step of
+    the last global give-up)."""
+    lds, flags = {}, set()
+    pc = [0] * len(actors)
+    polls = [0] * len(actors)
+    first_give_up, last_global = None, None
+    step = 0
+    while True:
+        moved = False
+        for a, ops in enumerate(actors):
+            while pc[a] < len(ops):
+                op = ops[pc[a]]
+                kind = op[0]
+                if kind == "post":
+                    lds[op[1]] = max(lds.get(op[1], 0), op[2])
+                elif kind == "add":
+                    lds[op[1]] = lds.get(op[1], 0) + 1
+                elif kind == "gpost":
+                    if op[1] != drop:
+                        flags.add(op[1])
+                elif kind == "wait":
+                    if lds.get(op[1], 0) < op[2]:
+                        break
+                elif kind == "gwait":
+                    if op[1] not in flags:
+                        break
+                pc[a] += 1
+                polls[a] = 0
+                moved = True
+        blocked = [a for a in range(len(actors)) if pc[a] < len(actors[a])]
+        if not blocked:
+            return [], first_give_up, last_global
+        if moved:
+            continue
+        if not bounded:
+            return blocked, None, None
+        # one poll for every blocked wave; those past their bound give up and go on
+        step += 1
+        gave = []
+        for a in blocked:
+            polls[a] += 1
+            kind = actors[a][pc[a]][0]
+            if kind == "wait":
+                out = polls[a] >= lds_limit
+            else:
+                out = polls[a] >= poll_limit or (first_give_up is not None and polls[a] % period == 0)
+            if out:
+                gave.append(a)
+                if kind == "gwait":
+                    last_global = step
+        for a in gave:
+            pc[a] += 1
+            polls[a] = 0
+        if gave and first_give_up is None:
+            first_give_up = step
+
+
+def _all_splits(m, form):
+    shapes, groups, grids = _cases()
+    for (D, I), G, grid in itertools.product(shapes[:4], groups, grids):
+        if form == 1 and I > 384:
+            continue
+        split, items = m.moe_work_split(form, G, D, I, grid)
+        yield D, I, G, grid, split, items
+
+
+@pytest.mark.parametrize("form", [0, 1])
+def test_wait_protocol_has_no_cycle(m, form):
+    build = _decode_actors if form == 0 else _grouped_actors
+    for D, I, G, grid, split, items in _all_splits(m, form):
+        blocked, _, _ = _run(build(split, items, D, I))
+        assert not blocked, (form, D, I, G, grid, blocked[:4])
+
+
+@pytest.mark.parametrize("form", [0, 1])
+def test_missing_block_gives_up_together(m, form):
+    """A planted fault in the model (one block's flag never published): without bounds
+    the consumers of its group block for good; with them every wave ends, and every
+    global wait that gave up did so within one status period of the first give-up
+    (it reads the status word every 256 polls), not after its own full bound."""
+    build = _decode_actors if form == 0 else _grouped_actors
+    D, I, G, grid = 3584, 384, 13, 33
+    split, items = m.moe_work_split(form, G, D, I, grid)
+    actors = build(split, items, D, I)
+    drop = tuple(items[len(items) // 2])
+    blocked, _, _ = _run(actors, drop=drop)
+    assert blocked, "the planted fault blocks nobody: the model does not see the flags"
+    blocked, first, last = _run(actors, drop=drop, bounded=True, lds_limit=10**6, poll_limit=4096, period=256)
+    assert not blocked
+    assert first is not None and first >= 4096
+    assert last - first <= 256 + 1, (first, last)
