@@ -202,7 +202,14 @@ typedef struct {
                          the other owners' partial sums, applies SwiGLU and MXFP8, publishes
                          codes and a call-tagged flag);
                          other values MOE_EINVAL */
-  int32_t reserved[3];
+  int32_t fc2_claims;  /* the decode form's whole-K kernel (exchange 0): 0 = default,
+                         static FC2 runs; 1 = FC2 tail claims -- the last grains of eight
+                         FC2 tiles of each workgroup's run are handed out through a
+                         call-tagged counter of that workgroup, to itself from the front
+                         and to the two workgroups before it in tile order from the back
+                         where they hold that expert's hidden.  The rows are the same bit
+                         for bit either way.  Other values MOE_EINVAL */
+  int32_t reserved[2];
   void* hidden_codes_dev;  /* optional u8 [B*topk, I]: the hidden's e4m3 codes per route */
   void* hidden_scales_dev; /* optional u8 [B*topk, I/32]: its E8M0 scales */
   /* moe_decode_run only (MOE_EINVAL for moe_experts_run when set): */

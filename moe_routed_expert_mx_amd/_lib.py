@@ -36,7 +36,7 @@ class moe_weights_t(ctypes.Structure):
 class moe_run_opts_t(ctypes.Structure):
     _fields_ = [("hidden_rule", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("col_tiles", ctypes.c_int32), ("ring", ctypes.c_int32), ("exchange", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3),
+                ("fc2_claims", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
                 ("hidden_codes_dev", ctypes.c_void_p), ("hidden_scales_dev", ctypes.c_void_p),
                 ("plan_dev", ctypes.c_void_p), ("plan_bytes", ctypes.c_size_t), ("status_dev", ctypes.c_void_p)]
 
@@ -168,8 +168,9 @@ def moe_units_export(units, B, topk, E, header, unit_expert, unit_rows, stream=N
                                                     _stream(stream)))
 
 
-def _opts(hidden_rule, grid, col_tiles, ring, hidden_codes, hidden_scales, plan=None, status=None, exchange=0):
-    return moe_run_opts_t(hidden_rule, grid, col_tiles, ring, exchange, (ctypes.c_int32 * 3)(0, 0, 0),
+def _opts(hidden_rule, grid, col_tiles, ring, hidden_codes, hidden_scales, plan=None, status=None, exchange=0,
+          fc2_claims=0):
+    return moe_run_opts_t(hidden_rule, grid, col_tiles, ring, exchange, fc2_claims, (ctypes.c_int32 * 2)(0, 0),
                           _ptr(hidden_codes), _ptr(hidden_scales), _ptr(plan), 0 if plan is None else _nbytes(plan),
                           _ptr(status))
 
@@ -183,23 +184,24 @@ def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, 
 
 
 def moe_decode_run(weights: moe_weights_t, x, ids, ws, out, *, hidden_rule=0, grid=0, ring=0, exchange=0,
-                   hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
+                   fc2_claims=0, hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
     """The whole step of a batch of B <= 8 tokens in one launch: x BF16 [B, D] (or uint16
     bits), ids int32 [B, topk] -> out BF16 [B*topk, D]; optional plan (u8, the moe_plan
     layout) and status (int32 [1]) outputs; exchange 0 (whole-K hidden blocks, the
-    default), 1 (tagged partial sums) or 2 (finished split blocks)."""
+    default), 1 (tagged partial sums) or 2 (finished split blocks); fc2_claims 1 turns
+    on the FC2 tail claims of exchange 0."""
     B, K = ids.shape
-    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, exchange)
+    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, exchange, fc2_claims)
     _check("moe_decode_run", lib.moe_decode_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(x), _ptr(ids), B, K,
                                                 _ptr(ws), _nbytes(ws), _ptr(out), _nbytes(out), _stream(stream)))
 
 
-def moe_decode_run_noalloc(weights: moe_weights_t, x, ids, out, *, hidden_rule=0, grid=0, ring=0,
+def moe_decode_run_noalloc(weights: moe_weights_t, x, ids, out, *, hidden_rule=0, grid=0, ring=0, fc2_claims=0,
                            hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
     """moe_decode_run with the library's fixed per-device scratch instead of a workspace
     (no allocation; the whole-K decode form only, MOE_ELIMIT beyond its limits)."""
     B, K = ids.shape
-    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, 0)
+    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, 0, fc2_claims)
     _check("moe_decode_run_noalloc", lib.moe_decode_run_noalloc(ctypes.byref(weights), ctypes.byref(opts), _ptr(x),
                                                                 _ptr(ids), B, K, _ptr(out), _nbytes(out),
                                                                 _stream(stream)))

@@ -594,7 +594,7 @@ constexpr int kMaxGroups = 1024;   // distinct experts per call (E <= 1024)
 
 struct WsLayout {
   size_t calls, status, arrive, flags, hcodes, hscales, partials;
-  size_t qcalls, qhq;  // decode form with whole-K FC1 blocks
+  size_t qcalls, qclaims, qhq;  // decode form with whole-K FC1 blocks
   size_t gcalls, gflags, ghid;  // grouped form with whole-K FC1 blocks
   size_t end;
   int64_t max_tiles, max_blocks;
@@ -648,6 +648,8 @@ WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   // (data, call) pairs (at most 128 distinct experts x 8 token columns x (IP/4 + 16))
   L.qcalls = off;
   off = align256(off + kMaxGrid * 4);
+  L.qclaims = off;  // FC2 claim counters, one per workgroup (call-tagged: never cleared)
+  off = align256(off + kMaxGrid * 8);
   L.qhq = off;
   off = align256(off + static_cast<size_t>(128) * 8 * (IP / 4 + 16) * 8);
   // grouped form with whole-K FC1 blocks: its call counters, a call-tagged flag per
@@ -2577,7 +2579,21 @@ constexpr uint32_t kQPre = 256;     // [32] popcount prefix of the bitmask words
 constexpr uint32_t kQExp = 384;     // [kQGMax] expert id of group g (ascending)
 constexpr uint32_t kQTok = 896;     // [kQGMax] token bitmask of group g
 constexpr uint32_t kQRow = 1408;    // [kQGMax][8] u16: pair t*K+s of group g's column c
-constexpr uint32_t kQTables = 3456;
+constexpr uint32_t kQTaken = 3456;  // [8] FC2 queue entries wave w's issue side has taken
+constexpr uint32_t kQPosted = 3488; // FC2 queue entries the claimer has posted
+constexpr uint32_t kQQueue = 3504;  // [kQRing] FC2 queue: first tile of a claimed grain, -1 = end
+constexpr uint32_t kQTables = 3584;
+
+// FC2 tail claims (experts page, ExpertsKernel: steal, claims, fc2_steal; runtime page,
+// dynamic(batch): a static FC2 split leaves the slowest workgroup as the launch's tail).
+// The last grains of each workgroup's FC2 run form its zone; a 64-bit counter per
+// workgroup, {call, back claims, front claims}, hands each grain out once: the owner
+// claims from the front, the workgroups before it in tile order from the back.
+constexpr int kQGrain = kQStream;  // FC2 tiles of a grain: one per streaming wave
+constexpr int kQZone = 4;          // most grains in a zone
+constexpr int kQAhead = 4;         // grains the claimer posts ahead of the slowest issue side
+constexpr int kQVictims = 2;       // workgroups after this one whose zones it may take from
+constexpr int kQRing = 16;         // queue entries (more than kQAhead plus the ring depth)
 
 struct QArgs {
   const uint8_t* w13p;
@@ -2590,11 +2606,13 @@ struct QArgs {
   uint64_t* hq;           // [kQGMax][8][hq_words] the hidden as (data, call) pairs: per
                           // column I/4 code words, then HB scale words
   uint32_t* calls;        // [kMaxGrid] per-workgroup call counters
+  uint64_t* claims;       // [kMaxGrid] per-workgroup FC2 claim counters {call, back, front}
   int32_t* err;           // status word (bit 0 id out of range, bit 1 repeated id, bit 2 a wait gave up)
   uint8_t* dump_codes;    // optional [B*K, I]
   uint8_t* dump_scales;   // optional [B*K, I/32]
   uint8_t* plan_dump;     // optional plan of x (moe_plan layout), written by workgroup 0
   int B, K, E, D, I, HB, NS1, IP, floor_rule, hq_words;
+  int zone;               // most grains of a claimable FC2 zone (0: static FC2 runs)
   uint32_t o_red, o_hid, o_xq, o_xs, o_ring;  // LDS offsets
   uint32_t xstr, xsstr, hid_bytes;            // x code row stride, x scale row stride, one hidden buffer
   int cb;                 // token columns a group can have: min(B, 8); sizes the LDS areas below
@@ -2690,19 +2708,91 @@ __host__ __device__ inline QWork q_work(int G, int HB, int NS1, int D, int nwg, 
   return q;
 }
 
+// The claimable zone of a workgroup's FC2 run: its last Z grains, Z at most `zone` and
+// at most half the run.  Only runs of at least 16 R tiles have one, so that every
+// streaming wave's static head holds R tiles or more: a wave's issue side, R slots ahead,
+// then reaches the claimed grains only once its FC1 slots are consumed (the claimer is
+// the finisher wave, busy with FC1 until then).  Returns Z; zb = the zone's first tile.
+__host__ __device__ inline int q_zone(const QWork& q, int zone, int R, int& zb) {
+  int Z = q.n2 >= 16 * R ? q.n2 / (2 * kQGrain) : 0;
+  Z = Z < zone ? Z : zone;
+  zb = q.first2 + q.n2 - Z * kQGrain;
+  return Z;
+}
+
+// A streaming wave's walk over its FC2 tiles: the head of the run (tiles w, w + 8, ...
+// below the zone), then tile w of each grain the claimer queues, until the end entry.
+// The issue side waits for each entry to be posted and reports it taken; the consume
+// side, R slots behind, reads entries already there.
+struct QTiles {
+  int t;        // next head tile
+  int zb;       // first tile of the zone
+  int q;        // next queue entry
+  int s;        // -2 once the end entry is read
+  int g, rt2;   // group and row tile of the next head tile (stepped without divisions)
+};
+
+__device__ __forceinline__ void q_tiles_init(QTiles& c, const QWork& q, int zb, int w) {
+  c.t = q.first2 + w;
+  c.zb = zb;
+  c.q = 0;
+  c.s = -1;
+  c.g = c.t / q.TPE;
+  c.rt2 = c.t - c.g * q.TPE;
+}
+
+// The next tile: true with its group g and row tile rt2, false at the end (without
+// claims, the end of the head).
+template <bool ISSUE, bool CLAIMS>
+__device__ __forceinline__ bool q_next_tile(uint32_t lb, int w, int TPE, QTiles& c, int32_t* err, int& g, int& rt2) {
+  if (c.t < c.zb) {
+    g = c.g;
+    rt2 = c.rt2;
+    c.t += kQStream;
+    c.rt2 += kQStream;
+#pragma unroll 1
+    while (c.rt2 >= TPE) {
+      c.rt2 -= TPE;
+      ++c.g;
+    }
+    return true;
+  }
+  if (!CLAIMS || c.s == -2) return false;
+  if (ISSUE) lds_wait<false>(lb + kQPosted, c.q + 1, err);
+  const int s = static_cast<int>(lds_uni(lb + kQQueue + 4 * static_cast<uint32_t>(c.q % kQRing)));
+  ++c.q;
+  if (ISSUE && (threadIdx.x & 63) == 0) lds_st4(lb + kQTaken + 4 * w, static_cast<uint32_t>(c.q));
+  if (s < 0) {
+    c.s = -2;
+    return false;
+  }
+  g = (s + w) / TPE;  // a claimed grain (claims only)
+  rt2 = s + w - g * TPE;
+  return true;
+}
+
+// One claim on a zone counter (lane 0's device-scope add; the old value to every lane).
+__device__ __forceinline__ uint64_t q_claim(uint64_t* ctr, uint64_t inc) {
+  uint64_t v = 0;
+  if ((threadIdx.x & 63) == 0) v = __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // The issue side of a streaming wave's slot sequence: its FC1 K steps (item by item),
-// then its FC2 tiles (w, w + 8, ... of the workgroup's run), then dummies (out-of-range
-// loads that write zeros and read no memory, so the vmcnt of a slot stays fixed).
+// then its FC2 tiles (QTiles), then dummies (out-of-range loads that write zeros and
+// read no memory, so the vmcnt of a slot stays fixed).
 struct QIssue {
   int k;          // slots issued
   int item, si;   // next FC1 step: item of the workgroup, step index (s = w + 8 si)
   int64_t step;   // its packed step index ((e * HB + j) * NS1 + s)
-  int g2, rt2;    // next FC2 tile: group and 16-row tile of its expert
-  int e2;         // expert of group g2 (cached)
+  QTiles tl;      // FC2 tiles
+  int g2, e2;     // group of the last FC2 tile issued and its expert
 };
 
-template <int NS2, int R>
-__device__ __forceinline__ void q_issue(const QArgs& a, const QWork& q, uint32_t lb, int w, int n1el, int n_el,
+template <int NS2, int R, bool CLAIMS>
+__device__ __forceinline__ void q_issue(const QArgs& a, const QWork& q, uint32_t lb, int w, int n1el,
                                         QIssue& is, __amdgpu_buffer_rsrc_t none) {
   const int l = threadIdx.x & 63;
   const uint32_t so = a.o_ring + static_cast<uint32_t>((w * R + is.k % R) * kQSlot);
@@ -2721,29 +2811,18 @@ __device__ __forceinline__ void q_issue(const QArgs& a, const QWork& q, uint32_t
       is.si = 0;
       ++is.item;
     }
-  } else if (is.k < n_el) {
-    if (is.k == n1el) {  // first FC2 tile of this wave
-      const int t = q.first2 + w;
-      is.g2 = t / q.TPE;
-      is.rt2 = t - is.g2 * q.TPE;
-      is.e2 = lds_uni(lb + kQExp + 4 * is.g2);
+  } else if (int g = 0, rt2 = 0; q_next_tile<true, CLAIMS>(lb, w, q.TPE, is.tl, a.err, g, rt2)) {
+    if (g != is.g2) {
+      is.g2 = g;
+      is.e2 = lds_uni(lb + kQExp + 4 * g);
     }
-    const int64_t tile = static_cast<int64_t>(is.e2) * q.TPE + is.rt2;
+    const int64_t tile = static_cast<int64_t>(is.e2) * q.TPE + rt2;
     const uint8_t* wb = a.w2p + tile * NS2 * 1024 + l * 16;
 #pragma unroll
     for (int s = 0; s < NS2; ++s) dma16(wb + s * 1024, so + s * 1024);
 #pragma unroll
     for (int s = NS2; s < 4; ++s) bdma16(none, kOutside, so + s * 1024);
     dma4(a.s2p + tile * 256 + l * 4, so + 4096);
-    is.rt2 += kQStream;
-    if (is.rt2 >= q.TPE && is.k + 1 < n_el) {
-#pragma unroll 1
-      while (is.rt2 >= q.TPE) {
-        is.rt2 -= q.TPE;
-        ++is.g2;
-      }
-      is.e2 = lds_uni(lb + kQExp + 4 * is.g2);
-    }
   } else {
 #pragma unroll
     for (int s = 0; s < 4; ++s) bdma16(none, kOutside, so + s * 1024);
@@ -2752,7 +2831,7 @@ __device__ __forceinline__ void q_issue(const QArgs& a, const QWork& q, uint32_t
   ++is.k;
 }
 
-template <int NS2, int R, bool WIDE>
+template <int NS2, int R, bool WIDE, bool CLAIMS>
 __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   agpr_form();
@@ -2766,6 +2845,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
 
   // ---- prologue: ids, raw x rows and the call number in flight together
   if (tid < 21) sw[tid] = 0u;  // sync words and the call number
+  if (CLAIMS && tid < 9) sw[kQTaken / 4 + tid] = 0u;  // the FC2 queue's taken and posted counts
   // the two hidden buffers start as zero codes with unit scales: the K-blocks past I (I
   // not a multiple of 128) then multiply zero-padded weights by zero, and the token
   // columns past a group's count hold finite values (their outputs are never stored)
@@ -2831,23 +2911,32 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   const int G = __builtin_amdgcn_readfirstlane(static_cast<int>(sw[kQGCount / 4]));
   __syncthreads();
 
-  const QWork q = q_work(G, HB, NS1, D, nwg, c, w < kQStream ? w : 0, q_item_tiles(D, NS2));
+  const int item_tiles = q_item_tiles(D, NS2);
+  const QWork q = q_work(G, HB, NS1, D, nwg, c, w < kQStream ? w : 0, item_tiles);
   const __amdgpu_buffer_rsrc_t none =
       __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
   const int nw1 = NS1 < kQStream ? NS1 : kQStream;  // waves that take FC1 steps
+  int zb = q.first2 + q.n2;
+  const int Z = CLAIMS ? q_zone(q, a.zone, R, zb) : 0;  // this workgroup's claimable FC2 grains
+  // without a zone the queue holds only its end entry, posted before anything can wait
+  // for it
+  if (CLAIMS && Z == 0 && w == kQFin && l == 0) {
+    lds_st4(lb + kQQueue, 0xffffffffu);
+    lds_st4(lb + kQPosted, 1u);
+  }
 
   // ---- streaming waves start their weight streams; the x plan does not gate them
   const int n1el = w < kQStream ? q.n1 * q.m1 : 0;
-  const int n2w = q.n2 > w ? (q.n2 - w + kQStream - 1) / kQStream : 0;
-  const int n_el = w < kQStream ? n1el + n2w : 0;
   QIssue is;
   is.k = 0;
   is.item = is.si = 0;
   is.step = 0;
-  is.g2 = is.rt2 = is.e2 = 0;
+  q_tiles_init(is.tl, q, zb, w);
+  is.g2 = -1;
+  is.e2 = 0;
   if (w < kQStream) {
 #pragma unroll 1
-    for (int k = 0; k < R; ++k) q_issue<NS2, R>(a, q, lb, w, n1el, n_el, is, none);
+    for (int k = 0; k < R; ++k) q_issue<NS2, R, CLAIMS>(a, q, lb, w, n1el, is, none);
   }
 
   // ---- the MXFP8 plan of x (experts page, plan_chunk / mx_block), all waves, into LDS
@@ -2922,7 +3011,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
         acc[1] = mfma_fp4_fp8(fp4_operand(a1), bop, acc[1], static_cast<int>((as >> 8) & 0xffu), sb);
         acc[2] = mfma_fp4_fp8(fp4_operand(a2), bop, acc[2], static_cast<int>((as >> 16) & 0xffu), sb);
         acc[3] = mfma_fp4_fp8(fp4_operand(a3), bop, acc[3], static_cast<int>(as >> 24), sb);
-        q_issue<NS2, R>(a, q, lb, w, n1el, n_el, is, none);  // into the slot just consumed
+        q_issue<NS2, R, CLAIMS>(a, q, lb, w, n1el, is, none);  // into the slot just consumed
       }
       // the wave's part of the block is done: hand its partial tiles (the block's token
       // columns) to the finisher once it has taken the last ones
@@ -2939,17 +3028,16 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
       if (l == 0) lds_st4(lb + kQProg + 4 * w, static_cast<uint32_t>(item + 1));
     }
 
-    // ---- FC2: this wave's tiles of the workgroup's run (w, w + 8, ...)
+    // ---- FC2: this wave's tiles of the workgroup's run (w, w + 8, ... of its head, then
+    // tile w of each claimed grain)
     int cur_seq = -1, orow = -1;
     uint32_t hbl = 0, hbs = 0;
-    int g = 0, rt2 = 0;
-    if (k < n_el) {
-      const int t = q.first2 + w;
-      g = t / q.TPE;
-      rt2 = t - g * q.TPE;
-    }
+    QTiles ct;
+    q_tiles_init(ct, q, zb, w);
 #pragma unroll 1
-    for (; k < n_el; ++k) {
+    for (;; ++k) {
+      int g = 0, rt2 = 0;
+      if (!q_next_tile<false, CLAIMS>(lb, w, q.TPE, ct, a.err, g, rt2)) break;
       wait_vm<(R - 1) * kQOps>();
       const uint32_t sa = lb + a.o_ring + static_cast<uint32_t>((w * R + k % R) * kQSlot);
       const int seq = g - g0;
@@ -2994,13 +3082,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
         const uint2 v = make_uint2(bf16_pair(o[0], o[1]), bf16_pair(o[2], o[3]));
         *reinterpret_cast<uint2*>(a.out + static_cast<int64_t>(orow) + 16 * rt2 + 4 * grp) = v;
       }
-      q_issue<NS2, R>(a, q, lb, w, n1el, n_el, is, none);
-      rt2 += kQStream;
-#pragma unroll 1
-      while (rt2 >= q.TPE) {
-        rt2 -= q.TPE;
-        ++g;
-      }
+      q_issue<NS2, R, CLAIMS>(a, q, lb, w, n1el, is, none);
     }
     if (l == 0) lds_st4(lb + kQProg2 + 4 * w, 0x7fffffffu);
     wait_vm<0>();  // the dummy slots land before the workgroup ends
@@ -3081,6 +3163,56 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     }
   }
 
+    if (CLAIMS && Z > 0) {
+      // FC2 tail claims: queue this workgroup's zone grains from the front, then grains
+      // of the zones of the next workgroups from the back where all their tiles belong to
+      // this workgroup's last expert (whose hidden its last buffer keeps), then the end.
+      // Each claim waits until every streaming wave has taken all but kQAhead of the
+      // posted grains, so grains stay unclaimed, and free for others, until needed.  A
+      // grain is computed by whoever claims it exactly as its owner would.
+      // re-arm this workgroup's counter for the call: {call, 0 back, 0 front}.  Claims by
+      // others that reach it first see the old call's tag and take nothing.
+      if (l == 0) st_dev_u64(a.claims + c, static_cast<uint64_t>(call) << 32);
+      int posted = 0;
+      auto pace = [&]() {
+        if (posted >= kQAhead) {
+#pragma unroll 1
+          for (int ww = 0; ww < kQStream; ++ww) lds_wait<false>(lb + kQTaken + 4 * ww, posted - kQAhead + 1, a.err);
+        }
+      };
+      auto post = [&](int first) {
+        if (l == 0) {
+          lds_st4(lb + kQQueue + 4 * static_cast<uint32_t>(posted % kQRing), static_cast<uint32_t>(first));
+          lds_st4(lb + kQPosted, static_cast<uint32_t>(posted + 1));
+        }
+        ++posted;
+      };
+#pragma unroll 1
+      for (;;) {
+        pace();
+        const uint64_t v = q_claim(a.claims + c, 1u);
+        const int f = static_cast<int>(v & 0xffffu), r = static_cast<int>((v >> 16) & 0xffffu);
+        if (static_cast<uint32_t>(v >> 32) != call || f + r >= Z) break;
+        post(zb + f * kQGrain);
+      }
+      const int glast = (q.first2 + q.n2 - 1) / q.TPE;
+#pragma unroll 1
+      for (int vc = c + 1; vc <= c + kQVictims && vc < nwg; ++vc) {
+        const QWork qv = q_work(G, HB, NS1, D, nwg, vc, 0, item_tiles);
+        int zbv = 0;
+        const int Zv = q_zone(qv, a.zone, R, zbv);
+        if (Zv == 0 || zbv / q.TPE != glast || (qv.first2 + qv.n2 - 1) / q.TPE != glast) continue;
+#pragma unroll 1
+        for (;;) {
+          pace();
+          const uint64_t v = q_claim(a.claims + vc, 1u << 16);
+          const int f = static_cast<int>(v & 0xffffu), r = static_cast<int>((v >> 16) & 0xffffu);
+          if (static_cast<uint32_t>(v >> 32) != call || f + r >= Zv) break;
+          post(zbv + (Zv - 1 - r) * kQGrain);
+        }
+      }
+      post(-1);
+    }
     // the call counters for the next call (which starts after this kernel has ended, so
     // nothing waits on the stores): every counter c, c + grid, c + 2 grid, ... below
     // kMaxGrid, so all of them stay equal whatever grid the next call uses
@@ -3091,7 +3223,9 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   // ================================================================= loader wave
   static_assert(kQLoad == kQStream + 1 && kQWG == 64 * (kQLoad + 1), "the loader is the last wave");
   // FC2: for each expert of the workgroup's run, in order, wait for its hidden (polling
-  // from the start of the call) and copy it into one of the two LDS hidden buffers
+  // from the start of the call) and copy it into one of the two LDS hidden buffers.  These
+  // polls give up after kPollLimit rounds without reading the status word: a status read
+  // in these loops lengthened the decode step by about a microsecond.
   const int nseq = q.n2 > 0 ? (q.first2 + q.n2 - 1) / q.TPE - g0 + 1 : 0;
 #pragma unroll 1
   for (int seq = 0; seq < nseq; ++seq) {
@@ -3134,7 +3268,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   #pragma unroll
         for (int u = 0; u < kQPoll; ++u) ok = ok && (u * 64 + l >= n || static_cast<uint32_t>(v[u] >> 32) == call);
         if (__all(ok)) break;
-        if (poll_expired(spins, a.err)) {
+        if (spins == kPollLimit) {
           if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
@@ -3173,7 +3307,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
             ok = ok && (idx >= n || static_cast<uint32_t>(v[u] >> 32) == call);
           }
           if (__all(ok)) break;
-          if (poll_expired(spins, a.err)) {
+          if (spins == kPollLimit) {
             if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
@@ -3973,7 +4107,7 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
   if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || o.col_tiles < 0 || o.col_tiles > (DEC ? 1 : 2) ||
-      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.fc2_claims < 0 || o.fc2_claims > 1 ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
     return MOE_EINVAL;
   if (!DEC && (o.plan_dev != nullptr || o.status_dev != nullptr || o.exchange != 0))
@@ -4169,20 +4303,23 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
 using QFn = void (*)(QArgs);
 // wide: an expert's hidden can exceed 512 pairs (more than four tokens at I = 384), so
 // the loader polls it in one pass (two slots per wave only)
+// claims: a separate instantiation (two slots per wave only), so that the static form
+// keeps its own code
 template <int NS2>
-QFn pick_q_r(int R, bool wide) {
+QFn pick_q_r(int R, bool wide, bool claims) {
+  if (claims) return wide ? decode_whole_kernel<NS2, 2, true, true> : decode_whole_kernel<NS2, 2, false, true>;
   switch (R) {
-    case 2: return wide ? decode_whole_kernel<NS2, 2, true> : decode_whole_kernel<NS2, 2, false>;
-    case 3: return decode_whole_kernel<NS2, 3, false>;
-    default: return decode_whole_kernel<NS2, 4, false>;
+    case 2: return wide ? decode_whole_kernel<NS2, 2, true, false> : decode_whole_kernel<NS2, 2, false, false>;
+    case 3: return decode_whole_kernel<NS2, 3, false, false>;
+    default: return decode_whole_kernel<NS2, 4, false, false>;
   }
 }
-QFn pick_q(int ns2, int R, bool wide) {
+QFn pick_q(int ns2, int R, bool wide, bool claims) {
   switch (ns2) {
-    case 1: return pick_q_r<1>(R, wide);
-    case 2: return pick_q_r<2>(R, wide);
-    case 3: return pick_q_r<3>(R, wide);
-    default: return pick_q_r<4>(R, wide);
+    case 1: return pick_q_r<1>(R, wide, claims);
+    case 2: return pick_q_r<2>(R, wide, claims);
+    case 3: return pick_q_r<3>(R, wide, claims);
+    default: return pick_q_r<4>(R, wide, claims);
   }
 }
 
@@ -4217,12 +4354,12 @@ bool whole_fits(const moe_weights_t* wts, int32_t B, int32_t topk) {
 }
 
 // The decode form with whole-K FC1 blocks on the given workspace areas: the call
-// counters [kMaxGrid], the default status word and the hidden exchange [kQGMax][8][IP/4 +
-// kQHB] pairs (from a caller's workspace, or from the allocation-free entry point's
-// fixed scratch).
+// counters [kMaxGrid], the FC2 claim counters [kMaxGrid], the default status word and
+// the hidden exchange [kQGMax][8][IP/4 + kQHB] pairs (from a caller's workspace, or from
+// the allocation-free entry point's fixed scratch).
 int launch_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids,
-                        int32_t B, int32_t topk, uint32_t* calls, int32_t* status, uint64_t* hq, void* out,
-                        void* stream);
+                        int32_t B, int32_t topk, uint32_t* calls, uint64_t* claims, int32_t* status, uint64_t* hq,
+                        void* out, void* stream);
 
 // The decode form with whole-K FC1 blocks (moe_run_opts_t.exchange == 0, the default,
 // for batches within whole_fits).
@@ -4236,13 +4373,13 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
   (void)out_bytes;
   uint8_t* base = static_cast<uint8_t*>(ws);
   return launch_decode_whole(wts, o, x, ids, B, topk, reinterpret_cast<uint32_t*>(base + L.qcalls),
-                             reinterpret_cast<int32_t*>(base + L.status), reinterpret_cast<uint64_t*>(base + L.qhq),
-                             out, stream);
+                             reinterpret_cast<uint64_t*>(base + L.qclaims), reinterpret_cast<int32_t*>(base + L.status),
+                             reinterpret_cast<uint64_t*>(base + L.qhq), out, stream);
 }
 
 int launch_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const void* x, const int32_t* ids,
-                        int32_t B, int32_t topk, uint32_t* calls, int32_t* status, uint64_t* hq, void* out,
-                        void* stream) {
+                        int32_t B, int32_t topk, uint32_t* calls, uint64_t* claims, int32_t* status, uint64_t* hq,
+                        void* out, void* stream) {
   const int E = wts->E, D = wts->D, I = wts->I;
   const int IP = (I + 127) / 128 * 128, ns2 = IP / 128;
   const QLds m = q_lds(B, D, IP);
@@ -4256,7 +4393,8 @@ int launch_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const
   while (R > 2 && m.bytes(R) > limit) --R;
   if (m.bytes(R) > limit) return MOE_EINVAL;
   const size_t lds = m.bytes(R);
-  const QFn fn = pick_q(ns2, R, m.cb * (I / 4 + I / 32) > 8 * 64);
+  if (o.fc2_claims && R != 2) return MOE_EINVAL;  // claims run with two slots per wave
+  const QFn fn = pick_q(ns2, R, m.cb * (I / 4 + I / 32) > 8 * 64, o.fc2_claims != 0);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(lds)) != hipSuccess)
     return MOE_EHIP;
@@ -4281,6 +4419,8 @@ int launch_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const
   a.hq = hq;
   a.hq_words = IP / 4 + kQHB;
   a.calls = calls;
+  a.claims = claims;
+  a.zone = o.fc2_claims ? kQZone : 0;
   a.err = o.status_dev ? static_cast<int32_t*>(o.status_dev) : status;
   a.dump_codes = static_cast<uint8_t*>(o.hidden_codes_dev);
   a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
@@ -4317,9 +4457,10 @@ int launch_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const
 // device address comes from hipGetSymbolAddress, once per device.
 constexpr size_t kScratchCalls = 0;                                  // u32 [kMaxGrid]
 constexpr size_t kScratchStatus = kScratchCalls + kMaxGrid * 4;      // i32 status word
-constexpr size_t kScratchHq = kScratchStatus + 256;                  // u64 [kQGMax][8][512 / 4 + kQHB]
+constexpr size_t kScratchClaims = kScratchStatus + 256;              // u64 [kMaxGrid] FC2 claim counters
+constexpr size_t kScratchHq = kScratchClaims + kMaxGrid * 8;         // u64 [kQGMax][8][512 / 4 + kQHB]
 constexpr size_t kScratchBytes = kScratchHq + static_cast<size_t>(kQGMax) * 8 * (512 / 4 + kQHB) * 8;
-static_assert(kScratchHq % 256 == 0, "aligned areas");
+static_assert(kScratchClaims % 256 == 0 && kScratchHq % 256 == 0, "aligned areas");
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -4534,7 +4675,7 @@ int moe_decode_run_noalloc(const moe_weights_t* wts, const moe_run_opts_t* opts,
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
   if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || o.col_tiles < 0 || o.col_tiles > 1 ||
-      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.exchange != 0 ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.exchange != 0 || o.fc2_claims < 0 || o.fc2_claims > 1 ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)) ||
       (o.plan_bytes != 0 && o.plan_dev == nullptr))
     return MOE_EINVAL;
@@ -4546,6 +4687,7 @@ int moe_decode_run_noalloc(const moe_weights_t* wts, const moe_run_opts_t* opts,
   uint8_t* base = scratch_ptr();
   if (base == nullptr) return MOE_EHIP;
   return launch_decode_whole(wts, o, x, ids, B, topk, reinterpret_cast<uint32_t*>(base + kScratchCalls),
+                             reinterpret_cast<uint64_t*>(base + kScratchClaims),
                              reinterpret_cast<int32_t*>(base + kScratchStatus),
                              reinterpret_cast<uint64_t*>(base + kScratchHq), out, stream);
 }

@@ -152,6 +152,11 @@ def test_decode_run_argument_checks(m):
     o.exchange = 3
     assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # no such exchange
     o = m.moe_run_opts_t()
+    o.fc2_claims = 2
+    assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # FC2 claims: 0 (off) or 1 (on)
+    assert L.moe_decode_run_noalloc(ctypes.byref(w), ctypes.byref(o), fake, fake, 2, 4, fake, big,
+                                    None) == m._lib.MOE_EINVAL
+    o = m.moe_run_opts_t()
     o.col_tiles = 2
     assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # the grouped kernel is not a decode form
     assert L.moe_decode_run_noalloc(ctypes.byref(w), ctypes.byref(o), fake, fake, 2, 4, fake, big,

@@ -595,6 +595,27 @@ def test_decode_form_grid_changes_between_calls(lib):
         _check_all(d, got, hc, hs, ref, what=f"decode/grid{grid}")
 
 
+@pytest.mark.parametrize("name,grid", [("decode_b8", 0), ("decode_b8", 61), ("decode_b1", 7), ("tiny", 0)])
+def test_decode_form_fc2_claims_bit_identical(lib, name, grid):
+    """FC2 tail claims (experts page, ExpertsKernel steal and claims; runtime page,
+    dynamic(batch)): whoever claims a grain computes it exactly as its owner would, so
+    rows and hidden are the same bit for bit with claims on and off (the default), over
+    repeated calls (the counters re-arm by call number), and meet the oracle bar.  The
+    grids make zones: decode_b8 on the full grid (59 tiles a run) and on 61 workgroups;
+    decode_b1 on 7 (its full grid leaves runs too short for a zone)."""
+    log(f"decode form claims on/off {name} grid={grid}")
+    d = workloads.generate(name)
+    layer = _layer(lib, d)
+    off, hco, hso, _, st = _decode_run(lib, layer, d, grid=grid)
+    assert st == 0
+    for _ in range(3):
+        on, hc, hs, _, st = _decode_run(lib, layer, d, grid=grid, fc2_claims=1)
+        assert st == 0
+        assert np.array_equal(on, off), "rows differ between claims on and off"
+        assert np.array_equal(hc, hco) and np.array_equal(hs, hso)
+    _check_all(d, on, hc, hs, _oracle(d), what=f"decode/{name}/claims/{grid}")
+
+
 def test_decode_form_flags_bad_ids(lib):
     """An id out of range is skipped and an id repeated within a token loses one of its
     routes; both are flagged in the status word, and every other route is exact."""

@@ -1,7 +1,8 @@
 """moe_decode_run_noalloc (the entry point for callers that cannot allocate) against
 moe_decode_run on the same inputs: rows, hidden dump and plan bit-identical, and both
 within the output bars against the oracle; two calls in a row, the second with a
-smaller batch, then the first batch again."""
+smaller batch, then the first batch again; the allocation-free call also once with the
+FC2 tail claims on (their counters live in the same fixed scratch)."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +22,7 @@ def lib():
     return m, MoeLayer
 
 
-def _both(m, layer, d):
+def _both(m, layer, d, claims=0):
     w = d["workload"]
     x = torch.from_numpy(d["x"]).to(DEV)
     ids = torch.from_numpy(d["ids"]).to(DEV)
@@ -37,7 +38,7 @@ def _both(m, layer, d):
                              status=status)
         else:
             m.moe_decode_run_noalloc(layer.structs[0], x, ids, out, hidden_codes=hc, hidden_scales=hs, plan=plan,
-                                     status=status)
+                                     status=status, fc2_claims=claims)
         torch.cuda.synchronize()
         res.append((out.view(torch.uint16).cpu().numpy(), hc.cpu().numpy(), hs.cpu().numpy(), plan.cpu().numpy(),
                     int(status.item())))
@@ -53,9 +54,9 @@ def test_noalloc_matches_workspace_form(lib):
     d3 = dict(d8)
     d3["x"], d3["ids"] = np.ascontiguousarray(d8["x"][:3]), np.ascontiguousarray(d8["ids"][:3])
     d3["workload"] = workloads.custom("b3", B=3, E=w.E, K=w.K, D=w.D, I=w.I)
-    for name, d in (("b8", d8), ("b3", d3), ("b8 again", d8)):
+    for name, d, claims in (("b8", d8, 0), ("b3", d3, 0), ("b8 again", d8, 0), ("b8 claims", d8, 1)):
         print(f"noalloc vs workspace: {name}", flush=True)
-        (a, ahc, ahs, ap, ast), (b, bhc, bhs, bp, bst) = _both(m, layer, d)
+        (a, ahc, ahs, ap, ast), (b, bhc, bhs, bp, bst) = _both(m, layer, d, claims)
         assert ast == 0 and bst == 0
         assert np.array_equal(a, b) and np.array_equal(ahc, bhc) and np.array_equal(ahs, bhs)
         assert np.array_equal(ap, bp)
