@@ -83,18 +83,20 @@ size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32
 /* The static work split of one experts launch, evaluated on the host (no device call;
  * for checking schedules on any machine).  It is the persistent grid's division of the
  * work among its workgroups (experts page, ExpertsKernel: each CTA's FC1 blocks and
- * its FC2 tile range).  form 0: the decode form's whole-K kernel, `groups` distinct
- * experts (<= 128, I <= 512); form 1: the grouped form, `groups` chunks of up to 32
- * routes of one expert (<= 1024).  An FC1 item is one 32-wide hidden block of one group;
- * there are groups * I/32 of them, and item i goes to workgroup i mod grid.  FC2 tiles
- * are the 16-row output tiles, groups * D/16 of them in group-major order.
+ * its FC2 tile range, and with steal the claimable zone at the end of that range).
+ * form 0: the decode form's whole-K kernel, `groups` distinct experts (<= 128, I <=
+ * 512); form 1: the grouped form, `groups` chunks of up to 32 routes of one expert (<=
+ * 1024).  An FC1 item is one 32-wide hidden block of one group; there are groups * I/32
+ * of them, and item i goes to workgroup i mod grid.  FC2 tiles are the 16-row output
+ * tiles, groups * D/16 of them in group-major order.  claims_ring: 0, or (form 0) the
+ * slots per wave (2..4) of a launch with FC2 tail claims, whose zones it then reports.
  * Outputs are host pointers:
- *   split i32 [grid, 4]: per workgroup {FC1 items, first FC2 tile, FC2 tiles, streaming
- *     waves per workgroup};
+ *   split i32 [grid, 6]: per workgroup {FC1 items, first FC2 tile, FC2 tiles, streaming
+ *     waves per workgroup, first tile of its claimable zone, grains of eight tiles in it};
  *   items i32 [groups * I/32, 2] (may be NULL): (group, hidden block) of item i.
- * MOE_EINVAL for a bad form, shape, group count or grid (1..2048). */
-int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t grid, int32_t* split,
-                   int32_t* items);
+ * MOE_EINVAL for a bad form, shape, group count, grid (1..2048) or claims_ring. */
+int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t grid, int32_t claims_ring,
+                   int32_t* split, int32_t* items);
 
 /* Bytes of the four packed weight buffers written by moe_pack_weights (experts page,
  * ExpertsKernel.schedule / produce: the weights stream tile by tile, 128 K at a time).

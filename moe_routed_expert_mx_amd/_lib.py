@@ -68,7 +68,7 @@ def _load():
         "moe_decode_run_noalloc": (c.c_int, [c.POINTER(moe_weights_t), c.POINTER(moe_run_opts_t), P, P, c.c_int32,
                                              c.c_int32, P, c.c_size_t, P]),
         "moe_combine": (c.c_int, [P, c.c_size_t, P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
-        "moe_work_split": (c.c_int, [c.c_int32] * 5 + [P, P]),
+        "moe_work_split": (c.c_int, [c.c_int32] * 6 + [P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -125,13 +125,14 @@ def moe_packed_weight_bytes(E: int, D: int, I: int):
     return tuple(o.value for o in out)
 
 
-def moe_work_split(form: int, groups: int, D: int, I: int, grid: int):
-    """Host-side static split of an experts launch: (split [grid, 4], items [groups*I/32, 2])
+def moe_work_split(form: int, groups: int, D: int, I: int, grid: int, claims_ring: int = 0):
+    """Host-side static split of an experts launch: (split [grid, 6], items [groups*I/32, 2])
     as numpy int32 arrays (no device call)."""
     import numpy as np
-    split = np.zeros((grid, 4), np.int32)
+    split = np.zeros((grid, 6), np.int32)
     items = np.zeros((max(groups * (I // 32), 1), 2), np.int32)
-    _check("moe_work_split", lib.moe_work_split(form, groups, D, I, grid, split.ctypes.data, items.ctypes.data))
+    _check("moe_work_split", lib.moe_work_split(form, groups, D, I, grid, claims_ring, split.ctypes.data,
+                                                items.ctypes.data))
     return split, items[:groups * (I // 32)]
 
 

@@ -2870,7 +2870,13 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
       }
     }
   }
-  if (w == kQFin && l == 0) sw[kQCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
+  if (w == kQFin && l == 0) {
+    const uint32_t call = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
+    sw[kQCall / 4] = call;
+    // re-arm this workgroup's claim counter for the call, {call, 0 back, 0 front}, early:
+    // claims by others that reach it first see the old call's tag and take nothing
+    if (CLAIMS) st_dev_u64(a.claims + c, static_cast<uint64_t>(call) << 32);
+  }
   __syncthreads();
 
   // ---- routing (experts page, the capacity <= 8 path: one unit per distinct expert,
@@ -3170,9 +3176,6 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
       // Each claim waits until every streaming wave has taken all but kQAhead of the
       // posted grains, so grains stay unclaimed, and free for others, until needed.  A
       // grain is computed by whoever claims it exactly as its owner would.
-      // re-arm this workgroup's counter for the call: {call, 0 back, 0 front}.  Claims by
-      // others that reach it first see the old call's tag and take nothing.
-      if (l == 0) st_dev_u64(a.claims + c, static_cast<uint64_t>(call) << 32);
       int posted = 0;
       auto pace = [&]() {
         if (posted >= kQAhead) {
@@ -4511,10 +4514,10 @@ size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32
   return ws_layout(E, D, I, topk, B_max).end;
 }
 
-int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t grid, int32_t* split,
-                   int32_t* items) {
+int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t grid, int32_t claims_ring,
+                   int32_t* split, int32_t* items) {
   if ((form != 0 && form != 1) || groups < 0 || !shape_ok(1, D, I) || grid < 1 || grid > kMaxGrid ||
-      split == nullptr)
+      split == nullptr || claims_ring < 0 || claims_ring == 1 || claims_ring > 4 || (form == 1 && claims_ring != 0))
     return MOE_EINVAL;
   const int HB = I / 32, NS1 = D / 128, NS2 = (I + 127) / 128;
   if (form == 0 && (groups > kQGMax || HB > kQHB)) return MOE_EINVAL;
@@ -4522,10 +4525,15 @@ int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t g
   for (int c = 0; c < grid; ++c) {
     const QWork q = form == 0 ? q_work(groups, HB, NS1, D, grid, c, 0, q_item_tiles(D, NS2))
                               : g_work(groups, HB, NS1, D, grid, c);
-    split[4 * c] = q.n1;
-    split[4 * c + 1] = q.first2;
-    split[4 * c + 2] = q.n2;
-    split[4 * c + 3] = form == 0 ? kQStream : kGStream;
+    int zb = q.first2 + q.n2;
+    const int Z = claims_ring ? q_zone(q, kQZone, claims_ring, zb) : 0;
+    int32_t* r = split + 6 * c;
+    r[0] = q.n1;
+    r[1] = q.first2;
+    r[2] = q.n2;
+    r[3] = form == 0 ? kQStream : kGStream;
+    r[4] = zb;
+    r[5] = Z;
   }
   if (items != nullptr) {
     for (int i = 0; i < groups * HB; ++i) {

@@ -84,14 +84,18 @@ def test_grouped_items_of_a_chunk_share_an_xcd(m):
 
 def test_split_rejects_bad_arguments(m):
     L = m._lib.lib
-    buf = np.zeros((4, 4), np.int32)
-    assert L.moe_work_split(2, 1, 3584, 384, 4, buf.ctypes.data, None) == m._lib.MOE_EINVAL
-    assert L.moe_work_split(0, 129, 3584, 384, 4, buf.ctypes.data, None) == m._lib.MOE_EINVAL
-    assert L.moe_work_split(1, 1025, 3584, 384, 4, buf.ctypes.data, None) == m._lib.MOE_EINVAL
-    assert L.moe_work_split(0, 1, 3584, 384, 0, buf.ctypes.data, None) == m._lib.MOE_EINVAL
-    assert L.moe_work_split(0, 1, 3584, 384, 2049, buf.ctypes.data, None) == m._lib.MOE_EINVAL
-    assert L.moe_work_split(0, 1, 3000, 384, 4, buf.ctypes.data, None) == m._lib.MOE_EINVAL
-    assert L.moe_work_split(0, 1, 3584, 384, 4, None, None) == m._lib.MOE_EINVAL
+    buf = np.zeros((4, 6), np.int32)
+    E = m._lib.MOE_EINVAL
+    assert L.moe_work_split(2, 1, 3584, 384, 4, 0, buf.ctypes.data, None) == E
+    assert L.moe_work_split(0, 129, 3584, 384, 4, 0, buf.ctypes.data, None) == E
+    assert L.moe_work_split(1, 1025, 3584, 384, 4, 0, buf.ctypes.data, None) == E
+    assert L.moe_work_split(0, 1, 3584, 384, 0, 0, buf.ctypes.data, None) == E
+    assert L.moe_work_split(0, 1, 3584, 384, 2049, 0, buf.ctypes.data, None) == E
+    assert L.moe_work_split(0, 1, 3000, 384, 4, 0, buf.ctypes.data, None) == E
+    assert L.moe_work_split(0, 1, 3584, 384, 4, 0, None, None) == E
+    assert L.moe_work_split(0, 1, 3584, 384, 4, 1, buf.ctypes.data, None) == E      # ring 2..4
+    assert L.moe_work_split(1, 1, 3584, 384, 4, 2, buf.ctypes.data, None) == E      # decode form only
+    assert L.moe_work_split(0, 1, 3584, 384, 4, 2, buf.ctypes.data, None) == m._lib.MOE_OK
 
 
 # ------------------------------------------------------------------------ protocol
@@ -285,3 +289,232 @@ def test_missing_block_gives_up_together(m, form):
     assert not blocked
     assert first is not None and first >= 4096
     assert last - first <= 256 + 1, (first, last)
+
+
+# ------------------------------------------------------------- FC2 tail claims
+def _kernel_constants():
+    """The claim constants, read from the kernel source (so that the model follows it)."""
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "moe_routed_expert_mx_amd", "csrc", "moe_mx.hip")).read()
+    get = lambda n: int(re.search(r"constexpr int %s = (\d+);" % n, src).group(1))
+    return {"ahead": get("kQAhead"), "victims": get("kQVictims"), "ring": get("kQRing"), "grain": 8}
+
+
+def _claims_model(split, items, D, I, R, K, rng):
+    """decode_whole_kernel with FC2 tail claims, as interleavable generators (each yields
+    the condition it waits on).  Streaming waves issue R slots ahead of what they consume;
+    a slot past the wave's head takes the next queue entry (waiting until it is posted) and
+    reports it taken.  The finisher, after FC1, re-arms its counter, claims its zone's
+    grains from the front (each claim once every wave has taken all but `ahead` of the
+    posted grains), then the zones of the next `victims` workgroups from the back where
+    they lie in its last group, then posts the end entry; without a zone it posts the end
+    entry first.  The counter is re-armed when the finisher starts; a claim that reaches a
+    counter not yet re-armed sees the old call's tag and takes nothing.  Returns the
+    generators and the record of computed tiles."""
+    NS1, HB, TPE = D // 128, I // 32, D // 16
+    grid = split.shape[0]
+    A, V, RING, GR = K["ahead"], K["victims"], K["ring"], K["grain"]
+    flags, ctr, done = set(), {}, []
+    call = 7
+
+    def wg(c):
+        n1, first2, n2, _, zb, Z = (int(v) for v in split[c])
+        st = {"prog": [0] * 8, "prog2": [0] * 8, "cons": 0, "ready": 0, "xdone": 0, "taken": [0] * 8,
+              "posted": 0, "queue": [None] * RING, "history": []}
+        g0 = first2 // TPE
+        glast = (first2 + n2 - 1) // TPE if n2 > 0 else -1
+
+        def post(first):
+            st["queue"][st["posted"] % RING] = first
+            st["history"].append(first)
+            st["posted"] += 1
+
+        def wave(w):
+            m1 = -(-(NS1 - w) // 8) if w < NS1 else 0
+            n1el = n1 * m1
+            issued = []
+            cur = {"t": first2 + w, "q": 0, "end": False}
+
+            def issue():
+                if len(issued) < n1el:
+                    issued.append(("fc1",))
+                    return
+                if cur["t"] < zb:
+                    issued.append(("tile", cur["t"]))
+                    cur["t"] += 8
+                    return
+                if cur["end"]:
+                    issued.append(("dummy",))
+                    return
+                q = cur["q"]
+                yield lambda: st["posted"] >= q + 1
+                s = st["queue"][q % RING]
+                assert s == st["history"][q], "a queue entry was overwritten before its issue read it"
+                cur["q"] += 1
+                st["taken"][w] = cur["q"]
+                if s < 0:
+                    cur["end"] = True
+                    issued.append(("dummy",))
+                else:
+                    issued.append(("tile", s + w))
+
+            for _ in range(R):
+                yield from issue()
+            st["xdone"] += 1
+            if n1el:
+                yield lambda: st["xdone"] >= 10
+            k = 0
+            for item in range(n1 if m1 else 0):
+                for _ in range(m1):
+                    assert issued[k] == ("fc1",)
+                    yield from issue()
+                    k += 1
+                yield lambda: st["cons"] >= item
+                st["prog"][w] = item + 1
+            # the consume side walks the same sequence R slots behind; every entry it
+            # reads was taken by the issue side, and is still in the ring
+            ch = {"t": first2 + w, "q": 0}
+            cur_seq = None
+            while True:
+                if ch["t"] < zb:
+                    t = ch["t"]
+                    ch["t"] += 8
+                else:
+                    q = ch["q"]
+                    assert q < st["posted"] and st["queue"][q % RING] == st["history"][q]
+                    s = st["history"][q]
+                    ch["q"] += 1
+                    if s < 0:
+                        break
+                    t = s + w
+                assert k < len(issued) and issued[k] == ("tile", t), "consume side off the issue side"
+                g = t // TPE
+                seq = g - g0
+                if seq != cur_seq:
+                    cur_seq = seq
+                    st["prog2"][w] = seq
+                    yield lambda: st["ready"] >= seq + 1
+                done.append((c, t, glast))
+                yield from issue()
+                k += 1
+            st["prog2"][w] = INF
+
+        def finisher():
+            ctr[c] = [call, 0, 0]   # re-armed for the call
+            if Z == 0:
+                post(-1)
+            st["xdone"] += 1
+            for kk in range(n1):
+                for ww in range(min(NS1, 8)):
+                    yield lambda: st["prog"][ww] >= kk + 1
+                st["cons"] = kk + 1
+                flags.add(tuple(items[c + kk * grid]))
+            if Z == 0:
+                return
+
+            def pace():
+                if st["posted"] >= A:
+                    need = st["posted"] - A + 1
+                    yield lambda: all(v >= need for v in st["taken"])
+
+            while True:
+                yield from pace()
+                tag, f, r = ctr[c]
+                ctr[c][1] += 1
+                if tag != call or f + r >= Z:
+                    break
+                post(zb + f * GR)
+            for vc in range(c + 1, min(c + V, grid - 1) + 1):
+                vn1, vf, vn2, _, vzb, vZ = (int(v) for v in split[vc])
+                if vZ == 0 or vzb // TPE != glast or (vf + vn2 - 1) // TPE != glast:
+                    continue
+                while True:
+                    yield from pace()
+                    word = ctr.setdefault(vc, ["old", 0, 0])   # not re-armed yet: an old tag
+                    tag, f, r = list(word)
+                    word[2] += 1
+                    if tag != call or f + r >= vZ:
+                        break
+                    post(vzb + (vZ - 1 - r) * GR)
+            post(-1)
+
+        def loader():
+            st["xdone"] += 1
+            for seq in range(_nseq(first2, n2, TPE)):
+                if seq >= 2:
+                    for ww in range(8):
+                        yield lambda: st["prog2"][ww] >= seq - 1
+                for j in range(HB):
+                    yield lambda: (g0 + seq, j) in flags
+                st["ready"] = seq + 1
+
+        return [wave(w) for w in range(8)] + [finisher(), loader()]
+
+    gens = []
+    for c in rng.permutation(grid):
+        gens += wg(int(c))
+    return gens, done
+
+
+def _interleave(gens, rng):
+    """Advances the generators in random order, one step at a time, until all are done;
+    returns the generators still blocked when nothing can move (none: no deadlock)."""
+    live = {i: (g, None) for i, g in enumerate(gens)}
+    while live:
+        moved = False
+        for i in rng.permutation(list(live)):
+            g, cond = live[i]
+            if cond is not None and not cond():
+                continue
+            try:
+                live[i] = (g, next(g))
+            except StopIteration:
+                del live[i]
+            moved = True
+        if not moved:
+            return list(live)
+    return []
+
+
+def _claims_runs(m, case, seeds=3):
+    """Runs the claims model of one case over `seeds` random interleavings, checking
+    every property; returns the tiles computed by thieves."""
+    G, D, I, grid = case
+    K = _kernel_constants()
+    R = 2
+    split, items = m.moe_work_split(0, G, D, I, grid, R)
+    assert split[:, 5].sum() > 0, "the case has no claimable zone"
+    TPE = D // 16
+    stolen = 0
+    for seed in range(seeds):
+        rng = np.random.default_rng(seed)
+        gens, done = _claims_model(split, items, D, I, R, K, rng)
+        blocked = _interleave(gens, rng)
+        assert not blocked, (case, seed, len(blocked))
+        tiles = sorted(t for _, t, _ in done)
+        assert tiles == list(range(G * TPE)), (case, seed)
+        for c, t, glast in done:
+            n1, first2, n2 = (int(v) for v in split[c, :3])
+            if not first2 <= t < first2 + n2:
+                assert t // TPE == glast, (case, seed, c, t)
+                stolen += 1
+    return stolen
+
+
+@pytest.mark.parametrize("case", [(13, 1024, 128, 33), (24, 1024, 128, 3), (65, 3584, 384, 61),
+                                  (9, 2048, 256, 7), (40, 512, 64, 16)])
+def test_claims_protocol_covers_every_tile_once(m, case):
+    """FC2 tail claims (experts page, ExpertsKernel steal and claims), modelled over random
+    interleavings: no wave waits for good, every FC2 tile is computed exactly once (a
+    grain goes to its owner or to one thief, never both), a thief computes only tiles of
+    its last group (whose hidden it holds), and no queue entry is read before it is
+    posted or after it is overwritten."""
+    _claims_runs(m, case)
+
+
+def test_claims_model_takes_grains_from_victims(m):
+    """The model reaches the thieves' path: in this case some interleavings hand zone
+    grains to the workgroup before their owner."""
+    assert _claims_runs(m, (13, 1024, 128, 33)) > 0
