@@ -173,6 +173,13 @@ int moe_units_export(const void* units_dev, size_t units_bytes, int32_t B, int32
                      void* header_dev, void* unit_expert_dev, void* unit_rows_dev,
                      int32_t max_units, void* stream);
 
+/* One row of a next-layer prefetch table (runtime page, PersistentExperts.run's ahead
+ * table of (address, bytes) rows): device memory the next launch will read. */
+typedef struct {
+  const void* addr;  /* device address, 16-byte aligned */
+  uint64_t bytes;    /* below 2^31 */
+} moe_prefetch_row_t;
+
 /* Options of moe_experts_run (zero-initialise for the defaults). */
 typedef struct {
   /* Exponent rule of the hidden requantization: 0 = default (the pages' choice: floor
@@ -222,6 +229,19 @@ typedef struct {
                               of range (skipped), bit 1 an id repeated within a token (one of
                               its routes is lost), bit 2 a wait gave up (never expected).
                               NULL: the flags go to a word of the workspace. */
+  /* moe_decode_run's whole-K kernel only (MOE_EINVAL elsewhere): next-layer weight
+   * prefetch (runtime page, run(x, ids, weights, ahead)).  A HOST array of up to 64 rows
+   * of device memory the next launch will read, typically its expert weights.  The
+   * kernel splits the rows' bytes over its workgroups; each workgroup's finisher wave,
+   * idle once its FC1 blocks are published, reads its share once through LDS, so that
+   * the bytes sit in the Infinity Cache when that launch starts.  The rows are read, never
+   * written, and change nothing this call computes; their memory must stay allocated
+   * until the call has run.  The table itself is copied into the launch: it may be freed
+   * when the call returns.  NULL with 0 rows: no prefetch.  MOE_EINVAL for more than 64
+   * rows, a NULL table with rows, a row of 2^31 bytes or more, or a row not 16-byte
+   * aligned. */
+  const moe_prefetch_row_t* ahead;
+  int32_t ahead_rows;
 } moe_run_opts_t;
 
 /* The routed experts (experts page, ExpertsKernel; runtime page, PersistentExperts.run):

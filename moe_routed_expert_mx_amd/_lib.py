@@ -38,7 +38,24 @@ class moe_run_opts_t(ctypes.Structure):
                 ("col_tiles", ctypes.c_int32), ("ring", ctypes.c_int32), ("exchange", ctypes.c_int32),
                 ("fc2_claims", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2),
                 ("hidden_codes_dev", ctypes.c_void_p), ("hidden_scales_dev", ctypes.c_void_p),
-                ("plan_dev", ctypes.c_void_p), ("plan_bytes", ctypes.c_size_t), ("status_dev", ctypes.c_void_p)]
+                ("plan_dev", ctypes.c_void_p), ("plan_bytes", ctypes.c_size_t), ("status_dev", ctypes.c_void_p),
+                ("ahead", ctypes.c_void_p), ("ahead_rows", ctypes.c_int32)]
+
+
+class moe_prefetch_row_t(ctypes.Structure):
+    _fields_ = [("addr", ctypes.c_void_p), ("bytes", ctypes.c_uint64)]
+
+
+def prefetch_rows(tensors_or_ranges):
+    """A next-layer prefetch table (ctypes array of moe_prefetch_row_t, row count) from device
+    tensors or (address, bytes) pairs."""
+    rows = []
+    for t in tensors_or_ranges:
+        if isinstance(t, tuple):
+            rows.append(moe_prefetch_row_t(t[0], t[1]))
+        else:
+            rows.append(moe_prefetch_row_t(t.data_ptr(), t.numel() * t.element_size()))
+    return (moe_prefetch_row_t * max(len(rows), 1))(*rows), len(rows)
 
 
 def _load():
@@ -170,10 +187,13 @@ def moe_units_export(units, B, topk, E, header, unit_expert, unit_rows, stream=N
 
 
 def _opts(hidden_rule, grid, col_tiles, ring, hidden_codes, hidden_scales, plan=None, status=None, exchange=0,
-          fc2_claims=0):
+          fc2_claims=0, ahead=None):
+    """ahead: None or (ctypes array of moe_prefetch_row_t, rows), e.g. from prefetch_rows();
+    the caller keeps the array alive until the call returns."""
+    table, rows = ahead if ahead is not None else (None, 0)
     return moe_run_opts_t(hidden_rule, grid, col_tiles, ring, exchange, fc2_claims, (ctypes.c_int32 * 2)(0, 0),
                           _ptr(hidden_codes), _ptr(hidden_scales), _ptr(plan), 0 if plan is None else _nbytes(plan),
-                          _ptr(status))
+                          _ptr(status), None if table is None else ctypes.cast(table, ctypes.c_void_p), rows)
 
 
 def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, out, *, hidden_rule=0, grid=0,
@@ -185,24 +205,27 @@ def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, 
 
 
 def moe_decode_run(weights: moe_weights_t, x, ids, ws, out, *, hidden_rule=0, grid=0, ring=0, exchange=0,
-                   fc2_claims=0, hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
+                   fc2_claims=0, ahead=None, hidden_codes=None, hidden_scales=None, plan=None, status=None,
+                   stream=None):
     """The whole step of a batch of B <= 8 tokens in one launch: x BF16 [B, D] (or uint16
     bits), ids int32 [B, topk] -> out BF16 [B*topk, D]; optional plan (u8, the moe_plan
     layout) and status (int32 [1]) outputs; exchange 0 (whole-K hidden blocks, the
     default), 1 (tagged partial sums) or 2 (finished split blocks); fc2_claims 1 turns
-    on the FC2 tail claims of exchange 0."""
+    on the FC2 tail claims of exchange 0; ahead (from prefetch_rows) names the next layer's
+    weights for the whole-K kernel to read into the Infinity Cache."""
     B, K = ids.shape
-    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, exchange, fc2_claims)
+    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, exchange, fc2_claims,
+                 ahead)
     _check("moe_decode_run", lib.moe_decode_run(ctypes.byref(weights), ctypes.byref(opts), _ptr(x), _ptr(ids), B, K,
                                                 _ptr(ws), _nbytes(ws), _ptr(out), _nbytes(out), _stream(stream)))
 
 
 def moe_decode_run_noalloc(weights: moe_weights_t, x, ids, out, *, hidden_rule=0, grid=0, ring=0, fc2_claims=0,
-                           hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
+                           ahead=None, hidden_codes=None, hidden_scales=None, plan=None, status=None, stream=None):
     """moe_decode_run with the library's fixed per-device scratch instead of a workspace
     (no allocation; the whole-K decode form only, MOE_ELIMIT beyond its limits)."""
     B, K = ids.shape
-    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, 0, fc2_claims)
+    opts = _opts(hidden_rule, grid, 0, ring, hidden_codes, hidden_scales, plan, status, 0, fc2_claims, ahead)
     _check("moe_decode_run_noalloc", lib.moe_decode_run_noalloc(ctypes.byref(weights), ctypes.byref(opts), _ptr(x),
                                                                 _ptr(ids), B, K, _ptr(out), _nbytes(out),
                                                                 _stream(stream)))

@@ -2595,6 +2595,48 @@ constexpr int kQAhead = 4;         // grains the claimer posts ahead of the slow
 constexpr int kQVictims = 2;       // workgroups after this one whose zones it may take from
 constexpr int kQRing = 16;         // queue entries (more than kQAhead plus the ring depth)
 
+// ---------------------------------------------------- next-layer weight prefetch
+// Next-layer weight prefetch (runtime page, PersistentExperts.run's ahead table): rows of
+// (address, bytes) of device memory the next launch reads.  Their bytes, cut into 1 KB
+// pieces, are split evenly over the workgroups; one wave of each reads its share into 1 KB
+// of LDS it no longer needs (bounds-checked buffer loads: a row's last piece reads
+// nothing past its end).  What matters is the side effect: the bytes pass through, and
+// stay in, the Infinity Cache, so that the next launch's first weight reads hit it.
+constexpr int kPfRows = 64;    // rows of a table (kernel arguments hold it)
+constexpr int kPfFlight = 32;  // pieces in flight per wave
+struct PfRow {
+  uint64_t addr;
+  uint32_t bytes;
+  uint32_t first;  // index of the row's first piece among all rows' pieces
+};
+struct PfTable {
+  int rows, pieces;
+  PfRow row[kPfRows];
+};
+
+__device__ __forceinline__ void pf_run(const PfTable& t, int c, int nwg, uint32_t dst) {
+  const int64_t P = t.pieces;
+  const int p0 = static_cast<int>(P * c / nwg), p1 = static_cast<int>(P * (c + 1) / nwg);
+  const int l = threadIdx.x & 63;
+  int r = 0, next = t.rows > 1 ? static_cast<int>(t.row[1].first) : p1;
+  auto at = [&](int k) { return rsrc(reinterpret_cast<const void*>(t.row[k].addr), t.row[k].bytes); };
+  __amdgpu_buffer_rsrc_t rs = at(0);
+  int n = 0;
+#pragma unroll 1
+  for (int p = p0; p < p1; ++p) {
+    if (p >= next) {
+#pragma unroll 1
+      while (r + 1 < t.rows && p >= static_cast<int>(t.row[r + 1].first)) ++r;
+      next = r + 1 < t.rows ? static_cast<int>(t.row[r + 1].first) : p1;
+      rs = at(r);
+    }
+    if (n >= kPfFlight) wait_vm<kPfFlight - 1>();
+    sdma16(rs, static_cast<uint32_t>(p - static_cast<int>(t.row[r].first)) * 1024u + 16u * l, 0u, dst);
+    ++n;
+  }
+  wait_vm<0>();
+}
+
 struct QArgs {
   const uint8_t* w13p;
   const uint8_t* s13p;
@@ -2617,6 +2659,7 @@ struct QArgs {
   uint32_t xstr, xsstr, hid_bytes;            // x code row stride, x scale row stride, one hidden buffer
   int cb;                 // token columns a group can have: min(B, 8); sizes the LDS areas below
   uint32_t red_wave;      // one wave's partial tiles: 4 tiles x cb columns x 16 rows x FP32
+  PfTable pf;             // next-layer prefetch rows
 };
 
 // Four 16-byte LDS reads at four addresses, one wait.
@@ -3221,6 +3264,8 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     // kMaxGrid, so all of them stay equal whatever grid the next call uses
 #pragma unroll 1
     for (int m = c + l * nwg; m < kMaxGrid; m += 64 * nwg) st_dev_u32(a.calls + m, call);
+    // next-layer weights: the workgroup's share, into the partial-sum area (free now)
+    if (a.pf.pieces > 0) pf_run(a.pf, c, nwg, a.o_red);
     return;
   }
   // ================================================================= loader wave
@@ -4028,6 +4073,31 @@ size_t lds_for(int R, int ns2, int g_cap, int u_cap, int IP, int B, int D) {
 }
 
 // ------------------------------------------------------------------ host helpers
+// The next-layer prefetch table of the options: rows <= kPfRows, each 16-byte aligned and
+// below 2^31 bytes (a buffer resource's range), pieces counted in 32 bits.
+bool pf_ok(const moe_run_opts_t& o) {
+  if (o.ahead_rows < 0 || o.ahead_rows > kPfRows || (o.ahead_rows > 0 && o.ahead == nullptr)) return false;
+  int64_t pieces = 0;
+  for (int r = 0; r < o.ahead_rows; ++r) {
+    const moe_prefetch_row_t& w = o.ahead[r];
+    if (w.bytes >= (1ull << 31) || (w.bytes > 0 && (w.addr == nullptr || reinterpret_cast<uintptr_t>(w.addr) % 16)))
+      return false;
+    pieces += static_cast<int64_t>((w.bytes + 1023) / 1024);
+  }
+  return pieces < (1ll << 31);
+}
+void pf_table(const moe_run_opts_t& o, PfTable& t) {
+  t.rows = 0;
+  t.pieces = 0;
+  for (int r = 0; r < o.ahead_rows; ++r) {
+    t.row[r].addr = reinterpret_cast<uint64_t>(o.ahead[r].addr);
+    t.row[r].bytes = static_cast<uint32_t>(o.ahead[r].bytes);
+    t.row[r].first = static_cast<uint32_t>(t.pieces);
+    t.pieces += static_cast<int>((o.ahead[r].bytes + 1023) / 1024);
+    t.rows = r + 1;
+  }
+}
+
 bool shape_ok(int64_t E, int64_t D, int64_t I) {
   return E >= 1 && E <= kMaxGroups && D >= 512 && D <= 16384 && D % 512 == 0 && I >= 32 && I <= 512 &&
          I % 32 == 0;
@@ -4110,10 +4180,10 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   std::memset(&o, 0, sizeof(o));
   if (opts) o = *opts;
   if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || o.col_tiles < 0 || o.col_tiles > (DEC ? 1 : 2) ||
-      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.fc2_claims < 0 || o.fc2_claims > 1 ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.fc2_claims < 0 || o.fc2_claims > 1 || !pf_ok(o) ||
       ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)))
     return MOE_EINVAL;
-  if (!DEC && (o.plan_dev != nullptr || o.status_dev != nullptr || o.exchange != 0))
+  if (!DEC && (o.plan_dev != nullptr || o.status_dev != nullptr || o.exchange != 0 || o.ahead_rows != 0))
     return MOE_EINVAL;  // decode-form options
   if (o.exchange < 0 || o.exchange > (DEC ? 2 : 0)) return MOE_EINVAL;
   if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
@@ -4124,6 +4194,7 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   // else finished split blocks
   if (DEC && o.exchange == 0 && whole_fits(wts, B, topk))
     return run_decode_whole(wts, o, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
+  if (o.ahead_rows != 0 || o.fc2_claims != 0) return MOE_EINVAL;  // options of the whole-K kernel only
   // the grouped form's default: whole-K FC1 blocks over 32-column chunks (col_tiles 0 or 2)
   // where the batch fits its tables; col_tiles 1 asks for the split-block kernel
   if (!DEC && o.col_tiles != 1 && grouped_fits(E, D, I, B, topk, o.grid ? o.grid : device_cus()))
@@ -4447,6 +4518,7 @@ int launch_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const
   a.hid_bytes = m.hid_bytes;
   a.cb = m.cb;
   a.red_wave = m.red_wave;
+  pf_table(o, a.pf);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kQWG), lds, as_stream(stream), a);
   return launch_status();
 }
@@ -4684,7 +4756,7 @@ int moe_decode_run_noalloc(const moe_weights_t* wts, const moe_run_opts_t* opts,
   if (opts) o = *opts;
   if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || o.col_tiles < 0 || o.col_tiles > 1 ||
       (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.exchange != 0 || o.fc2_claims < 0 || o.fc2_claims > 1 ||
-      ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)) ||
+      !pf_ok(o) || ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)) ||
       (o.plan_bytes != 0 && o.plan_dev == nullptr))
     return MOE_EINVAL;
   if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;

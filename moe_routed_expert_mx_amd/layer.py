@@ -43,6 +43,18 @@ class MoeLayer:
         self.units = torch.empty(_lib.moe_units_bytes(self.B_max, self.topk, self.E), dtype=torch.uint8,
                                  device=self.device)
 
+    def prefetch_table(self, replica: int, experts) -> tuple:
+        """The next-layer prefetch table (runtime page, run(..., ahead)) naming the packed
+        weights of `experts` in replica `replica`: four rows per expert (FC1 codes and
+        scales, FC2 codes and scales), each expert's slab being contiguous in the packed
+        layout.  Pass it as ``ahead=`` to a decode-form forward() of another layer."""
+        ranges = []
+        for t in self.packed[replica]:
+            per = t.numel() // self.E
+            for e in experts:
+                ranges.append((t.data_ptr() + int(e) * per, per))
+        return _lib.prefetch_rows(ranges)
+
     def out_buffer(self, B: int) -> torch.Tensor:
         return torch.empty(B * self.topk, self.D, dtype=torch.bfloat16, device=self.device)
 

@@ -151,6 +151,25 @@ def test_decode_run_argument_checks(m):
     o = m.moe_run_opts_t()
     o.exchange = 3
     assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # no such exchange
+    # next-layer prefetch table: at most 64 rows, 16-byte aligned, below 2^31 bytes each
+    table, n = m._lib.prefetch_rows([(0x1000, 4096)] * 65)
+    o = m.moe_run_opts_t()
+    o.ahead, o.ahead_rows = ctypes.cast(table, ctypes.c_void_p), 65
+    assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL
+    o.ahead_rows = 0
+    o.ahead = None
+    o.ahead_rows = 3                                           # rows without a table
+    assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL
+    for row in ((0x1008, 4096), (0x1000, 1 << 31), (0, 16)):
+        table, n = m._lib.prefetch_rows([row])
+        o.ahead, o.ahead_rows = ctypes.cast(table, ctypes.c_void_p), n
+        assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL, row
+        assert L.moe_decode_run_noalloc(ctypes.byref(w), ctypes.byref(o), fake, fake, 2, 4, fake, big,
+                                        None) == m._lib.MOE_EINVAL
+    table, n = m._lib.prefetch_rows([(0x1000, 4096)])
+    o.ahead, o.ahead_rows = ctypes.cast(table, ctypes.c_void_p), n
+    assert L.moe_experts_run(ctypes.byref(w), ctypes.byref(o), fake, fake, big, 1, 4, fake, big, fake, big,
+                             None) == m._lib.MOE_EINVAL             # the decode form's option
     o = m.moe_run_opts_t()
     o.fc2_claims = 2
     assert dec(2, 4, opts=o) == m._lib.MOE_EINVAL              # FC2 claims: 0 (off) or 1 (on)

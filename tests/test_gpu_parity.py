@@ -616,6 +616,27 @@ def test_decode_form_fc2_claims_bit_identical(lib, name, grid):
     _check_all(d, on, hc, hs, _oracle(d), what=f"decode/{name}/claims/{grid}")
 
 
+@pytest.mark.parametrize("name", ["decode_b1", "tiny"])
+def test_decode_form_next_layer_prefetch(lib, name):
+    """Next-layer weight prefetch (runtime page, run(x, ids, weights, ahead)): a call that
+    also reads another replica's expert weights into the Infinity Cache computes the same
+    rows and hidden, bit for bit, as one without, and meets the oracle bar."""
+    log(f"decode form prefetch {name}")
+    d = workloads.generate(name)
+    w = d["workload"]
+    m, MoeLayer = lib
+    layer = MoeLayer(d["w13"], d["s13"], d["w2"], d["s2"], B_max=w.B, topk=w.K, device=DEV, replicas=2)
+    experts = np.unique(d["ids"])[:16]
+    ahead = layer.prefetch_table(1, experts)
+    base, hc0, hs0, _, st = _decode_run(lib, layer, d)
+    assert st == 0
+    for _ in range(2):
+        got, hc, hs, _, st = _decode_run(lib, layer, d, ahead=ahead)
+        assert st == 0
+        assert np.array_equal(got, base) and np.array_equal(hc, hc0) and np.array_equal(hs, hs0)
+    _check_all(d, got, hc, hs, _oracle(d), what=f"decode/{name}/ahead")
+
+
 def test_decode_form_flags_bad_ids(lib):
     """An id out of range is skipped and an id repeated within a token loses one of its
     routes; both are flagged in the status word, and every other route is exact."""
