@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 KERNEL_SRC = os.path.join(ROOT, "moe_routed_expert_mx_amd", "csrc", "moe_mx.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "experts_kernel_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernel_traffic.json")
 
 
 def kernel_hash() -> str:
@@ -129,11 +129,18 @@ def measure(d: dict, steps: int, warmup: int, *, eager: bool = False, path: str 
     def comb(i):
         layer.combine(out, rw, y)
 
+    def one_launch(i):  # B > 8: the whole step as one launch (plan and chunk table inside it)
+        layer.forward(x, ids, out, replica=i % R, path="decode")
+
+    seqs = [("step", step), ("kernel", kernel), ("combine", comb)]
+    if not decode:
+        seqs.append(("one_launch", one_launch))
+
     graphs = {}
     if not eager:
         # one graph of all `steps` steps for each timed sequence: exactly `steps` steps
         # are timed, each on its own replica
-        for key, fn in (("step", step), ("kernel", kernel), ("combine", comb)):
+        for key, fn in seqs:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(steps):
@@ -160,6 +167,7 @@ def measure(d: dict, steps: int, warmup: int, *, eager: bool = False, path: str 
     step_us = timed("step", step)
     kernel_us = timed("kernel", kernel)
     combine_us = timed("combine", comb)
+    one_launch_us = timed("one_launch", one_launch) if not decode else None
     combine_bytes = w.B * w.K * w.D * 2 + w.B * w.K * 4 + w.B * w.D * 2  # rows, weights, y
 
     io_bytes = w.B * w.D * 2 + w.B * w.K * 4 + w.B * w.K * w.D * 2  # x, ids, out
@@ -180,6 +188,7 @@ def measure(d: dict, steps: int, warmup: int, *, eager: bool = False, path: str 
         "kernel_gbs": kernel_bytes / (kernel_us * 1e-6) / 1e9,
         "flops": 6 * w.I * w.D * w.B * w.K,
         "combine_us": combine_us, "combine_alg_bytes": combine_bytes,
+        "one_launch_step_us": one_launch_us,
         "combine_gbs": combine_bytes / (combine_us * 1e-6) / 1e9,
     }
     log(json.dumps({"config_detail": res}), file=sys.stderr)
@@ -317,6 +326,11 @@ def main():
             "cpu_baseline": {k: {"us": round(v["value"], 1), "cores": v["cores"], "sample": v["sample"]}
                              for k, v in cpu.get(n, {}).items()},
         }
+        if r["one_launch_step_us"] is not None:
+            line["per_workload"][n]["one_launch"] = {
+                "kernel": "grouped_kernel (one launch)", "us": round(r["one_launch_step_us"], 3),
+                "note": "the step as one moe_decode_run launch (plan and chunk table inside the grouped "
+                        "kernel); the default step is moe_plan_group + moe_experts_run"}
     print(json.dumps(line), flush=True)
 
 

@@ -75,7 +75,8 @@ size_t moe_units_bytes(int32_t B, int32_t topk, int32_t E);
 
 /* Bytes of the caller-owned workspace of the experts kernel for calls with up to B_max
  * tokens (runtime page, scratch()): call counters, hidden-block flags and arrival
- * counters, the hidden-exchange images and the FC1 partial sums.  Its layout is a
+ * counters, the hidden-exchange images, the FC1 partial sums, and the plan the one-launch
+ * grouped form (moe_decode_run, B > 8) makes with its per-workgroup flags.  Its layout is a
  * function of (E, D, I, topk) and its size, so one workspace serves every batch up to
  * the B_max it was sized for.  0 on invalid sizes. */
 size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32_t topk);
@@ -264,10 +265,20 @@ int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
                     int32_t topk, void* ws_dev, size_t ws_bytes, void* out_dev, size_t out_bytes,
                     void* stream);
 
-/* The whole step of a small batch in one launch (B <= 8): the kernel also quantizes x
- * and routes the batch itself (experts page, the capacity <= 8 path of ExpertsKernel,
- * which skips the plan and group kernels: one unit per distinct expert, its tokens in
- * token order, the same table moe_group writes for such a batch).
+/* The whole step of a batch in one launch: the kernel also quantizes x and routes the
+ * batch itself.  B <= 8: the experts page's capacity <= 8 path of ExpertsKernel, which
+ * skips the plan and group kernels (one unit per distinct expert, its tokens in token
+ * order, the same table moe_group writes for such a batch).  B > 8: the grouped kernel
+ * (as moe_experts_run with col_tiles 0) with the plan and the chunk table made inside the
+ * launch (experts page, plan_chunk and ExpertsGroupKernel; the early group release the
+ * runtime page describes taken to its end): every workgroup quantizes a share of x and
+ * publishes it (device-coherent stores, call-tagged flag), builds the chunk table from ids
+ * in its own LDS, and starts its weight stream at once; its first x reads wait for the
+ * whole plan.  The rows are the same bit for bit as moe_plan_group + moe_experts_run's;
+ * options as there (col_tiles 0 or 2, grid, hidden dump), plus plan_dev and status_dev;
+ * exchange, fc2_claims and ahead must be 0 (MOE_EINVAL), and batches beyond the grouped
+ * kernel's limits (I > 384, more than 1024 chunks, more than 32 FC1 blocks or 8 FC2
+ * chunks per workgroup, B * topk >= 65535) are MOE_EINVAL.
  * Inputs x_dev BF16 [B, D] and ids_dev i32 [B, topk]; outputs as moe_experts_run
  * (out_dev BF16 [B*topk, D], top-k order; optional hidden dump), plus the optional plan
  * and status word of moe_run_opts_t.  The FC1 -> FC2 exchange is chosen by
@@ -276,7 +287,7 @@ int moe_experts_run(const moe_weights_t* weights, const moe_run_opts_t* opts,
  * split-block variants of the experts kernel (the workspace from moe_workspace_bytes
  * holds any of them).  The FP32 sums of one call are summed in a fixed order, so repeated
  * calls give identical rows.  Ids out of range are skipped and flagged (status bit 0).
- * Errors: MOE_EINVAL for B > 8 or the cases of moe_experts_run; MOE_ENOSPACE likewise.
+ * Errors: MOE_EINVAL for the cases of moe_experts_run; MOE_ENOSPACE likewise.
  * The same residency and no-overlap rules as moe_experts_run apply. */
 int moe_decode_run(const moe_weights_t* weights, const moe_run_opts_t* opts, const void* x_dev,
                    const int32_t* ids_dev, int32_t B, int32_t topk, void* ws_dev, size_t ws_bytes,

@@ -207,7 +207,8 @@ def moe_experts_run(weights: moe_weights_t, plan, units, B: int, topk: int, ws, 
 def moe_decode_run(weights: moe_weights_t, x, ids, ws, out, *, hidden_rule=0, grid=0, ring=0, exchange=0,
                    fc2_claims=0, ahead=None, hidden_codes=None, hidden_scales=None, plan=None, status=None,
                    stream=None):
-    """The whole step of a batch of B <= 8 tokens in one launch: x BF16 [B, D] (or uint16
+    """The whole step of a batch in one launch (B <= 8: the decode kernel; B > 8: the
+    grouped kernel making its own plan and chunk table): x BF16 [B, D] (or uint16
     bits), ids int32 [B, topk] -> out BF16 [B*topk, D]; optional plan (u8, the moe_plan
     layout) and status (int32 [1]) outputs; exchange 0 (whole-K hidden blocks, the
     default), 1 (tagged partial sums) or 2 (finished split blocks); fc2_claims 1 turns

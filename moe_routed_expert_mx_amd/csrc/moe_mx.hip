@@ -177,6 +177,35 @@ __device__ __forceinline__ void plan_quarter(const uint8_t* __restrict__ x, int6
   if ((idx4 & 3) == 0) scales[idx4 >> 2] = static_cast<uint8_t>(e + 127);
 }
 
+// plan_quarter with device-coherent stores (sc1: written through to memory, so that other
+// workgroups of the same launch read them after an acquire; no L2 write-back needed).
+__device__ __forceinline__ void plan_quarter_dev(const uint8_t* __restrict__ x, int64_t idx4, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales) {
+  const uint4 q = ld16(x + idx4 * 16);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float v[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int e = mx_exponent(amax, false);
+  const float sc = exp2_neg(e);
+  uint32_t c[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    c[k] = to_e4m3(v[4 * k] * sc) | (to_e4m3(v[4 * k + 1] * sc) << 8) | (to_e4m3(v[4 * k + 2] * sc) << 16) |
+           (to_e4m3(v[4 * k + 3] * sc) << 24);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(codes + idx4 * 8), static_cast<uint64_t>(c[0]) | (static_cast<uint64_t>(c[1]) << 32),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((idx4 & 3) == 0)
+    __hip_atomic_store(scales + (idx4 >> 2), static_cast<uint8_t>(e + 127), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ x, int64_t nblocks,
                                                    uint8_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
@@ -596,6 +625,7 @@ struct WsLayout {
   size_t calls, status, arrive, flags, hcodes, hscales, partials;
   size_t qcalls, qclaims, qhq;  // decode form with whole-K FC1 blocks
   size_t gcalls, gflags, ghid;  // grouped form with whole-K FC1 blocks
+  size_t gplan, gpflags;        // the grouped form in one launch: its plan, its plan flags
   size_t end;
   int64_t max_tiles, max_blocks;
   int64_t dec_slots;  // decode-form partial-sum slots (512 tagged pairs each)
@@ -615,7 +645,6 @@ int64_t max_tiles_for(int64_t U, int E) {
 
 WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   WsLayout L{};
-  (void)D;
   const int64_t U = static_cast<int64_t>(B_max) * K;
   const int HB = I / 32;
   const int64_t IP = (I + 127) / 128 * 128;
@@ -662,6 +691,12 @@ WsLayout ws_layout(int E, int D, int I, int K, int B_max) {
   off = align256(off + static_cast<size_t>(chunks) * HB * 4);
   L.ghid = off;
   off = align256(off + static_cast<size_t>(chunks) * kChunkCols * (IP + 16) + 1024);
+  // the grouped form in one launch (moe_decode_run, B > 8): the plan it makes (x codes,
+  // then scales) and a call-tagged flag per workgroup for its share
+  L.gplan = off;
+  off = align256(off + static_cast<size_t>(B_max) * D / 32 * 33);
+  L.gpflags = off;
+  off = align256(off + kMaxGrid * 4);
   L.end = off;
   return L;
 }
@@ -3424,10 +3459,13 @@ constexpr uint32_t kGPub = 32;     // [kGStream] staged items of wave w the load
 constexpr uint32_t kGProg2 = 64;   // [kGStream] wave w is done with every FC2 chunk sequence < value
 constexpr uint32_t kGReady = 96;   // FC2 chunk sequences loaded into the hidden buffer
 constexpr uint32_t kGCall = 100;   // this call's number
+constexpr uint32_t kGXReady = 104; // the one-launch form: every workgroup's share of the plan is out
 constexpr uint32_t kGWords = 128;  // bytes of the words above (cleared at the start)
 constexpr uint32_t kGExp = 128;    // [kGChunks] u16 expert of chunk ch
-constexpr uint32_t kGTok = kGExp + 2 * kGChunks;  // [kGItems][32] u16 token of item k's column (0xffff: padded)
-constexpr uint32_t kGTables = kGTok + 2 * kGItems * kChunkCols;
+constexpr uint32_t kGTok = kGExp + 2 * kGChunks;  // [kGItems][32] u16 pair t*K+s of item k's column (0xffff: padded)
+constexpr int kGSeqMax = 8;        // chunks of a workgroup's FC2 run (the one-launch form)
+constexpr uint32_t kGPairs = kGTok + 2 * kGItems * kChunkCols;  // [kGSeqMax][32] u16 pairs of the run's chunks
+constexpr uint32_t kGTables = kGPairs + 2 * kGSeqMax * kChunkCols;
 
 struct GArgs {
   const uint8_t* w13p;
@@ -3450,6 +3488,11 @@ struct GArgs {
   uint32_t out_bytes;       // bytes of the output rows
   uint32_t colb;            // bytes of one hidden column (IP + 16)
   uint32_t o_ring, o_hid, hid_code_bytes;  // LDS: rings; hidden buffer (FC1: staging), its code bytes
+  // the one-launch form: the kernel makes the plan (into `plan`) and the chunk table itself
+  const uint8_t* x;         // BF16 [B, D]
+  const int32_t* ids;       // [B, K]
+  uint32_t* pflags;         // [kMaxGrid] call-tagged: workgroup c's share of the plan is out
+  int E;
 };
 
 __device__ __forceinline__ int lds_u16(uint32_t addr) {
@@ -3565,11 +3608,12 @@ __device__ __forceinline__ void g_xoffsets(const GArgs& a, uint32_t lb, int wi, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int col = 8 * i + (l >> 3);
-    const int tok = lds_u16(tb + 2 * col);
+    const int pr = lds_u16(tb + 2 * col);
     const int part = (l & 7) ^ (col & 7);
-    xo[i] = tok == 0xffff ? kOutside : static_cast<uint32_t>(tok * a.D + 16 * part);
+    xo[i] = pr == 0xffff ? kOutside : static_cast<uint32_t>(pr / a.K * a.D + 16 * part);
   }
-  const int ts = l < kChunkCols ? lds_u16(tb + 2 * l) : 0xffff;
+  const int ps = l < kChunkCols ? lds_u16(tb + 2 * l) : 0xffff;
+  const int ts = ps == 0xffff ? 0xffff : ps / a.K;
   x0 = xo[0];
   x1 = xo[1];
   x2 = xo[2];
@@ -3642,8 +3686,22 @@ __device__ __forceinline__ void g_start(const GArgs& a, const QWork& q, uint32_t
   }
 }
 
-// The slot at cursor c: always kGOps DMA instructions.
-template <int NS2>
+// The x part of an FC1 slot: the chunk's 32 columns of the step as whole lines, and their
+// scale words (kGOps / 2 DMA instructions).
+__device__ __forceinline__ void g_issue_x(const GArgs& a, int w, const GCursor& c, __amdgpu_buffer_rsrc_t rx) {
+  const uint32_t so = a.o_ring + static_cast<uint32_t>((w * kGR + c.k % kGR) * kGSlot);
+  const uint32_t ks = static_cast<uint32_t>(128 * c.si);
+  sdma16(rx, c.xo0, ks, so + kGHalf);
+  sdma16(rx, c.xo1, ks, so + kGHalf + 1024);
+  sdma16(rx, c.xo2, ks, so + kGHalf + 2048);
+  sdma16(rx, c.xo3, ks, so + kGHalf + 3072);
+  sdma4(rx, c.xso, static_cast<uint32_t>(4 * c.si), so + kGHalf + 4096);
+}
+
+// The slot at cursor c: always kGOps DMA instructions.  WITH_X false: an FC1 slot's
+// weights only (the one-launch form's first slots, whose x part waits for the plan:
+// g_issue_x then).
+template <int NS2, bool WITH_X = true>
 __device__ __forceinline__ void g_issue(const GArgs& a, const QWork& q, uint32_t lb, int w, int n1el, int n_el,
                                         int n2w, const GCursor& c, __amdgpu_buffer_rsrc_t rx,
                                         __amdgpu_buffer_rsrc_t none) {
@@ -3661,12 +3719,7 @@ __device__ __forceinline__ void g_issue(const GArgs& a, const QWork& q, uint32_t
 #pragma unroll
     for (int t = 0; t < 4; ++t) sdma16<kNT>(rw, v16, st * 4096 + t * 1024, so + t * 1024);
     sdma4<kNT>(rs, v4, st * 256, so + 4096);
-    const uint32_t ks = static_cast<uint32_t>(128 * s);
-    sdma16(rx, c.xo0, ks, so + kGHalf);
-    sdma16(rx, c.xo1, ks, so + kGHalf + 1024);
-    sdma16(rx, c.xo2, ks, so + kGHalf + 2048);
-    sdma16(rx, c.xo3, ks, so + kGHalf + 3072);
-    sdma4(rx, c.xso, static_cast<uint32_t>(4 * s), so + kGHalf + 4096);
+    if (WITH_X) g_issue_x(a, w, c, rx);
   } else if (c.k < n_el) {
     // two FC2 tiles of the wave's sequence (the second may lie past it: nothing loaded)
     int chunk = c.chunk, rt2 = c.rt2;
@@ -3818,7 +3871,148 @@ __device__ __forceinline__ void g_finish(const GArgs& a, v4f (&acc)[4][kGTiles],
   }
 }
 
-template <int NS2>
+// ------------------------------------------ the grouped form in one launch (prologue)
+// The one-launch form's prologue, in every workgroup: (1) its share of the MXFP8 plan of
+// x (experts page, plan_chunk / mx_block; four lanes per 32-element block), stored
+// device-coherent and published with a call-tagged flag; (2) the chunk table of the batch
+// (experts page, ExpertsGroupKernel: each expert's routes in token order, cut into chunks
+// of 32), built in LDS from the ids -- per-expert token bitmasks, route counts, an
+// exclusive scan of the chunk counts -- using `scr`, LDS no DMA has reached yet; then one
+// more pass over the routes places each route of a chunk this workgroup needs (its FC1
+// items' and its FC2 run's) at its rank.  It leaves the chunks' experts in kGExp, the
+// pairs of its FC1 items in kGTok and those of its FC2 run in kGPairs, and returns the
+// chunk count (uniform).
+__device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, uint32_t call) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ uint32_t wsum[kGWG / 64];
+  __shared__ int s_flags, s_total;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwg = gridDim.x, c = blockIdx.x;
+  const int E = a.E, K = a.K, U = a.B * K, W = (a.B + 31) / 32;
+  // (1) the plan share: 32-element blocks [c nb / grid, (c + 1) nb / grid)
+  {
+    const int64_t nb = static_cast<int64_t>(a.B) * a.D / 32;
+    const int64_t b0 = nb * c / nwg, b1 = nb * (c + 1) / nwg;
+    uint8_t* codes = const_cast<uint8_t*>(a.plan);
+    for (int64_t idx4 = 4 * b0 + tid; idx4 < 4 * b1; idx4 += kGWG)
+      plan_quarter_dev(a.x, idx4, codes, codes + static_cast<int64_t>(a.B) * a.D);
+    wait_stores();  // every lane's device-coherent stores are done ...
+    __syncthreads();
+    if (tid == 0) st_dev_u32(a.pflags + c, call);  // ... before the share's flag
+  }
+  // (2) the chunk table
+  uint32_t* masks = reinterpret_cast<uint32_t*>(smem + scr);  // [W][E]
+  int* routes = reinterpret_cast<int*>(masks + W * E);        // [E] route counts, then token counts
+  int* chunk0 = routes + E;                                   // [E] first chunk
+  int* slot = chunk0 + E;                                     // [kGChunks] the chunk's row of `rows`
+  uint16_t* rows = reinterpret_cast<uint16_t*>(slot + kGChunks);  // [kGItems + kGSeqMax][32] pairs
+  for (int i = tid; i < W * E; i += kGWG) masks[i] = 0u;
+  for (int i = tid; i < E; i += kGWG) routes[i] = 0;
+  for (int i = tid; i < kGChunks; i += kGWG) slot[i] = 0x7fffffff;
+  for (int i = tid; i < (kGItems + kGSeqMax) * kChunkCols; i += kGWG) rows[i] = 0xffff;
+  if (tid == 0) s_flags = 0;
+  constexpr int kHeld = 8;  // routes held in registers per thread (all of them for U <= 4608)
+  int ev[kHeld];
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h) ev[h] = tid + h * kGWG < U ? a.ids[tid + h * kGWG] : -1;
+  __syncthreads();
+  int bad = 0;
+  auto mark = [&](int r, int e) {
+    if (e < 0 || e >= E) {
+      bad = 1;
+      return;
+    }
+    const int t = r / K;
+    atomicOr(&masks[(t >> 5) * E + e], 1u << (t & 31));
+    atomicAdd(&routes[e], 1);
+  };
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h)
+    if (tid + h * kGWG < U) mark(tid + h * kGWG, ev[h]);
+  for (int r = tid + kHeld * kGWG; r < U; r += kGWG) mark(r, a.ids[r]);
+  if (bad) atomicOr(&s_flags, 1);
+  __syncthreads();
+  // thread i holds experts 2i and 2i + 1: their token counts and chunk counts, scanned
+  int cnt[2], nch[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = 2 * tid + h;
+    cnt[h] = 0;
+    if (e < E) {
+      for (int wd = 0; wd < W; ++wd) cnt[h] += __popc(masks[wd * E + e]);
+      if (cnt[h] != routes[e]) atomicOr(&s_flags, 2);  // an id repeated within a token
+    }
+    nch[h] = (cnt[h] + kChunkCols - 1) / kChunkCols;
+  }
+  const uint32_t local = static_cast<uint32_t>(nch[0] + nch[1]);
+  const uint32_t incl = wave_scan_u32(local);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+  for (int wv = 0; wv < wave; ++wv) before += wsum[wv];
+  if (tid == kGWG - 1) s_total = static_cast<int>(before + incl);
+  const int first = static_cast<int>(before + incl - local);
+  // the chunk entries of this thread's experts (after every count is read)
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = 2 * tid + h;
+    if (e < E) {
+      const int c0 = first + (h ? nch[0] : 0);
+      routes[e] = cnt[h];
+      chunk0[e] = c0;
+      for (int q = 0; q < nch[h] && c0 + q < kGChunks; ++q) reinterpret_cast<uint16_t*>(smem + kGExp)[c0 + q] = static_cast<uint16_t>(e);
+    }
+  }
+  __syncthreads();
+  const int n_chunks = s_total;
+  if (c == 0 && tid == 0 && s_flags != 0) __hip_atomic_fetch_or(a.err, s_flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the chunks this workgroup needs, its FC1 items' (k < n1) and its FC2 run's (k = n1 +
+  // sequence): each chunk's row of `rows` is the least k that needs it
+  const QWork q = g_work(n_chunks, a.HB, a.NS1, a.D, nwg, c);
+  const int n1 = q.n1 < kGItems ? q.n1 : kGItems;
+  const int g0 = q.first2 / q.TPE;
+  int nseq = q.n2 > 0 ? (q.first2 + q.n2 - 1) / q.TPE - g0 + 1 : 0;
+  nseq = nseq < kGSeqMax ? nseq : kGSeqMax;
+  int my_ch = n_chunks;  // the chunk of k = tid
+  if (tid < n1 + nseq) {
+    int jj;
+    my_ch = g0 + tid - n1;
+    if (tid < n1) g_item(c + tid * nwg, n_chunks, a.HB, my_ch, jj);
+    if (my_ch < n_chunks) atomicMin(&slot[my_ch], tid);
+  }
+  __syncthreads();
+  // every route of a needed chunk, at its rank: its position among its expert's routes in
+  // token order (the token bits below it)
+  auto place = [&](int r, int e) {
+    if (e < 0 || e >= E) return;
+    const int t = r / K, tw = t >> 5;
+    int rank = __popc(masks[tw * E + e] & ((1u << (t & 31)) - 1u));
+    for (int wd = 0; wd < tw; ++wd) rank += __popc(masks[wd * E + e]);
+    const int sl = slot[chunk0[e] + rank / kChunkCols];
+    if (sl < kGItems + kGSeqMax) rows[sl * kChunkCols + rank % kChunkCols] = static_cast<uint16_t>(r);
+  };
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h)
+    if (tid + h * kGWG < U) place(tid + h * kGWG, ev[h]);
+  for (int r = tid + kHeld * kGWG; r < U; r += kGWG) place(r, a.ids[r]);
+  __syncthreads();
+  // row k of the tables: the row of thread k's chunk, shared through LDS
+  int* kch = reinterpret_cast<int*>(rows + (kGItems + kGSeqMax) * kChunkCols);  // [kGItems + kGSeqMax]
+  if (tid < n1 + nseq) kch[tid] = my_ch < n_chunks ? slot[my_ch] : -1;
+  __syncthreads();
+  for (int idx = tid; idx < (n1 + nseq) * kChunkCols; idx += kGWG) {
+    const int k = idx / kChunkCols, cl = idx - k * kChunkCols;
+    const int row = kch[k];
+    const uint16_t v = row >= 0 ? rows[row * kChunkCols + cl] : static_cast<uint16_t>(0xffff);
+    if (k < n1) reinterpret_cast<uint16_t*>(smem + kGTok)[idx] = v;
+    else reinterpret_cast<uint16_t*>(smem + kGPairs)[idx - n1 * kChunkCols] = v;
+  }
+  __syncthreads();
+  return n_chunks;
+}
+
+template <int NS2, bool FUSED>
 __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   agpr_form();
@@ -3829,23 +4023,31 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
   const int HB = a.HB, NS1 = a.NS1;
   uint32_t* sw = reinterpret_cast<uint32_t*>(smem);
 
-  // ---- prologue: the chunk count, the chunks' experts and the token columns of this
+  // ---- prologue: the chunk count, the chunks' experts and the pair columns of this
   // workgroup's FC1 items, all requested at once (read for every possible chunk: the
-  // table holds max_chunks records, and the item numbering depends on the chunk count)
+  // table holds max_chunks records, and the item numbering depends on the chunk count);
+  // the one-launch form makes them, and its share of the plan, itself
   if (tid < static_cast<int>(kGWords / 4)) sw[tid] = 0u;
-  const int n_chunks = a.hdr[4];
-  for (int ch = tid; ch < a.max_chunks && ch < kGChunks; ch += kGWG)
-    reinterpret_cast<uint16_t*>(smem + kGExp)[ch] = static_cast<uint16_t>(a.c_expert[ch]);
-  const int n1_cap = (n_chunks * HB - c + nwg - 1) / nwg;  // this workgroup's FC1 items
-  for (int idx = tid; idx < n1_cap * kChunkCols && idx < kGItems * kChunkCols; idx += kGWG) {
-    const int k = idx / kChunkCols, cl = idx - k * kChunkCols;
-    int ch, jj;
-    g_item(c + k * nwg, n_chunks, HB, ch, jj);
-    const int pr = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
-    reinterpret_cast<uint16_t*>(smem + kGTok)[idx] = static_cast<uint16_t>(pr >= 0 ? pr / a.K : 0xffff);
+  int n_chunks = 0;
+  if constexpr (FUSED) {
+    if (tid == 0) sw[kGCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
+    __syncthreads();
+    n_chunks = g_fused_prologue(a, a.o_ring, sw[kGCall / 4]);
+  } else {
+    n_chunks = a.hdr[4];
+    for (int ch = tid; ch < a.max_chunks && ch < kGChunks; ch += kGWG)
+      reinterpret_cast<uint16_t*>(smem + kGExp)[ch] = static_cast<uint16_t>(a.c_expert[ch]);
+    const int n1_cap = (n_chunks * HB - c + nwg - 1) / nwg;  // this workgroup's FC1 items
+    for (int idx = tid; idx < n1_cap * kChunkCols && idx < kGItems * kChunkCols; idx += kGWG) {
+      const int k = idx / kChunkCols, cl = idx - k * kChunkCols;
+      int ch, jj;
+      g_item(c + k * nwg, n_chunks, HB, ch, jj);
+      const int pr = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
+      reinterpret_cast<uint16_t*>(smem + kGTok)[idx] = static_cast<uint16_t>(pr >= 0 ? pr : 0xffff);
+    }
+    if (tid == 0) sw[kGCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
+    __syncthreads();
   }
-  if (tid == 0) sw[kGCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
-  __syncthreads();
 
   const QWork q = g_work(n_chunks, HB, NS1, a.D, nwg, c);
   const int g0 = q.first2 / q.TPE;  // chunk of the workgroup's first FC2 tile (sequence 0)
@@ -3866,11 +4068,26 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
     GCursor ic, cs;  // issue side (two slots ahead), consume side
     g_start(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
     g_start(a, q, lb, w, n1el, n_el, n_chunks, cs, false);
-    static_assert(kGR == 2, "the wait counts below assume two slots");
-#pragma unroll 1
-    for (int p = 0; p < kGR; ++p) {
-      g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
+    static_assert(kGR == 2 && kGOps == 10, "the wait counts below assume two slots of ten");
+    // the one-launch form: the first two slots' weights now, their x once the whole plan is
+    // out (both slots are FC1 steps of the wave's first item: an item has NS1 >= 2 steps)
+    const bool split = FUSED && n1el > 0;
+    if (split) {
+      GCursor c0 = ic;
+      g_issue<NS2, false>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
       g_step(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
+      GCursor c1 = ic;
+      g_issue<NS2, false>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
+      g_step(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
+      g_wait_lds(lb + kGXReady, 1, a.err);
+      g_issue_x(a, w, c0, rx);
+      g_issue_x(a, w, c1, rx);
+    } else {
+#pragma unroll 1
+      for (int p = 0; p < kGR; ++p) {
+        g_issue<NS2>(a, q, lb, w, n1el, n_el, n2w, ic, rx, none);
+        g_step(a, q, lb, w, n1el, n_el, n_chunks, ic, true);
+      }
     }
     v4f acc[4][kGTiles];
     const uint32_t xq_lo = static_cast<uint32_t>(col * 128 + 16 * (grp ^ (col & 7)));
@@ -3882,7 +4099,8 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
       // slot k has landed: younger are the next slot and the row stores of the last two
       // consumed slots (kGStores after each FC2 slot)
       const int nf = k - n1el < 0 ? 0 : (k - n1el > 2 ? 2 : k - n1el);
-      if (nf == 0) wait_vm<kGOps>();
+      if (split && k == 0) wait_vm<kGOps / 2>();  // younger: slot 1's x part only
+      else if (nf == 0) wait_vm<kGOps>();
       else if (nf == 1) wait_vm<kGOps + kGStores>();
       else wait_vm<kGOps + 2 * kGStores>();
       const uint32_t sa = lb + a.o_ring + static_cast<uint32_t>((w * kGR + k % kGR) * kGSlot);
@@ -3971,6 +4189,25 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
 
   // ================================================================= loader wave
   const uint32_t call = static_cast<uint32_t>(lds_uni(lb + kGCall));
+  if constexpr (FUSED) {
+    // the one-launch form: wait until every workgroup's share of the plan is out, then
+    // acquire (the L2 and L1 drop what they held of the plan's lines) before the streaming
+    // waves read x
+#pragma unroll 1
+    for (uint32_t spins = 0;; ++spins) {
+      bool ok = true;
+      for (int i = l; i < nwg; i += 64) ok = ok && ld_dev_u32(a.pflags + i) == call;
+      if (__all(ok)) break;
+      if (poll_expired(spins, a.err)) {
+        if (l == 0) __hip_atomic_fetch_or(a.err, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    wait_vm<0>();
+    if (l == 0) lds_st4(lb + kGXReady, 1u);
+  }
   // FC1: publish the staged hidden blocks in the workgroup's item order (item k is wave
   // k mod 8's (k / 8)-th): codes and scale of each column (device-coherent stores), then
   // the block's flag with the call number
@@ -3989,8 +4226,8 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
     st_dev_u64(dst + 32 * j + 16 * part + 8, static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32));
     if (part == 0) st_dev_u8(dst + a.IP + j, static_cast<uint8_t>(sc));
     if (a.dump_codes != nullptr) {
-      const int pair = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
-      if (pair >= 0) {
+      const int pair = k < kGItems ? lds_u16(lb + kGTok + static_cast<uint32_t>((k * kChunkCols + cl) * 2)) : 0xffff;
+      if (pair != 0xffff) {
         *reinterpret_cast<uint4*>(a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 16 * part) = v;
         if (part == 0) a.dump_scales[static_cast<int64_t>(pair) * HB + j] = static_cast<uint8_t>(sc);
       }
@@ -4028,7 +4265,13 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
     for (uint32_t off = 0; off < a.hid_code_bytes; off += 1024)
       __builtin_amdgcn_global_load_lds(src + off + l * 16, (lds_void*)(smem + hb + off), 16, 0, 16 /* sc1 */);
     if (l < kChunkCols) {
-      const int pr = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + l];
+      int pr;
+      if constexpr (FUSED) {
+        pr = lds_u16(lb + kGPairs + static_cast<uint32_t>((seq * kChunkCols + l) * 2));
+        pr = pr == 0xffff ? -1 : pr;
+      } else {
+        pr = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + l];
+      }
       lds_st4(lb + hb + a.hid_code_bytes + 4 * l, static_cast<uint32_t>(pr));
     }
     wait_vm<0>();
@@ -4163,8 +4406,8 @@ int run_decode_whole(const moe_weights_t* wts, const moe_run_opts_t& o, const vo
                      int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream);
 bool whole_fits(const moe_weights_t* wts, int32_t B, int32_t topk);
 bool grouped_fits(int E, int D, int I, int B, int K, int grid);
-int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, int32_t B,
-                int32_t topk, void* ws, size_t ws_bytes, void* out, void* stream);
+int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, const void* x,
+                const int32_t* ids, int32_t B, int32_t topk, void* ws, size_t ws_bytes, void* out, void* stream);
 
 // Checks, kernel variant, grid and arguments shared by both forms; enqueues one launch.
 template <bool DEC>
@@ -4198,7 +4441,7 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
   // the grouped form's default: whole-K FC1 blocks over 32-column chunks (col_tiles 0 or 2)
   // where the batch fits its tables; col_tiles 1 asks for the split-block kernel
   if (!DEC && o.col_tiles != 1 && grouped_fits(E, D, I, B, topk, o.grid ? o.grid : device_cus()))
-    return run_grouped(wts, o, plan, units, B, topk, ws, ws_bytes, out, stream);
+    return run_grouped(wts, o, plan, units, nullptr, nullptr, B, topk, ws, ws_bytes, out, stream);
   if (!DEC && o.col_tiles == 2) return MOE_EINVAL;
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
   if (B_cap < B) return MOE_ENOSPACE;
@@ -4271,11 +4514,11 @@ int run_experts(const moe_weights_t* wts, const moe_run_opts_t* opts, const void
 
 // ------------------------------------------------- grouped form, whole-K FC1 blocks (host)
 using GFn = void (*)(GArgs);
-GFn pick_g(int ns2) {
+GFn pick_g(int ns2, bool fused) {
   switch (ns2) {
-    case 1: return grouped_kernel<1>;
-    case 2: return grouped_kernel<2>;
-    default: return grouped_kernel<3>;
+    case 1: return fused ? grouped_kernel<1, true> : grouped_kernel<1, false>;
+    case 2: return fused ? grouped_kernel<2, true> : grouped_kernel<2, false>;
+    default: return fused ? grouped_kernel<3, true> : grouped_kernel<3, false>;
   }
 }
 
@@ -4309,9 +4552,26 @@ bool grouped_fits(int E, int D, int I, int B, int K, int grid) {
   const int64_t items = (chunks * (I / 32) + grid - 1) / grid;
   return I <= 384 && chunks <= kGChunks && items <= kGItems && grouped_lds(D, I).total <= kGLdsMax;
 }
+// The one-launch form also keeps the pairs of a workgroup's FC2 chunks (at most kGSeqMax)
+// and builds the chunk table in the ring's LDS (token bitmasks [B/32][E], two counts per
+// expert, a row index per chunk and the rows of the needed chunks) before any DMA; pair
+// indices are u16.
+bool grouped_fused_fits(int E, int D, int I, int B, int K, int grid) {
+  const int64_t U = static_cast<int64_t>(B) * K;
+  const int64_t chunks = max_chunks_for(U, U < E ? U : E);
+  const int64_t TPE = D / 16, cap = (chunks * TPE + grid - 1) / grid;
+  const int64_t seqs = (cap + TPE - 1) / TPE + 1;
+  const int64_t scratch = (static_cast<int64_t>((B + 31) / 32) * E + 2 * E + kGChunks) * 4 +
+                          (kGItems + kGSeqMax) * (2 * kChunkCols + 4);
+  return grouped_fits(E, D, I, B, K, grid) && seqs <= kGSeqMax && U < 0xffff && E <= 2 * kGWG &&
+         scratch <= static_cast<int64_t>(kGStream) * kGR * kGSlot;
+}
 
-int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, int32_t B,
-                int32_t topk, void* ws, size_t ws_bytes, void* out, void* stream) {
+// The grouped kernel.  units != NULL: on the plan and unit table of moe_plan_group;
+// units == NULL: the one-launch form, which makes them itself from x and ids.
+int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* plan, const void* units, const void* x,
+                const int32_t* ids, int32_t B, int32_t topk, void* ws, size_t ws_bytes, void* out, void* stream) {
+  const bool fused = units == nullptr;
   const int E = wts->E, D = wts->D, I = wts->I;
   const int IP = (I + 127) / 128 * 128, ns2 = IP / 128, HB = I / 32, NS1 = D / 128;
   const int B_cap = ws_batch_capacity(E, D, I, topk, ws_bytes);
@@ -4321,7 +4581,7 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   const GLds G = grouped_lds(D, I);
   const size_t lds = G.total;
   if (lds > static_cast<size_t>(device_lds_limit())) return MOE_EINVAL;
-  const GFn fn = pick_g(ns2);
+  const GFn fn = pick_g(ns2, fused);
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(lds)) != hipSuccess)
     return MOE_EHIP;
@@ -4333,7 +4593,7 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   if (cap > kMaxGrid) cap = kMaxGrid;
   if (o.grid > cap) return MOE_EINVAL;  // the grid must be co-resident
   const int grid = o.grid ? o.grid : cap;
-  if (!grouped_fits(E, D, I, B, topk, grid)) return MOE_EINVAL;
+  if (!(fused ? grouped_fused_fits(E, D, I, B, topk, grid) : grouped_fits(E, D, I, B, topk, grid))) return MOE_EINVAL;
 
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint8_t* ub = static_cast<uint8_t*>(const_cast<void*>(units));
@@ -4344,14 +4604,24 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   a.w2p = static_cast<const uint8_t*>(wts->w2);
   a.s2p = static_cast<const uint8_t*>(wts->s2);
   a.plan = static_cast<const uint8_t*>(plan);
-  a.hdr = reinterpret_cast<const int32_t*>(ub + UL.hdr);
-  a.c_expert = reinterpret_cast<const int32_t*>(ub + UL.c_expert);
-  a.c_pairs = reinterpret_cast<const int32_t*>(ub + UL.c_pairs);
+  if (fused) {
+    // the plan goes to the caller's plan buffer when there is one, else to the workspace
+    a.plan = o.plan_dev != nullptr ? static_cast<const uint8_t*>(o.plan_dev) : base + L.gplan;
+    a.x = static_cast<const uint8_t*>(x);
+    a.ids = ids;
+    a.pflags = reinterpret_cast<uint32_t*>(base + L.gpflags);
+    a.E = E;
+  } else {
+    a.hdr = reinterpret_cast<const int32_t*>(ub + UL.hdr);
+    a.c_expert = reinterpret_cast<const int32_t*>(ub + UL.c_expert);
+    a.c_pairs = reinterpret_cast<const int32_t*>(ub + UL.c_pairs);
+  }
   a.out = static_cast<uint16_t*>(out);
   a.hid = base + L.ghid;
   a.flags = reinterpret_cast<uint32_t*>(base + L.gflags);
   a.calls = reinterpret_cast<uint32_t*>(base + L.gcalls);
-  a.err = reinterpret_cast<int32_t*>(ub + UL.hdr) + 3;
+  a.err = fused ? (o.status_dev ? static_cast<int32_t*>(o.status_dev) : reinterpret_cast<int32_t*>(base + L.status))
+                : reinterpret_cast<int32_t*>(ub + UL.hdr) + 3;
   a.dump_codes = static_cast<uint8_t*>(o.hidden_codes_dev);
   a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
   a.B = B;
@@ -4371,6 +4641,29 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   a.hid_code_bytes = G.code_bytes;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kGWG), lds, as_stream(stream), a);
   return launch_status();
+}
+
+// The whole step of a batch of B > 8 in one launch: the grouped kernel making its plan and
+// chunk table itself (the options of the grouped form; plan_dev and status_dev as in the
+// decode form).
+int run_step_grouped(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* x, const int32_t* ids,
+                     int32_t B, int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
+  if (!wts || !ws || !out || B < 1 || topk < 1 || topk > 64 || static_cast<int64_t>(B) * topk >= 0xffff)
+    return MOE_EINVAL;
+  const int E = wts->E, D = wts->D, I = wts->I;
+  if (!shape_ok(E, D, I) || !wts->w13 || !wts->s13 || !wts->w2 || !wts->s2) return MOE_EINVAL;
+  moe_run_opts_t o;
+  std::memset(&o, 0, sizeof(o));
+  if (opts) o = *opts;
+  if (o.hidden_rule < 0 || o.hidden_rule > 2 || o.grid < 0 || (o.col_tiles != 0 && o.col_tiles != 2) ||
+      (o.ring != 0 && (o.ring < 2 || o.ring > 4)) || o.exchange != 0 || o.fc2_claims != 0 || o.ahead_rows != 0 ||
+      ((o.hidden_codes_dev == nullptr) != (o.hidden_scales_dev == nullptr)) ||
+      (o.plan_bytes != 0 && o.plan_dev == nullptr))
+    return MOE_EINVAL;
+  if (out_bytes < static_cast<size_t>(B) * topk * D * 2) return MOE_ENOSPACE;
+  if (o.plan_dev != nullptr && o.plan_bytes < static_cast<size_t>(B) * D / 32 * 33) return MOE_ENOSPACE;
+  if (!grouped_fused_fits(E, D, I, B, topk, o.grid ? o.grid : device_cus())) return MOE_EINVAL;
+  return run_grouped(wts, o, nullptr, nullptr, x, ids, B, topk, ws, ws_bytes, out, stream);
 }
 
 // ------------------------------------------------- decode form, whole-K FC1 blocks (host)
@@ -4742,7 +5035,8 @@ int moe_experts_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const 
 
 int moe_decode_run(const moe_weights_t* wts, const moe_run_opts_t* opts, const void* x, const int32_t* ids,
                    int32_t B, int32_t topk, void* ws, size_t ws_bytes, void* out, size_t out_bytes, void* stream) {
-  if (!x || !ids || B > kDecodeMax) return MOE_EINVAL;
+  if (!x || !ids) return MOE_EINVAL;
+  if (B > kDecodeMax) return run_step_grouped(wts, opts, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
   return run_experts<true>(wts, opts, nullptr, nullptr, 0, x, ids, B, topk, ws, ws_bytes, out, out_bytes, stream);
 }
 

@@ -64,8 +64,9 @@ class MoeLayer:
     def forward(self, x: torch.Tensor, ids: torch.Tensor, out: torch.Tensor | None = None, *, replica: int = 0,
                 stream=None, path: str = "auto", **opts) -> torch.Tensor:
         """x: BF16 [B, D] (or its uint16 bits), ids: int32 [B, topk], both on the device.
-        path: "decode" (one launch, B <= 8), "grouped" (plan and units in one launch, then experts) or "auto"
-        (the decode form for B <= 8 when AUTO_DECODE is set, else grouped)."""
+        path: "decode" (one launch: for B <= 8 the decode kernel, for B > 8 the grouped kernel making its own
+        plan and chunk table), "grouped" (plan and units in one launch, then experts) or "auto" (the decode form
+        for B <= 8 when AUTO_DECODE is set, else grouped)."""
         B = x.shape[0]
         if B > self.B_max or ids.shape != (B, self.topk):
             raise ValueError("batch larger than B_max or ids of the wrong shape")
@@ -92,6 +93,8 @@ class MoeLayer:
         else runs experts_kernel."""
         decode = path == "decode" or (path == "auto" and self.AUTO_DECODE and B <= self.DECODE_MAX)
         routes = B * self.topk
+        if decode and B > self.DECODE_MAX:
+            return "grouped_kernel (one launch)"
         if decode:
             whole = (min(self.E, routes) <= 128 and routes <= 640 and B * self.D // 32 <= 2560 and self.I <= 512)
             return "decode_whole_kernel" if exchange in (None, 0) and whole else "experts_kernel (decode form)"

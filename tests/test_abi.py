@@ -125,7 +125,7 @@ def test_combine_argument_checks():
 
 
 def test_decode_run_argument_checks(m):
-    """moe_decode_run (the one-launch form for B <= 8) checks its arguments on the host;
+    """moe_decode_run (the whole step in one launch) checks its arguments on the host;
     the decode-only options are refused by moe_experts_run."""
     L = m._lib.lib
     fake = ctypes.c_void_p(0x1000)
@@ -136,7 +136,17 @@ def test_decode_run_argument_checks(m):
         o = opts if opts is not None else m.moe_run_opts_t()
         return L.moe_decode_run(ctypes.byref(w), ctypes.byref(o), x, ids, B, K, fake, ws, fake, out, None)
 
-    assert dec(9, 4) == m._lib.MOE_EINVAL                    # more than 8 tokens
+    # more than 8 tokens: the grouped kernel in one launch, which refuses the options of
+    # the whole-K decode kernel and the split-block exchanges on the host
+    for field, value in (("fc2_claims", 1), ("exchange", 1), ("col_tiles", 1)):
+        o = m.moe_run_opts_t()
+        setattr(o, field, value)
+        assert dec(9, 4, opts=o) == m._lib.MOE_EINVAL, field
+    table, n = m._lib.prefetch_rows([(0x1000, 4096)])
+    o = m.moe_run_opts_t()
+    o.ahead, o.ahead_rows = ctypes.cast(table, ctypes.c_void_p), n
+    assert dec(9, 4, opts=o) == m._lib.MOE_EINVAL
+    assert dec(9, 4, out=9 * 4 * 512 * 2 - 1) == m._lib.MOE_ENOSPACE
     assert dec(0, 4) == m._lib.MOE_EINVAL
     assert dec(1, 0) == m._lib.MOE_EINVAL
     assert dec(1, 4, x=None) == m._lib.MOE_EINVAL

@@ -429,6 +429,60 @@ def test_experts_small_shapes(lib, case, grid, ring):
     _check_all(d, got, hc, hs, ref, what=f"{name}/{grid}/{ring}")
 
 
+# ------------------------------------------------------------ the grouped form, one launch
+def _one_launch(lib, layer, d, **opts):
+    """moe_decode_run for B > 8: the grouped kernel with its plan and chunk table made
+    inside the launch; rows, hidden dump, the plan it made, status."""
+    m, _ = lib
+    w = d["workload"]
+    plan = torch.zeros(m.moe_plan_bytes(w.B, w.D), dtype=torch.uint8, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got, hc, hs = _run(layer, d, path="decode", plan=plan, status=status, **opts)
+    return got, hc, hs, plan.cpu().numpy(), int(status.cpu().numpy()[0])
+
+
+@pytest.mark.parametrize("name", ["grouped_b64", "wide_b256"])
+def test_grouped_one_launch_matches_three_calls(lib, name):
+    """The step in one launch (experts page, plan_chunk and ExpertsGroupKernel inside the
+    experts launch) against moe_plan_group + moe_experts_run on the same batch: the plan
+    bit-exact against the oracle's, and rows and hidden bit for bit the same (the same
+    chunks, items and FP32 summation order), over repeated calls of both forms in turn."""
+    log(f"grouped one launch {name}")
+    d = workloads.generate(name)
+    layer = _layer(lib, d)
+    ref, hcr, hsr = _run(layer, d, path="grouped", col_tiles=2)
+    for _ in range(2):
+        got, hc, hs, plan, st = _one_launch(lib, layer, d)
+        assert st == 0
+        _check_plan(d, plan)
+        assert np.array_equal(got, ref), "rows differ from the three-call form"
+        assert np.array_equal(hc, hcr) and np.array_equal(hs, hsr)
+        again, _, _ = _run(layer, d, path="grouped", col_tiles=2)
+        assert np.array_equal(again, ref)
+    if name == "grouped_b64":
+        _check_all(d, got, hc, hs, _oracle(d), what=f"{name}/one_launch")
+
+
+FUSED_SMALL = [c for c in SMALL if c[1] > 8]
+
+
+@pytest.mark.parametrize("case", FUSED_SMALL, ids=[c[0] for c in FUSED_SMALL])
+@pytest.mark.parametrize("grid", [0, 33, 64, 200])
+def test_grouped_one_launch_small_shapes(lib, case, grid):
+    """The one-launch grouped form on ragged shapes and grids: the plan bit-exact, rows
+    equal to the three-call form's, and all of them against the oracle."""
+    name, B, E, K, D, I, routing = case
+    log(f"grouped one launch small {name} grid={grid}")
+    d = workloads.generate(workloads.custom(name, B=B, E=E, K=K, D=D, I=I, routing=routing, seed=11))
+    layer = _layer(lib, d, B_max=max(B, 40))
+    got, hc, hs, plan, st = _one_launch(lib, layer, d, grid=grid)
+    assert st == 0
+    _check_plan(d, plan)
+    ref, _, _ = _run(layer, d, path="grouped", col_tiles=2, grid=grid)
+    assert np.array_equal(got, ref)
+    _check_all(d, got, hc, hs, _oracle(d), what=f"one_launch/{name}/{grid}")
+
+
 def test_everybody_on_one_expert(lib):
     """All 200 tokens route to the same 2 experts: 13 column tiles per expert, looped
     over in weight passes of 4."""
