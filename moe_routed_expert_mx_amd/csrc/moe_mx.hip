@@ -4210,31 +4210,45 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
   }
   // FC1: publish the staged hidden blocks in the workgroup's item order (item k is wave
   // k mod 8's (k / 8)-th): codes and scale of each column (device-coherent stores), then
-  // the block's flag with the call number
+  // the block's flag with the call number.  The items found staged together (the waves
+  // tend to finish theirs at the same time) go out under one wait for their stores; a
+  // wave may refill its staging area once the loader has read it.
 #pragma unroll 1
-  for (int k = 0; k < q.n1; ++k) {
-    const int ww = k % kGStream, m = k / kGStream;
-    g_wait(lb + kGStaged + 4 * ww, m + 1, a.err);
-    int ch, j;
-    g_item(c + k * nwg, n_chunks, HB, ch, j);
-    const uint32_t stg = lb + a.o_hid + static_cast<uint32_t>(ww) * kGStage;
-    const int cl = l >> 1, part = l & 1;  // lane: 16 code bytes of column cl
-    const uint4 v = lds_ld16(stg + static_cast<uint32_t>(cl * 32 + 16 * part));
-    const uint32_t sc = lds_ld4(stg + 1024 + 4 * static_cast<uint32_t>(cl));
-    uint8_t* dst = a.hid + (static_cast<int64_t>(ch) * kChunkCols + cl) * a.colb;
-    st_dev_u64(dst + 32 * j + 16 * part, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
-    st_dev_u64(dst + 32 * j + 16 * part + 8, static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32));
-    if (part == 0) st_dev_u8(dst + a.IP + j, static_cast<uint8_t>(sc));
-    if (a.dump_codes != nullptr) {
-      const int pair = k < kGItems ? lds_u16(lb + kGTok + static_cast<uint32_t>((k * kChunkCols + cl) * 2)) : 0xffff;
-      if (pair != 0xffff) {
-        *reinterpret_cast<uint4*>(a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 16 * part) = v;
-        if (part == 0) a.dump_scales[static_cast<int64_t>(pair) * HB + j] = static_cast<uint8_t>(sc);
+  for (int k = 0; k < q.n1;) {
+    g_wait(lb + kGStaged + 4 * (k % kGStream), k / kGStream + 1, a.err);
+    int k1 = k + 1;  // one past the batch
+#pragma unroll 1
+    while (k1 < q.n1 && lds_uni(lb + kGStaged + 4 * (k1 % kGStream)) >= k1 / kGStream + 1) ++k1;
+#pragma unroll 1
+    for (int kk = k; kk < k1; ++kk) {
+      const int ww = kk % kGStream, m = kk / kGStream;
+      int ch, j;
+      g_item(c + kk * nwg, n_chunks, HB, ch, j);
+      const uint32_t stg = lb + a.o_hid + static_cast<uint32_t>(ww) * kGStage;
+      const int cl = l >> 1, part = l & 1;  // lane: 16 code bytes of column cl
+      const uint4 v = lds_ld16(stg + static_cast<uint32_t>(cl * 32 + 16 * part));
+      const uint32_t sc = lds_ld4(stg + 1024 + 4 * static_cast<uint32_t>(cl));
+      if (l == 0) lds_st4(lb + kGPub + 4 * ww, static_cast<uint32_t>(m + 1));  // after the reads (in order)
+      uint8_t* dst = a.hid + (static_cast<int64_t>(ch) * kChunkCols + cl) * a.colb;
+      st_dev_u64(dst + 32 * j + 16 * part, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32));
+      st_dev_u64(dst + 32 * j + 16 * part + 8, static_cast<uint64_t>(v.z) | (static_cast<uint64_t>(v.w) << 32));
+      if (part == 0) st_dev_u8(dst + a.IP + j, static_cast<uint8_t>(sc));
+      if (a.dump_codes != nullptr) {
+        const int pair = kk < kGItems ? lds_u16(lb + kGTok + static_cast<uint32_t>((kk * kChunkCols + cl) * 2)) : 0xffff;
+        if (pair != 0xffff) {
+          *reinterpret_cast<uint4*>(a.dump_codes + static_cast<int64_t>(pair) * a.I + 32 * j + 16 * part) = v;
+          if (part == 0) a.dump_scales[static_cast<int64_t>(pair) * HB + j] = static_cast<uint8_t>(sc);
+        }
       }
     }
     wait_stores();
-    if (l == 0) st_dev_u32(a.flags + static_cast<int64_t>(ch) * HB + j, call);
-    if (l == 0) lds_st4(lb + kGPub + 4 * ww, static_cast<uint32_t>(m + 1));
+#pragma unroll 1
+    for (int kk = k; kk < k1; ++kk) {
+      int ch, j;
+      g_item(c + kk * nwg, n_chunks, HB, ch, j);
+      if (l == 0) st_dev_u32(a.flags + static_cast<int64_t>(ch) * HB + j, call);
+    }
+    k = k1;
   }
   // FC2: for each chunk of the workgroup's run, in order: wait for its HB block flags,
   // then copy its hidden (codes and scales, device-coherent DMA) and its columns' pair
