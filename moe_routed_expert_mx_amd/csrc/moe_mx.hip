@@ -3882,13 +3882,18 @@ __device__ __forceinline__ void g_finish(const GArgs& a, v4f (&acc)[4][kGTiles],
 // items' and its FC2 run's) at its rank.  It leaves the chunks' experts in kGExp, the
 // pairs of its FC1 items in kGTok and those of its FC2 run in kGPairs, and returns the
 // chunk count (uniform).
-__device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, uint32_t call) {
+__device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, uint32_t call, bool& x_early) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ uint32_t wsum[kGWG / 64];
   __shared__ int s_flags, s_total;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwg = gridDim.x, c = blockIdx.x;
   const int E = a.E, K = a.K, U = a.B * K, W = (a.B + 31) / 32;
+  // the routes, requested first (they arrive while the plan share is made)
+  constexpr int kHeld = 8;  // routes held in registers per thread (all of them for U <= 4608)
+  int ev[kHeld];
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h) ev[h] = tid + h * kGWG < U ? a.ids[tid + h * kGWG] : -1;
   // (1) the plan share: 32-element blocks [c nb / grid, (c + 1) nb / grid)
   {
     const int64_t nb = static_cast<int64_t>(a.B) * a.D / 32;
@@ -3911,18 +3916,18 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
   for (int i = tid; i < kGChunks; i += kGWG) slot[i] = 0x7fffffff;
   for (int i = tid; i < (kGItems + kGSeqMax) * kChunkCols; i += kGWG) rows[i] = 0xffff;
   if (tid == 0) s_flags = 0;
-  constexpr int kHeld = 8;  // routes held in registers per thread (all of them for U <= 4608)
-  int ev[kHeld];
-#pragma unroll
-  for (int h = 0; h < kHeld; ++h) ev[h] = tid + h * kGWG < U ? a.ids[tid + h * kGWG] : -1;
   __syncthreads();
   int bad = 0;
+  // the token of route r, r / K, as a multiply-high: exact, since the error of kinv is
+  // below 2^-32 K and r < 2^16
+  const uint64_t kinv = (uint64_t{1} << 32) / static_cast<uint64_t>(K) + 1u;
+  auto token = [&](int r) { return static_cast<int>((static_cast<uint64_t>(r) * kinv) >> 32); };
   auto mark = [&](int r, int e) {
     if (e < 0 || e >= E) {
       bad = 1;
       return;
     }
-    const int t = r / K;
+    const int t = token(r);
     atomicOr(&masks[(t >> 5) * E + e], 1u << (t & 31));
     atomicAdd(&routes[e], 1);
   };
@@ -3959,7 +3964,7 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
     const int e = 2 * tid + h;
     if (e < E) {
       const int c0 = first + (h ? nch[0] : 0);
-      routes[e] = cnt[h];
+      routes[e] = 0;  // from here on: 1 when a chunk of e is needed here
       chunk0[e] = c0;
       for (int q = 0; q < nch[h] && c0 + q < kGChunks; ++q) reinterpret_cast<uint16_t*>(smem + kGExp)[c0 + q] = static_cast<uint16_t>(e);
     }
@@ -3979,23 +3984,52 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
     int jj;
     my_ch = g0 + tid - n1;
     if (tid < n1) g_item(c + tid * nwg, n_chunks, a.HB, my_ch, jj);
-    if (my_ch < n_chunks) atomicMin(&slot[my_ch], tid);
+    if (my_ch < n_chunks) {
+      atomicMin(&slot[my_ch], tid);
+      routes[reinterpret_cast<const uint16_t*>(smem + kGExp)[my_ch]] = 1;
+    }
+  }
+  // the loader wave asks early whether every workgroup's plan share is out (the answer is
+  // read after the placement below)
+  uint32_t pf[4] = {0u, 0u, 0u, 0u};
+  if (wave == kGStream) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < nwg) pf[i] = ld_dev_u32(a.pflags + lane + 64 * i);
   }
   __syncthreads();
   // every route of a needed chunk, at its rank: its position among its expert's routes in
   // token order (the token bits below it)
+  auto needed = [&](int e) { return e >= 0 && e < E && routes[e] != 0; };  // a chunk of e is needed here
   auto place = [&](int r, int e) {
-    if (e < 0 || e >= E) return;
-    const int t = r / K, tw = t >> 5;
+    const int t = token(r), tw = t >> 5;
     int rank = __popc(masks[tw * E + e] & ((1u << (t & 31)) - 1u));
     for (int wd = 0; wd < tw; ++wd) rank += __popc(masks[wd * E + e]);
     const int sl = slot[chunk0[e] + rank / kChunkCols];
     if (sl < kGItems + kGSeqMax) rows[sl * kChunkCols + rank % kChunkCols] = static_cast<uint16_t>(r);
   };
+  // a lane's held routes that are needed, then one of them per pass: the wave makes as
+  // many passes as its busiest lane has such routes (few: a workgroup needs the chunks of
+  // a handful of experts), not one per held route
+  uint32_t todo = 0;
 #pragma unroll
   for (int h = 0; h < kHeld; ++h)
-    if (tid + h * kGWG < U) place(tid + h * kGWG, ev[h]);
-  for (int r = tid + kHeld * kGWG; r < U; r += kGWG) place(r, a.ids[r]);
+    if (tid + h * kGWG < U && needed(ev[h])) todo |= 1u << h;
+#pragma unroll 1
+  while (__any(todo != 0)) {
+    if (todo != 0) {
+      const int hn = __ffs(todo) - 1;
+      todo &= todo - 1u;
+      int e = 0;
+#pragma unroll
+      for (int h = 0; h < kHeld; ++h) e = h == hn ? ev[h] : e;
+      place(tid + hn * kGWG, e);
+    }
+  }
+  for (int r = tid + kHeld * kGWG; r < U; r += kGWG) {
+    const int e = a.ids[r];
+    if (needed(e)) place(r, e);
+  }
   __syncthreads();
   // row k of the tables: the row of thread k's chunk, shared through LDS
   int* kch = reinterpret_cast<int*>(rows + (kGItems + kGSeqMax) * kChunkCols);  // [kGItems + kGSeqMax]
@@ -4007,6 +4041,12 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
     const uint16_t v = row >= 0 ? rows[row * kChunkCols + cl] : static_cast<uint16_t>(0xffff);
     if (k < n1) reinterpret_cast<uint16_t*>(smem + kGTok)[idx] = v;
     else reinterpret_cast<uint16_t*>(smem + kGPairs)[idx - n1 * kChunkCols] = v;
+  }
+  if (wave == kGStream) {
+    bool ok = nwg <= 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok = ok && (lane + 64 * i >= nwg || pf[i] == call);
+    x_early = __all(ok);
   }
   __syncthreads();
   return n_chunks;
@@ -4029,10 +4069,11 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
   // the one-launch form makes them, and its share of the plan, itself
   if (tid < static_cast<int>(kGWords / 4)) sw[tid] = 0u;
   int n_chunks = 0;
+  bool x_early = false;  // the one-launch form's loader: every plan share was out already
   if constexpr (FUSED) {
     if (tid == 0) sw[kGCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
     __syncthreads();
-    n_chunks = g_fused_prologue(a, a.o_ring, sw[kGCall / 4]);
+    n_chunks = g_fused_prologue(a, a.o_ring, sw[kGCall / 4], x_early);
   } else {
     n_chunks = a.hdr[4];
     for (int ch = tid; ch < a.max_chunks && ch < kGChunks; ch += kGWG)
@@ -4194,7 +4235,7 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
     // acquire (the L2 and L1 drop what they held of the plan's lines) before the streaming
     // waves read x
 #pragma unroll 1
-    for (uint32_t spins = 0;; ++spins) {
+    for (uint32_t spins = 0; !x_early; ++spins) {
       bool ok = true;
       for (int i = l; i < nwg; i += 64) ok = ok && ld_dev_u32(a.pflags + i) == call;
       if (__all(ok)) break;
