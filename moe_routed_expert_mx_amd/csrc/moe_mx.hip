@@ -379,6 +379,10 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
   for (int i = tid; i < E; i += kGroupThreads) routes[i] = 0;
   if (tid == 0) flags = 0;
   __syncthreads();
+  // the token of route r, r / K, as a multiply-high: exact, since the error of kinv is
+  // below 2^-32 K and r < 2^16
+  const uint64_t kinv = (uint64_t{1} << 32) / static_cast<uint64_t>(K) + 1u;
+  auto token = [&](int r) { return static_cast<int>((static_cast<uint64_t>(r) * kinv) >> 32); };
   int bad = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -388,7 +392,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
       if (e < 0 || e >= E) {
         bad = 1;
       } else {
-        const int t = r / K;
+        const int t = token(r);
         atomicOr(&masks[(t >> 5) * E + e], 1u << (t & 31));
         atomicAdd(&routes[e], 1);
       }
@@ -400,7 +404,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
       bad = 1;
       continue;
     }
-    const int t = r / K;
+    const int t = token(r);
     atomicOr(&masks[(t >> 5) * E + e], 1u << (t & 31));
     atomicAdd(&routes[e], 1);
   }
@@ -485,7 +489,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
   // among its expert's routes in token order
   auto place = [&](int r, int e) {
     if (e < 0 || e >= E) return;
-    const int t = r / K, tw = t >> 5;
+    const int t = token(r), tw = t >> 5;
     int rank = __popc(masks[tw * E + e] & ((1u << (t & 31)) - 1u));
     for (int w = 0; w < tw; ++w) rank += __popc(masks[w * E + e]);
     tbl.unit_rows[(unit0[e] + (rank >> 3)) * 8 + (rank & 7)] = r;
