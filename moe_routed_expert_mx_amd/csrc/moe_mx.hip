@@ -3504,19 +3504,33 @@ __device__ __forceinline__ int lds_u16(uint32_t addr) {
 }
 
 // FC1 item i -> (chunk, hidden block).  The HB items of a chunk get indices congruent mod
-// 8 (in the chunk groups of eight; the last, partial group is interleaved), so that with
-// item i dealt to workgroup i mod grid they run on workgroups of one XCD (workgroup c runs
-// on XCD c mod 8).
+// 8, so that with item i dealt to workgroup i mod grid they run on workgroups of one XCD
+// (workgroup c runs on XCD c mod 8) and its x rows and hidden stay in one L2.  Chunks go
+// in groups of 8 kGRun: residue class r takes the kGRun consecutive chunks kGRun r ..,
+// and a block's items of those chunks are 8 apart, so they run at the same time.  An
+// expert's chunks are consecutive, so the chunks of an expert with more than 32 routes
+// mostly stream the same weights on one XCD at once, the second read served by L2.  The
+// chunks left over form groups of eight (one chunk per class); the last, partial group
+// is interleaved.
+constexpr int kGRun = 4;
 __host__ __device__ inline void g_item(int i, int n_chunks, int HB, int& ch, int& j) {
-  const int full = (n_chunks >> 3) * 8 * HB;
-  if (i < full) {
-    const int g = i / (8 * HB), r = i - g * 8 * HB;
+  const int span = 8 * kGRun;
+  const int big = n_chunks / span * span;          // chunks in groups of 8 kGRun
+  const int small = (n_chunks - big) / 8 * 8;      // then in groups of eight
+  const int i_big = big * HB, i_small = i_big + small * HB;
+  if (i < i_big) {
+    const int g = i / (span * HB), r = i - g * span * HB;
+    const int t = r >> 3;  // r = 8 (kGRun j + s) + class
+    j = t / kGRun;
+    ch = span * g + kGRun * (r & 7) + (t - j * kGRun);
+  } else if (i < i_small) {
+    const int i1 = i - i_big, g = i1 / (8 * HB), r = i1 - g * 8 * HB;
     j = r >> 3;
-    ch = 8 * g + (r & 7);
+    ch = big + 8 * g + (r & 7);
   } else {
-    const int rem = n_chunks & 7, i2 = i - full;
+    const int rem = n_chunks - big - small, i2 = i - i_small;
     j = i2 / rem;
-    ch = (n_chunks & ~7) + (i2 - j * rem);
+    ch = big + small + (i2 - j * rem);
   }
 }
 

@@ -82,6 +82,25 @@ def test_grouped_items_of_a_chunk_share_an_xcd(m):
         assert all(len(v) == 1 for v in xcd.values()), (G, grid, D, I)
 
 
+def test_grouped_consecutive_chunks_stream_together(m):
+    """Grouped form: in the groups of 32 chunks, four consecutive chunks share an XCD and
+    a hidden block's items of those chunks lie within 24 of each other (the same round of
+    items at a grid of 256), so an expert cut into two chunks mostly reads its weights
+    once per XCD at the same time."""
+    for G, (D, I) in itertools.product([32, 64, 170, 300], [(3584, 256), (3584, 384)]):
+        HB = I // 32
+        _, items = m.moe_work_split(1, G, D, I, 256)
+        where = {}
+        for i, (ch, j) in enumerate(items.tolist()):
+            where[(ch, j)] = i
+        big = G // 32 * 32
+        for ch in range(0, big, 4):
+            for j in range(HB):
+                idx = [where[(c, j)] for c in range(ch, ch + 4)]
+                assert len({x % 8 for x in idx}) == 1, (G, ch, j)
+                assert max(idx) - min(idx) <= 24, (G, ch, j)
+
+
 def test_split_rejects_bad_arguments(m):
     L = m._lib.lib
     buf = np.zeros((4, 6), np.int32)
