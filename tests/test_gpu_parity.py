@@ -483,6 +483,23 @@ def test_grouped_one_launch_small_shapes(lib, case, grid):
     _check_all(d, got, hc, hs, _oracle(d), what=f"one_launch/{name}/{grid}")
 
 
+@pytest.mark.parametrize("routing", ["uniform", "zipf"])
+def test_grouped_one_launch_many_routes(lib, routing):
+    """8800 routes (B = 1100, top-8): more than the one-launch prologue holds in registers
+    (4608 routes: the rest are read again in its loops) and more than moe_group holds
+    (8192); the one-launch rows and hidden bit for bit those of the three-call form, and
+    both against the oracle."""
+    log(f"grouped one launch many routes {routing}")
+    d = workloads.generate(workloads.custom("many", B=1100, E=64, K=8, D=512, I=128, routing=routing, seed=5))
+    layer = _layer(lib, d)
+    got, hc, hs, plan, st = _one_launch(lib, layer, d)
+    assert st == 0
+    _check_plan(d, plan)
+    ref, hcr, hsr = _run(layer, d, path="grouped")
+    assert np.array_equal(got, ref) and np.array_equal(hc, hcr) and np.array_equal(hs, hsr)
+    _check_all(d, got, hc, hs, _oracle(d), what=f"one_launch/many/{routing}")
+
+
 def test_everybody_on_one_expert(lib):
     """All 200 tokens route to the same 2 experts: 13 column tiles per expert, looped
     over in weight passes of 4."""
