@@ -4007,14 +4007,6 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
       routes[reinterpret_cast<const uint16_t*>(smem + kGExp)[my_ch]] = 1;
     }
   }
-  // the loader wave asks early whether every workgroup's plan share is out (the answer is
-  // read after the placement below)
-  uint32_t pf[4] = {0u, 0u, 0u, 0u};
-  if (wave == kGStream) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < nwg) pf[i] = ld_dev_u32(a.pflags + lane + 64 * i);
-  }
   __syncthreads();
   // every route of a needed chunk, at its rank: its position among its expert's routes in
   // token order (the token bits below it)
@@ -4033,6 +4025,16 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
 #pragma unroll
   for (int h = 0; h < kHeld; ++h)
     if (tid + h * kGWG < U && needed(ev[h])) todo |= 1u << h;
+  // the loader wave asks early whether every workgroup's plan share is out; the answer is
+  // read after the placement.  The held routes pass through an empty asm first, so that
+  // no later use of them waits for a load (a wait for them would also wait for these).
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h) asm volatile("" : "+v"(ev[h]));
+  uint32_t pf[4] = {0u, 0u, 0u, 0u};
+  if (wave == kGStream) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pf[i] = ld_dev_u32(a.pflags + min(lane + 64 * i, nwg - 1));  // no branch
+  }
 #pragma unroll 1
   while (__any(todo != 0)) {
     if (todo != 0) {
