@@ -3912,18 +3912,7 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
   int ev[kHeld];
 #pragma unroll
   for (int h = 0; h < kHeld; ++h) ev[h] = tid + h * kGWG < U ? a.ids[tid + h * kGWG] : -1;
-  // (1) the plan share: 32-element blocks [c nb / grid, (c + 1) nb / grid)
-  {
-    const int64_t nb = static_cast<int64_t>(a.B) * a.D / 32;
-    const int64_t b0 = nb * c / nwg, b1 = nb * (c + 1) / nwg;
-    uint8_t* codes = const_cast<uint8_t*>(a.plan);
-    for (int64_t idx4 = 4 * b0 + tid; idx4 < 4 * b1; idx4 += kGWG)
-      plan_quarter_dev(a.x, idx4, codes, codes + static_cast<int64_t>(a.B) * a.D);
-    wait_stores();  // every lane's device-coherent stores are done ...
-    __syncthreads();
-    if (tid == 0) st_dev_u32(a.pflags + c, call);  // ... before the share's flag
-  }
-  // (2) the chunk table
+  // (2) the chunk table's LDS, set up while the loads are in flight
   uint32_t* masks = reinterpret_cast<uint32_t*>(smem + scr);  // [W][E]
   int* routes = reinterpret_cast<int*>(masks + W * E);        // [E] route counts, then token counts
   int* chunk0 = routes + E;                                   // [E] first chunk
@@ -3934,6 +3923,16 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
   for (int i = tid; i < kGChunks; i += kGWG) slot[i] = 0x7fffffff;
   for (int i = tid; i < (kGItems + kGSeqMax) * kChunkCols; i += kGWG) rows[i] = 0xffff;
   if (tid == 0) s_flags = 0;
+  // (1) the plan share: 32-element blocks [c nb / grid, (c + 1) nb / grid); its
+  // device-coherent stores drain while the routes are marked, and the share's flag goes
+  // out after that
+  {
+    const int64_t nb = static_cast<int64_t>(a.B) * a.D / 32;
+    const int64_t b0 = nb * c / nwg, b1 = nb * (c + 1) / nwg;
+    uint8_t* codes = const_cast<uint8_t*>(a.plan);
+    for (int64_t idx4 = 4 * b0 + tid; idx4 < 4 * b1; idx4 += kGWG)
+      plan_quarter_dev(a.x, idx4, codes, codes + static_cast<int64_t>(a.B) * a.D);
+  }
   __syncthreads();
   int bad = 0;
   // the token of route r, r / K, as a multiply-high: exact, since the error of kinv is
@@ -3954,7 +3953,9 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
     if (tid + h * kGWG < U) mark(tid + h * kGWG, ev[h]);
   for (int r = tid + kHeld * kGWG; r < U; r += kGWG) mark(r, a.ids[r]);
   if (bad) atomicOr(&s_flags, 1);
+  wait_stores();  // every lane's device-coherent plan stores are done ...
   __syncthreads();
+  if (tid == 0) st_dev_u32(a.pflags + c, call);  // ... before the share's flag
   // thread i holds experts 2i and 2i + 1: their token counts and chunk counts, scanned
   int cnt[2], nch[2];
 #pragma unroll
