@@ -179,9 +179,9 @@ __device__ __forceinline__ void plan_quarter(const uint8_t* __restrict__ x, int6
 
 // plan_quarter with device-coherent stores (sc1: written through to memory, so that other
 // workgroups of the same launch read them after an acquire; no L2 write-back needed).
-__device__ __forceinline__ void plan_quarter_dev(const uint8_t* __restrict__ x, int64_t idx4, uint8_t* __restrict__ codes,
-                                                 uint8_t* __restrict__ scales) {
-  const uint4 q = ld16(x + idx4 * 16);
+// From the quarter's 16 bytes of x, already loaded.
+__device__ __forceinline__ void plan_quarter_dev_v(const uint4 q, int64_t idx4, uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   float v[8];
   float amax = 0.0f;
@@ -204,6 +204,10 @@ __device__ __forceinline__ void plan_quarter_dev(const uint8_t* __restrict__ x, 
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if ((idx4 & 3) == 0)
     __hip_atomic_store(scales + (idx4 >> 2), static_cast<uint8_t>(e + 127), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void plan_quarter_dev(const uint8_t* __restrict__ x, int64_t idx4, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales) {
+  plan_quarter_dev_v(ld16(x + idx4 * 16), idx4, codes, scales);
 }
 
 __global__ __launch_bounds__(256) void plan_kernel(const uint8_t* __restrict__ x, int64_t nblocks,
@@ -3912,6 +3916,12 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
   int ev[kHeld];
 #pragma unroll
   for (int h = 0; h < kHeld; ++h) ev[h] = tid + h * kGWG < U ? a.ids[tid + h * kGWG] : -1;
+  // the plan share: 32-element blocks [c nb / grid, (c + 1) nb / grid), four lanes per
+  // block; the first quarter of each lane is requested with the routes
+  const int64_t nb = static_cast<int64_t>(a.B) * a.D / 32;
+  const int64_t b0 = nb * c / nwg, b1 = nb * (c + 1) / nwg, q0 = 4 * b0 + tid;
+  uint4 xq = ld16(a.x + (q0 < 4 * b1 ? q0 : 0) * 16);  // unconditional: no select waits for it
+  compiler_fence();  // the load stays ahead of the LDS set-up below
   // (2) the chunk table's LDS, set up while the loads are in flight
   uint32_t* masks = reinterpret_cast<uint32_t*>(smem + scr);  // [W][E]
   int* routes = reinterpret_cast<int*>(masks + W * E);        // [E] route counts, then token counts
@@ -3923,15 +3933,18 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
   for (int i = tid; i < kGChunks; i += kGWG) slot[i] = 0x7fffffff;
   for (int i = tid; i < (kGItems + kGSeqMax) * kChunkCols; i += kGWG) rows[i] = 0xffff;
   if (tid == 0) s_flags = 0;
-  // (1) the plan share: 32-element blocks [c nb / grid, (c + 1) nb / grid); its
-  // device-coherent stores drain while the routes are marked, and the share's flag goes
-  // out after that
+  // (1) the plan share.  The held routes and the first x quarter pass through an empty
+  // asm first: one wait for all of them, before any store, so that no later use of the
+  // routes waits for the plan's stores, which drain while the routes are marked (the
+  // share's flag goes out after that)
+#pragma unroll
+  for (int h = 0; h < kHeld; ++h) asm volatile("" : "+v"(ev[h]));
+  asm volatile("" : "+v"(xq.x), "+v"(xq.y), "+v"(xq.z), "+v"(xq.w));
   {
-    const int64_t nb = static_cast<int64_t>(a.B) * a.D / 32;
-    const int64_t b0 = nb * c / nwg, b1 = nb * (c + 1) / nwg;
     uint8_t* codes = const_cast<uint8_t*>(a.plan);
-    for (int64_t idx4 = 4 * b0 + tid; idx4 < 4 * b1; idx4 += kGWG)
-      plan_quarter_dev(a.x, idx4, codes, codes + static_cast<int64_t>(a.B) * a.D);
+    uint8_t* scales = codes + static_cast<int64_t>(a.B) * a.D;
+    if (q0 < 4 * b1) plan_quarter_dev_v(xq, q0, codes, scales);
+    for (int64_t idx4 = q0 + kGWG; idx4 < 4 * b1; idx4 += kGWG) plan_quarter_dev(a.x, idx4, codes, scales);
   }
   __syncthreads();
   int bad = 0;
