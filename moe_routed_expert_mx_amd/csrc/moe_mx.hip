@@ -3492,6 +3492,7 @@ struct GArgs {
   uint8_t* dump_codes;      // optional [B*K, I]
   uint8_t* dump_scales;     // optional [B*K, I/32]
   int B, K, D, I, HB, NS1, IP, floor_rule, max_chunks;
+  uint64_t kinv;            // floor(2^32 / K) + 1: the token of pair p is (p kinv) >> 32, exactly (p < 2^16)
   uint32_t plan_bytes;      // bytes of the plan (x codes, then x scales)
   uint32_t out_bytes;       // bytes of the output rows
   uint32_t colb;            // bytes of one hidden column (IP + 16)
@@ -3632,10 +3633,11 @@ __device__ __forceinline__ void g_xoffsets(const GArgs& a, uint32_t lb, int wi, 
     const int col = 8 * i + (l >> 3);
     const int pr = lds_u16(tb + 2 * col);
     const int part = (l & 7) ^ (col & 7);
-    xo[i] = pr == 0xffff ? kOutside : static_cast<uint32_t>(pr / a.K * a.D + 16 * part);
+    const int t = static_cast<int>((static_cast<uint64_t>(pr) * a.kinv) >> 32);  // pr / K
+    xo[i] = pr == 0xffff ? kOutside : static_cast<uint32_t>(t * a.D + 16 * part);
   }
   const int ps = l < kChunkCols ? lds_u16(tb + 2 * l) : 0xffff;
-  const int ts = ps == 0xffff ? 0xffff : ps / a.K;
+  const int ts = ps == 0xffff ? 0xffff : static_cast<int>((static_cast<uint64_t>(ps) * a.kinv) >> 32);
   x0 = xo[0];
   x1 = xo[1];
   x2 = xo[2];
@@ -3950,7 +3952,7 @@ __device__ __forceinline__ int g_fused_prologue(const GArgs& a, uint32_t scr, ui
   int bad = 0;
   // the token of route r, r / K, as a multiply-high: exact, since the error of kinv is
   // below 2^-32 K and r < 2^16
-  const uint64_t kinv = (uint64_t{1} << 32) / static_cast<uint64_t>(K) + 1u;
+  const uint64_t kinv = a.kinv;
   auto token = [&](int r) { return static_cast<int>((static_cast<uint64_t>(r) * kinv) >> 32); };
   auto mark = [&](int r, int e) {
     if (e < 0 || e >= E) {
@@ -4715,6 +4717,7 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   a.dump_scales = static_cast<uint8_t*>(o.hidden_scales_dev);
   a.B = B;
   a.K = topk;
+  a.kinv = (uint64_t{1} << 32) / static_cast<uint64_t>(topk) + 1u;
   a.D = D;
   a.I = I;
   a.HB = HB;
