@@ -89,7 +89,8 @@ size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32
  * 512); form 1: the grouped form, `groups` chunks of up to 32 routes of one expert (<=
  * 1024).  An FC1 item is one 32-wide hidden block of one group; there are groups * I/32
  * of them, and item i goes to workgroup i mod grid.  FC2 tiles are the 16-row output
- * tiles, groups * D/16 of them in group-major order.  claims_ring: 0, or (form 0) the
+ * tiles, groups * D/16 of them in group-major order, in equal runs (the grouped form's
+ * three-call launch balances its runs on bytes instead: moe_grouped_runs).  claims_ring: 0, or (form 0) the
  * slots per wave (2..4) of a launch with FC2 tail claims, whose zones it then reports.
  * Outputs are host pointers:
  *   split i32 [grid, 6]: per workgroup {FC1 items, first FC2 tile, FC2 tiles, streaming
@@ -98,6 +99,21 @@ size_t moe_workspace_bytes(int32_t E, int32_t D, int32_t I, int32_t B_max, int32
  * MOE_EINVAL for a bad form, shape, group count, grid (1..2048) or claims_ring. */
 int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t grid, int32_t claims_ring,
                    int32_t* split, int32_t* items);
+
+/* The FC2 runs of the grouped form as moe_experts_run's three-call form sets them (no
+ * device call).  The experts page gives each CTA a contiguous share of the FC2 stream
+ * (ExpertsKernel.partition); here the shares are balanced on the bytes a 16-row tile
+ * moves rather than on tile counts: its FP4 weights and scales, 16 (I/2 + I/32) bytes,
+ * and its BF16 output rows, 32 bytes per live column of its chunk.  Run c starts at the
+ * first tile whose cost-so-far reaches floor(W c / grid), W the total.  The one-launch
+ * form (moe_decode_run, B > 8) keeps equal tile counts (moe_work_split, form 1).
+ * chunk_cols: host i32 [chunks], the live columns of each chunk (1..32, chunks of one
+ * expert consecutive, as moe_group orders them); runs: host i32 [grid, 2], per
+ * workgroup {first FC2 tile, FC2 tiles}.  MOE_EINVAL for chunks outside 0..1024, a count
+ * outside 1..32 or more than 65536 columns in all, an unsupported shape or I > 384, a
+ * grid outside 1..2048, or a NULL pointer. */
+int moe_grouped_runs(int32_t chunks, const int32_t* chunk_cols, int32_t D, int32_t I, int32_t grid,
+                     int32_t* runs);
 
 /* Bytes of the four packed weight buffers written by moe_pack_weights (experts page,
  * ExpertsKernel.schedule / produce: the weights stream tile by tile, 128 K at a time).

@@ -86,6 +86,7 @@ def _load():
                                              c.c_int32, P, c.c_size_t, P]),
         "moe_combine": (c.c_int, [P, c.c_size_t, P, c.c_int32, c.c_int32, c.c_int32, P, c.c_size_t, P]),
         "moe_work_split": (c.c_int, [c.c_int32] * 6 + [P, P]),
+        "moe_grouped_runs": (c.c_int, [c.c_int32, P, c.c_int32, c.c_int32, c.c_int32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -96,7 +97,8 @@ def _load():
 lib = _load()
 EXPORTED = ("moe_status_string", "moe_plan_bytes", "moe_units_bytes", "moe_workspace_bytes", "moe_packed_weight_bytes",
             "moe_pack_weights", "moe_workspace_init", "moe_plan", "moe_group", "moe_plan_group", "moe_units_export",
-            "moe_experts_run", "moe_decode_run", "moe_decode_run_noalloc", "moe_combine", "moe_work_split")
+            "moe_experts_run", "moe_decode_run", "moe_decode_run_noalloc", "moe_combine", "moe_work_split",
+            "moe_grouped_runs")
 
 
 def status_string(status: int) -> str:
@@ -151,6 +153,17 @@ def moe_work_split(form: int, groups: int, D: int, I: int, grid: int, claims_rin
     _check("moe_work_split", lib.moe_work_split(form, groups, D, I, grid, claims_ring, split.ctypes.data,
                                                 items.ctypes.data))
     return split, items[:groups * (I // 32)]
+
+
+def moe_grouped_runs(chunk_cols, D: int, I: int, grid: int):
+    """Host-side FC2 runs of the grouped form's three-call launch: [grid, 2] int32
+    {first tile, tiles} from the chunks' live column counts (no device call)."""
+    import numpy as np
+    cols = np.ascontiguousarray(chunk_cols, dtype=np.int32)
+    runs = np.zeros((grid, 2), np.int32)
+    _check("moe_grouped_runs", lib.moe_grouped_runs(len(cols), cols.ctypes.data if len(cols) else None, D, I, grid,
+                                                    runs.ctypes.data))
+    return runs
 
 
 def moe_pack_weights(E, D, I, w13, s13, w2, s2, w13p, s13p, w2p, s2p, stream=None):

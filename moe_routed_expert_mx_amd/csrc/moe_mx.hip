@@ -263,7 +263,8 @@ struct Table {
   // chunks of the grouped kernel: each expert's routes, in token order, cut into runs of
   // kChunkCols token columns (one weight pass of that expert each)
   int32_t* c_expert;     // [C]
-  int32_t* c_ncols;      // [C] real columns (1..kChunkCols)
+  int32_t* c_cols;       // [C] real columns of the chunks before | real columns (1..kChunkCols) << 20
+                         // (hdr[5]: the real columns of all chunks)
   int32_t* c_pairs;      // [C, kChunkCols] pair indices t*K + s, -1 where padded
 };
 constexpr int kChunkCols = 32;  // token columns per chunk: two 16-column MFMA tiles
@@ -271,7 +272,7 @@ constexpr int kChunkCols = 32;  // token columns per chunk: two 16-column MFMA t
 constexpr size_t align256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
 struct UnitsLayout {
-  size_t hdr, unit_expert, unit_rows, g_expert, g_unit0, g_nunits, g_tile0, c_expert, c_ncols, c_pairs, end;
+  size_t hdr, unit_expert, unit_rows, g_expert, g_unit0, g_nunits, g_tile0, c_expert, c_cols, c_pairs, end;
   int64_t max_chunks;
 };
 
@@ -301,7 +302,7 @@ UnitsLayout units_layout(int B, int K, int E) {
   off += G * 4;
   L.c_expert = align256(off);
   off = L.c_expert + L.max_chunks * 4;
-  L.c_ncols = off;
+  L.c_cols = off;
   off += L.max_chunks * 4;
   L.c_pairs = align256(off);
   off = L.c_pairs + L.max_chunks * kChunkCols * 4;
@@ -319,7 +320,7 @@ Table table_at(uint8_t* base, const UnitsLayout& L) {
   t.g_nunits = reinterpret_cast<int32_t*>(base + L.g_nunits);
   t.g_tile0 = reinterpret_cast<int32_t*>(base + L.g_tile0);
   t.c_expert = reinterpret_cast<int32_t*>(base + L.c_expert);
-  t.c_ncols = reinterpret_cast<int32_t*>(base + L.c_ncols);
+  t.c_cols = reinterpret_cast<int32_t*>(base + L.c_cols);
   t.c_pairs = reinterpret_cast<int32_t*>(base + L.c_pairs);
   return t;
 }
@@ -376,8 +377,8 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
   int* unit0 = routes + E;                                                   // [E]
   int* chunk0 = unit0 + E;                                                   // [E]
   int* ncols = chunk0 + E;                                                   // [chunks]
-  __shared__ uint32_t wsum[2][kGroupThreads / 64];
-  __shared__ uint32_t s_tot[2];
+  __shared__ uint32_t wsum[3][kGroupThreads / 64];
+  __shared__ uint32_t s_tot[3];
   __shared__ int flags, s_c_lo, s_c_hi;
   for (int i = tid; i < E * W; i += kGroupThreads) masks[i] = 0;
   for (int i = tid; i < E; i += kGroupThreads) routes[i] = 0;
@@ -420,7 +421,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
   // carries into the next)
   const int ew = (E + 63) >> 6;
   int cnt = 0, units = 0, chunks = 0, grp = 0, tiles = 0;
-  uint32_t s0 = 0, s1 = 0;
+  uint32_t s0 = 0, s1 = 0, s2 = 0;
   if (wave < ew) {
     if (tid < E) {
       int c0 = 0, c1 = 0, c2 = 0, c3 = 0, w = 0;
@@ -440,9 +441,11 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
     tiles = (units + 1) >> 1;
     s0 = wave_scan_u32(static_cast<uint32_t>(units) | (static_cast<uint32_t>(grp) << 16));
     s1 = wave_scan_u32(static_cast<uint32_t>(tiles) | (static_cast<uint32_t>(chunks) << 16));
+    s2 = wave_scan_u32(static_cast<uint32_t>(cnt));
     if (lane == 63) {
       wsum[0][wave] = s0;
       wsum[1][wave] = s1;
+      wsum[2][wave] = s2;
     }
   }
   __syncthreads();
@@ -450,6 +453,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
     for (int w = 0; w < wave; ++w) {
       s0 += wsum[0][w];
       s1 += wsum[1][w];
+      s2 += wsum[2][w];
     }
     const int iu = static_cast<int>(s0 & 0xffffu), ig = static_cast<int>(s0 >> 16);
     const int it = static_cast<int>(s1 & 0xffffu), ic = static_cast<int>(s1 >> 16);
@@ -461,6 +465,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
     if (tid == E - 1) {
       s_tot[0] = s0;
       s_tot[1] = s1;
+      s_tot[2] = s2;
     }
     if (tid == lo) s_c_lo = c0;
     if (tid == hi - 1) s_c_hi = ic;
@@ -469,7 +474,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
         const int nc = cnt - q * kChunkCols < kChunkCols ? cnt - q * kChunkCols : kChunkCols;
         ncols[c0 + q] = nc;
         tbl.c_expert[c0 + q] = tid;
-        tbl.c_ncols[c0 + q] = nc;
+        tbl.c_cols[c0 + q] = (static_cast<int>(s2) - cnt + q * kChunkCols) | (nc << 20);
       }
       if (cnt > 0) {
         tbl.g_expert[gi] = tid;
@@ -488,6 +493,7 @@ __device__ __forceinline__ void group_body(const int32_t* __restrict__ ids, int 
     tbl.hdr[2] = static_cast<int>(s_tot[1] & 0xffffu);
     tbl.hdr[3] = flags;
     tbl.hdr[4] = static_cast<int>(s_tot[1] >> 16);
+    tbl.hdr[5] = static_cast<int>(s_tot[2]);
   }
   // unit-row and chunk entries of the routes [r_lo, r_hi): rank = the route's position
   // among its expert's routes in token order
@@ -3468,7 +3474,9 @@ constexpr uint32_t kGProg2 = 64;   // [kGStream] wave w is done with every FC2 c
 constexpr uint32_t kGReady = 96;   // FC2 chunk sequences loaded into the hidden buffer
 constexpr uint32_t kGCall = 100;   // this call's number
 constexpr uint32_t kGXReady = 104; // the one-launch form: every workgroup's share of the plan is out
-constexpr uint32_t kGWords = 128;  // bytes of the words above (cleared at the start)
+constexpr uint32_t kGWords = 120;  // bytes of the words above (cleared at the start)
+constexpr uint32_t kGRun0 = 120;   // the three-call form: first FC2 tile of this run, posted by
+constexpr uint32_t kGRun1 = 124;   // the chunk's thread before the first barrier; of the next run
 constexpr uint32_t kGExp = 128;    // [kGChunks] u16 expert of chunk ch
 constexpr uint32_t kGTok = kGExp + 2 * kGChunks;  // [kGItems][32] u16 pair t*K+s of item k's column (0xffff: padded)
 constexpr int kGSeqMax = 8;        // chunks of a workgroup's FC2 run (the one-launch form)
@@ -3483,6 +3491,7 @@ struct GArgs {
   const uint8_t* plan;      // x codes [B, D], then scales [B, D/32]
   const int32_t* hdr;       // unit table header (n_chunks at [4])
   const int32_t* c_expert;  // [max_chunks]
+  const int32_t* c_cols;    // [max_chunks] live columns before the chunk | its live columns << 20
   const int32_t* c_pairs;   // [max_chunks][32]
   uint16_t* out;            // BF16 [B*K, D]
   uint8_t* hid;             // [max_chunks][32 columns][IP + 16]: IP code bytes, then HB scales
@@ -3554,6 +3563,46 @@ __host__ __device__ inline QWork g_work(int n_chunks, int HB, int NS1, int D, in
   q.first2 = c * cap < N2 ? c * cap : N2;
   q.n2 = N2 - q.first2 < cap ? N2 - q.first2 : cap;
   return q;
+}
+
+// FC2 runs balanced on the bytes a tile moves (the three-call form, whose unit table
+// lists each chunk's live columns and the live columns before it): its weights, 16 rows x
+// (I/2 + I/32) bytes, and its output rows, 16 x 2 bytes per live column.  In units of 16
+// bytes a tile of chunk ch costs u = 17 I / 32 + 2 n_ch, and the chunks before ch cost
+// S(ch) = TPE (17 I / 32 ch + 2 P(ch)), P(ch) = the live columns before ch.  Workgroup c's
+// run starts at the first tile whose start S(ch) + o u is at least floor(W c / grid), W =
+// S(n_chunks), so the runs are contiguous, in chunk order, and cover every tile once.
+// W < 2^31 for every shape the grouped kernel takes (TPE <= 1024, I <= 384, <= 1024
+// chunks, <= 65536 columns), so all of it is 32-bit.
+__host__ __device__ inline uint32_t g_cost_before(int ch, int prefix_cols, int TPE, int I) {
+  return static_cast<uint32_t>(TPE) * (static_cast<uint32_t>(17 * I / 32) * ch + 2u * prefix_cols);
+}
+__host__ __device__ inline uint32_t g_run_target(uint32_t W, int t, int nwg) {
+  const uint32_t q = W / nwg, r = W - q * nwg;
+  return q * t + r * t / nwg;  // floor(W t / nwg), r t < 2^16
+}
+// The run start for target `tgt` in chunk ch (S(ch) <= tgt < S(ch + 1)).
+__host__ __device__ inline int g_run_start(uint32_t tgt, uint32_t s_lo, int ncols, int ch, int TPE, int I) {
+  const uint32_t u = 17u * I / 32u + 2u * ncols;
+  return ch * TPE + static_cast<int>((tgt - s_lo + u - 1u) / u);
+}
+// Host form (schedule checks): the run of workgroup c from the chunks' live columns.
+inline void g_run_host(const int32_t* ncols, int n_chunks, int D, int I, int nwg, int c, int& first, int& n2) {
+  const int TPE = D / 16;
+  int P = 0;
+  for (int ch = 0; ch < n_chunks; ++ch) P += ncols[ch];
+  const uint32_t W = g_cost_before(n_chunks, P, TPE, I);
+  int t0 = 0, t1 = n_chunks * TPE;
+  int pre = 0;
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const uint32_t lo = g_cost_before(ch, pre, TPE, I), hi = g_cost_before(ch + 1, pre + ncols[ch], TPE, I);
+    const uint32_t tg0 = g_run_target(W, c, nwg), tg1 = g_run_target(W, c + 1, nwg);
+    if (c > 0 && lo <= tg0 && tg0 < hi) t0 = g_run_start(tg0, lo, ncols[ch], ch, TPE, I);
+    if (c + 1 < nwg && lo <= tg1 && tg1 < hi) t1 = g_run_start(tg1, lo, ncols[ch], ch, TPE, I);
+    pre += ncols[ch];
+  }
+  first = n_chunks > 0 ? t0 : 0;
+  n2 = n_chunks > 0 ? t1 - t0 : 0;
 }
 
 // Bounded LDS wait of the streaming waves.  They wait only on words that their own
@@ -4112,21 +4161,64 @@ __global__ __launch_bounds__(kGWG) void grouped_kernel(GArgs a) {
     n_chunks = g_fused_prologue(a, a.o_ring, sw[kGCall / 4], x_early);
   } else {
     n_chunks = a.hdr[4];
-    for (int ch = tid; ch < a.max_chunks && ch < kGChunks; ch += kGWG)
-      reinterpret_cast<uint16_t*>(smem + kGExp)[ch] = static_cast<uint16_t>(a.c_expert[ch]);
     const int n1_cap = (n_chunks * HB - c + nwg - 1) / nwg;  // this workgroup's FC1 items
-    for (int idx = tid; idx < n1_cap * kChunkCols && idx < kGItems * kChunkCols; idx += kGWG) {
-      const int k = idx / kChunkCols, cl = idx - k * kChunkCols;
-      int ch, jj;
-      g_item(c + k * nwg, n_chunks, HB, ch, jj);
-      const int pr = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
-      reinterpret_cast<uint16_t*>(smem + kGTok)[idx] = static_cast<uint16_t>(pr >= 0 ? pr : 0xffff);
+    static_assert(kGChunks <= 2 * kGWG && kGItems * kChunkCols <= 2 * kGWG, "two entries a thread");
+    // loads first: two chunk records a thread, then two pair columns of the items (their
+    // addresses need the chunk count)
+    int ex[2], cc[2], pr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + i * kGWG;
+      const bool v = ch < a.max_chunks && ch < kGChunks;
+      ex[i] = v ? a.c_expert[ch] : 0;
+      cc[i] = v ? a.c_cols[ch] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + i * kGWG;
+      pr[i] = -1;
+      if (idx < n1_cap * kChunkCols && idx < kGItems * kChunkCols) {
+        const int k = idx / kChunkCols, cl = idx - k * kChunkCols;
+        int ch, jj;
+        g_item(c + k * nwg, n_chunks, HB, ch, jj);
+        pr[i] = a.c_pairs[static_cast<int64_t>(ch) * kChunkCols + cl];
+      }
+    }
+    // the byte-balanced FC2 runs (g_run_start): the thread of the chunk that holds this
+    // run's start, and the next run's, posts it
+    const int TPE = a.D / 16;
+    const uint32_t W = g_cost_before(n_chunks, a.hdr[5], TPE, a.I);
+    const uint32_t tgt0 = g_run_target(W, c, nwg), tgt1 = g_run_target(W, c + 1, nwg);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + i * kGWG;
+      const int p0 = cc[i] & 0xfffff, nc = cc[i] >> 20;
+      if (ch < n_chunks) {
+        const uint32_t lo = g_cost_before(ch, p0, TPE, a.I), hi = g_cost_before(ch + 1, p0 + nc, TPE, a.I);
+        if (lo <= tgt0 && tgt0 < hi) sw[kGRun0 / 4] = static_cast<uint32_t>(g_run_start(tgt0, lo, nc, ch, TPE, a.I));
+        if (lo <= tgt1 && tgt1 < hi) sw[kGRun1 / 4] = static_cast<uint32_t>(g_run_start(tgt1, lo, nc, ch, TPE, a.I));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ch = tid + i * kGWG, idx = tid + i * kGWG;
+      if (ch < a.max_chunks && ch < kGChunks) reinterpret_cast<uint16_t*>(smem + kGExp)[ch] = static_cast<uint16_t>(ex[i]);
+      if (idx < n1_cap * kChunkCols && idx < kGItems * kChunkCols)
+        reinterpret_cast<uint16_t*>(smem + kGTok)[idx] = static_cast<uint16_t>(pr[i] >= 0 ? pr[i] : 0xffff);
     }
     if (tid == 0) sw[kGCall / 4] = ld_dev_u32(a.calls + c) + 1u;  // stored back at the end
     __syncthreads();
   }
 
-  const QWork q = g_work(n_chunks, HB, NS1, a.D, nwg, c);
+  QWork q = g_work(n_chunks, HB, NS1, a.D, nwg, c);
+  if constexpr (!FUSED) {
+    // run c starts at tile 0 for c = 0 and the last ends at the last tile; no chunk, no run
+    const int N2 = n_chunks * q.TPE;
+    const int t0 = c == 0 ? 0 : static_cast<int>(sw[kGRun0 / 4]);
+    const int t1 = c + 1 == nwg ? N2 : static_cast<int>(sw[kGRun1 / 4]);
+    q.first2 = n_chunks > 0 ? t0 : 0;
+    q.n2 = n_chunks > 0 ? t1 - t0 : 0;
+  }
   const int g0 = q.first2 / q.TPE;  // chunk of the workgroup's first FC2 tile (sequence 0)
   const __amdgpu_buffer_rsrc_t none =
       __builtin_amdgcn_make_buffer_rsrc(static_cast<void*>(a.out), static_cast<short>(0), 0u, 0x00020000);
@@ -4705,6 +4797,7 @@ int run_grouped(const moe_weights_t* wts, const moe_run_opts_t& o, const void* p
   } else {
     a.hdr = reinterpret_cast<const int32_t*>(ub + UL.hdr);
     a.c_expert = reinterpret_cast<const int32_t*>(ub + UL.c_expert);
+    a.c_cols = reinterpret_cast<const int32_t*>(ub + UL.c_cols);
     a.c_pairs = reinterpret_cast<const int32_t*>(ub + UL.c_pairs);
   }
   a.out = static_cast<uint16_t*>(out);
@@ -5000,6 +5093,20 @@ int moe_work_split(int32_t form, int32_t groups, int32_t D, int32_t I, int32_t g
       items[2 * i + 1] = j;
     }
   }
+  return MOE_OK;
+}
+
+int moe_grouped_runs(int32_t chunks, const int32_t* chunk_cols, int32_t D, int32_t I, int32_t grid, int32_t* runs) {
+  if (chunks < 0 || chunks > kGChunks || !shape_ok(1, D, I) || I > 384 || grid < 1 || grid > kMaxGrid ||
+      runs == nullptr || (chunks > 0 && chunk_cols == nullptr))
+    return MOE_EINVAL;
+  int64_t cols = 0;
+  for (int ch = 0; ch < chunks; ++ch) {
+    if (chunk_cols[ch] < 1 || chunk_cols[ch] > kChunkCols) return MOE_EINVAL;
+    cols += chunk_cols[ch];
+  }
+  if (cols > 65536) return MOE_EINVAL;
+  for (int c = 0; c < grid; ++c) g_run_host(chunk_cols, chunks, D, I, grid, c, runs[2 * c], runs[2 * c + 1]);
   return MOE_OK;
 }
 

@@ -5,7 +5,8 @@ The split comes from the library itself (moe_work_split evaluates the kernels' o
 split functions on the host), so these tests check the code that runs, not a copy.
 
 * Cover: every FC1 item (one 32-wide hidden block of one group) goes to exactly one
-  workgroup, and the FC2 runs partition the output tiles.
+  workgroup, and the FC2 runs partition the output tiles (the grouped form's three-call
+  launch balances its runs on bytes: moe_grouped_runs, also checked for balance).
 * Protocol: each workgroup's waves are modelled as ordered lists of posts and waits on
   their workgroup's LDS words, and on global block flags, in the order the kernels take
   them (experts page, ExpertsKernel: a co-resident grid whose CTAs wait on other CTAs'
@@ -99,6 +100,94 @@ def test_grouped_consecutive_chunks_stream_together(m):
                 idx = [where[(c, j)] for c in range(ch, ch + 4)]
                 assert len({x % 8 for x in idx}) == 1, (G, ch, j)
                 assert max(idx) - min(idx) <= 24, (G, ch, j)
+
+
+# ------------------------------------------------------- grouped form: byte-balanced runs
+def _chunk_cols(rng, n, kind):
+    if kind == "full":
+        return np.full(n, 32, np.int32)
+    if kind == "zipf":  # a few experts with several full chunks, then one small chunk each
+        return np.where(rng.random(n) < 0.3, 32, rng.integers(1, 6, n)).astype(np.int32)
+    return rng.integers(1, 33, n).astype(np.int32)
+
+
+def _tile_costs(cols, D, I):
+    """Cost of each FC2 tile in 16-byte units: its weights and scales, 16 (I/2 + I/32)
+    bytes, and its BF16 output rows, 16 rows x 2 bytes per live column of its chunk."""
+    return np.repeat(17 * I // 32 + 2 * cols.astype(np.int64), D // 16)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "zipf", "full"])
+def test_grouped_runs_partition_and_balance(m, kind):
+    """The three-call grouped launch's FC2 runs: contiguous, in chunk order, covering every
+    tile once, each run's cost within one tile of the mean share."""
+    rng = np.random.default_rng({"uniform": 1, "zipf": 2, "full": 3}[kind])
+    for D, I in [(3584, 384), (3584, 256), (512, 32), (7168, 128)]:
+        for n in [0, 1, 7, 151, 169, 1024]:
+            if n * 32 > 65536 and kind == "full":
+                continue
+            cols = _chunk_cols(rng, n, kind)
+            cost = _tile_costs(cols, D, I)
+            for grid in [1, 7, 8, 256, 257]:
+                runs = m.moe_grouped_runs(cols, D, I, grid)
+                first, n2 = runs[:, 0], runs[:, 1]
+                assert (n2 >= 0).all() and n2.sum() == n * (D // 16), (D, I, n, grid)
+                assert first[0] == 0 and (first[1:] == first[:-1] + n2[:-1]).all(), (D, I, n, grid)
+                if n == 0:
+                    continue
+                S = np.concatenate([[0], np.cumsum(cost)])
+                share = S[-1] / grid
+                run_cost = S[first + n2] - S[first]
+                assert (np.abs(run_cost - share) <= cost.max() + 1).all(), (D, I, n, grid)
+                if kind == "full":  # equal tile costs: tile counts differ by at most one
+                    assert n2.max() - n2.min() <= 1
+
+
+def test_grouped_runs_balance_a_skewed_batch(m):
+    """Chunks of a Zipf-routed batch (popular experts in full chunks first, then one
+    small chunk per tail expert): equal tile counts put ~1.3x the mean bytes on the first
+    workgroups; the byte-balanced runs stay within a tile of the mean."""
+    cols = np.array([32] * 40 + [3] * 110, np.int32)
+    D, I, grid = 3584, 256, 256
+    cost = _tile_costs(cols, D, I)
+    S = np.concatenate([[0], np.cumsum(cost)])
+    runs = m.moe_grouped_runs(cols, D, I, grid)
+    bal = S[runs[:, 0] + runs[:, 1]] - S[runs[:, 0]]
+    split, _ = m.moe_work_split(1, len(cols), D, I, grid)
+    eq = S[split[:, 1] + split[:, 2]] - S[split[:, 1]]
+    assert eq.max() / eq.mean() > 1.25
+    assert bal.max() / bal.mean() < 1.02
+
+
+def test_grouped_runs_protocol_has_no_cycle(m):
+    """The grouped kernel's wait protocol with byte-balanced runs in place of equal ones."""
+    rng = np.random.default_rng(4)
+    for D, I in [(3584, 384), (512, 32)]:
+        for n in [1, 13, 65, 128]:
+            cols = _chunk_cols(rng, n, "zipf")
+            for grid in [1, 8, 33, 256]:
+                split, items = m.moe_work_split(1, n, D, I, grid)
+                split[:, 1:3] = m.moe_grouped_runs(cols, D, I, grid)
+                blocked, _, _ = _run(_grouped_actors(split, items, D, I))
+                assert not blocked, (D, I, n, grid, blocked[:4])
+
+
+def test_grouped_runs_reject_bad_arguments(m):
+    L, E = m._lib.lib, m._lib.MOE_EINVAL
+    cols = np.full(4, 8, np.int32)
+    runs = np.zeros((4, 2), np.int32)
+    ok = L.moe_grouped_runs(4, cols.ctypes.data, 3584, 384, 4, runs.ctypes.data)
+    assert ok == m._lib.MOE_OK
+    bad = np.array([8, 0, 8, 8], np.int32)
+    assert L.moe_grouped_runs(4, bad.ctypes.data, 3584, 384, 4, runs.ctypes.data) == E     # 0 columns
+    bad = np.array([8, 33, 8, 8], np.int32)
+    assert L.moe_grouped_runs(4, bad.ctypes.data, 3584, 384, 4, runs.ctypes.data) == E     # > 32 columns
+    assert L.moe_grouped_runs(1025, cols.ctypes.data, 3584, 384, 4, runs.ctypes.data) == E  # > 1024 chunks
+    assert L.moe_grouped_runs(4, cols.ctypes.data, 3584, 512, 4, runs.ctypes.data) == E    # I > 384
+    assert L.moe_grouped_runs(4, cols.ctypes.data, 3000, 384, 4, runs.ctypes.data) == E    # D % 512
+    assert L.moe_grouped_runs(4, cols.ctypes.data, 3584, 384, 0, runs.ctypes.data) == E    # grid
+    assert L.moe_grouped_runs(4, None, 3584, 384, 4, runs.ctypes.data) == E
+    assert L.moe_grouped_runs(4, cols.ctypes.data, 3584, 384, 4, None) == E
 
 
 def test_split_rejects_bad_arguments(m):
