@@ -407,6 +407,7 @@ SMALL = [
     ("many_tiles", 24, 10, 5, 1536, 160, "zipf"),
     ("one_token", 1, 8, 3, 512, 64, "uniform"),
     ("hot_expert", 70, 4, 1, 512, 128, "uniform"),   # ~17 tokens x 4 experts, K = 1
+    ("skewed", 96, 40, 2, 512, 128, "zipf"),         # full chunks of the hot experts, then 1-3 route chunks
 ]
 
 
