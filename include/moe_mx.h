@@ -166,7 +166,8 @@ int moe_plan(const void* x_dev, int32_t B, int32_t D, void* plan_dev, size_t pla
  * t*topk + s, -1 where padded.  Also lists the distinct experts ("groups") with their
  * first unit, unit count and first 16-column tile, and cuts each expert's routes, in the
  * same order, into chunks of 32 (the grouped kernel's weight-pass width): per chunk its
- * expert and 32 pair indices (-1 padded), in ascending expert order.
+ * expert, its live columns and the live columns before it, and 32 pair indices (-1
+ * padded), in ascending expert order.
  * Written into `units_dev` (moe_units_bytes(B, topk, E) bytes); run it before
  * moe_experts_run on the same stream. */
 int moe_group(const int32_t* ids_dev, int32_t B, int32_t topk, int32_t E, void* units_dev,
@@ -269,8 +270,8 @@ typedef struct {
  * One persistent, co-resident kernel.  By default (col_tiles 0) the grouped kernel: an
  * FC1 work item is one 32-wide hidden block of one 32-route chunk over the whole of K,
  * so one workgroup applies SwiGLU and MXFP8 to it and publishes it (device-coherent
- * stores, a call-tagged flag); FC2 tiles are dealt as contiguous runs, and each chunk's
- * FC2 waits for its hidden blocks.  The one-tile experts kernel (col_tiles 1) instead
+ * stores, a call-tagged flag); FC2 tiles are dealt as contiguous runs balanced on the
+ * bytes they move (moe_grouped_runs), and each chunk's FC2 waits for its hidden blocks.  The one-tile experts kernel (col_tiles 1) instead
  * gives every workgroup an equal contiguous slice of the FC1 weight stream, then of the
  * FC2 weight stream, and FC2 waits per expert for the split blocks FC1 slices publish.
  * The grid is sized from the kernel's occupancy so that it is resident at once; do not
