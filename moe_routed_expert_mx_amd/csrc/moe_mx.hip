@@ -3190,6 +3190,9 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
   const uint32_t call = static_cast<uint32_t>(lds_uni(lb + kQCall));
   if (w == kQFin) {
     // =============================================================== finisher wave
+    // the control waves issue ahead of the streaming waves on their SIMDs: the finisher's
+    // SwiGLU and requantization, and the loader's polls, are on the step's critical path
+    __builtin_amdgcn_s_setprio(2);
     // FC1: finish the workgroup's hidden blocks in order
 #pragma unroll 1
   for (int k = 0; k < q.n1; ++k) {
@@ -3318,6 +3321,7 @@ __global__ __launch_bounds__(kQWG) void decode_whole_kernel(QArgs a) {
     return;
   }
   // ================================================================= loader wave
+  __builtin_amdgcn_s_setprio(2);  // as the finisher
   static_assert(kQLoad == kQStream + 1 && kQWG == 64 * (kQLoad + 1), "the loader is the last wave");
   // FC2: for each expert of the workgroup's run, in order, wait for its hidden (polling
   // from the start of the call) and copy it into one of the two LDS hidden buffers.  These
